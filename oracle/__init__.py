@@ -1,0 +1,166 @@
+"""fp64 CPU oracle for causal kernelized linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package.  The HIP path (efficient_transformer_amd) never imports it, and the
+two share no code.  The arithmetic lives in oracle.c (plain C, float64, OpenMP
+over independent heads); this module only builds that file and marshals numpy
+arrays into it.
+
+Method: "Transformers are RNNs: Fast Autoregressive Transformers with Linear
+Attention" (Katharopoulos et al., 2020), page of that title, Proposed method and
+Main findings.  phi(x) = elu(x) + 1; S_i = sum_{j<=i} phi(k_j) v_j^T;
+z_i = sum_{j<=i} phi(k_j); out_i = phi(q_i)^T S_i / phi(q_i)^T z_i.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+
+
+def compile_lib(src: str, dst: str) -> str:
+    """gcc -O3 (no fast-math) with OpenMP; the build used for the oracle and for test mutants."""
+    tmp = dst + ".tmp"
+    cmd = ["gcc", "-O3", "-fopenmp", "-shared", "-fPIC", "-Wall", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, dst)
+    return dst
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so."""
+    if force or not os.path.exists(LIB_PATH):
+        compile_lib(_SRC, LIB_PATH)
+    return LIB_PATH
+
+
+class Oracle:
+    """ctypes bindings of one build of oracle.c (the default build, or a test's mutant)."""
+
+    def __init__(self, path: str):
+        L = ctypes.CDLL(path)
+        L.oracle_phi1.restype = ctypes.c_double
+        L.oracle_phi1.argtypes = [ctypes.c_double]
+        L.oracle_phi.argtypes = [_dp, _dp, _i64]
+        L.oracle_max_threads.restype = ctypes.c_int
+        L.oracle_causal.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int]
+        L.oracle_causal_rows.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64,
+                                         ctypes.POINTER(_i64), _i64, _dp, ctypes.c_int]
+        L.oracle_noncausal.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int]
+        L.oracle_decode_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int]
+        self.L = L
+        self.path = path
+
+    def max_threads(self) -> int:
+        return int(self.L.oracle_max_threads())
+
+    def phi(self, x) -> np.ndarray:
+        x = _f64(x)
+        y = np.empty_like(x)
+        self.L.oracle_phi(_p(x), _p(y), x.size)
+        return y
+
+    def causal(self, Q, K, V, threads: int = 0):
+        """Causal outputs by the running-sum recurrence.
+
+        Q, K: [..., N, D]; V: [..., N, M] (leading dims are independent heads).
+        Returns (out [..., N, M], S [..., D, M], z [..., D]); S, z are the final state.
+        """
+        Q, K, V = _f64(Q), _f64(K), _f64(V)
+        *lead, N, D = Q.shape
+        M = V.shape[-1]
+        assert K.shape == Q.shape and tuple(V.shape[:-1]) == tuple(Q.shape[:-1])
+        BH = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, N, M))
+        S = np.empty((*lead, D, M))
+        z = np.empty((*lead, D))
+        self.L.oracle_causal(_p(Q), _p(K), _p(V), _p(out), _p(S), _p(z), BH, N, D, M, threads)
+        return out, S, z
+
+    def causal_rows(self, Qh, Kh, Vh, rows, threads: int = 0) -> np.ndarray:
+        """Selected output rows of ONE head, from the quadratic definition.
+
+        Qh, Kh: [n, D]; Vh: [n, M] with n > max(rows) (row i reads rows 0..i only).
+        """
+        Qh, Kh, Vh = _f64(Qh), _f64(Kh), _f64(Vh)
+        n, D = Qh.shape
+        M = Vh.shape[1]
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((r.size, M))
+        self.L.oracle_causal_rows(_p(Qh), _p(Kh), _p(Vh), n, D, M,
+                                  r.ctypes.data_as(ctypes.POINTER(_i64)), r.size, _p(out), threads)
+        return out
+
+    def noncausal(self, Q, K, V, threads: int = 0) -> np.ndarray:
+        Q, K, V = _f64(Q), _f64(K), _f64(V)
+        *lead, N, D = Q.shape
+        M = V.shape[-1]
+        BH = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, N, M))
+        self.L.oracle_noncausal(_p(Q), _p(K), _p(V), _p(out), BH, N, D, M, threads)
+        return out
+
+    def decode_step(self, S, z, q, k, v, threads: int = 0) -> np.ndarray:
+        """One recurrent step; S [..., D, M] and z [..., D] (float64, contiguous) update in place."""
+        assert S.dtype == np.float64 and S.flags.c_contiguous
+        assert z.dtype == np.float64 and z.flags.c_contiguous
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        D, M = S.shape[-2], S.shape[-1]
+        BH = S.size // (D * M)
+        assert q.size == BH * D and k.size == BH * D and v.size == BH * M and z.size == BH * D
+        out = np.empty(v.shape)
+        self.L.oracle_decode_step(_p(S), _p(z), _p(q), _p(k), _p(v), _p(out), BH, D, M, threads)
+        return out
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def max_threads() -> int:
+    return default().max_threads()
+
+
+def phi(x):
+    return default().phi(x)
+
+
+def causal(Q, K, V, threads: int = 0):
+    return default().causal(Q, K, V, threads)
+
+
+def causal_rows(Qh, Kh, Vh, rows, threads: int = 0):
+    return default().causal_rows(Qh, Kh, Vh, rows, threads)
+
+
+def noncausal(Q, K, V, threads: int = 0):
+    return default().noncausal(Q, K, V, threads)
+
+
+def decode_step(S, z, q, k, v, threads: int = 0):
+    return default().decode_step(S, z, q, k, v, threads)

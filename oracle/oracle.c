@@ -1,0 +1,194 @@
+/*
+ * Oracle for causal kernelized linear attention -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Only the test suite, the smoke check and the bench's CPU-baseline leg may load
+ * this library.  The HIP product path never calls it and shares no code with it.
+ *
+ * Everything is float64 on the host, written as plainly as possible so that it
+ * can be checked against the pages by eye.  The method is that of
+ * "Transformers are RNNs: Fast Autoregressive Transformers with Linear Attention"
+ * (Katharopoulos et al., 2020), as reviewed on the page of that title:
+ *
+ *   - Proposed method: softmax similarity is replaced by a dot product of feature
+ *     maps phi(q)^T phi(k); by associativity the attention becomes
+ *     phi(Q) (phi(K)^T V), a sum computed once and reused by every query.
+ *   - Proposed method: causal masking is kept by updating the cumulative sums
+ *     S_i and Z_i one position at a time (linear time, constant memory); the
+ *     causal model is an RNN with the two memories (S, z).
+ *   - Main findings: the feature map is elu based; phi(x) = elu(x) + 1.
+ *
+ * With S_i = sum_{j<=i} phi(k_j) v_j^T (D x M) and z_i = sum_{j<=i} phi(k_j) (D):
+ *     out_i = phi(q_i)^T S_i / (phi(q_i)^T z_i).
+ *
+ * Layouts (row major, contiguous): Q, K [BH][N][D]; V, out [BH][N][M];
+ * S [BH][D][M] (row d, column m); z [BH][D].
+ *
+ * Every function here is pinned by tests outside this file (hand-derived exact
+ * values, closed forms, invariants and 50-digit evaluations); none is "parity
+ * unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* phi(x) = elu(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise.
+ * (Page "Transformers are RNNs", Main findings: elu-based feature map.)
+ * The exp branch is elu(x) + 1 = (exp(x) - 1) + 1 written without the
+ * cancellation. */
+double oracle_phi1(double x) { return x > 0.0 ? x + 1.0 : exp(x); }
+
+void oracle_phi(const double *x, double *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = oracle_phi1(x[i]);
+}
+
+static int pick_threads(int threads) {
+#ifdef _OPENMP
+    return threads > 0 ? threads : omp_get_max_threads();
+#else
+    (void)threads;
+    return 1;
+#endif
+}
+
+int oracle_max_threads(void) { return pick_threads(0); }
+
+/* Causal attention by the running sums of the page (Proposed method: S_i and
+ * Z_i updated step by step).  Per head: S = 0, z = 0; for i = 0..N-1 add
+ * phi(k_i) v_i^T to S and phi(k_i) to z, then read out with phi(q_i).
+ * S_out / z_out (may be NULL) receive the final state S_{N-1}, z_{N-1}. */
+void oracle_causal(const double *Q, const double *K, const double *V, double *out,
+                   double *S_out, double *z_out,
+                   int64_t BH, int64_t N, int64_t D, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *z = (double *)calloc((size_t)D, sizeof(double));
+        double *f = (double *)malloc((size_t)D * sizeof(double));
+        double *g = (double *)malloc((size_t)D * sizeof(double));
+        const double *Qh = Q + h * N * D, *Kh = K + h * N * D, *Vh = V + h * N * M;
+        double *Oh = out + h * N * M;
+        for (int64_t i = 0; i < N; ++i) {
+            const double *k = Kh + i * D, *q = Qh + i * D, *v = Vh + i * M;
+            for (int64_t d = 0; d < D; ++d) f[d] = oracle_phi1(k[d]);
+            for (int64_t d = 0; d < D; ++d) {
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += f[d] * v[m];
+                z[d] += f[d];
+            }
+            for (int64_t d = 0; d < D; ++d) g[d] = oracle_phi1(q[d]);
+            double den = 0.0;
+            for (int64_t d = 0; d < D; ++d) den += g[d] * z[d];
+            for (int64_t m = 0; m < M; ++m) {
+                double num = 0.0;
+                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];
+                Oh[i * M + m] = num / den;
+            }
+        }
+        if (S_out) memcpy(S_out + h * D * M, S, (size_t)(D * M) * sizeof(double));
+        if (z_out) memcpy(z_out + h * D, z, (size_t)D * sizeof(double));
+        free(S); free(z); free(f); free(g);
+    }
+}
+
+/* Causal attention straight from its definition, for selected rows of ONE head:
+ *   out_i = sum_{j<=i} (phi(q_i).phi(k_j)) v_j / sum_{j<=i} phi(q_i).phi(k_j).
+ * (Page "Transformers are RNNs", Proposed method: the softmax similarity is
+ * replaced by the feature-map dot product; causal masking keeps j <= i.)
+ * Cost O(i (D + M)) per row, so single rows of very long sequences can be
+ * checked one by one.  Q, K: [N][D], V: [N][M], out: [nrows][M]. */
+void oracle_causal_rows(const double *Q, const double *K, const double *V,
+                        int64_t N, int64_t D, int64_t M,
+                        const int64_t *rows, int64_t nrows, double *out, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows[r];
+        double *o = out + r * M;
+        if (i < 0 || i >= N) {
+            for (int64_t m = 0; m < M; ++m) o[m] = NAN;
+            continue;
+        }
+        double *g = (double *)malloc((size_t)D * sizeof(double));
+        double *num = (double *)calloc((size_t)M, sizeof(double));
+        for (int64_t d = 0; d < D; ++d) g[d] = oracle_phi1(Q[i * D + d]);
+        double den = 0.0;
+        for (int64_t j = 0; j <= i; ++j) {
+            double w = 0.0;
+            for (int64_t d = 0; d < D; ++d) w += g[d] * oracle_phi1(K[j * D + d]);
+            for (int64_t m = 0; m < M; ++m) num[m] += w * V[j * M + m];
+            den += w;
+        }
+        for (int64_t m = 0; m < M; ++m) o[m] = num[m] / den;
+        free(g); free(num);
+    }
+}
+
+/* Non-causal attention in the associative form of the page (Proposed method:
+ * phi(Q) (phi(K)^T V), the sum computed once and reused for every query):
+ * S = sum_j phi(k_j) v_j^T, z = sum_j phi(k_j); out_i = phi(q_i)^T S / phi(q_i).z. */
+void oracle_noncausal(const double *Q, const double *K, const double *V, double *out,
+                      int64_t BH, int64_t N, int64_t D, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *z = (double *)calloc((size_t)D, sizeof(double));
+        double *g = (double *)malloc((size_t)D * sizeof(double));
+        const double *Qh = Q + h * N * D, *Kh = K + h * N * D, *Vh = V + h * N * M;
+        double *Oh = out + h * N * M;
+        for (int64_t j = 0; j < N; ++j) {
+            for (int64_t d = 0; d < D; ++d) {
+                double f = oracle_phi1(Kh[j * D + d]);
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += f * Vh[j * M + m];
+                z[d] += f;
+            }
+        }
+        for (int64_t i = 0; i < N; ++i) {
+            for (int64_t d = 0; d < D; ++d) g[d] = oracle_phi1(Qh[i * D + d]);
+            double den = 0.0;
+            for (int64_t d = 0; d < D; ++d) den += g[d] * z[d];
+            for (int64_t m = 0; m < M; ++m) {
+                double num = 0.0;
+                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];
+                Oh[i * M + m] = num / den;
+            }
+        }
+        free(S); free(z); free(g);
+    }
+}
+
+/* One recurrent (autoregressive) step for BH independent heads.
+ * (Page "Transformers are RNNs", Proposed method: the causal transformer is an
+ * RNN with the memories (S, z); Main findings: the internal state is updated
+ * incrementally.)  The new token enters the state first, then the output is read
+ * (the sums run over j <= i): S += phi(k) v^T; z += phi(k);
+ * out = phi(q)^T S / phi(q).z.  S [BH][D][M] and z [BH][D] are updated in place;
+ * q, k [BH][D]; v, out [BH][M]. */
+void oracle_decode_step(double *S, double *z, const double *q, const double *k,
+                        const double *v, double *out,
+                        int64_t BH, int64_t D, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        double *Sh = S + h * D * M, *zh = z + h * D;
+        const double *qh = q + h * D, *kh = k + h * D, *vh = v + h * M;
+        double *oh = out + h * M;
+        for (int64_t d = 0; d < D; ++d) {
+            double f = oracle_phi1(kh[d]);
+            for (int64_t m = 0; m < M; ++m) Sh[d * M + m] += f * vh[m];
+            zh[d] += f;
+        }
+        double den = 0.0;
+        for (int64_t d = 0; d < D; ++d) den += oracle_phi1(qh[d]) * zh[d];
+        for (int64_t m = 0; m < M; ++m) {
+            double num = 0.0;
+            for (int64_t d = 0; d < D; ++d) num += oracle_phi1(qh[d]) * Sh[d * M + m];
+            oh[m] = num / den;
+        }
+    }
+}

@@ -1,0 +1,282 @@
+"""Pins of the fp64 oracle against facts outside it.
+
+Helpers, not a test module: `run_all(o)` runs every pin against an oracle build
+`o` (oracle.Oracle) and returns the list of failures.  tests/test_oracle.py runs
+it on the real build (no failure allowed) and on deliberately broken copies of
+oracle.c (each must be caught), so that the pins are known to bite.
+
+What pins what (page: "Transformers are RNNs", Katharopoulos et al. 2020):
+  * golden/*.json  -- hand-derived exact values (phi, causal, non-causal, state,
+                      decode), D != M so that a transposed state shows;
+  * brute force    -- the quadratic masked form tril(phi(Q) phi(K)^T) V,
+                      row-normalised, in numpy (Proposed method: the
+                      associativity rewrite leaves this result unchanged);
+  * mpmath         -- the definition at 50 digits on tiny inputs;
+  * invariants     -- V = 1 gives 1; out_0 = v_0; causal last row = non-causal
+                      row; affine equivariance in V; outputs in the convex hull
+                      of the visible values; no dependence on future positions or
+                      on other queries; key-order invariance of the non-causal form;
+  * RNN form       -- decode steps reproduce causal rows and the final state
+                      (Proposed method: the causal model is an RNN with memories S, z);
+  * chunked algebra -- a blockwise fp64 evaluation (the form the GPU kernels
+                      use) agrees with the recurrence for chunk 1, 3, 16 and N.
+"""
+from __future__ import annotations
+
+import glob
+import json
+import os
+import re
+
+import mpmath
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def np_phi(x):
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def brute_causal(Q, K, V):
+    """Quadratic masked form for one head: W = tril(phi(Q) phi(K)^T); out = W V / W 1."""
+    W = np.tril(np_phi(Q) @ np_phi(K).T)
+    return (W @ V) / W.sum(axis=1, keepdims=True)
+
+
+def brute_noncausal(Q, K, V):
+    W = np_phi(Q) @ np_phi(K).T
+    return (W @ V) / W.sum(axis=1, keepdims=True)
+
+
+def chunked_causal(Q, K, V, C):
+    """Blockwise evaluation: intra-chunk masked quadratic term plus the state of earlier chunks."""
+    N, D = Q.shape
+    M = V.shape[1]
+    FQ, FK = np_phi(Q), np_phi(K)
+    S = np.zeros((D, M))
+    z = np.zeros(D)
+    out = np.empty((N, M))
+    for c0 in range(0, N, C):
+        c1 = min(N, c0 + C)
+        A = np.tril(FQ[c0:c1] @ FK[c0:c1].T)
+        num = A @ V[c0:c1] + FQ[c0:c1] @ S
+        den = A.sum(axis=1) + FQ[c0:c1] @ z
+        out[c0:c1] = num / den[:, None]
+        S = S + FK[c0:c1].T @ V[c0:c1]
+        z = z + FK[c0:c1].sum(axis=0)
+    return out, S, z
+
+
+_NUM = re.compile(r"(?<![A-Za-z_])(\d+\.?\d*(?:[eE][-+]?\d+)?)")
+
+
+def _mp_eval(expr: str):
+    """Evaluate an exact expression (numbers, + - * /, exp) at 50 digits."""
+    mpmath.mp.dps = 50
+    src = _NUM.sub(lambda m: f"mpf('{m.group(1)}')", expr)
+    return eval(src, {"__builtins__": {}, "exp": mpmath.exp, "mpf": mpmath.mpf}, {})
+
+
+def _expect(arr):
+    return np.array([[float(_mp_eval(e)) for e in row] for row in arr]) if isinstance(arr[0], list) \
+        else np.array([float(_mp_eval(e)) for e in arr])
+
+
+def _close(name, got, want, rtol, fails):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    if got.shape != want.shape:
+        fails.append(f"{name}: shape {got.shape} != {want.shape}")
+        return
+    if not np.all(np.isfinite(got)):
+        fails.append(f"{name}: non-finite values")
+        return
+    err = np.max(np.abs(got - want) / np.maximum(np.abs(want), 1e-300)) if got.size else 0.0
+    # absolute floor for exact zeros
+    abs_err = np.max(np.abs(got - want)) if got.size else 0.0
+    if not (err <= rtol or abs_err <= rtol * 1e-3):
+        fails.append(f"{name}: max rel err {err:.3e} > {rtol:.1e}")
+
+
+def pin_golden(o, fails):
+    with open(os.path.join(GOLDEN, "phi_values.json")) as f:
+        g = json.load(f)
+    xs = np.array([float(a) for a, _ in g["cases"]])
+    want = np.array([float(_mp_eval(b)) for _, b in g["cases"]])
+    _close("golden phi (vector)", o.phi(xs), want, 1e-15, fails)
+    _close("golden phi (scalar)", [o.L.oracle_phi1(float(x)) for x in xs], want, 1e-15, fails)
+    for path in sorted(glob.glob(os.path.join(GOLDEN, "causal_*.json"))):
+        name = os.path.basename(path)
+        with open(path) as f:
+            g = json.load(f)
+        Q, K, V = (np.array(g[k], dtype=np.float64) for k in ("Q", "K", "V"))
+        out, S, z = o.causal(Q[None], K[None], V[None])
+        _close(f"{name} causal", out[0], _expect(g["causal"]), 1e-14, fails)
+        _close(f"{name} state S", S[0], _expect(g["S"]), 1e-14, fails)
+        _close(f"{name} state z", z[0], _expect(g["z"]), 1e-14, fails)
+        rows = o.causal_rows(Q, K, V, np.arange(Q.shape[0]))
+        _close(f"{name} causal_rows", rows, _expect(g["causal"]), 1e-14, fails)
+        _close(f"{name} noncausal", o.noncausal(Q[None], K[None], V[None])[0],
+               _expect(g["noncausal"]), 1e-14, fails)
+        D, M = K.shape[1], V.shape[1]
+        Sd = np.zeros((1, D, M))
+        zd = np.zeros((1, D))
+        outs = [o.decode_step(Sd, zd, Q[i][None], K[i][None], V[i][None])[0] for i in range(Q.shape[0])]
+        _close(f"{name} decode outputs", np.array(outs), _expect(g["causal"]), 1e-14, fails)
+        _close(f"{name} decode state S", Sd[0], _expect(g["S"]), 1e-14, fails)
+        _close(f"{name} decode state z", zd[0], _expect(g["z"]), 1e-14, fails)
+
+
+def _rand(rng, N, D, M, scale=1.0):
+    return (rng.normal(size=(N, D)) * scale, rng.normal(size=(N, D)) * scale, rng.normal(size=(N, M)))
+
+
+SHAPES = [(1, 1, 1), (2, 1, 3), (3, 2, 1), (7, 3, 2), (16, 16, 3), (64, 3, 16), (33, 16, 16), (64, 2, 5)]
+
+
+def pin_bruteforce(o, fails):
+    rng = np.random.default_rng(1234)
+    for (N, D, M) in SHAPES:
+        for scale in (0.5, 1.0, 3.0):
+            Q, K, V = _rand(rng, N, D, M, scale)
+            want = brute_causal(Q, K, V)
+            out, S, z = o.causal(Q[None], K[None], V[None])
+            _close(f"brute causal N{N} D{D} M{M} s{scale}", out[0], want, 1e-11, fails)
+            _close(f"brute causal_rows N{N} D{D} M{M} s{scale}",
+                   o.causal_rows(Q, K, V, np.arange(N)), want, 1e-11, fails)
+            _close(f"brute noncausal N{N} D{D} M{M} s{scale}",
+                   o.noncausal(Q[None], K[None], V[None])[0], brute_noncausal(Q, K, V), 1e-11, fails)
+            _close(f"brute final S N{N} D{D} M{M}", S[0], np_phi(K).T @ V, 1e-11, fails)
+            _close(f"brute final z N{N} D{D} M{M}", z[0], np_phi(K).sum(axis=0), 1e-12, fails)
+    # several heads at once: each head independent of the others
+    Q = rng.normal(size=(3, 2, 9, 4))
+    K = rng.normal(size=(3, 2, 9, 4))
+    V = rng.normal(size=(3, 2, 9, 5))
+    out, _, _ = o.causal(Q, K, V)
+    for b in range(3):
+        for h in range(2):
+            _close(f"brute multihead b{b} h{h}", out[b, h], brute_causal(Q[b, h], K[b, h], V[b, h]), 1e-11, fails)
+
+
+def pin_mpmath(o, fails):
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(99)
+    for (N, D, M) in [(1, 1, 1), (4, 2, 3), (6, 3, 2), (8, 1, 2)]:
+        Q, K, V = _rand(rng, N, D, M, 2.0)
+
+        def ph(x):
+            x = mpmath.mpf(float(x))
+            return x + 1 if x > 0 else mpmath.exp(x)
+
+        want = np.zeros((N, M))
+        for i in range(N):
+            num = [mpmath.mpf(0)] * M
+            den = mpmath.mpf(0)
+            for j in range(i + 1):
+                w = mpmath.fsum(ph(Q[i, d]) * ph(K[j, d]) for d in range(D))
+                den += w
+                for m in range(M):
+                    num[m] += w * mpmath.mpf(float(V[j, m]))
+            for m in range(M):
+                want[i, m] = float(num[m] / den)
+        out, _, _ = o.causal(Q[None], K[None], V[None])
+        err = np.max(np.abs(out[0] - want) / np.maximum(np.abs(want).max(axis=1, keepdims=True), 1e-300))
+        if not err <= 1e-13:
+            fails.append(f"mpmath N{N} D{D} M{M}: row-relative err {err:.3e} > 1e-13")
+
+
+def pin_invariants(o, fails):
+    rng = np.random.default_rng(7)
+    for (N, D, M) in [(13, 4, 6), (40, 8, 3), (64, 16, 16)]:
+        Q, K, V = _rand(rng, N, D, M, 1.5)
+        out, S, z = o.causal(Q[None], K[None], V[None])
+        out = out[0]
+        ones = o.causal(Q[None], K[None], np.ones((1, N, M)))[0][0]
+        if not np.max(np.abs(ones - 1.0)) <= 1e-14:
+            fails.append(f"ones invariant N{N}: {np.max(np.abs(ones - 1.0)):.3e}")
+        nc_ones = o.noncausal(Q[None], K[None], np.ones((1, N, M)))[0]
+        if not np.max(np.abs(nc_ones - 1.0)) <= 1e-14:
+            fails.append(f"non-causal ones invariant N{N}")
+        _close(f"first row N{N}", out[0], V[0], 1e-14, fails)
+        nc = o.noncausal(Q[None], K[None], V[None])[0]
+        _close(f"last row causal=noncausal N{N}", out[-1], nc[-1], 1e-12, fails)
+        a, c = -2.5, rng.normal(size=M)
+        aff = o.causal(Q[None], K[None], (a * V + c)[None])[0][0]
+        _close(f"affine equivariance N{N}", aff, a * out + c, 1e-11, fails)
+        lo = np.minimum.accumulate(V, axis=0)
+        hi = np.maximum.accumulate(V, axis=0)
+        if not (np.all(out >= lo - 1e-12) and np.all(out <= hi + 1e-12)):
+            fails.append(f"convex hull N{N}")
+        # causality: changing positions after i leaves rows <= i unchanged
+        i = N // 2
+        Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+        Q2[i + 1:] += 1.0
+        K2[i + 1:] -= 0.7
+        V2[i + 1:] *= 3.0
+        out2 = o.causal(Q2[None], K2[None], V2[None])[0][0]
+        if not np.array_equal(out2[: i + 1], out[: i + 1]):
+            fails.append(f"causality N{N}")
+        if np.allclose(out2[i + 1:], out[i + 1:]):
+            fails.append(f"future positions ignored entirely N{N}")
+        # row i depends on q only through q_i
+        Q3 = Q.copy()
+        Q3[:i] += 0.9
+        out3 = o.causal(Q3[None], K[None], V[None])[0][0]
+        if not np.array_equal(out3[i:], out[i:]):
+            fails.append(f"query locality N{N}")
+        # non-causal: order of keys does not matter, query order permutes rows
+        perm = rng.permutation(N)
+        ncp = o.noncausal(Q[None], K[perm][None], V[perm][None])[0]
+        _close(f"non-causal key permutation N{N}", ncp, nc, 1e-12, fails)
+        ncq = o.noncausal(Q[perm][None], K[None], V[None])[0]
+        _close(f"non-causal query permutation N{N}", ncq, nc[perm], 1e-12, fails)
+
+
+def pin_rnn(o, fails):
+    rng = np.random.default_rng(5)
+    for (BH, N, D, M) in [(3, 20, 4, 6), (2, 50, 16, 8)]:
+        Q = rng.normal(size=(BH, N, D))
+        K = rng.normal(size=(BH, N, D))
+        V = rng.normal(size=(BH, N, M))
+        out, S, z = o.causal(Q, K, V)
+        Sd = np.zeros((BH, D, M))
+        zd = np.zeros((BH, D))
+        dec = np.stack([o.decode_step(Sd, zd, Q[:, t], K[:, t], V[:, t]) for t in range(N)], axis=1)
+        _close(f"decode == causal rows BH{BH} N{N}", dec, out, 1e-12, fails)
+        _close(f"decode state == causal state BH{BH} N{N}", Sd, S, 1e-12, fails)
+        _close(f"decode z == causal z BH{BH} N{N}", zd, z, 1e-12, fails)
+        # resume from a copied state (the state is the whole history)
+        t0 = N // 3
+        S1 = np.zeros((BH, D, M))
+        z1 = np.zeros((BH, D))
+        for t in range(t0):
+            o.decode_step(S1, z1, Q[:, t], K[:, t], V[:, t])
+        S2, z2 = S1.copy(), z1.copy()
+        res = np.stack([o.decode_step(S2, z2, Q[:, t], K[:, t], V[:, t]) for t in range(t0, N)], axis=1)
+        _close(f"decode resume BH{BH}", res, out[:, t0:], 1e-12, fails)
+
+
+def pin_chunked(o, fails):
+    rng = np.random.default_rng(11)
+    for (N, D, M) in [(64, 8, 5), (100, 16, 16)]:
+        Q, K, V = _rand(rng, N, D, M)
+        out, S, z = o.causal(Q[None], K[None], V[None])
+        for C in (1, 3, 16, N):
+            co, cS, cz = chunked_causal(Q, K, V, C)
+            _close(f"chunked C{C} N{N}", co, out[0], 1e-12, fails)
+            _close(f"chunked state C{C} N{N}", cS, S[0], 1e-12, fails)
+
+
+ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked]
+
+
+def run_all(o, pins=ALL_PINS):
+    fails = []
+    for p in pins:
+        try:
+            p(o, fails)
+        except Exception as e:  # a crash in a pin is a failure of the oracle under test
+            fails.append(f"{p.__name__}: raised {type(e).__name__}: {e}")
+    return fails

@@ -1,0 +1,62 @@
+"""The oracle against its pins, and the pins against planted mistakes (CPU only)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ORACLE_SRC = os.path.join(os.path.dirname(HERE), "oracle", "oracle.c")
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    fails = oracle_pins.run_all(oracle.default(), pins=[pin])
+    assert not fails, "\n".join(fails)
+
+
+# Plausible mistakes, each planted in a copy of oracle.c; the pins must catch every one.
+MUTANTS = {
+    "elu_without_plus_one": ("return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x) - 1.0;"),
+    "exp_feature_map": ("return x > 0.0 ? x + 1.0 : exp(x);", "return exp(x);"),
+    "phi_branch_sign": ("return x > 0.0 ? x + 1.0 : exp(x);", "return x < 0.0 ? x + 1.0 : exp(x);"),
+    "dropped_normaliser": ("Oh[i * M + m] = num / den;\n            }\n        }\n        if (S_out)",
+                           "Oh[i * M + m] = num;\n            }\n        }\n        if (S_out)"),
+    "transposed_state_update": ("for (int64_t m = 0; m < M; ++m) S[d * M + m] += f[d] * v[m];",
+                                "for (int64_t m = 0; m < M; ++m) S[m * D + d] += f[d] * v[m];"),
+    "numerator_sign": ("for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];\n                Oh[i * M + m]",
+                       "for (int64_t d = 0; d < D; ++d) num -= g[d] * S[d * M + m];\n                Oh[i * M + m]"),
+    "exclusive_mask_rows": ("for (int64_t j = 0; j <= i; ++j) {", "for (int64_t j = 0; j < i; ++j) {"),
+    "query_key_swap_rows": ("w += g[d] * oracle_phi1(K[j * D + d]);", "w += g[d] * oracle_phi1(Q[j * D + d]);"),
+    "value_index_rows": ("num[m] += w * V[j * M + m];", "num[m] += w * V[i * M + m];"),
+    "noncausal_wrong_z": ("for (int64_t d = 0; d < D; ++d) den += g[d] * z[d];\n            for (int64_t m = 0; m < M; ++m) {\n                double num = 0.0;\n                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];\n                Oh[i * M + m] = num / den;\n            }\n        }\n        free(S); free(z); free(g);",
+                          "for (int64_t d = 0; d < D; ++d) den += g[d] * z[0];\n            for (int64_t m = 0; m < M; ++m) {\n                double num = 0.0;\n                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];\n                Oh[i * M + m] = num / den;\n            }\n        }\n        free(S); free(z); free(g);"),
+    "decode_overwrites_z": ("zh[d] += f;", "zh[d] = f;"),
+    "decode_den_uses_k": ("den += oracle_phi1(qh[d]) * zh[d];", "den += oracle_phi1(kh[d]) * zh[d];"),
+    "decode_reads_before_update": (
+        "        for (int64_t d = 0; d < D; ++d) {\n            double f = oracle_phi1(kh[d]);\n            for (int64_t m = 0; m < M; ++m) Sh[d * M + m] += f * vh[m];\n            zh[d] += f;\n        }\n        double den = 0.0;\n        for (int64_t d = 0; d < D; ++d) den += oracle_phi1(qh[d]) * zh[d];\n        for (int64_t m = 0; m < M; ++m) {\n            double num = 0.0;\n            for (int64_t d = 0; d < D; ++d) num += oracle_phi1(qh[d]) * Sh[d * M + m];\n            oh[m] = num / den;\n        }\n",
+        "        double den = 0.0;\n        for (int64_t d = 0; d < D; ++d) den += oracle_phi1(qh[d]) * zh[d];\n        for (int64_t m = 0; m < M; ++m) {\n            double num = 0.0;\n            for (int64_t d = 0; d < D; ++d) num += oracle_phi1(qh[d]) * Sh[d * M + m];\n            oh[m] = num / den;\n        }\n        for (int64_t d = 0; d < D; ++d) {\n            double f = oracle_phi1(kh[d]);\n            for (int64_t m = 0; m < M; ++m) Sh[d * M + m] += f * vh[m];\n            zh[d] += f;\n        }\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mut = tmp_path / f"{name}.c"
+    mut.write_text(src.replace(old, new, 1))  # the first site (functions appear in file order)
+    lib = oracle.compile_lib(str(mut), str(tmp_path / f"lib{name}.so"))
+    fails = oracle_pins.run_all(oracle.Oracle(lib))
+    assert fails, f"planted mistake {name} was not caught by any pin"
+
+
+def test_threads_do_not_change_results():
+    rng = np.random.default_rng(3)
+    Q, K, V = rng.normal(size=(6, 30, 8)), rng.normal(size=(6, 30, 8)), rng.normal(size=(6, 30, 4))
+    a = oracle.causal(Q, K, V, threads=1)
+    b = oracle.causal(Q, K, V, threads=4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
