@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Throughput of causal kernelized linear attention on one MI355X.
+
+Method: "Transformers are RNNs: Fast Autoregressive Transformers with Linear
+Attention" (Katharopoulos et al., 2020) -- parallel (chunked prefill) mode and
+recurrent (decode) mode, both through the C ABI of liblinattn.so.
+
+Headline (`value`): prefill tokens/s on fp32 inputs, B=8 H=8 N=1024 D=M=64
+(one token = one position across all heads), inputs resident in HBM, rotated
+over enough buffer sets that the 256 MB last-level cache cannot hold them.
+A step is one la_forward_chunked call over one batch.
+
+Also reported in the same JSON line: the dominant kernel's roofline (HIP
+events around each launch of it), the fp64 CPU oracle timed on a bounded
+sample of the same workload, the recurrent decode workload (256 streams x 8
+heads, D=M=64, 4096 steps from a zero state) and the two bf16 prefill
+workloads.  Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+FP32_MFMA_PEAK_TFS = 157.3  # dense fp32 matrix
+BF16_MFMA_PEAK_TFS = 2516.6  # dense bf16 matrix
+LLC_BYTES = 256 << 20       # Infinity Cache
+
+METRIC = "causal linear-attention tokens/sec (prefill, decode) and % of MFMA/HBM roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(cfg) -> int:
+    """Algorithmic bytes of one prefill call: read Q, K, V once, write out (fp32) once."""
+    s = 4 if cfg["dtype"] == "f32" else 2
+    BH, N, D, M = cfg["B"] * cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    return BH * N * ((2 * D + M) * s + 4 * M)
+
+
+def prefill_flops_min(cfg) -> int:
+    """Algorithmic flops: per head-token, state update 2DM + readout 2DM + normaliser 4D + divide M."""
+    BH, N, D, M = cfg["B"] * cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    return BH * N * (4 * D * M + 4 * D + M)
+
+
+def decode_bytes_per_step(cfg) -> int:
+    """Per step: S and z read and written, q k v read, out written (all fp32)."""
+    BH, D, M = cfg["B"] * cfg["H"], cfg["D"], cfg["M"]
+    return BH * (2 * 4 * D * M + 2 * 4 * D + 4 * (2 * D + M) + 4 * M)
+
+
+def make_prefill_sets(cfg, nsets, dev):
+    import torch
+    import synthetic
+    sets = []
+    for r in range(nsets):
+        Q = synthetic.draw_torch(r, synthetic.TID_Q, (cfg["B"], cfg["H"], cfg["N"], cfg["D"]), cfg["sigma"],
+                                 cfg["dtype"], dev)
+        K = synthetic.draw_torch(r, synthetic.TID_K, (cfg["B"], cfg["H"], cfg["N"], cfg["D"]), cfg["sigma"],
+                                 cfg["dtype"], dev)
+        V = synthetic.draw_torch(r, synthetic.TID_V, (cfg["B"], cfg["H"], cfg["N"], cfg["M"]), cfg["sigma"],
+                                 cfg["dtype"], dev)
+        out = torch.empty((cfg["B"], cfg["H"], cfg["N"], cfg["M"]), dtype=torch.float32, device=dev)
+        sets.append((Q, K, V, out))
+    torch.cuda.synchronize()
+    return sets
+
+
+def bench_prefill(cfg, steps, warmup, dev, kernel_timing=True):
+    """Returns a dict of timings for one prefill workload."""
+    import torch
+    import efficient_transformer_amd as ea
+    from efficient_transformer_amd import linattn as L
+
+    code = L.LA_F32 if cfg["dtype"] == "f32" else L.LA_BF16
+    B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    C, G, wsb = ea.forward_plan(B, H, N, D, M, True, code, cfg.get("chunk", 0))
+    nbytes = prefill_bytes(cfg)
+    nsets = max(1, math.ceil(1.25 * LLC_BYTES / nbytes))
+    sets = make_prefill_sets(cfg, nsets, dev)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        Q, K, V, out = sets[i % nsets]
+        ea.forward_chunked(Q, K, V, causal=True, chunk=C, out=out, workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = dict(chunk=C, segments=G, nsets=nsets, ms_per_step=ms, tokens_per_s=B * N / (ms * 1e-3),
+               bytes=nbytes, flops_min=prefill_flops_min(cfg))
+    if kernel_timing:
+        # Same work through the stage entry points, with events around the launches of
+        # each stage kernel (all on `stream`, the stream the library launches on).
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        for i in range(steps + warmup):
+            Q, K, V, out = sets[i % nsets]
+            e = ev[i - warmup] if i >= warmup else None
+            if e: e[0].record(stream)
+            if G > 1:
+                ea.segment_states(K, V, ws, C, G, G - 1, stream=stream)
+            if e: e[1].record(stream)
+            if G > 1:
+                ea.segment_scan(ws, B, H, D, M, G, G - 1, stream=stream)
+            if e: e[2].record(stream)
+            ea.segment_outputs(Q, K, V, out, ws, C, G, causal=True, stream=stream)
+            if e: e[3].record(stream)
+        torch.cuda.synchronize()
+        t_state = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+        t_scan = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+        t_out = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
+        res.update(us_state=t_state * 1e3, us_scan=t_scan * 1e3, us_output=t_out * 1e3)
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(cfg, reps, dev, warm_steps=64):
+    import torch
+    import efficient_transformer_amd as ea
+    import synthetic
+
+    B, H, D, M, T = cfg["B"], cfg["H"], cfg["D"], cfg["M"], cfg["T"]
+    q = synthetic.draw_torch(0, synthetic.TID_DQ, (T, B, H, D), cfg["sigma"], cfg["dtype"], dev)
+    k = synthetic.draw_torch(0, synthetic.TID_DK, (T, B, H, D), cfg["sigma"], cfg["dtype"], dev)
+    v = synthetic.draw_torch(0, synthetic.TID_DV, (T, B, H, M), cfg["sigma"], cfg["dtype"], dev)
+    S = torch.zeros((B, H, D, M), device=dev)
+    z = torch.zeros((B, H, D), device=dev)
+    out = torch.empty((B, H, M), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for t in range(warm_steps):
+        ea.decode_step(S, z, q[t], k[t], v[t], out=out, stream=stream)
+    times = []
+    for _ in range(reps):
+        S.zero_()
+        z.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(T):
+            ea.decode_step(S, z, q[t], k[t], v[t], out=out, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    # per-launch kernel time: events around single launches
+    n = 256
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for t in range(n):
+        evs[t][0].record(stream)
+        ea.decode_step(S, z, q[t], k[t], v[t], out=out, stream=stream)
+        evs[t][1].record(stream)
+    torch.cuda.synchronize()
+    us_kernel = sum(a.elapsed_time(b) for a, b in evs) / n * 1e3
+    best = min(times)
+    per_step_bytes = decode_bytes_per_step(cfg)
+    del q, k, v
+    torch.cuda.empty_cache()
+    return dict(ms_total_best=best, ms_total_all=times, us_per_step=best * 1e3 / T,
+                tokens_per_s=B * T / (best * 1e-3), us_kernel_event=us_kernel,
+                bytes_per_step=per_step_bytes,
+                effective_GBs=per_step_bytes * T / (best * 1e-3) / 1e9,
+                kernel_GBs=per_step_bytes / (us_kernel * 1e-6) / 1e9)
+
+
+def cpu_baseline(cfg, target_s=12.0):
+    """fp64 oracle (C, OpenMP over heads) on a bounded sample of the prefill workload."""
+    import numpy as np
+    import oracle
+    import synthetic
+
+    oracle.build(force=False)
+    threads = len(os.sched_getaffinity(0))
+    Q, K, V = synthetic.prefill_inputs(cfg, 0)
+    Qf, Kf, Vf = (synthetic.as_f64(x, cfg["dtype"]) for x in (Q, K, V))
+    B, N = cfg["B"], cfg["N"]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.causal(Qf, Kf, Vf, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 1000:
+            break
+    return dict(value=B * N * reps / el, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{reps} full causal passes over the B={B} H={cfg['H']} N={N} D=M={cfg['D']} "
+                       f"fp32 workload ({el:.1f} s wall, fp64, {threads} threads)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="only the headline prefill workload")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              "sharding over several GPUs is not part of this benchmark", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synthetic
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = dict(synthetic.CONFIGS["cfg2"])
+    log(f"prefill {cfg}")
+    pre = bench_prefill(cfg, args.steps, args.warmup, dev)
+    log(f"prefill: {pre}")
+    kernel_us = pre["us_output"]
+    achieved = pre["bytes"] / (kernel_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel=f"seg_output_kernel<float,{cfg['D']},{cfg['M']},{pre['chunk']},causal>",
+                    kernel_us=round(kernel_us, 2), algorithmic_bytes=pre["bytes"],
+                    mfma_fp32_frac_at_min_flops=round(pre["flops_min"] / (kernel_us * 1e-6) / 1e12
+                                                      / FP32_MFMA_PEAK_TFS, 4))
+
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "causal linear attention prefill, fp32, B=8 H=8 N=1024 D=M=64, phi=elu+1",
+                   "B": cfg["B"], "H": cfg["H"], "N": cfg["N"], "D": cfg["D"], "M": cfg["M"],
+                   "chunk": pre["chunk"], "segments": pre["segments"], "buffer_sets": pre["nsets"],
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages_us": {"segment_states": round(pre["us_state"], 2), "segment_scan": round(pre["us_scan"], 2),
+                      "segment_outputs": round(pre["us_output"], 2)},
+    }
+
+    if not args.no_extras:
+        dcfg = dict(synthetic.CONFIGS["cfg5"])
+        log("decode ...")
+        dec = bench_decode(dcfg, 3, dev)
+        log(f"decode: {dec}")
+        line["decode"] = {
+            "workload": "recurrent decode, fp32, 256 streams x H=8, D=M=64, 4096 steps from zero state",
+            "tokens_per_s": round(dec["tokens_per_s"], 1), "us_per_step": round(dec["us_per_step"], 3),
+            "effective_GBs": round(dec["effective_GBs"], 1),
+            "frac_hbm_peak": round(dec["effective_GBs"] / HBM_PEAK_GBS, 4),
+            "kernel_us_event": round(dec["us_kernel_event"], 3),
+            "bytes_per_step": dec["bytes_per_step"],
+            "note": "the 34 MB state stays resident in the 256 MB last-level cache between steps"}
+        others = {}
+        for name in ("cfg3", "cfg4"):
+            c = dict(synthetic.CONFIGS[name])
+            log(f"prefill {name} ...")
+            r = bench_prefill(c, max(10, args.steps // 4), 5, dev)
+            log(f"{name}: {r}")
+            others[name] = {
+                "workload": f"causal prefill bf16 in, fp32 out, B={c['B']} H={c['H']} N={c['N']} D=M={c['D']}",
+                "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
+                "chunk": r["chunk"], "segments": r["segments"],
+                "step_GBs": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+                "frac_hbm_peak_step": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "stages_us": {"segment_states": round(r["us_state"], 2), "segment_scan": round(r["us_scan"], 2),
+                              "segment_outputs": round(r["us_output"], 2)}}
+        line["other_workloads"] = others
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(dict(synthetic.CONFIGS["cfg2"]))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,18 @@
+"""Causal kernelized linear attention ("Transformers are RNNs") on MI355X.
+
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI of
+liblinattn.so (include/linattn.h).  This package is the thin Python binding:
+argument marshalling only; PyTorch supplies device memory and streams.
+"""
+from .linattn import (  # noqa: F401
+    LinAttnError,
+    decode_step,
+    forward_chunked,
+    forward_plan,
+    lib_path,
+    segment_outputs,
+    segment_scan,
+    segment_states,
+    version,
+    workspace_bytes,
+)

@@ -1,0 +1,253 @@
+// C ABI of the linear-attention library: argument validation, planning, launch.
+// Declarations and the contract of every entry point are in include/linattn.h.
+#include <limits.h>
+
+#include "la_launch.hpp"
+#include "linattn.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool dim_ok(int64_t x) { return x == 16 || x == 32 || x == 64 || x == 128; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Plan {
+    int chunk = 0;
+    int segments = 0;
+    int chunks_per_segment = 0;
+    int nstates = 0;  // segment states the causal/non-causal path computes
+    size_t ws_bytes = 0;
+};
+
+// Validate the shape arguments shared by the prefill entry points.
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || M <= 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    // index arithmetic uses int for counts and size_t for element offsets
+    if (N > INT_MAX || B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
+    if (B > 0 && H > 0 && N > 0) {
+        const int64_t per_head = N * (D > M ? D : M);
+        if (per_head > INT64_MAX / (B * H)) return LA_ERR_UNSUPPORTED;
+    }
+    return LA_OK;
+}
+
+size_t state_ws_bytes(int64_t BH, int64_t D, int64_t M, int G) {
+    return (size_t)BH * (size_t)(G + 1) * (size_t)(D * M + D) * sizeof(float);
+}
+
+// The planner: chunk length, number of segments and workspace.
+int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype, int chunk_req,
+              Plan *plan) {
+    int st = check_shape(B, H, N, D, M, dtype);
+    if (st != LA_OK) return st;
+    if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
+    int C = 0;
+    if (chunk_req == 0) {
+        for (int c : {64, 32, 16}) {
+            if (la::prefill_supported(dtype, (int)D, (int)M, c)) {
+                C = c;
+                break;
+            }
+        }
+    } else if (chunk_req == 16 || chunk_req == 32 || chunk_req == 64) {
+        C = chunk_req;
+    } else {
+        return LA_ERR_UNSUPPORTED;
+    }
+    if (C == 0 || !la::prefill_supported(dtype, (int)D, (int)M, C)) return LA_ERR_UNSUPPORTED;
+    plan->chunk = C;
+    const int64_t BH = B * H;
+    if (BH == 0 || N == 0) {
+        plan->segments = 0;
+        plan->chunks_per_segment = 0;
+        plan->nstates = 0;
+        plan->ws_bytes = 0;
+        return LA_OK;
+    }
+    const int64_t n_chunks = (N + C - 1) / C;
+    // Enough workgroups to cover the 256 compute units a few times over; a
+    // segment's state costs (D*M + D) floats of traffic, so segments stay a few
+    // chunks long when the sequence allows.
+    const int64_t target_wg = 1024;
+    int64_t G = (target_wg + BH - 1) / BH;
+    const int64_t min_cps = 2;
+    if (G > (n_chunks + min_cps - 1) / min_cps) G = (n_chunks + min_cps - 1) / min_cps;
+    if (G < 1) G = 1;
+    const int64_t cps = (n_chunks + G - 1) / G;
+    G = (n_chunks + cps - 1) / cps;
+    plan->segments = (int)G;
+    plan->chunks_per_segment = (int)cps;
+    plan->nstates = causal ? (int)G - 1 : (int)G;
+    plan->ws_bytes = (causal && G == 1) ? 0 : state_ws_bytes(BH, D, M, (int)G);
+    return LA_OK;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+LA_API const char *la_status_str(int status) {
+    switch (status) {
+        case LA_OK: return "LA_OK";
+        case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG: invalid argument";
+        case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: unsupported shape, chunk or plan";
+        case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
+        case LA_ERR_HIP: return "LA_ERR_HIP: HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+LA_API int la_version(void) { return kVersion; }
+
+LA_API int la_forward_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                           int chunk_req, int *chunk_out, int *segments_out, size_t *workspace_bytes_out) {
+    Plan p;
+    const int st = make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p);
+    if (st != LA_OK) return st;
+    if (chunk_out) *chunk_out = p.chunk;
+    if (segments_out) *segments_out = p.segments;
+    if (workspace_bytes_out) *workspace_bytes_out = p.ws_bytes;
+    return LA_OK;
+}
+
+LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                                         int dtype, int chunk_req) {
+    Plan p;
+    return make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p) == LA_OK ? p.ws_bytes : 0;
+}
+
+LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                              int64_t N, int64_t D, int64_t M, int causal, int dtype, int chunk_req,
+                              void *workspace, size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+    Plan p;
+    int st = make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p);
+    if (st != LA_OK) return st;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+    const int64_t BH = B * H;
+    if (BH == 0) return LA_OK;
+    hipStream_t s = as_stream(stream);
+    if (N == 0) {
+        if (S_out == nullptr) return LA_OK;
+        hipError_t e = la::fill_zero(S_out, (size_t)(BH * D * M), s);
+        if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * D), s);
+        return hip_status(e);
+    }
+    if (!Q || !K || !V || !out) return LA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+    if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) return LA_ERR_WORKSPACE;
+    if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
+    float *ws = static_cast<float *>(workspace);
+    const int dt = dtype, Di = (int)D, Mi = (int)M, C = p.chunk, G = p.segments, cps = p.chunks_per_segment;
+    (void)hipGetLastError();  // clear a stale error so that the checks below report this call's launches
+    hipError_t e = hipSuccess;
+    if (p.nstates > 0) e = la::prefill_states(dt, Di, Mi, C, K, V, ws, (int)BH, (int)N, G, cps, p.nstates, s);
+    if (e == hipSuccess && p.ws_bytes > 0)
+        e = la::prefill_scan(ws, (int)BH, Di, Mi, G, p.nstates, causal ? nullptr : S_out, causal ? nullptr : z_out,
+                             s);
+    if (e == hipSuccess)
+        e = la::prefill_outputs(dt, Di, Mi, C, Q, K, V, out, ws, (int)BH, (int)N, G, cps, causal,
+                                causal ? S_out : nullptr, causal ? z_out : nullptr, s);
+    return hip_status(e);
+}
+
+// ---- stage entry points ----------------------------------------------------
+
+namespace {
+int check_stage(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments,
+                size_t ws_bytes, const void *ws) {
+    int st = check_shape(B, H, N, D, M, dtype);
+    if (st != LA_OK) return st;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return LA_ERR_UNSUPPORTED;
+    if (!la::prefill_supported(dtype, (int)D, (int)M, chunk)) return LA_ERR_UNSUPPORTED;
+    if (segments < 1) return LA_ERR_INVALID_ARG;
+    const int64_t n_chunks = (N + chunk - 1) / chunk;
+    if (N > 0) {
+        const int64_t cps = (n_chunks + segments - 1) / segments;
+        // every segment must own at least one chunk
+        if ((int64_t)(segments - 1) * cps >= n_chunks) return LA_ERR_UNSUPPORTED;
+    }
+    if ((int64_t)B * H * segments > INT_MAX / 256) return LA_ERR_UNSUPPORTED;
+    const size_t need = state_ws_bytes(B * H, D, M, segments);
+    if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return LA_ERR_INVALID_ARG;
+    return LA_OK;
+}
+int cps_of(int64_t N, int chunk, int segments) {
+    const int64_t n_chunks = (N + chunk - 1) / chunk;
+    return (int)((n_chunks + segments - 1) / segments);
+}
+}  // namespace
+
+LA_API int la_segment_states(const void *K, const void *V, float *ws, size_t ws_bytes, int64_t B, int64_t H,
+                             int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, int nstates,
+                             void *stream) {
+    int st = check_stage(B, H, N, D, M, dtype, chunk, segments, ws_bytes, ws);
+    if (st != LA_OK) return st;
+    if (nstates != segments && nstates != segments - 1) return LA_ERR_INVALID_ARG;
+    if (B * H == 0 || N == 0 || nstates == 0) return LA_OK;
+    if (!K || !V || !aligned16(K) || !aligned16(V)) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::prefill_states(dtype, (int)D, (int)M, chunk, K, V, ws, (int)(B * H), (int)N, segments,
+                                         cps_of(N, chunk, segments), nstates, as_stream(stream)));
+}
+
+LA_API int la_segment_scan(float *ws, size_t ws_bytes, int64_t B, int64_t H, int64_t D, int64_t M, int segments,
+                           int nstates, float *S_out, float *z_out, void *stream) {
+    if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (segments < 1) return LA_ERR_INVALID_ARG;
+    if (nstates != segments && nstates != segments - 1) return LA_ERR_INVALID_ARG;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+    if (B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
+    const size_t need = state_ws_bytes(B * H, D, M, segments);
+    if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
+    if (!aligned16(ws)) return LA_ERR_INVALID_ARG;
+    if (B * H == 0) return LA_OK;
+    (void)hipGetLastError();
+    return hip_status(la::prefill_scan(ws, (int)(B * H), (int)D, (int)M, segments, nstates, S_out, z_out,
+                                       as_stream(stream)));
+}
+
+LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, float *out, const float *ws,
+                              size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
+                              int dtype, int chunk, int segments, float *S_out, float *z_out, void *stream) {
+    int st = check_stage(B, H, N, D, M, dtype, chunk, segments, ws_bytes, ws);
+    if (st != LA_OK) return st;
+    if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+    if (B * H == 0 || N == 0) return LA_OK;
+    if (!Q || !out || !aligned16(Q) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+    if (causal && (!K || !V || !aligned16(K) || !aligned16(V))) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::prefill_outputs(dtype, (int)D, (int)M, chunk, Q, K, V, out, ws, (int)(B * H), (int)N,
+                                          segments, cps_of(N, chunk, segments), causal, causal ? S_out : nullptr,
+                                          causal ? z_out : nullptr, as_stream(stream)));
+}
+
+// ---- recurrent mode ---------------------------------------------------------
+
+LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, const void *v, float *out, int64_t B,
+                          int64_t H, int64_t D, int64_t M, int dtype, void *stream) {
+    if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (B * H == 0) return LA_OK;
+    if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
+    if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::decode_step(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device-side building blocks for the linear-attention kernels (gfx950 / CDNA4).
+//
+// MFMA operand layouts used throughout (64-lane wavefront, lane = 16*g + l16):
+//   v_mfma_f32_16x16x4_f32     A: lane holds A[l16][g]          B: B[g][l16]
+//   v_mfma_f32_16x16x16_bf16   A: lane holds A[l16][4g .. 4g+3] B: B[4g .. 4g+3][l16]
+//   v_mfma_f32_16x16x32_bf16   A: lane holds A[l16][8g .. 8g+7] B: B[8g .. 8g+7][l16]
+//   result (all three)         lane holds C[4g + r][l16], r = 0..3
+// The contraction index may be permuted freely as long as A and B use the same
+// permutation, which the tile routines exploit to avoid register transposes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+using bf16 = __bf16;
+
+// phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (page "Transformers are
+// RNNs", Main findings: elu-based feature map).  Branch free (a select).
+__device__ __forceinline__ float phi(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+
+template <typename T> __device__ __forceinline__ float to_f32(T x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// value after a round trip through T (identity for float)
+template <typename T> __device__ __forceinline__ float round_as(float x) { return to_f32<T>(from_f32<T>(x)); }
+
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
+
+// acc += A (16 x K) * B (K x 16) where, for lane (g, l16), row l16 of A starts at
+// `a` and column l16 of B starts at `b`; the K elements of each are contiguous.
+// T = bf16 uses 32-wide (or for K == 16, 16-wide) MFMA steps.
+template <int K>
+__device__ __forceinline__ f32x4 tile_dot_bf16(const bf16 *a, const bf16 *b, int g, f32x4 acc) {
+    static_assert(K % 16 == 0, "K must be a multiple of 16");
+    if constexpr (K % 32 == 0) {
+#pragma unroll
+        for (int ks = 0; ks < K / 32; ++ks) {
+            bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + ks * 32 + 8 * g);
+            bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + ks * 32 + 8 * g);
+            acc = mma_bf16_k32(av, bv, acc);
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < K / 16; ++ks) {
+            bf16x4 av = *reinterpret_cast<const bf16x4 *>(a + ks * 16 + 4 * g);
+            bf16x4 bv = *reinterpret_cast<const bf16x4 *>(b + ks * 16 + 4 * g);
+            acc = mma_bf16_k16(av, bv, acc);
+        }
+    }
+    return acc;
+}
+
+// fp32 variant with strided operands: for contraction index k = 4*ks + g the lane
+// reads A at a[k * a_ks] (a points at row l16 of A) and B at b[k * b_ks] (b points
+// at column l16 of B).
+template <int K>
+__device__ __forceinline__ f32x4 tile_dot_f32(const float *a, int a_ks, const float *b, int b_ks, int g,
+                                              f32x4 acc) {
+    static_assert(K % 4 == 0, "K must be a multiple of 4");
+#pragma unroll
+    for (int ks = 0; ks < K / 4; ++ks) {
+        const int k = 4 * ks + g;
+        acc = mma_f32(a[k * a_ks], b[k * b_ks], acc);
+    }
+    return acc;
+}
+
+// sum of x over the four lanes {l16, l16+16, l16+32, l16+48}
+__device__ __forceinline__ float sum_over_groups(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+}  // namespace la

@@ -1,0 +1,39 @@
+// Host-side launchers behind the C ABI (internal; not part of the public header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+// Prefill stage launchers for one element type (0 = fp32, 1 = bf16).
+// Each returns hipErrorInvalidValue for a (D, M, C) combination that has no kernel.
+bool prefill_supported(int dtype, int D, int M, int C);
+hipError_t prefill_states(int dtype, int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N,
+                          int G, int CPS, int nstates, hipStream_t stream);
+hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                           const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out, float *z_out,
+                           hipStream_t stream);
+hipError_t prefill_scan(float *ws, int BH, int D, int M, int G, int nstates, float *S_out, float *z_out,
+                        hipStream_t stream);
+hipError_t fill_zero(float *p, size_t n, hipStream_t stream);
+
+hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
+                       float *out, int BH, hipStream_t stream);
+
+// per element type (defined in la_prefill_f32.hip / la_prefill_bf16.hip)
+bool prefill_supported_f32(int D, int M, int C);
+bool prefill_supported_bf16(int D, int M, int C);
+hipError_t prefill_states_f32(int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N, int G,
+                              int CPS, int nstates, hipStream_t stream);
+hipError_t prefill_states_bf16(int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N, int G,
+                               int CPS, int nstates, hipStream_t stream);
+hipError_t prefill_outputs_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                               const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out,
+                               float *z_out, hipStream_t stream);
+hipError_t prefill_outputs_bf16(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                                const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out,
+                                float *z_out, hipStream_t stream);
+
+}  // namespace la

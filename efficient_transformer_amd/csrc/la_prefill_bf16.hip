@@ -1,0 +1,39 @@
+// Prefill kernels instantiated for bf16 inputs: D, M in {16, 32, 64, 128}, C in {16, 32, 64}.
+#include "la_launch.hpp"
+#include "la_prefill.hpp"
+
+namespace la {
+
+#define LA_FOR_C(D_, M_, X) X(D_, M_, 16) X(D_, M_, 32) X(D_, M_, 64)
+#define LA_FOR_M(D_, X) LA_FOR_C(D_, 16, X) LA_FOR_C(D_, 32, X) LA_FOR_C(D_, 64, X) LA_FOR_C(D_, 128, X)
+#define LA_FOR_ALL(X) LA_FOR_M(16, X) LA_FOR_M(32, X) LA_FOR_M(64, X) LA_FOR_M(128, X)
+
+bool prefill_supported_bf16(int D, int M, int C) {
+#define X(D_, M_, C_) \
+    if (D == D_ && M == M_ && C == C_) return Cfg<la::bf16, D_, M_, C_>::fits;
+    LA_FOR_ALL(X)
+#undef X
+    return false;
+}
+
+hipError_t prefill_states_bf16(int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N, int G,
+                              int CPS, int nstates, hipStream_t stream) {
+#define X(D_, M_, C_) \
+    if (D == D_ && M == M_ && C == C_) return run_states<la::bf16, D_, M_, C_>(K, V, ws, BH, N, G, CPS, nstates, stream);
+    LA_FOR_ALL(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t prefill_outputs_bf16(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                               const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out,
+                               float *z_out, hipStream_t stream) {
+#define X(D_, M_, C_) \
+    if (D == D_ && M == M_ && C == C_) \
+        return run_outputs<la::bf16, D_, M_, C_>(Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream);
+    LA_FOR_ALL(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

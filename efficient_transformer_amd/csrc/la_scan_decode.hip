@@ -1,0 +1,222 @@
+// Segment scan, zero fill, recurrent decode step, and the dtype dispatch of the
+// prefill stages.
+#include "la_device.hpp"
+#include "la_launch.hpp"
+
+namespace la {
+
+// ---------------------------------------------------------------------------
+// Exclusive prefix over the segment states of each head, in segment order,
+// plus the total in slot G (page "Transformers are RNNs", Proposed method:
+// cumulative sums).  One thread per state element; one-dimensional grid:
+// block b -> head b / nblk, element block b % nblk.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void seg_scan_kernel(float *__restrict__ ws, int E, int nblk, int G, int nstates,
+                                                       float *__restrict__ S_out, float *__restrict__ z_out, int DM) {
+    const int bh = blockIdx.x / nblk;
+    const int e = (blockIdx.x % nblk) * blockDim.x + threadIdx.x;
+    if (e >= E) return;
+    float *base = ws + (size_t)bh * (G + 1) * E + e;
+    float run = 0.0f;
+    for (int s = 0; s < nstates; ++s) {
+        const float x = base[(size_t)s * E];
+        base[(size_t)s * E] = run;
+        run += x;
+    }
+    for (int s = nstates; s < G; ++s) base[(size_t)s * E] = run;
+    base[(size_t)G * E] = run;
+    if (S_out != nullptr) {
+        if (e < DM)
+            S_out[(size_t)bh * DM + e] = run;
+        else
+            z_out[(size_t)bh * (E - DM) + (e - DM)] = run;
+    }
+}
+
+hipError_t prefill_scan(float *ws, int BH, int D, int M, int G, int nstates, float *S_out, float *z_out,
+                        hipStream_t stream) {
+    const int E = D * M + D;
+    const int nblk = (E + 255) / 256;
+    if (BH <= 0) return hipSuccess;
+    hipLaunchKernelGGL(seg_scan_kernel, dim3((unsigned)(nblk * BH)), dim3(256), 0, stream, ws, E, nblk, G, nstates,
+                       S_out, z_out, D * M);
+    return hipGetLastError();
+}
+
+// A fill kernel rather than hipMemsetAsync, so the call stays valid under graph capture.
+__global__ __launch_bounds__(256) void fill_zero_kernel(float *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0.0f;
+}
+
+hipError_t fill_zero(float *p, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+bool prefill_supported(int dtype, int D, int M, int C) {
+    return dtype == 0 ? prefill_supported_f32(D, M, C) : prefill_supported_bf16(D, M, C);
+}
+
+hipError_t prefill_states(int dtype, int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N,
+                          int G, int CPS, int nstates, hipStream_t stream) {
+    return dtype == 0 ? prefill_states_f32(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream)
+                      : prefill_states_bf16(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream);
+}
+
+hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                           const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out, float *z_out,
+                           hipStream_t stream) {
+    return dtype == 0 ? prefill_outputs_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
+                      : prefill_outputs_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Recurrent decode step (page "Transformers are RNNs", Proposed method: the
+// causal model is an RNN with memories S and z; Main findings: incremental
+// state updates).  One workgroup per head.  Thread layout: M/4 lanes span a
+// row of S with one float4 each; the workgroup covers RP rows per pass and
+// PASSES passes cover all D rows, so each thread keeps D*M/(4*threads) float4
+// of S in registers.  All loads of S are issued before any arithmetic, the
+// state is read once and written once.
+//   S += phi(k) v^T;  z += phi(k);  num = phi(q)^T S;  den = phi(q).z;  out = num/den
+// ---------------------------------------------------------------------------
+template <int D, int M>
+struct DecCfg {
+    static constexpr int NW = (D * M / 4096) > 1 ? D * M / 4096 : 1;  // wavefronts per head
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int LPR = M / 4;                                  // lanes per row
+    static constexpr int RP = THREADS / LPR;                           // rows per pass
+    static constexpr int PASSES = D / RP;
+    static_assert(PASSES * RP == D, "row split");
+};
+
+template <typename T>
+__device__ __forceinline__ f32x4 load4(const T *p);
+template <>
+__device__ __forceinline__ f32x4 load4<float>(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 load4<bf16>(const bf16 *p) {
+    bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+
+template <typename T, int D, int M>
+__global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *__restrict__ S, float *__restrict__ z,
+                                                                      const T *__restrict__ q,
+                                                                      const T *__restrict__ k,
+                                                                      const T *__restrict__ v,
+                                                                      float *__restrict__ out) {
+    using G = DecCfg<D, M>;
+    __shared__ float sq[D], sk[D];
+    __shared__ f32x4 sred[G::NW][G::LPR];
+    __shared__ float sden[G::NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const size_t bh = blockIdx.x;
+    const int col4 = tid % G::LPR, roff = tid / G::LPR;
+
+    f32x4 *Sh = reinterpret_cast<f32x4 *>(S + bh * D * M);
+    f32x4 Sv[G::PASSES];
+#pragma unroll
+    for (int p = 0; p < G::PASSES; ++p) Sv[p] = Sh[(roff + p * G::RP) * G::LPR + col4];
+    const f32x4 vv = load4<T>(v + bh * M + col4 * 4);
+    float zz[(D + G::THREADS - 1) / G::THREADS];
+#pragma unroll
+    for (int i = 0; i < (D + G::THREADS - 1) / G::THREADS; ++i) {
+        const int d = tid + i * G::THREADS;
+        if (d < D) {
+            zz[i] = z[bh * D + d];
+            sq[d] = phi(to_f32(q[bh * D + d]));
+            sk[d] = phi(to_f32(k[bh * D + d]));
+        }
+    }
+    __syncthreads();
+
+    // z += phi(k); partial den = phi(q) . z
+    float den = 0.0f;
+#pragma unroll
+    for (int i = 0; i < (D + G::THREADS - 1) / G::THREADS; ++i) {
+        const int d = tid + i * G::THREADS;
+        if (d < D) {
+            zz[i] += sk[d];
+            z[bh * D + d] = zz[i];
+            den += sq[d] * zz[i];
+        }
+    }
+
+    // S += phi(k) v^T; partial num = phi(q)^T S over this thread's rows
+    f32x4 num = zero4();
+#pragma unroll
+    for (int p = 0; p < G::PASSES; ++p) {
+        const int d = roff + p * G::RP;
+        const float fk = sk[d], fq = sq[d];
+        f32x4 s = Sv[p];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            s[j] += fk * vv[j];
+            num[j] += fq * s[j];
+        }
+        Sh[d * G::LPR + col4] = s;
+    }
+
+    // reduce num over the lanes of a wavefront that share col4, then over wavefronts
+#pragma unroll
+    for (int sh = G::LPR; sh < 64; sh <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) num[j] += __shfl_xor(num[j], sh, 64);
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) den += __shfl_xor(den, sh, 64);
+    if (G::NW > 1) {
+        if (lane < G::LPR) sred[w][lane] = num;
+        if (lane == 0) sden[w] = den;
+        __syncthreads();
+        if (w == 0 && lane < G::LPR) {
+            num = sred[0][lane];
+            den = sden[0];
+#pragma unroll
+            for (int ww = 1; ww < G::NW; ++ww) {
+                const f32x4 o = sred[ww][lane];
+                for (int j = 0; j < 4; ++j) num[j] += o[j];
+                den += sden[ww];
+            }
+        }
+    }
+    if (w == 0 && lane < G::LPR) {
+        const float inv = 1.0f / den;
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = num[j] * inv;
+        *reinterpret_cast<f32x4 *>(out + bh * M + lane * 4) = o;
+    }
+}
+
+template <typename T, int D, int M>
+hipError_t run_decode(float *S, float *z, const void *q, const void *k, const void *v, float *out, int BH,
+                      hipStream_t stream) {
+    if (BH <= 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<T, D, M>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream, S, z,
+                       (const T *)q, (const T *)k, (const T *)v, out);
+    return hipGetLastError();
+}
+
+hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
+                       float *out, int BH, hipStream_t stream) {
+#define X(D_, M_)                                                                        \
+    if (D == D_ && M == M_)                                                              \
+        return dtype == 0 ? run_decode<float, D_, M_>(S, z, q, k, v, out, BH, stream)    \
+                          : run_decode<bf16, D_, M_>(S, z, q, k, v, out, BH, stream);
+#define XM(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
+    XM(16) XM(32) XM(64) XM(128)
+#undef XM
+#undef X
+    return hipErrorInvalidValue;
+}
+
+}  // namespace la

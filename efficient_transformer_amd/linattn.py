@@ -1,0 +1,204 @@
+"""ctypes binding of liblinattn.so (include/linattn.h): marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; torch is used
+to hold device memory and to name the stream.  If the library has not been
+built, every call raises -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblinattn.so")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+LA_F32, LA_BF16 = 0, 1
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/linattn.h
+SIGNATURES = {
+    "la_status_str": (ctypes.c_char_p, [_int]),
+    "la_version": (_int, []),
+    "la_forward_plan": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _int,
+                               ctypes.POINTER(_int), ctypes.POINTER(_int), ctypes.POINTER(_sz)]),
+    "la_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int, _int, _int]),
+    "la_forward_chunked": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                  _vp, _sz, _vp, _vp, _vp]),
+    "la_segment_states": (_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
+    "la_segment_scan": (_int, [_vp, _sz, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
+    "la_segment_outputs": (_int, [_vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                  _int, _vp, _vp, _vp]),
+    "la_decode_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
+}
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)}")
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first (__graft_entry__.build() "
+                "or python -m efficient_transformer_amd.build_lib); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().la_status_str(status).decode()
+
+
+def version() -> int:
+    return int(lib().la_version())
+
+
+def _check(status: int, where: str) -> None:
+    if status != LA_OK:
+        raise LinAttnError(status, where)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return LA_F32
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, shape, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def forward_plan(B, H, N, D, M, causal=True, dtype=LA_F32, chunk=0):
+    """(chunk, segments, workspace_bytes) chosen by the library for this problem."""
+    c, g, w = _int(0), _int(0), _sz(0)
+    _check(lib().la_forward_plan(B, H, N, D, M, int(bool(causal)), dtype, chunk,
+                                 ctypes.byref(c), ctypes.byref(g), ctypes.byref(w)), "la_forward_plan")
+    return c.value, g.value, w.value
+
+
+def workspace_bytes(B, H, N, D, M, causal=True, dtype=LA_F32, chunk=0) -> int:
+    return forward_plan(B, H, N, D, M, causal, dtype, chunk)[2]
+
+
+def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_out=None, z_out=None,
+                    stream=None):
+    """Parallel-mode attention: Q, K [B,H,N,D], V [B,H,N,M] (float32 or bfloat16) -> out [B,H,N,M] float32.
+
+    With S_out [B,H,D,M] and z_out [B,H,D] (float32) the final state is written too.
+    """
+    import torch
+    if Q.dim() != 4:
+        raise ValueError("Q must be [B, H, N, D]")
+    B, H, N, D = Q.shape
+    M = V.shape[-1]
+    dev = Q.device
+    _require(Q, "Q", (B, H, N, D))
+    _require(K, "K", (B, H, N, D), Q.dtype, dev)
+    _require(V, "V", (B, H, N, M), Q.dtype, dev)
+    dt = _dtype_code(Q)
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
+    _require(out, "out", (B, H, N, M), torch.float32, dev)
+    if (S_out is None) != (z_out is None):
+        raise ValueError("give both S_out and z_out, or neither")
+    if S_out is not None:
+        _require(S_out, "S_out", (B, H, D, M), torch.float32, dev)
+        _require(z_out, "z_out", (B, H, D), torch.float32, dev)
+    need = workspace_bytes(B, H, N, D, M, causal, dt, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().la_forward_chunked(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, int(bool(causal)), dt,
+                                  chunk, _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
+    _check(st, "la_forward_chunked")
+    return out
+
+
+def segment_states(K, V, ws, chunk, segments, nstates, stream=None):
+    B, H, N, D = K.shape
+    M = V.shape[-1]
+    st = lib().la_segment_states(_ptr(K), _ptr(V), _ptr(ws), ws.numel() * ws.element_size(), B, H, N, D, M,
+                                 _dtype_code(K), chunk, segments, nstates, _stream(stream, K.device))
+    _check(st, "la_segment_states")
+
+
+def segment_scan(ws, B, H, D, M, segments, nstates, S_out=None, z_out=None, stream=None):
+    st = lib().la_segment_scan(_ptr(ws), ws.numel() * ws.element_size(), B, H, D, M, segments, nstates,
+                               _ptr(S_out), _ptr(z_out), _stream(stream, ws.device))
+    _check(st, "la_segment_scan")
+
+
+def segment_outputs(Q, K, V, out, ws, chunk, segments, causal=True, S_out=None, z_out=None, stream=None):
+    B, H, N, D = Q.shape
+    M = out.shape[-1]
+    st = lib().la_segment_outputs(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                  B, H, N, D, M, int(bool(causal)), _dtype_code(Q), chunk, segments,
+                                  _ptr(S_out), _ptr(z_out), _stream(stream, Q.device))
+    _check(st, "la_segment_outputs")
+
+
+def decode_step(S, z, q, k, v, out=None, stream=None):
+    """One recurrent step: S [B,H,D,M], z [B,H,D] (float32, updated in place); q, k [B,H,D]; v [B,H,M]."""
+    import torch
+    if S.dim() != 4:
+        raise ValueError("S must be [B, H, D, M]")
+    B, H, D, M = S.shape
+    dev = S.device
+    _require(S, "S", (B, H, D, M), torch.float32)
+    _require(z, "z", (B, H, D), torch.float32, dev)
+    _require(q, "q", (B, H, D), None, dev)
+    _require(k, "k", (B, H, D), q.dtype, dev)
+    _require(v, "v", (B, H, M), q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+    _require(out, "out", (B, H, M), torch.float32, dev)
+    st = lib().la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, D, M,
+                              _dtype_code(q), _stream(stream, dev))
+    _check(st, "la_decode_step")
+    return out

@@ -1,0 +1,158 @@
+/*
+ * linattn -- causal kernelized linear attention on AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Transformers are RNNs: Fast Autoregressive Transformers with Linear
+ * Attention" (Katharopoulos et al., 2020), page of that title:
+ *   - Proposed method: the softmax similarity is replaced by phi(q)^T phi(k);
+ *     associativity gives phi(Q) (phi(K)^T V) with the sum computed once;
+ *     causal masking is kept by the cumulative sums S_i, Z_i, updated step by
+ *     step; the causal model is an RNN with the two memories (S, z).
+ *   - Main findings: phi is elu based: phi(x) = elu(x) + 1, i.e. x + 1 for x > 0
+ *     and exp(x) otherwise.
+ *   With S_i = sum_{j<=i} phi(k_j) v_j^T (D x M) and z_i = sum_{j<=i} phi(k_j) (D):
+ *     out_i = phi(q_i)^T S_i / (phi(q_i)^T z_i)        (causal)
+ *     out_i = phi(q_i)^T S_{N-1} / (phi(q_i)^T z_{N-1}) (non-causal)
+ *   No 1/sqrt(D) scaling and no epsilon in the denominator (phi > 0 keeps it positive).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, row major, contiguous, in device memory owned by the
+ *     caller; the library never allocates, frees or keeps a pointer.
+ *     Q, K: [B][H][N][D]; V, out: [B][H][N][M]; S: [B][H][D][M]; z: [B][H][D].
+ *   - Input element type: LA_F32 (float) or LA_BF16 (bfloat16 bit patterns,
+ *     uint16).  Arithmetic and accumulation are fp32; out, S and z are fp32.
+ *   - D and M must each be 16, 32, 64 or 128.  All device pointers must be
+ *     16-byte aligned.  Outputs must not alias inputs.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting.  Concurrent calls that share a
+ *     workspace race; calls with separate workspaces are thread safe.
+ *   - Every call validates all arguments before it enqueues anything; on error
+ *     it returns a status below and writes nothing.  It never aborts and never
+ *     throws.  LA_ERR_HIP reports a launch failure from the HIP runtime.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define LA_API __attribute__((visibility("default")))
+#else
+#define LA_API
+#endif
+
+enum la_status {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misalignment, bad flag */
+    LA_ERR_UNSUPPORTED = 2, /* D, M, chunk or segment count outside the supported set */
+    LA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    LA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+};
+
+enum la_dtype { LA_F32 = 0, LA_BF16 = 1 };
+
+/* Human-readable name of a status code (static string; never NULL). */
+LA_API const char *la_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+LA_API int la_version(void);
+
+/*
+ * Execution plan of the parallel (prefill) mode.
+ *
+ * The sequence of each (b, h) is cut into chunks of `chunk` positions, and the
+ * chunks into `segments` contiguous groups of whole chunks.  Inside a chunk the
+ * masked quadratic term phi(Q_c) phi(K_c)^T V_c is formed directly; across
+ * chunks the running state (S, z) carries the sums (page "Transformers are
+ * RNNs", Proposed method: cumulative sums updated step by step, sum computed
+ * once and reused).  Segments are walked in parallel; an exclusive prefix over
+ * their summed states links them.
+ *
+ * chunk_req: 0 = automatic, else 16, 32 or 64.  On LA_OK writes the chosen chunk,
+ * the segment count and the workspace size (bytes) that la_forward_chunked
+ * needs.  Pure host computation; makes no HIP call.  Any output pointer may be NULL.
+ */
+LA_API int la_forward_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                           int causal, int dtype, int chunk_req,
+                           int *chunk_out, int *segments_out, size_t *workspace_bytes_out);
+
+/* Workspace bytes la_forward_chunked needs for these arguments (0 on invalid arguments). */
+LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                         int causal, int dtype, int chunk_req);
+
+/*
+ * Parallel-mode attention (prefill / training forward).
+ *
+ * causal = 1: out_i uses positions j <= i (diagonal included).
+ * causal = 0: every out_i uses all N positions.
+ * out: [B][H][N][M] fp32, fully written.
+ * workspace: device memory of at least la_forward_workspace_bytes(...) bytes,
+ *   no initial contents required, clobbered by the call.  May be NULL when that
+ *   size is 0.
+ * S_out [B][H][D][M], z_out [B][H][D]: optional (NULL to skip; both or neither);
+ *   receive the final state S_{N-1}, z_{N-1}, so that la_decode_step can
+ *   continue the sequence.
+ * N = 0 or B*H = 0 is a valid empty call (with N = 0 and S_out given, the state
+ * is written as zeros).
+ */
+LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float *out,
+                              int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                              int causal, int dtype, int chunk_req,
+                              void *workspace, size_t workspace_bytes,
+                              float *S_out, float *z_out, void *stream);
+
+/*
+ * The three stages la_forward_chunked runs, exposed with an explicit plan
+ * (chunk, segments), e.g. for a sequence sharded over devices: each device
+ * runs la_segment_states on its shard, the per-shard states are exchanged, and
+ * la_segment_outputs runs from the exchanged prefix.
+ *
+ * ws layout (fp32): [B*H][segments + 1][D*M + D]; slot s of a head holds a state
+ * (S row major [D][M], then z [D]).
+ *
+ * la_segment_states: slot s (s < nstates, nstates = segments or segments - 1)
+ *   := sum over the positions of segment s of phi(k_j) v_j^T and phi(k_j).
+ * la_segment_scan: turns slots 0..segments-1 into exclusive prefixes (slot s :=
+ *   sum of the states of segments < s, in segment order) and writes the sum of
+ *   all nstates states to slot `segments`; writes it to S_out/z_out if given
+ *   (only meaningful when nstates == segments).
+ * la_segment_outputs: out rows of segment s from slot s (causal) or from slot
+ *   `segments` (non-causal); with causal = 1 and S_out/z_out given, the last
+ *   segment also writes the final state.
+ * ws_bytes must be at least (B*H) * (segments+1) * (D*M+D) * 4.
+ */
+LA_API int la_segment_states(const void *K, const void *V, float *ws, size_t ws_bytes,
+                             int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                             int dtype, int chunk, int segments, int nstates, void *stream);
+LA_API int la_segment_scan(float *ws, size_t ws_bytes, int64_t B, int64_t H, int64_t D, int64_t M,
+                           int segments, int nstates, float *S_out, float *z_out, void *stream);
+LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, float *out,
+                              const float *ws, size_t ws_bytes,
+                              int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                              int causal, int dtype, int chunk, int segments,
+                              float *S_out, float *z_out, void *stream);
+
+/*
+ * One recurrent (autoregressive) step for B*H independent heads (page
+ * "Transformers are RNNs", Proposed method: the causal model as an RNN with
+ * memories (S, z); Main findings: the state is updated incrementally).
+ *   S += phi(k) v^T;  z += phi(k);  out = phi(q)^T S / (phi(q)^T z)
+ * The token enters the state before the read-out, matching the causal mode's
+ * j <= i.  S [B][H][D][M] and z [B][H][D] (fp32) are read and rewritten in place
+ * (start from zeros for an empty history).  q, k: [B][H][D]; v: [B][H][M];
+ * out: [B][H][M] fp32.  The state is the whole history: copying S and z out and
+ * back resumes a sequence exactly.
+ */
+LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, const void *v,
+                          float *out, int64_t B, int64_t H, int64_t D, int64_t M,
+                          int dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

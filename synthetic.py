@@ -28,8 +28,9 @@ _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
 _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
-# tensor ids of a prefill call; a decode step t uses 3*t + {0, 1, 2}
+# tensor ids: prefill Q, K, V; decode q, k, v over all steps ([T, B, H, width])
 TID_Q, TID_K, TID_V = 0, 1, 2
+TID_DQ, TID_DK, TID_DV = 3, 4, 5
 
 
 def splitmix64(x: np.ndarray) -> np.ndarray:
@@ -148,17 +149,73 @@ def prefill_head_rows(cfg: dict, seed: int, tensor_id: int, bh: int, n0: int, n1
     return draw(seed, tensor_id, (n1 - n0, width), cfg["sigma"], cfg["dtype"], start=start)
 
 
+def decode_inputs(cfg: dict, seed: int, t0: int, t1: int):
+    """q, k ([t1-t0, B, H, D]) and v ([t1-t0, B, H, M]) for decode steps t0..t1-1."""
+    B, H, D, M = cfg["B"], cfg["H"], cfg["D"], cfg["M"]
+    s, dt = cfg["sigma"], cfg["dtype"]
+    T = t1 - t0
+    q = draw(seed, TID_DQ, (T, B, H, D), s, dt, start=t0 * B * H * D)
+    k = draw(seed, TID_DK, (T, B, H, D), s, dt, start=t0 * B * H * D)
+    v = draw(seed, TID_DV, (T, B, H, M), s, dt, start=t0 * B * H * M)
+    return q, k, v
+
+
 def decode_step_inputs(cfg: dict, seed: int, step: int, heads=None):
-    """q, k ([B,H,D]) and v ([B,H,M]) for decode step `step` (optionally only some flat heads)."""
+    """q, k ([B,H,D]) and v ([B,H,M]) for decode step `step` (or [len(heads), width] for some flat heads)."""
     B, H, D, M = cfg["B"], cfg["H"], cfg["D"], cfg["M"]
     s, dt = cfg["sigma"], cfg["dtype"]
     if heads is None:
-        q = draw(seed, 3 * step + 0, (B, H, D), s, dt)
-        k = draw(seed, 3 * step + 1, (B, H, D), s, dt)
-        v = draw(seed, 3 * step + 2, (B, H, M), s, dt)
-        return q, k, v
+        q, k, v = decode_inputs(cfg, seed, step, step + 1)
+        return q[0], k[0], v[0]
     heads = list(heads)
-    q = np.stack([draw(seed, 3 * step + 0, (D,), s, dt, start=h * D) for h in heads])
-    k = np.stack([draw(seed, 3 * step + 1, (D,), s, dt, start=h * D) for h in heads])
-    v = np.stack([draw(seed, 3 * step + 2, (M,), s, dt, start=h * M) for h in heads])
+    BH = B * H
+    q = np.stack([draw(seed, TID_DQ, (D,), s, dt, start=(step * BH + h) * D) for h in heads])
+    k = np.stack([draw(seed, TID_DK, (D,), s, dt, start=(step * BH + h) * D) for h in heads])
+    v = np.stack([draw(seed, TID_DV, (M,), s, dt, start=(step * BH + h) * M) for h in heads])
     return q, k, v
+
+
+def draw_torch(seed: int, tensor_id: int, shape, sigma: float = 1.0, dtype: str = "f32", device="cuda:0",
+               start: int = 0, chunk: int = 1 << 26):
+    """The same generator in torch int64/float64 arithmetic on `device` (for large benchmark inputs).
+
+    Integer steps are exact (two's-complement wraparound equals arithmetic modulo
+    2**64); the float64 log/cos may differ from numpy's in the last place, so an
+    occasional float32 value can differ by one ulp from draw().  Parity tests use
+    draw(); this variant only feeds timing runs.
+    """
+    import torch
+
+    def c64(x: int) -> int:  # uint64 constant as the int64 with the same bits
+        return x - (1 << 64) if x >= (1 << 63) else x
+
+    def lsr(x, s: int):
+        return (x >> s) & ((1 << (64 - s)) - 1)
+
+    def mix(x):
+        z = x + c64(0x9E3779B97F4A7C15)
+        z = (z ^ lsr(z, 30)) * c64(0xBF58476D1CE4E5B9)
+        z = (z ^ lsr(z, 27)) * c64(0x94D049BB133111EB)
+        return z ^ lsr(z, 31)
+
+    base = int(_base(seed, tensor_id))
+    base = c64(base)
+    n = 1
+    for s_ in shape:
+        n *= int(s_)
+    out = torch.empty(n, dtype=torch.float32, device=device)
+    for lo in range(0, n, chunk):
+        hi = min(n, lo + chunk)
+        idx = torch.arange(start + lo, start + hi, dtype=torch.int64, device=device)
+        ra = mix(base ^ (2 * idx))
+        rb = mix(base ^ (2 * idx + 1))
+        ua = lsr(ra, 11).to(torch.float64) * 2.0 ** -53
+        ub = lsr(rb, 11).to(torch.float64) * 2.0 ** -53
+        g = torch.sqrt(-2.0 * torch.log1p(-ua)) * torch.cos(2.0 * torch.pi * ub)
+        out[lo:hi] = (sigma * g).to(torch.float32)
+    out = out.view(*shape)
+    if dtype == "f32":
+        return out
+    if dtype == "bf16":
+        return out.to(torch.bfloat16)  # round to nearest even
+    raise ValueError(dtype)

@@ -1,0 +1,157 @@
+"""The C-ABI library on the CPU: it loads, exports what include/linattn.h declares,
+plans as documented, and rejects bad arguments before touching the GPU.
+
+Only calls that the library answers from its argument checks are made here (they
+return before any HIP runtime call), so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from efficient_transformer_amd import build_lib, linattn
+    if not os.path.exists(linattn.LIB_PATH):
+        build_lib.build(force=True)
+    return linattn
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"LA_API\s+[\w\s\*]+?\b(la_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("la_forward_chunked", "la_decode_step", "la_forward_workspace_bytes", "la_forward_plan",
+              "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(la_\w+)", out))
+    assert set(declared_symbols()) == exported, "exports differ from the header"
+    assert set(L.SIGNATURES) == set(declared_symbols()), "binding signatures differ from the header"
+
+
+def test_status_strings(L):
+    for code in range(5):
+        assert L.status_str(code).startswith(["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED",
+                                              "LA_ERR_WORKSPACE", "LA_ERR_HIP"][code])
+    assert L.status_str(99) == "unknown status"
+    assert L.version() >= 100
+
+
+@pytest.mark.parametrize("B,H,N,D,M,causal,dtype,chunk", [
+    (1, 1, 64, 16, 16, 1, 0, 16), (8, 8, 1024, 64, 64, 1, 0, 0), (4, 8, 3072, 64, 64, 1, 1, 0),
+    (1, 16, 65536, 128, 128, 1, 1, 0), (2, 3, 257, 32, 128, 0, 0, 32), (1, 1, 1, 128, 16, 1, 1, 64),
+    (3, 1, 100, 16, 64, 1, 0, 0), (1, 2, 5000, 128, 128, 1, 0, 0)])
+def test_plan_covers_the_sequence(L, B, H, N, D, M, causal, dtype, chunk):
+    C, G, ws = L.forward_plan(B, H, N, D, M, causal, dtype, chunk)
+    if chunk:
+        assert C == chunk
+    assert C in (16, 32, 64)
+    n_chunks = -(-N // C)
+    cps = -(-n_chunks // G)
+    assert 1 <= G <= n_chunks
+    assert (G - 1) * cps < n_chunks <= G * cps  # every segment owns at least one chunk
+    E = D * M + D
+    if causal and G == 1:
+        assert ws == 0
+    else:
+        assert ws == B * H * (G + 1) * E * 4
+    assert L.workspace_bytes(B, H, N, D, M, causal, dtype, chunk) == ws
+
+
+def test_plan_fp32_large_state_uses_smaller_chunk(L):
+    # fp32 operands at D = M = 128 do not fit a 64-position chunk in LDS
+    C, _, _ = L.forward_plan(1, 1, 4096, 128, 128, 1, 0, 0)
+    assert C == 32
+    with pytest.raises(L.LinAttnError) as e:
+        L.forward_plan(1, 1, 4096, 128, 128, 1, 0, 64)
+    assert e.value.status == L.LA_ERR_UNSUPPORTED
+
+
+def _fwd(L, Q=None, K=None, V=None, out=None, B=1, H=1, N=64, D=16, M=16, causal=1, dtype=0, chunk=0,
+         ws=None, ws_bytes=0, S=None, z=None):
+    return L.lib().la_forward_chunked(Q, K, V, out, B, H, N, D, M, causal, dtype, chunk, ws, ws_bytes, S, z, None)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=48), 2), (dict(M=8), 2), (dict(D=256), 2), (dict(dtype=2), 1), (dict(causal=2), 1),
+    (dict(chunk=128), 2), (dict(chunk=8), 2), (dict(N=-1), 1), (dict(B=-1), 1), (dict(H=-3), 1),
+    (dict(Q=None), 1), (dict(out=None), 1), (dict(V=FAKE + 4), 1), (dict(S=FAKE), 1),
+])
+def test_forward_rejects_bad_arguments(L, kw, status):
+    args = dict(Q=FAKE, K=FAKE, V=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    assert _fwd(L, **args) == status
+
+
+def test_forward_workspace_checks(L):
+    need = L.workspace_bytes(1, 1, 4096, 64, 64, 1, 0, 0)
+    assert need > 0
+    assert _fwd(L, Q=FAKE, K=FAKE, V=FAKE, out=FAKE, N=4096, D=64, M=64, ws=None, ws_bytes=0) == L.LA_ERR_WORKSPACE
+    assert _fwd(L, Q=FAKE, K=FAKE, V=FAKE, out=FAKE, N=4096, D=64, M=64, ws=FAKE,
+                ws_bytes=need - 1) == L.LA_ERR_WORKSPACE
+    assert _fwd(L, Q=FAKE, K=FAKE, V=FAKE, out=FAKE, N=4096, D=64, M=64, ws=FAKE + 8,
+                ws_bytes=need) == L.LA_ERR_INVALID_ARG
+
+
+def test_empty_batch_is_a_no_op(L):
+    # B*H == 0 returns before any pointer or HIP use
+    assert _fwd(L, B=0, H=4, N=64) == L.LA_OK
+    assert L.lib().la_decode_step(None, None, None, None, None, None, 0, 8, 64, 64, 0, None) == L.LA_OK
+
+
+def test_decode_rejects_bad_arguments(L):
+    f = L.lib().la_decode_step
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 48, 64, 0, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 3, None) == L.LA_ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 2, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
+
+
+def test_stage_entry_points_check_plans(L):
+    lib = L.lib()
+    # segments must each own a chunk: 4 chunks cannot make 5 non-empty segments
+    assert lib.la_segment_states(FAKE, FAKE, FAKE, 1 << 30, 2, 1, 256, 64, 64, 0, 64, 5, 5,
+                                 None) == L.LA_ERR_UNSUPPORTED
+    assert lib.la_segment_states(FAKE, FAKE, FAKE, 16, 2, 1, 256, 64, 64, 0, 64, 2, 2, None) == L.LA_ERR_WORKSPACE
+    assert lib.la_segment_states(FAKE, FAKE, FAKE, 1 << 30, 2, 1, 256, 64, 64, 0, 64, 2, 0,
+                                 None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_segment_scan(FAKE, 16, 2, 1, 64, 64, 2, 1, None, None, None) == L.LA_ERR_WORKSPACE
+    assert lib.la_segment_scan(FAKE, 1 << 30, 2, 1, 64, 64, 2, 1, FAKE, None, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_segment_outputs(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 1, 256, 64, 64, 3, 0, 64, 2,
+                                  None, None, None) == L.LA_ERR_INVALID_ARG
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "efficient_transformer_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text and "liboracle" not in text, f
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    code = ("import efficient_transformer_amd.linattn as L; L.LIB_PATH = '/nonexistent/liblinattn.so'; L._lib = None\n"
+            "try:\n    L.version()\nexcept RuntimeError as e:\n    print('raised', 'no fallback' in str(e))\n")
+    r = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert "raised True" in r.stdout, r.stdout + r.stderr

@@ -1,0 +1,215 @@
+"""Parity of the HIP prefill path (la_forward_chunked and its stages) with the fp64 oracle.
+
+Every case draws seeded inputs, runs the C ABI on cuda:0 and compares element by
+element with the oracle at the tolerance of the input type (fp32 1e-4, bf16 2e-2,
+row-wise relative; see gpu_helpers).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_helpers import TOL, rowwise_rel, to_dev, whole_rel
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import efficient_transformer_amd as ea
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return ea
+
+
+def run_prefill(ea, cfg, seed, causal=True, chunk=None, with_state=False):
+    Q, K, V = synthetic.prefill_inputs(cfg, seed)
+    dt = cfg["dtype"]
+    Qd, Kd, Vd = to_dev(Q, dt), to_dev(K, dt), to_dev(V, dt)
+    S = z = None
+    if with_state:
+        B, H, D, M = cfg["B"], cfg["H"], cfg["D"], cfg["M"]
+        S = torch.full((B, H, D, M), float("nan"), device=DEV)
+        z = torch.full((B, H, D), float("nan"), device=DEV)
+    out = ea.forward_chunked(Qd, Kd, Vd, causal=causal, chunk=cfg.get("chunk", 0) if chunk is None else chunk,
+                             S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    if with_state:
+        return (Q, K, V), res, S.cpu().numpy(), z.cpu().numpy()
+    return (Q, K, V), res
+
+
+def f64(x, dt):
+    return synthetic.as_f64(x, dt)
+
+
+def small_cfg(dtype, B, H, N, D, M, sigma=1.0):
+    return dict(kind="prefill", B=B, H=H, N=N, D=D, M=M, sigma=sigma, dtype=dtype, chunk=0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_cfg1_parity(ea, seed):
+    cfg = synthetic.CONFIGS["cfg1"]
+    (Q, K, V), out = run_prefill(ea, cfg, seed)
+    ref, _, _ = oracle.causal(f64(Q, "f32"), f64(K, "f32"), f64(V, "f32"))
+    assert rowwise_rel(out, ref) <= TOL["f32"]
+
+
+SHAPES = [(16, 16), (32, 64), (64, 32), (64, 64), (128, 128), (16, 128), (128, 16)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,M", SHAPES)
+@pytest.mark.parametrize("N", [1, 33, 300])
+@pytest.mark.parametrize("chunk", [0, 16, 32, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_small_parity(ea, dtype, D, M, N, chunk, causal):
+    if chunk and not ea.linattn.lib().la_forward_plan(1, 1, max(N, 1), D, M, int(causal),
+                                                      0 if dtype == "f32" else 1, chunk, None, None, None) == 0:
+        pytest.skip("chunk does not fit LDS for this shape")
+    cfg = small_cfg(dtype, 2, 3, N, D, M)
+    (Q, K, V), out = run_prefill(ea, cfg, seed=N + D + M, causal=causal, chunk=chunk)
+    Qf, Kf, Vf = f64(Q, dtype), f64(K, dtype), f64(V, dtype)
+    ref = oracle.causal(Qf, Kf, Vf)[0] if causal else oracle.noncausal(Qf, Kf, Vf)
+    err = rowwise_rel(out, ref)
+    assert err <= TOL[dtype], f"row-wise rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N", [1, 100, 1000])
+def test_final_state(ea, dtype, causal, N):
+    cfg = small_cfg(dtype, 2, 2, N, 64, 32)
+    (Q, K, V), out, S, z = run_prefill(ea, cfg, seed=7, causal=causal, with_state=True)
+    _, S_ref, z_ref = oracle.causal(f64(Q, dtype), f64(K, dtype), f64(V, dtype))
+    tol = 1e-5 if dtype == "f32" else 1e-5  # state sums are fp32 on both input types
+    assert whole_rel(S, S_ref) <= tol
+    assert whole_rel(z, z_ref) <= tol
+
+
+def test_empty_sequence_writes_zero_state(ea):
+    Q = torch.empty((2, 3, 0, 16), device=DEV)
+    V = torch.empty((2, 3, 0, 32), device=DEV)
+    S = torch.full((2, 3, 16, 32), 5.0, device=DEV)
+    z = torch.full((2, 3, 16), 5.0, device=DEV)
+    out = ea.forward_chunked(Q, Q, V, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 3, 0, 32)
+    assert torch.count_nonzero(S).item() == 0 and torch.count_nonzero(z).item() == 0
+
+
+def test_cfg2_full(ea):
+    cfg = synthetic.CONFIGS["cfg2"]
+    (Q, K, V), out = run_prefill(ea, cfg, 0)
+    ref, _, _ = oracle.causal(f64(Q, "f32"), f64(K, "f32"), f64(V, "f32"))
+    err = rowwise_rel(out, ref)
+    print(f"cfg2 row-wise rel err {err:.3e}")
+    assert err <= TOL["f32"]
+
+
+def test_cfg3_full(ea):
+    cfg = synthetic.CONFIGS["cfg3"]
+    (Q, K, V), out = run_prefill(ea, cfg, 0)
+    ref, _, _ = oracle.causal(f64(Q, "bf16"), f64(K, "bf16"), f64(V, "bf16"))
+    err = rowwise_rel(out, ref)
+    print(f"cfg3 row-wise rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
+def test_cfg4_sampled(ea):
+    """Full-size long-sequence run; two whole heads by the recurrence, sampled rows of the rest."""
+    cfg = synthetic.CONFIGS["cfg4"]
+    (Q, K, V), out = run_prefill(ea, cfg, 0)
+    Q, K, V = Q[0], K[0], V[0]
+    out = out[0]
+    heads = [0, 15]
+    ref, _, _ = oracle.causal(f64(Q[heads], "bf16"), f64(K[heads], "bf16"), f64(V[heads], "bf16"))
+    for i, h in enumerate(heads):
+        err = rowwise_rel(out[h], ref[i])
+        print(f"cfg4 head {h} row-wise rel err {err:.3e}")
+        assert err <= TOL["bf16"]
+    rng = np.random.default_rng(0)
+    N = cfg["N"]
+    for h in range(1, 15):
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, N - 1], rng.integers(0, N, 4)]))
+        n = rows.max() + 1
+        ref = oracle.causal_rows(f64(Q[h, :n], "bf16"), f64(K[h, :n], "bf16"), f64(V[h, :n], "bf16"), rows)
+        err = rowwise_rel(out[h, rows], ref)
+        assert err <= TOL["bf16"], f"head {h}: {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ones_invariant(ea, dtype):
+    cfg = small_cfg(dtype, 2, 2, 700, 64, 64)
+    Q, K, _ = synthetic.prefill_inputs(cfg, 3)
+    ones = np.ones((2, 2, 700, 64), np.float32)
+    Vd = to_dev(ones if dtype == "f32" else synthetic.f32_to_bf16_bits(ones), dtype)
+    out = ea.forward_chunked(to_dev(Q, dtype), to_dev(K, dtype), Vd)
+    torch.cuda.synchronize()
+    err = np.abs(out.cpu().numpy() - 1.0).max()
+    assert err <= (1e-5 if dtype == "f32" else 1e-2), err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_first_row_and_last_row(ea, dtype):
+    cfg = small_cfg(dtype, 1, 4, 333, 32, 64)
+    Q, K, V = synthetic.prefill_inputs(cfg, 4)
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    c = ea.forward_chunked(Qd, Kd, Vd, causal=True).cpu().numpy()
+    nc = ea.forward_chunked(Qd, Kd, Vd, causal=False).cpu().numpy()
+    v0 = f64(V, dtype)[:, :, 0]
+    assert rowwise_rel(c[:, :, 0], v0) <= 1e-6
+    assert rowwise_rel(c[:, :, -1], nc[:, :, -1]) <= TOL[dtype]
+
+
+def test_bitwise_repeatable(ea):
+    cfg = synthetic.CONFIGS["cfg3"]
+    Q, K, V = synthetic.prefill_inputs(cfg, 1)
+    Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
+    a = ea.forward_chunked(Qd, Kd, Vd)
+    b = ea.forward_chunked(Qd, Kd, Vd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stages_equal_forward(ea, dtype):
+    from efficient_transformer_amd import linattn as L
+    cfg = small_cfg(dtype, 2, 2, 1000, 64, 64)
+    Q, K, V = synthetic.prefill_inputs(cfg, 5)
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    code = L.LA_F32 if dtype == "f32" else L.LA_BF16
+    C, G, wsb = ea.forward_plan(2, 2, 1000, 64, 64, True, code, 0)
+    ref = ea.forward_chunked(Qd, Kd, Vd)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(ref)
+    ea.segment_states(Kd, Vd, ws, C, G, G - 1)
+    ea.segment_scan(ws, 2, 2, 64, 64, G, G - 1)
+    ea.segment_outputs(Qd, Kd, Vd, out, ws, C, G)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("segments", [1, 2, 3, 7, 16])
+def test_segment_counts(ea, segments):
+    """Any split of the chunks into segments gives the oracle's result."""
+    dtype = "f32"
+    cfg = small_cfg(dtype, 1, 3, 1000, 32, 32)
+    Q, K, V = synthetic.prefill_inputs(cfg, 6)
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    C = 64
+    E = 32 * 32 + 32
+    ws = torch.empty(3 * (segments + 1) * E * 4, dtype=torch.uint8, device=DEV)
+    out = torch.empty((1, 3, 1000, 32), device=DEV)
+    S = torch.empty((1, 3, 32, 32), device=DEV)
+    z = torch.empty((1, 3, 32), device=DEV)
+    ea.segment_states(Kd, Vd, ws, C, segments, segments)
+    ea.segment_scan(ws, 1, 3, 32, 32, segments, segments)
+    ea.segment_outputs(Qd, Kd, Vd, out, ws, C, segments, causal=True, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    ref, S_ref, z_ref = oracle.causal(f64(Q, dtype), f64(K, dtype), f64(V, dtype))
+    assert rowwise_rel(out.cpu().numpy(), ref) <= TOL[dtype]
+    assert whole_rel(S.cpu().numpy(), S_ref) <= 1e-5

@@ -54,3 +54,13 @@ def test_prefill_head_rows_match_full_draw():
     Q, K, V = synthetic.prefill_inputs(cfg, seed=2)
     rows = synthetic.prefill_head_rows(cfg, 2, synthetic.TID_V, bh=1, n0=10, n1=20, width=cfg["M"])
     assert np.array_equal(rows, V[0, 1, 10:20])
+
+
+def test_torch_generator_matches_numpy_on_cpu():
+    a = synthetic.draw(5, 4, (3, 1000), sigma=0.5)
+    b = synthetic.draw_torch(5, 4, (3, 1000), sigma=0.5, device="cpu").numpy()
+    assert np.mean(a == b) > 0.999
+    assert np.max(np.abs(a - b)) <= 1e-6
+    a16 = synthetic.draw(5, 4, (2000,), dtype="bf16", start=77)
+    b16 = synthetic.draw_torch(5, 4, (2000,), dtype="bf16", device="cpu", start=77).view(torch.int16).numpy()
+    assert np.mean(a16 == b16.view(np.uint16)) > 0.999
