@@ -2,11 +2,16 @@
 //
 // MFMA operand layouts used throughout (64-lane wavefront, lane = 16*g + l16):
 //   v_mfma_f32_16x16x4_f32     A: lane holds A[l16][g]          B: B[g][l16]
-//   v_mfma_f32_16x16x16_bf16   A: lane holds A[l16][4g .. 4g+3] B: B[4g .. 4g+3][l16]
 //   v_mfma_f32_16x16x32_bf16   A: lane holds A[l16][8g .. 8g+7] B: B[8g .. 8g+7][l16]
-//   result (all three)         lane holds C[4g + r][l16], r = 0..3
+//   result (both)              lane holds C[4g + r][l16], r = 0..3
 // The contraction index may be permuted freely as long as A and B use the same
 // permutation, which the tile routines exploit to avoid register transposes.
+//
+// Only one MFMA shape per element type is used.  A 16-deep bf16 contraction is
+// done as a 32-deep one with the upper half of every lane's slots zero: chaining
+// v_mfma_f32_16x16x16_bf16 and v_mfma_f32_16x16x32_bf16 on one accumulator, with
+// no wait states between them in the generated code, gave wrong values in half
+// of the result rows on gfx950.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,7 +22,6 @@ namespace la {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 using bf16 = __bf16;
 
 // phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (page "Transformers are
@@ -42,16 +46,19 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
 __device__ __forceinline__ f32x4 mma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// a 16-deep contraction on the 32-deep instruction: slots 4..7 of every lane are zero
 __device__ __forceinline__ f32x4 mma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+    const bf16 zero = (bf16)0.0f;
+    bf16x8 a8 = {a[0], a[1], a[2], a[3], zero, zero, zero, zero};
+    bf16x8 b8 = {b[0], b[1], b[2], b[3], zero, zero, zero, zero};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
 // acc += A (16 x K) * B (K x 16) where, for lane (g, l16), row l16 of A starts at
 // `a` and column l16 of B starts at `b`; the K elements of each are contiguous.
-// T = bf16 uses 32-wide (or for K == 16, 16-wide) MFMA steps.
+// 32-deep MFMA steps (K == 16 runs as one zero-padded step).
 template <int K>
 __device__ __forceinline__ f32x4 tile_dot_bf16(const bf16 *a, const bf16 *b, int g, f32x4 acc) {
     static_assert(K % 16 == 0, "K must be a multiple of 16");
