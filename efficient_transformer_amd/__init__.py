@@ -8,11 +8,14 @@ from .linattn import (  # noqa: F401
     LinAttnError,
     decode_step,
     forward_chunked,
+    forward_fused,
     forward_plan,
+    fused_workspace_bytes,
     lib_path,
     segment_outputs,
     segment_scan,
     segment_states,
     version,
     workspace_bytes,
+    workspace_init,
 )

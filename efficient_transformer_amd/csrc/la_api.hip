@@ -68,20 +68,28 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
         return LA_OK;
     }
     const int64_t n_chunks = (N + C - 1) / C;
-    // Enough workgroups to cover the 256 compute units a few times over; a
-    // segment's state costs (D*M + D) floats of traffic, so segments stay a few
-    // chunks long when the sequence allows.
+    // Causal: one workgroup per segment, fused kernel with a look-back across
+    // segments.  Segments are as short as possible (one chunk: phase B reuses the
+    // chunk phase A staged) while the grid stays within a few waves of the 256
+    // compute units; longer sequences get several chunks per segment.
+    // Non-causal: the three stage kernels, with segments sized the same way.
     const int64_t target_wg = 1024;
-    int64_t G = (target_wg + BH - 1) / BH;
-    const int64_t min_cps = 2;
-    if (G > (n_chunks + min_cps - 1) / min_cps) G = (n_chunks + min_cps - 1) / min_cps;
-    if (G < 1) G = 1;
-    const int64_t cps = (n_chunks + G - 1) / G;
+    int64_t cps = (n_chunks * BH + target_wg - 1) / target_wg;
+    if (cps < 1) cps = 1;
+    int64_t G = (n_chunks + cps - 1) / cps;
+    cps = (n_chunks + G - 1) / G;
     G = (n_chunks + cps - 1) / cps;
+    if (BH * G > INT_MAX / 256) return LA_ERR_UNSUPPORTED;
     plan->segments = (int)G;
     plan->chunks_per_segment = (int)cps;
-    plan->nstates = causal ? (int)G - 1 : (int)G;
-    plan->ws_bytes = (causal && G == 1) ? 0 : state_ws_bytes(BH, D, M, (int)G);
+    const int E = (int)(D * M + D);
+    if (causal) {
+        plan->nstates = 0;
+        plan->ws_bytes = G == 1 ? 0 : la::fused_ws_bytes(BH, (int)G, E);
+    } else {
+        plan->nstates = (int)G;
+        plan->ws_bytes = state_ws_bytes(BH, D, M, (int)G);
+    }
     return LA_OK;
 }
 
@@ -144,18 +152,26 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return LA_ERR_INVALID_ARG;
     if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) return LA_ERR_WORKSPACE;
     if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
-    float *ws = static_cast<float *>(workspace);
     const int dt = dtype, Di = (int)D, Mi = (int)M, C = p.chunk, G = p.segments, cps = p.chunks_per_segment;
     (void)hipGetLastError();  // clear a stale error so that the checks below report this call's launches
     hipError_t e = hipSuccess;
-    if (p.nstates > 0) e = la::prefill_states(dt, Di, Mi, C, K, V, ws, (int)BH, (int)N, G, cps, p.nstates, s);
-    if (e == hipSuccess && p.ws_bytes > 0)
-        e = la::prefill_scan(ws, (int)BH, Di, Mi, G, p.nstates, causal ? nullptr : S_out, causal ? nullptr : z_out,
-                             s);
-    if (e == hipSuccess)
-        e = la::prefill_outputs(dt, Di, Mi, C, Q, K, V, out, ws, (int)BH, (int)N, G, cps, causal,
-                                causal ? S_out : nullptr, causal ? z_out : nullptr, s);
+    if (causal) {
+        e = la::prefill_fused(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out, s);
+    } else {
+        float *ws = static_cast<float *>(workspace);
+        e = la::prefill_states(dt, Di, Mi, C, K, V, ws, (int)BH, (int)N, G, cps, G, s);
+        if (e == hipSuccess) e = la::prefill_scan(ws, (int)BH, Di, Mi, G, G, S_out, z_out, s);
+        if (e == hipSuccess)
+            e = la::prefill_outputs(dt, Di, Mi, C, Q, K, V, out, ws, (int)BH, (int)N, G, cps, 0, nullptr, nullptr, s);
+    }
     return hip_status(e);
+}
+
+LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
+    if (workspace_bytes == 0) return LA_OK;
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes % 4 != 0) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::fill_zero(static_cast<float *>(workspace), workspace_bytes / 4, as_stream(stream)));
 }
 
 // ---- stage entry points ----------------------------------------------------
@@ -185,6 +201,41 @@ int cps_of(int64_t N, int chunk, int segments) {
     return (int)((n_chunks + segments - 1) / segments);
 }
 }  // namespace
+
+LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                            int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
+                            size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+    int st = check_shape(B, H, N, D, M, dtype);
+    if (st != LA_OK) return st;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return LA_ERR_UNSUPPORTED;
+    if (!la::prefill_supported(dtype, (int)D, (int)M, chunk)) return LA_ERR_UNSUPPORTED;
+    if (segments < 1) return LA_ERR_INVALID_ARG;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+    const int64_t BH = B * H;
+    if (N > 0) {
+        const int64_t n_chunks = (N + chunk - 1) / chunk;
+        const int64_t cps = (n_chunks + segments - 1) / segments;
+        if ((int64_t)(segments - 1) * cps >= n_chunks) return LA_ERR_UNSUPPORTED;
+    }
+    if (BH * segments > INT_MAX / 256) return LA_ERR_UNSUPPORTED;
+    const size_t need = segments > 1 ? la::fused_ws_bytes(BH, segments, (int)(D * M + D)) : 0;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
+    if (BH == 0) return LA_OK;
+    hipStream_t s = as_stream(stream);
+    if (N == 0) {
+        if (S_out == nullptr) return LA_OK;
+        hipError_t e = la::fill_zero(S_out, (size_t)(BH * D * M), s);
+        if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * D), s);
+        return hip_status(e);
+    }
+    if (!Q || !K || !V || !out) return LA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::prefill_fused(dtype, (int)D, (int)M, chunk, Q, K, V, out, workspace, (int)BH, (int)N,
+                                        segments, cps_of(N, chunk, segments), S_out, z_out, s));
+}
 
 LA_API int la_segment_states(const void *K, const void *V, float *ws, size_t ws_bytes, int64_t B, int64_t H,
                              int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, int nstates,

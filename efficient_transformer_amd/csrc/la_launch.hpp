@@ -7,6 +7,16 @@
 
 namespace la {
 
+// Workspace layout of the fused causal kernel (shared by host sizing and device code):
+// header words, then one flag word per segment (padded to 64 words), then the
+// aggregate and the inclusive state of every segment (E floats each).
+constexpr int kWsHeaderWords = 64;
+__host__ __device__ inline size_t fused_flag_words(long BHG) { return ((size_t)BHG + 63) / 64 * 64; }
+__host__ __device__ inline size_t fused_ws_bytes(long BH, int G, int E) {
+    const size_t BHG = (size_t)BH * (size_t)G;
+    return (kWsHeaderWords + fused_flag_words((long)BHG)) * 4 + 2 * BHG * (size_t)E * 4;
+}
+
 // Prefill stage launchers for one element type (0 = fp32, 1 = bf16).
 // Each returns hipErrorInvalidValue for a (D, M, C) combination that has no kernel.
 bool prefill_supported(int dtype, int D, int M, int C);
@@ -15,6 +25,9 @@ hipError_t prefill_states(int dtype, int D, int M, int C, const void *K, const v
 hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
                            const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out, float *z_out,
                            hipStream_t stream);
+hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                         void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+size_t prefill_lds_bytes(int dtype, int D, int M, int C);
 hipError_t prefill_scan(float *ws, int BH, int D, int M, int G, int nstates, float *S_out, float *z_out,
                         hipStream_t stream);
 hipError_t fill_zero(float *p, size_t n, hipStream_t stream);
@@ -23,6 +36,12 @@ hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *
                        float *out, int BH, hipStream_t stream);
 
 // per element type (defined in la_prefill_f32.hip / la_prefill_bf16.hip)
+hipError_t prefill_fused_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
+                             int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+hipError_t prefill_fused_bf16(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
+                              int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+size_t prefill_lds_bytes_f32(int D, int M, int C);
+size_t prefill_lds_bytes_bf16(int D, int M, int C);
 bool prefill_supported_f32(int D, int M, int C);
 bool prefill_supported_bf16(int D, int M, int C);
 hipError_t prefill_states_f32(int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N, int G,

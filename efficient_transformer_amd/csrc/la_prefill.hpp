@@ -3,33 +3,37 @@
 // Page "Transformers are RNNs" (Katharopoulos et al., 2020), Proposed method:
 // attention with the similarity phi(q)^T phi(k) is rewritten by associativity as
 // phi(Q) (phi(K)^T V); causal masking is kept by the cumulative sums S_i, Z_i.
-// Here each head's sequence is cut into chunks of C positions and the chunks
-// into segments.  Within a chunk the masked quadratic term is formed on MFMA;
-// across chunks the state (S, z) carries the sums; across segments an exclusive
-// prefix of per-segment states links the pieces.  Per chunk c with state
-// (S, z) of all earlier positions:
+// Each head's sequence is cut into chunks of C positions and the chunks into
+// segments of whole chunks.  For a chunk c with the state (S, z) of all
+// earlier positions:
 //   A   = tril(phi(Q_c) phi(K_c)^T)               (C x C, diagonal kept)
 //   num = A V_c + phi(Q_c) S                      (C x M)
 //   den = rowsum(A) + phi(Q_c) z                  (C)
 //   out = num / den
 //   S  += phi(K_c)^T V_c ;  z += colsum(phi(K_c))
+// A workgroup (4 wavefronts) owns one segment.  Phase A sums its segment's
+// state; the states are chained across segments by an exclusive prefix
+// (published per segment, decoupled look-back in the fused kernel); phase B
+// walks the segment's chunks from the prefix and writes the outputs.
 //
-// One workgroup (4 wavefronts) walks one segment chunk by chunk, keeping S in
-// MFMA accumulators and a copy in LDS for the read-out of the next chunk.
+// Work split inside a workgroup: wavefront w owns the output / state columns
+// m-tiles {w, w+4, ...}.  It keeps S[:, its m-tiles] in MFMA accumulators,
+// updates them (phi(K)^T V) and reads them out (phi(Q) S) straight from
+// registers; the masked C x C matrix A is computed once per chunk (tiles
+// shared out over the wavefronts) and passed through LDS.
 //
-// LDS layouts (element type T):
-//   fp32 : phi(Q) [C][D+4], phi(K) [C][D+4], V [C][M+4], S [D][M+4]
-//   bf16 : phi(Q) [C][D+8], phi(K) [C][D+8], phi(K)^T [D][C+8], V^T [M][C+8],
-//          S^T [M][D+8]
-//   z (fp32, rounded like S) [D]
+// LDS (element type T = float or bf16):
+//   phi(Q) [C][D+p]   phi(K) [C][D+p]   A [C][C+p]
+//   fp32: V [C][M+p]             bf16: V^T [M][C+p], phi(K)^T [D][C+p]
+//   fp32 side arrays: z [D], column-sum partials, row-sum partials, phi(q).z
 // bf16 MFMA operands need the contraction index contiguous per lane, hence the
-// transposed copies; fp32 MFMA takes one element per lane and reads the
-// natural layouts with strides.
+// transposed copies; fp32 MFMA takes one element per lane.
 #pragma once
 
 #include <type_traits>
 
 #include "la_device.hpp"
+#include "la_launch.hpp"
 
 namespace la {
 
@@ -41,34 +45,36 @@ template <typename T, int D, int M, int C>
 struct Cfg {
     static constexpr bool F32 = std::is_same<T, float>::value;
     static constexpr int RT = C / 16, DT = D / 16, MT = M / 16;
-    static constexpr int NWR = RT < kWaves ? RT : kWaves;  // wave groups over row tiles
-    static constexpr int NWM = kWaves / NWR;               // wave groups over m tiles
-    static constexpr int S_TILES = DT * MT;
-    static constexpr int S_PER_WAVE = (S_TILES + kWaves - 1) / kWaves;
+    static constexpr int MTW = (MT + kWaves - 1) / kWaves;  // m-tiles per wavefront
+    static constexpr int NA = RT * (RT + 1) / 2;            // lower-triangle tiles of A
     static constexpr int PAD = F32 ? 4 : 8;
-    static constexpr int LQ = D + PAD;  // row stride of phi(Q), phi(K) (and S^T for bf16)
-    static constexpr int LV = M + PAD;  // fp32: row stride of V and S
-    static constexpr int LT = C + PAD;  // bf16: row stride of phi(K)^T and V^T
-    static constexpr int E = D * M + D;  // floats per state slot
+    static constexpr int LQ = D + PAD;  // rows of phi(Q), phi(K)
+    static constexpr int LA = C + PAD;  // rows of A
+    static constexpr int LV = M + PAD;  // fp32: rows of V
+    static constexpr int LT = C + PAD;  // bf16: rows of V^T and phi(K)^T
+    static constexpr int E = D * M + D; // floats of one state (S then z)
+    static constexpr int NZP = kThreads / D;  // column-sum partial groups
+    static constexpr int ZROWS = C / NZP;     // rows per partial
+    static_assert(ZROWS * NZP == C || ZROWS == 0, "column-sum split");
 
-    // element offsets of the output kernel's LDS carve-up
+    // T-element offsets
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * LQ;
-    static constexpr int oV = oK + C * LQ;                 // fp32: V; bf16: V^T
+    static constexpr int oV = oK + C * LQ;
     static constexpr int nV = F32 ? C * LV : M * LT;
-    static constexpr int oKt = oV + nV;                    // bf16 only
+    static constexpr int oKt = oV + nV;
     static constexpr int nKt = F32 ? 0 : D * LT;
-    static constexpr int oS = oKt + nKt;                   // fp32: S; bf16: S^T
-    static constexpr int nS = F32 ? D * LV : M * LQ;
-    static constexpr int nT_out = oS + nS;
-    static constexpr size_t out_bytes = ((nT_out * sizeof(T) + 15) / 16) * 16 + D * sizeof(float);
-
-    // state kernel: fp32 phi(K) [C][LQ] + V [C][LV]; bf16 phi(K)^T [D][LT] + V^T [M][LT]
-    static constexpr int sK_n = F32 ? C * LQ : D * LT;
-    static constexpr int sV_n = F32 ? C * LV : M * LT;
-    static constexpr size_t state_bytes = (sK_n + sV_n) * sizeof(T);
-
-    static constexpr bool fits = out_bytes <= kMaxLds && state_bytes <= kMaxLds;
+    static constexpr int oA = oKt + nKt;
+    static constexpr int nT = oA + C * LA;
+    static constexpr size_t fbase = ((nT * sizeof(T) + 15) / 16) * 16;
+    // float offsets (from fbase)
+    static constexpr int fz = 0;
+    static constexpr int fzp = fz + D;
+    static constexpr int fdenp = fzp + (NZP > 0 ? NZP : 1) * D;
+    static constexpr int fqz = fdenp + RT * C;
+    static constexpr int nF = fqz + C;
+    static constexpr size_t bytes = fbase + nF * sizeof(float);
+    static constexpr bool fits = bytes + 64 <= kMaxLds;
 };
 
 // ---------------------------------------------------------------------------
@@ -170,177 +176,458 @@ struct Stage {
     }
 };
 
+
 // ---------------------------------------------------------------------------
-// State update S += phi(K_c)^T V_c for the S tiles this wavefront owns
-// (tile t = w + kWaves*i, t = dt*MT + mt); result lane layout
-// acc[i][r] = S[dt*16 + 4g + r][mt*16 + l16].
+// Workspace of the fused kernel (fp32 words):
+//   header (64 words): [0] ticket counter, [1] finished-workgroup counter,
+//                      [2] epoch, [3] error flag (look-back gave up)
+//   flags  [BH][G] (uint32, padded to 64 words): epoch << 2 | 1 aggregate ready,
+//                                                epoch << 2 | 2 inclusive ready
+//   aggregate states [BH][G][E], inclusive states [BH][G][E]
+// The header and flags must be zero before the first call with a given plan;
+// the last workgroup of every call resets the counters and advances the
+// epoch, which makes all flags of the call stale.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, int NS>
-__device__ __forceinline__ void state_update(f32x4 (&acc)[NS], const T *sKx,
-                                             const T *sVx, int w, int g, int l16) {
+struct FusedWs {
+    unsigned *hdr;
+    unsigned *flags;
+    float *agg;
+    float *incl;
+    __device__ FusedWs(void *ws, long BH, int G, int E) {
+        hdr = static_cast<unsigned *>(ws);
+        flags = hdr + kWsHeaderWords;
+        agg = reinterpret_cast<float *>(flags + fused_flag_words((long)BH * G));
+        incl = agg + (size_t)BH * G * E;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The per-chunk engine shared by the kernels.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int M, int C>
+struct Engine {
     using G = Cfg<T, D, M, C>;
+    static constexpr int DT = G::DT, MTW = G::MTW, RT = G::RT;
+    T *sQ, *sK, *sV, *sKt, *sA;
+    float *sz, *szp, *sdenp, *sqz;
+    int tid, lane, w, g, l16;
+
+    __device__ __forceinline__ explicit Engine(unsigned char *smem) {
+        T *t = reinterpret_cast<T *>(smem);
+        sQ = t + G::oQ;
+        sK = t + G::oK;
+        sV = t + G::oV;
+        sKt = t + G::oKt;
+        sA = t + G::oA;
+        float *f = reinterpret_cast<float *>(smem + G::fbase);
+        sz = f + G::fz;
+        szp = f + G::fzp;
+        sdenp = f + G::fdenp;
+        sqz = f + G::fqz;
+        tid = threadIdx.x;
+        lane = tid & 63;
+        w = tid >> 6;
+        g = lane >> 4;
+        l16 = lane & 15;
+    }
+
+    __device__ __forceinline__ bool owns(int i) const { return G::MT % kWaves == 0 || w + kWaves * i < G::MT; }
+    __device__ __forceinline__ int mtile(int i) const { return w + kWaves * i; }
+
+    // The upper triangle of A is never written by a_tiles; zero it (all of A) once.
+    __device__ __forceinline__ void clear_a() const {
+        for (int e = tid; e < C * G::LA; e += kThreads) sA[e] = from_f32<T>(0.0f);
+    }
+
+    __device__ __forceinline__ void store_q(const Stage<T, C, D> &st, int row0, int N) const {
+        st.template store_natural<true>(sQ, G::LQ, row0, N, tid);
+    }
+    __device__ __forceinline__ void store_kv(const Stage<T, C, D> &stK, const Stage<T, C, M> &stV, int row0,
+                                             int N) const {
+        if constexpr (G::F32) {
+            stK.template store_natural<true>(sK, G::LQ, row0, N, tid);
+            stV.template store_natural<false>(sV, G::LV, row0, N, tid);
+        } else {
+            stK.template store_transposed<true, true>(sKt, G::LT, sK, G::LQ, row0, N, tid);
+            stV.template store_transposed<false, false>(sV, G::LT, nullptr, 0, row0, N, tid);
+        }
+    }
+
+    // Column sums of phi(K_c): partial sums over ZROWS rows into szp[q][d].
+    __device__ __forceinline__ void z_partials() const {
+        const int q = tid / D, d = tid % D;
+        if (q < G::NZP) {
+            float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < G::S_PER_WAVE; ++i) {
-        const int t = w + kWaves * i;
-        if (G::S_TILES % kWaves == 0 || t < G::S_TILES) {
-            const int dt = t / G::MT, mt = t % G::MT;
-            if constexpr (G::F32) {
-                // A = phi(K)^T: row d, contraction over keys -> sK[key][d]
-                acc[i] = tile_dot_f32<C>(sKx + dt * 16 + l16, G::LQ, sVx + mt * 16 + l16, G::LV, g, acc[i]);
-            } else {
-                acc[i] = tile_dot_bf16<C>(sKx + (dt * 16 + l16) * G::LT, sVx + (mt * 16 + l16) * G::LT, g, acc[i]);
+            for (int r = 0; r < G::ZROWS; ++r) s += to_f32(sK[(q * G::ZROWS + r) * G::LQ + d]);
+            szp[q * D + d] = s;
+        }
+    }
+    __device__ __forceinline__ float z_delta() const {  // thread tid < D, after a barrier
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < G::NZP; ++q) s += szp[q * D + tid];
+        return s;
+    }
+
+    // S[:, own m-tiles] += phi(K_c)^T V_c.  acc[dt][i][r] = S[dt*16 + 4g + r][mt_i*16 + l16].
+    __device__ __forceinline__ void state_update(f32x4 (&acc)[DT][MTW]) const {
+        if constexpr (G::F32) {
+#pragma unroll 4
+            for (int ks = 0; ks < C / 4; ++ks) {
+                const int key = 4 * ks + g;
+                float bv[MTW];
+#pragma unroll
+                for (int i = 0; i < MTW; ++i) bv[i] = owns(i) ? sV[key * G::LV + mtile(i) * 16 + l16] : 0.0f;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const float a = sK[key * G::LQ + dt * 16 + l16];
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i)
+                        if (owns(i)) acc[dt][i] = mma_f32(a, bv[i], acc[dt][i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) {
+                if (!owns(i)) continue;
+                const T *vrow = sV + (mtile(i) * 16 + l16) * G::LT;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    acc[dt][i] = tile_dot_bf16<C>(sKt + (dt * 16 + l16) * G::LT, vrow, g, acc[dt][i]);
             }
         }
     }
-}
 
-// column sums of phi(K_c) for z (thread tid < D owns z[tid])
-template <typename T, int D, int M, int C>
-__device__ __forceinline__ float z_update(float z, const T *sKx, int tid) {
-    using G = Cfg<T, D, M, C>;
-    if (tid < D) {
-#pragma unroll 8
-        for (int key = 0; key < C; ++key) {
-            if constexpr (G::F32)
-                z += sKx[key * G::LQ + tid];
-            else
-                z += to_f32(sKx[tid * G::LT + key]);
+    // Lower-triangle tiles of A (tile t = w, w+4, ... in row-major order of (rt, kt<=rt)),
+    // rounded to T, into sA[query][key]; their row sums into sdenp[kt][query].
+    __device__ __forceinline__ void a_tiles() const {
+#pragma unroll
+        for (int t = w; t < G::NA; t += kWaves) {
+            int rt = 0;
+            while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
+            const int kt = t - rt * (rt + 1) / 2;
+            f32x4 a = zero4();
+            const T *krow = sK + (kt * 16 + l16) * G::LQ;
+            const T *qrow = sQ + (rt * 16 + l16) * G::LQ;
+            if constexpr (G::F32) {
+                // contraction index d = g*(D/4) + j: each lane reads a contiguous quarter of the row
+#pragma unroll
+                for (int j4 = 0; j4 < D / 16; ++j4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(krow + g * (D / 4) + 4 * j4);
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(qrow + g * (D / 4) + 4 * j4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) a = mma_f32(av[j], bv[j], a);
+                }
+            } else {
+                a = tile_dot_bf16<D>(krow, qrow, g, a);
+            }
+            // a[r] = A[query = rt*16 + l16][key = kt*16 + 4g + r]
+            float rs = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (kt == rt && 4 * g + r > l16) a[r] = 0.0f;
+                a[r] = round_as<T>(a[r]);
+                rs += a[r];
+            }
+            T *arow = sA + (rt * 16 + l16) * G::LA + kt * 16 + 4 * g;
+            if constexpr (G::F32) {
+                *reinterpret_cast<f32x4 *>(arow) = a;
+            } else {
+                bf16x4 v = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+                *reinterpret_cast<bf16x4 *>(arow) = v;
+            }
+            rs = sum_over_groups(rs);
+            if (g == 0) sdenp[kt * C + rt * 16 + l16] = rs;
         }
     }
-    return z;
-}
 
-// Copy the register state into the LDS read-out copy (rounded to T).
-template <typename T, int D, int M, int C, int NS>
-__device__ __forceinline__ void state_to_lds(const f32x4 (&acc)[NS], float z, T *sS,
-                                             float *sz, int w, int g, int l16, int tid) {
-    using G = Cfg<T, D, M, C>;
+    // phi(q_i) . z for every row i of the chunk -> sqz[i]
+    __device__ __forceinline__ void qz_rows() const {
+        constexpr int TPR = kThreads / C;  // threads per row (4, 8 or 16), consecutive lanes
+        const int i = tid / TPR, p = tid % TPR;
+        const T *qr = sQ + i * G::LQ;
+        float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < G::S_PER_WAVE; ++i) {
-        const int t = w + kWaves * i;
-        if (G::S_TILES % kWaves == 0 || t < G::S_TILES) {
-            const int dt = t / G::MT, mt = t % G::MT;
+        for (int j = 0; j < D / TPR; ++j) s += to_f32(qr[p * (D / TPR) + j]) * sz[p * (D / TPR) + j];
+#pragma unroll
+        for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (p == 0) sqz[i] = s;
+    }
+
+    // 1 / den for row `lane` (lanes >= C return 0); needs sdenp and sqz (after a barrier)
+    template <bool CAUSAL>
+    __device__ __forceinline__ float row_inv() const {
+        if (lane >= C) return 0.0f;
+        const int rt = lane / 16;
+        float den = sqz[lane];
+        if constexpr (CAUSAL) {
+#pragma unroll
+            for (int kt = 0; kt < RT; ++kt)
+                if (kt <= rt) den += sdenp[kt * C + lane];
+        }
+        return 1.0f / den;
+    }
+
+    // out rows of the chunk for the own m-tiles: (A V_c + phi(Q_c) S) * inv
+    // (non-causal: phi(Q_c) S * inv with S the total state).
+    template <bool CAUSAL>
+    __device__ __forceinline__ void outputs(const f32x4 (&S)[DT][MTW], float inv, float *__restrict__ Oh, int row0,
+                                            int N, bool poison) const {
+        // bf16 copies of the state for the read-out operands
+        [[maybe_unused]] bf16x4 Sb[DT][MTW];
+        if constexpr (!G::F32) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < MTW; ++i)
+                    Sb[dt][i] = bf16x4{(bf16)S[dt][i][0], (bf16)S[dt][i][1], (bf16)S[dt][i][2], (bf16)S[dt][i][3]};
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int qrow = rt * 16 + l16;
+            f32x4 o[MTW];
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) o[i] = zero4();
+            // intra-chunk term A V_c over keys 0 .. 16(rt+1)-1
+            if constexpr (!CAUSAL) {
+            } else if constexpr (G::F32) {
+                const int nsteps = 4 * (rt + 1);  // keys per lane group
+                const float *arow = sA + qrow * G::LA + g * nsteps;
+#pragma unroll
+                for (int j4 = 0; j4 < rt + 1; ++j4) {
+                    const f32x4 av = *reinterpret_cast<const f32x4 *>(arow + 4 * j4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = g * nsteps + 4 * j4 + j;
+#pragma unroll
+                        for (int i = 0; i < MTW; ++i)
+                            if (owns(i)) o[i] = mma_f32(av[j], sV[key * G::LV + mtile(i) * 16 + l16], o[i]);
+                    }
+                }
+            } else if constexpr (RT == 1) {
+                const bf16x4 av = *reinterpret_cast<const bf16x4 *>(sA + qrow * G::LA + 4 * g);
+#pragma unroll
+                for (int i = 0; i < MTW; ++i) {
+                    if (!owns(i)) continue;
+                    const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(sV + (mtile(i) * 16 + l16) * G::LT + 4 * g);
+                    o[i] = mma_bf16_k16(av, bv, o[i]);
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < (rt + 2) / 2; ++kk) {
+                    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sA + qrow * G::LA + kk * 32 + 8 * g);
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i) {
+                        if (!owns(i)) continue;
+                        const bf16x8 bv =
+                            *reinterpret_cast<const bf16x8 *>(sV + (mtile(i) * 16 + l16) * G::LT + kk * 32 + 8 * g);
+                        o[i] = mma_bf16_k32(av, bv, o[i]);
+                    }
+                }
+            }
+            // inter-chunk term phi(Q_c) S with S from registers:
+            // contraction slot of lane (g, l16) at step (dt, r) is d = dt*16 + 4g + r
             if constexpr (G::F32) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sS[(dt * 16 + 4 * g + r) * G::LV + mt * 16 + l16] = acc[i][r];
+                for (int dt = 0; dt < DT; ++dt) {
+                    const f32x4 qv = *reinterpret_cast<const f32x4 *>(sQ + qrow * G::LQ + dt * 16 + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+#pragma unroll
+                        for (int i = 0; i < MTW; ++i)
+                            if (owns(i)) o[i] = mma_f32(qv[r], S[dt][i][r], o[i]);
+                }
+            } else if constexpr (DT == 1) {
+                const bf16x4 qv = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + 4 * g);
+#pragma unroll
+                for (int i = 0; i < MTW; ++i)
+                    if (owns(i)) o[i] = mma_bf16_k16(qv, Sb[0][i], o[i]);
             } else {
-                bf16x4 v = {(bf16)acc[i][0], (bf16)acc[i][1], (bf16)acc[i][2], (bf16)acc[i][3]};
-                *reinterpret_cast<bf16x4 *>(sS + (mt * 16 + l16) * G::LQ + dt * 16 + 4 * g) = v;
+#pragma unroll
+                for (int p = 0; p < DT / 2; ++p) {
+                    const bf16x4 q0 = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + (2 * p) * 16 + 4 * g);
+                    const bf16x4 q1 = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + (2 * p + 1) * 16 + 4 * g);
+                    const bf16x8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i) {
+                        if (!owns(i)) continue;
+                        const bf16x4 s0 = Sb[2 * p][i], s1 = Sb[2 * p + 1][i];
+                        const bf16x8 sv = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+                        o[i] = mma_bf16_k32(qv, sv, o[i]);
+                    }
+                }
+            }
+            // normalise and store: lane holds rows rt*16 + 4g + r, column mt*16 + l16
+            float inv_r[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) inv_r[r] = __shfl(inv, rt * 16 + 4 * g + r, 64);
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) {
+                if (!owns(i)) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int grow = row0 + rt * 16 + 4 * g + r;
+                    if (grow < N)
+                        Oh[(size_t)grow * M + mtile(i) * 16 + l16] = poison ? __builtin_nanf("") : o[i][r] * inv_r[r];
+                }
             }
         }
     }
-    if (tid < D) sz[tid] = round_as<T>(z);
-}
 
-// Load a state slot ([D][M] then [D], fp32) into the register layout.
-template <typename T, int D, int M, int C, int NS>
-__device__ __forceinline__ void state_from_global(f32x4 (&acc)[NS], float &z,
-                                                  const float *st, int w, int g, int l16, int tid) {
-    using G = Cfg<T, D, M, C>;
+    // ---- state slots ([D][M] row major, then z[D]) <-> register layout ----
+    __device__ __forceinline__ void state_store(const f32x4 (&acc)[DT][MTW], float z, float *Sd, float *zd) const {
 #pragma unroll
-    for (int i = 0; i < G::S_PER_WAVE; ++i) {
-        const int t = w + kWaves * i;
-        acc[i] = zero4();
-        if (G::S_TILES % kWaves == 0 || t < G::S_TILES) {
-            const int dt = t / G::MT, mt = t % G::MT;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][r] = st[(dt * 16 + 4 * g + r) * M + mt * 16 + l16];
-        }
+            for (int i = 0; i < MTW; ++i) {
+                if (!owns(i)) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sd[(dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16] = acc[dt][i][r];
+            }
+        if (tid < D) zd[tid] = z;
     }
-    z = tid < D ? st[D * M + tid] : 0.0f;
-}
-
-template <typename T, int D, int M, int C, int NS>
-__device__ __forceinline__ void state_to_global(const f32x4 (&acc)[NS], float z,
-                                                float *S, float *zp, int w, int g, int l16, int tid) {
-    using G = Cfg<T, D, M, C>;
-#pragma unroll
-    for (int i = 0; i < G::S_PER_WAVE; ++i) {
-        const int t = w + kWaves * i;
-        if (G::S_TILES % kWaves == 0 || t < G::S_TILES) {
-            const int dt = t / G::MT, mt = t % G::MT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[(dt * 16 + 4 * g + r) * M + mt * 16 + l16] = acc[i][r];
-        }
+    __device__ __forceinline__ void state_store(const f32x4 (&acc)[DT][MTW], float z, float *slot) const {
+        state_store(acc, z, slot, slot + D * M);
     }
-    if (tid < D) zp[tid] = z;
-}
+    __device__ __forceinline__ void state_add(f32x4 (&acc)[DT][MTW], float &z, const float *slot) const {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) {
+                if (!owns(i)) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[dt][i][r] += slot[(dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16];
+            }
+        if (tid < D) z += slot[D * M + tid];
+    }
+    __device__ __forceinline__ static void zero_state(f32x4 (&acc)[DT][MTW]) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) acc[dt][i] = zero4();
+    }
+};
 
 // ---------------------------------------------------------------------------
-// Stage 1: per-segment summed state (S, z) of phi(k_j) v_j^T, phi(k_j).
-// Grid: BH * nstates workgroups; workgroup -> (bh, s).
+// Phase A: sum the state over chunks [c0, c1) into acc / z (thread tid < D owns z[tid]).
+// Leaves the last chunk's phi(K), V in LDS.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C>
-__global__ __launch_bounds__(kThreads) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
-                                                             float *__restrict__ ws, int N, int G_, int CPS,
-                                                             int nstates) {
-    using G = Cfg<T, D, M, C>;
-    __shared__ __attribute__((aligned(16))) T smem[G::sK_n + G::sV_n];
-    T *sKx = smem;
-    T *sVx = smem + G::sK_n;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
-    const int bh = blockIdx.x / nstates, s = blockIdx.x % nstates;
-    const int n_chunks = (N + C - 1) / C;
-    const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
-    const T *Kh = K + (size_t)bh * N * D;
-    const T *Vh = V + (size_t)bh * N * M;
-
-    f32x4 acc[G::S_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < G::S_PER_WAVE; ++i) acc[i] = zero4();
-    float z = 0.0f;
-
+__device__ __forceinline__ void phase_a(const Engine<T, D, M, C> &e, const T *__restrict__ Kh,
+                                        const T *__restrict__ Vh, int N, int c0, int c1,
+                                        f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z) {
     Stage<T, C, D> stK;
     Stage<T, C, M> stV;
-    if (c0 < c1) {
-        stK.load(Kh, c0 * C, N, tid);
-        stV.load(Vh, c0 * C, N, tid);
+    stK.load(Kh, c0 * C, N, e.tid);
+    stV.load(Vh, c0 * C, N, e.tid);
+    for (int c = c0; c < c1; ++c) {
+        const int row0 = c * C;
+        __syncthreads();  // LDS free (previous chunk's readers are done)
+        e.store_kv(stK, stV, row0, N);
+        __syncthreads();
+        if (c + 1 < c1) {
+            stK.load(Kh, row0 + C, N, e.tid);
+            stV.load(Vh, row0 + C, N, e.tid);
+        }
+        e.z_partials();
+        e.state_update(acc);
+        __syncthreads();
+        if (e.tid < D) z += e.z_delta();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Phase B: outputs of chunks [c0, c1) starting from the state (S, z) of all
+// earlier positions.  kv_staged: chunk c0's phi(K), V are already in LDS.
+// advance_last: also advance the state over the last chunk (for the final state).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int M, int C, bool CAUSAL>
+__device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__restrict__ Qh,
+                                        const T *__restrict__ Kh, const T *__restrict__ Vh,
+                                        float *__restrict__ Oh, int N, int c0, int c1, bool kv_staged,
+                                        bool advance_last, Stage<T, C, D> &stQ,
+                                        f32x4 (&S)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z,
+                                        bool poison) {
+    Stage<T, C, D> stK;
+    Stage<T, C, M> stV;
+    if (CAUSAL && !kv_staged) {
+        stK.load(Kh, c0 * C, N, e.tid);
+        stV.load(Vh, c0 * C, N, e.tid);
     }
     for (int c = c0; c < c1; ++c) {
         const int row0 = c * C;
-        if constexpr (G::F32) {
-            stK.template store_natural<true>(sKx, G::LQ, row0, N, tid);
-            stV.template store_natural<false>(sVx, G::LV, row0, N, tid);
-        } else {
-            stK.template store_transposed<true, false>(sKx, G::LT, nullptr, 0, row0, N, tid);
-            stV.template store_transposed<false, false>(sVx, G::LT, nullptr, 0, row0, N, tid);
-        }
+        const bool stage_kv = CAUSAL && !(kv_staged && c == c0);
+        __syncthreads();  // LDS free
+        e.store_q(stQ, row0, N);
+        if (stage_kv) e.store_kv(stK, stV, row0, N);
+        if (e.tid < D) e.sz[e.tid] = round_as<T>(z);
         __syncthreads();
         if (c + 1 < c1) {
-            stK.load(Kh, row0 + C, N, tid);
-            stV.load(Vh, row0 + C, N, tid);
+            stQ.load(Qh, row0 + C, N, e.tid);
+            if (CAUSAL) {
+                stK.load(Kh, row0 + C, N, e.tid);
+                stV.load(Vh, row0 + C, N, e.tid);
+            }
         }
-        state_update<T, D, M, C>(acc, sKx, sVx, w, g, l16);
-        z = z_update<T, D, M, C>(z, sKx, tid);
+        if (CAUSAL) e.a_tiles();
+        e.qz_rows();
+        const bool adv = CAUSAL && (c + 1 < c1 || advance_last);
+        if (adv) e.z_partials();
         __syncthreads();
+        const float inv = e.template row_inv<CAUSAL>();
+        e.template outputs<CAUSAL>(S, inv, Oh, row0, N, poison);
+        if (adv) {
+            e.state_update(S);
+            if (e.tid < D) z += e.z_delta();
+        }
     }
-    float *slot = ws + ((size_t)bh * (G_ + 1) + s) * G::E;
-    state_to_global<T, D, M, C>(acc, z, slot, slot + D * M, w, g, l16, tid);
 }
 
 // ---------------------------------------------------------------------------
-// Stage 3: outputs of one segment, from the exclusive prefix in its slot
-// (causal) or from the total in slot G (non-causal).
+// Fused causal kernel: phase A, decoupled look-back over segments, phase B.
+// Workgroups take tickets in launch order; ticket t -> segment t / BH of head
+// t % BH, so a workgroup only waits on segments with smaller tickets, which
+// are running or finished.  With G == 1 there is no look-back and no workspace.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                              const T *__restrict__ V, float *__restrict__ out,
-                                                              const float *__restrict__ ws, int N, int G_,
-                                                              int CPS, float *__restrict__ S_out,
-                                                              float *__restrict__ z_out) {
-    using G = Cfg<T, D, M, C>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem_raw[G::out_bytes];
-    T *smem = reinterpret_cast<T *>(smem_raw);
-    T *sQ = smem + G::oQ;
-    T *sK = smem + G::oK;
-    T *sV = smem + G::oV;   // fp32: V natural; bf16: V^T
-    T *sKt = smem + G::oKt; // bf16 only
-    T *sS = smem + G::oS;   // fp32: S natural; bf16: S^T
-    float *sz = reinterpret_cast<float *>(smem_raw + ((G::nT_out * sizeof(T) + 15) / 16) * 16);
+constexpr long kSpinLimit = 1L << 22;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, l16 = lane & 15;
-    const int bh = blockIdx.x / G_, s = blockIdx.x % G_;
+template <typename T, int D, int M, int C>
+__global__ __launch_bounds__(kThreads) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+                                                                const T *__restrict__ V, float *__restrict__ out,
+                                                                void *ws_raw, int BH, int N, int G_, int CPS,
+                                                                float *__restrict__ S_out, float *__restrict__ z_out) {
+    using Gc = Cfg<T, D, M, C>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
+    __shared__ unsigned sh_word[2];
+    Engine<T, D, M, C> e(smem);
+    const int tid = e.tid;
+
+    int bh, s;
+    unsigned epoch = 0;
+    FusedWs ws(ws_raw, BH, G_ > 1 ? G_ : 1, Gc::E);
+    if (G_ > 1) {
+        if (tid == 0) {
+            sh_word[0] = atomicAdd(&ws.hdr[0], 1u);
+            sh_word[1] = __hip_atomic_load(&ws.hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const unsigned t = sh_word[0];
+        epoch = sh_word[1];
+        __syncthreads();  // sh_word is reused below
+        if (t >= (unsigned)(BH * G_)) {
+            // counters not reset by an earlier failed call: report and do nothing
+            if (tid == 0) __hip_atomic_store(&ws.hdr[3], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        s = (int)(t / (unsigned)BH);
+        bh = (int)(t % (unsigned)BH);
+    } else {
+        bh = blockIdx.x;
+        s = 0;
+    }
+    const unsigned ep = (epoch & 0x3fffffffu) << 2;
+
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
     const T *Qh = Q + (size_t)bh * N * D;
@@ -348,169 +635,186 @@ __global__ __launch_bounds__(kThreads) void seg_output_kernel(const T *__restric
     const T *Vh = V + (size_t)bh * N * M;
     float *Oh = out + (size_t)bh * N * M;
 
-    f32x4 acc[G::S_PER_WAVE];
+    e.clear_a();
+
+    f32x4 acc[Gc::DT][Gc::MTW];
+    Engine<T, D, M, C>::zero_state(acc);
+    float zacc = 0.0f;
+    const bool last = s == G_ - 1;
+    const bool want_final = S_out != nullptr;
+    const bool run_a = G_ > 1 && (!last || want_final);
+    if (run_a) phase_a<T, D, M, C>(e, Kh, Vh, N, c0, c1, acc, zacc);
+
+    Stage<T, C, D> stQ;
+    stQ.load(Qh, c0 * C, N, tid);
+
+    f32x4 pre[Gc::DT][Gc::MTW];
+    Engine<T, D, M, C>::zero_state(pre);
+    float zpre = 0.0f;
+    bool failed = false;
+    if (G_ > 1) {
+        const size_t my = (size_t)bh * G_ + s;
+        if (!last) {
+            // publish the segment aggregate
+            e.state_store(acc, zacc, ws.agg + my * Gc::E);
+            __threadfence();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(&ws.flags[my], ep | 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // look back: sum aggregates of s-1, s-2, ... until an inclusive prefix
+        for (int j = s - 1; j >= 0; --j) {
+            const size_t other = (size_t)bh * G_ + j;
+            if (tid == 0) {
+                unsigned st = 0;
+                long spins = 0;
+                while (true) {
+                    const unsigned f = __hip_atomic_load(&ws.flags[other], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                    if ((f & ~3u) == ep && (f & 3u) != 0) {
+                        st = f & 3u;
+                        break;
+                    }
+                    if (++spins > kSpinLimit) {
+                        st = 0;
+                        __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                sh_word[0] = st;
+            }
+            __syncthreads();
+            const unsigned st = sh_word[0];
+            __threadfence();
+            if (st == 0) {
+                failed = true;
+                break;
+            }
+            e.state_add(pre, zpre, (st == 2u ? ws.incl : ws.agg) + other * Gc::E);
+            __syncthreads();  // sh_word reuse
+            if (st == 2u) break;
+        }
+        if (!last && s > 0) {
+            // publish the inclusive prefix (segment 0's aggregate already is one)
+            f32x4 inc[Gc::DT][Gc::MTW];
+            const float nan = __builtin_nanf("");
+#pragma unroll
+            for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < Gc::MTW; ++i) {
+                    inc[dt][i] = pre[dt][i] + acc[dt][i];
+                    if (failed) inc[dt][i] = f32x4{nan, nan, nan, nan};
+                }
+            e.state_store(inc, failed ? nan : zpre + zacc, ws.incl + my * Gc::E);
+            __threadfence();
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(&ws.flags[my], ep | 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (last && want_final) {
+            f32x4 fin[Gc::DT][Gc::MTW];
+#pragma unroll
+            for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < Gc::MTW; ++i) fin[dt][i] = pre[dt][i] + acc[dt][i];
+            e.state_store(fin, zpre + zacc, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+        }
+    }
+
+    // phase B from the prefix; with a single-chunk segment phase A left K, V in LDS
+    const bool kv_staged = run_a && (c1 - c0 == 1);
+    phase_b<T, D, M, C, true>(e, Qh, Kh, Vh, Oh, N, c0, c1, kv_staged, G_ == 1 && want_final, stQ, pre, zpre,
+                              failed);
+
+    if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+
+    if (G_ > 1) {
+        // the last workgroup to finish resets the counters and advances the epoch
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned done = atomicAdd(&ws.hdr[1], 1u);
+            if (done == (unsigned)(BH * G_) - 1u) {
+                __hip_atomic_store(&ws.hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&ws.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&ws.hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stage kernels (explicit three-step form; also the non-causal path).
+// Stage workspace: [BH][G + 1][E]; slot s = state of segment s, later its
+// exclusive prefix; slot G = total.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int M, int C>
+__global__ __launch_bounds__(kThreads) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
+                                                             float *__restrict__ ws, int N, int G_, int CPS,
+                                                             int nstates) {
+    using Gc = Cfg<T, D, M, C>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
+    Engine<T, D, M, C> e(smem);
+    const int bh = blockIdx.x / nstates, s = blockIdx.x % nstates;
+    const int n_chunks = (N + C - 1) / C;
+    const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
+    f32x4 acc[Gc::DT][Gc::MTW];
+    Engine<T, D, M, C>::zero_state(acc);
     float z = 0.0f;
-    if constexpr (CAUSAL) {
-        if (s > 0) {
-            state_from_global<T, D, M, C>(acc, z, ws + ((size_t)bh * (G_ + 1) + s) * G::E, w, g, l16, tid);
-        } else {
-#pragma unroll
-            for (int i = 0; i < G::S_PER_WAVE; ++i) acc[i] = zero4();
-        }
-        state_to_lds<T, D, M, C>(acc, z, sS, sz, w, g, l16, tid);
+    phase_a<T, D, M, C>(e, K + (size_t)bh * N * D, V + (size_t)bh * N * M, N, c0, c1, acc, z);
+    e.state_store(acc, z, ws + ((size_t)bh * (G_ + 1) + s) * Gc::E);
+}
+
+template <typename T, int D, int M, int C, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+                                                              const T *__restrict__ V, float *__restrict__ out,
+                                                              const float *__restrict__ ws, int N, int G_, int CPS,
+                                                              float *__restrict__ S_out, float *__restrict__ z_out) {
+    using Gc = Cfg<T, D, M, C>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
+    Engine<T, D, M, C> e(smem);
+    const int bh = blockIdx.x / G_, s = blockIdx.x % G_;
+    const int n_chunks = (N + C - 1) / C;
+    const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
+    const T *Qh = Q + (size_t)bh * N * D;
+    f32x4 S[Gc::DT][Gc::MTW];
+    Engine<T, D, M, C>::zero_state(S);
+    float z = 0.0f;
+    if (CAUSAL) {
+        if (s > 0) e.state_add(S, z, ws + ((size_t)bh * (G_ + 1) + s) * Gc::E);
     } else {
-        const float *st = ws + ((size_t)bh * (G_ + 1) + G_) * G::E;
-        for (int e = tid; e < D * M; e += kThreads) {
-            const int d = e / M, m = e % M;
-            if constexpr (G::F32)
-                sS[d * G::LV + m] = st[e];
-            else
-                sS[m * G::LQ + d] = (bf16)st[e];
-        }
-        if (tid < D) sz[tid] = round_as<T>(st[D * M + tid]);
+        e.state_add(S, z, ws + ((size_t)bh * (G_ + 1) + G_) * Gc::E);
     }
-
-    Stage<T, C, D> stQ, stK;
-    Stage<T, C, M> stV;
-    if (c0 < c1) {
-        stQ.load(Qh, c0 * C, N, tid);
-        if constexpr (CAUSAL) {
-            stK.load(Kh, c0 * C, N, tid);
-            stV.load(Vh, c0 * C, N, tid);
-        }
-    }
-    const int rgrp = w % G::NWR, mgrp = w / G::NWR;
-
-    for (int c = c0; c < c1; ++c) {
-        const int row0 = c * C;
-        stQ.template store_natural<true>(sQ, G::LQ, row0, N, tid);
-        if constexpr (CAUSAL) {
-            if constexpr (G::F32) {
-                stK.template store_natural<true>(sK, G::LQ, row0, N, tid);
-                stV.template store_natural<false>(sV, G::LV, row0, N, tid);
-            } else {
-                stK.template store_transposed<true, true>(sKt, G::LT, sK, G::LQ, row0, N, tid);
-                stV.template store_transposed<false, false>(sV, G::LT, nullptr, 0, row0, N, tid);
-            }
-        }
-        __syncthreads();
-        if (c + 1 < c1) {
-            stQ.load(Qh, row0 + C, N, tid);
-            if constexpr (CAUSAL) {
-                stK.load(Kh, row0 + C, N, tid);
-                stV.load(Vh, row0 + C, N, tid);
-            }
-        }
-
-        for (int rt = rgrp; rt < G::RT; rt += G::NWR) {
-            const int qrow = rt * 16 + l16;
-            f32x4 at[G::RT];
-            float den = 0.0f;
-            if constexpr (CAUSAL) {
-#pragma unroll
-                for (int kt = 0; kt < G::RT; ++kt) {
-                    at[kt] = zero4();
-                    if (kt <= rt) {
-                        f32x4 a = zero4();
-                        if constexpr (G::F32)
-                            a = tile_dot_f32<D>(sK + (kt * 16 + l16) * G::LQ, 1, sQ + qrow * G::LQ, 1, g, a);
-                        else
-                            a = tile_dot_bf16<D>(sK + (kt * 16 + l16) * G::LQ, sQ + qrow * G::LQ, g, a);
-                        // a[r] = A[query = rt*16 + l16][key = kt*16 + 4g + r]
-                        if (kt == rt) {
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (4 * g + r > l16) a[r] = 0.0f;
-                        }
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            a[r] = round_as<T>(a[r]);
-                            den += a[r];
-                        }
-                        at[kt] = a;
-                    }
-                }
-            }
-            {
-                const T *qr = sQ + qrow * G::LQ + g * (D / 4);
-                const float *zr = sz + g * (D / 4);
-#pragma unroll
-                for (int j = 0; j < D / 4; ++j) den += to_f32(qr[j]) * zr[j];
-            }
-            den = sum_over_groups(den);
-            const float inv = 1.0f / den;
-            float inv_r[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) inv_r[r] = __shfl(inv, 4 * g + r, 64);
-
-            for (int mt = mgrp; mt < G::MT; mt += G::NWM) {
-                f32x4 o = zero4();
-                if constexpr (CAUSAL) {
-                    if constexpr (G::F32) {
-#pragma unroll
-                        for (int kt = 0; kt < G::RT; ++kt) {
-                            if (kt <= rt) {
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    o = mma_f32(at[kt][r], sV[(kt * 16 + 4 * g + r) * G::LV + mt * 16 + l16], o);
-                            }
-                        }
-                    } else if constexpr (G::RT == 1) {
-                        bf16x4 a = {(bf16)at[0][0], (bf16)at[0][1], (bf16)at[0][2], (bf16)at[0][3]};
-                        bf16x4 b = *reinterpret_cast<const bf16x4 *>(sV + (mt * 16 + l16) * G::LT + 4 * g);
-                        o = mma_bf16_k16(a, b, o);
-                    } else {
-#pragma unroll
-                        for (int p = 0; p < G::RT / 2; ++p) {
-                            const int kt0 = 2 * p, kt1 = 2 * p + 1;
-                            if (kt0 <= rt) {
-                                const T *vrow = sV + (mt * 16 + l16) * G::LT;
-                                bf16x4 b0 = *reinterpret_cast<const bf16x4 *>(vrow + kt0 * 16 + 4 * g);
-                                bf16x4 b1 = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
-                                if (kt1 <= rt) b1 = *reinterpret_cast<const bf16x4 *>(vrow + kt1 * 16 + 4 * g);
-                                bf16x8 a = {(bf16)at[kt0][0], (bf16)at[kt0][1], (bf16)at[kt0][2], (bf16)at[kt0][3],
-                                            (bf16)at[kt1][0], (bf16)at[kt1][1], (bf16)at[kt1][2], (bf16)at[kt1][3]};
-                                bf16x8 b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-                                o = mma_bf16_k32(a, b, o);
-                            }
-                        }
-                    }
-                }
-                // inter-chunk term phi(Q_c) S
-                if constexpr (G::F32)
-                    o = tile_dot_f32<D>(sQ + qrow * G::LQ, 1, sS + mt * 16 + l16, G::LV, g, o);
-                else
-                    o = tile_dot_bf16<D>(sQ + qrow * G::LQ, sS + (mt * 16 + l16) * G::LQ, g, o);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int grow = row0 + rt * 16 + 4 * g + r;
-                    if (grow < N) Oh[(size_t)grow * M + mt * 16 + l16] = o[r] * inv_r[r];
-                }
-            }
-        }
-
-        if constexpr (CAUSAL) {
-            state_update<T, D, M, C>(acc, G::F32 ? sK : sKt, sV, w, g, l16);
-            z = z_update<T, D, M, C>(z, G::F32 ? sK : sKt, tid);
-        }
-        __syncthreads();
-        if constexpr (CAUSAL) state_to_lds<T, D, M, C>(acc, z, sS, sz, w, g, l16, tid);
-    }
-
-    if constexpr (CAUSAL) {
-        if (S_out != nullptr && s == G_ - 1)
-            state_to_global<T, D, M, C>(acc, z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D, w, g, l16, tid);
-    }
+    if (CAUSAL) e.clear_a();
+    Stage<T, C, D> stQ;
+    stQ.load(Qh, c0 * C, N, e.tid);
+    const bool fin = CAUSAL && S_out != nullptr && s == G_ - 1;
+    phase_b<T, D, M, C, CAUSAL>(e, Qh, K + (size_t)bh * N * D, V + (size_t)bh * N * M, out + (size_t)bh * N * M, N,
+                                c0, c1, false, fin, stQ, S, z, false);
+    if (fin) e.state_store(S, z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
 }
 
 // ---------------------------------------------------------------------------
 // Host-side launchers (instantiated per element type in la_prefill_*.hip).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C>
+hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
+                     int CPS, float *S_out, float *z_out, hipStream_t stream) {
+    using Gc = Cfg<T, D, M, C>;
+    if constexpr (!Gc::fits) {
+        return hipErrorInvalidValue;
+    } else {
+        if (BH <= 0 || G_ <= 0) return hipSuccess;
+        const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
+        hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C>), dim3(grid), dim3(kThreads), 0, stream, (const T *)Q,
+                           (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out);
+        return hipGetLastError();
+    }
+}
+
+template <typename T, int D, int M, int C>
 hipError_t run_states(const void *K, const void *V, float *ws, int BH, int N, int G_, int CPS, int nstates,
                       hipStream_t stream) {
-    using G = Cfg<T, D, M, C>;
-    if constexpr (!G::fits) {
+    using Gc = Cfg<T, D, M, C>;
+    if constexpr (!Gc::fits) {
         return hipErrorInvalidValue;
     } else {
         if (nstates <= 0 || BH <= 0) return hipSuccess;
@@ -523,8 +827,8 @@ hipError_t run_states(const void *K, const void *V, float *ws, int BH, int N, in
 template <typename T, int D, int M, int C>
 hipError_t run_outputs(const void *Q, const void *K, const void *V, float *out, const float *ws, int BH, int N,
                        int G_, int CPS, int causal, float *S_out, float *z_out, hipStream_t stream) {
-    using G = Cfg<T, D, M, C>;
-    if constexpr (!G::fits) {
+    using Gc = Cfg<T, D, M, C>;
+    if constexpr (!Gc::fits) {
         return hipErrorInvalidValue;
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;

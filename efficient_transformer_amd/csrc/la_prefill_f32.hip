@@ -25,6 +25,24 @@ hipError_t prefill_states_f32(int D, int M, int C, const void *K, const void *V,
     return hipErrorInvalidValue;
 }
 
+hipError_t prefill_fused_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
+                             int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream) {
+#define X(D_, M_, C_) \
+    if (D == D_ && M == M_ && C == C_) \
+        return run_fused<float, D_, M_, C_>(Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream);
+    LA_FOR_ALL(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+size_t prefill_lds_bytes_f32(int D, int M, int C) {
+#define X(D_, M_, C_) \
+    if (D == D_ && M == M_ && C == C_) return Cfg<float, D_, M_, C_>::bytes;
+    LA_FOR_ALL(X)
+#undef X
+    return 0;
+}
+
 hipError_t prefill_outputs_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
                                const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out,
                                float *z_out, hipStream_t stream) {

@@ -29,6 +29,9 @@ SIGNATURES = {
     "la_forward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int, _int, _int]),
     "la_forward_chunked": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _vp, _sz, _vp, _vp, _vp]),
+    "la_workspace_init": (_int, [_vp, _sz, _vp]),
+    "la_forward_fused": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz,
+                                _vp, _vp, _vp]),
     "la_segment_states": (_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
     "la_segment_scan": (_int, [_vp, _sz, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "la_segment_outputs": (_int, [_vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
@@ -126,11 +129,35 @@ def workspace_bytes(B, H, N, D, M, causal=True, dtype=LA_F32, chunk=0) -> int:
     return forward_plan(B, H, N, D, M, causal, dtype, chunk)[2]
 
 
+_ws_cache = {}
+
+
+def workspace_init(ws, stream=None):
+    """Zero a workspace before its first use (or before reuse with another plan)."""
+    _check(lib().la_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream, ws.device)),
+           "la_workspace_init")
+
+
+def _cached_workspace(nbytes, device, stream, key):
+    """A zero-initialised workspace kept per (device, stream, plan); calls with one plan on one
+    stream run in order, so they may share it."""
+    import torch
+    sid = (stream if stream is not None else torch.cuda.current_stream(device)).cuda_stream
+    k = (str(device), sid, key)
+    ws = _ws_cache.get(k)
+    if ws is None:
+        ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+        _ws_cache[k] = ws
+    return ws
+
+
 def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_out=None, z_out=None,
                     stream=None):
     """Parallel-mode attention: Q, K [B,H,N,D], V [B,H,N,M] (float32 or bfloat16) -> out [B,H,N,M] float32.
 
     With S_out [B,H,D,M] and z_out [B,H,D] (float32) the final state is written too.
+    A given `workspace` must have been zeroed (workspace_init) for this plan; by
+    default a cached, zeroed one is used.
     """
     import torch
     if Q.dim() != 4:
@@ -150,13 +177,40 @@ def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_o
     if S_out is not None:
         _require(S_out, "S_out", (B, H, D, M), torch.float32, dev)
         _require(z_out, "z_out", (B, H, D), torch.float32, dev)
-    need = workspace_bytes(B, H, N, D, M, causal, dt, chunk)
+    C, G, need = forward_plan(B, H, N, D, M, causal, dt, chunk)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _cached_workspace(need, dev, stream, ("chunked", B * H, N, D, M, bool(causal), dt, C, G))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().la_forward_chunked(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, int(bool(causal)), dt,
                                   chunk, _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
     _check(st, "la_forward_chunked")
+    return out
+
+
+def fused_workspace_bytes(B, H, D, M, segments) -> int:
+    if segments <= 1:
+        return 0
+    bhg = B * H * segments
+    return (64 + 64 * ((bhg + 63) // 64)) * 4 + 2 * bhg * (D * M + D) * 4
+
+
+def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None):
+    """The causal fused kernel with an explicit plan (chunk, segments)."""
+    import torch
+    B, H, N, D = Q.shape
+    M = V.shape[-1]
+    dev = Q.device
+    _require(K, "K", (B, H, N, D), Q.dtype, dev)
+    _require(V, "V", (B, H, N, M), Q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
+    need = fused_workspace_bytes(B, H, D, M, segments)
+    if workspace is None and need > 0:
+        workspace = _cached_workspace(need, dev, stream, ("fused", B * H, N, D, M, _dtype_code(Q), chunk, segments))
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().la_forward_fused(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(Q), chunk,
+                                segments, _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
+    _check(st, "la_forward_fused")
     return out
 
 

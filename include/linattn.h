@@ -87,12 +87,17 @@ LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_
 /*
  * Parallel-mode attention (prefill / training forward).
  *
- * causal = 1: out_i uses positions j <= i (diagonal included).
- * causal = 0: every out_i uses all N positions.
+ * causal = 1: out_i uses positions j <= i (diagonal included); one fused
+ *   kernel whose workgroups (one per segment) pass summed states forward with
+ *   a decoupled look-back.
+ * causal = 0: every out_i uses all N positions (three stage kernels).
  * out: [B][H][N][M] fp32, fully written.
- * workspace: device memory of at least la_forward_workspace_bytes(...) bytes,
- *   no initial contents required, clobbered by the call.  May be NULL when that
- *   size is 0.
+ * workspace: device memory of at least la_forward_workspace_bytes(...) bytes
+ *   (NULL allowed when that size is 0).  Causal calls keep counters and flags
+ *   in it: it must be zeroed (la_workspace_init) before its first use and
+ *   again before it is used with a different plan (B*H, N, D, M, dtype or
+ *   chunk); every completed call leaves it ready for the next call with the
+ *   same plan.  Calls that run concurrently must not share a workspace.
  * S_out [B][H][D][M], z_out [B][H][D]: optional (NULL to skip; both or neither);
  *   receive the final state S_{N-1}, z_{N-1}, so that la_decode_step can
  *   continue the sequence.
@@ -105,9 +110,26 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
                               void *workspace, size_t workspace_bytes,
                               float *S_out, float *z_out, void *stream);
 
+/* Zero a workspace (an enqueued fill kernel; graph-capture safe). bytes % 4 == 0. */
+LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
 /*
- * The three stages la_forward_chunked runs, exposed with an explicit plan
- * (chunk, segments), e.g. for a sequence sharded over devices: each device
+ * The causal fused kernel of la_forward_chunked with an explicit plan: chunk
+ * (16, 32 or 64) and segments (each segment must own at least one chunk).
+ * Workspace: 0 bytes when segments == 1, else
+ *   (64 + 64*ceil(B*H*segments/64)) * 4 + 2 * B*H*segments * (D*M + D) * 4 bytes,
+ * initialised as for la_forward_chunked.  S_out / z_out as for la_forward_chunked.
+ */
+LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out,
+                            int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                            int dtype, int chunk, int segments,
+                            void *workspace, size_t workspace_bytes,
+                            float *S_out, float *z_out, void *stream);
+
+/*
+ * The three stages of the non-causal path, usable for causal attention too,
+ * exposed with an explicit plan (chunk, segments) -- e.g. for a sequence
+ * sharded over devices: each device
  * runs la_segment_states on its shard, the per-shard states are exchanged, and
  * la_segment_outputs runs from the exchanged prefix.
  *

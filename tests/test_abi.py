@@ -31,7 +31,8 @@ def declared_symbols():
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("la_forward_chunked", "la_decode_step", "la_forward_workspace_bytes", "la_forward_plan",
-              "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version"):
+              "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version",
+              "la_forward_fused", "la_workspace_init"):
         assert s in syms
 
 
@@ -67,20 +68,20 @@ def test_plan_covers_the_sequence(L, B, H, N, D, M, causal, dtype, chunk):
     assert 1 <= G <= n_chunks
     assert (G - 1) * cps < n_chunks <= G * cps  # every segment owns at least one chunk
     E = D * M + D
-    if causal and G == 1:
-        assert ws == 0
+    if causal:
+        bhg = B * H * G
+        assert ws == (0 if G == 1 else (64 + 64 * ((bhg + 63) // 64)) * 4 + 2 * bhg * E * 4)
     else:
         assert ws == B * H * (G + 1) * E * 4
     assert L.workspace_bytes(B, H, N, D, M, causal, dtype, chunk) == ws
 
 
-def test_plan_fp32_large_state_uses_smaller_chunk(L):
-    # fp32 operands at D = M = 128 do not fit a 64-position chunk in LDS
-    C, _, _ = L.forward_plan(1, 1, 4096, 128, 128, 1, 0, 0)
-    assert C == 32
-    with pytest.raises(L.LinAttnError) as e:
-        L.forward_plan(1, 1, 4096, 128, 128, 1, 0, 64)
-    assert e.value.status == L.LA_ERR_UNSUPPORTED
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_plan_default_chunk(L, dtype):
+    for D in (16, 32, 64, 128):
+        for M in (16, 32, 64, 128):
+            C, _, _ = L.forward_plan(1, 1, 4096, D, M, 1, dtype, 0)
+            assert C == 64
 
 
 def _fwd(L, Q=None, K=None, V=None, out=None, B=1, H=1, N=64, D=16, M=16, causal=1, dtype=0, chunk=0,
@@ -139,6 +140,25 @@ def test_stage_entry_points_check_plans(L):
     assert lib.la_segment_scan(FAKE, 1 << 30, 2, 1, 64, 64, 2, 1, FAKE, None, None) == L.LA_ERR_INVALID_ARG
     assert lib.la_segment_outputs(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 2, 1, 256, 64, 64, 3, 0, 64, 2,
                                   None, None, None) == L.LA_ERR_INVALID_ARG
+
+
+def test_fused_entry_point_checks(L):
+    f = L.lib().la_forward_fused
+    need = L.fused_workspace_bytes(2, 2, 64, 64, 4)
+    # 1000 positions in chunks of 64: 16 chunks; 4 segments of 4 chunks
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, FAKE, need - 4, None, None, None) == L.LA_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 5, FAKE, 1 << 30, None, None,
+             None) == L.LA_ERR_UNSUPPORTED  # a segment would own no chunk
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 48, 4, FAKE, need, None, None, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 0, FAKE, need, None, None, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, FAKE + 4, need, None, None,
+             None) == L.LA_ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, FAKE, need, None, None, None) == L.LA_ERR_INVALID_ARG
+    w = L.lib().la_workspace_init
+    assert w(None, 0, None) == L.LA_OK
+    assert w(None, 64, None) == L.LA_ERR_INVALID_ARG
+    assert w(FAKE + 4, 64, None) == L.LA_ERR_INVALID_ARG
+    assert w(FAKE, 66, None) == L.LA_ERR_INVALID_ARG
 
 
 def test_product_path_never_imports_the_oracle():

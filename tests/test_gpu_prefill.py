@@ -172,32 +172,106 @@ def test_first_row_and_last_row(ea, dtype):
     assert err <= TOL[dtype], f"rowwise_rel {err:.3e}"
 
 
-def test_bitwise_repeatable(ea):
+def test_stage_path_bitwise_repeatable(ea):
+    """The three-stage path sums states in a fixed order: repeated calls agree bit for bit."""
     cfg = synthetic.CONFIGS["cfg3"]
     Q, K, V = synthetic.prefill_inputs(cfg, 1)
     Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
-    a = ea.forward_chunked(Qd, Kd, Vd)
-    b = ea.forward_chunked(Qd, Kd, Vd)
+    B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    C, G = 64, 12
+    ws = torch.empty(B * H * (G + 1) * (D * M + D) * 4, dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(2):
+        out = torch.empty((B, H, N, M), device=DEV)
+        ea.segment_states(Kd, Vd, ws, C, G, G - 1)
+        ea.segment_scan(ws, B, H, D, M, G, G - 1)
+        ea.segment_outputs(Qd, Kd, Vd, out, ws, C, G)
+        outs.append(out)
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_fused_repeat_on_one_workspace(ea):
+    """Consecutive causal calls reuse one workspace (its epoch advances each call); the
+    look-back may sum the prefix in a different order, so results agree to rounding."""
+    cfg = synthetic.CONFIGS["cfg3"]
+    Q, K, V = synthetic.prefill_inputs(cfg, 1)
+    Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
+    ref = oracle.causal(f64(Q, "bf16"), f64(K, "bf16"), f64(V, "bf16"))[0]
+    B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    nbytes = max(ea.fused_workspace_bytes(B, H, D, M, 24), ea.fused_workspace_bytes(B, H, D, M, 48))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    ea.workspace_init(ws)
+    outs = [ea.forward_fused(Qd, Kd, Vd, 64, 24, workspace=ws) for _ in range(4)]
+    torch.cuda.synchronize()
+    for o in outs:
+        err = rowwise_rel(o.cpu().numpy(), ref)
+        assert err <= TOL["bf16"], f"{err:.3e}"
+    err = rowwise_rel(outs[3].cpu().numpy(), outs[0].cpu().numpy())
+    assert err <= 1e-2, f"{err:.3e}"
+    # the same memory with another plan, after re-initialisation
+    ea.workspace_init(ws)
+    outs = [ea.forward_fused(Qd, Kd, Vd, 32, 48, workspace=ws) for _ in range(2)]
+    torch.cuda.synchronize()
+    for o in outs:
+        err = rowwise_rel(o.cpu().numpy(), ref)
+        assert err <= TOL["bf16"], f"{err:.3e}"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_stages_equal_forward(ea, dtype):
+@pytest.mark.parametrize("chunk,segments", [(64, 1), (64, 2), (64, 3), (64, 16), (32, 32), (16, 63), (16, 21)])
+def test_fused_segments(ea, dtype, chunk, segments):
+    """The fused causal kernel over explicit segment counts, with the final state."""
+    B, H, N, D, M = 2, 2, 1000, 64, 32
+    cfg = small_cfg(dtype, B, H, N, D, M)
+    Q, K, V = synthetic.prefill_inputs(cfg, 8)
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    S = torch.full((B, H, D, M), float("nan"), device=DEV)
+    z = torch.full((B, H, D), float("nan"), device=DEV)
+    out = ea.forward_fused(Qd, Kd, Vd, chunk, segments, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    ref, S_ref, z_ref = oracle.causal(f64(Q, dtype), f64(K, dtype), f64(V, dtype))
+    err = rowwise_rel(out.cpu().numpy(), ref)
+    assert err <= TOL[dtype], f"out {err:.3e}"
+    stol = 1e-5 if dtype == "f32" else TOL["bf16"]
+    err = whole_rel(S.cpu().numpy(), S_ref)
+    assert err <= stol, f"S {err:.3e}"
+    err = whole_rel(z.cpu().numpy(), z_ref)
+    assert err <= stol, f"z {err:.3e}"
+
+
+def test_fused_long_lookback(ea):
+    """Many short segments per head: long look-back chains."""
+    B, H, N, D, M = 1, 3, 8192, 32, 32
+    cfg = small_cfg("f32", B, H, N, D, M)
+    Q, K, V = synthetic.prefill_inputs(cfg, 9)
+    Qd, Kd, Vd = to_dev(Q, "f32"), to_dev(K, "f32"), to_dev(V, "f32")
+    out = ea.forward_fused(Qd, Kd, Vd, 16, 512)
+    torch.cuda.synchronize()
+    ref = oracle.causal(f64(Q, "f32"), f64(K, "f32"), f64(V, "f32"))[0]
+    err = rowwise_rel(out.cpu().numpy(), ref)
+    assert err <= TOL["f32"], f"{err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stages_match_oracle(ea, dtype):
+    """The three stage kernels run by hand, and the fused default, both against the oracle."""
     from efficient_transformer_amd import linattn as L
     cfg = small_cfg(dtype, 2, 2, 1000, 64, 64)
     Q, K, V = synthetic.prefill_inputs(cfg, 5)
     Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
-    code = L.LA_F32 if dtype == "f32" else L.LA_BF16
-    C, G, wsb = ea.forward_plan(2, 2, 1000, 64, 64, True, code, 0)
-    ref = ea.forward_chunked(Qd, Kd, Vd)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
-    out = torch.empty_like(ref)
+    C, G = 64, 4
+    ws = torch.empty(2 * 2 * (G + 1) * (64 * 64 + 64) * 4, dtype=torch.uint8, device=DEV)
+    out = torch.empty((2, 2, 1000, 64), device=DEV)
     ea.segment_states(Kd, Vd, ws, C, G, G - 1)
     ea.segment_scan(ws, 2, 2, 64, 64, G, G - 1)
     ea.segment_outputs(Qd, Kd, Vd, out, ws, C, G)
+    fused = ea.forward_chunked(Qd, Kd, Vd)
     torch.cuda.synchronize()
-    assert torch.equal(out, ref)
+    ref = oracle.causal(f64(Q, dtype), f64(K, dtype), f64(V, dtype))[0]
+    for got in (out, fused):
+        err = rowwise_rel(got.cpu().numpy(), ref)
+        assert err <= TOL[dtype], f"{err:.3e}"
 
 
 @pytest.mark.parametrize("segments", [1, 2, 3, 4, 6, 16])
