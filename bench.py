@@ -76,8 +76,8 @@ def make_prefill_sets(cfg, nsets, dev):
     return sets
 
 
-def bench_prefill(cfg, steps, warmup, dev, kernel_timing=True):
-    """Returns a dict of timings for one prefill workload."""
+def bench_prefill(cfg, steps, warmup, dev):
+    """Timings of one causal prefill workload (la_forward_chunked: one fused kernel per call)."""
     import torch
     import efficient_transformer_amd as ea
     from efficient_transformer_amd import linattn as L
@@ -88,7 +88,7 @@ def bench_prefill(cfg, steps, warmup, dev, kernel_timing=True):
     nbytes = prefill_bytes(cfg)
     nsets = max(1, math.ceil(1.25 * LLC_BYTES / nbytes))
     sets = make_prefill_sets(cfg, nsets, dev)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # zeroed once; each call leaves it ready
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
@@ -105,32 +105,19 @@ def bench_prefill(cfg, steps, warmup, dev, kernel_timing=True):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    res = dict(chunk=C, segments=G, nsets=nsets, ms_per_step=ms, tokens_per_s=B * N / (ms * 1e-3),
-               bytes=nbytes, flops_min=prefill_flops_min(cfg))
-    if kernel_timing:
-        # Same work through the stage entry points, with events around the launches of
-        # each stage kernel (all on `stream`, the stream the library launches on).
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-        for i in range(steps + warmup):
-            Q, K, V, out = sets[i % nsets]
-            e = ev[i - warmup] if i >= warmup else None
-            if e: e[0].record(stream)
-            if G > 1:
-                ea.segment_states(K, V, ws, C, G, G - 1, stream=stream)
-            if e: e[1].record(stream)
-            if G > 1:
-                ea.segment_scan(ws, B, H, D, M, G, G - 1, stream=stream)
-            if e: e[2].record(stream)
-            ea.segment_outputs(Q, K, V, out, ws, C, G, causal=True, stream=stream)
-            if e: e[3].record(stream)
-        torch.cuda.synchronize()
-        t_state = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-        t_scan = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-        t_out = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
-        res.update(us_state=t_state * 1e3, us_scan=t_scan * 1e3, us_output=t_out * 1e3)
+    # kernel duration: HIP events around every launch (the library enqueues one
+    # kernel per causal call on `stream`)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us_kernel = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
     del sets
     torch.cuda.empty_cache()
-    return res
+    return dict(chunk=C, segments=G, nsets=nsets, ms_per_step=ms, tokens_per_s=B * N / (ms * 1e-3),
+                bytes=nbytes, flops_min=prefill_flops_min(cfg), us_kernel=us_kernel)
 
 
 def bench_decode(cfg, reps, dev, warm_steps=64):
@@ -231,11 +218,11 @@ def main():
     log(f"prefill {cfg}")
     pre = bench_prefill(cfg, args.steps, args.warmup, dev)
     log(f"prefill: {pre}")
-    kernel_us = pre["us_output"]
+    kernel_us = pre["us_kernel"]
     achieved = pre["bytes"] / (kernel_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    kernel=f"seg_output_kernel<float,{cfg['D']},{cfg['M']},{pre['chunk']},causal>",
+                    kernel=f"fused_causal_kernel<float,{cfg['D']},{cfg['M']},{pre['chunk']}>",
                     kernel_us=round(kernel_us, 2), algorithmic_bytes=pre["bytes"],
                     mfma_fp32_frac_at_min_flops=round(pre["flops_min"] / (kernel_us * 1e-6) / 1e12
                                                       / FP32_MFMA_PEAK_TFS, 4))
@@ -258,8 +245,6 @@ def main():
                    "chunk": pre["chunk"], "segments": pre["segments"], "buffer_sets": pre["nsets"],
                    "parallelism": "single GPU"},
         "roofline": roofline,
-        "stages_us": {"segment_states": round(pre["us_state"], 2), "segment_scan": round(pre["us_scan"], 2),
-                      "segment_outputs": round(pre["us_output"], 2)},
     }
 
     if not args.no_extras:
@@ -285,10 +270,9 @@ def main():
                 "workload": f"causal prefill bf16 in, fp32 out, B={c['B']} H={c['H']} N={c['N']} D=M={c['D']}",
                 "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
                 "chunk": r["chunk"], "segments": r["segments"],
-                "step_GBs": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
-                "frac_hbm_peak_step": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "stages_us": {"segment_states": round(r["us_state"], 2), "segment_scan": round(r["us_scan"], 2),
-                              "segment_outputs": round(r["us_output"], 2)}}
+                "kernel_us": round(r["us_kernel"], 2),
+                "kernel_GBs": round(r["bytes"] / (r["us_kernel"] * 1e-6) / 1e9, 1),
+                "frac_hbm_peak_kernel": round(r["bytes"] / (r["us_kernel"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         line["other_workloads"] = others
 
     if not args.no_cpu_baseline:

@@ -47,11 +47,11 @@ struct Cfg {
     static constexpr int RT = C / 16, DT = D / 16, MT = M / 16;
     static constexpr int MTW = (MT + kWaves - 1) / kWaves;  // m-tiles per wavefront
     static constexpr int NA = RT * (RT + 1) / 2;            // lower-triangle tiles of A
-    static constexpr int PAD = F32 ? 4 : 8;
+    static constexpr int PAD = F32 ? 12 : 8;
     static constexpr int LQ = D + PAD;  // rows of phi(Q), phi(K)
     static constexpr int LA = C + PAD;  // rows of A
     static constexpr int LV = M + PAD;  // fp32: rows of V
-    static constexpr int LT = C + PAD;  // bf16: rows of V^T and phi(K)^T
+    static constexpr int LT = C;        // bf16: rows of V^T and phi(K)^T (swizzled, see tsw)
     static constexpr int E = D * M + D; // floats of one state (S then z)
     static constexpr int NZP = kThreads / D;  // column-sum partial groups
     static constexpr int ZROWS = C / NZP;     // rows per partial
@@ -84,6 +84,17 @@ struct Cfg {
 //       the transposed store can write four keys of one column at once.
 // Rows at or beyond N are stored as zeros (after phi, so they add nothing).
 // ---------------------------------------------------------------------------
+// Element offset of `key` within a row of a transposed bf16 tile (unpadded rows of
+// C keys).  Keys are grouped in octets (16 bytes); octet o of row r is stored at
+// position o ^ ((r / 8) ^ r) mod (C / 8).  The staging writes (one column j of
+// sixteen row blocks: rows 8*cv + j) and the MFMA operand reads (sixteen
+// consecutive rows, one octet each) then spread over the LDS banks.
+template <int C>
+__device__ __forceinline__ int tsw(int row, int key) {
+    constexpr int mask = C / 8 - 1;
+    return ((((key >> 3) ^ (row >> 3) ^ row) & mask) << 3) | (key & 7);
+}
+
 template <typename T, int C, int W>
 struct Stage {
     static constexpr bool F32 = std::is_same<T, float>::value;
@@ -102,17 +113,25 @@ struct Stage {
                 const int rq = item / NV, cv = item % NV;
 #pragma unroll
                 for (int i = 0; i < RPI; ++i) {
-                    const int grow = row0 + rq * RPI + i;
-                    r[p][i] = grow < N ? *reinterpret_cast<const uint4 *>(head + (size_t)grow * W + cv * VEC)
-                                       : make_uint4(0u, 0u, 0u, 0u);
+                    // rows past the end re-read the last row (no branch); the stores zero them
+                    const int grow = min(row0 + rq * RPI + i, N - 1);
+                    r[p][i] = *reinterpret_cast<const uint4 *>(head + (size_t)grow * W + cv * VEC);
                 }
             }
         }
     }
 
-    // natural layout dst[row][col], optionally through phi
+    // natural layout dst[row][col], optionally through phi.  Rows at or past N
+    // (only in the last chunk) are zeroed; full chunks take a branch-free path.
     template <bool PHI>
     __device__ __forceinline__ void store_natural(T *dst, int ld, int row0, int N, int tid) const {
+        if (row0 + C <= N)
+            store_natural_impl<PHI, false>(dst, ld, row0, N, tid);
+        else
+            store_natural_impl<PHI, true>(dst, ld, row0, N, tid);
+    }
+    template <bool PHI, bool TAIL>
+    __device__ __forceinline__ void store_natural_impl(T *dst, int ld, int row0, int N, int tid) const {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int item = tid + p * kThreads;
@@ -121,12 +140,12 @@ struct Stage {
 #pragma unroll
                 for (int i = 0; i < RPI; ++i) {
                     const int row = rq * RPI + i;
-                    const bool ok = row0 + row < N;
+                    const float keep = (!TAIL || row0 + row < N) ? 1.0f : 0.0f;
                     if constexpr (F32) {
                         f32x4 x = __builtin_bit_cast(f32x4, r[p][i]);
                         f32x4 y;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) y[j] = ok ? (PHI ? phi(x[j]) : x[j]) : 0.0f;
+                        for (int j = 0; j < 4; ++j) y[j] = (PHI ? phi(x[j]) : x[j]) * keep;
                         *reinterpret_cast<f32x4 *>(dst + row * ld + cv * 4) = y;
                     } else {
                         bf16x8 x = __builtin_bit_cast(bf16x8, r[p][i]);
@@ -134,7 +153,7 @@ struct Stage {
 #pragma unroll
                         for (int j = 0; j < 8; ++j) {
                             const float f = (float)x[j];
-                            y[j] = (bf16)(ok ? (PHI ? phi(f) : f) : 0.0f);
+                            y[j] = (bf16)((PHI ? phi(f) : f) * keep);
                         }
                         *reinterpret_cast<bf16x8 *>(dst + row * ld + cv * 8) = y;
                     }
@@ -147,6 +166,14 @@ struct Stage {
     template <bool PHI, bool ALSO_NATURAL>
     __device__ __forceinline__ void store_transposed(T *dst_t, int ldt, T *dst_n, int ldn, int row0, int N,
                                                      int tid) const {
+        if (row0 + C <= N)
+            store_transposed_impl<PHI, ALSO_NATURAL, false>(dst_t, ldt, dst_n, ldn, row0, N, tid);
+        else
+            store_transposed_impl<PHI, ALSO_NATURAL, true>(dst_t, ldt, dst_n, ldn, row0, N, tid);
+    }
+    template <bool PHI, bool ALSO_NATURAL, bool TAIL>
+    __device__ __forceinline__ void store_transposed_impl(T *dst_t, int ldt, T *dst_n, int ldn, int row0, int N,
+                                                          int tid) const {
         static_assert(!F32, "transposed staging is for bf16 operands");
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
@@ -156,12 +183,12 @@ struct Stage {
                 bf16x8 y[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool ok = row0 + rq * 4 + i < N;
+                    const float keep = (!TAIL || row0 + rq * 4 + i < N) ? 1.0f : 0.0f;
                     bf16x8 x = __builtin_bit_cast(bf16x8, r[p][i]);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         const float f = (float)x[j];
-                        y[i][j] = (bf16)(ok ? (PHI ? phi(f) : f) : 0.0f);
+                        y[i][j] = (bf16)((PHI ? phi(f) : f) * keep);
                     }
                     if constexpr (ALSO_NATURAL)
                         *reinterpret_cast<bf16x8 *>(dst_n + (rq * 4 + i) * ldn + cv * 8) = y[i];
@@ -169,7 +196,8 @@ struct Stage {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     bf16x4 t = {y[0][j], y[1][j], y[2][j], y[3][j]};
-                    *reinterpret_cast<bf16x4 *>(dst_t + (cv * 8 + j) * ldt + rq * 4) = t;
+                    const int row = cv * 8 + j;
+                    *reinterpret_cast<bf16x4 *>(dst_t + row * ldt + tsw<C>(row, rq * 4)) = t;
                 }
             }
         }
@@ -179,8 +207,8 @@ struct Stage {
 
 // ---------------------------------------------------------------------------
 // Workspace of the fused kernel (fp32 words):
-//   header (64 words): [0] ticket counter, [1] finished-workgroup counter,
-//                      [2] epoch, [3] error flag (look-back gave up)
+//   header (64 words): [1] finished-workgroup counter, [2] epoch,
+//                      [3] error flag (look-back gave up)
 //   flags  [BH][G] (uint32, padded to 64 words): epoch << 2 | 1 aggregate ready,
 //                                                epoch << 2 | 2 inclusive ready
 //   aggregate states [BH][G][E], inclusive states [BH][G][E]
@@ -256,7 +284,7 @@ struct Engine {
     // Column sums of phi(K_c): partial sums over ZROWS rows into szp[q][d].
     __device__ __forceinline__ void z_partials() const {
         const int q = tid / D, d = tid % D;
-        if (q < G::NZP) {
+        if (G::NZP * D == kThreads || q < G::NZP) {
             float s = 0.0f;
 #pragma unroll
             for (int r = 0; r < G::ZROWS; ++r) s += to_f32(sK[(q * G::ZROWS + r) * G::LQ + d]);
@@ -291,12 +319,33 @@ struct Engine {
 #pragma unroll
             for (int i = 0; i < MTW; ++i) {
                 if (!owns(i)) continue;
-                const T *vrow = sV + (mtile(i) * 16 + l16) * G::LT;
+                const int vr = mtile(i) * 16 + l16;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
-                    acc[dt][i] = tile_dot_bf16<C>(sKt + (dt * 16 + l16) * G::LT, vrow, g, acc[dt][i]);
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int kr = dt * 16 + l16;
+                    acc[dt][i] = dot_t(sKt + kr * G::LT, kr, sV + vr * G::LT, vr, acc[dt][i]);
+                }
             }
         }
+    }
+
+    // bf16: acc += A B over the C keys of two transposed (swizzled) rows: lane reads
+    // row `ra` of A and row `rb` of B, contraction slots = keys.
+    __device__ __forceinline__ f32x4 dot_t(const T *a, int ra, const T *b, int rb, f32x4 acc) const {
+        if constexpr (C % 32 == 0) {
+#pragma unroll
+            for (int ks = 0; ks < C / 32; ++ks) {
+                const int key = ks * 32 + 8 * g;
+                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + tsw<C>(ra, key));
+                const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + tsw<C>(rb, key));
+                acc = mma_bf16_k32(av, bv, acc);
+            }
+        } else {
+            const bf16x4 av = *reinterpret_cast<const bf16x4 *>(a + tsw<C>(ra, 4 * g));
+            const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(b + tsw<C>(rb, 4 * g));
+            acc = mma_bf16_k16(av, bv, acc);
+        }
+        return acc;
     }
 
     // Lower-triangle tiles of A (tile t = w, w+4, ... in row-major order of (rt, kt<=rt)),
@@ -369,30 +418,18 @@ struct Engine {
         return 1.0f / den;
     }
 
-    // out rows of the chunk for the own m-tiles: (A V_c + phi(Q_c) S) * inv
-    // (non-causal: phi(Q_c) S * inv with S the total state).
-    template <bool CAUSAL>
-    __device__ __forceinline__ void outputs(const f32x4 (&S)[DT][MTW], float inv, float *__restrict__ Oh, int row0,
-                                            int N, bool poison) const {
-        // bf16 copies of the state for the read-out operands
-        [[maybe_unused]] bf16x4 Sb[DT][MTW];
-        if constexpr (!G::F32) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int i = 0; i < MTW; ++i)
-                    Sb[dt][i] = bf16x4{(bf16)S[dt][i][0], (bf16)S[dt][i][1], (bf16)S[dt][i][2], (bf16)S[dt][i][3]};
-        }
+    // Output tiles of the chunk for the own m-tiles.  Each MFMA takes the V / S side
+    // as its A operand and the A / phi(Q) side as its B operand, so a result tile is
+    // out^T: lane (g, l16) holds out[query rt*16 + l16][m*16 + 4g .. +3], four
+    // consecutive columns, stored with one 16-byte write.
+    //   intra():   o += (A V_c)^T           (needs sA, V; not the earlier state)
+    //   readout(): o += (phi(Q_c) S)^T, then o * inv -> out   (S from registers)
+    __device__ __forceinline__ void intra(f32x4 (&o)[RT][MTW]) const {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int qrow = rt * 16 + l16;
-            f32x4 o[MTW];
-#pragma unroll
-            for (int i = 0; i < MTW; ++i) o[i] = zero4();
-            // intra-chunk term A V_c over keys 0 .. 16(rt+1)-1
-            if constexpr (!CAUSAL) {
-            } else if constexpr (G::F32) {
-                const int nsteps = 4 * (rt + 1);  // keys per lane group
+            if constexpr (G::F32) {
+                const int nsteps = 4 * (rt + 1);  // keys per lane group: g*nsteps .. (g+1)*nsteps-1
                 const float *arow = sA + qrow * G::LA + g * nsteps;
 #pragma unroll
                 for (int j4 = 0; j4 < rt + 1; ++j4) {
@@ -402,31 +439,41 @@ struct Engine {
                         const int key = g * nsteps + 4 * j4 + j;
 #pragma unroll
                         for (int i = 0; i < MTW; ++i)
-                            if (owns(i)) o[i] = mma_f32(av[j], sV[key * G::LV + mtile(i) * 16 + l16], o[i]);
+                            if (owns(i)) o[rt][i] = mma_f32(sV[key * G::LV + mtile(i) * 16 + l16], av[j], o[rt][i]);
                     }
                 }
             } else if constexpr (RT == 1) {
-                const bf16x4 av = *reinterpret_cast<const bf16x4 *>(sA + qrow * G::LA + 4 * g);
+                const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(sA + qrow * G::LA + 4 * g);
 #pragma unroll
                 for (int i = 0; i < MTW; ++i) {
                     if (!owns(i)) continue;
-                    const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(sV + (mtile(i) * 16 + l16) * G::LT + 4 * g);
-                    o[i] = mma_bf16_k16(av, bv, o[i]);
+                    const int vr = mtile(i) * 16 + l16;
+                    const bf16x4 av = *reinterpret_cast<const bf16x4 *>(sV + vr * G::LT + tsw<C>(vr, 4 * g));
+                    o[rt][i] = mma_bf16_k16(av, bv, o[rt][i]);
                 }
             } else {
 #pragma unroll
                 for (int kk = 0; kk < (rt + 2) / 2; ++kk) {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(sA + qrow * G::LA + kk * 32 + 8 * g);
+                    const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(sA + qrow * G::LA + kk * 32 + 8 * g);
 #pragma unroll
                     for (int i = 0; i < MTW; ++i) {
                         if (!owns(i)) continue;
-                        const bf16x8 bv =
-                            *reinterpret_cast<const bf16x8 *>(sV + (mtile(i) * 16 + l16) * G::LT + kk * 32 + 8 * g);
-                        o[i] = mma_bf16_k32(av, bv, o[i]);
+                        const int vr = mtile(i) * 16 + l16;
+                        const bf16x8 av =
+                            *reinterpret_cast<const bf16x8 *>(sV + vr * G::LT + tsw<C>(vr, kk * 32 + 8 * g));
+                        o[rt][i] = mma_bf16_k32(av, bv, o[rt][i]);
                     }
                 }
             }
-            // inter-chunk term phi(Q_c) S with S from registers:
+        }
+    }
+
+    __device__ __forceinline__ void readout(f32x4 (&o)[RT][MTW], const f32x4 (&S)[DT][MTW], float inv,
+                                            float *__restrict__ Oh, int row0, int N, bool poison) const {
+        const bool full = row0 + C <= N;  // uniform: no per-row bounds checks needed
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int qrow = rt * 16 + l16;
             // contraction slot of lane (g, l16) at step (dt, r) is d = dt*16 + 4g + r
             if constexpr (G::F32) {
 #pragma unroll
@@ -436,13 +483,16 @@ struct Engine {
                     for (int r = 0; r < 4; ++r)
 #pragma unroll
                         for (int i = 0; i < MTW; ++i)
-                            if (owns(i)) o[i] = mma_f32(qv[r], S[dt][i][r], o[i]);
+                            if (owns(i)) o[rt][i] = mma_f32(S[dt][i][r], qv[r], o[rt][i]);
                 }
             } else if constexpr (DT == 1) {
                 const bf16x4 qv = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + 4 * g);
 #pragma unroll
-                for (int i = 0; i < MTW; ++i)
-                    if (owns(i)) o[i] = mma_bf16_k16(qv, Sb[0][i], o[i]);
+                for (int i = 0; i < MTW; ++i) {
+                    if (!owns(i)) continue;
+                    const bf16x4 sb = {(bf16)S[0][i][0], (bf16)S[0][i][1], (bf16)S[0][i][2], (bf16)S[0][i][3]};
+                    o[rt][i] = mma_bf16_k16(sb, qv, o[rt][i]);
+                }
             } else {
 #pragma unroll
                 for (int p = 0; p < DT / 2; ++p) {
@@ -452,27 +502,34 @@ struct Engine {
 #pragma unroll
                     for (int i = 0; i < MTW; ++i) {
                         if (!owns(i)) continue;
-                        const bf16x4 s0 = Sb[2 * p][i], s1 = Sb[2 * p + 1][i];
-                        const bf16x8 sv = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-                        o[i] = mma_bf16_k32(qv, sv, o[i]);
+                        const f32x4 s0 = S[2 * p][i], s1 = S[2 * p + 1][i];
+                        const bf16x8 sv = {(bf16)s0[0], (bf16)s0[1], (bf16)s0[2], (bf16)s0[3],
+                                           (bf16)s1[0], (bf16)s1[1], (bf16)s1[2], (bf16)s1[3]};
+                        o[rt][i] = mma_bf16_k32(sv, qv, o[rt][i]);
                     }
                 }
             }
-            // normalise and store: lane holds rows rt*16 + 4g + r, column mt*16 + l16
-            float inv_r[4];
+            // normalise and store
+            const float inv_q = __shfl(inv, qrow, 64);
+            const int grow = row0 + qrow;
+            if (full || grow < N) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) inv_r[r] = __shfl(inv, rt * 16 + 4 * g + r, 64);
+                for (int i = 0; i < MTW; ++i) {
+                    if (!owns(i)) continue;
+                    f32x4 v;
 #pragma unroll
-            for (int i = 0; i < MTW; ++i) {
-                if (!owns(i)) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int grow = row0 + rt * 16 + 4 * g + r;
-                    if (grow < N)
-                        Oh[(size_t)grow * M + mtile(i) * 16 + l16] = poison ? __builtin_nanf("") : o[i][r] * inv_r[r];
+                    for (int r = 0; r < 4; ++r) v[r] = poison ? __builtin_nanf("") : o[rt][i][r] * inv_q;
+                    *reinterpret_cast<f32x4 *>(Oh + (size_t)grow * M + mtile(i) * 16 + 4 * g) = v;
                 }
             }
         }
+    }
+
+    __device__ __forceinline__ static void zero_out(f32x4 (&o)[RT][MTW]) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) o[rt][i] = zero4();
     }
 
     // ---- state slots ([D][M] row major, then z[D]) <-> register layout ----
@@ -501,6 +558,86 @@ struct Engine {
             }
         if (tid < D) z += slot[D * M + tid];
     }
+    // Agent-coherent variants for the states exchanged between workgroups: every
+    // access carries the agent scope (write-through stores, loads that miss
+    // stale cache lines), so no cache-wide write-back or invalidate is needed.
+    __device__ __forceinline__ void state_store_coherent(const f32x4 (&acc)[DT][MTW], float z, float *slot) const {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) {
+                if (!owns(i)) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __hip_atomic_store(slot + (dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16, acc[dt][i][r],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        if (tid < D) __hip_atomic_store(slot + D * M + tid, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ __forceinline__ void state_add_coherent(f32x4 (&acc)[DT][MTW], float &z, const float *slot) const {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < MTW; ++i) {
+                if (!owns(i)) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[dt][i][r] += __hip_atomic_load(slot + (dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        if (tid < D) z += __hip_atomic_load(slot + D * M + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // pre += *first + agg[j0] + ... + agg[j1-1] (slots of E floats), coherent loads
+    // issued NB slots at a time so that their latencies overlap; fixed order.
+    __device__ __forceinline__ void state_add_slots(f32x4 (&acc)[DT][MTW], float &z, const float *first,
+                                                    const float *agg, int j0, int j1) const {
+        constexpr int PER = DT * MTW * 4;
+        constexpr int NB = PER <= 16 ? 4 : (PER <= 32 ? 2 : 1);
+        state_add_coherent(acc, z, first);
+        for (int jb = j0; jb < j1; jb += NB) {
+            float t[NB][PER];
+            float tz[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const float *slot = agg + (size_t)(jb + k < j1 ? jb + k : jb) * G::E;
+                int n = 0;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r, ++n)
+                            t[k][n] = owns(i) ? __hip_atomic_load(slot + (dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16,
+                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                              : 0.0f;
+                tz[k] = tid < D ? __hip_atomic_load(slot + D * M + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                if (jb + k >= j1) break;
+                int n = 0;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < MTW; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r, ++n) acc[dt][i][r] += t[k][n];
+                z += tz[k];
+            }
+        }
+    }
+
+    // Publish: wait until this wave's coherent stores are complete, then let one
+    // thread raise the flag once every wave of the workgroup has done so.
+    __device__ __forceinline__ void publish_flag(unsigned *flag, unsigned value) const {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
     __device__ __forceinline__ static void zero_state(f32x4 (&acc)[DT][MTW]) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -511,64 +648,74 @@ struct Engine {
 
 // ---------------------------------------------------------------------------
 // Phase A: sum the state over chunks [c0, c1) into acc / z (thread tid < D owns z[tid]).
-// Leaves the last chunk's phi(K), V in LDS.
+// Leaves the last chunk's phi(K), V in LDS.  Global loads run two chunks ahead
+// (two register buffers, used alternately).
 // ---------------------------------------------------------------------------
+template <typename T, int D, int M, int C>
+struct KVBuf {
+    Stage<T, C, D> k;
+    Stage<T, C, M> v;
+    __device__ __forceinline__ void load(const T *Kh, const T *Vh, int c, int N, int tid) {
+        k.load(Kh, c * C, N, tid);
+        v.load(Vh, c * C, N, tid);
+    }
+};
+
 template <typename T, int D, int M, int C>
 __device__ __forceinline__ void phase_a(const Engine<T, D, M, C> &e, const T *__restrict__ Kh,
                                         const T *__restrict__ Vh, int N, int c0, int c1,
                                         f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z) {
-    Stage<T, C, D> stK;
-    Stage<T, C, M> stV;
-    stK.load(Kh, c0 * C, N, e.tid);
-    stV.load(Vh, c0 * C, N, e.tid);
-    for (int c = c0; c < c1; ++c) {
-        const int row0 = c * C;
+    KVBuf<T, D, M, C> b0, b1;
+    b0.load(Kh, Vh, c0, N, e.tid);
+    if (c0 + 1 < c1) b1.load(Kh, Vh, c0 + 1, N, e.tid);
+    auto step = [&](KVBuf<T, D, M, C> &b, int c) {
         __syncthreads();  // LDS free (previous chunk's readers are done)
-        e.store_kv(stK, stV, row0, N);
+        e.store_kv(b.k, b.v, c * C, N);
         __syncthreads();
-        if (c + 1 < c1) {
-            stK.load(Kh, row0 + C, N, e.tid);
-            stV.load(Vh, row0 + C, N, e.tid);
-        }
+        if (c + 2 < c1) b.load(Kh, Vh, c + 2, N, e.tid);
         e.z_partials();
         e.state_update(acc);
         __syncthreads();
         if (e.tid < D) z += e.z_delta();
+    };
+    for (int c = c0; c < c1; c += 2) {
+        step(b0, c);
+        if (c + 1 < c1) step(b1, c + 1);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Phase B: outputs of chunks [c0, c1) starting from the state (S, z) of all
-// earlier positions.  kv_staged: chunk c0's phi(K), V are already in LDS.
-// advance_last: also advance the state over the last chunk (for the final state).
+// earlier positions.  q0 already holds (or is loading) chunk c0's Q.
+// kv_staged: chunk c0's phi(K), V are already in LDS.  advance_last: also
+// advance the state over the last chunk (for the final state).  Loads run two
+// chunks ahead.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C, bool CAUSAL>
 __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__restrict__ Qh,
                                         const T *__restrict__ Kh, const T *__restrict__ Vh,
                                         float *__restrict__ Oh, int N, int c0, int c1, bool kv_staged,
-                                        bool advance_last, Stage<T, C, D> &stQ,
+                                        bool advance_last, Stage<T, C, D> &q0,
                                         f32x4 (&S)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z,
                                         bool poison) {
-    Stage<T, C, D> stK;
-    Stage<T, C, M> stV;
-    if (CAUSAL && !kv_staged) {
-        stK.load(Kh, c0 * C, N, e.tid);
-        stV.load(Vh, c0 * C, N, e.tid);
+    Stage<T, C, D> q1;
+    KVBuf<T, D, M, C> b0, b1;
+    if (CAUSAL && !kv_staged) b0.load(Kh, Vh, c0, N, e.tid);
+    if (c0 + 1 < c1) {
+        q1.load(Qh, (c0 + 1) * C, N, e.tid);
+        if (CAUSAL) b1.load(Kh, Vh, c0 + 1, N, e.tid);
     }
-    for (int c = c0; c < c1; ++c) {
+    auto step = [&](Stage<T, C, D> &q, KVBuf<T, D, M, C> &b, int c) {
         const int row0 = c * C;
         const bool stage_kv = CAUSAL && !(kv_staged && c == c0);
         __syncthreads();  // LDS free
-        e.store_q(stQ, row0, N);
-        if (stage_kv) e.store_kv(stK, stV, row0, N);
+        e.store_q(q, row0, N);
+        if (stage_kv) e.store_kv(b.k, b.v, row0, N);
         if (e.tid < D) e.sz[e.tid] = round_as<T>(z);
         __syncthreads();
-        if (c + 1 < c1) {
-            stQ.load(Qh, row0 + C, N, e.tid);
-            if (CAUSAL) {
-                stK.load(Kh, row0 + C, N, e.tid);
-                stV.load(Vh, row0 + C, N, e.tid);
-            }
+        if (c + 2 < c1) {
+            q.load(Qh, (c + 2) * C, N, e.tid);
+            if (CAUSAL) b.load(Kh, Vh, c + 2, N, e.tid);
         }
         if (CAUSAL) e.a_tiles();
         e.qz_rows();
@@ -576,55 +723,51 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__
         if (adv) e.z_partials();
         __syncthreads();
         const float inv = e.template row_inv<CAUSAL>();
-        e.template outputs<CAUSAL>(S, inv, Oh, row0, N, poison);
+        f32x4 o[Cfg<T, D, M, C>::RT][Cfg<T, D, M, C>::MTW];
+        Engine<T, D, M, C>::zero_out(o);
+        if (CAUSAL) e.intra(o);
+        e.readout(o, S, inv, Oh, row0, N, poison);
         if (adv) {
             e.state_update(S);
             if (e.tid < D) z += e.z_delta();
         }
+    };
+    for (int c = c0; c < c1; c += 2) {
+        step(q0, b0, c);
+        if (c + 1 < c1) step(q1, b1, c + 1);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Fused causal kernel: phase A, decoupled look-back over segments, phase B.
-// Workgroups take tickets in launch order; ticket t -> segment t / BH of head
-// t % BH, so a workgroup only waits on segments with smaller tickets, which
-// are running or finished.  With G == 1 there is no look-back and no workspace.
+// With G == 1 there is no look-back and no workspace.
 // ---------------------------------------------------------------------------
 constexpr long kSpinLimit = 1L << 22;
 
 template <typename T, int D, int M, int C>
-__global__ __launch_bounds__(kThreads) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+__global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                 const T *__restrict__ V, float *__restrict__ out,
                                                                 void *ws_raw, int BH, int N, int G_, int CPS,
                                                                 float *__restrict__ S_out, float *__restrict__ z_out) {
     using Gc = Cfg<T, D, M, C>;
+    using En = Engine<T, D, M, C>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
     __shared__ unsigned sh_word[2];
-    Engine<T, D, M, C> e(smem);
+    En e(smem);
     const int tid = e.tid;
 
-    int bh, s;
+    // Work item: block b -> segment b / BH of head b % BH.  Workgroups are
+    // dispatched in block order, so a workgroup only ever waits on segments of
+    // smaller block index, which are resident or finished; the waits are also
+    // bounded (kSpinLimit) and a timeout poisons the outputs instead of hanging.
+    const int bh = (int)(blockIdx.x % (unsigned)BH);
+    const int s = (int)(blockIdx.x / (unsigned)BH);
     unsigned epoch = 0;
     FusedWs ws(ws_raw, BH, G_ > 1 ? G_ : 1, Gc::E);
     if (G_ > 1) {
-        if (tid == 0) {
-            sh_word[0] = atomicAdd(&ws.hdr[0], 1u);
-            sh_word[1] = __hip_atomic_load(&ws.hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (tid == 0) sh_word[1] = __hip_atomic_load(&ws.hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        const unsigned t = sh_word[0];
         epoch = sh_word[1];
-        __syncthreads();  // sh_word is reused below
-        if (t >= (unsigned)(BH * G_)) {
-            // counters not reset by an earlier failed call: report and do nothing
-            if (tid == 0) __hip_atomic_store(&ws.hdr[3], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return;
-        }
-        s = (int)(t / (unsigned)BH);
-        bh = (int)(t % (unsigned)BH);
-    } else {
-        bh = blockIdx.x;
-        s = 0;
     }
     const unsigned ep = (epoch & 0x3fffffffu) << 2;
 
@@ -638,62 +781,88 @@ __global__ __launch_bounds__(kThreads) void fused_causal_kernel(const T *__restr
     e.clear_a();
 
     f32x4 acc[Gc::DT][Gc::MTW];
-    Engine<T, D, M, C>::zero_state(acc);
+    En::zero_state(acc);
     float zacc = 0.0f;
     const bool last = s == G_ - 1;
     const bool want_final = S_out != nullptr;
     const bool run_a = G_ > 1 && (!last || want_final);
     if (run_a) phase_a<T, D, M, C>(e, Kh, Vh, N, c0, c1, acc, zacc);
+    const size_t my = (size_t)bh * G_ + s;
+    // publish the segment aggregate before any other load is in flight (the
+    // publication waits for every outstanding memory operation of the wave)
+    if (G_ > 1 && !last) {
+        e.state_store_coherent(acc, zacc, ws.agg + my * Gc::E);
+        e.publish_flag(&ws.flags[my], ep | 1u);
+    }
 
     Stage<T, C, D> stQ;
     stQ.load(Qh, c0 * C, N, tid);
 
+    // A one-chunk segment still holds its phi(K), V in LDS: form A and the
+    // intra-chunk term now, while earlier segments may still be publishing.
+    f32x4 o[Gc::RT][Gc::MTW];
+    En::zero_out(o);
+    const bool single = run_a && (c1 - c0 == 1);
+    if (single) {
+        e.store_q(stQ, c0 * C, N);
+        __syncthreads();
+        e.a_tiles();
+        __syncthreads();
+        e.intra(o);
+    }
+
     f32x4 pre[Gc::DT][Gc::MTW];
-    Engine<T, D, M, C>::zero_state(pre);
+    En::zero_state(pre);
     float zpre = 0.0f;
     bool failed = false;
-    if (G_ > 1) {
-        const size_t my = (size_t)bh * G_ + s;
-        if (!last) {
-            // publish the segment aggregate
-            e.state_store(acc, zacc, ws.agg + my * Gc::E);
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) __hip_atomic_store(&ws.flags[my], ep | 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // look back: sum aggregates of s-1, s-2, ... until an inclusive prefix
-        for (int j = s - 1; j >= 0; --j) {
-            const size_t other = (size_t)bh * G_ + j;
-            if (tid == 0) {
-                unsigned st = 0;
-                long spins = 0;
-                while (true) {
-                    const unsigned f = __hip_atomic_load(&ws.flags[other], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-                    if ((f & ~3u) == ep && (f & 3u) != 0) {
-                        st = f & 3u;
+    if (G_ > 1 && s > 0) {
+        // Look back: wavefront 0 polls the flags of segments s-1, s-2, ... (one
+        // lane per segment, 64 at a time, relaxed loads) until it finds the
+        // nearest segment j* whose inclusive prefix is published (segment 0's
+        // aggregate is its inclusive prefix) with every aggregate between j*
+        // and s ready.  The prefix is then incl(j*) + agg(j*+1) + ... + agg(s-1).
+        if (e.w == 0) {
+            const unsigned *fl = ws.flags + (size_t)bh * G_;
+            int base = s - 1;
+            int jstar = -1;
+            long spins = 0;
+            while (true) {
+                const int j = base - e.lane;
+                unsigned f = 0u;
+                if (j >= 0) f = __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool ok = j >= 0 && (f & ~3u) == ep && (f & 3u) != 0u;
+                const bool inc = ok && ((f & 3u) == 2u || j == 0);
+                const unsigned long long okm = __ballot(ok), incm = __ballot(inc);
+                if (incm != 0ull) {
+                    const int first = __builtin_ctzll(incm);
+                    const unsigned long long need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
+                    if ((okm & need) == need) {
+                        jstar = base - first;
                         break;
                     }
-                    if (++spins > kSpinLimit) {
-                        st = 0;
-                        __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
+                } else if (okm == ~0ull) {
+                    base -= 64;  // 64 aggregates ready, none inclusive: look further back
+                    continue;
                 }
-                sh_word[0] = st;
+                if (++spins > kSpinLimit) {
+                    if (e.lane == 0) __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    jstar = -1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
             }
-            __syncthreads();
-            const unsigned st = sh_word[0];
-            __threadfence();
-            if (st == 0) {
-                failed = true;
-                break;
-            }
-            e.state_add(pre, zpre, (st == 2u ? ws.incl : ws.agg) + other * Gc::E);
-            __syncthreads();  // sh_word reuse
-            if (st == 2u) break;
+            if (e.lane == 0) sh_word[0] = (unsigned)(jstar + 1);
         }
-        if (!last && s > 0) {
+        __syncthreads();
+        const int jstar = (int)sh_word[0] - 1;
+        if (jstar < 0) {
+            failed = true;
+        } else {
+            const size_t h0 = (size_t)bh * G_;
+            e.state_add_slots(pre, zpre, (jstar == 0 ? ws.agg : ws.incl) + (h0 + jstar) * Gc::E,
+                              ws.agg + h0 * Gc::E, jstar + 1, s);
+        }
+        if (!last) {
             // publish the inclusive prefix (segment 0's aggregate already is one)
             f32x4 inc[Gc::DT][Gc::MTW];
             const float nan = __builtin_nanf("");
@@ -704,36 +873,39 @@ __global__ __launch_bounds__(kThreads) void fused_causal_kernel(const T *__restr
                     inc[dt][i] = pre[dt][i] + acc[dt][i];
                     if (failed) inc[dt][i] = f32x4{nan, nan, nan, nan};
                 }
-            e.state_store(inc, failed ? nan : zpre + zacc, ws.incl + my * Gc::E);
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) __hip_atomic_store(&ws.flags[my], ep | 2u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (last && want_final) {
-            f32x4 fin[Gc::DT][Gc::MTW];
-#pragma unroll
-            for (int dt = 0; dt < Gc::DT; ++dt)
-#pragma unroll
-                for (int i = 0; i < Gc::MTW; ++i) fin[dt][i] = pre[dt][i] + acc[dt][i];
-            e.state_store(fin, zpre + zacc, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+            e.state_store_coherent(inc, failed ? nan : zpre + zacc, ws.incl + my * Gc::E);
+            e.publish_flag(&ws.flags[my], ep | 2u);
         }
     }
+    if (G_ > 1 && last && want_final) {
+        f32x4 fin[Gc::DT][Gc::MTW];
+#pragma unroll
+        for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < Gc::MTW; ++i) fin[dt][i] = pre[dt][i] + acc[dt][i];
+        e.state_store(fin, zpre + zacc, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+    }
 
-    // phase B from the prefix; with a single-chunk segment phase A left K, V in LDS
-    const bool kv_staged = run_a && (c1 - c0 == 1);
-    phase_b<T, D, M, C, true>(e, Qh, Kh, Vh, Oh, N, c0, c1, kv_staged, G_ == 1 && want_final, stQ, pre, zpre,
-                              failed);
-
-    if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+    if (single) {
+        // the rest of the one-chunk segment: normaliser and the inter-chunk term
+        if (tid < D) e.sz[tid] = round_as<T>(zpre);
+        __syncthreads();
+        e.qz_rows();
+        __syncthreads();
+        const float inv = e.template row_inv<true>();
+        e.readout(o, pre, inv, Oh, c0 * C, N, failed);
+    } else {
+        phase_b<T, D, M, C, true>(e, Qh, Kh, Vh, Oh, N, c0, c1, false, G_ == 1 && want_final, stQ, pre, zpre,
+                                  failed);
+        if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+    }
 
     if (G_ > 1) {
         // the last workgroup to finish resets the counters and advances the epoch
-        __threadfence();
         __syncthreads();
         if (tid == 0) {
             const unsigned done = atomicAdd(&ws.hdr[1], 1u);
             if (done == (unsigned)(BH * G_) - 1u) {
-                __hip_atomic_store(&ws.hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(&ws.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(&ws.hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -764,7 +936,7 @@ __global__ __launch_bounds__(kThreads) void seg_state_kernel(const T *__restrict
 }
 
 template <typename T, int D, int M, int C, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+__global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                               const T *__restrict__ V, float *__restrict__ out,
                                                               const float *__restrict__ ws, int N, int G_, int CPS,
                                                               float *__restrict__ S_out, float *__restrict__ z_out) {
