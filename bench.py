@@ -36,6 +36,31 @@ LLC_BYTES = 256 << 20       # Infinity Cache
 METRIC = "causal linear-attention tokens/sec (prefill, decode) and % of MFMA/HBM roofline"
 
 
+def csrc_sha256_16() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "efficient_transformer_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(summary: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", summary)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch: ", "csrc_sha256_16: ")))
+    if fields.get("csrc_sha256_16", "").strip() != csrc_sha256_16():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -191,6 +216,34 @@ def cpu_baseline(cfg, target_s=12.0):
                        f"fp32 workload ({el:.1f} s wall, fp64, {threads} threads)")
 
 
+def profile_run(dev):
+    """Untimed launches for counter collection: 4 headline prefill calls, 4 decode steps and
+    4 copies of a 512 MiB fp32 buffer (known traffic: 512 MiB read + 512 MiB written each)."""
+    import torch
+    import efficient_transformer_amd as ea
+    import synthetic
+    cfg = dict(synthetic.CONFIGS["cfg2"])
+    sets = make_prefill_sets(cfg, 1, dev)
+    Q, K, V, out = sets[0]
+    for _ in range(4):
+        ea.forward_chunked(Q, K, V, causal=True, out=out)
+    d = dict(synthetic.CONFIGS["cfg5"])
+    B, H, D, M = d["B"], d["H"], d["D"], d["M"]
+    S = torch.zeros((B, H, D, M), device=dev)
+    z = torch.zeros((B, H, D), device=dev)
+    q = synthetic.draw_torch(0, synthetic.TID_DQ, (B, H, D), 1.0, "f32", dev)
+    k = synthetic.draw_torch(0, synthetic.TID_DK, (B, H, D), 1.0, "f32", dev)
+    v = synthetic.draw_torch(0, synthetic.TID_DV, (B, H, M), 1.0, "f32", dev)
+    for _ in range(4):
+        ea.decode_step(S, z, q, k, v)
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("profile run done")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +251,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline prefill workload")
+    ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
+                    help="profile: a few untimed launches of the headline kernel, of the decode kernel and of a "
+                         "plain 512 MiB device copy (for hardware-counter runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -214,6 +270,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.mode == "profile":
+        profile_run(dev)
+        return
+
     cfg = dict(synthetic.CONFIGS["cfg2"])
     log(f"prefill {cfg}")
     pre = bench_prefill(cfg, args.steps, args.warmup, dev)
@@ -221,7 +281,8 @@ def main():
     kernel_us = pre["us_kernel"]
     achieved = pre["bytes"] / (kernel_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4),
+                    traffic=measured_traffic("prefill_fused_f32_B8H8N1024_D64M64.md"),
                     kernel=f"fused_causal_kernel<float,{cfg['D']},{cfg['M']},{pre['chunk']}>",
                     kernel_us=round(kernel_us, 2), algorithmic_bytes=pre["bytes"],
                     mfma_fp32_frac_at_min_flops=round(pre["flops_min"] / (kernel_us * 1e-6) / 1e12

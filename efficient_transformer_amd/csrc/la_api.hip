@@ -46,12 +46,11 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
     if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
     int C = 0;
     if (chunk_req == 0) {
-        for (int c : {64, 32, 16}) {
-            if (la::prefill_supported(dtype, (int)D, (int)M, c)) {
-                C = c;
-                break;
-            }
-        }
+        // fp32 operands with a small state run 32-position chunks (less masked
+        // quadratic work per position on the slower fp32 MFMA); otherwise 64
+        C = (dtype == LA_F32 && D * M <= 4096) ? 32 : 64;
+        if (!la::prefill_supported(dtype, (int)D, (int)M, C)) C = 32;
+        if (!la::prefill_supported(dtype, (int)D, (int)M, C)) C = 16;
     } else if (chunk_req == 16 || chunk_req == 32 || chunk_req == 64) {
         C = chunk_req;
     } else {
@@ -68,12 +67,13 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
         return LA_OK;
     }
     const int64_t n_chunks = (N + C - 1) / C;
-    // Causal: one workgroup per segment, fused kernel with a look-back across
-    // segments.  Segments are as short as possible (one chunk: phase B reuses the
-    // chunk phase A staged) while the grid stays within a few waves of the 256
-    // compute units; longer sequences get several chunks per segment.
+    // One workgroup per segment; all workgroups of a call resident at once: 256
+    // compute units times the workgroups that fit on one (two when the state is
+    // at most 64 x 64, one otherwise).  Segments are whole chunks; every segment
+    // carries (D*M + D) floats of published state, so fewer, longer segments.
+    // Causal: the fused kernel (look-back across segments).
     // Non-causal: the three stage kernels, with segments sized the same way.
-    const int64_t target_wg = 1024;
+    const int64_t target_wg = (D * M <= 4096) ? 512 : 256;
     int64_t cps = (n_chunks * BH + target_wg - 1) / target_wg;
     if (cps < 1) cps = 1;
     int64_t G = (n_chunks + cps - 1) / cps;
