@@ -222,12 +222,12 @@ def profile_run(dev):
     import torch
     import efficient_transformer_amd as ea
     import synthetic
-    cfg = dict(synthetic.CONFIGS["cfg2"])
+    cfg = dict(synthetic.WORKLOADS["prefill_f32_b8h8_n1024_d64"])
     sets = make_prefill_sets(cfg, 1, dev)
     Q, K, V, out = sets[0]
     for _ in range(4):
         ea.forward_chunked(Q, K, V, causal=True, out=out)
-    d = dict(synthetic.CONFIGS["cfg5"])
+    d = dict(synthetic.WORKLOADS["decode_f32_256x8_t4096_d64"])
     B, H, D, M = d["B"], d["H"], d["D"], d["M"]
     S = torch.zeros((B, H, D, M), device=dev)
     z = torch.zeros((B, H, D), device=dev)
@@ -274,7 +274,7 @@ def main():
         profile_run(dev)
         return
 
-    cfg = dict(synthetic.CONFIGS["cfg2"])
+    cfg = dict(synthetic.WORKLOADS["prefill_f32_b8h8_n1024_d64"])
     log(f"prefill {cfg}")
     pre = bench_prefill(cfg, args.steps, args.warmup, dev)
     log(f"prefill: {pre}")
@@ -309,7 +309,7 @@ def main():
     }
 
     if not args.no_extras:
-        dcfg = dict(synthetic.CONFIGS["cfg5"])
+        dcfg = dict(synthetic.WORKLOADS["decode_f32_256x8_t4096_d64"])
         log("decode ...")
         dec = bench_decode(dcfg, 3, dev)
         log(f"decode: {dec}")
@@ -322,8 +322,8 @@ def main():
             "bytes_per_step": dec["bytes_per_step"],
             "note": "the 34 MB state stays resident in the 256 MB last-level cache between steps"}
         others = {}
-        for name in ("cfg3", "cfg4"):
-            c = dict(synthetic.CONFIGS[name])
+        for name in ("prefill_bf16_b4h8_n3072_d64", "prefill_bf16_b1h16_n65536_d128"):
+            c = dict(synthetic.WORKLOADS[name])
             log(f"prefill {name} ...")
             r = bench_prefill(c, max(10, args.steps // 4), 5, dev)
             log(f"{name}: {r}")
@@ -338,7 +338,7 @@ def main():
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        line["cpu_baseline"] = cpu_baseline(dict(synthetic.CONFIGS["cfg2"]))
+        line["cpu_baseline"] = cpu_baseline(dict(synthetic.WORKLOADS["prefill_f32_b8h8_n1024_d64"]))
     print(json.dumps(line), flush=True)
 
 

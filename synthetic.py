@@ -122,13 +122,13 @@ def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(x, dtype=np.float32).astype(np.float64)
 
 
-# The five workloads (shapes and distributions of the pages' experiments, i.i.d. content).
-CONFIGS = {
-    "cfg1": dict(kind="prefill", B=1, H=1, N=64, D=16, M=16, sigma=1.0, dtype="f32", chunk=16),
-    "cfg2": dict(kind="prefill", B=8, H=8, N=1024, D=64, M=64, sigma=1.0, dtype="f32", chunk=0),
-    "cfg3": dict(kind="prefill", B=4, H=8, N=3072, D=64, M=64, sigma=0.5, dtype="bf16", chunk=0),
-    "cfg4": dict(kind="prefill", B=1, H=16, N=65536, D=128, M=128, sigma=1.0, dtype="bf16", chunk=0),
-    "cfg5": dict(kind="decode", B=256, H=8, T=4096, D=64, M=64, sigma=1.0, dtype="f32"),
+# The five workloads, named by what they are (shapes and distributions of the pages experiments, i.i.d. content).
+WORKLOADS = {
+    "prefill_f32_n64_d16": dict(kind="prefill", B=1, H=1, N=64, D=16, M=16, sigma=1.0, dtype="f32", chunk=16),
+    "prefill_f32_b8h8_n1024_d64": dict(kind="prefill", B=8, H=8, N=1024, D=64, M=64, sigma=1.0, dtype="f32", chunk=0),
+    "prefill_bf16_b4h8_n3072_d64": dict(kind="prefill", B=4, H=8, N=3072, D=64, M=64, sigma=0.5, dtype="bf16", chunk=0),
+    "prefill_bf16_b1h16_n65536_d128": dict(kind="prefill", B=1, H=16, N=65536, D=128, M=128, sigma=1.0, dtype="bf16", chunk=0),
+    "decode_f32_256x8_t4096_d64": dict(kind="decode", B=256, H=8, T=4096, D=64, M=64, sigma=1.0, dtype="f32"),
 }
 
 

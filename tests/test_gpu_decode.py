@@ -117,9 +117,9 @@ def test_decode_resume_is_bitwise(ea):
     assert torch.equal(S, S3) and torch.equal(z, z3)
 
 
-def test_cfg5_sampled(ea):
+def test_decode_256x8_t4096_sampled(ea):
     """Full decode workload (256 streams x 8 heads, 4096 steps); 16 sampled heads against the oracle."""
-    cfg = synthetic.CONFIGS["cfg5"]
+    cfg = synthetic.WORKLOADS["decode_f32_256x8_t4096_d64"]
     B, H, D, M, T = cfg["B"], cfg["H"], cfg["D"], cfg["M"], cfg["T"]
     BH = B * H
     rng = np.random.default_rng(0)
@@ -147,7 +147,7 @@ def test_cfg5_sampled(ea):
     zo = np.zeros((len(heads), D))
     ref = np.stack([oracle.decode_step(So, zo, q[t], k[t], v[t]) for t in range(T)])
     err = rowwise_rel(got, ref)
-    print(f"cfg5 sampled row-wise rel err {err:.3e}")
+    print(f"256x8 t4096 sampled row-wise rel err {err:.3e}")
     assert err <= TOL["f32"], f"{err:.3e}"
     err = whole_rel(S.view(BH, D, M)[hidx].cpu().numpy(), So)
     assert err <= 1e-5, f"whole_rel {err:.3e} > {1e-5}"

@@ -51,8 +51,8 @@ def small_cfg(dtype, B, H, N, D, M, sigma=1.0):
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
-def test_cfg1_parity(ea, seed):
-    cfg = synthetic.CONFIGS["cfg1"]
+def test_prefill_f32_n64_d16_parity(ea, seed):
+    cfg = synthetic.WORKLOADS["prefill_f32_n64_d16"]
     (Q, K, V), out = run_prefill(ea, cfg, seed)
     ref, _, _ = oracle.causal(f64(Q, "f32"), f64(K, "f32"), f64(V, "f32"))
     err = rowwise_rel(out, ref)
@@ -106,27 +106,27 @@ def test_empty_sequence_writes_zero_state(ea):
     assert torch.count_nonzero(S).item() == 0 and torch.count_nonzero(z).item() == 0
 
 
-def test_cfg2_full(ea):
-    cfg = synthetic.CONFIGS["cfg2"]
+def test_prefill_f32_b8h8_n1024_full(ea):
+    cfg = synthetic.WORKLOADS["prefill_f32_b8h8_n1024_d64"]
     (Q, K, V), out = run_prefill(ea, cfg, 0)
     ref, _, _ = oracle.causal(f64(Q, "f32"), f64(K, "f32"), f64(V, "f32"))
     err = rowwise_rel(out, ref)
-    print(f"cfg2 row-wise rel err {err:.3e}")
+    print(f"b8h8 n1024 row-wise rel err {err:.3e}")
     assert err <= TOL["f32"], f"{err:.3e}"
 
 
-def test_cfg3_full(ea):
-    cfg = synthetic.CONFIGS["cfg3"]
+def test_prefill_bf16_b4h8_n3072_full(ea):
+    cfg = synthetic.WORKLOADS["prefill_bf16_b4h8_n3072_d64"]
     (Q, K, V), out = run_prefill(ea, cfg, 0)
     ref, _, _ = oracle.causal(f64(Q, "bf16"), f64(K, "bf16"), f64(V, "bf16"))
     err = rowwise_rel(out, ref)
-    print(f"cfg3 row-wise rel err {err:.3e}")
+    print(f"b4h8 n3072 row-wise rel err {err:.3e}")
     assert err <= TOL["bf16"], f"{err:.3e}"
 
 
-def test_cfg4_sampled(ea):
+def test_prefill_bf16_n65536_d128_sampled(ea):
     """Full-size long-sequence run; two whole heads by the recurrence, sampled rows of the rest."""
-    cfg = synthetic.CONFIGS["cfg4"]
+    cfg = synthetic.WORKLOADS["prefill_bf16_b1h16_n65536_d128"]
     (Q, K, V), out = run_prefill(ea, cfg, 0)
     Q, K, V = Q[0], K[0], V[0]
     out = out[0]
@@ -134,7 +134,7 @@ def test_cfg4_sampled(ea):
     ref, _, _ = oracle.causal(f64(Q[heads], "bf16"), f64(K[heads], "bf16"), f64(V[heads], "bf16"))
     for i, h in enumerate(heads):
         err = rowwise_rel(out[h], ref[i])
-        print(f"cfg4 head {h} row-wise rel err {err:.3e}")
+        print(f"n65536 head {h} row-wise rel err {err:.3e}")
         assert err <= TOL["bf16"], f"{err:.3e}"
     rng = np.random.default_rng(0)
     N = cfg["N"]
@@ -174,7 +174,7 @@ def test_first_row_and_last_row(ea, dtype):
 
 def test_stage_path_bitwise_repeatable(ea):
     """The three-stage path sums states in a fixed order: repeated calls agree bit for bit."""
-    cfg = synthetic.CONFIGS["cfg3"]
+    cfg = synthetic.WORKLOADS["prefill_bf16_b4h8_n3072_d64"]
     Q, K, V = synthetic.prefill_inputs(cfg, 1)
     Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
     B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
@@ -194,7 +194,7 @@ def test_stage_path_bitwise_repeatable(ea):
 def test_fused_repeat_on_one_workspace(ea):
     """Consecutive causal calls reuse one workspace (its epoch advances each call); the
     look-back may sum the prefix in a different order, so results agree to rounding."""
-    cfg = synthetic.CONFIGS["cfg3"]
+    cfg = synthetic.WORKLOADS["prefill_bf16_b4h8_n3072_d64"]
     Q, K, V = synthetic.prefill_inputs(cfg, 1)
     Qd, Kd, Vd = to_dev(Q, "bf16"), to_dev(K, "bf16"), to_dev(V, "bf16")
     ref = oracle.causal(f64(Q, "bf16"), f64(K, "bf16"), f64(V, "bf16"))[0]

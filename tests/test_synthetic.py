@@ -42,7 +42,7 @@ def test_bf16_round_to_nearest_even_matches_torch():
 
 
 def test_decode_head_subset_matches_full_draw():
-    cfg = dict(synthetic.CONFIGS["cfg5"], B=4, H=2)
+    cfg = dict(synthetic.WORKLOADS["decode_f32_256x8_t4096_d64"], B=4, H=2)
     q, k, v = synthetic.decode_step_inputs(cfg, 0, step=5)
     qs, ks, vs = synthetic.decode_step_inputs(cfg, 0, step=5, heads=[1, 6])
     assert np.array_equal(qs, q.reshape(8, -1)[[1, 6]])
@@ -50,7 +50,7 @@ def test_decode_head_subset_matches_full_draw():
 
 
 def test_prefill_head_rows_match_full_draw():
-    cfg = dict(synthetic.CONFIGS["cfg3"], B=1, H=2, N=50)
+    cfg = dict(synthetic.WORKLOADS["prefill_bf16_b4h8_n3072_d64"], B=1, H=2, N=50)
     Q, K, V = synthetic.prefill_inputs(cfg, seed=2)
     rows = synthetic.prefill_head_rows(cfg, 2, synthetic.TID_V, bh=1, n0=10, n1=20, width=cfg["M"])
     assert np.array_equal(rows, V[0, 1, 10:20])
