@@ -9,6 +9,7 @@ from .linattn import (  # noqa: F401
     decode_step,
     forward_chunked,
     forward_fused,
+    forward_onepass,
     forward_plan,
     fused_workspace_bytes,
     lib_path,

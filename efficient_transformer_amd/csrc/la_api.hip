@@ -17,6 +17,7 @@ struct Plan {
     int segments = 0;
     int chunks_per_segment = 0;
     int nstates = 0;  // segment states the causal/non-causal path computes
+    bool onepass = false;  // causal: one-pass kernel (segments of at most 4 chunks)
     size_t ws_bytes = 0;
 };
 
@@ -85,6 +86,7 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
     const int E = (int)(D * M + D);
     if (causal) {
         plan->nstates = 0;
+        plan->onepass = cps <= la::kOnePassMaxChunks && la::prefill_onepass_supported(dtype, (int)D, (int)M, C);
         plan->ws_bytes = G == 1 ? 0 : la::fused_ws_bytes(BH, (int)G, E);
     } else {
         plan->nstates = (int)G;
@@ -155,7 +157,9 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
     const int dt = dtype, Di = (int)D, Mi = (int)M, C = p.chunk, G = p.segments, cps = p.chunks_per_segment;
     (void)hipGetLastError();  // clear a stale error so that the checks below report this call's launches
     hipError_t e = hipSuccess;
-    if (causal) {
+    if (causal && p.onepass) {
+        e = la::prefill_onepass(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out, s);
+    } else if (causal) {
         e = la::prefill_fused(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out, s);
     } else {
         float *ws = static_cast<float *>(workspace);
@@ -202,13 +206,16 @@ int cps_of(int64_t N, int chunk, int segments) {
 }
 }  // namespace
 
-LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                            int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
-                            size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+namespace {
+// Shared validation and launch of the two explicit-plan causal entry points.
+int forward_explicit(bool onepass, const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                     int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
+                     size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
     int st = check_shape(B, H, N, D, M, dtype);
     if (st != LA_OK) return st;
     if (chunk != 16 && chunk != 32 && chunk != 64) return LA_ERR_UNSUPPORTED;
     if (!la::prefill_supported(dtype, (int)D, (int)M, chunk)) return LA_ERR_UNSUPPORTED;
+    if (onepass && !la::prefill_onepass_supported(dtype, (int)D, (int)M, chunk)) return LA_ERR_UNSUPPORTED;
     if (segments < 1) return LA_ERR_INVALID_ARG;
     if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
     if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
@@ -217,6 +224,7 @@ LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *
         const int64_t n_chunks = (N + chunk - 1) / chunk;
         const int64_t cps = (n_chunks + segments - 1) / segments;
         if ((int64_t)(segments - 1) * cps >= n_chunks) return LA_ERR_UNSUPPORTED;
+        if (onepass && cps > la::kOnePassMaxChunks) return LA_ERR_UNSUPPORTED;
     }
     if (BH * segments > INT_MAX / 256) return LA_ERR_UNSUPPORTED;
     const size_t need = segments > 1 ? la::fused_ws_bytes(BH, segments, (int)(D * M + D)) : 0;
@@ -233,8 +241,26 @@ LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *
     if (!Q || !K || !V || !out) return LA_ERR_INVALID_ARG;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    return hip_status(la::prefill_fused(dtype, (int)D, (int)M, chunk, Q, K, V, out, workspace, (int)BH, (int)N,
-                                        segments, cps_of(N, chunk, segments), S_out, z_out, s));
+    const int cps = cps_of(N, chunk, segments);
+    return hip_status(onepass ? la::prefill_onepass(dtype, (int)D, (int)M, chunk, Q, K, V, out, workspace, (int)BH,
+                                                    (int)N, segments, cps, S_out, z_out, s)
+                              : la::prefill_fused(dtype, (int)D, (int)M, chunk, Q, K, V, out, workspace, (int)BH,
+                                                  (int)N, segments, cps, S_out, z_out, s));
+}
+}  // namespace
+
+LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                            int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
+                            size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+    return forward_explicit(false, Q, K, V, out, B, H, N, D, M, dtype, chunk, segments, workspace, workspace_bytes,
+                            S_out, z_out, stream);
+}
+
+LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                              int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
+                              size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+    return forward_explicit(true, Q, K, V, out, B, H, N, D, M, dtype, chunk, segments, workspace, workspace_bytes,
+                            S_out, z_out, stream);
 }
 
 LA_API int la_segment_states(const void *K, const void *V, float *ws, size_t ws_bytes, int64_t B, int64_t H,

@@ -22,6 +22,7 @@ namespace la {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 using bf16 = __bf16;
 
 // phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (page "Transformers are

@@ -27,6 +27,11 @@ hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const 
                            hipStream_t stream);
 hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
                          void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+// One-pass causal kernel: segments of at most 4 chunks (see la_prefill.hpp).
+constexpr int kOnePassMaxChunks = 4;
+bool prefill_onepass_supported(int dtype, int D, int M, int C);
+hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                           void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
 size_t prefill_lds_bytes(int dtype, int D, int M, int C);
 hipError_t prefill_scan(float *ws, int BH, int D, int M, int G, int nstates, float *S_out, float *z_out,
                         hipStream_t stream);
@@ -40,6 +45,13 @@ hipError_t prefill_fused_f32(int D, int M, int C, const void *Q, const void *K, 
                              int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
 hipError_t prefill_fused_bf16(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
                               int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+hipError_t prefill_onepass_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                               void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+hipError_t prefill_onepass_bf16(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                                void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out,
+                                hipStream_t stream);
+bool prefill_onepass_supported_f32(int D, int M, int C);
+bool prefill_onepass_supported_bf16(int D, int M, int C);
 size_t prefill_lds_bytes_f32(int D, int M, int C);
 size_t prefill_lds_bytes_bf16(int D, int M, int C);
 bool prefill_supported_f32(int D, int M, int C);

@@ -11,13 +11,16 @@
 //   den = rowsum(A) + phi(Q_c) z                  (C)
 //   out = num / den
 //   S  += phi(K_c)^T V_c ;  z += colsum(phi(K_c))
-// A workgroup (4 wavefronts) owns one segment.  Phase A sums its segment's
-// state; the states are chained across segments by an exclusive prefix
-// (published per segment, decoupled look-back in the fused kernel); phase B
-// walks the segment's chunks from the prefix and writes the outputs.
+// A workgroup owns one segment.  In the two-phase fused kernel, phase A sums
+// the segment's state; the states are chained across segments by an
+// exclusive prefix (published per segment, decoupled look-back); phase B
+// walks the segment's chunks from the prefix and writes the outputs.  The
+// one-pass kernel (segments of at most four chunks) reads the segment once and
+// applies the prefix after the look-back.
 //
-// Work split inside a workgroup: wavefront w owns the output / state columns
-// m-tiles {w, w+4, ...}.  It keeps S[:, its m-tiles] in MFMA accumulators,
+// Work split inside a workgroup of NW wavefronts (8 when M = 128, else 4):
+// wavefront w owns the output / state columns m-tiles {w, w+NW, ...}.  It
+// keeps S[:, its m-tiles] in MFMA accumulators,
 // updates them (phi(K)^T V) and reads them out (phi(Q) S) straight from
 // registers; the masked C x C matrix A is computed once per chunk (tiles
 // shared out over the wavefronts) and passed through LDS.
@@ -37,15 +40,19 @@
 
 namespace la {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr size_t kMaxLds = 160 * 1024;
 
 template <typename T, int D, int M, int C>
 struct Cfg {
     static constexpr bool F32 = std::is_same<T, float>::value;
     static constexpr int RT = C / 16, DT = D / 16, MT = M / 16;
-    static constexpr int MTW = (MT + kWaves - 1) / kWaves;  // m-tiles per wavefront
+    // Wavefronts per workgroup: one per 16-column m-tile when M = 128 (two per
+    // SIMD, half the registers per wavefront), else four.
+    static constexpr int NW = MT >= 8 ? 8 : 4;
+    static constexpr int THREADS = 64 * NW;
+    // Workgroups per CU the register budget is sized for.
+    static constexpr int MIN_WG = (NW == 4 && D * M <= 4096) ? 2 : 1;
+    static constexpr int MTW = (MT + NW - 1) / NW;  // m-tiles per wavefront
     static constexpr int NA = RT * (RT + 1) / 2;            // lower-triangle tiles of A
     static constexpr int PAD = F32 ? 12 : 8;
     static constexpr int LQ = D + PAD;  // rows of phi(Q), phi(K)
@@ -53,9 +60,11 @@ struct Cfg {
     static constexpr int LV = M + PAD;  // fp32: rows of V
     static constexpr int LT = C;        // bf16: rows of V^T and phi(K)^T (swizzled, see tsw)
     static constexpr int E = D * M + D; // floats of one state (S then z)
-    static constexpr int NZP = kThreads / D;  // column-sum partial groups
-    static constexpr int ZROWS = C / NZP;     // rows per partial
-    static_assert(ZROWS * NZP == C || ZROWS == 0, "column-sum split");
+    static constexpr int NZP = THREADS / D < C ? THREADS / D : C;  // column-sum partial groups
+    static constexpr int ZROWS = C / NZP;                            // rows per partial
+    static_assert(ZROWS * NZP == C && NZP * D <= THREADS, "column-sum split");
+    static constexpr int TPR = THREADS / C < D ? THREADS / C : D;    // threads per row of phi(q).z
+    static_assert(TPR <= 64 && (64 % TPR) == 0 && TPR * C <= THREADS, "phi(q).z split");
 
     // T-element offsets
     static constexpr int oQ = 0;
@@ -80,8 +89,8 @@ struct Cfg {
 // ---------------------------------------------------------------------------
 // Staging of a C x W tile of a [N][W] head matrix: global -> registers -> LDS.
 // fp32: an item is one 16-byte vector of one row (rows of W/4 items).
-// bf16: an item is one 16-byte column block of four consecutive rows, so that
-//       the transposed store can write four keys of one column at once.
+// bf16: an item is one 16-byte column block of RPI (4 or 2) consecutive rows, so that
+//       the transposed store can write RPI keys of one column at once.
 // Rows at or beyond N are stored as zeros (after phi, so they add nothing).
 // ---------------------------------------------------------------------------
 // Element offset of `key` within a row of a transposed bf16 tile (unpadded rows of
@@ -95,21 +104,22 @@ __device__ __forceinline__ int tsw(int row, int key) {
     return ((((key >> 3) ^ (row >> 3) ^ row) & mask) << 3) | (key & 7);
 }
 
-template <typename T, int C, int W>
+template <typename T, int C, int W, int NT>
 struct Stage {
     static constexpr bool F32 = std::is_same<T, float>::value;
     static constexpr int VEC = 16 / (int)sizeof(T);
     static constexpr int NV = W / VEC;
-    static constexpr int RPI = F32 ? 1 : 4;
+    // bf16 rows per item: four, or two where four would leave threads without an item
+    static constexpr int RPI = F32 ? 1 : ((C / 4) * (W / 8) >= NT ? 4 : 2);
     static constexpr int ITEMS = (C / RPI) * NV;
-    static constexpr int PER = (ITEMS + kThreads - 1) / kThreads;
+    static constexpr int PER = (ITEMS + NT - 1) / NT;
     uint4 r[PER][RPI];
 
     __device__ __forceinline__ void load(const T *__restrict__ head, int row0, int N, int tid) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int item = tid + p * kThreads;
-            if (ITEMS % kThreads == 0 || item < ITEMS) {
+            const int item = tid + p * NT;
+            if (ITEMS % NT == 0 || item < ITEMS) {
                 const int rq = item / NV, cv = item % NV;
 #pragma unroll
                 for (int i = 0; i < RPI; ++i) {
@@ -134,8 +144,8 @@ struct Stage {
     __device__ __forceinline__ void store_natural_impl(T *dst, int ld, int row0, int N, int tid) const {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int item = tid + p * kThreads;
-            if (ITEMS % kThreads == 0 || item < ITEMS) {
+            const int item = tid + p * NT;
+            if (ITEMS % NT == 0 || item < ITEMS) {
                 const int rq = item / NV, cv = item % NV;
 #pragma unroll
                 for (int i = 0; i < RPI; ++i) {
@@ -177,13 +187,13 @@ struct Stage {
         static_assert(!F32, "transposed staging is for bf16 operands");
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int item = tid + p * kThreads;
-            if (ITEMS % kThreads == 0 || item < ITEMS) {
+            const int item = tid + p * NT;
+            if (ITEMS % NT == 0 || item < ITEMS) {
                 const int rq = item / NV, cv = item % NV;
-                bf16x8 y[4];
+                bf16x8 y[RPI];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float keep = (!TAIL || row0 + rq * 4 + i < N) ? 1.0f : 0.0f;
+                for (int i = 0; i < RPI; ++i) {
+                    const float keep = (!TAIL || row0 + rq * RPI + i < N) ? 1.0f : 0.0f;
                     bf16x8 x = __builtin_bit_cast(bf16x8, r[p][i]);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
@@ -191,13 +201,18 @@ struct Stage {
                         y[i][j] = (bf16)((PHI ? phi(f) : f) * keep);
                     }
                     if constexpr (ALSO_NATURAL)
-                        *reinterpret_cast<bf16x8 *>(dst_n + (rq * 4 + i) * ldn + cv * 8) = y[i];
+                        *reinterpret_cast<bf16x8 *>(dst_n + (rq * RPI + i) * ldn + cv * 8) = y[i];
                 }
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    bf16x4 t = {y[0][j], y[1][j], y[2][j], y[3][j]};
                     const int row = cv * 8 + j;
-                    *reinterpret_cast<bf16x4 *>(dst_t + row * ldt + tsw<C>(row, rq * 4)) = t;
+                    if constexpr (RPI == 4) {
+                        bf16x4 t = {y[0][j], y[1][j], y[2][j], y[3][j]};
+                        *reinterpret_cast<bf16x4 *>(dst_t + row * ldt + tsw<C>(row, rq * 4)) = t;
+                    } else {
+                        bf16x2 t = {y[0][j], y[1][j]};
+                        *reinterpret_cast<bf16x2 *>(dst_t + row * ldt + tsw<C>(row, rq * 2)) = t;
+                    }
                 }
             }
         }
@@ -259,18 +274,18 @@ struct Engine {
         l16 = lane & 15;
     }
 
-    __device__ __forceinline__ bool owns(int i) const { return G::MT % kWaves == 0 || w + kWaves * i < G::MT; }
-    __device__ __forceinline__ int mtile(int i) const { return w + kWaves * i; }
+    __device__ __forceinline__ bool owns(int i) const { return G::MT % G::NW == 0 || w + G::NW * i < G::MT; }
+    __device__ __forceinline__ int mtile(int i) const { return w + G::NW * i; }
 
     // The upper triangle of A is never written by a_tiles; zero it (all of A) once.
     __device__ __forceinline__ void clear_a() const {
-        for (int e = tid; e < C * G::LA; e += kThreads) sA[e] = from_f32<T>(0.0f);
+        for (int e = tid; e < C * G::LA; e += G::THREADS) sA[e] = from_f32<T>(0.0f);
     }
 
-    __device__ __forceinline__ void store_q(const Stage<T, C, D> &st, int row0, int N) const {
+    __device__ __forceinline__ void store_q(const Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &st, int row0, int N) const {
         st.template store_natural<true>(sQ, G::LQ, row0, N, tid);
     }
-    __device__ __forceinline__ void store_kv(const Stage<T, C, D> &stK, const Stage<T, C, M> &stV, int row0,
+    __device__ __forceinline__ void store_kv(const Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &stK, const Stage<T, C, M, Cfg<T, D, M, C>::THREADS> &stV, int row0,
                                              int N) const {
         if constexpr (G::F32) {
             stK.template store_natural<true>(sK, G::LQ, row0, N, tid);
@@ -284,7 +299,7 @@ struct Engine {
     // Column sums of phi(K_c): partial sums over ZROWS rows into szp[q][d].
     __device__ __forceinline__ void z_partials() const {
         const int q = tid / D, d = tid % D;
-        if (G::NZP * D == kThreads || q < G::NZP) {
+        if (G::NZP * D == G::THREADS || q < G::NZP) {
             float s = 0.0f;
 #pragma unroll
             for (int r = 0; r < G::ZROWS; ++r) s += to_f32(sK[(q * G::ZROWS + r) * G::LQ + d]);
@@ -352,7 +367,7 @@ struct Engine {
     // rounded to T, into sA[query][key]; their row sums into sdenp[kt][query].
     __device__ __forceinline__ void a_tiles() const {
 #pragma unroll
-        for (int t = w; t < G::NA; t += kWaves) {
+        for (int t = w; t < G::NA; t += G::NW) {
             int rt = 0;
             while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
             const int kt = t - rt * (rt + 1) / 2;
@@ -391,23 +406,25 @@ struct Engine {
         }
     }
 
-    // phi(q_i) . z for every row i of the chunk -> sqz[i]
-    __device__ __forceinline__ void qz_rows() const {
-        constexpr int TPR = kThreads / C;  // threads per row (4, 8 or 16), consecutive lanes
+    // phi(q_i) . z for every row i of the chunk -> dst[i] (default sqz)
+    __device__ __forceinline__ void qz_rows() const { qz_rows_to(sqz); }
+    __device__ __forceinline__ void qz_rows_to(float *dst) const {
+        constexpr int TPR = G::TPR;  // threads per row, consecutive lanes
         const int i = tid / TPR, p = tid % TPR;
+        if (G::TPR * C < G::THREADS && i >= C) return;  // whole wavefronts beyond the rows
         const T *qr = sQ + i * G::LQ;
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < D / TPR; ++j) s += to_f32(qr[p * (D / TPR) + j]) * sz[p * (D / TPR) + j];
 #pragma unroll
         for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (p == 0) sqz[i] = s;
+        if (p == 0) dst[i] = s;
     }
 
-    // 1 / den for row `lane` (lanes >= C return 0); needs sdenp and sqz (after a barrier)
+    // den for row `lane` (lanes >= C return 1); needs sdenp and sqz (after a barrier)
     template <bool CAUSAL>
-    __device__ __forceinline__ float row_inv() const {
-        if (lane >= C) return 0.0f;
+    __device__ __forceinline__ float row_den() const {
+        if (lane >= C) return 1.0f;
         const int rt = lane / 16;
         float den = sqz[lane];
         if constexpr (CAUSAL) {
@@ -415,7 +432,11 @@ struct Engine {
             for (int kt = 0; kt < RT; ++kt)
                 if (kt <= rt) den += sdenp[kt * C + lane];
         }
-        return 1.0f / den;
+        return den;
+    }
+    template <bool CAUSAL>
+    __device__ __forceinline__ float row_inv() const {
+        return 1.0f / row_den<CAUSAL>();
     }
 
     // Output tiles of the chunk for the own m-tiles.  Each MFMA takes the V / S side
@@ -468,14 +489,13 @@ struct Engine {
         }
     }
 
-    __device__ __forceinline__ void readout(f32x4 (&o)[RT][MTW], const f32x4 (&S)[DT][MTW], float inv,
-                                            float *__restrict__ Oh, int row0, int N, bool poison) const {
-        const bool full = row0 + C <= N;  // uniform: no per-row bounds checks needed
+    // o += (phi(Q_c) S)^T for the chunk's rows of sQ, S from registers
+    __device__ __forceinline__ void readout_mma(f32x4 (&o)[RT][MTW], const f32x4 (&S)[DT][MTW]) const {
+        if constexpr (G::F32) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int qrow = rt * 16 + l16;
-            // contraction slot of lane (g, l16) at step (dt, r) is d = dt*16 + 4g + r
-            if constexpr (G::F32) {
+            for (int rt = 0; rt < RT; ++rt) {
+                const int qrow = rt * 16 + l16;
+                // contraction slot of lane (g, l16) at step (dt, r) is d = dt*16 + 4g + r
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt) {
                     const f32x4 qv = *reinterpret_cast<const f32x4 *>(sQ + qrow * G::LQ + dt * 16 + 4 * g);
@@ -485,31 +505,54 @@ struct Engine {
                         for (int i = 0; i < MTW; ++i)
                             if (owns(i)) o[rt][i] = mma_f32(S[dt][i][r], qv[r], o[rt][i]);
                 }
-            } else if constexpr (DT == 1) {
+            }
+        } else if constexpr (DT == 1) {
+            bf16x4 sb[MTW];
+#pragma unroll
+            for (int i = 0; i < MTW; ++i)
+                sb[i] = bf16x4{(bf16)S[0][i][0], (bf16)S[0][i][1], (bf16)S[0][i][2], (bf16)S[0][i][3]};
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int qrow = rt * 16 + l16;
                 const bf16x4 qv = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + 4 * g);
 #pragma unroll
+                for (int i = 0; i < MTW; ++i)
+                    if (owns(i)) o[rt][i] = mma_bf16_k16(sb[i], qv, o[rt][i]);
+            }
+        } else {
+            // the bf16 copy of the state is made once per call, not per row tile
+            bf16x8 sv[DT / 2][MTW];
+#pragma unroll
+            for (int p = 0; p < DT / 2; ++p)
+#pragma unroll
                 for (int i = 0; i < MTW; ++i) {
-                    if (!owns(i)) continue;
-                    const bf16x4 sb = {(bf16)S[0][i][0], (bf16)S[0][i][1], (bf16)S[0][i][2], (bf16)S[0][i][3]};
-                    o[rt][i] = mma_bf16_k16(sb, qv, o[rt][i]);
+                    const f32x4 s0 = S[2 * p][i], s1 = S[2 * p + 1][i];
+                    sv[p][i] = bf16x8{(bf16)s0[0], (bf16)s0[1], (bf16)s0[2], (bf16)s0[3],
+                                      (bf16)s1[0], (bf16)s1[1], (bf16)s1[2], (bf16)s1[3]};
                 }
-            } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const int qrow = rt * 16 + l16;
 #pragma unroll
                 for (int p = 0; p < DT / 2; ++p) {
                     const bf16x4 q0 = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + (2 * p) * 16 + 4 * g);
                     const bf16x4 q1 = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + (2 * p + 1) * 16 + 4 * g);
                     const bf16x8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
 #pragma unroll
-                    for (int i = 0; i < MTW; ++i) {
-                        if (!owns(i)) continue;
-                        const f32x4 s0 = S[2 * p][i], s1 = S[2 * p + 1][i];
-                        const bf16x8 sv = {(bf16)s0[0], (bf16)s0[1], (bf16)s0[2], (bf16)s0[3],
-                                           (bf16)s1[0], (bf16)s1[1], (bf16)s1[2], (bf16)s1[3]};
-                        o[rt][i] = mma_bf16_k32(sv, qv, o[rt][i]);
-                    }
+                    for (int i = 0; i < MTW; ++i)
+                        if (owns(i)) o[rt][i] = mma_bf16_k32(sv[p][i], qv, o[rt][i]);
                 }
             }
-            // normalise and store
+        }
+    }
+
+    // out[row0 + rows] = o * (1 / den) of the row (inv: lane r holds row r's factor)
+    __device__ __forceinline__ void store_rows(const f32x4 (&o)[RT][MTW], float inv, float *__restrict__ Oh, int row0,
+                                               int N, bool poison) const {
+        const bool full = row0 + C <= N;  // uniform: no per-row bounds checks needed
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int qrow = rt * 16 + l16;
             const float inv_q = __shfl(inv, qrow, 64);
             const int grow = row0 + qrow;
             if (full || grow < N) {
@@ -523,6 +566,12 @@ struct Engine {
                 }
             }
         }
+    }
+
+    __device__ __forceinline__ void readout(f32x4 (&o)[RT][MTW], const f32x4 (&S)[DT][MTW], float inv,
+                                            float *__restrict__ Oh, int row0, int N, bool poison) const {
+        readout_mma(o, S);
+        store_rows(o, inv, Oh, row0, N, poison);
     }
 
     __device__ __forceinline__ static void zero_out(f32x4 (&o)[RT][MTW]) {
@@ -653,8 +702,8 @@ struct Engine {
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C>
 struct KVBuf {
-    Stage<T, C, D> k;
-    Stage<T, C, M> v;
+    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> k;
+    Stage<T, C, M, Cfg<T, D, M, C>::THREADS> v;
     __device__ __forceinline__ void load(const T *Kh, const T *Vh, int c, int N, int tid) {
         k.load(Kh, c * C, N, tid);
         v.load(Vh, c * C, N, tid);
@@ -695,17 +744,17 @@ template <typename T, int D, int M, int C, bool CAUSAL>
 __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__restrict__ Qh,
                                         const T *__restrict__ Kh, const T *__restrict__ Vh,
                                         float *__restrict__ Oh, int N, int c0, int c1, bool kv_staged,
-                                        bool advance_last, Stage<T, C, D> &q0,
+                                        bool advance_last, Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q0,
                                         f32x4 (&S)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z,
                                         bool poison) {
-    Stage<T, C, D> q1;
+    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> q1;
     KVBuf<T, D, M, C> b0, b1;
     if (CAUSAL && !kv_staged) b0.load(Kh, Vh, c0, N, e.tid);
     if (c0 + 1 < c1) {
         q1.load(Qh, (c0 + 1) * C, N, e.tid);
         if (CAUSAL) b1.load(Kh, Vh, c0 + 1, N, e.tid);
     }
-    auto step = [&](Stage<T, C, D> &q, KVBuf<T, D, M, C> &b, int c) {
+    auto step = [&](Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q, KVBuf<T, D, M, C> &b, int c) {
         const int row0 = c * C;
         const bool stage_kv = CAUSAL && !(kv_staged && c == c0);
         __syncthreads();  // LDS free
@@ -744,8 +793,97 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__
 // ---------------------------------------------------------------------------
 constexpr long kSpinLimit = 1L << 22;
 
+// Decoupled look-back of segment s > 0 of head bh (every thread of the
+// workgroup calls it).  Wavefront 0 polls the flags of segments s-1, s-2, ...
+// (one lane per segment, 64 at a time, relaxed loads) until it finds the
+// nearest segment j* whose inclusive prefix is published (segment 0's
+// aggregate is its inclusive prefix) with every aggregate between j* and s
+// ready; the prefix is then incl(j*) + agg(j*+1) + ... + agg(s-1), added into
+// pre / zpre.  Waits are bounded (kSpinLimit polls); on a timeout the error
+// word of the workspace is set and false is returned.
 template <typename T, int D, int M, int C>
-__global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+__device__ __forceinline__ bool look_back(const Engine<T, D, M, C> &e, const FusedWs &ws, unsigned *sh_word, int bh,
+                                          int s, int G_, unsigned ep,
+                                          f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &zpre) {
+    using Gc = Cfg<T, D, M, C>;
+    if (e.w == 0) {
+        const unsigned *fl = ws.flags + (size_t)bh * G_;
+        int base = s - 1;
+        int jstar = -1;
+        long spins = 0;
+        while (true) {
+            const int j = base - e.lane;
+            unsigned f = 0u;
+            if (j >= 0) f = __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool ok = j >= 0 && (f & ~3u) == ep && (f & 3u) != 0u;
+            const bool inc = ok && ((f & 3u) == 2u || j == 0);
+            const unsigned long long okm = __ballot(ok), incm = __ballot(inc);
+            if (incm != 0ull) {
+                const int first = __builtin_ctzll(incm);
+                const unsigned long long need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
+                if ((okm & need) == need) {
+                    jstar = base - first;
+                    break;
+                }
+            } else if (okm == ~0ull) {
+                base -= 64;  // 64 aggregates ready, none inclusive: look further back
+                continue;
+            }
+            if (++spins > kSpinLimit) {
+                if (e.lane == 0) __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                jstar = -1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (e.lane == 0) sh_word[0] = (unsigned)(jstar + 1);
+    }
+    __syncthreads();
+    const int jstar = (int)sh_word[0] - 1;
+    if (jstar < 0) return false;
+    const size_t h0 = (size_t)bh * G_;
+    e.state_add_slots(pre, zpre, (jstar == 0 ? ws.agg : ws.incl) + (h0 + jstar) * Gc::E, ws.agg + h0 * Gc::E,
+                      jstar + 1, s);
+    return true;
+}
+
+// Publish the inclusive prefix pre + acc of segment `my` (NaN after a failed look-back).
+template <typename T, int D, int M, int C>
+__device__ __forceinline__ void publish_inclusive(const Engine<T, D, M, C> &e, const FusedWs &ws, size_t my,
+                                                  unsigned ep,
+                                                  const f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW],
+                                                  float zpre,
+                                                  const f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW],
+                                                  float zacc, bool failed) {
+    using Gc = Cfg<T, D, M, C>;
+    f32x4 inc[Gc::DT][Gc::MTW];
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < Gc::MTW; ++i) {
+            inc[dt][i] = pre[dt][i] + acc[dt][i];
+            if (failed) inc[dt][i] = f32x4{nan, nan, nan, nan};
+        }
+    e.state_store_coherent(inc, failed ? nan : zpre + zacc, ws.incl + my * Gc::E);
+    e.publish_flag(&ws.flags[my], ep | 2u);
+}
+
+// The last workgroup of a call to finish resets the finished-workgroup counter
+// and advances the epoch (every flag of the call becomes stale).
+__device__ __forceinline__ void finish_call(const FusedWs &ws, unsigned epoch, unsigned n_wg) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned done = atomicAdd(&ws.hdr[1], 1u);
+        if (done == n_wg - 1u) {
+            __hip_atomic_store(&ws.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&ws.hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <typename T, int D, int M, int C>
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                 const T *__restrict__ V, float *__restrict__ out,
                                                                 void *ws_raw, int BH, int N, int G_, int CPS,
                                                                 float *__restrict__ S_out, float *__restrict__ z_out) {
@@ -795,7 +933,7 @@ __global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void fused_causa
         e.publish_flag(&ws.flags[my], ep | 1u);
     }
 
-    Stage<T, C, D> stQ;
+    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> stQ;
     stQ.load(Qh, c0 * C, N, tid);
 
     // A one-chunk segment still holds its phi(K), V in LDS: form A and the
@@ -816,66 +954,8 @@ __global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void fused_causa
     float zpre = 0.0f;
     bool failed = false;
     if (G_ > 1 && s > 0) {
-        // Look back: wavefront 0 polls the flags of segments s-1, s-2, ... (one
-        // lane per segment, 64 at a time, relaxed loads) until it finds the
-        // nearest segment j* whose inclusive prefix is published (segment 0's
-        // aggregate is its inclusive prefix) with every aggregate between j*
-        // and s ready.  The prefix is then incl(j*) + agg(j*+1) + ... + agg(s-1).
-        if (e.w == 0) {
-            const unsigned *fl = ws.flags + (size_t)bh * G_;
-            int base = s - 1;
-            int jstar = -1;
-            long spins = 0;
-            while (true) {
-                const int j = base - e.lane;
-                unsigned f = 0u;
-                if (j >= 0) f = __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const bool ok = j >= 0 && (f & ~3u) == ep && (f & 3u) != 0u;
-                const bool inc = ok && ((f & 3u) == 2u || j == 0);
-                const unsigned long long okm = __ballot(ok), incm = __ballot(inc);
-                if (incm != 0ull) {
-                    const int first = __builtin_ctzll(incm);
-                    const unsigned long long need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
-                    if ((okm & need) == need) {
-                        jstar = base - first;
-                        break;
-                    }
-                } else if (okm == ~0ull) {
-                    base -= 64;  // 64 aggregates ready, none inclusive: look further back
-                    continue;
-                }
-                if (++spins > kSpinLimit) {
-                    if (e.lane == 0) __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    jstar = -1;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(1);
-            }
-            if (e.lane == 0) sh_word[0] = (unsigned)(jstar + 1);
-        }
-        __syncthreads();
-        const int jstar = (int)sh_word[0] - 1;
-        if (jstar < 0) {
-            failed = true;
-        } else {
-            const size_t h0 = (size_t)bh * G_;
-            e.state_add_slots(pre, zpre, (jstar == 0 ? ws.agg : ws.incl) + (h0 + jstar) * Gc::E,
-                              ws.agg + h0 * Gc::E, jstar + 1, s);
-        }
-        if (!last) {
-            // publish the inclusive prefix (segment 0's aggregate already is one)
-            f32x4 inc[Gc::DT][Gc::MTW];
-            const float nan = __builtin_nanf("");
-#pragma unroll
-            for (int dt = 0; dt < Gc::DT; ++dt)
-#pragma unroll
-                for (int i = 0; i < Gc::MTW; ++i) {
-                    inc[dt][i] = pre[dt][i] + acc[dt][i];
-                    if (failed) inc[dt][i] = f32x4{nan, nan, nan, nan};
-                }
-            e.state_store_coherent(inc, failed ? nan : zpre + zacc, ws.incl + my * Gc::E);
-            e.publish_flag(&ws.flags[my], ep | 2u);
-        }
+        failed = !look_back<T, D, M, C>(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
+        if (!last) publish_inclusive<T, D, M, C>(e, ws, (size_t)bh * G_ + s, ep, pre, zpre, acc, zacc, failed);
     }
     if (G_ > 1 && last && want_final) {
         f32x4 fin[Gc::DT][Gc::MTW];
@@ -900,17 +980,174 @@ __global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void fused_causa
         if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
     }
 
+    if (G_ > 1) finish_call(ws, epoch, (unsigned)(BH * G_));
+}
+
+// ---------------------------------------------------------------------------
+// One-pass causal kernel, for segments of at most kOnePassChunks chunks.
+// The workgroup reads its segment once.  Per chunk it forms A, the intra-chunk
+// term and phi(Q_c) times the state summed so far inside the segment, keeps
+// the unnormalised rows in registers (and phi(Q_c) and the partial
+// denominators in LDS), and advances the segment-local state.  It then
+// publishes the local state (the segment aggregate), looks back for the
+// prefix (S_p, z_p) of the earlier segments and finishes every row:
+//   out = (o + phi(q) S_p) / (den + phi(q) . z_p).
+// Same workspace, flags and epoch protocol as the fused kernel.
+// ---------------------------------------------------------------------------
+constexpr int kOnePassChunks = 4;
+
+// LDS: phi(Q) of the whole segment [ROWS][LQ] at the start, its last chunk
+// doubling as the engine's phi(Q) tile (the engine's layout starts at
+// `shift`), then the partial denominators and phi(q).z_prefix of every row.
+template <typename T, int D, int M, int C>
+struct OnePassLds {
+    using Gc = Cfg<T, D, M, C>;
+    static constexpr int ROWS = kOnePassChunks * C;
+    static constexpr size_t shift = (size_t)(kOnePassChunks - 1) * C * Gc::LQ * sizeof(T);
+    static_assert(shift % 16 == 0, "phi(Q) rows keep 16-byte alignment");
+    static constexpr size_t oDen = ((shift + Gc::bytes + 15) / 16) * 16;
+    static constexpr size_t oQz = oDen + ROWS * sizeof(float);
+    static constexpr size_t bytes = oQz + ROWS * sizeof(float);
+    // every workgroup the planner places on one CU must fit
+    static constexpr bool fits = (bytes + 64) * Gc::MIN_WG <= kMaxLds;
+};
+
+template <typename T, int D, int M, int C>
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void onepass_causal_kernel(
+    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, float *__restrict__ out,
+    void *ws_raw, int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out) {
+    using Gc = Cfg<T, D, M, C>;
+    using L1 = OnePassLds<T, D, M, C>;
+    using En = Engine<T, D, M, C>;
+    constexpr int NC = kOnePassChunks;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L1::bytes];
+    __shared__ unsigned sh_word[2];
+    En e(smem + L1::shift);
+    T *const sQs = reinterpret_cast<T *>(smem);
+    float *const sden = reinterpret_cast<float *>(smem + L1::oDen);
+    float *const sqzs = reinterpret_cast<float *>(smem + L1::oQz);
+    const int tid = e.tid;
+
+    // block b -> segment b / BH of head b % BH (dispatch order, as in the fused kernel)
+    const int bh = (int)(blockIdx.x % (unsigned)BH);
+    const int s = (int)(blockIdx.x / (unsigned)BH);
+    unsigned epoch = 0;
+    FusedWs ws(ws_raw, BH, G_ > 1 ? G_ : 1, Gc::E);
     if (G_ > 1) {
-        // the last workgroup to finish resets the counters and advances the epoch
+        if (tid == 0) sh_word[1] = __hip_atomic_load(&ws.hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        if (tid == 0) {
-            const unsigned done = atomicAdd(&ws.hdr[1], 1u);
-            if (done == (unsigned)(BH * G_) - 1u) {
-                __hip_atomic_store(&ws.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&ws.hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            }
+        epoch = sh_word[1];
+    }
+    const unsigned ep = (epoch & 0x3fffffffu) << 2;
+
+    const int n_chunks = (N + C - 1) / C;
+    const int c0 = s * CPS;
+    const int nc = min(CPS, n_chunks - c0);  // 1 .. NC (the planner guarantees it)
+    const T *Qh = Q + (size_t)bh * N * D;
+    const T *Kh = K + (size_t)bh * N * D;
+    const T *Vh = V + (size_t)bh * N * M;
+    float *Oh = out + (size_t)bh * N * M;
+    const bool last = s == G_ - 1;
+    const bool want_final = S_out != nullptr;
+
+    e.clear_a();
+    f32x4 S[Gc::DT][Gc::MTW];
+    En::zero_state(S);
+    float z = 0.0f;
+    f32x4 o[NC][Gc::RT][Gc::MTW];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) En::zero_out(o[j]);
+
+    Stage<T, C, D, Gc::THREADS> q0, q1;
+    KVBuf<T, D, M, C> b0, b1;
+    q0.load(Qh, c0 * C, N, tid);
+    b0.load(Kh, Vh, c0, N, tid);
+    if (nc > 1) {
+        q1.load(Qh, (c0 + 1) * C, N, tid);
+        b1.load(Kh, Vh, c0 + 1, N, tid);
+    }
+    auto step = [&](Stage<T, C, D, Gc::THREADS> &q, KVBuf<T, D, M, C> &b, int j, f32x4 (&oj)[Gc::RT][Gc::MTW]) {
+        const int c = c0 + j, row0 = c * C;
+        __syncthreads();  // sK, sV, sA, side arrays free
+        e.sQ = sQs + j * C * Gc::LQ;
+        e.store_q(q, row0, N);
+        e.store_kv(b.k, b.v, row0, N);
+        if (tid < D) e.sz[tid] = round_as<T>(z);
+        __syncthreads();
+        if (j + 2 < nc) {
+            q.load(Qh, (c + 2) * C, N, tid);
+            b.load(Kh, Vh, c + 2, N, tid);
+        }
+        e.a_tiles();
+        e.qz_rows();
+        // the last segment needs its local state only for the final state
+        const bool adv = j + 1 < nc || !last || want_final;
+        if (adv) e.z_partials();
+        __syncthreads();
+        if (e.w == 0 && e.lane < C) sden[j * C + e.lane] = e.template row_den<true>();
+        e.intra(oj);
+        if (j > 0) e.readout_mma(oj, S);
+        if (adv) {
+            e.state_update(S);
+            if (tid < D) z += e.z_delta();
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        if (j < nc) {
+            if (j & 1)
+                step(q1, b1, j, o[j]);
+            else
+                step(q0, b0, j, o[j]);
         }
     }
+
+    const size_t my = (size_t)bh * G_ + s;
+    if (G_ > 1 && !last) {
+        e.state_store_coherent(S, z, ws.agg + my * Gc::E);
+        e.publish_flag(&ws.flags[my], ep | 1u);
+    }
+    f32x4 pre[Gc::DT][Gc::MTW];
+    En::zero_state(pre);
+    float zpre = 0.0f;
+    bool failed = false;
+    const bool has_prefix = G_ > 1 && s > 0;
+    if (has_prefix) {
+        failed = !look_back<T, D, M, C>(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
+        if (!last) publish_inclusive<T, D, M, C>(e, ws, my, ep, pre, zpre, S, z, failed);
+    }
+    if (last && want_final) {
+        f32x4 fin[Gc::DT][Gc::MTW];
+#pragma unroll
+        for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < Gc::MTW; ++i) fin[dt][i] = pre[dt][i] + S[dt][i];
+        e.state_store(fin, zpre + z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+    }
+
+    // finish the rows with the prefix
+    if (has_prefix) {
+        if (tid < D) e.sz[tid] = round_as<T>(zpre);
+        __syncthreads();
+        for (int j = 0; j < nc; ++j) {
+            e.sQ = sQs + j * C * Gc::LQ;
+            e.qz_rows_to(sqzs + j * C);
+        }
+    }
+    __syncthreads();  // sden, sqzs visible to every wavefront
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        if (j < nc) {
+            float inv = 0.0f;
+            if (e.lane < C) inv = 1.0f / (sden[j * C + e.lane] + (has_prefix ? sqzs[j * C + e.lane] : 0.0f));
+            if (has_prefix) {
+                e.sQ = sQs + j * C * Gc::LQ;
+                e.readout_mma(o[j], pre);
+            }
+            e.store_rows(o[j], inv, Oh, (c0 + j) * C, N, failed);
+        }
+    }
+    if (G_ > 1) finish_call(ws, epoch, (unsigned)(BH * G_));
 }
 
 // ---------------------------------------------------------------------------
@@ -919,7 +1156,7 @@ __global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void fused_causa
 // exclusive prefix; slot G = total.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C>
-__global__ __launch_bounds__(kThreads) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS)) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
                                                              float *__restrict__ ws, int N, int G_, int CPS,
                                                              int nstates) {
     using Gc = Cfg<T, D, M, C>;
@@ -936,7 +1173,7 @@ __global__ __launch_bounds__(kThreads) void seg_state_kernel(const T *__restrict
 }
 
 template <typename T, int D, int M, int C, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                               const T *__restrict__ V, float *__restrict__ out,
                                                               const float *__restrict__ ws, int N, int G_, int CPS,
                                                               float *__restrict__ S_out, float *__restrict__ z_out) {
@@ -956,7 +1193,7 @@ __global__ __launch_bounds__(kThreads, (D * M <= 4096 ? 2 : 1)) void seg_output_
         e.state_add(S, z, ws + ((size_t)bh * (G_ + 1) + G_) * Gc::E);
     }
     if (CAUSAL) e.clear_a();
-    Stage<T, C, D> stQ;
+    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> stQ;
     stQ.load(Qh, c0 * C, N, e.tid);
     const bool fin = CAUSAL && S_out != nullptr && s == G_ - 1;
     phase_b<T, D, M, C, CAUSAL>(e, Qh, K + (size_t)bh * N * D, V + (size_t)bh * N * M, out + (size_t)bh * N * M, N,
@@ -976,8 +1213,23 @@ hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, vo
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
-        hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C>), dim3(grid), dim3(kThreads), 0, stream, (const T *)Q,
+        hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
                            (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out);
+        return hipGetLastError();
+    }
+}
+
+template <typename T, int D, int M, int C>
+hipError_t run_onepass(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
+                       int CPS, float *S_out, float *z_out, hipStream_t stream) {
+    using Gc = Cfg<T, D, M, C>;
+    if constexpr (!(Gc::fits && OnePassLds<T, D, M, C>::fits)) {
+        return hipErrorInvalidValue;
+    } else {
+        if (BH <= 0 || G_ <= 0) return hipSuccess;
+        if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((onepass_causal_kernel<T, D, M, C>), dim3((unsigned)(BH * G_)), dim3(Gc::THREADS), 0,
+                           stream, (const T *)Q, (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out);
         return hipGetLastError();
     }
 }
@@ -990,7 +1242,7 @@ hipError_t run_states(const void *K, const void *V, float *ws, int BH, int N, in
         return hipErrorInvalidValue;
     } else {
         if (nstates <= 0 || BH <= 0) return hipSuccess;
-        hipLaunchKernelGGL((seg_state_kernel<T, D, M, C>), dim3((unsigned)(BH * nstates)), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((seg_state_kernel<T, D, M, C>), dim3((unsigned)(BH * nstates)), dim3(Gc::THREADS), 0, stream,
                            (const T *)K, (const T *)V, ws, N, G_, CPS, nstates);
         return hipGetLastError();
     }
@@ -1004,7 +1256,7 @@ hipError_t run_outputs(const void *Q, const void *K, const void *V, float *out, 
         return hipErrorInvalidValue;
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
-        const dim3 grid((unsigned)(BH * G_)), block(kThreads);
+        const dim3 grid((unsigned)(BH * G_)), block(Gc::THREADS);
         if (causal)
             hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, true>), grid, block, 0, stream, (const T *)Q,
                                (const T *)K, (const T *)V, out, ws, N, G_, CPS, S_out, z_out);
@@ -1014,5 +1266,10 @@ hipError_t run_outputs(const void *Q, const void *K, const void *V, float *out, 
         return hipGetLastError();
     }
 }
+
+// Every (D, M, C) the library instantiates: D, M in {16, 32, 64, 128}, C in {16, 32, 64}.
+#define LA_FOR_C(D_, M_, X) X(D_, M_, 16) X(D_, M_, 32) X(D_, M_, 64)
+#define LA_FOR_M(D_, X) LA_FOR_C(D_, 16, X) LA_FOR_C(D_, 32, X) LA_FOR_C(D_, 64, X) LA_FOR_C(D_, 128, X)
+#define LA_FOR_ALL(X) LA_FOR_M(16, X) LA_FOR_M(32, X) LA_FOR_M(64, X) LA_FOR_M(128, X)
 
 }  // namespace la

@@ -4,9 +4,6 @@
 
 namespace la {
 
-#define LA_FOR_C(D_, M_, X) X(D_, M_, 16) X(D_, M_, 32) X(D_, M_, 64)
-#define LA_FOR_M(D_, X) LA_FOR_C(D_, 16, X) LA_FOR_C(D_, 32, X) LA_FOR_C(D_, 64, X) LA_FOR_C(D_, 128, X)
-#define LA_FOR_ALL(X) LA_FOR_M(16, X) LA_FOR_M(32, X) LA_FOR_M(64, X) LA_FOR_M(128, X)
 
 bool prefill_supported_bf16(int D, int M, int C) {
 #define X(D_, M_, C_) \

@@ -63,6 +63,16 @@ hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const vo
                       : prefill_fused_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream);
 }
 
+hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                           void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream) {
+    return dtype == 0 ? prefill_onepass_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream)
+                      : prefill_onepass_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream);
+}
+
+bool prefill_onepass_supported(int dtype, int D, int M, int C) {
+    return dtype == 0 ? prefill_onepass_supported_f32(D, M, C) : prefill_onepass_supported_bf16(D, M, C);
+}
+
 size_t prefill_lds_bytes(int dtype, int D, int M, int C) {
     return dtype == 0 ? prefill_lds_bytes_f32(D, M, C) : prefill_lds_bytes_bf16(D, M, C);
 }

@@ -32,6 +32,8 @@ SIGNATURES = {
     "la_workspace_init": (_int, [_vp, _sz, _vp]),
     "la_forward_fused": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz,
                                 _vp, _vp, _vp]),
+    "la_forward_onepass": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz,
+                                  _vp, _vp, _vp]),
     "la_segment_states": (_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
     "la_segment_scan": (_int, [_vp, _sz, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "la_segment_outputs": (_int, [_vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
@@ -195,7 +197,16 @@ def fused_workspace_bytes(B, H, D, M, segments) -> int:
 
 
 def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None):
-    """The causal fused kernel with an explicit plan (chunk, segments)."""
+    """The causal two-phase fused kernel with an explicit plan (chunk, segments)."""
+    return _forward_explicit("la_forward_fused", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream)
+
+
+def forward_onepass(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None):
+    """The causal one-pass kernel with an explicit plan (segments of at most 4 chunks)."""
+    return _forward_explicit("la_forward_onepass", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream)
+
+
+def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream):
     import torch
     B, H, N, D = Q.shape
     M = V.shape[-1]
@@ -206,11 +217,11 @@ def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None
         out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
     need = fused_workspace_bytes(B, H, D, M, segments)
     if workspace is None and need > 0:
-        workspace = _cached_workspace(need, dev, stream, ("fused", B * H, N, D, M, _dtype_code(Q), chunk, segments))
+        workspace = _cached_workspace(need, dev, stream, (name, B * H, N, D, M, _dtype_code(Q), chunk, segments))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().la_forward_fused(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(Q), chunk,
-                                segments, _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
-    _check(st, "la_forward_fused")
+    st = getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(Q), chunk,
+                              segments, _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
+    _check(st, name)
     return out
 
 

@@ -87,9 +87,11 @@ LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_
 /*
  * Parallel-mode attention (prefill / training forward).
  *
- * causal = 1: out_i uses positions j <= i (diagonal included); one fused
- *   kernel whose workgroups (one per segment) pass summed states forward with
- *   a decoupled look-back.
+ * causal = 1: out_i uses positions j <= i (diagonal included); one kernel
+ *   whose workgroups (one per segment) pass summed states forward with a
+ *   decoupled look-back: the one-pass kernel (la_forward_onepass) when the
+ *   plan's segments hold at most 4 chunks, else the two-phase fused kernel
+ *   (la_forward_fused).
  * causal = 0: every out_i uses all N positions (three stage kernels).
  * out: [B][H][N][M] fp32, fully written.
  * workspace: device memory of at least la_forward_workspace_bytes(...) bytes
@@ -125,6 +127,24 @@ LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *
                             int dtype, int chunk, int segments,
                             void *workspace, size_t workspace_bytes,
                             float *S_out, float *z_out, void *stream);
+
+/*
+ * The causal one-pass kernel of la_forward_chunked with an explicit plan:
+ * chunk (16, 32 or 64) and segments, each segment owning at least one and at
+ * most 4 chunks (LA_ERR_UNSUPPORTED otherwise, or when the kernel's LDS does
+ * not fit this (D, M, chunk)).  Each workgroup reads its segment's Q, K, V
+ * once, keeps its unnormalised rows on chip while it publishes its segment
+ * state and looks back for the prefix of the earlier segments, then writes
+ * out = (num + phi(q) S_prefix) / (den + phi(q) . z_prefix)  (page
+ * "Transformers are RNNs", Proposed method: the same cumulative sums, split
+ * at the segment start).  Workspace size and initialisation as for
+ * la_forward_fused (the two kernels share the format, not a live workspace).
+ */
+LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, float *out,
+                              int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                              int dtype, int chunk, int segments,
+                              void *workspace, size_t workspace_bytes,
+                              float *S_out, float *z_out, void *stream);
 
 /*
  * The three stages of the non-causal path, usable for causal attention too,

@@ -240,6 +240,103 @@ def test_fused_segments(ea, dtype, chunk, segments):
     assert err <= stol, f"z {err:.3e}"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,M", SHAPES)
+def test_fused_shapes(ea, dtype, D, M):
+    """The two-phase fused kernel (phase A, look-back, phase B) on every shape."""
+    cfg = small_cfg(dtype, 1, 2, 300, D, M)
+    Q, K, V = synthetic.prefill_inputs(cfg, 12)
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    out = ea.forward_fused(Qd, Kd, Vd, 32, 3)  # 10 chunks: segments of 4, 4, 2
+    torch.cuda.synchronize()
+    ref = oracle.causal(f64(Q, dtype), f64(K, dtype), f64(V, dtype))[0]
+    err = rowwise_rel(out.cpu().numpy(), ref)
+    assert err <= TOL[dtype], f"{err:.3e}"
+
+
+# ---- one-pass kernel (segments of at most four chunks) ----------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,M", SHAPES)
+def test_onepass_shapes(ea, dtype, D, M):
+    cfg = small_cfg(dtype, 1, 2, 300, D, M)
+    Q, K, V = synthetic.prefill_inputs(cfg, 13)
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    S = torch.full((1, 2, D, M), float("nan"), device=DEV)
+    z = torch.full((1, 2, D), float("nan"), device=DEV)
+    try:
+        out = ea.forward_onepass(Qd, Kd, Vd, 32, 3, S_out=S, z_out=z)  # 10 chunks: segments of 4, 4, 2
+    except ea.LinAttnError as e:
+        # the planner only picks the one-pass kernel where its LDS fits
+        assert e.status == 2 and D > M, str(e)
+        pytest.skip("one-pass phi(Q) tiles do not fit in LDS for this shape")
+    torch.cuda.synchronize()
+    ref, S_ref, z_ref = oracle.causal(f64(Q, dtype), f64(K, dtype), f64(V, dtype))
+    err = rowwise_rel(out.cpu().numpy(), ref)
+    assert err <= TOL[dtype], f"out {err:.3e}"
+    stol = 1e-5 if dtype == "f32" else TOL["bf16"]
+    assert whole_rel(S.cpu().numpy(), S_ref) <= stol
+    assert whole_rel(z.cpu().numpy(), z_ref) <= stol
+
+
+ONEPASS_PLANS = [(1000, 32, 8), (1000, 32, 11), (1000, 32, 16), (1000, 32, 32), (1000, 16, 16), (1000, 16, 63),
+                 (100, 32, 1), (97, 16, 2), (1, 16, 1)]
+# 64-position chunks: bf16 only (fp32 tiles of 64 rows do not fit twice per CU)
+ONEPASS_PLANS_BF16 = [(1000, 64, 4), (1000, 64, 6), (1000, 64, 8), (1000, 64, 16), (200, 64, 1)]
+
+
+@pytest.mark.parametrize("dtype,N,chunk,segments", [("f32",) + p for p in ONEPASS_PLANS] +
+                         [("bf16",) + p for p in ONEPASS_PLANS + ONEPASS_PLANS_BF16])
+def test_onepass_segments(ea, dtype, N, chunk, segments):
+    """Explicit segment counts (1 to 4 chunks per segment, ragged tails), with the final state."""
+    B, H, D, M = 2, 2, 64, 32
+    cfg = small_cfg(dtype, B, H, N, D, M)
+    Q, K, V = synthetic.prefill_inputs(cfg, 14)
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    S = torch.full((B, H, D, M), float("nan"), device=DEV)
+    z = torch.full((B, H, D), float("nan"), device=DEV)
+    out = ea.forward_onepass(Qd, Kd, Vd, chunk, segments, S_out=S, z_out=z)
+    torch.cuda.synchronize()
+    ref, S_ref, z_ref = oracle.causal(f64(Q, dtype), f64(K, dtype), f64(V, dtype))
+    err = rowwise_rel(out.cpu().numpy(), ref)
+    assert err <= TOL[dtype], f"out {err:.3e}"
+    stol = 1e-5 if dtype == "f32" else TOL["bf16"]
+    assert whole_rel(S.cpu().numpy(), S_ref) <= stol
+    assert whole_rel(z.cpu().numpy(), z_ref) <= stol
+
+
+def test_onepass_long_lookback(ea):
+    """One chunk per segment, 512 segments per head."""
+    B, H, N, D, M = 1, 3, 8192, 32, 32
+    cfg = small_cfg("f32", B, H, N, D, M)
+    Q, K, V = synthetic.prefill_inputs(cfg, 15)
+    Qd, Kd, Vd = to_dev(Q, "f32"), to_dev(K, "f32"), to_dev(V, "f32")
+    out = ea.forward_onepass(Qd, Kd, Vd, 16, 512)
+    torch.cuda.synchronize()
+    ref = oracle.causal(f64(Q, "f32"), f64(K, "f32"), f64(V, "f32"))[0]
+    err = rowwise_rel(out.cpu().numpy(), ref)
+    assert err <= TOL["f32"], f"{err:.3e}"
+
+
+def test_onepass_repeat_on_one_workspace(ea):
+    """Repeated one-pass calls on one workspace, then the two-phase kernel on the same
+    (re-initialised) memory: every result matches the oracle."""
+    cfg = synthetic.WORKLOADS["prefill_f32_b8h8_n1024_d64"]
+    Q, K, V = synthetic.prefill_inputs(cfg, 2)
+    Qd, Kd, Vd = to_dev(Q, "f32"), to_dev(K, "f32"), to_dev(V, "f32")
+    ref = oracle.causal(f64(Q, "f32"), f64(K, "f32"), f64(V, "f32"))[0]
+    B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    ws = torch.empty(ea.fused_workspace_bytes(B, H, D, M, 8), dtype=torch.uint8, device=DEV)
+    ea.workspace_init(ws)
+    outs = [ea.forward_onepass(Qd, Kd, Vd, 32, 8, workspace=ws) for _ in range(3)]
+    ea.workspace_init(ws)
+    outs.append(ea.forward_fused(Qd, Kd, Vd, 32, 8, workspace=ws))
+    torch.cuda.synchronize()
+    for o in outs:
+        err = rowwise_rel(o.cpu().numpy(), ref)
+        assert err <= TOL["f32"], f"{err:.3e}"
+
+
 def test_fused_long_lookback(ea):
     """Many short segments per head: long look-back chains."""
     B, H, N, D, M = 1, 3, 8192, 32, 32
