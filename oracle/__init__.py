@@ -53,6 +53,8 @@ class Oracle:
         L.oracle_phi.argtypes = [_dp, _dp, _i64]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_causal.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int]
+        L.oracle_causal_from.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64,
+                                         ctypes.c_int]
         L.oracle_causal_rows.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64,
                                          ctypes.POINTER(_i64), _i64, _dp, ctypes.c_int]
         L.oracle_noncausal.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int]
@@ -84,6 +86,24 @@ class Oracle:
         S = np.empty((*lead, D, M))
         z = np.empty((*lead, D))
         self.L.oracle_causal(_p(Q), _p(K), _p(V), _p(out), _p(S), _p(z), BH, N, D, M, threads)
+        return out, S, z
+
+    def causal_from(self, Q, K, V, S0, z0, threads: int = 0):
+        """Causal outputs continued from the carried state (S0 [..., D, M], z0 [..., D]).
+
+        Returns (out [..., N, M], S [..., D, M], z [..., D]) like causal().
+        """
+        Q, K, V, S0, z0 = _f64(Q), _f64(K), _f64(V), _f64(S0), _f64(z0)
+        *lead, N, D = Q.shape
+        M = V.shape[-1]
+        assert K.shape == Q.shape and tuple(V.shape[:-1]) == tuple(Q.shape[:-1])
+        assert tuple(S0.shape) == (*lead, D, M) and tuple(z0.shape) == (*lead, D)
+        BH = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, N, M))
+        S = np.empty((*lead, D, M))
+        z = np.empty((*lead, D))
+        self.L.oracle_causal_from(_p(Q), _p(K), _p(V), _p(S0), _p(z0), _p(out), _p(S), _p(z), BH, N, D, M,
+                                  threads)
         return out, S, z
 
     def causal_rows(self, Qh, Kh, Vh, rows, threads: int = 0) -> np.ndarray:
@@ -152,6 +172,10 @@ def phi(x):
 
 def causal(Q, K, V, threads: int = 0):
     return default().causal(Q, K, V, threads)
+
+
+def causal_from(Q, K, V, S0, z0, threads: int = 0):
+    return default().causal_from(Q, K, V, S0, z0, threads)
 
 
 def causal_rows(Qh, Kh, Vh, rows, threads: int = 0):

@@ -95,6 +95,45 @@ void oracle_causal(const double *Q, const double *K, const double *V, double *ou
     }
 }
 
+/* Causal attention continued from a carried state: the same running sums, but
+ * the memories start at (S0, z0) -- the state left by the positions before this
+ * block -- instead of zero.  (Page "Transformers are RNNs", Proposed method: the
+ * causal model is an RNN whose memories S and z carry all earlier positions.)
+ * S0 [BH][D][M], z0 [BH][D]; S_out / z_out (may be NULL) receive the final state. */
+void oracle_causal_from(const double *Q, const double *K, const double *V,
+                        const double *S0, const double *z0, double *out,
+                        double *S_out, double *z_out,
+                        int64_t BH, int64_t N, int64_t D, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        double *S = (double *)malloc((size_t)(D * M) * sizeof(double));
+        double *z = (double *)malloc((size_t)D * sizeof(double));
+        memcpy(S, S0 + h * D * M, (size_t)(D * M) * sizeof(double));
+        memcpy(z, z0 + h * D, (size_t)D * sizeof(double));
+        const double *Qh = Q + h * N * D, *Kh = K + h * N * D, *Vh = V + h * N * M;
+        double *Oh = out + h * N * M;
+        for (int64_t i = 0; i < N; ++i) {
+            const double *k = Kh + i * D, *q = Qh + i * D, *v = Vh + i * M;
+            for (int64_t d = 0; d < D; ++d) {
+                double f = oracle_phi1(k[d]);
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += f * v[m];
+                z[d] += f;
+            }
+            double den = 0.0;
+            for (int64_t d = 0; d < D; ++d) den += oracle_phi1(q[d]) * z[d];
+            for (int64_t m = 0; m < M; ++m) {
+                double num = 0.0;
+                for (int64_t d = 0; d < D; ++d) num += oracle_phi1(q[d]) * S[d * M + m];
+                Oh[i * M + m] = num / den;
+            }
+        }
+        if (S_out) memcpy(S_out + h * D * M, S, (size_t)(D * M) * sizeof(double));
+        if (z_out) memcpy(z_out + h * D, z, (size_t)D * sizeof(double));
+        free(S); free(z);
+    }
+}
+
 /* Causal attention straight from its definition, for selected rows of ONE head:
  *   out_i = sum_{j<=i} (phi(q_i).phi(k_j)) v_j / sum_{j<=i} phi(q_i).phi(k_j).
  * (Page "Transformers are RNNs", Proposed method: the softmax similarity is

@@ -269,7 +269,26 @@ def pin_chunked(o, fails):
             _close(f"chunked state C{C} N{N}", cS, S[0], 1e-12, fails)
 
 
-ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked]
+def pin_continue(o, fails):
+    """A sequence cut in two: the second part continued from the state of the first
+    (computed here with numpy, phi(K1)^T V1 and the column sums of phi(K1)) gives the
+    rows of the whole sequence, checked against the quadratic masked form."""
+    rng = np.random.default_rng(17)
+    for (N, n1, D, M) in [(9, 4, 3, 2), (30, 1, 2, 5), (40, 25, 16, 3), (20, 19, 4, 4)]:
+        Q, K, V = _rand(rng, N, D, M)
+        want = brute_causal(Q, K, V)
+        S0 = np_phi(K[:n1]).T @ V[:n1]
+        z0 = np_phi(K[:n1]).sum(axis=0)
+        out, S, z = o.causal_from(Q[None, n1:], K[None, n1:], V[None, n1:], S0[None], z0[None])
+        _close(f"continue rows N{N} n1={n1}", out[0], want[n1:], 1e-11, fails)
+        _close(f"continue final S N{N} n1={n1}", S[0], np_phi(K).T @ V, 1e-11, fails)
+        _close(f"continue final z N{N} n1={n1}", z[0], np_phi(K).sum(axis=0), 1e-12, fails)
+        # from the zero state it is plain causal attention
+        zo = o.causal_from(Q[None], K[None], V[None], np.zeros((1, D, M)), np.zeros((1, D)))[0]
+        _close(f"continue from zero N{N}", zo[0], want, 1e-11, fails)
+
+
+ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked, pin_continue]
 
 
 def run_all(o, pins=ALL_PINS):

@@ -34,6 +34,12 @@ MUTANTS = {
     "noncausal_wrong_z": ("for (int64_t d = 0; d < D; ++d) den += g[d] * z[d];\n            for (int64_t m = 0; m < M; ++m) {\n                double num = 0.0;\n                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];\n                Oh[i * M + m] = num / den;\n            }\n        }\n        free(S); free(z); free(g);",
                           "for (int64_t d = 0; d < D; ++d) den += g[d] * z[0];\n            for (int64_t m = 0; m < M; ++m) {\n                double num = 0.0;\n                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];\n                Oh[i * M + m] = num / den;\n            }\n        }\n        free(S); free(z); free(g);"),
     "decode_overwrites_z": ("zh[d] += f;", "zh[d] = f;"),
+    "continue_ignores_z0": ("memcpy(z, z0 + h * D, (size_t)D * sizeof(double));",
+                            "memset(z, 0, (size_t)D * sizeof(double));"),
+    "continue_ignores_S0": ("memcpy(S, S0 + h * D * M, (size_t)(D * M) * sizeof(double));",
+                            "memset(S, 0, (size_t)(D * M) * sizeof(double));"),
+    "continue_transposed_update": ("for (int64_t m = 0; m < M; ++m) S[d * M + m] += f * v[m];",
+                                   "for (int64_t m = 0; m < M; ++m) S[m * D + d] += f * v[m];"),
     "decode_den_uses_k": ("den += oracle_phi1(qh[d]) * zh[d];", "den += oracle_phi1(kh[d]) * zh[d];"),
     "decode_reads_before_update": (
         "        for (int64_t d = 0; d < D; ++d) {\n            double f = oracle_phi1(kh[d]);\n            for (int64_t m = 0; m < M; ++m) Sh[d * M + m] += f * vh[m];\n            zh[d] += f;\n        }\n        double den = 0.0;\n        for (int64_t d = 0; d < D; ++d) den += oracle_phi1(qh[d]) * zh[d];\n        for (int64_t m = 0; m < M; ++m) {\n            double num = 0.0;\n            for (int64_t d = 0; d < D; ++d) num += oracle_phi1(qh[d]) * Sh[d * M + m];\n            oh[m] = num / den;\n        }\n",
