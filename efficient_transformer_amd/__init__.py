@@ -7,7 +7,9 @@ argument marshalling only; PyTorch supplies device memory and streams.
 from .linattn import (  # noqa: F401
     LinAttnError,
     decode_step,
+    decode_steps,
     forward_chunked,
+    forward_continue,
     forward_fused,
     forward_onepass,
     forward_plan,

@@ -158,9 +158,11 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
     (void)hipGetLastError();  // clear a stale error so that the checks below report this call's launches
     hipError_t e = hipSuccess;
     if (causal && p.onepass) {
-        e = la::prefill_onepass(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out, s);
+        e = la::prefill_onepass(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out,
+                                nullptr, nullptr, s);
     } else if (causal) {
-        e = la::prefill_fused(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out, s);
+        e = la::prefill_fused(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out, nullptr,
+                              nullptr, s);
     } else {
         float *ws = static_cast<float *>(workspace);
         e = la::prefill_states(dt, Di, Mi, C, K, V, ws, (int)BH, (int)N, G, cps, G, s);
@@ -168,6 +170,48 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
         if (e == hipSuccess)
             e = la::prefill_outputs(dt, Di, Mi, C, Q, K, V, out, ws, (int)BH, (int)N, G, cps, 0, nullptr, nullptr, s);
     }
+    return hip_status(e);
+}
+
+LA_API int la_forward_continue(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                               int64_t N, int64_t D, int64_t M, int dtype, int chunk_req, const float *S_in,
+                               const float *z_in, void *workspace, size_t workspace_bytes, float *S_out,
+                               float *z_out, void *stream) {
+    Plan p;
+    int st = make_plan(B, H, N, D, M, 1, dtype, chunk_req, &p);
+    if (st != LA_OK) return st;
+    if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_in && (!aligned16(S_in) || !aligned16(z_in))) return LA_ERR_INVALID_ARG;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+    const int64_t BH = B * H;
+    if (BH == 0) return LA_OK;
+    hipStream_t s = as_stream(stream);
+    if (N == 0) {
+        if (S_out == nullptr) return LA_OK;
+        (void)hipGetLastError();
+        if (S_in == nullptr) {
+            hipError_t e = la::fill_zero(S_out, (size_t)(BH * D * M), s);
+            if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * D), s);
+            return hip_status(e);
+        }
+        hipError_t e = hipSuccess;
+        if (S_out != S_in)
+            e = hipMemcpyAsync(S_out, S_in, (size_t)(BH * D * M) * sizeof(float), hipMemcpyDeviceToDevice, s);
+        if (e == hipSuccess && z_out != z_in)
+            e = hipMemcpyAsync(z_out, z_in, (size_t)(BH * D) * sizeof(float), hipMemcpyDeviceToDevice, s);
+        return hip_status(e);
+    }
+    if (!Q || !K || !V || !out) return LA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+    if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) return LA_ERR_WORKSPACE;
+    if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    const int dt = dtype, Di = (int)D, Mi = (int)M, C = p.chunk, G = p.segments, cps = p.chunks_per_segment;
+    hipError_t e = p.onepass ? la::prefill_onepass(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps,
+                                                   S_out, z_out, S_in, z_in, s)
+                             : la::prefill_fused(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps,
+                                                 S_out, z_out, S_in, z_in, s);
     return hip_status(e);
 }
 
@@ -209,14 +253,17 @@ int cps_of(int64_t N, int chunk, int segments) {
 namespace {
 // Shared validation and launch of the two explicit-plan causal entry points.
 int forward_explicit(bool onepass, const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                     int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
-                     size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+                     int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, const float *S_in,
+                     const float *z_in, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
+                     void *stream) {
     int st = check_shape(B, H, N, D, M, dtype);
     if (st != LA_OK) return st;
     if (chunk != 16 && chunk != 32 && chunk != 64) return LA_ERR_UNSUPPORTED;
     if (!la::prefill_supported(dtype, (int)D, (int)M, chunk)) return LA_ERR_UNSUPPORTED;
     if (onepass && !la::prefill_onepass_supported(dtype, (int)D, (int)M, chunk)) return LA_ERR_UNSUPPORTED;
     if (segments < 1) return LA_ERR_INVALID_ARG;
+    if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_in && (!aligned16(S_in) || !aligned16(z_in))) return LA_ERR_INVALID_ARG;
     if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
     if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
     const int64_t BH = B * H;
@@ -234,8 +281,17 @@ int forward_explicit(bool onepass, const void *Q, const void *K, const void *V, 
     hipStream_t s = as_stream(stream);
     if (N == 0) {
         if (S_out == nullptr) return LA_OK;
-        hipError_t e = la::fill_zero(S_out, (size_t)(BH * D * M), s);
-        if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * D), s);
+        (void)hipGetLastError();
+        hipError_t e = hipSuccess;
+        if (S_in == nullptr) {
+            e = la::fill_zero(S_out, (size_t)(BH * D * M), s);
+            if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * D), s);
+        } else {
+            if (S_out != S_in)
+                e = hipMemcpyAsync(S_out, S_in, (size_t)(BH * D * M) * sizeof(float), hipMemcpyDeviceToDevice, s);
+            if (e == hipSuccess && z_out != z_in)
+                e = hipMemcpyAsync(z_out, z_in, (size_t)(BH * D) * sizeof(float), hipMemcpyDeviceToDevice, s);
+        }
         return hip_status(e);
     }
     if (!Q || !K || !V || !out) return LA_ERR_INVALID_ARG;
@@ -243,24 +299,26 @@ int forward_explicit(bool onepass, const void *Q, const void *K, const void *V, 
     (void)hipGetLastError();
     const int cps = cps_of(N, chunk, segments);
     return hip_status(onepass ? la::prefill_onepass(dtype, (int)D, (int)M, chunk, Q, K, V, out, workspace, (int)BH,
-                                                    (int)N, segments, cps, S_out, z_out, s)
+                                                    (int)N, segments, cps, S_out, z_out, S_in, z_in, s)
                               : la::prefill_fused(dtype, (int)D, (int)M, chunk, Q, K, V, out, workspace, (int)BH,
-                                                  (int)N, segments, cps, S_out, z_out, s));
+                                                  (int)N, segments, cps, S_out, z_out, S_in, z_in, s));
 }
 }  // namespace
 
 LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                            int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
-                            size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
-    return forward_explicit(false, Q, K, V, out, B, H, N, D, M, dtype, chunk, segments, workspace, workspace_bytes,
-                            S_out, z_out, stream);
+                            int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, const float *S_in,
+                            const float *z_in, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
+                            void *stream) {
+    return forward_explicit(false, Q, K, V, out, B, H, N, D, M, dtype, chunk, segments, S_in, z_in, workspace,
+                            workspace_bytes, S_out, z_out, stream);
 }
 
 LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                              int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, void *workspace,
-                              size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
-    return forward_explicit(true, Q, K, V, out, B, H, N, D, M, dtype, chunk, segments, workspace, workspace_bytes,
-                            S_out, z_out, stream);
+                              int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, const float *S_in,
+                              const float *z_in, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
+                              void *stream) {
+    return forward_explicit(true, Q, K, V, out, B, H, N, D, M, dtype, chunk, segments, S_in, z_in, workspace,
+                            workspace_bytes, S_out, z_out, stream);
 }
 
 LA_API int la_segment_states(const void *K, const void *V, float *ws, size_t ws_bytes, int64_t B, int64_t H,
@@ -325,6 +383,22 @@ LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, cons
         return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
     return hip_status(la::decode_step(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), as_stream(stream)));
+}
+
+LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, const void *v, float *out, int64_t B,
+                           int64_t H, int64_t T, int64_t D, int64_t M, int dtype, void *stream) {
+    if (B < 0 || H < 0 || T < 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (B * H > INT_MAX || T > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (B * H > 0 && T > INT64_MAX / (B * H * (D > M ? D : M))) return LA_ERR_UNSUPPORTED;
+    if (B * H == 0 || T == 0) return LA_OK;
+    if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
+    if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::decode_steps(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), (int)T,
+                                       as_stream(stream)));
 }
 
 }  // extern "C"

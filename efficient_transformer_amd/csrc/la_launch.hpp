@@ -26,12 +26,12 @@ hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const 
                            const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out, float *z_out,
                            hipStream_t stream);
 hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
-                         void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+                         void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream);
 // One-pass causal kernel: segments of at most 4 chunks (see la_prefill.hpp).
 constexpr int kOnePassMaxChunks = 4;
 bool prefill_onepass_supported(int dtype, int D, int M, int C);
 hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
-                           void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+                           void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream);
 size_t prefill_lds_bytes(int dtype, int D, int M, int C);
 hipError_t prefill_scan(float *ws, int BH, int D, int M, int G, int nstates, float *S_out, float *z_out,
                         hipStream_t stream);
@@ -39,16 +39,19 @@ hipError_t fill_zero(float *p, size_t n, hipStream_t stream);
 
 hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
                        float *out, int BH, hipStream_t stream);
+hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
+                        float *out, int BH, int Tn, hipStream_t stream);
 
 // per element type (defined in la_prefill_f32.hip / la_prefill_bf16.hip)
 hipError_t prefill_fused_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
-                             int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+                             int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream);
 hipError_t prefill_fused_bf16(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
-                              int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+                              int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream);
 hipError_t prefill_onepass_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
-                               void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream);
+                               void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream);
 hipError_t prefill_onepass_bf16(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
                                 void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out,
+                                const float *S_in, const float *z_in,
                                 hipStream_t stream);
 bool prefill_onepass_supported_f32(int D, int M, int C);
 bool prefill_onepass_supported_bf16(int D, int M, int C);

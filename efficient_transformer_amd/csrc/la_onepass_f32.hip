@@ -15,10 +15,11 @@ bool prefill_onepass_supported_f32(int D, int M, int C) {
 }
 
 hipError_t prefill_onepass_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
-                             int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream) {
+                             int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
+                             const float *z_in, hipStream_t stream) {
 #define X(D_, M_, C_) \
     if (D == D_ && M == M_ && C == C_) \
-        return run_onepass<float, D_, M_, C_>(Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream);
+        return run_onepass<float, D_, M_, C_>(Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
     LA_FOR_ALL(X)
 #undef X
     return hipErrorInvalidValue;

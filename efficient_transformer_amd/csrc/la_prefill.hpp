@@ -596,16 +596,20 @@ struct Engine {
     __device__ __forceinline__ void state_store(const f32x4 (&acc)[DT][MTW], float z, float *slot) const {
         state_store(acc, z, slot, slot + D * M);
     }
-    __device__ __forceinline__ void state_add(f32x4 (&acc)[DT][MTW], float &z, const float *slot) const {
+    __device__ __forceinline__ void state_add(f32x4 (&acc)[DT][MTW], float &z, const float *Sd,
+                                              const float *zd) const {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int i = 0; i < MTW; ++i) {
                 if (!owns(i)) continue;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[dt][i][r] += slot[(dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16];
+                for (int r = 0; r < 4; ++r) acc[dt][i][r] += Sd[(dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16];
             }
-        if (tid < D) z += slot[D * M + tid];
+        if (tid < D) z += zd[tid];
+    }
+    __device__ __forceinline__ void state_add(f32x4 (&acc)[DT][MTW], float &z, const float *slot) const {
+        state_add(acc, z, slot, slot + D * M);
     }
     // Agent-coherent variants for the states exchanged between workgroups: every
     // access carries the agent scope (write-through stores, loads that miss
@@ -886,7 +890,8 @@ template <typename T, int D, int M, int C>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                 const T *__restrict__ V, float *__restrict__ out,
                                                                 void *ws_raw, int BH, int N, int G_, int CPS,
-                                                                float *__restrict__ S_out, float *__restrict__ z_out) {
+                                                                float *__restrict__ S_out, float *__restrict__ z_out,
+                                                                const float *S_in, const float *z_in) {
     using Gc = Cfg<T, D, M, C>;
     using En = Engine<T, D, M, C>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
@@ -926,10 +931,27 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const bool run_a = G_ > 1 && (!last || want_final);
     if (run_a) phase_a<T, D, M, C>(e, Kh, Vh, N, c0, c1, acc, zacc);
     const size_t my = (size_t)bh * G_ + s;
-    // publish the segment aggregate before any other load is in flight (the
+    // Prefix of the segment: the carried initial state (segment 0, when given),
+    // later the look-back's sum of the earlier segments.
+    f32x4 pre[Gc::DT][Gc::MTW];
+    En::zero_state(pre);
+    float zpre = 0.0f;
+    const bool init = S_in != nullptr && s == 0;
+    if (init) e.state_add(pre, zpre, S_in + (size_t)bh * D * M, z_in + (size_t)bh * D);
+    // publish the segment aggregate (segment 0: with the initial state, so that
+    // it stays the inclusive prefix) before any other load is in flight (the
     // publication waits for every outstanding memory operation of the wave)
     if (G_ > 1 && !last) {
-        e.state_store_coherent(acc, zacc, ws.agg + my * Gc::E);
+        if (init) {
+            f32x4 a0[Gc::DT][Gc::MTW];
+#pragma unroll
+            for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < Gc::MTW; ++i) a0[dt][i] = acc[dt][i] + pre[dt][i];
+            e.state_store_coherent(a0, zacc + zpre, ws.agg + my * Gc::E);
+        } else {
+            e.state_store_coherent(acc, zacc, ws.agg + my * Gc::E);
+        }
         e.publish_flag(&ws.flags[my], ep | 1u);
     }
 
@@ -949,9 +971,6 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         e.intra(o);
     }
 
-    f32x4 pre[Gc::DT][Gc::MTW];
-    En::zero_state(pre);
-    float zpre = 0.0f;
     bool failed = false;
     if (G_ > 1 && s > 0) {
         failed = !look_back<T, D, M, C>(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
@@ -1015,7 +1034,8 @@ struct OnePassLds {
 template <typename T, int D, int M, int C>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void onepass_causal_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, float *__restrict__ out,
-    void *ws_raw, int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out) {
+    void *ws_raw, int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out,
+    const float *S_in, const float *z_in) {
     using Gc = Cfg<T, D, M, C>;
     using L1 = OnePassLds<T, D, M, C>;
     using En = Engine<T, D, M, C>;
@@ -1103,16 +1123,28 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     }
 
     const size_t my = (size_t)bh * G_ + s;
-    if (G_ > 1 && !last) {
-        e.state_store_coherent(S, z, ws.agg + my * Gc::E);
-        e.publish_flag(&ws.flags[my], ep | 1u);
-    }
+    // prefix: the carried initial state for segment 0 (when given), else the look-back's
     f32x4 pre[Gc::DT][Gc::MTW];
     En::zero_state(pre);
     float zpre = 0.0f;
+    const bool init = S_in != nullptr && s == 0;
+    if (init) e.state_add(pre, zpre, S_in + (size_t)bh * D * M, z_in + (size_t)bh * D);
+    if (G_ > 1 && !last) {
+        if (init) {
+            f32x4 a0[Gc::DT][Gc::MTW];
+#pragma unroll
+            for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+                for (int i = 0; i < Gc::MTW; ++i) a0[dt][i] = S[dt][i] + pre[dt][i];
+            e.state_store_coherent(a0, z + zpre, ws.agg + my * Gc::E);
+        } else {
+            e.state_store_coherent(S, z, ws.agg + my * Gc::E);
+        }
+        e.publish_flag(&ws.flags[my], ep | 1u);
+    }
     bool failed = false;
-    const bool has_prefix = G_ > 1 && s > 0;
-    if (has_prefix) {
+    const bool has_prefix = (G_ > 1 && s > 0) || init;
+    if (G_ > 1 && s > 0) {
         failed = !look_back<T, D, M, C>(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
         if (!last) publish_inclusive<T, D, M, C>(e, ws, my, ep, pre, zpre, S, z, failed);
     }
@@ -1206,7 +1238,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C>
 hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
-                     int CPS, float *S_out, float *z_out, hipStream_t stream) {
+                     int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
     if constexpr (!Gc::fits) {
         return hipErrorInvalidValue;
@@ -1214,14 +1246,15 @@ hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, vo
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
         hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
-                           (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out);
+                           (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out, S_in, z_in);
         return hipGetLastError();
     }
 }
 
 template <typename T, int D, int M, int C>
 hipError_t run_onepass(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
-                       int CPS, float *S_out, float *z_out, hipStream_t stream) {
+                       int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+                       hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
     if constexpr (!(Gc::fits && OnePassLds<T, D, M, C>::fits)) {
         return hipErrorInvalidValue;
@@ -1229,7 +1262,8 @@ hipError_t run_onepass(const void *Q, const void *K, const void *V, float *out, 
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
         hipLaunchKernelGGL((onepass_causal_kernel<T, D, M, C>), dim3((unsigned)(BH * G_)), dim3(Gc::THREADS), 0,
-                           stream, (const T *)Q, (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out);
+                           stream, (const T *)Q, (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out,
+                           S_in, z_in);
         return hipGetLastError();
     }
 }

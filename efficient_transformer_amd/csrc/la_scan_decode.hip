@@ -58,15 +58,17 @@ hipError_t fill_zero(float *p, size_t n, hipStream_t stream) {
 }
 
 hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
-                         void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream) {
-    return dtype == 0 ? prefill_fused_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream)
-                      : prefill_fused_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream);
+                         void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
+                         const float *z_in, hipStream_t stream) {
+    return dtype == 0 ? prefill_fused_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+                      : prefill_fused_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
 }
 
 hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
-                           void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, hipStream_t stream) {
-    return dtype == 0 ? prefill_onepass_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream)
-                      : prefill_onepass_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, stream);
+                           void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
+                         const float *z_in, hipStream_t stream) {
+    return dtype == 0 ? prefill_onepass_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+                      : prefill_onepass_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
 }
 
 bool prefill_onepass_supported(int dtype, int D, int M, int C) {
@@ -224,6 +226,131 @@ hipError_t run_decode(float *S, float *z, const void *q, const void *k, const vo
     hipLaunchKernelGGL((decode_kernel<T, D, M>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream, S, z,
                        (const T *)q, (const T *)k, (const T *)v, out);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Recurrent decode over T consecutive tokens of every head, the state held in
+// registers for the whole call (read once, written once).  The same RNN step as
+// decode_kernel, repeated: for t = 0..T-1
+//   S += phi(k_t) v_t^T;  z += phi(k_t);  out_t = phi(q_t)^T S / phi(q_t).z
+// Thread layout as decode_kernel; each thread also keeps z of its own rows (the
+// rows d = roff + p*RP, replicated over the LPR lanes of a row), so phi(q).z is
+// reduced together with the numerator.  Tokens are staged TB at a time in LDS
+// (phi applied once); q, k [BH][T][D], v, out [BH][T][M].
+// ---------------------------------------------------------------------------
+constexpr int kDecodeTokenBlock = 16;
+
+template <typename T, int D, int M>
+__global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_steps_kernel(
+    float *__restrict__ S, float *__restrict__ z, const T *__restrict__ q, const T *__restrict__ k,
+    const T *__restrict__ v, float *__restrict__ out, int Tn) {
+    using G = DecCfg<D, M>;
+    constexpr int TB = kDecodeTokenBlock;
+    __shared__ float sq[TB][D], sk[TB][D];
+    __shared__ f32x4 sv[TB][G::LPR];
+    __shared__ f32x4 sred[2][G::NW][G::LPR];
+    __shared__ float sden[2][G::NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const size_t bh = blockIdx.x;
+    const int col4 = tid % G::LPR, roff = tid / G::LPR;
+
+    f32x4 *Sh = reinterpret_cast<f32x4 *>(S + bh * D * M);
+    f32x4 Sv[G::PASSES];
+    float zl[G::PASSES];
+#pragma unroll
+    for (int p = 0; p < G::PASSES; ++p) {
+        Sv[p] = Sh[(roff + p * G::RP) * G::LPR + col4];
+        zl[p] = z[bh * D + roff + p * G::RP];
+    }
+    const size_t tok0 = bh * (size_t)Tn;
+    for (int t0 = 0; t0 < Tn; t0 += TB) {
+        const int nt = min(TB, Tn - t0);
+        __syncthreads();  // the previous block's readers are done
+        const T *qb = q + (tok0 + t0) * D, *kb = k + (tok0 + t0) * D;
+        for (int e = tid; e < nt * D; e += G::THREADS) {
+            sq[e / D][e % D] = phi(to_f32(qb[e]));
+            sk[e / D][e % D] = phi(to_f32(kb[e]));
+        }
+        const T *vb = v + (tok0 + t0) * M;
+        for (int e = tid; e < nt * G::LPR; e += G::THREADS) sv[e / G::LPR][e % G::LPR] = load4<T>(vb + e * 4);
+        __syncthreads();
+        for (int t = 0; t < nt; ++t) {
+            const f32x4 vv = sv[t][col4];
+            f32x4 num = zero4();
+            float dn = 0.0f;
+#pragma unroll
+            for (int p = 0; p < G::PASSES; ++p) {
+                const int d = roff + p * G::RP;
+                const float fk = sk[t][d], fq = sq[t][d];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    Sv[p][j] += fk * vv[j];
+                    num[j] += fq * Sv[p][j];
+                }
+                zl[p] += fk;
+                dn += fq * zl[p];
+            }
+            // sum over the lanes of the wavefront that share col4 (distinct rows)
+#pragma unroll
+            for (int sh = G::LPR; sh < 64; sh <<= 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) num[j] += __shfl_xor(num[j], sh, 64);
+                dn += __shfl_xor(dn, sh, 64);
+            }
+            if (G::NW > 1) {
+                const int buf = t & 1;  // two buffers: one barrier per token
+                if (lane < G::LPR) sred[buf][w][lane] = num;
+                if (lane == 0) sden[buf][w] = dn;
+                __syncthreads();
+                if (w == 0 && lane < G::LPR) {
+                    num = sred[buf][0][lane];
+                    dn = sden[buf][0];
+#pragma unroll
+                    for (int ww = 1; ww < G::NW; ++ww) {
+                        const f32x4 o = sred[buf][ww][lane];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) num[j] += o[j];
+                        dn += sden[buf][ww];
+                    }
+                }
+            }
+            if (w == 0 && lane < G::LPR) {
+                const float inv = 1.0f / dn;
+                f32x4 o;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[j] = num[j] * inv;
+                *reinterpret_cast<f32x4 *>(out + (tok0 + t0 + t) * M + lane * 4) = o;
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < G::PASSES; ++p) {
+        Sh[(roff + p * G::RP) * G::LPR + col4] = Sv[p];
+        if (col4 == 0) z[bh * D + roff + p * G::RP] = zl[p];
+    }
+}
+
+template <typename T, int D, int M>
+hipError_t run_decode_steps(float *S, float *z, const void *q, const void *k, const void *v, float *out, int BH,
+                            int Tn, hipStream_t stream) {
+    if (BH <= 0 || Tn <= 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_steps_kernel<T, D, M>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream,
+                       S, z, (const T *)q, (const T *)k, (const T *)v, out, Tn);
+    return hipGetLastError();
+}
+
+hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
+                        float *out, int BH, int Tn, hipStream_t stream) {
+#define X(D_, M_)                                                                                  \
+    if (D == D_ && M == M_)                                                                        \
+        return dtype == 0 ? run_decode_steps<float, D_, M_>(S, z, q, k, v, out, BH, Tn, stream)    \
+                          : run_decode_steps<bf16, D_, M_>(S, z, q, k, v, out, BH, Tn, stream);
+#define XM(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
+    XM(16) XM(32) XM(64) XM(128)
+#undef XM
+#undef X
+    return hipErrorInvalidValue;
 }
 
 hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,

@@ -30,15 +30,18 @@ SIGNATURES = {
     "la_forward_chunked": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _vp, _sz, _vp, _vp, _vp]),
     "la_workspace_init": (_int, [_vp, _sz, _vp]),
-    "la_forward_fused": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz,
-                                _vp, _vp, _vp]),
-    "la_forward_onepass": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz,
-                                  _vp, _vp, _vp]),
+    "la_forward_continue": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp,
+                                   _vp, _sz, _vp, _vp, _vp]),
+    "la_forward_fused": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp,
+                                _vp, _sz, _vp, _vp, _vp]),
+    "la_forward_onepass": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp,
+                                  _vp, _sz, _vp, _vp, _vp]),
     "la_segment_states": (_int, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
     "la_segment_scan": (_int, [_vp, _sz, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "la_segment_outputs": (_int, [_vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _int, _vp, _vp, _vp]),
     "la_decode_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
+    "la_decode_steps": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
 }
 
 
@@ -196,17 +199,46 @@ def fused_workspace_bytes(B, H, D, M, segments) -> int:
     return (64 + 64 * ((bhg + 63) // 64)) * 4 + 2 * bhg * (D * M + D) * 4
 
 
-def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None):
+def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None,
+                  S_in=None, z_in=None):
     """The causal two-phase fused kernel with an explicit plan (chunk, segments)."""
-    return _forward_explicit("la_forward_fused", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream)
+    return _forward_explicit("la_forward_fused", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream,
+                             S_in, z_in)
 
 
-def forward_onepass(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None):
+def forward_onepass(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None,
+                    S_in=None, z_in=None):
     """The causal one-pass kernel with an explicit plan (segments of at most 4 chunks)."""
-    return _forward_explicit("la_forward_onepass", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream)
+    return _forward_explicit("la_forward_onepass", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream,
+                             S_in, z_in)
 
 
-def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream):
+def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_out=None, z_out=None, stream=None):
+    """Causal attention continuing from the carried state (S_in [B,H,D,M], z_in [B,H,D], fp32)."""
+    import torch
+    B, H, N, D = Q.shape
+    M = V.shape[-1]
+    dev = Q.device
+    _require(K, "K", (B, H, N, D), Q.dtype, dev)
+    _require(V, "V", (B, H, N, M), Q.dtype, dev)
+    if S_in is not None:
+        _require(S_in, "S_in", (B, H, D, M), torch.float32, dev)
+        _require(z_in, "z_in", (B, H, D), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
+    dt = _dtype_code(Q)
+    C, G, need = forward_plan(B, H, N, D, M, True, dt, chunk)
+    if workspace is None and need > 0:
+        workspace = _cached_workspace(need, dev, stream, ("chunked", B * H, N, D, M, True, dt, C, G))
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().la_forward_continue(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, dt, chunk, _ptr(S_in),
+                                   _ptr(z_in), _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out),
+                                   _stream(stream, dev))
+    _check(st, "la_forward_continue")
+    return out
+
+
+def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream, S_in, z_in):
     import torch
     B, H, N, D = Q.shape
     M = V.shape[-1]
@@ -220,7 +252,8 @@ def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_o
         workspace = _cached_workspace(need, dev, stream, (name, B * H, N, D, M, _dtype_code(Q), chunk, segments))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(Q), chunk,
-                              segments, _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
+                              segments, _ptr(S_in), _ptr(z_in), _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out),
+                              _stream(stream, dev))
     _check(st, name)
     return out
 
@@ -266,4 +299,27 @@ def decode_step(S, z, q, k, v, out=None, stream=None):
     st = lib().la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, D, M,
                               _dtype_code(q), _stream(stream, dev))
     _check(st, "la_decode_step")
+    return out
+
+
+def decode_steps(S, z, q, k, v, out=None, stream=None):
+    """T recurrent steps in one call: S [B,H,D,M], z [B,H,D] (float32, updated in place);
+    q, k [B,H,T,D]; v [B,H,T,M]; returns out [B,H,T,M]."""
+    import torch
+    if S.dim() != 4 or q.dim() != 4:
+        raise ValueError("S must be [B, H, D, M] and q [B, H, T, D]")
+    B, H, D, M = S.shape
+    T = q.shape[2]
+    dev = S.device
+    _require(S, "S", (B, H, D, M), torch.float32)
+    _require(z, "z", (B, H, D), torch.float32, dev)
+    _require(q, "q", (B, H, T, D), None, dev)
+    _require(k, "k", (B, H, T, D), q.dtype, dev)
+    _require(v, "v", (B, H, T, M), q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, H, T, M), dtype=torch.float32, device=dev)
+    _require(out, "out", (B, H, T, M), torch.float32, dev)
+    st = lib().la_decode_steps(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, D, M,
+                               _dtype_code(q), _stream(stream, dev))
+    _check(st, "la_decode_steps")
     return out

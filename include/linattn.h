@@ -112,6 +112,27 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
                               void *workspace, size_t workspace_bytes,
                               float *S_out, float *z_out, void *stream);
 
+/*
+ * Causal attention continuing a sequence from a carried state: the positions
+ * of this call come after earlier ones whose state is (S_in, z_in), so
+ *   out_i = phi(q_i)^T (S_in + S_i) / phi(q_i)^T (z_in + z_i)
+ * with S_i, z_i summed over this call's positions j <= i (page "Transformers
+ * are RNNs", Proposed method: the causal model is an RNN whose memories S and z
+ * carry every earlier position, so a sequence can be processed in pieces).
+ * S_in [B][H][D][M], z_in [B][H][D] fp32: both, or neither (then the state is
+ * zero and the call equals la_forward_chunked with causal = 1).  S_out / z_out
+ * receive the state after the last position; they may be S_in / z_in
+ * themselves (in-place continuation).  Plan, chunk_req and workspace as for
+ * la_forward_chunked with causal = 1 (la_forward_workspace_bytes(..., 1, ...)).
+ * With N = 0, S_out / z_out receive a copy of S_in / z_in (zeros without them).
+ */
+LA_API int la_forward_continue(const void *Q, const void *K, const void *V, float *out,
+                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                               int dtype, int chunk_req,
+                               const float *S_in, const float *z_in,
+                               void *workspace, size_t workspace_bytes,
+                               float *S_out, float *z_out, void *stream);
+
 /* Zero a workspace (an enqueued fill kernel; graph-capture safe). bytes % 4 == 0. */
 LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
@@ -120,11 +141,13 @@ LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stre
  * (16, 32 or 64) and segments (each segment must own at least one chunk).
  * Workspace: 0 bytes when segments == 1, else
  *   (64 + 64*ceil(B*H*segments/64)) * 4 + 2 * B*H*segments * (D*M + D) * 4 bytes,
- * initialised as for la_forward_chunked.  S_out / z_out as for la_forward_chunked.
+ * initialised as for la_forward_chunked.  S_in / z_in as for la_forward_continue
+ * (NULL: start from zero); S_out / z_out as for la_forward_chunked.
  */
 LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out,
                             int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                             int dtype, int chunk, int segments,
+                            const float *S_in, const float *z_in,
                             void *workspace, size_t workspace_bytes,
                             float *S_out, float *z_out, void *stream);
 
@@ -139,10 +162,12 @@ LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *
  * "Transformers are RNNs", Proposed method: the same cumulative sums, split
  * at the segment start).  Workspace size and initialisation as for
  * la_forward_fused (the two kernels share the format, not a live workspace).
+ * S_in / z_in as for la_forward_continue (NULL: start from zero).
  */
 LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, float *out,
                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                               int dtype, int chunk, int segments,
+                              const float *S_in, const float *z_in,
                               void *workspace, size_t workspace_bytes,
                               float *S_out, float *z_out, void *stream);
 
@@ -192,6 +217,19 @@ LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, float
 LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, const void *v,
                           float *out, int64_t B, int64_t H, int64_t D, int64_t M,
                           int dtype, void *stream);
+
+/*
+ * T consecutive recurrent steps of every head in one call (the state is read
+ * once and written once; page "Transformers are RNNs", Proposed method: the
+ * RNN update applied token after token).  Equivalent to T calls of
+ * la_decode_step with q, k, v, out of token t, up to rounding.
+ * q, k: [B][H][T][D]; v, out: [B][H][T][M]; S, z updated in place.
+ * T = 0 is a valid empty call.  Same element types, alignment and status
+ * codes as la_decode_step.
+ */
+LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, const void *v,
+                           float *out, int64_t B, int64_t H, int64_t T, int64_t D, int64_t M,
+                           int dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("la_forward_chunked", "la_decode_step", "la_forward_workspace_bytes", "la_forward_plan",
               "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version",
-              "la_forward_fused", "la_forward_onepass", "la_workspace_init"):
+              "la_forward_fused", "la_forward_onepass", "la_forward_continue", "la_workspace_init"):
         assert s in syms
 
 
@@ -146,14 +146,12 @@ def test_fused_entry_point_checks(L):
     f = L.lib().la_forward_fused
     need = L.fused_workspace_bytes(2, 2, 64, 64, 4)
     # 1000 positions in chunks of 64: 16 chunks; 4 segments of 4 chunks
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, FAKE, need - 4, None, None, None) == L.LA_ERR_WORKSPACE
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 5, FAKE, 1 << 30, None, None,
-             None) == L.LA_ERR_UNSUPPORTED  # a segment would own no chunk
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 48, 4, FAKE, need, None, None, None) == L.LA_ERR_UNSUPPORTED
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 0, FAKE, need, None, None, None) == L.LA_ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, FAKE + 4, need, None, None,
-             None) == L.LA_ERR_INVALID_ARG
-    assert f(None, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, FAKE, need, None, None, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, None, None, FAKE, need - 4, None, None, None) == L.LA_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 5, None, None, FAKE, 1 << 30, None, None, None) == L.LA_ERR_UNSUPPORTED  # a segment would own no chunk
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 48, 4, None, None, FAKE, need, None, None, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 0, None, None, FAKE, need, None, None, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, None, None, FAKE + 4, need, None, None, None) == L.LA_ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 4, None, None, FAKE, need, None, None, None) == L.LA_ERR_INVALID_ARG
     w = L.lib().la_workspace_init
     assert w(None, 0, None) == L.LA_OK
     assert w(None, 64, None) == L.LA_ERR_INVALID_ARG
@@ -165,22 +163,45 @@ def test_onepass_entry_point_checks(L):
     f = L.lib().la_forward_onepass
     need = L.fused_workspace_bytes(2, 2, 64, 64, 2)
     # 1000 positions in chunks of 64: 16 chunks; 2 segments would hold 8 chunks each (> 4)
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 2, FAKE, need, None, None, None) == L.LA_ERR_UNSUPPORTED
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 17, FAKE, 1 << 30, None, None,
-             None) == L.LA_ERR_UNSUPPORTED  # a segment would own no chunk
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 2, None, None, FAKE, need, None, None, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 64, 17, None, None, FAKE, 1 << 30, None, None, None) == L.LA_ERR_UNSUPPORTED  # a segment would own no chunk
     need4 = L.fused_workspace_bytes(2, 2, 64, 64, 4)
     bf16 = 1
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, bf16, 64, 4, FAKE, need4 - 4, None, None,
-             None) == L.LA_ERR_WORKSPACE
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, bf16, 64, 0, FAKE, need4, None, None,
-             None) == L.LA_ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, bf16, 64, 4, FAKE, need4, FAKE, None,
-             None) == L.LA_ERR_INVALID_ARG  # S_out without z_out
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, bf16, 64, 4, None, None, FAKE, need4 - 4, None, None, None) == L.LA_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, bf16, 64, 0, None, None, FAKE, need4, None, None, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, bf16, 64, 4, None, None, FAKE, need4, FAKE, None, None) == L.LA_ERR_INVALID_ARG  # S_out without z_out
     # fp32 operands with 64-position chunks: the segment's phi(Q) tiles do not fit in LDS
     # (two workgroups per CU for D = M = 64, one for D = M = 128)
     for d in (64, 128):
-        assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 256, d, d, 0, 64, 1, None, 0, None, None,
-                 None) == L.LA_ERR_UNSUPPORTED
+        assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 256, d, d, 0, 64, 1, None, None, None, 0, None, None, None) == L.LA_ERR_UNSUPPORTED
+
+
+def test_continue_entry_point_checks(L):
+    f = L.lib().la_forward_continue
+    need = L.lib().la_forward_workspace_bytes(2, 2, 1000, 64, 64, 1, 0, 0)
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 0, FAKE, None, FAKE, need, None, None,
+             None) == L.LA_ERR_INVALID_ARG  # S_in without z_in
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 0, FAKE + 4, FAKE, FAKE, need, None, None,
+             None) == L.LA_ERR_INVALID_ARG  # misaligned S_in
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 0, FAKE, FAKE, FAKE, need - 4, None, None,
+             None) == L.LA_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 48, 64, 0, 0, FAKE, FAKE, FAKE, need, None, None,
+             None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 2, 0, FAKE, FAKE, FAKE, need, None, None,
+             None) == L.LA_ERR_INVALID_ARG  # dtype
+    assert f(None, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 0, FAKE, FAKE, FAKE, need, None, None,
+             None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 2, 1000, 64, 64, 0, 0, FAKE, FAKE, None, 0, None, None, None) == L.LA_OK
+
+
+def test_decode_steps_checks(L):
+    f = L.lib().la_decode_steps
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, -1, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 48, 64, 0, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 3, None) == L.LA_ERR_INVALID_ARG
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
+    assert f(None, None, None, None, None, None, 2, 2, 0, 64, 64, 0, None) == L.LA_OK  # T = 0
 
 
 def test_product_path_never_imports_the_oracle():
