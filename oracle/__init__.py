@@ -59,6 +59,8 @@ class Oracle:
                                          ctypes.POINTER(_i64), _i64, _dp, ctypes.c_int]
         L.oracle_noncausal.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int]
         L.oracle_decode_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int]
+        L.oracle_causal_backward.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64,
+                                             ctypes.c_int]
         self.L = L
         self.path = path
 
@@ -142,6 +144,20 @@ class Oracle:
         return out
 
 
+    def causal_backward(self, Q, K, V, dO, threads: int = 0):
+        """Gradients (dQ, dK, dV) of causal attention for the output gradient dO [..., N, M]."""
+        Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+        *lead, N, D = Q.shape
+        M = V.shape[-1]
+        assert K.shape == Q.shape and V.shape == dO.shape and tuple(V.shape[:-1]) == tuple(Q.shape[:-1])
+        BH = int(np.prod(lead)) if lead else 1
+        dQ = np.empty(Q.shape)
+        dK = np.empty(K.shape)
+        dV = np.empty(V.shape)
+        self.L.oracle_causal_backward(_p(Q), _p(K), _p(V), _p(dO), _p(dQ), _p(dK), _p(dV), BH, N, D, M, threads)
+        return dQ, dK, dV
+
+
 def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
 
@@ -188,3 +204,7 @@ def noncausal(Q, K, V, threads: int = 0):
 
 def decode_step(S, z, q, k, v, threads: int = 0):
     return default().decode_step(S, z, q, k, v, threads)
+
+
+def causal_backward(Q, K, V, dO, threads: int = 0):
+    return default().causal_backward(Q, K, V, dO, threads)

@@ -231,3 +231,82 @@ void oracle_decode_step(double *S, double *z, const double *q, const double *k,
         }
     }
 }
+
+/* Derivative of phi: 1 for x > 0, exp(x) otherwise (continuous, 1 at 0). */
+static double oracle_dphi1(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+/* Gradients of causal attention (the training half of the parallel mode; page
+ * "Transformers are RNNs", Proposed method: gradients in linear time, so that
+ * training keeps constant memory like the forward running sums).
+ * The chain rule through out_i = num_i / den_i with num_i = phi(q_i)^T S_i and
+ * den_i = phi(q_i)^T z_i gives, with g_i = phi(q_i), f_j = phi(k_j),
+ *   r_i = dout_i / den_i  (M),  c_i = -(dout_i . out_i) / den_i,
+ *   dL/dg_i = S_i r_i + c_i z_i                          (sums over j <= i)
+ *   dL/df_j = R_j v_j + w_j,  dL/dv_j = R_j^T f_j        (sums over i >= j)
+ * where R_j = sum_{i>=j} g_i r_i^T (D x M) and w_j = sum_{i>=j} c_i g_i (D):
+ * a forward running sum for the query side and a reverse one for the key and
+ * value side.  Then dq = dL/dg * phi'(q), dk = dL/df * phi'(k).
+ * dO [BH][N][M] (the output gradient); dQ, dK [BH][N][D], dV [BH][N][M]. */
+void oracle_causal_backward(const double *Q, const double *K, const double *V, const double *dO,
+                            double *dQ, double *dK, double *dV,
+                            int64_t BH, int64_t N, int64_t D, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const double *Qh = Q + h * N * D, *Kh = K + h * N * D, *Vh = V + h * N * M, *dOh = dO + h * N * M;
+        double *dQh = dQ + h * N * D, *dKh = dK + h * N * D, *dVh = dV + h * N * M;
+        double *S = (double *)calloc((size_t)(D * M), sizeof(double));
+        double *z = (double *)calloc((size_t)D, sizeof(double));
+        double *r = (double *)malloc((size_t)(N * M) * sizeof(double));
+        double *c = (double *)malloc((size_t)N * sizeof(double));
+        double *o = (double *)malloc((size_t)M * sizeof(double));
+        /* forward running sums: outputs, r_i, c_i and the query-side gradient */
+        for (int64_t i = 0; i < N; ++i) {
+            const double *q = Qh + i * D, *k = Kh + i * D, *v = Vh + i * M, *dout = dOh + i * M;
+            for (int64_t d = 0; d < D; ++d) {
+                double f = oracle_phi1(k[d]);
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += f * v[m];
+                z[d] += f;
+            }
+            double den = 0.0;
+            for (int64_t d = 0; d < D; ++d) den += oracle_phi1(q[d]) * z[d];
+            double dot = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double num = 0.0;
+                for (int64_t d = 0; d < D; ++d) num += oracle_phi1(q[d]) * S[d * M + m];
+                o[m] = num / den;
+                dot += dout[m] * o[m];
+            }
+            for (int64_t m = 0; m < M; ++m) r[i * M + m] = dout[m] / den;
+            c[i] = -dot / den;
+            for (int64_t d = 0; d < D; ++d) {
+                double dg = c[i] * z[d];
+                for (int64_t m = 0; m < M; ++m) dg += S[d * M + m] * r[i * M + m];
+                dQh[i * D + d] = dg * oracle_dphi1(q[d]);
+            }
+        }
+        /* reverse running sums: key- and value-side gradients */
+        double *R = S, *w = z; /* reused, cleared */
+        memset(R, 0, (size_t)(D * M) * sizeof(double));
+        memset(w, 0, (size_t)D * sizeof(double));
+        for (int64_t j = N - 1; j >= 0; --j) {
+            const double *q = Qh + j * D, *k = Kh + j * D, *v = Vh + j * M;
+            for (int64_t d = 0; d < D; ++d) {
+                double g = oracle_phi1(q[d]);
+                for (int64_t m = 0; m < M; ++m) R[d * M + m] += g * r[j * M + m];
+                w[d] += c[j] * g;
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                double df = w[d];
+                for (int64_t m = 0; m < M; ++m) df += R[d * M + m] * v[m];
+                dKh[j * D + d] = df * oracle_dphi1(k[d]);
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                double dv = 0.0;
+                for (int64_t d = 0; d < D; ++d) dv += R[d * M + m] * oracle_phi1(k[d]);
+                dVh[j * M + m] = dv;
+            }
+        }
+        free(S); free(z); free(r); free(c); free(o);
+    }
+}

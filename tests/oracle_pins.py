@@ -288,7 +288,59 @@ def pin_continue(o, fails):
         _close(f"continue from zero N{N}", zo[0], want, 1e-11, fails)
 
 
-ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked, pin_continue]
+def pin_backward(o, fails):
+    """Gradients against (a) fp64 autograd through the quadratic masked form (torch CPU),
+    (b) central finite differences of the oracle's forward, (c) closed forms: the value
+    gradients sum to the output gradients (outputs are convex combinations of values),
+    and row 0 does not depend on q_0 (out_0 = v_0)."""
+    import torch
+    rng = np.random.default_rng(41)
+
+    def quad(Qt, Kt, Vt):
+        ph = lambda x: torch.where(x > 0, x + 1, torch.exp(x))
+        W = torch.tril(ph(Qt) @ ph(Kt).T)
+        return (W @ Vt) / W.sum(dim=1, keepdim=True)
+
+    for (N, D, M) in [(1, 2, 3), (5, 3, 2), (16, 4, 7), (33, 16, 16)]:
+        for scale in (0.5, 2.0):
+            Q, K, V = _rand(rng, N, D, M, scale)
+            dO = rng.normal(size=(N, M))
+            dQ, dK, dV = o.causal_backward(Q[None], K[None], V[None], dO[None])
+            Qt, Kt, Vt = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V)]
+            (quad(Qt, Kt, Vt) * torch.tensor(dO)).sum().backward()
+            for nm, got, want in (("dQ", dQ[0], Qt.grad.numpy()), ("dK", dK[0], Kt.grad.numpy()),
+                                  ("dV", dV[0], Vt.grad.numpy())):
+                err = np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-3)  # exact zeros at N = 1
+                if not err <= 1e-11:
+                    fails.append(f"backward autograd {nm} N{N} D{D} M{M} s{scale}: {err:.3e}")
+            _close(f"backward sum dV N{N}", dV[0].sum(axis=0), dO.sum(axis=0), 1e-11, fails)
+            if not np.max(np.abs(dQ[0, 0])) <= 1e-12:
+                fails.append(f"backward dq_0 != 0 N{N}")
+    # central differences of the forward on a tiny case
+    N, D, M = 6, 3, 4
+    Q, K, V = _rand(rng, N, D, M, 1.0)
+    dO = rng.normal(size=(N, M))
+    dQ, dK, dV = o.causal_backward(Q[None], K[None], V[None], dO[None])
+    loss = lambda Q_, K_, V_: float(np.sum(o.causal(Q_[None], K_[None], V_[None])[0][0] * dO))
+    h = 1e-6
+    for nm, X, G in (("Q", Q, dQ[0]), ("K", K, dK[0]), ("V", V, dV[0])):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += h
+            Xm[idx] -= h
+            args_p = [Q, K, V]
+            args_m = [Q, K, V]
+            pos = "QKV".index(nm)
+            args_p[pos], args_m[pos] = Xp, Xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.max(np.abs(num - G)) / max(np.max(np.abs(G)), 1e-300)
+        if not err <= 1e-6:
+            fails.append(f"backward finite differences d{nm}: {err:.3e}")
+
+
+ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked, pin_continue,
+            pin_backward]
 
 
 def run_all(o, pins=ALL_PINS):

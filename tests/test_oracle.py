@@ -34,6 +34,15 @@ MUTANTS = {
     "noncausal_wrong_z": ("for (int64_t d = 0; d < D; ++d) den += g[d] * z[d];\n            for (int64_t m = 0; m < M; ++m) {\n                double num = 0.0;\n                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];\n                Oh[i * M + m] = num / den;\n            }\n        }\n        free(S); free(z); free(g);",
                           "for (int64_t d = 0; d < D; ++d) den += g[d] * z[0];\n            for (int64_t m = 0; m < M; ++m) {\n                double num = 0.0;\n                for (int64_t d = 0; d < D; ++d) num += g[d] * S[d * M + m];\n                Oh[i * M + m] = num / den;\n            }\n        }\n        free(S); free(z); free(g);"),
     "decode_overwrites_z": ("zh[d] += f;", "zh[d] = f;"),
+    "backward_c_sign": ("c[i] = -dot / den;", "c[i] = dot / den;"),
+    "backward_dq_phi_not_derivative": ("dQh[i * D + d] = dg * oracle_dphi1(q[d]);",
+                                       "dQh[i * D + d] = dg * oracle_phi1(q[d]);"),
+    "backward_dv_uses_q": ("dv += R[d * M + m] * oracle_phi1(k[d]);", "dv += R[d * M + m] * oracle_phi1(q[d]);"),
+    "backward_missing_w": ("double df = w[d];", "double df = 0.0;"),
+    "backward_dk_no_chain_rule": ("dKh[j * D + d] = df * oracle_dphi1(k[d]);", "dKh[j * D + d] = df;"),
+    "backward_reverse_sum_exclusive": (
+        "                for (int64_t m = 0; m < M; ++m) R[d * M + m] += g * r[j * M + m];\n                w[d] += c[j] * g;\n            }\n            for (int64_t d = 0; d < D; ++d) {\n                double df = w[d];",
+        "                for (int64_t m = 0; m < M; ++m) R[d * M + m] += 0.0 * g * r[j * M + m];\n                w[d] += c[j] * g;\n            }\n            for (int64_t d = 0; d < D; ++d) {\n                double df = w[d];"),
     "continue_ignores_z0": ("memcpy(z, z0 + h * D, (size_t)D * sizeof(double));",
                             "memset(z, 0, (size_t)D * sizeof(double));"),
     "continue_ignores_S0": ("memcpy(S, S0 + h * D * M, (size_t)(D * M) * sizeof(double));",
