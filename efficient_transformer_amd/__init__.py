@@ -6,6 +6,7 @@ argument marshalling only; PyTorch supplies device memory and streams.
 """
 from .linattn import (  # noqa: F401
     LinAttnError,
+    backward,
     decode_step,
     decode_steps,
     forward_chunked,

@@ -385,6 +385,76 @@ LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, cons
     return hip_status(la::decode_step(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), as_stream(stream)));
 }
 
+namespace {
+// Backward plan: chunks of kBackwardChunk positions, segments sized like the
+// forward planner's (about 512 workgroups, or 256 for states above 64 x 64).
+struct BwdPlan {
+    int G = 0, cps = 0;
+    size_t states_bytes = 0, den_bytes = 0, ws_bytes = 0;
+};
+int bwd_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype, BwdPlan *p) {
+    int st = check_shape(B, H, N, D, M, dtype);
+    if (st != LA_OK) return st;
+    const int64_t BH = B * H;
+    if (BH == 0 || N == 0) return LA_OK;
+    const int C = la::kBackwardChunk;
+    if (!la::prefill_supported(dtype, (int)D, (int)M, C)) return LA_ERR_UNSUPPORTED;
+    const int64_t n_chunks = (N + C - 1) / C;
+    const int64_t target_wg = (D * M <= 4096) ? 512 : 256;
+    int64_t cps = (n_chunks * BH + target_wg - 1) / target_wg;
+    if (cps < 1) cps = 1;
+    int64_t G = (n_chunks + cps - 1) / cps;
+    cps = (n_chunks + G - 1) / G;
+    G = (n_chunks + cps - 1) / cps;
+    if (BH * G > INT_MAX / 256) return LA_ERR_UNSUPPORTED;
+    p->G = (int)G;
+    p->cps = (int)cps;
+    p->states_bytes = state_ws_bytes(BH, D, M, (int)G);
+    p->den_bytes = ((size_t)(BH * N) * sizeof(float) + 255) / 256 * 256;
+    p->ws_bytes = 2 * p->states_bytes + p->den_bytes;
+    return LA_OK;
+}
+}  // namespace
+
+LA_API size_t la_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype) {
+    BwdPlan p;
+    return bwd_plan(B, H, N, D, M, dtype, &p) == LA_OK ? p.ws_bytes : 0;
+}
+
+LA_API int la_backward_chunked(const void *Q, const void *K, const void *V, const float *out, const float *dout,
+                               float *dQ, float *dK, float *dV, int64_t B, int64_t H, int64_t N, int64_t D,
+                               int64_t M, int dtype, void *workspace, size_t workspace_bytes, void *stream) {
+    BwdPlan p;
+    int st = bwd_plan(B, H, N, D, M, dtype, &p);
+    if (st != LA_OK) return st;
+    const int64_t BH = B * H;
+    if (BH == 0 || N == 0) return LA_OK;
+    if (!Q || !K || !V || !out || !dout || !dQ || !dK || !dV) return LA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(dout) || !aligned16(dQ) ||
+        !aligned16(dK) || !aligned16(dV))
+        return LA_ERR_INVALID_ARG;
+    if (workspace == nullptr || workspace_bytes < p.ws_bytes) return LA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return LA_ERR_INVALID_ARG;
+    unsigned char *w = static_cast<unsigned char *>(workspace);
+    float *fwd_ws = reinterpret_cast<float *>(w);
+    float *rev_ws = reinterpret_cast<float *>(w + p.states_bytes);
+    float *den = reinterpret_cast<float *>(w + 2 * p.states_bytes);
+    const int C = la::kBackwardChunk, G = p.G, cps = p.cps, Di = (int)D, Mi = (int)M, E = (int)(D * M + D);
+    hipStream_t s = as_stream(stream);
+    (void)hipGetLastError();
+    hipError_t e = hipSuccess;
+    if (G > 1) {
+        e = la::prefill_states(dtype, Di, Mi, C, K, V, fwd_ws, (int)BH, (int)N, G, cps, G - 1, s);
+        if (e == hipSuccess) e = la::prefill_scan(fwd_ws, (int)BH, Di, Mi, G, G - 1, nullptr, nullptr, s);
+    }
+    if (e == hipSuccess)
+        e = la::backward_dq(dtype, Di, Mi, Q, K, V, out, dout, fwd_ws, rev_ws, den, dQ, (int)BH, (int)N, G, cps, s);
+    if (e == hipSuccess && G > 1) e = la::backward_rev_scan(rev_ws, (int)BH, E, G, s);
+    if (e == hipSuccess)
+        e = la::backward_dkv(dtype, Di, Mi, Q, K, V, out, dout, rev_ws, den, dK, dV, (int)BH, (int)N, G, cps, s);
+    return hip_status(e);
+}
+
 LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, const void *v, float *out, int64_t B,
                            int64_t H, int64_t T, int64_t D, int64_t M, int dtype, void *stream) {
     if (B < 0 || H < 0 || T < 0) return LA_ERR_INVALID_ARG;

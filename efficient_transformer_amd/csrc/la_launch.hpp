@@ -37,6 +37,16 @@ hipError_t prefill_scan(float *ws, int BH, int D, int M, int G, int nstates, flo
                         hipStream_t stream);
 hipError_t fill_zero(float *p, size_t n, hipStream_t stream);
 
+// Backward (la_backward.hip): chunk of 32 positions, stage workspaces as the forward's.
+constexpr int kBackwardChunk = 32;
+hipError_t backward_dq(int dtype, int D, int M, const void *Q, const void *K, const void *V, const float *O,
+                       const float *dO, const float *fwd_ws, float *rev_ws, float *den, float *dQ, int BH, int N,
+                       int G, int CPS, hipStream_t stream);
+hipError_t backward_dkv(int dtype, int D, int M, const void *Q, const void *K, const void *V, const float *O,
+                        const float *dO, const float *rev_ws, const float *den, float *dK, float *dV, int BH, int N,
+                        int G, int CPS, hipStream_t stream);
+hipError_t backward_rev_scan(float *ws, int BH, int E, int G, hipStream_t stream);
+
 hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
                        float *out, int BH, hipStream_t stream);
 hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,

@@ -40,6 +40,9 @@ SIGNATURES = {
     "la_segment_scan": (_int, [_vp, _sz, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "la_segment_outputs": (_int, [_vp, _vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _int, _vp, _vp, _vp]),
+    "la_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
+    "la_backward_chunked": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int,
+                                   _vp, _sz, _vp]),
     "la_decode_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_decode_steps": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
 }
@@ -323,3 +326,27 @@ def decode_steps(S, z, q, k, v, out=None, stream=None):
                                _dtype_code(q), _stream(stream, dev))
     _check(st, "la_decode_steps")
     return out
+
+
+def backward(Q, K, V, out, dout, workspace=None, stream=None):
+    """Gradients (dQ, dK, dV) of causal attention; out is the forward's output."""
+    import torch
+    B, H, N, D = Q.shape
+    M = V.shape[-1]
+    dev = Q.device
+    _require(K, "K", (B, H, N, D), Q.dtype, dev)
+    _require(V, "V", (B, H, N, M), Q.dtype, dev)
+    _require(out, "out", (B, H, N, M), torch.float32, dev)
+    _require(dout, "dout", (B, H, N, M), torch.float32, dev)
+    dt = _dtype_code(Q)
+    need = int(lib().la_backward_workspace_bytes(B, H, N, D, M, dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    dQ = torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dK = torch.empty((B, H, N, D), dtype=torch.float32, device=dev)
+    dV = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
+    st = lib().la_backward_chunked(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(dout), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                   B, H, N, D, M, dt, _ptr(workspace), wbytes, _stream(stream, dev))
+    _check(st, "la_backward_chunked")
+    return dQ, dK, dV

@@ -219,6 +219,31 @@ LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, cons
                           int dtype, void *stream);
 
 /*
+ * Gradients of causal attention (training backward of the parallel mode; page
+ * "Transformers are RNNs", Proposed method: gradients in linear time and
+ * constant memory, by running sums like the forward pass).  For a loss L with
+ * dout = dL/dout, with g = phi(q), f = phi(k), den_i = g_i . z_i:
+ *   r_i = dout_i / den_i,  c_i = -(dout_i . out_i) / den_i
+ *   dL/dq_i = (S_i r_i + c_i z_i) * phi'(q_i)            (sums over j <= i)
+ *   dL/dk_j = (R_j v_j + w_j) * phi'(k_j),  dL/dv_j = R_j^T phi(k_j)
+ * with R_j = sum_{i>=j} g_i r_i^T, w_j = sum_{i>=j} c_i g_i (sums over i >= j)
+ * and phi'(x) = 1 for x > 0, exp(x) otherwise.
+ * out: the forward's output [B][H][N][M] fp32 (from la_forward_chunked, causal);
+ * dout [B][H][N][M] fp32; dQ, dK [B][H][N][D] and dV [B][H][N][M] fp32, fully
+ * written.  Q, K, V as for the forward (fp32 or bf16); all arithmetic fp32.
+ * workspace: at least la_backward_workspace_bytes(...) bytes, no
+ * initialisation needed (every byte the call reads it writes first).
+ * Five kernels on `stream`: segment states, their scan, dQ (with the reverse
+ * segment states), the reverse scan, dK and dV.
+ */
+LA_API size_t la_backward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                          int dtype);
+LA_API int la_backward_chunked(const void *Q, const void *K, const void *V, const float *out,
+                               const float *dout, float *dQ, float *dK, float *dV,
+                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * T consecutive recurrent steps of every head in one call (the state is read
  * once and written once; page "Transformers are RNNs", Proposed method: the
  * RNN update applied token after token).  Equivalent to T calls of

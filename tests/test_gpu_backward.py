@@ -1,0 +1,104 @@
+"""Parity of the HIP backward (la_backward_chunked) with the fp64 oracle's
+gradients (page "Transformers are RNNs", Proposed method: linear-time gradients
+by running sums).  The GPU forward's output is fed to the GPU backward, as in
+training; the oracle recomputes everything in fp64."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_helpers import TOL, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SHAPES = [(16, 16), (32, 64), (64, 32), (64, 64), (128, 128), (16, 128), (128, 16)]
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import efficient_transformer_amd as ea
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return ea
+
+
+def pcfg(dtype, B, H, N, D, M):
+    return dict(kind="prefill", B=B, H=H, N=N, D=D, M=M, sigma=1.0, dtype=dtype, chunk=0)
+
+
+def run(ea, dtype, B, H, N, D, M, seed):
+    Q, K, V = synthetic.prefill_inputs(pcfg(dtype, B, H, N, D, M), seed)
+    dO = synthetic.draw(seed + 1000, 7, (B, H, N, M), 1.0, "f32")
+    Qd, Kd, Vd = to_dev(Q, dtype), to_dev(K, dtype), to_dev(V, dtype)
+    dOd = torch.from_numpy(np.ascontiguousarray(dO)).to(DEV)
+    out = ea.forward_chunked(Qd, Kd, Vd)
+    dQ, dK, dV = ea.backward(Qd, Kd, Vd, out, dOd)
+    torch.cuda.synchronize()
+    ref = oracle.causal_backward(synthetic.as_f64(Q, dtype), synthetic.as_f64(K, dtype),
+                                 synthetic.as_f64(V, dtype), dO.astype(np.float64))
+    return (dQ.cpu().numpy(), dK.cpu().numpy(), dV.cpu().numpy()), ref
+
+
+def check(got, ref, tol):
+    """max |x - y| over the tensor relative to max |y| (floored at 1e-2: with one
+    position the exact query and key gradients are zero)."""
+    for name, x, y in zip(("dQ", "dK", "dV"), got, ref):
+        assert np.all(np.isfinite(x)), name
+        err = float(np.abs(x - y).max() / max(np.abs(y).max(), 1e-2))
+        assert err <= tol, f"{name} whole-tensor relative error {err:.3e} > {tol}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D,M", SHAPES)
+@pytest.mark.parametrize("N", [1, 33, 300])
+def test_backward_parity(ea, dtype, D, M, N):
+    got, ref = run(ea, dtype, 1, 2, N, D, M, 40)
+    # fp32 arithmetic throughout; bf16 inputs carry the bf16 forward output's error into c_i
+    check(got, ref, 1e-4 if dtype == "f32" else TOL["bf16"])
+
+
+def test_backward_first_row_has_no_query_gradient(ea):
+    """out_0 = v_0 whatever q_0 and k_0 are."""
+    got, _ = run(ea, "f32", 1, 2, 50, 64, 64, 41)
+    assert np.all(got[0][:, :, 0] == 0.0)
+
+
+def test_backward_value_gradients_sum_to_output_gradients(ea):
+    B, H, N, D, M = 2, 2, 200, 32, 64
+    Q, K, V = synthetic.prefill_inputs(pcfg("f32", B, H, N, D, M), 42)
+    dO = synthetic.draw(42, 7, (B, H, N, M), 1.0, "f32")
+    Qd, Kd, Vd = to_dev(Q, "f32"), to_dev(K, "f32"), to_dev(V, "f32")
+    dOd = torch.from_numpy(np.ascontiguousarray(dO)).to(DEV)
+    out = ea.forward_chunked(Qd, Kd, Vd)
+    _, _, dV = ea.backward(Qd, Kd, Vd, out, dOd)
+    torch.cuda.synchronize()
+    s = dV.double().sum(dim=2).cpu().numpy()
+    assert np.max(np.abs(s - dO.astype(np.float64).sum(axis=2))) <= 1e-3 * np.max(np.abs(s))
+
+
+def test_backward_headline_shape(ea):
+    """B=8 H=8 N=1024 D=M=64 fp32 (many segments per head)."""
+    got, ref = run(ea, "f32", 8, 8, 1024, 64, 64, 43)
+    check(got, ref, 1e-4)
+
+
+def test_backward_long_sequence(ea):
+    """N=8192 with D=M=128 bf16: long reverse and forward segment scans."""
+    got, ref = run(ea, "bf16", 1, 2, 8192, 128, 128, 44)
+    check(got, ref, TOL["bf16"])
+
+
+def test_backward_repeatable(ea):
+    """The backward uses no atomics or look-back: bitwise repeatable."""
+    B, H, N, D, M = 2, 3, 700, 64, 64
+    Q, K, V = synthetic.prefill_inputs(pcfg("f32", B, H, N, D, M), 45)
+    dO = synthetic.draw(45, 7, (B, H, N, M), 1.0, "f32")
+    Qd, Kd, Vd = to_dev(Q, "f32"), to_dev(K, "f32"), to_dev(V, "f32")
+    dOd = torch.from_numpy(np.ascontiguousarray(dO)).to(DEV)
+    out = ea.forward_chunked(Qd, Kd, Vd)
+    a = ea.backward(Qd, Kd, Vd, out, dOd)
+    b = ea.backward(Qd, Kd, Vd, out, dOd)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
