@@ -13,8 +13,9 @@ A step is one la_forward_chunked call over one batch.
 Also reported in the same JSON line: the dominant kernel's roofline (HIP
 events around each launch of it), the fp64 CPU oracle timed on a bounded
 sample of the same workload, the recurrent decode workload (256 streams x 8
-heads, D=M=64, 4096 steps from a zero state) and the two bf16 prefill
-workloads.  Prints exactly one JSON line on stdout; progress goes to stderr.
+heads, D=M=64, 4096 steps from a zero state), the two bf16 prefill
+workloads, the backward pass on the headline shape and the multi-token
+decode (16 tokens per call).  Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -192,6 +193,86 @@ def bench_decode(cfg, reps, dev, warm_steps=64):
                 kernel_GBs=per_step_bytes / (us_kernel * 1e-6) / 1e9)
 
 
+def backward_bytes(cfg) -> int:
+    """Algorithmic bytes of one backward call: read q, k, v, out, dout; write dq, dk, dv."""
+    s_in = 4 if cfg["dtype"] == "f32" else 2
+    D, M = cfg["D"], cfg["M"]
+    return cfg["B"] * cfg["H"] * cfg["N"] * ((2 * D + M) * s_in + 8 * M + 8 * D + 4 * M)
+
+
+def bench_backward(cfg, steps, dev):
+    """la_backward_chunked on a prefill workload (five kernels per call), inputs rotated over
+    enough buffer sets to exceed the last-level cache."""
+    import torch
+    import efficient_transformer_amd as ea
+    import synthetic
+
+    B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    nbytes = backward_bytes(cfg)
+    nsets = max(1, math.ceil(1.25 * LLC_BYTES / nbytes))
+    sets = []
+    for i in range(nsets):
+        Q, K, V = [synthetic.draw_torch(10 + i, t, (B, H, N, W), cfg["sigma"], cfg["dtype"], dev)
+                   for t, W in ((0, D), (1, D), (2, M))]
+        dO = synthetic.draw_torch(10 + i, 7, (B, H, N, M), 1.0, "f32", dev)
+        out = ea.forward_chunked(Q, K, V)
+        sets.append((Q, K, V, out, dO))
+    ws = torch.empty(max(16, int(ea.linattn.lib().la_backward_workspace_bytes(B, H, N, D, M, 0 if cfg["dtype"] == "f32" else 1))),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(3):
+        ea.backward(*sets[i % nsets], workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        ea.backward(*sets[i % nsets], workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del sets
+    torch.cuda.empty_cache()
+    return dict(ms_per_step=ms, tokens_per_s=B * N / (ms * 1e-3), bytes=nbytes, nsets=nsets,
+                GBs=nbytes / (ms * 1e-3) / 1e9)
+
+
+def bench_decode_steps(cfg, T, calls, dev):
+    """la_decode_steps: T tokens of every head per call, the state held in registers."""
+    import torch
+    import efficient_transformer_amd as ea
+    import synthetic
+
+    B, H, D, M = cfg["B"], cfg["H"], cfg["D"], cfg["M"]
+    q = synthetic.draw_torch(1, synthetic.TID_DQ, (B, H, T, D), cfg["sigma"], cfg["dtype"], dev)
+    k = synthetic.draw_torch(1, synthetic.TID_DK, (B, H, T, D), cfg["sigma"], cfg["dtype"], dev)
+    v = synthetic.draw_torch(1, synthetic.TID_DV, (B, H, T, M), cfg["sigma"], cfg["dtype"], dev)
+    S = torch.zeros((B, H, D, M), device=dev)
+    z = torch.zeros((B, H, D), device=dev)
+    out = torch.empty((B, H, T, M), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(5):
+        ea.decode_steps(S, z, q, k, v, out=out, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        ea.decode_steps(S, z, q, k, v, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    per_call = B * H * ((8 * D * M + 8 * D) + T * (4 * (2 * D + M) + 4 * M))
+    return dict(T=T, us_per_call=ms * 1e3, tokens_per_s=B * T / (ms * 1e-3), bytes_per_call=per_call,
+                GBs=per_call / (ms * 1e-3) / 1e9)
+
+
+def causal_kernel_name(cfg, chunk, segments) -> str:
+    n_chunks = -(-cfg["N"] // chunk)
+    cps = -(-n_chunks // segments)
+    kind = "onepass_causal_kernel" if cps <= 4 else "fused_causal_kernel"
+    t = "float" if cfg["dtype"] == "f32" else "bf16"
+    return f"{kind}<{t},{cfg['D']},{cfg['M']},{chunk}>"
+
+
 def cpu_baseline(cfg, target_s=12.0):
     """fp64 oracle (C, OpenMP over heads) on a bounded sample of the prefill workload."""
     import numpy as np
@@ -217,7 +298,8 @@ def cpu_baseline(cfg, target_s=12.0):
 
 
 def profile_run(dev):
-    """Untimed launches for counter collection: 4 headline prefill calls, 4 decode steps and
+    """Untimed launches for counter collection: 4 headline prefill calls, 4 decode steps,
+    2 backward calls, 2 multi-token decode calls, 2 calls of each bf16 prefill workload and
     4 copies of a 512 MiB fp32 buffer (known traffic: 512 MiB read + 512 MiB written each)."""
     import torch
     import efficient_transformer_amd as ea
@@ -236,6 +318,21 @@ def profile_run(dev):
     v = synthetic.draw_torch(0, synthetic.TID_DV, (B, H, M), 1.0, "f32", dev)
     for _ in range(4):
         ea.decode_step(S, z, q, k, v)
+    # the other kernels, once each
+    dO = synthetic.draw_torch(0, 7, tuple(out.shape), 1.0, "f32", dev)
+    for _ in range(2):
+        ea.backward(Q, K, V, out, dO)
+    qs = synthetic.draw_torch(1, synthetic.TID_DQ, (B, H, 16, D), 1.0, "f32", dev)
+    ks = synthetic.draw_torch(1, synthetic.TID_DK, (B, H, 16, D), 1.0, "f32", dev)
+    vs = synthetic.draw_torch(1, synthetic.TID_DV, (B, H, 16, M), 1.0, "f32", dev)
+    for _ in range(2):
+        ea.decode_steps(S, z, qs, ks, vs)
+    for name in ("prefill_bf16_b4h8_n3072_d64", "prefill_bf16_b1h16_n65536_d128"):
+        c = dict(synthetic.WORKLOADS[name])
+        Qb, Kb, Vb, ob = make_prefill_sets(c, 1, dev)[0]
+        for _ in range(2):
+            ea.forward_chunked(Qb, Kb, Vb, causal=True, out=ob)
+        del Qb, Kb, Vb, ob
     src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(4):
@@ -282,8 +379,8 @@ def main():
     achieved = pre["bytes"] / (kernel_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4),
-                    traffic=measured_traffic("prefill_fused_f32_B8H8N1024_D64M64.md"),
-                    kernel=f"fused_causal_kernel<float,{cfg['D']},{cfg['M']},{pre['chunk']}>",
+                    traffic=measured_traffic("prefill_f32_B8H8N1024_D64M64.md"),
+                    kernel=causal_kernel_name(cfg, pre["chunk"], pre["segments"]),
                     kernel_us=round(kernel_us, 2), algorithmic_bytes=pre["bytes"],
                     mfma_fp32_frac_at_min_flops=round(pre["flops_min"] / (kernel_us * 1e-6) / 1e12
                                                       / FP32_MFMA_PEAK_TFS, 4))
@@ -335,6 +432,23 @@ def main():
                 "kernel_GBs": round(r["bytes"] / (r["us_kernel"] * 1e-6) / 1e9, 1),
                 "frac_hbm_peak_kernel": round(r["bytes"] / (r["us_kernel"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         line["other_workloads"] = others
+        log("backward ...")
+        bw = bench_backward(cfg, max(10, args.steps // 4), dev)
+        log(f"backward: {bw}")
+        line["backward"] = {
+            "workload": "gradients dQ, dK, dV of causal attention, fp32, B=8 H=8 N=1024 D=M=64",
+            "tokens_per_s": round(bw["tokens_per_s"], 1), "ms_per_step": round(bw["ms_per_step"], 5),
+            "algorithmic_bytes": bw["bytes"], "GBs": round(bw["GBs"], 1),
+            "frac_hbm_peak": round(bw["GBs"] / HBM_PEAK_GBS, 4), "buffer_sets": bw["nsets"],
+            "note": "one la_backward_chunked call = five kernels; time between events around the calls"}
+        log("decode steps ...")
+        ds = bench_decode_steps(dcfg, 16, 200, dev)
+        log(f"decode steps: {ds}")
+        line["decode_steps"] = {
+            "workload": "recurrent decode, 16 tokens per call, fp32, 256 streams x H=8, D=M=64",
+            "tokens_per_s": round(ds["tokens_per_s"], 1), "us_per_call": round(ds["us_per_call"], 2),
+            "bytes_per_call": ds["bytes_per_call"], "GBs": round(ds["GBs"], 1),
+            "frac_hbm_peak": round(ds["GBs"] / HBM_PEAK_GBS, 4)}
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
