@@ -12,9 +12,11 @@ namespace la {
 // aggregate and the inclusive state of every segment (E floats each).
 constexpr int kWsHeaderWords = 64;
 __host__ __device__ inline size_t fused_flag_words(long BHG) { return ((size_t)BHG + 63) / 64 * 64; }
+// floats of one exchanged state slot: E = D*M + D padded to whole 256-byte blocks
+__host__ __device__ inline int fused_slot_floats(int E) { return (E + 63) / 64 * 64; }
 __host__ __device__ inline size_t fused_ws_bytes(long BH, int G, int E) {
     const size_t BHG = (size_t)BH * (size_t)G;
-    return (kWsHeaderWords + fused_flag_words((long)BHG)) * 4 + 2 * BHG * (size_t)E * 4;
+    return (kWsHeaderWords + fused_flag_words((long)BHG)) * 4 + 2 * BHG * (size_t)fused_slot_floats(E) * 4;
 }
 
 // Prefill stage launchers for one element type (0 = fp32, 1 = bf16).

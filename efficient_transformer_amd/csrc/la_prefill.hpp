@@ -60,6 +60,7 @@ struct Cfg {
     static constexpr int LV = M + PAD;  // fp32: rows of V
     static constexpr int LT = C;        // bf16: rows of V^T and phi(K)^T (swizzled, see tsw)
     static constexpr int E = D * M + D; // floats of one state (S then z)
+    static constexpr int EP = (E + 63) / 64 * 64;  // exchanged-state slot: whole 256-byte blocks
     static constexpr int NZP = THREADS / D < C ? THREADS / D : C;  // column-sum partial groups
     static constexpr int ZROWS = C / NZP;                            // rows per partial
     static_assert(ZROWS * NZP == C && NZP * D <= THREADS, "column-sum split");
@@ -226,7 +227,9 @@ struct Stage {
 //                      [3] error flag (look-back gave up)
 //   flags  [BH][G] (uint32, padded to 64 words): epoch << 2 | 1 aggregate ready,
 //                                                epoch << 2 | 2 inclusive ready
-//   aggregate states [BH][G][E], inclusive states [BH][G][E]
+//   aggregate states [BH][G][EP], inclusive states [BH][G][EP] (EP: E padded to
+//   whole 256-byte blocks; the slot layout is the lane order of the register
+//   tiles, see Engine::slot_store)
 // The header and flags must be zero before the first call with a given plan;
 // the last workgroup of every call resets the counters and advances the
 // epoch, which makes all flags of the call stale.
@@ -240,7 +243,7 @@ struct FusedWs {
         hdr = static_cast<unsigned *>(ws);
         flags = hdr + kWsHeaderWords;
         agg = reinterpret_cast<float *>(flags + fused_flag_words((long)BH * G));
-        incl = agg + (size_t)BH * G * E;
+        incl = agg + (size_t)BH * G * fused_slot_floats(E);
     }
 };
 
@@ -269,7 +272,7 @@ struct Engine {
         sqz = f + G::fqz;
         tid = threadIdx.x;
         lane = tid & 63;
-        w = tid >> 6;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile choices become scalar branches
         g = lane >> 4;
         l16 = lane & 15;
     }
@@ -296,20 +299,42 @@ struct Engine {
         }
     }
 
-    // Column sums of phi(K_c): partial sums over ZROWS rows into szp[q][d].
+    // Column sums of phi(K_c).  fp32: partial sums over ZROWS rows into szp[q][d].
+    // bf16: row sums of the transposed tile phi(K)^T (a row holds all C keys of one
+    // column d, in permuted octets), 16-byte reads, into szp[d].
+    static constexpr int ZP = G::F32 ? G::NZP : 1;  // partials per column
     __device__ __forceinline__ void z_partials() const {
-        const int q = tid / D, d = tid % D;
-        if (G::NZP * D == G::THREADS || q < G::NZP) {
-            float s = 0.0f;
+        if constexpr (G::F32) {
+            const int q = tid / D, d = tid % D;
+            if (G::NZP * D == G::THREADS || q < G::NZP) {
+                float s = 0.0f;
 #pragma unroll
-            for (int r = 0; r < G::ZROWS; ++r) s += to_f32(sK[(q * G::ZROWS + r) * G::LQ + d]);
-            szp[q * D + d] = s;
+                for (int r = 0; r < G::ZROWS; ++r) s += to_f32(sK[(q * G::ZROWS + r) * G::LQ + d]);
+                szp[q * D + d] = s;
+            }
+        } else {
+            constexpr int TPD = G::THREADS / D < C / 8 ? G::THREADS / D : C / 8;  // threads per column
+            constexpr int OCT = C / 8 / TPD;                                       // octets per thread
+            const int d = tid / TPD, p = tid % TPD;
+            if (TPD * D == G::THREADS || d < D) {
+                const T *row = sKt + d * G::LT + p * OCT * 8;
+                float s = 0.0f;
+#pragma unroll
+                for (int o = 0; o < OCT; ++o) {
+                    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(row + 8 * o);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) s += (float)v[j];
+                }
+#pragma unroll
+                for (int sh = TPD / 2; sh > 0; sh >>= 1) s += __shfl_xor(s, sh, 64);
+                if (p == 0) szp[d] = s;
+            }
         }
     }
     __device__ __forceinline__ float z_delta() const {  // thread tid < D, after a barrier
         float s = 0.0f;
 #pragma unroll
-        for (int q = 0; q < G::NZP; ++q) s += szp[q * D + tid];
+        for (int q = 0; q < ZP; ++q) s += szp[q * D + tid];
         return s;
     }
 
@@ -363,46 +388,64 @@ struct Engine {
         return acc;
     }
 
-    // Lower-triangle tiles of A (tile t = w, w+4, ... in row-major order of (rt, kt<=rt)),
-    // rounded to T, into sA[query][key]; their row sums into sdenp[kt][query].
+    // Lower-triangle tiles of A (tile t = w, w+NW, ... in row-major order of (rt, kt<=rt)),
+    // rounded to T, into sA[query][key]; their row sums into sdenp[kt][query].  All of
+    // a wavefront's tile products are issued before any epilogue, so their latencies
+    // overlap.
+    static __device__ __forceinline__ int tile_row(int t) {
+        int rt = 0;
+        while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
+        return rt;
+    }
     __device__ __forceinline__ void a_tiles() const {
+        constexpr int NTW = (G::NA + G::NW - 1) / G::NW;  // tiles per wavefront (at most)
+        f32x4 acc[NTW];
 #pragma unroll
-        for (int t = w; t < G::NA; t += G::NW) {
-            int rt = 0;
-            while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
-            const int kt = t - rt * (rt + 1) / 2;
-            f32x4 a = zero4();
-            const T *krow = sK + (kt * 16 + l16) * G::LQ;
-            const T *qrow = sQ + (rt * 16 + l16) * G::LQ;
-            if constexpr (G::F32) {
-                // contraction index d = g*(D/4) + j: each lane reads a contiguous quarter of the row
+        for (int k = 0; k < NTW; ++k) {
+            const int t = w + G::NW * k;
+            acc[k] = zero4();
+            if (G::NA % G::NW == 0 || t < G::NA) {
+                const int rt = tile_row(t), kt = t - rt * (rt + 1) / 2;
+                const T *krow = sK + (kt * 16 + l16) * G::LQ;
+                const T *qrow = sQ + (rt * 16 + l16) * G::LQ;
+                if constexpr (G::F32) {
+                    // contraction index d = g*(D/4) + j: each lane reads a contiguous quarter of the row
 #pragma unroll
-                for (int j4 = 0; j4 < D / 16; ++j4) {
-                    const f32x4 av = *reinterpret_cast<const f32x4 *>(krow + g * (D / 4) + 4 * j4);
-                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(qrow + g * (D / 4) + 4 * j4);
+                    for (int j4 = 0; j4 < D / 16; ++j4) {
+                        const f32x4 av = *reinterpret_cast<const f32x4 *>(krow + g * (D / 4) + 4 * j4);
+                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(qrow + g * (D / 4) + 4 * j4);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) a = mma_f32(av[j], bv[j], a);
+                        for (int j = 0; j < 4; ++j) acc[k] = mma_f32(av[j], bv[j], acc[k]);
+                    }
+                } else {
+                    acc[k] = tile_dot_bf16<D>(krow, qrow, g, acc[k]);
                 }
-            } else {
-                a = tile_dot_bf16<D>(krow, qrow, g, a);
             }
-            // a[r] = A[query = rt*16 + l16][key = kt*16 + 4g + r]
-            float rs = 0.0f;
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (kt == rt && 4 * g + r > l16) a[r] = 0.0f;
-                a[r] = round_as<T>(a[r]);
-                rs += a[r];
+        for (int k = 0; k < NTW; ++k) {
+            const int t = w + G::NW * k;
+            if (G::NA % G::NW == 0 || t < G::NA) {
+                const int rt = tile_row(t), kt = t - rt * (rt + 1) / 2;
+                f32x4 a = acc[k];
+                // a[r] = A[query = rt*16 + l16][key = kt*16 + 4g + r]
+                float rs = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (kt == rt && 4 * g + r > l16) a[r] = 0.0f;
+                    a[r] = round_as<T>(a[r]);
+                    rs += a[r];
+                }
+                T *arow = sA + (rt * 16 + l16) * G::LA + kt * 16 + 4 * g;
+                if constexpr (G::F32) {
+                    *reinterpret_cast<f32x4 *>(arow) = a;
+                } else {
+                    bf16x4 v = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+                    *reinterpret_cast<bf16x4 *>(arow) = v;
+                }
+                rs = sum_over_groups(rs);
+                if (g == 0) sdenp[kt * C + rt * 16 + l16] = rs;
             }
-            T *arow = sA + (rt * 16 + l16) * G::LA + kt * 16 + 4 * g;
-            if constexpr (G::F32) {
-                *reinterpret_cast<f32x4 *>(arow) = a;
-            } else {
-                bf16x4 v = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-                *reinterpret_cast<bf16x4 *>(arow) = v;
-            }
-            rs = sum_over_groups(rs);
-            if (g == 0) sdenp[kt * C + rt * 16 + l16] = rs;
         }
     }
 
@@ -410,12 +453,34 @@ struct Engine {
     __device__ __forceinline__ void qz_rows() const { qz_rows_to(sqz); }
     __device__ __forceinline__ void qz_rows_to(float *dst) const {
         constexpr int TPR = G::TPR;  // threads per row, consecutive lanes
+        constexpr int EPT = D / TPR;  // elements per thread, contiguous
+        constexpr int VW = 16 / (int)sizeof(T);
         const int i = tid / TPR, p = tid % TPR;
         if (G::TPR * C < G::THREADS && i >= C) return;  // whole wavefronts beyond the rows
-        const T *qr = sQ + i * G::LQ;
+        const T *qr = sQ + i * G::LQ + p * EPT;
+        const float *zr = sz + p * EPT;
         float s = 0.0f;
+        if constexpr (EPT % VW == 0) {
+            // 16-byte reads of the phi(q) row and of z
 #pragma unroll
-        for (int j = 0; j < D / TPR; ++j) s += to_f32(qr[p * (D / TPR) + j]) * sz[p * (D / TPR) + j];
+            for (int v = 0; v < EPT / VW; ++v) {
+                if constexpr (G::F32) {
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(qr + 4 * v);
+                    const f32x4 b = *reinterpret_cast<const f32x4 *>(zr + 4 * v);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) s += a[j] * b[j];
+                } else {
+                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(qr + 8 * v);
+                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(zr + 8 * v);
+                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(zr + 8 * v + 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) s += (float)a[j] * b0[j] + (float)a[4 + j] * b1[j];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) s += to_f32(qr[j]) * zr[j];
+        }
 #pragma unroll
         for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
         if (p == 0) dst[i] = s;
@@ -611,71 +676,60 @@ struct Engine {
     __device__ __forceinline__ void state_add(f32x4 (&acc)[DT][MTW], float &z, const float *slot) const {
         state_add(acc, z, slot, slot + D * M);
     }
-    // Agent-coherent variants for the states exchanged between workgroups: every
-    // access carries the agent scope (write-through stores, loads that miss
-    // stale cache lines), so no cache-wide write-back or invalidate is needed.
-    __device__ __forceinline__ void state_store_coherent(const f32x4 (&acc)[DT][MTW], float z, float *slot) const {
+    // ---- states exchanged between workgroups (fused and one-pass kernels) ----
+    // Slot layout (private to these kernels): the register tiles in lane order,
+    // tile (dt, mt) at floats ((dt*MT + mt)*64 + lane)*4 .. +3, then z[D] at D*M;
+    // slots are padded to whole 256-byte blocks so that no cache line is shared
+    // between slots.  Writers store write-through at agent scope (buffer stores
+    // with sc1); a flag is raised only after the stores complete.  Readers load
+    // a slot only after its flag, with plain cacheable loads: each slot is
+    // written once per call and never read before its flag, so no stale copy of
+    // it can be cached (caches are invalidated at kernel start).
+    __device__ __forceinline__ int xoff(int dt, int i) const { return ((dt * G::MT + mtile(i)) * 64 + lane) * 4; }
+    __device__ __forceinline__ void slot_store(const f32x4 (&acc)[DT][MTW], float z, float *slot) const {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(slot, (short)0, G::EP * 4, 0x00020000);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int i = 0; i < MTW; ++i) {
                 if (!owns(i)) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    __hip_atomic_store(slot + (dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16, acc[dt][i][r],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[dt][i]), rs, xoff(dt, i) * 4, 0,
+                                                       kCachePolicyAgent);
             }
         if (tid < D) __hip_atomic_store(slot + D * M + tid, z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __device__ __forceinline__ void state_add_coherent(f32x4 (&acc)[DT][MTW], float &z, const float *slot) const {
+    // pre += *first + agg[j0] + ... + agg[j1-1] (slots of EP floats), loads issued NB
+    // slots at a time so that their latencies overlap; fixed summation order.
+    __device__ __forceinline__ void state_add_slots(f32x4 (&acc)[DT][MTW], float &z, const float *first,
+                                                    const float *agg, int j0, int j1) const {
+        constexpr int PER = DT * MTW;  // 16-byte loads per slot and lane
+        constexpr int NB = PER <= 4 ? 4 : (PER <= 8 ? 2 : 1);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < MTW; ++i) {
-                if (!owns(i)) continue;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[dt][i][r] += __hip_atomic_load(slot + (dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        if (tid < D) z += __hip_atomic_load(slot + D * M + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // pre += *first + agg[j0] + ... + agg[j1-1] (slots of E floats), coherent loads
-    // issued NB slots at a time so that their latencies overlap; fixed order.
-    __device__ __forceinline__ void state_add_slots(f32x4 (&acc)[DT][MTW], float &z, const float *first,
-                                                    const float *agg, int j0, int j1) const {
-        constexpr int PER = DT * MTW * 4;
-        constexpr int NB = PER <= 16 ? 4 : (PER <= 32 ? 2 : 1);
-        state_add_coherent(acc, z, first);
+            for (int i = 0; i < MTW; ++i)
+                if (owns(i)) acc[dt][i] += *reinterpret_cast<const f32x4 *>(first + xoff(dt, i));
+        if (tid < D) z += first[D * M + tid];
         for (int jb = j0; jb < j1; jb += NB) {
-            float t[NB][PER];
+            f32x4 t[NB][DT][MTW];
             float tz[NB];
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
-                const float *slot = agg + (size_t)(jb + k < j1 ? jb + k : jb) * G::E;
-                int n = 0;
+                const float *slot = agg + (size_t)(jb + k < j1 ? jb + k : jb) * G::EP;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                     for (int i = 0; i < MTW; ++i)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r, ++n)
-                            t[k][n] = owns(i) ? __hip_atomic_load(slot + (dt * 16 + 4 * g + r) * M + mtile(i) * 16 + l16,
-                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                              : 0.0f;
-                tz[k] = tid < D ? __hip_atomic_load(slot + D * M + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : 0.0f;
+                        t[k][dt][i] = owns(i) ? *reinterpret_cast<const f32x4 *>(slot + xoff(dt, i)) : zero4();
+                tz[k] = tid < D ? slot[D * M + tid] : 0.0f;
             }
 #pragma unroll
             for (int k = 0; k < NB; ++k) {
                 if (jb + k >= j1) break;
-                int n = 0;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                    for (int i = 0; i < MTW; ++i)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r, ++n) acc[dt][i][r] += t[k][n];
+                    for (int i = 0; i < MTW; ++i) acc[dt][i] += t[k][dt][i];
                 z += tz[k];
             }
         }
@@ -701,8 +755,7 @@ struct Engine {
 
 // ---------------------------------------------------------------------------
 // Phase A: sum the state over chunks [c0, c1) into acc / z (thread tid < D owns z[tid]).
-// Leaves the last chunk's phi(K), V in LDS.  Global loads run two chunks ahead
-// (two register buffers, used alternately).
+// Leaves the last chunk's phi(K), V in LDS.  Global loads run one chunk ahead.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C>
 struct KVBuf {
@@ -718,22 +771,21 @@ template <typename T, int D, int M, int C>
 __device__ __forceinline__ void phase_a(const Engine<T, D, M, C> &e, const T *__restrict__ Kh,
                                         const T *__restrict__ Vh, int N, int c0, int c1,
                                         f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z) {
-    KVBuf<T, D, M, C> b0, b1;
-    b0.load(Kh, Vh, c0, N, e.tid);
-    if (c0 + 1 < c1) b1.load(Kh, Vh, c0 + 1, N, e.tid);
-    auto step = [&](KVBuf<T, D, M, C> &b, int c) {
+    // One chunk of loads in flight: chunk c+1 is requested right after chunk c is
+    // staged, so a whole chunk of work covers its latency.  The load is issued
+    // unconditionally (index clamped to the last chunk; a clamped reload is an L2
+    // hit) so that the compiler's wait counts stay exact.
+    KVBuf<T, D, M, C> b;
+    b.load(Kh, Vh, c0, N, e.tid);
+    for (int c = c0; c < c1; ++c) {
         __syncthreads();  // LDS free (previous chunk's readers are done)
         e.store_kv(b.k, b.v, c * C, N);
         __syncthreads();
-        if (c + 2 < c1) b.load(Kh, Vh, c + 2, N, e.tid);
+        b.load(Kh, Vh, min(c + 1, c1 - 1), N, e.tid);
         e.z_partials();
         e.state_update(acc);
         __syncthreads();
         if (e.tid < D) z += e.z_delta();
-    };
-    for (int c = c0; c < c1; c += 2) {
-        step(b0, c);
-        if (c + 1 < c1) step(b1, c + 1);
     }
 }
 
@@ -741,8 +793,8 @@ __device__ __forceinline__ void phase_a(const Engine<T, D, M, C> &e, const T *__
 // Phase B: outputs of chunks [c0, c1) starting from the state (S, z) of all
 // earlier positions.  q0 already holds (or is loading) chunk c0's Q.
 // kv_staged: chunk c0's phi(K), V are already in LDS.  advance_last: also
-// advance the state over the last chunk (for the final state).  Loads run two
-// chunks ahead.
+// advance the state over the last chunk (for the final state).  Loads run one
+// chunk ahead.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C, bool CAUSAL>
 __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__restrict__ Qh,
@@ -751,14 +803,11 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__
                                         bool advance_last, Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q0,
                                         f32x4 (&S)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z,
                                         bool poison) {
-    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> q1;
-    KVBuf<T, D, M, C> b0, b1;
-    if (CAUSAL && !kv_staged) b0.load(Kh, Vh, c0, N, e.tid);
-    if (c0 + 1 < c1) {
-        q1.load(Qh, (c0 + 1) * C, N, e.tid);
-        if (CAUSAL) b1.load(Kh, Vh, c0 + 1, N, e.tid);
-    }
-    auto step = [&](Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q, KVBuf<T, D, M, C> &b, int c) {
+    // loads as in phase_a: one chunk ahead, unconditional (clamped)
+    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q = q0;
+    KVBuf<T, D, M, C> b;
+    if (CAUSAL && !kv_staged) b.load(Kh, Vh, c0, N, e.tid);
+    for (int c = c0; c < c1; ++c) {
         const int row0 = c * C;
         const bool stage_kv = CAUSAL && !(kv_staged && c == c0);
         __syncthreads();  // LDS free
@@ -766,10 +815,9 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__
         if (stage_kv) e.store_kv(b.k, b.v, row0, N);
         if (e.tid < D) e.sz[e.tid] = round_as<T>(z);
         __syncthreads();
-        if (c + 2 < c1) {
-            q.load(Qh, (c + 2) * C, N, e.tid);
-            if (CAUSAL) b.load(Kh, Vh, c + 2, N, e.tid);
-        }
+        const int cn = min(c + 1, c1 - 1);
+        q.load(Qh, cn * C, N, e.tid);
+        if (CAUSAL) b.load(Kh, Vh, cn, N, e.tid);
         if (CAUSAL) e.a_tiles();
         e.qz_rows();
         const bool adv = CAUSAL && (c + 1 < c1 || advance_last);
@@ -784,10 +832,6 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__
             e.state_update(S);
             if (e.tid < D) z += e.z_delta();
         }
-    };
-    for (int c = c0; c < c1; c += 2) {
-        step(q0, b0, c);
-        if (c + 1 < c1) step(q1, b1, c + 1);
     }
 }
 
@@ -846,7 +890,7 @@ __device__ __forceinline__ bool look_back(const Engine<T, D, M, C> &e, const Fus
     const int jstar = (int)sh_word[0] - 1;
     if (jstar < 0) return false;
     const size_t h0 = (size_t)bh * G_;
-    e.state_add_slots(pre, zpre, (jstar == 0 ? ws.agg : ws.incl) + (h0 + jstar) * Gc::E, ws.agg + h0 * Gc::E,
+    e.state_add_slots(pre, zpre, (jstar == 0 ? ws.agg : ws.incl) + (h0 + jstar) * Gc::EP, ws.agg + h0 * Gc::EP,
                       jstar + 1, s);
     return true;
 }
@@ -869,7 +913,7 @@ __device__ __forceinline__ void publish_inclusive(const Engine<T, D, M, C> &e, c
             inc[dt][i] = pre[dt][i] + acc[dt][i];
             if (failed) inc[dt][i] = f32x4{nan, nan, nan, nan};
         }
-    e.state_store_coherent(inc, failed ? nan : zpre + zacc, ws.incl + my * Gc::E);
+    e.slot_store(inc, failed ? nan : zpre + zacc, ws.incl + my * Gc::EP);
     e.publish_flag(&ws.flags[my], ep | 2u);
 }
 
@@ -948,9 +992,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
             for (int dt = 0; dt < Gc::DT; ++dt)
 #pragma unroll
                 for (int i = 0; i < Gc::MTW; ++i) a0[dt][i] = acc[dt][i] + pre[dt][i];
-            e.state_store_coherent(a0, zacc + zpre, ws.agg + my * Gc::E);
+            e.slot_store(a0, zacc + zpre, ws.agg + my * Gc::EP);
         } else {
-            e.state_store_coherent(acc, zacc, ws.agg + my * Gc::E);
+            e.slot_store(acc, zacc, ws.agg + my * Gc::EP);
         }
         e.publish_flag(&ws.flags[my], ep | 1u);
     }
@@ -1078,15 +1122,14 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 #pragma unroll
     for (int j = 0; j < NC; ++j) En::zero_out(o[j]);
 
-    Stage<T, C, D, Gc::THREADS> q0, q1;
-    KVBuf<T, D, M, C> b0, b1;
-    q0.load(Qh, c0 * C, N, tid);
-    b0.load(Kh, Vh, c0, N, tid);
-    if (nc > 1) {
-        q1.load(Qh, (c0 + 1) * C, N, tid);
-        b1.load(Kh, Vh, c0 + 1, N, tid);
-    }
-    auto step = [&](Stage<T, C, D, Gc::THREADS> &q, KVBuf<T, D, M, C> &b, int j, f32x4 (&oj)[Gc::RT][Gc::MTW]) {
+    // loads one chunk ahead, unconditional (clamped to the segment's last chunk)
+    // so the compiler's wait counts stay exact (see phase_a)
+    const int clast = c0 + nc - 1;
+    Stage<T, C, D, Gc::THREADS> q;
+    KVBuf<T, D, M, C> b;
+    q.load(Qh, c0 * C, N, tid);
+    b.load(Kh, Vh, c0, N, tid);
+    auto step = [&](int j, f32x4 (&oj)[Gc::RT][Gc::MTW]) {
         const int c = c0 + j, row0 = c * C;
         __syncthreads();  // sK, sV, sA, side arrays free
         e.sQ = sQs + j * C * Gc::LQ;
@@ -1094,9 +1137,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         e.store_kv(b.k, b.v, row0, N);
         if (tid < D) e.sz[tid] = round_as<T>(z);
         __syncthreads();
-        if (j + 2 < nc) {
-            q.load(Qh, (c + 2) * C, N, tid);
-            b.load(Kh, Vh, c + 2, N, tid);
+        if (j + 1 < NC) {  // compile-time: no load past the last possible step
+            q.load(Qh, min(c + 1, clast) * C, N, tid);
+            b.load(Kh, Vh, min(c + 1, clast), N, tid);
         }
         e.a_tiles();
         e.qz_rows();
@@ -1114,12 +1157,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     };
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
-        if (j < nc) {
-            if (j & 1)
-                step(q1, b1, j, o[j]);
-            else
-                step(q0, b0, j, o[j]);
-        }
+        if (j < nc) step(j, o[j]);
     }
 
     const size_t my = (size_t)bh * G_ + s;
@@ -1136,9 +1174,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
             for (int dt = 0; dt < Gc::DT; ++dt)
 #pragma unroll
                 for (int i = 0; i < Gc::MTW; ++i) a0[dt][i] = S[dt][i] + pre[dt][i];
-            e.state_store_coherent(a0, z + zpre, ws.agg + my * Gc::E);
+            e.slot_store(a0, z + zpre, ws.agg + my * Gc::EP);
         } else {
-            e.state_store_coherent(S, z, ws.agg + my * Gc::E);
+            e.slot_store(S, z, ws.agg + my * Gc::EP);
         }
         e.publish_flag(&ws.flags[my], ep | 1u);
     }

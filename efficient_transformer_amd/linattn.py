@@ -199,7 +199,8 @@ def fused_workspace_bytes(B, H, D, M, segments) -> int:
     if segments <= 1:
         return 0
     bhg = B * H * segments
-    return (64 + 64 * ((bhg + 63) // 64)) * 4 + 2 * bhg * (D * M + D) * 4
+    slot = (D * M + D + 63) // 64 * 64  # one exchanged state, padded to whole 256-byte blocks
+    return (64 + 64 * ((bhg + 63) // 64)) * 4 + 2 * bhg * slot * 4
 
 
 def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None,

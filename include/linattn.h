@@ -140,7 +140,8 @@ LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stre
  * The causal fused kernel of la_forward_chunked with an explicit plan: chunk
  * (16, 32 or 64) and segments (each segment must own at least one chunk).
  * Workspace: 0 bytes when segments == 1, else
- *   (64 + 64*ceil(B*H*segments/64)) * 4 + 2 * B*H*segments * (D*M + D) * 4 bytes,
+ *   (64 + 64*ceil(B*H*segments/64)) * 4 + 2 * B*H*segments * P * 4 bytes with
+ *   P = 64*ceil((D*M + D)/64) (one state padded to whole 256-byte blocks),
  * initialised as for la_forward_chunked.  S_in / z_in as for la_forward_continue
  * (NULL: start from zero); S_out / z_out as for la_forward_chunked.
  */

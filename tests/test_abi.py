@@ -70,7 +70,8 @@ def test_plan_covers_the_sequence(L, B, H, N, D, M, causal, dtype, chunk):
     E = D * M + D
     if causal:
         bhg = B * H * G
-        assert ws == (0 if G == 1 else (64 + 64 * ((bhg + 63) // 64)) * 4 + 2 * bhg * E * 4)
+        P = (E + 63) // 64 * 64
+        assert ws == (0 if G == 1 else (64 + 64 * ((bhg + 63) // 64)) * 4 + 2 * bhg * P * 4)
     else:
         assert ws == B * H * (G + 1) * E * 4
     assert L.workspace_bytes(B, H, N, D, M, causal, dtype, chunk) == ws
