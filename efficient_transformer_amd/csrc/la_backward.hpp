@@ -111,7 +111,7 @@ struct BwdEngine {
         sCol = smem + G::oCol;
         tid = threadIdx.x;
         lane = tid & 63;
-        w = tid >> 6;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
         g = lane >> 4;
         l16 = lane & 15;
     }
@@ -121,13 +121,13 @@ struct BwdEngine {
     __device__ __forceinline__ int mtile(int i) const { return w + kBwdWaves * i; }
 
     // Masked C x C product tiles: out[a][b] = sum_k X[a][k] Y[b][k] over K columns,
-    // kept where (UPPER ? b >= a : b <= a), plus add_b[b] (if given) on kept
-    // entries; written to dst[a][b].  Row tiles (at, bt) of the kept triangle are
+    // kept where (UPPER ? b >= a : b <= a), plus add_a[a] and add_b[b] (if given)
+    // on kept entries; written to dst[a][b].  Row tiles (at, bt) of the kept triangle are
     // shared out over the wavefronts.  Rows of X and Y are read as f32x4 (the
     // contraction index d = g*(K/4) + j is contiguous per lane).
     template <int K, bool UPPER>
     __device__ __forceinline__ void tri_tiles(const float *X, int ldx, const float *Y, int ldy, const float *add_b,
-                                              float *dst) const {
+                                              float *dst, const float *add_a = nullptr) const {
         constexpr int NA = RT * (RT + 1) / 2;
         for (int t = w; t < NA; t += kBwdWaves) {
             int hi = 0;
@@ -147,11 +147,12 @@ struct BwdEngine {
             }
             // acc[r] = out[a = at*16 + l16][b = bt*16 + 4g + r]
             const int a = at * 16 + l16;
+            const float ya = add_a ? add_a[a] : 0.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int b = bt * 16 + 4 * g + r;
                 const bool keep = UPPER ? (b >= a) : (b <= a);
-                float v = acc[r] + (add_b ? add_b[b] : 0.0f);
+                float v = acc[r] + ya + (add_b ? add_b[b] : 0.0f);
                 acc[r] = keep ? v : 0.0f;
             }
             *reinterpret_cast<f32x4 *>(dst + a * G::LC + bt * 16 + 4 * g) = acc;
@@ -187,10 +188,22 @@ struct BwdEngine {
     // dot products of rows: out[i] = X[i] . Y[i] over K columns (TPR threads per row)
     template <int K>
     __device__ __forceinline__ void row_dots(const float *X, int ldx, const float *Y, int ldy, float *out) const {
-        constexpr int TPR = kBwdThreads / C;  // 8
+        constexpr int TPR = kBwdThreads / C;  // 8 threads per row, each K/8 contiguous columns
+        constexpr int EPT = K / TPR;
         const int i = tid / TPR, p = tid % TPR;
+        const float *x = X + i * ldx + p * EPT, *y = Y + i * ldy + p * EPT;
         float s = 0.0f;
-        for (int k = p; k < K; k += TPR) s += X[i * ldx + k] * Y[i * ldy + k];
+        if constexpr (EPT % 4 == 0) {
+#pragma unroll
+            for (int v = 0; v < EPT / 4; ++v) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(x + 4 * v);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(y + 4 * v);
+                s += (a[0] * b[0] + a[1] * b[1]) + (a[2] * b[2] + a[3] * b[3]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPT; ++k) s += x[k] * y[k];
+        }
 #pragma unroll
         for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
         if (p == 0) out[i] = s;
@@ -263,27 +276,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const T *__restrict
         e.template row_dots<M>(e.sR, Gc::LM, e.sO, Gc::LM, e.sCc);
         __syncthreads();
         if (tid < C) {
+            // row sum of tril(A): the tile rows as 16-byte reads
             float den = e.sQz[tid];
-            for (int j = 0; j < C; ++j) den += e.sP[tid * Gc::LC + j];
+#pragma unroll
+            for (int j4 = 0; j4 < C / 4; ++j4) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(e.sP + tid * Gc::LC + 4 * j4);
+                den += (a[0] + a[1]) + (a[2] + a[3]);
+            }
             if (row0 + tid >= N) den = 1.0f;  // padding rows: r = c = 0
-            e.sDen[tid] = den;
-            e.sCc[tid] = -e.sCc[tid] / den;
+            const float inv = 1.0f / den;
+            e.sDen[tid] = inv;  // 1 / den from here on
+            e.sCc[tid] = -e.sCc[tid] * inv;
             if (row0 + tid < N) den_out[(size_t)bh * N + row0 + tid] = den;
         }
         __syncthreads();
-        for (int x = tid; x < C * M; x += kBwdThreads) {
-            const int i = x / M, m = x % M;
-            e.sR[i * Gc::LM + m] /= e.sDen[i];
+        for (int x = tid; x < C * M / 4; x += kBwdThreads) {
+            const int i = x / (M / 4), m4 = x % (M / 4);
+            f32x4 *p = reinterpret_cast<f32x4 *>(e.sR + i * Gc::LM + 4 * m4);
+            *p = *p * e.sDen[i];
         }
         __syncthreads();
         // B = tril(R V^T + c 1^T): B[i][j] = r_i . v_j + c_i for j <= i (stored [i][j])
-        // (the c_i term is added per row a = i: use add over a via a second pass below)
-        e.template tri_tiles<M, false>(e.sR, Gc::LM, e.sV, Gc::LM, nullptr, e.sP);
-        __syncthreads();
-        for (int x = tid; x < C * C; x += kBwdThreads) {
-            const int i = x / C, j = x % C;
-            if (j <= i) e.sP[i * Gc::LC + j] += e.sCc[i];
-        }
+        e.template tri_tiles<M, false>(e.sR, Gc::LM, e.sV, Gc::LM, nullptr, e.sP, e.sCc);
         __syncthreads();
         // dG^T tiles for the own d-tiles, rows i of the chunk
 #pragma unroll
@@ -438,9 +452,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(const T *__restric
         e.template row_dots<M>(e.sR, Gc::LM, e.sO, Gc::LM, e.sCc);
         __syncthreads();
         if (tid < C) e.sCc[tid] = -e.sCc[tid] / e.sDen[tid];
-        for (int x = tid; x < C * M; x += kBwdThreads) {
-            const int i = x / M, m = x % M;
-            e.sR[i * Gc::LM + m] /= e.sDen[i];
+        for (int x = tid; x < C * M / 4; x += kBwdThreads) {
+            const int i = x / (M / 4), m4 = x % (M / 4);
+            f32x4 *p = reinterpret_cast<f32x4 *>(e.sR + i * Gc::LM + 4 * m4);
+            *p = *p * (1.0f / e.sDen[i]);
         }
         __syncthreads();
         // P[j][i] = v_j . r_i + c_i (i >= j);  P2[j][i] = f_j . g_i (i >= j)

@@ -59,9 +59,11 @@ def test_backward_parity(ea, dtype, D, M, N):
 
 
 def test_backward_first_row_has_no_query_gradient(ea):
-    """out_0 = v_0 whatever q_0 and k_0 are."""
+    """out_0 = v_0 whatever q_0 and k_0 are: dq_0 vanishes up to fp32 rounding
+    (r_0 . v_0 + c_0 cancels)."""
     got, _ = run(ea, "f32", 1, 2, 50, 64, 64, 41)
-    assert np.all(got[0][:, :, 0] == 0.0)
+    dq = got[0]
+    assert np.max(np.abs(dq[:, :, 0])) <= 1e-5 * np.max(np.abs(dq))
 
 
 def test_backward_value_gradients_sum_to_output_gradients(ea):
