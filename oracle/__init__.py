@@ -59,6 +59,8 @@ class Oracle:
                                          ctypes.POINTER(_i64), _i64, _dp, ctypes.c_int]
         L.oracle_noncausal.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int]
         L.oracle_decode_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int]
+        L.oracle_softmax_scan.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int]
+        L.oracle_softmax_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int]
         L.oracle_causal_backward.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64,
                                              ctypes.c_int]
         self.L = L
@@ -158,6 +160,35 @@ class Oracle:
         return dQ, dK, dV
 
 
+    def softmax_scan(self, q, K, V, threads: int = 0):
+        """Softmax attention of one query per head over every prefix (q [..., D], K [..., N, D],
+        V [..., N, M]).  Returns (out [..., N, M], m [...], u [...], w [..., M]), the last three
+        the final state (max score, sum of exp, sum of exp-weighted values)."""
+        q, K, V = _f64(q), _f64(K), _f64(V)
+        *lead, N, D = K.shape
+        M = V.shape[-1]
+        assert tuple(q.shape) == (*lead, D) and tuple(V.shape[:-1]) == tuple(K.shape[:-1])
+        BH = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, N, M))
+        m = np.empty(tuple(lead))
+        u = np.empty(tuple(lead))
+        w = np.empty((*lead, M))
+        self.L.oracle_softmax_scan(_p(q), _p(K), _p(V), _p(out), _p(m), _p(u), _p(w), BH, N, D, M, threads)
+        return out, m, u, w
+
+    def softmax_step(self, m, u, w, q, k, v, threads: int = 0) -> np.ndarray:
+        """One token; m, u [...], w [..., M] (float64, contiguous) update in place."""
+        for a in (m, u, w):
+            assert a.dtype == np.float64 and a.flags.c_contiguous
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        M = w.shape[-1]
+        BH = m.size
+        D = q.size // BH
+        out = np.empty(v.shape)
+        self.L.oracle_softmax_step(_p(m), _p(u), _p(w), _p(q), _p(k), _p(v), _p(out), BH, D, M, threads)
+        return out
+
+
 def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
 
@@ -208,3 +239,11 @@ def decode_step(S, z, q, k, v, threads: int = 0):
 
 def causal_backward(Q, K, V, dO, threads: int = 0):
     return default().causal_backward(Q, K, V, dO, threads)
+
+
+def softmax_scan(q, K, V, threads: int = 0):
+    return default().softmax_scan(q, K, V, threads)
+
+
+def softmax_step(m, u, w, q, k, v, threads: int = 0):
+    return default().softmax_step(m, u, w, q, k, v, threads)

@@ -310,3 +310,64 @@ void oracle_causal_backward(const double *Q, const double *K, const double *V, c
         free(S); free(z); free(r); free(c); free(o);
     }
 }
+
+/* Softmax attention of one query per head over every prefix, as an RNN
+ * (page "Attention as an RNN", Proposed method: attention is an RNN whose
+ * many-to-many outputs -- the attention of the query over each prefix -- are
+ * computed with a running state; the query is a learned vector q).  With
+ * s_i = q . k_i (no scaling; a caller scales q), the state after position k is
+ * (m_k, u_k, w_k) = (max_{i<=k} s_i, sum_{i<=k} exp(s_i - m_k),
+ * sum_{i<=k} exp(s_i - m_k) v_i), updated position by position:
+ *   m' = max(m, s);  u' = u e^{m - m'} + e^{s - m'};  w' = w e^{m - m'} + e^{s - m'} v
+ * and out_k = w_k / u_k.  q [BH][D]; K [BH][N][D]; V, out [BH][N][M];
+ * m_out, u_out [BH], w_out [BH][M] (may be NULL): the final state. */
+void oracle_softmax_scan(const double *q, const double *K, const double *V, double *out,
+                         double *m_out, double *u_out, double *w_out,
+                         int64_t BH, int64_t N, int64_t D, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const double *qh = q + h * D, *Kh = K + h * N * D, *Vh = V + h * N * M;
+        double *Oh = out + h * N * M;
+        double *w = (double *)calloc((size_t)M, sizeof(double));
+        double m = -INFINITY, u = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+            double s = 0.0;
+            for (int64_t d = 0; d < D; ++d) s += qh[d] * Kh[i * D + d];
+            const double mn = m > s ? m : s;
+            const double a = exp(m - mn), b = exp(s - mn);
+            u = u * a + b;
+            for (int64_t j = 0; j < M; ++j) {
+                w[j] = w[j] * a + b * Vh[i * M + j];
+                Oh[i * M + j] = w[j] / u;
+            }
+            m = mn;
+        }
+        if (m_out) m_out[h] = m;
+        if (u_out) u_out[h] = u;
+        if (w_out) memcpy(w_out + h * M, w, (size_t)M * sizeof(double));
+        free(w);
+    }
+}
+
+/* One token of the same RNN for BH heads (constant memory): the state
+ * (m [BH], u [BH], w [BH][M]) is updated in place with (k, v) and the output is
+ * the attention of q over every token seen so far.  q, k [BH][D]; v, out [BH][M].
+ * A fresh state is m = -inf, u = 0, w = 0. */
+void oracle_softmax_step(double *m, double *u, double *w, const double *q, const double *k,
+                         const double *v, double *out, int64_t BH, int64_t D, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        double s = 0.0;
+        for (int64_t d = 0; d < D; ++d) s += q[h * D + d] * k[h * D + d];
+        const double mn = m[h] > s ? m[h] : s;
+        const double a = exp(m[h] - mn), b = exp(s - mn);
+        u[h] = u[h] * a + b;
+        for (int64_t j = 0; j < M; ++j) {
+            w[h * M + j] = w[h * M + j] * a + b * v[h * M + j];
+            out[h * M + j] = w[h * M + j] / u[h];
+        }
+        m[h] = mn;
+    }
+}

@@ -339,8 +339,65 @@ def pin_backward(o, fails):
             fails.append(f"backward finite differences d{nm}: {err:.3e}")
 
 
+def pin_softmax_scan(o, fails):
+    """Softmax attention of one query over every prefix: against scipy's softmax on each
+    prefix (library routine), 50-digit mpmath, closed forms (V = 1; q = 0 gives prefix means;
+    out_0 = v_0; the final state), scores far beyond exp's range, and the one-token RNN."""
+    from scipy.special import softmax as sp_softmax
+    rng = np.random.default_rng(51)
+    for (N, D, M, scale) in [(1, 3, 2, 1.0), (9, 4, 3, 1.0), (40, 16, 5, 3.0), (33, 8, 8, 30.0)]:
+        q = rng.normal(size=D) * scale
+        K = rng.normal(size=(N, D))
+        V = rng.normal(size=(N, M))
+        out, m, u, w = o.softmax_scan(q[None], K[None], V[None])
+        sc = K @ q
+        want = np.stack([sp_softmax(sc[:k + 1]) @ V[:k + 1] for k in range(N)])
+        _close(f"softmax scan N{N} D{D} M{M} s{scale}", out[0], want, 1e-11, fails)
+        _close(f"softmax final m N{N}", np.array([m[0]]), np.array([sc.max()]), 1e-14, fails)
+        e = np.exp(sc - sc.max())
+        _close(f"softmax final u N{N}", np.array([u[0]]), np.array([e.sum()]), 1e-12, fails)
+        _close(f"softmax final w N{N}", w[0], e @ V, 1e-12, fails)
+        ones = o.softmax_scan(q[None], K[None], np.ones((1, N, M)))[0][0]
+        if not np.max(np.abs(ones - 1.0)) <= 1e-14:
+            fails.append(f"softmax ones invariant N{N}")
+        zq = o.softmax_scan(np.zeros((1, D)), K[None], V[None])[0][0]
+        _close(f"softmax q=0 prefix means N{N}", zq, np.cumsum(V, axis=0) / np.arange(1, N + 1)[:, None], 1e-12,
+               fails)
+        _close(f"softmax first row N{N}", out[0, 0], V[0], 1e-14, fails)
+        # the one-token RNN reproduces every row and the state
+        ms, us, ws = np.full(1, -np.inf), np.zeros(1), np.zeros((1, M))
+        steps = np.stack([o.softmax_step(ms, us, ws, q[None], K[None, i], V[None, i]) for i in range(N)], axis=1)
+        _close(f"softmax step == scan N{N}", steps[0], out[0], 1e-12, fails)
+        _close(f"softmax step state N{N}", ws[0], w[0], 1e-12, fails)
+    # scores beyond the range of exp: stays finite, equals the shifted definition
+    q = np.array([800.0, -800.0])
+    K = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 0.1], [-1.0, 0.0]])
+    V = rng.normal(size=(4, 3))
+    out = o.softmax_scan(q[None], K[None], V[None])[0][0]
+    sc = K @ q
+    want = np.stack([sp_softmax(sc[:k + 1]) @ V[:k + 1] for k in range(4)])
+    if not np.all(np.isfinite(out)):
+        fails.append("softmax scan overflow")
+    _close("softmax scan extreme scores", out, want, 1e-12, fails)
+    # 50-digit evaluation of the definition
+    mpmath.mp.dps = 50
+    N, D, M = 6, 3, 2
+    q = rng.normal(size=D) * 4
+    K = rng.normal(size=(N, D))
+    V = rng.normal(size=(N, M))
+    out = o.softmax_scan(q[None], K[None], V[None])[0][0]
+    for k in range(N):
+        ws_ = [mpmath.exp(mpmath.fsum(mpmath.mpf(float(q[d])) * mpmath.mpf(float(K[i, d])) for d in range(D)))
+               for i in range(k + 1)]
+        tot = mpmath.fsum(ws_)
+        for j in range(M):
+            val = float(mpmath.fsum(ws_[i] * mpmath.mpf(float(V[i, j])) for i in range(k + 1)) / tot)
+            if not abs(out[k, j] - val) <= 1e-13 * max(1.0, abs(val)):
+                fails.append(f"softmax mpmath row {k} col {j}")
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked, pin_continue,
-            pin_backward]
+            pin_backward, pin_softmax_scan]
 
 
 def run_all(o, pins=ALL_PINS):

@@ -43,6 +43,10 @@ MUTANTS = {
     "backward_reverse_sum_exclusive": (
         "                for (int64_t m = 0; m < M; ++m) R[d * M + m] += g * r[j * M + m];\n                w[d] += c[j] * g;\n            }\n            for (int64_t d = 0; d < D; ++d) {\n                double df = w[d];",
         "                for (int64_t m = 0; m < M; ++m) R[d * M + m] += 0.0 * g * r[j * M + m];\n                w[d] += c[j] * g;\n            }\n            for (int64_t d = 0; d < D; ++d) {\n                double df = w[d];"),
+    "softmax_w_not_rescaled": ("                w[j] = w[j] * a + b * Vh[i * M + j];", "                w[j] = w[j] + b * Vh[i * M + j];"),
+    "softmax_max_not_carried": ("                Oh[i * M + j] = w[j] / u;\n            }\n            m = mn;", "                Oh[i * M + j] = w[j] / u;\n            }\n            m = 0.0;"),
+    "softmax_rescale_sign": ("            const double a = exp(m - mn), b = exp(s - mn);\n            u = u * a + b;", "            const double a = exp(mn - m), b = exp(s - mn);\n            u = u * a + b;"),
+    "softmax_step_u_not_rescaled": ("        u[h] = u[h] * a + b;", "        u[h] = u[h] + b;"),
     "continue_ignores_z0": ("memcpy(z, z0 + h * D, (size_t)D * sizeof(double));",
                             "memset(z, 0, (size_t)D * sizeof(double));"),
     "continue_ignores_S0": ("memcpy(S, S0 + h * D * M, (size_t)(D * M) * sizeof(double));",
