@@ -19,6 +19,8 @@ from .linattn import (  # noqa: F401
     segment_outputs,
     segment_scan,
     segment_states,
+    softmax_scan,
+    softmax_step,
     version,
     workspace_bytes,
     workspace_init,

@@ -455,6 +455,61 @@ LA_API int la_backward_chunked(const void *Q, const void *K, const void *V, cons
     return hip_status(e);
 }
 
+namespace {
+int scan_check(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype, int64_t *items) {
+    if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (N > INT_MAX || B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
+    const int64_t R = la::softmax_scan_rows((int)M);
+    const int64_t NS = (N + R - 1) / R;
+    if (B * H * NS > INT_MAX / 64) return LA_ERR_UNSUPPORTED;
+    *items = B * H * NS;
+    return LA_OK;
+}
+}  // namespace
+
+LA_API size_t la_softmax_scan_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M) {
+    int64_t items = 0;
+    if (scan_check(B, H, N, D, M, LA_F32, &items) != LA_OK) return 0;
+    const int64_t NS = B * H > 0 ? items / (B * H) : 0;
+    return NS > 1 ? la::scan_ws_bytes((long)items, (int)M) : 0;
+}
+
+LA_API int la_softmax_scan(const void *q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                           int64_t N, int64_t D, int64_t M, int dtype, void *workspace, size_t workspace_bytes,
+                           float *m_out, float *u_out, float *w_out, void *stream) {
+    int64_t items = 0;
+    int st = scan_check(B, H, N, D, M, dtype, &items);
+    if (st != LA_OK) return st;
+    if ((m_out == nullptr) != (u_out == nullptr) || (m_out == nullptr) != (w_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if (w_out && !aligned16(w_out)) return LA_ERR_INVALID_ARG;
+    if (B * H == 0 || N == 0) return LA_OK;
+    if (!q || !K || !V || !out) return LA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+    const size_t need = la_softmax_scan_workspace_bytes(B, H, N, D, M);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LA_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::softmax_scan(dtype, (int)D, (int)M, q, K, V, out, workspace, (int)(B * H), (int)N, m_out,
+                                       u_out, w_out, as_stream(stream)));
+}
+
+LA_API int la_softmax_step(float *m, float *u, float *w, const void *q, const void *k, const void *v, float *out,
+                           int64_t B, int64_t H, int64_t D, int64_t M, int dtype, void *stream) {
+    if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (B * H == 0) return LA_OK;
+    if (!m || !u || !w || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::softmax_step(dtype, (int)D, (int)M, m, u, w, q, k, v, out, (int)(B * H),
+                                       as_stream(stream)));
+}
+
 LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, const void *v, float *out, int64_t B,
                            int64_t H, int64_t T, int64_t D, int64_t M, int dtype, void *stream) {
     if (B < 0 || H < 0 || T < 0) return LA_ERR_INVALID_ARG;

@@ -19,6 +19,19 @@ __host__ __device__ inline size_t fused_ws_bytes(long BH, int G, int E) {
     return (kWsHeaderWords + fused_flag_words((long)BHG)) * 4 + 2 * BHG * (size_t)fused_slot_floats(E) * 4;
 }
 
+// Softmax scan (la_softmax_scan.hip): one state = M value sums + max + sum,
+// padded to whole 256-byte blocks; workspace = header + flags + 2 states per
+// segment of softmax_scan_rows(M) rows.
+__host__ __device__ constexpr int scan_slot_floats(int M) { return (M + 2 + 63) / 64 * 64; }
+__host__ __device__ inline size_t scan_ws_bytes(long items, int M) {
+    return (kWsHeaderWords + fused_flag_words(items)) * 4 + 2 * (size_t)items * (size_t)scan_slot_floats(M) * 4;
+}
+int softmax_scan_rows(int M);
+hipError_t softmax_scan(int dtype, int D, int M, const void *q, const void *K, const void *V, float *out, void *ws,
+                        int BH, int N, float *m_out, float *u_out, float *w_out, hipStream_t stream);
+hipError_t softmax_step(int dtype, int D, int M, float *m, float *u, float *w, const void *q, const void *k,
+                        const void *v, float *out, int BH, hipStream_t stream);
+
 // Prefill stage launchers for one element type (0 = fp32, 1 = bf16).
 // Each returns hipErrorInvalidValue for a (D, M, C) combination that has no kernel.
 bool prefill_supported(int dtype, int D, int M, int C);

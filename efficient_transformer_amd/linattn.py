@@ -43,6 +43,10 @@ SIGNATURES = {
     "la_backward_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int]),
     "la_backward_chunked": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int,
                                    _vp, _sz, _vp]),
+    "la_softmax_scan_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "la_softmax_scan": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp, _sz, _vp, _vp, _vp,
+                               _vp]),
+    "la_softmax_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_decode_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_decode_steps": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
 }
@@ -351,3 +355,42 @@ def backward(Q, K, V, out, dout, workspace=None, stream=None):
                                    B, H, N, D, M, dt, _ptr(workspace), wbytes, _stream(stream, dev))
     _check(st, "la_backward_chunked")
     return dQ, dK, dV
+
+
+def softmax_scan(q, K, V, out=None, workspace=None, m_out=None, u_out=None, w_out=None, stream=None):
+    """Softmax attention of one query per head (q [B,H,D]) over every prefix of K, V."""
+    import torch
+    B, H, N, D = K.shape
+    M = V.shape[-1]
+    dev = K.device
+    _require(q, "q", (B, H, D), K.dtype, dev)
+    _require(V, "V", (B, H, N, M), K.dtype, dev)
+    if out is None:
+        out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
+    need = int(lib().la_softmax_scan_workspace_bytes(B, H, N, D, M))
+    if workspace is None and need > 0:
+        workspace = _cached_workspace(need, dev, stream, ("softmax_scan", B * H, N, D, M))
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().la_softmax_scan(_ptr(q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(K), _ptr(workspace),
+                               wbytes, _ptr(m_out), _ptr(u_out), _ptr(w_out), _stream(stream, dev))
+    _check(st, "la_softmax_scan")
+    return out
+
+
+def softmax_step(m, u, w, q, k, v, out=None, stream=None):
+    """One token: state m, u [B,H] and w [B,H,M] (float32, in place); q, k [B,H,D]; v [B,H,M]."""
+    import torch
+    B, H, M = w.shape
+    D = q.shape[-1]
+    dev = w.device
+    _require(m, "m", (B, H), torch.float32, dev)
+    _require(u, "u", (B, H), torch.float32, dev)
+    _require(q, "q", (B, H, D), None, dev)
+    _require(k, "k", (B, H, D), q.dtype, dev)
+    _require(v, "v", (B, H, M), q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+    st = lib().la_softmax_step(_ptr(m), _ptr(u), _ptr(w), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, D, M,
+                               _dtype_code(q), _stream(stream, dev))
+    _check(st, "la_softmax_step")
+    return out

@@ -257,6 +257,39 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
                            float *out, int64_t B, int64_t H, int64_t T, int64_t D, int64_t M,
                            int dtype, void *stream);
 
+/*
+ * Softmax attention as an RNN (page "Attention as an RNN", Proposed method:
+ * attention's many-to-many RNN outputs computed with a parallel prefix scan;
+ * the query is a learned vector).  One query q per head; with s_i = q . k_i (no
+ * scaling -- scale q beforehand) every position k receives the softmax
+ * attention of q over positions 0..k:
+ *   out_k = sum_{i<=k} exp(s_i) v_i / sum_{i<=k} exp(s_i),
+ * evaluated with the running state (m, u, w) = (max s, sum exp(s - m),
+ * sum exp(s - m) v), which never overflows.
+ * q: [B][H][D]; K: [B][H][N][D]; V: [B][H][N][M] (fp32 or bf16); out
+ * [B][H][N][M] fp32.  m_out, u_out [B][H] and w_out [B][H][M] fp32: optional
+ * (all or none), the state after the last position, for la_softmax_step.
+ * workspace: la_softmax_scan_workspace_bytes(...) bytes (0 when every head fits
+ * one segment of 64 positions, 32 when M = 128), zeroed (la_workspace_init)
+ * before its first use, then reusable by later calls with the same shape;
+ * calls sharing a workspace must not overlap.
+ */
+LA_API size_t la_softmax_scan_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M);
+LA_API int la_softmax_scan(const void *q, const void *K, const void *V, float *out,
+                           int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
+                           void *workspace, size_t workspace_bytes,
+                           float *m_out, float *u_out, float *w_out, void *stream);
+
+/*
+ * One token of the same RNN for every head, in constant memory: the state
+ * m [B][H], u [B][H], w [B][H][M] (fp32, updated in place; a fresh state is
+ * m = -inf, u = 0, w = 0) takes (k, v) and out receives the attention of q over
+ * every token seen so far.  q, k [B][H][D]; v, out [B][H][M].
+ */
+LA_API int la_softmax_step(float *m, float *u, float *w, const void *q, const void *k,
+                           const void *v, float *out, int64_t B, int64_t H, int64_t D,
+                           int64_t M, int dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     for s in ("la_forward_chunked", "la_decode_step", "la_forward_workspace_bytes", "la_forward_plan",
               "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version",
-              "la_forward_fused", "la_forward_onepass", "la_forward_continue", "la_workspace_init"):
+              "la_forward_fused", "la_forward_onepass", "la_forward_continue", "la_workspace_init",
+              "la_backward_chunked", "la_decode_steps", "la_softmax_scan", "la_softmax_step"):
         assert s in syms
 
 
@@ -203,6 +204,26 @@ def test_decode_steps_checks(L):
     assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
     assert f(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
     assert f(None, None, None, None, None, None, 2, 2, 0, 64, 64, 0, None) == L.LA_OK  # T = 0
+
+
+def test_softmax_scan_checks(L):
+    f = L.lib().la_softmax_scan
+    need = L.lib().la_softmax_scan_workspace_bytes(2, 2, 1000, 64, 64)
+    items = 2 * 2 * 16  # segments of 64 positions
+    assert need == (64 + 64 * ((items + 63) // 64)) * 4 + 2 * items * 128 * 4
+    assert L.lib().la_softmax_scan_workspace_bytes(2, 2, 64, 64, 64) == 0  # one segment per head
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 48, 64, 0, FAKE, need, None, None, None, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 2, FAKE, need, None, None, None, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, FAKE, need - 4, None, None, None,
+             None) == L.LA_ERR_WORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, FAKE, need, FAKE, None, None,
+             None) == L.LA_ERR_INVALID_ARG  # m_out without u_out, w_out
+    assert f(None, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, FAKE, need, None, None, None, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 0, 64, 64, 0, None, 0, None, None, None, None) == L.LA_OK
+    g = L.lib().la_softmax_step
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 48, 0, None) == L.LA_ERR_UNSUPPORTED
+    assert g(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
+    assert g(FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
 
 
 def test_product_path_never_imports_the_oracle():
