@@ -14,8 +14,8 @@ Also reported in the same JSON line: the dominant kernel's roofline (HIP
 events around each launch of it), the fp64 CPU oracle timed on a bounded
 sample of the same workload, the recurrent decode workload (256 streams x 8
 heads, D=M=64, 4096 steps from a zero state), the two bf16 prefill
-workloads, the backward pass on the headline shape and the multi-token
-decode (16 tokens per call).  Prints exactly one JSON line on stdout; progress goes to stderr.
+workloads, the backward pass on the headline shape, the multi-token
+decode (16 tokens per call) and the softmax-attention RNN scan.  Prints exactly one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -265,6 +265,44 @@ def bench_decode_steps(cfg, T, calls, dev):
                 GBs=per_call / (ms * 1e-3) / 1e9)
 
 
+def bench_softmax_scan(cfg, steps, dev):
+    """la_softmax_scan (one query per head) on a prefill-shaped workload, inputs rotated past
+    the last-level cache.  Algorithmic bytes: read q, k, v once, write out once."""
+    import torch
+    import efficient_transformer_amd as ea
+    import synthetic
+
+    B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
+    s_in = 4 if cfg["dtype"] == "f32" else 2
+    nbytes = B * H * (D * s_in + N * (D * s_in + M * s_in + 4 * M))
+    nsets = max(1, math.ceil(1.25 * LLC_BYTES / nbytes))
+    sets = []
+    for i in range(nsets):
+        q = synthetic.draw_torch(20 + i, 9, (B, H, D), 0.125, cfg["dtype"], dev)
+        K = synthetic.draw_torch(20 + i, 1, (B, H, N, D), cfg["sigma"], cfg["dtype"], dev)
+        V = synthetic.draw_torch(20 + i, 2, (B, H, N, M), cfg["sigma"], cfg["dtype"], dev)
+        sets.append((q, K, V, torch.empty((B, H, N, M), device=dev)))
+    wsb = int(ea.linattn.lib().la_softmax_scan_workspace_bytes(B, H, N, D, M))
+    ws = torch.zeros(max(16, wsb), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(5):
+        q, K, V, o = sets[i % nsets]
+        ea.softmax_scan(q, K, V, out=o, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        q, K, V, o = sets[i % nsets]
+        ev[i][0].record(stream)
+        ea.softmax_scan(q, K, V, out=o, workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+    del sets
+    torch.cuda.empty_cache()
+    return dict(us_kernel=us, tokens_per_s=B * N / (us * 1e-6), bytes=nbytes, nsets=nsets,
+                GBs=nbytes / (us * 1e-6) / 1e9)
+
+
 def causal_kernel_name(cfg, chunk, segments) -> str:
     n_chunks = -(-cfg["N"] // chunk)
     cps = -(-n_chunks // segments)
@@ -299,7 +337,7 @@ def cpu_baseline(cfg, target_s=12.0):
 
 def profile_run(dev):
     """Untimed launches for counter collection: 4 headline prefill calls, 4 decode steps,
-    2 backward calls, 2 multi-token decode calls, 2 calls of each bf16 prefill workload and
+    2 backward calls, 2 multi-token decode calls, 2 softmax scans, 2 calls of each bf16 prefill workload and
     4 copies of a 512 MiB fp32 buffer (known traffic: 512 MiB read + 512 MiB written each)."""
     import torch
     import efficient_transformer_amd as ea
@@ -327,6 +365,9 @@ def profile_run(dev):
     vs = synthetic.draw_torch(1, synthetic.TID_DV, (B, H, 16, M), 1.0, "f32", dev)
     for _ in range(2):
         ea.decode_steps(S, z, qs, ks, vs)
+    qs1 = synthetic.draw_torch(1, 9, (cfg["B"], cfg["H"], cfg["D"]), 0.125, "f32", dev)
+    for _ in range(2):
+        ea.softmax_scan(qs1, K, V)
     for name in ("prefill_bf16_b4h8_n3072_d64", "prefill_bf16_b1h16_n65536_d128"):
         c = dict(synthetic.WORKLOADS[name])
         Qb, Kb, Vb, ob = make_prefill_sets(c, 1, dev)[0]
@@ -449,6 +490,16 @@ def main():
             "tokens_per_s": round(ds["tokens_per_s"], 1), "us_per_call": round(ds["us_per_call"], 2),
             "bytes_per_call": ds["bytes_per_call"], "GBs": round(ds["GBs"], 1),
             "frac_hbm_peak": round(ds["GBs"] / HBM_PEAK_GBS, 4)}
+
+        log("softmax scan ...")
+        sm = bench_softmax_scan(cfg, max(10, args.steps // 4), dev)
+        log(f"softmax scan: {sm}")
+        line["softmax_scan"] = {
+            "workload": "softmax attention of one query per head over every prefix (RNN form), fp32, "
+                        "B=8 H=8 N=1024 D=M=64",
+            "tokens_per_s": round(sm["tokens_per_s"], 1), "kernel_us": round(sm["us_kernel"], 2),
+            "algorithmic_bytes": sm["bytes"], "GBs": round(sm["GBs"], 1),
+            "frac_hbm_peak": round(sm["GBs"] / HBM_PEAK_GBS, 4), "buffer_sets": sm["nsets"]}
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -10,8 +10,8 @@
 //   (m1, u1, w1) + (m2, u2, w2) = (m, u1 e^{m1-m} + u2 e^{m2-m}, w1 e^{m1-m} + w2 e^{m2-m}),
 //   m = max(m1, m2).
 //
-// Scan kernel: one wavefront per segment of R rows of one head (R = 64, or 32
-// when M = 128; lanes are value columns).  The wavefront
+// Scan kernel: one wavefront per segment of R = 32 rows of one head (lanes are
+// value columns).  The wavefront
 //   1. stages its K tile in LDS (coalesced) and forms s_i, one row per lane;
 //   2. runs the recurrence over its rows, keeping every row's local state
 //      (w_i in the register that held v_i; m_i, u_i in lane i);
@@ -19,6 +19,7 @@
 //      head (decoupled look-back, the same flag / epoch protocol as the prefill
 //      kernels; a state is only M + 2 floats) and publishes its inclusive state;
 //   4. writes out_i = prefix + local state of row i, normalised.
+// A one-thread kernel enqueued after the scan advances the epoch.
 // Workspace: 64 header words, one flag word per segment (padded to 64 words),
 // then the aggregate and the inclusive state of every segment (SP floats each).
 #include <math.h>
@@ -35,7 +36,7 @@ constexpr int kScanWaves = 4;
 
 template <int D, int M>
 struct ScanCfg {
-    static constexpr int R = M > 64 ? 32 : 64;  // rows per segment (one wavefront)
+    static constexpr int R = 32;                // rows per segment (one wavefront)
     static constexpr int CPL = M > 64 ? 2 : 1;  // value columns per lane
     static constexpr int LK = D + 4;            // LDS row of the K tile (floats)
     static constexpr int SP = scan_slot_floats(M);
@@ -152,20 +153,40 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         if (lane == 0) __hip_atomic_store(&flags[my], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    // prefix (pm, pu, pw) += the state in `slot`, in scan order (earlier segment first)
-    auto add_front = [&](const float *slot) {
-        const float sm = slot[M], su = slot[M + 1];
+    // prefix (pm, pu, pw) = prefix + state (sm, su, sw): the state comes after the prefix
+    auto add_back = [&](float sm, float su, const float *sw) {
         const float mn = fmaxf(sm, pm);
         if (mn != -INFINITY) {
-            const float a = __expf(sm - mn), b = __expf(pm - mn);
-            pu = su * a + pu * b;
+            const float a = __expf(pm - mn), b = __expf(sm - mn);
+            pu = pu * a + su * b;
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const int col = lane + 64 * c;
-                const float sv = col < M ? slot[col] : 0.0f;
-                pw[c] = sv * a + pw[c] * b;
-            }
+            for (int c = 0; c < CPL; ++c) pw[c] = pw[c] * a + sw[c] * b;
             pm = mn;
+        }
+    };
+    // load up to LB states at once (their latencies overlap), then combine in order
+    constexpr int LB = 16;
+    auto add_slots = [&](const float *first, int j0, int j1) {  // first, then agg of segments j0 .. j1-1
+        {
+            float sw[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) sw[c] = lane + 64 * c < M ? first[lane + 64 * c] : 0.0f;
+            add_back(first[M], first[M + 1], sw);
+        }
+        for (int jb = j0; jb < j1; jb += LB) {
+            float tm[LB], tu[LB], tw[LB][CPL];
+#pragma unroll
+            for (int k = 0; k < LB; ++k) {
+                const int j = jb + k < j1 ? jb + k : jb;
+                const float *slot = agg + ((size_t)j * BH + bh) * G::SP;
+                tm[k] = slot[M];
+                tu[k] = slot[M + 1];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) tw[k][c] = lane + 64 * c < M ? slot[lane + 64 * c] : 0.0f;
+            }
+#pragma unroll
+            for (int k = 0; k < LB; ++k)
+                if (jb + k < j1) add_back(tm[k], tu[k], tw[k]);
         }
     };
     if (NS > 1 && !last) {
@@ -204,9 +225,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         if (jstar < 0) {
             failed = true;
         } else {
-            // walk back from seg-1 to j*: each earlier state goes in front of the prefix
-            for (int j = seg - 1; j > jstar; --j) add_front(agg + ((size_t)j * BH + bh) * G::SP);
-            add_front((jstar == 0 ? agg : incl) + ((size_t)jstar * BH + bh) * G::SP);
+            add_slots((jstar == 0 ? agg : incl) + ((size_t)jstar * BH + bh) * G::SP, jstar + 1, seg);
         }
         if (!last) {
             // inclusive = prefix + local
@@ -250,15 +269,12 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         }
     }
 
-    // the last wavefront to finish resets the counter and advances the epoch
-    if (NS > 1 && lane == 0) {
-        const unsigned done = atomicAdd(&hdr[1], 1u);
-        if (done == (unsigned)items - 1u) {
-            __hip_atomic_store(&hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
+
+// Advances the epoch after a scan (enqueued behind it on the same stream): every
+// flag of the finished call becomes stale.  One thread instead of a
+// completion counter that thousands of wavefronts would update at once.
+static __global__ void scan_epoch_kernel(unsigned *hdr) { hdr[2] = hdr[2] + 1u; }
 
 // One token of the RNN for every head: one wavefront per head, lanes = value
 // columns; s = q . k reduced over the wavefront.
@@ -303,6 +319,7 @@ hipError_t run_scan(const void *q, const void *K, const void *V, float *out, voi
     const unsigned blocks = (unsigned)((items + kScanWaves - 1) / kScanWaves);
     hipLaunchKernelGGL((softmax_scan_kernel<T, D, M>), dim3(blocks), dim3(64 * kScanWaves), 0, stream, (const T *)q,
                        (const T *)K, (const T *)V, out, ws, BH, N, NS, m_out, u_out, w_out);
+    if (NS > 1) hipLaunchKernelGGL(scan_epoch_kernel, dim3(1), dim3(1), 0, stream, static_cast<unsigned *>(ws));
     return hipGetLastError();
 }
 
@@ -317,7 +334,7 @@ hipError_t run_step(float *m, float *u, float *w, const void *q, const void *k, 
 
 }  // namespace
 
-int softmax_scan_rows(int M) { return M > 64 ? 32 : 64; }
+int softmax_scan_rows(int) { return 32; }
 
 hipError_t softmax_scan(int dtype, int D, int M, const void *q, const void *K, const void *V, float *out, void *ws,
                         int BH, int N, float *m_out, float *u_out, float *w_out, hipStream_t stream) {
