@@ -223,7 +223,7 @@ struct Stage {
 
 // ---------------------------------------------------------------------------
 // Workspace of the fused kernel (fp32 words):
-//   header (64 words): [1] finished-workgroup counter, [2] epoch,
+//   header (64 words): [1] finished-head counter, [2] epoch,
 //                      [3] error flag (look-back gave up)
 //   flags  [BH][G] (uint32, padded to 64 words): epoch << 2 | 1 aggregate ready,
 //                                                epoch << 2 | 2 inclusive ready
@@ -917,13 +917,18 @@ __device__ __forceinline__ void publish_inclusive(const Engine<T, D, M, C> &e, c
     e.publish_flag(&ws.flags[my], ep | 2u);
 }
 
-// The last workgroup of a call to finish resets the finished-workgroup counter
-// and advances the epoch (every flag of the call becomes stale).
-__device__ __forceinline__ void finish_call(const FusedWs &ws, unsigned epoch, unsigned n_wg) {
+// Called by the last segment of every head once its look-back is done.  Every
+// segment of that head has then read the epoch (each published a flag tagged
+// with it, and a segment only publishes its inclusive state after its own
+// look-back), so when the last of the n_heads heads has counted, no workgroup of
+// the call will read the epoch again: that one resets the counter and advances
+// the epoch (every flag of the call becomes stale).  One atomic per head instead
+// of one per workgroup.
+__device__ __forceinline__ void finish_call(const FusedWs &ws, unsigned epoch, unsigned n_heads) {
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned done = atomicAdd(&ws.hdr[1], 1u);
-        if (done == n_wg - 1u) {
+        if (done == n_heads - 1u) {
             __hip_atomic_store(&ws.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&ws.hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -1043,7 +1048,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
     }
 
-    if (G_ > 1) finish_call(ws, epoch, (unsigned)(BH * G_));
+    if (G_ > 1 && last) finish_call(ws, epoch, (unsigned)BH);
 }
 
 // ---------------------------------------------------------------------------
@@ -1217,7 +1222,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
             e.store_rows(o[j], inv, Oh, (c0 + j) * C, N, failed);
         }
     }
-    if (G_ > 1) finish_call(ws, epoch, (unsigned)(BH * G_));
+    if (G_ > 1 && last) finish_call(ws, epoch, (unsigned)BH);
 }
 
 // ---------------------------------------------------------------------------

@@ -19,7 +19,8 @@
 //      head (decoupled look-back, the same flag / epoch protocol as the prefill
 //      kernels; a state is only M + 2 floats) and publishes its inclusive state;
 //   4. writes out_i = prefix + local state of row i, normalised.
-// A one-thread kernel enqueued after the scan advances the epoch.
+// The last segment of every head counts itself done after its look-back; the
+// last head to count advances the epoch (as in the prefill kernels).
 // Workspace: 64 header words, one flag word per segment (padded to 64 words),
 // then the aggregate and the inclusive state of every segment (SP floats each).
 #include <math.h>
@@ -238,6 +239,15 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
             publish(ep | 2u);
         }
     }
+    if (NS > 1 && last && lane == 0) {
+        // every segment of this head has read the epoch (see the prefill kernels'
+        // finish_call): count the head, and the last head advances the epoch
+        const unsigned done = atomicAdd(&hdr[1], 1u);
+        if (done == (unsigned)BH - 1u) {
+            __hip_atomic_store(&hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     if (last && m_out != nullptr) {
         const float mn = fmaxf(pm, m);
         const float a = mn == -INFINITY ? 0.0f : __expf(pm - mn), b = mn == -INFINITY ? 0.0f : __expf(m - mn);
@@ -270,11 +280,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
     }
 
 }
-
-// Advances the epoch after a scan (enqueued behind it on the same stream): every
-// flag of the finished call becomes stale.  One thread instead of a
-// completion counter that thousands of wavefronts would update at once.
-static __global__ void scan_epoch_kernel(unsigned *hdr) { hdr[2] = hdr[2] + 1u; }
 
 // One token of the RNN for every head: one wavefront per head, lanes = value
 // columns; s = q . k reduced over the wavefront.
@@ -319,7 +324,6 @@ hipError_t run_scan(const void *q, const void *K, const void *V, float *out, voi
     const unsigned blocks = (unsigned)((items + kScanWaves - 1) / kScanWaves);
     hipLaunchKernelGGL((softmax_scan_kernel<T, D, M>), dim3(blocks), dim3(64 * kScanWaves), 0, stream, (const T *)q,
                        (const T *)K, (const T *)V, out, ws, BH, N, NS, m_out, u_out, w_out);
-    if (NS > 1) hipLaunchKernelGGL(scan_epoch_kernel, dim3(1), dim3(1), 0, stream, static_cast<unsigned *>(ws));
     return hipGetLastError();
 }
 
