@@ -63,6 +63,9 @@ class Oracle:
         L.oracle_softmax_step.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int]
         L.oracle_causal_backward.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64,
                                              ctypes.c_int]
+        L.oracle_feature_map.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.oracle_attention_mapped.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                              ctypes.c_int]
         self.L = L
         self.path = path
 
@@ -189,6 +192,41 @@ class Oracle:
         return out
 
 
+    FEATURE_KINDS = {"elu": 0, "prf": 1, "trf": 2}
+
+    def feature_map(self, X, W, F: int, kind: str, normalize: bool = False, threads: int = 0) -> np.ndarray:
+        """Features of every row of X [..., D]: kind "elu" (F = D, W unused), "prf" (W [F, D])
+        or "trf" (W [F/2, D]); normalize scales each row to unit length first.  Returns [..., F]."""
+        X = _f64(X)
+        D = X.shape[-1]
+        rows = X.size // D if D else 0
+        k = self.FEATURE_KINDS[kind]
+        if k == 0:
+            assert F == D
+            W = np.zeros(1)
+        else:
+            W = _f64(W)
+            assert W.shape == ((F if k == 1 else F // 2), D)
+        out = np.empty((*X.shape[:-1], F))
+        self.L.oracle_feature_map(_p(X), _p(W), _p(out), rows, D, F, k, int(bool(normalize)), threads)
+        return out
+
+    def attention_mapped(self, Fq, Fk, V, causal: bool = True, threads: int = 0):
+        """Linear attention on mapped features Fq, Fk [..., N, F] (no feature map applied).
+        Returns (out [..., N, M], S [..., F, M], z [..., F]) with S, z the sums over all positions."""
+        Fq, Fk, V = _f64(Fq), _f64(Fk), _f64(V)
+        *lead, N, F = Fq.shape
+        M = V.shape[-1]
+        assert Fk.shape == Fq.shape and tuple(V.shape[:-1]) == tuple(Fq.shape[:-1])
+        BH = int(np.prod(lead)) if lead else 1
+        out = np.empty((*lead, N, M))
+        S = np.empty((*lead, F, M))
+        z = np.empty((*lead, F))
+        self.L.oracle_attention_mapped(_p(Fq), _p(Fk), _p(V), _p(out), _p(S), _p(z), BH, N, F, M, int(bool(causal)),
+                                       threads)
+        return out, S, z
+
+
 def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
 
@@ -247,3 +285,11 @@ def softmax_scan(q, K, V, threads: int = 0):
 
 def softmax_step(m, u, w, q, k, v, threads: int = 0):
     return default().softmax_step(m, u, w, q, k, v, threads)
+
+
+def feature_map(X, W, F: int, kind: str, normalize: bool = False, threads: int = 0):
+    return default().feature_map(X, W, F, kind, normalize, threads)
+
+
+def attention_mapped(Fq, Fk, V, causal: bool = True, threads: int = 0):
+    return default().attention_mapped(Fq, Fk, V, causal, threads)

@@ -371,3 +371,119 @@ void oracle_softmax_step(double *m, double *u, double *w, const double *q, const
         m[h] = mn;
     }
 }
+
+/* Random-feature maps with feature dimension F (page "Stable, Fast and Accurate:
+ * Kernelized Attention with Relative Positional Encoding", Proposed method and
+ * Main findings: kernelized attention with the feature maps PRF, TRF,
+ * Sphere-PRF and ORF, feature dimension as small as 16; normalised queries and
+ * keys for large norms).  The page gives no formula; these are the published
+ * random-feature estimators of the softmax kernel exp(q . k), whose expected
+ * dot product phi(q) . phi(k) over w ~ N(0, I) is exactly exp(q . k):
+ *   kind 0 (elu):  phi(x) = elu(x) + 1 elementwise, F = D, W unused;
+ *   kind 1 (PRF, positive):      phi_f(x) = exp(w_f . x - |x|^2 / 2) / sqrt(F),
+ *                                W [F][D];
+ *   kind 2 (TRF, trigonometric): with P = F / 2 projections W [P][D] and
+ *                                c(x) = exp(|x|^2 / 2) / sqrt(P):
+ *                                phi_p(x) = c sin(w_p . x), phi_{P+p}(x) = c cos(w_p . x).
+ * ORF and Sphere-PRF are PRF with a differently drawn W (orthogonal rows; rows on
+ * a sphere), which the caller passes in.  normalize != 0 first scales every row
+ * x to unit length (x = 0 stays 0).  X [rows][D]; out [rows][F]. */
+void oracle_feature_map(const double *X, const double *W, double *out, int64_t rows, int64_t D, int64_t F,
+                        int kind, int normalize, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t r = 0; r < rows; ++r) {
+        double *x = (double *)malloc((size_t)D * sizeof(double));
+        double sq = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            x[d] = X[r * D + d];
+            sq += x[d] * x[d];
+        }
+        if (normalize && sq > 0.0) {
+            const double len = sqrt(sq);
+            sq = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                x[d] /= len;
+                sq += x[d] * x[d];
+            }
+        }
+        double *o = out + r * F;
+        if (kind == 0) {
+            for (int64_t d = 0; d < D; ++d) o[d] = oracle_phi1(x[d]);
+        } else if (kind == 1) {
+            for (int64_t f = 0; f < F; ++f) {
+                double p = 0.0;
+                for (int64_t d = 0; d < D; ++d) p += W[f * D + d] * x[d];
+                o[f] = exp(p - 0.5 * sq) / sqrt((double)F);
+            }
+        } else {
+            const int64_t P = F / 2;
+            const double c = exp(0.5 * sq) / sqrt((double)P);
+            for (int64_t p = 0; p < P; ++p) {
+                double a = 0.0;
+                for (int64_t d = 0; d < D; ++d) a += W[p * D + d] * x[d];
+                o[p] = c * sin(a);
+                o[P + p] = c * cos(a);
+            }
+        }
+        free(x);
+    }
+}
+
+/* Linear attention on features that are already mapped (Fq = phi(Q), Fk = phi(K),
+ * [BH][N][F]): the running sums of the page "Transformers are RNNs" (Proposed
+ * method) with no feature map applied.  causal != 0: S_i, z_i over j <= i, read
+ * out with Fq_i after position i enters; causal == 0: the sums over all j, read
+ * out once per row.  S_out [BH][F][M], z_out [BH][F] (may be NULL): the sums over
+ * all N positions. */
+void oracle_attention_mapped(const double *Fq, const double *Fk, const double *V, double *out, double *S_out,
+                             double *z_out, int64_t BH, int64_t N, int64_t F, int64_t M, int causal,
+                             int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        double *S = (double *)calloc((size_t)(F * M), sizeof(double));
+        double *z = (double *)calloc((size_t)F, sizeof(double));
+        const double *Qh = Fq + h * N * F, *Kh = Fk + h * N * F, *Vh = V + h * N * M;
+        double *Oh = out + h * N * M;
+        if (causal) {
+            /* add position i, then read out row i */
+            for (int64_t i = 0; i < N; ++i) {
+                const double *f = Kh + i * F, *g = Qh + i * F, *v = Vh + i * M;
+                for (int64_t d = 0; d < F; ++d) {
+                    for (int64_t m = 0; m < M; ++m) S[d * M + m] += f[d] * v[m];
+                    z[d] += f[d];
+                }
+                double den = 0.0;
+                for (int64_t d = 0; d < F; ++d) den += g[d] * z[d];
+                for (int64_t m = 0; m < M; ++m) {
+                    double num = 0.0;
+                    for (int64_t d = 0; d < F; ++d) num += g[d] * S[d * M + m];
+                    Oh[i * M + m] = num / den;
+                }
+            }
+        } else {
+            /* add every position, then read out every row */
+            for (int64_t j = 0; j < N; ++j) {
+                const double *f = Kh + j * F, *v = Vh + j * M;
+                for (int64_t d = 0; d < F; ++d) {
+                    for (int64_t m = 0; m < M; ++m) S[d * M + m] += f[d] * v[m];
+                    z[d] += f[d];
+                }
+            }
+            for (int64_t i = 0; i < N; ++i) {
+                const double *g = Qh + i * F;
+                double den = 0.0;
+                for (int64_t d = 0; d < F; ++d) den += g[d] * z[d];
+                for (int64_t m = 0; m < M; ++m) {
+                    double num = 0.0;
+                    for (int64_t d = 0; d < F; ++d) num += g[d] * S[d * M + m];
+                    Oh[i * M + m] = num / den;
+                }
+            }
+        }
+        if (S_out) memcpy(S_out + h * F * M, S, (size_t)(F * M) * sizeof(double));
+        if (z_out) memcpy(z_out + h * F, z, (size_t)F * sizeof(double));
+        free(S); free(z);
+    }
+}

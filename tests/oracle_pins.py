@@ -396,8 +396,94 @@ def pin_softmax_scan(o, fails):
                 fails.append(f"softmax mpmath row {k} col {j}")
 
 
+def pin_features(o, fails):
+    """Random-feature maps (page "Stable, Fast and Accurate: Kernelized Attention with Relative
+    Positional Encoding": PRF, TRF and their variants) and linear attention on mapped features.
+
+    * unbiasedness: over w ~ N(0, I) the mean of phi(q) . phi(k) is exp(q . k) for PRF and TRF
+      (Monte Carlo with 2^17 features, bound from the sample variance);
+    * exact identities that hold for ANY W and are computed another way:
+      PRF  phi(x) . phi(y) = mean_f exp(w_f . (x + y) - (|x|^2 + |y|^2) / 2),
+      TRF  phi(x) . phi(y) = exp((|x|^2 + |y|^2) / 2) mean_p cos(w_p . (x - y)),
+      so  TRF phi(x) . phi(x) = exp(|x|^2);  W = 0 gives PRF exp(-(|x|^2+|y|^2)/2);
+    * normalisation: phi(c x) = phi(x) for c > 0, and equals phi(x / |x|) without it;
+    * the elu kind is phi (pinned above);
+    * attention on mapped features: the quadratic masked form in numpy (causal and not),
+      the final sums, the elu features reproduce the causal oracle, and with many PRF
+      features linear attention approaches softmax attention."""
+    rng = np.random.default_rng(71)
+    # unbiasedness
+    D = 3
+    q = np.array([0.3, -0.5, 0.2])
+    k = np.array([-0.1, 0.4, 0.6])
+    F = 1 << 17
+    W = rng.normal(size=(F, D))
+    want = np.exp(q @ k)
+    fq, fk = o.feature_map(q[None], W, F, "prf"), o.feature_map(k[None], W, F, "prf")
+    per = fq[0] * fk[0] * F  # one estimate per feature
+    if not abs(per.mean() - want) <= 6 * per.std() / np.sqrt(F):
+        fails.append(f"prf unbiased: {per.mean():.6f} vs {want:.6f}")
+    P = F // 2
+    Wt = W[:P]
+    fq, fk = o.feature_map(q[None], Wt, F, "trf"), o.feature_map(k[None], Wt, F, "trf")
+    per = (fq[0, :P] * fk[0, :P] + fq[0, P:] * fk[0, P:]) * P
+    if not abs(per.mean() - want) <= 6 * per.std() / np.sqrt(P):
+        fails.append(f"trf unbiased: {per.mean():.6f} vs {want:.6f}")
+    # exact identities for arbitrary W
+    for (D, F) in [(4, 8), (16, 16), (7, 32)]:
+        X = rng.normal(size=(5, D)) * 0.7
+        Y = rng.normal(size=(5, D)) * 0.7
+        W = rng.normal(size=(F, D))
+        fx, fy = o.feature_map(X, W, F, "prf"), o.feature_map(Y, W, F, "prf")
+        nx, ny = (X * X).sum(1), (Y * Y).sum(1)
+        want = np.exp((X + Y) @ W.T - 0.5 * (nx + ny)[:, None]).mean(axis=1)
+        _close(f"prf identity D{D} F{F}", (fx * fy).sum(1), want, 1e-12, fails)
+        if not np.all(fx > 0):
+            fails.append("prf features not positive")
+        f0 = o.feature_map(X, np.zeros((F, D)), F, "prf")
+        _close(f"prf W=0 D{D}", f0, np.repeat(np.exp(-0.5 * nx)[:, None] / np.sqrt(F), F, axis=1), 1e-13, fails)
+        Wt = W[:F // 2]
+        tx, ty = o.feature_map(X, Wt, F, "trf"), o.feature_map(Y, Wt, F, "trf")
+        want = np.exp(0.5 * (nx + ny)) * np.cos((X - Y) @ Wt.T).mean(axis=1)
+        _close(f"trf identity D{D} F{F}", (tx * ty).sum(1), want, 1e-11, fails)
+        _close(f"trf self D{D} F{F}", (tx * tx).sum(1), np.exp(nx), 1e-12, fails)
+        for kind, Wk in (("prf", W), ("trf", Wt)):
+            a = o.feature_map(X * 3.7, Wk, F, kind, normalize=True)
+            b = o.feature_map(X, Wk, F, kind, normalize=True)
+            c = o.feature_map(X / np.sqrt(nx)[:, None], Wk, F, kind)
+            _close(f"{kind} normalised scale D{D}", a, b, 1e-12, fails)
+            _close(f"{kind} normalised = unit rows D{D}", b, c, 1e-12, fails)
+        _close(f"elu kind D{D}", o.feature_map(X, None, D, "elu"), o.phi(X), 0.0, fails)
+    # attention on mapped features
+    for (N, F, M) in [(1, 4, 3), (9, 5, 2), (40, 16, 7)]:
+        Fq = np.abs(rng.normal(size=(2, N, F))) + 0.05
+        Fk = np.abs(rng.normal(size=(2, N, F))) + 0.05
+        V = rng.normal(size=(2, N, M))
+        out, S, z = o.attention_mapped(Fq, Fk, V, causal=True)
+        outn, Sn, zn = o.attention_mapped(Fq, Fk, V, causal=False)
+        for h in range(2):
+            A = Fq[h] @ Fk[h].T
+            L = np.tril(A)
+            _close(f"mapped causal N{N} F{F}", out[h], (L @ V[h]) / L.sum(1, keepdims=True), 1e-12, fails)
+            _close(f"mapped non-causal N{N} F{F}", outn[h], (A @ V[h]) / A.sum(1, keepdims=True), 1e-12, fails)
+            for nm, SS, zz in (("causal", S, z), ("non-causal", Sn, zn)):
+                _close(f"mapped {nm} S N{N}", SS[h], Fk[h].T @ V[h], 1e-12, fails)
+                _close(f"mapped {nm} z N{N}", zz[h], Fk[h].sum(0), 1e-12, fails)
+    Q, K, V = rng.normal(size=(2, 30, 6)), rng.normal(size=(2, 30, 6)), rng.normal(size=(2, 30, 4))
+    _close("mapped elu = causal", o.attention_mapped(o.phi(Q), o.phi(K), V)[0], o.causal(Q, K, V)[0], 1e-12, fails)
+    # many PRF features: linear attention approaches softmax attention
+    N, D, M, F = 6, 4, 3, 1 << 16
+    Q, K, V = rng.normal(size=(N, D)) * 0.4, rng.normal(size=(N, D)) * 0.4, rng.normal(size=(N, M))
+    W = rng.normal(size=(F, D))
+    got = o.attention_mapped(o.feature_map(Q, W, F, "prf")[None], o.feature_map(K, W, F, "prf")[None], V[None])[0][0]
+    E = np.tril(np.exp(Q @ K.T))
+    soft = (E @ V) / E.sum(1, keepdims=True)
+    if not np.max(np.abs(got - soft)) <= 2e-2 * np.max(np.abs(soft)):
+        fails.append(f"prf attention vs softmax: {np.max(np.abs(got - soft)):.3e}")
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked, pin_continue,
-            pin_backward, pin_softmax_scan]
+            pin_backward, pin_softmax_scan, pin_features]
 
 
 def run_all(o, pins=ALL_PINS):

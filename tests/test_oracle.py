@@ -53,6 +53,19 @@ MUTANTS = {
                             "memset(S, 0, (size_t)(D * M) * sizeof(double));"),
     "continue_transposed_update": ("for (int64_t m = 0; m < M; ++m) S[d * M + m] += f * v[m];",
                                    "for (int64_t m = 0; m < M; ++m) S[m * D + d] += f * v[m];"),
+    "prf_norm_sign": ("o[f] = exp(p - 0.5 * sq) / sqrt((double)F);", "o[f] = exp(p + 0.5 * sq) / sqrt((double)F);"),
+    "prf_no_scale": ("o[f] = exp(p - 0.5 * sq) / sqrt((double)F);", "o[f] = exp(p - 0.5 * sq);"),
+    "trf_cos_as_sin": ("o[P + p] = c * cos(a);", "o[P + p] = c * sin(a);"),
+    "trf_no_magnitude": ("const double c = exp(0.5 * sq) / sqrt((double)P);", "const double c = 1.0 / sqrt((double)P);"),
+    "normalize_ignored": ("if (normalize && sq > 0.0) {", "if (0 && normalize && sq > 0.0) {"),
+    "normalize_keeps_old_norm": ("            sq = 0.0;\n            for (int64_t d = 0; d < D; ++d) {\n                x[d] /= len;",
+                                 "            for (int64_t d = 0; d < D; ++d) {\n                x[d] /= len;"),
+    "mapped_causal_as_noncausal": ("        if (causal) {\n            /* add position i, then read out row i */",
+                                   "        if (0) {\n            /* add position i, then read out row i */"),
+    "mapped_den_uses_k": ("for (int64_t d = 0; d < F; ++d) den += g[d] * z[d];",
+                          "for (int64_t d = 0; d < F; ++d) den += f[d] * z[d];"),
+    "mapped_noncausal_sums_q": ("const double *f = Kh + j * F, *v = Vh + j * M;",
+                                "const double *f = Qh + j * F, *v = Vh + j * M;"),
     "decode_den_uses_k": ("den += oracle_phi1(qh[d]) * zh[d];", "den += oracle_phi1(kh[d]) * zh[d];"),
     "decode_reads_before_update": (
         "        for (int64_t d = 0; d < D; ++d) {\n            double f = oracle_phi1(kh[d]);\n            for (int64_t m = 0; m < M; ++m) Sh[d * M + m] += f * vh[m];\n            zh[d] += f;\n        }\n        double den = 0.0;\n        for (int64_t d = 0; d < D; ++d) den += oracle_phi1(qh[d]) * zh[d];\n        for (int64_t m = 0; m < M; ++m) {\n            double num = 0.0;\n            for (int64_t d = 0; d < D; ++d) num += oracle_phi1(qh[d]) * Sh[d * M + m];\n            oh[m] = num / den;\n        }\n",
