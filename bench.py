@@ -303,6 +303,57 @@ def bench_softmax_scan(cfg, steps, dev):
                 GBs=nbytes / (us * 1e-6) / 1e9)
 
 
+def bench_features(cfg, steps, dev):
+    """Random features (16 positive random features, orthogonal projection) then causal
+    linear attention on them, on the headline shape: one la_feature_map launch (Q and K)
+    and one prefill launch per step, inputs rotated past the last-level cache.  Each
+    launch is bracketed by its own events."""
+    import torch
+    import efficient_transformer_amd as ea
+    import synthetic
+
+    B, H, N, D, M, F = (cfg[k] for k in ("B", "H", "N", "D", "M", "F"))
+    map_bytes = B * H * N * (2 * D * 4 + 2 * F * 4)
+    attn_bytes = B * H * N * ((2 * F + M) * 4 + 4 * M)
+    nsets = max(1, math.ceil(1.25 * LLC_BYTES / (map_bytes + attn_bytes)))
+    W = torch.from_numpy(ea.draw_projection(F, D, "orthogonal", 0)).to(dev)
+    sets = []
+    for i in range(nsets):
+        Xq = synthetic.draw_torch(30 + i, synthetic.TID_Q, (B, H, N, D), cfg["sigma"], "f32", dev)
+        Xk = synthetic.draw_torch(30 + i, synthetic.TID_K, (B, H, N, D), cfg["sigma"], "f32", dev)
+        V = synthetic.draw_torch(30 + i, synthetic.TID_V, (B, H, N, M), 1.0, "f32", dev)
+        fq = torch.empty((B, H, N, F), device=dev)
+        fk = torch.empty((B, H, N, F), device=dev)
+        sets.append((Xq, Xk, V, fq, fk, torch.empty((B, H, N, M), device=dev)))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        Xq, Xk, V, fq, fk, o = sets[i % nsets]
+        if ev:
+            ev[0].record(stream)
+        ea.feature_map(Xq, W, F, cfg["feature"], out=fq, X2=Xk, out2=fk, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        ea.forward_chunked(fq, fk, V, causal=True, out=o, stream=stream, features=True)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(5):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    us_map = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e3
+    us_attn = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e3
+    us_step = sum(e[0].elapsed_time(e[2]) for e in evs) / steps * 1e3
+    del sets
+    torch.cuda.empty_cache()
+    return dict(us_step=us_step, us_map=us_map, us_attn=us_attn, map_bytes=map_bytes, attn_bytes=attn_bytes,
+                tokens_per_s=B * N / (us_step * 1e-6), nsets=nsets)
+
+
 def causal_kernel_name(cfg, chunk, segments) -> str:
     n_chunks = -(-cfg["N"] // chunk)
     cps = -(-n_chunks // segments)
@@ -337,7 +388,8 @@ def cpu_baseline(cfg, target_s=12.0):
 
 def profile_run(dev):
     """Untimed launches for counter collection: 4 headline prefill calls, 4 decode steps,
-    2 backward calls, 2 multi-token decode calls, 2 softmax scans, 2 calls of each bf16 prefill workload and
+    2 backward calls, 2 multi-token decode calls, 2 softmax scans, 2 random-feature maps and prefills
+    on them, 2 calls of each bf16 prefill workload and
     4 copies of a 512 MiB fp32 buffer (known traffic: 512 MiB read + 512 MiB written each)."""
     import torch
     import efficient_transformer_amd as ea
@@ -368,6 +420,11 @@ def profile_run(dev):
     qs1 = synthetic.draw_torch(1, 9, (cfg["B"], cfg["H"], cfg["D"]), 0.125, "f32", dev)
     for _ in range(2):
         ea.softmax_scan(qs1, K, V)
+    fc = dict(synthetic.WORKLOADS["prefill_prf16_f32_b8h8_n1024_d64"])
+    Wf = torch.from_numpy(ea.draw_projection(fc["F"], fc["D"], "orthogonal", 0)).to(dev)
+    for _ in range(2):
+        fq, fk = ea.feature_map(Q, Wf, fc["F"], "prf", X2=K)
+        ea.forward_chunked(fq, fk, V, causal=True, features=True)
     for name in ("prefill_bf16_b4h8_n3072_d64", "prefill_bf16_b1h16_n65536_d128"):
         c = dict(synthetic.WORKLOADS[name])
         Qb, Kb, Vb, ob = make_prefill_sets(c, 1, dev)[0]
@@ -500,6 +557,20 @@ def main():
             "tokens_per_s": round(sm["tokens_per_s"], 1), "kernel_us": round(sm["us_kernel"], 2),
             "algorithmic_bytes": sm["bytes"], "GBs": round(sm["GBs"], 1),
             "frac_hbm_peak": round(sm["GBs"] / HBM_PEAK_GBS, 4), "buffer_sets": sm["nsets"]}
+
+        log("random features ...")
+        fcfg = dict(synthetic.WORKLOADS["prefill_prf16_f32_b8h8_n1024_d64"])
+        fe = bench_features(fcfg, max(10, args.steps // 4), dev)
+        log(f"features: {fe}")
+        line["features"] = {
+            "workload": "16 positive random features (orthogonal projection) of q, k, then causal linear "
+                        "attention on them, fp32, B=8 H=8 N=1024 D=M=64",
+            "tokens_per_s": round(fe["tokens_per_s"], 1), "us_per_step": round(fe["us_step"], 2),
+            "feature_map_us": round(fe["us_map"], 2), "attention_us": round(fe["us_attn"], 2),
+            "feature_map_GBs": round(fe["map_bytes"] / (fe["us_map"] * 1e-6) / 1e9, 1),
+            "attention_GBs": round(fe["attn_bytes"] / (fe["us_attn"] * 1e-6) / 1e9, 1),
+            "feature_map_bytes": fe["map_bytes"], "attention_bytes": fe["attn_bytes"],
+            "buffer_sets": fe["nsets"]}
 
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

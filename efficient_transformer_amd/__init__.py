@@ -4,11 +4,13 @@ The computation runs in hand-written HIP kernels for gfx950 behind the C ABI of
 liblinattn.so (include/linattn.h).  This package is the thin Python binding:
 argument marshalling only; PyTorch supplies device memory and streams.
 """
+from .features import draw_projection  # noqa: F401
 from .linattn import (  # noqa: F401
     LinAttnError,
     backward,
     decode_step,
     decode_steps,
+    feature_map,
     forward_chunked,
     forward_continue,
     forward_fused,

@@ -24,7 +24,7 @@ struct Plan {
 // Validate the shape arguments shared by the prefill entry points.
 int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype) {
     if (B < 0 || H < 0 || N < 0 || D <= 0 || M <= 0) return LA_ERR_INVALID_ARG;
-    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
     // index arithmetic uses int for counts and size_t for element offsets
     if (N > INT_MAX || B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
@@ -49,7 +49,7 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
     if (chunk_req == 0) {
         // fp32 operands with a small state run 32-position chunks (less masked
         // quadratic work per position on the slower fp32 MFMA); otherwise 64
-        C = (dtype == LA_F32 && D * M <= 4096) ? 32 : 64;
+        C = (dtype != LA_BF16 && D * M <= 4096) ? 32 : 64;
         if (!la::prefill_supported(dtype, (int)D, (int)M, C)) C = 32;
         if (!la::prefill_supported(dtype, (int)D, (int)M, C)) C = 16;
     } else if (chunk_req == 16 || chunk_req == 32 || chunk_req == 64) {
@@ -374,7 +374,7 @@ LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, float
 LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, const void *v, float *out, int64_t B,
                           int64_t H, int64_t D, int64_t M, int dtype, void *stream) {
     if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
-    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
     if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
     if (B * H == 0) return LA_OK;
@@ -393,6 +393,8 @@ struct BwdPlan {
     size_t states_bytes = 0, den_bytes = 0, ws_bytes = 0;
 };
 int bwd_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype, BwdPlan *p) {
+    // the gradient is taken through phi = elu + 1; features computed elsewhere are not covered
+    if (dtype == LA_F32_FEATURES) return LA_ERR_UNSUPPORTED;
     int st = check_shape(B, H, N, D, M, dtype);
     if (st != LA_OK) return st;
     const int64_t BH = B * H;
@@ -513,7 +515,7 @@ LA_API int la_softmax_step(float *m, float *u, float *w, const void *q, const vo
 LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, const void *v, float *out, int64_t B,
                            int64_t H, int64_t T, int64_t D, int64_t M, int dtype, void *stream) {
     if (B < 0 || H < 0 || T < 0) return LA_ERR_INVALID_ARG;
-    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
     if (B * H > INT_MAX || T > INT_MAX) return LA_ERR_UNSUPPORTED;
     if (B * H > 0 && T > INT64_MAX / (B * H * (D > M ? D : M))) return LA_ERR_UNSUPPORTED;
@@ -524,6 +526,27 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
     (void)hipGetLastError();
     return hip_status(la::decode_steps(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), (int)T,
                                        as_stream(stream)));
+}
+
+// ---- feature maps ----------------------------------------------------------
+
+LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2, int64_t rows, int64_t D,
+                          int dtype, const float *W, int64_t F, int kind, int flags, void *stream) {
+    if (rows < 0 || D <= 0 || F <= 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (kind != LA_FEATURE_ELU && kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
+    if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
+    if (kind == LA_FEATURE_ELU && F != D) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(F)) return LA_ERR_UNSUPPORTED;
+    if (rows > INT64_MAX / 256) return LA_ERR_UNSUPPORTED;
+    if ((rows + 63) / 64 > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if ((X2 == nullptr) != (out2 == nullptr)) return LA_ERR_INVALID_ARG;
+    if (rows == 0) return LA_OK;
+    if (!out || !X || (kind != LA_FEATURE_ELU && !W)) return LA_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned16(X) || (X2 && (!aligned16(X2) || !aligned16(out2)))) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::feature_map(dtype, (int)D, (int)F, kind, X, out, X2, out2, W, (long)rows,
+                                      (flags & LA_FEATURE_NORMALIZE) != 0, as_stream(stream)));
 }
 
 }  // extern "C"

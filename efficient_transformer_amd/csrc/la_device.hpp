@@ -33,6 +33,12 @@ using bf16 = __bf16;
 // phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (page "Transformers are
 // RNNs", Main findings: elu-based feature map).  Branch free (a select).
 __device__ __forceinline__ float phi(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+// phi when P, else the identity (the input already holds features).
+template <bool P>
+__device__ __forceinline__ float phi_if(float x) {
+    if constexpr (P) return phi(x);
+    else return x;
+}
 
 template <typename T> __device__ __forceinline__ float to_f32(T x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }

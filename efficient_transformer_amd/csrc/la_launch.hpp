@@ -7,6 +7,10 @@
 
 namespace la {
 
+// Element types of the inputs: fp32, bf16, or fp32 rows that already hold the
+// features phi(q), phi(k) (the kernels then apply no feature map).
+constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeF32Features = 2;
+
 // Workspace layout of the fused causal kernel (shared by host sizing and device code):
 // header words, then one flag word per segment (padded to 64 words), then the
 // aggregate and the inclusive state of every segment (E floats each).
@@ -32,7 +36,7 @@ hipError_t softmax_scan(int dtype, int D, int M, const void *q, const void *K, c
 hipError_t softmax_step(int dtype, int D, int M, float *m, float *u, float *w, const void *q, const void *k,
                         const void *v, float *out, int BH, hipStream_t stream);
 
-// Prefill stage launchers for one element type (0 = fp32, 1 = bf16).
+// Prefill stage launchers for one element type (kDtype*).
 // Each returns hipErrorInvalidValue for a (D, M, C) combination that has no kernel.
 bool prefill_supported(int dtype, int D, int M, int C);
 hipError_t prefill_states(int dtype, int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N,
@@ -66,6 +70,27 @@ hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *
                        float *out, int BH, hipStream_t stream);
 hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
                         float *out, int BH, int Tn, hipStream_t stream);
+
+// Random-feature map (la_features.hip): kind 0 elu (F = D), 1 positive, 2
+// trigonometric; X2 / out2 optional (a second tensor in the same launch).
+hipError_t feature_map(int dtype, int D, int F, int kind, const void *X, float *out, const void *X2, float *out2,
+                       const float *W, long rows, bool norm, hipStream_t stream);
+
+// feature inputs (la_feat_prefill.hip, la_feat_onepass.hip)
+bool prefill_supported_feat(int D, int M, int C);
+size_t prefill_lds_bytes_feat(int D, int M, int C);
+bool prefill_onepass_supported_feat(int D, int M, int C);
+hipError_t prefill_states_feat(int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N, int G,
+                               int CPS, int nstates, hipStream_t stream);
+hipError_t prefill_fused_feat(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,
+                              int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
+                              const float *z_in, hipStream_t stream);
+hipError_t prefill_outputs_feat(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                                const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out,
+                                float *z_out, hipStream_t stream);
+hipError_t prefill_onepass_feat(int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+                                void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out,
+                                const float *S_in, const float *z_in, hipStream_t stream);
 
 // per element type (defined in la_prefill_f32.hip / la_prefill_bf16.hip)
 hipError_t prefill_fused_f32(int D, int M, int C, const void *Q, const void *K, const void *V, float *out, void *ws,

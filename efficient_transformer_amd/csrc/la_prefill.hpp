@@ -250,7 +250,9 @@ struct FusedWs {
 // ---------------------------------------------------------------------------
 // The per-chunk engine shared by the kernels.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C>
+// PHI: apply the feature map phi while staging Q and K (false: the inputs already
+// hold features, e.g. random features computed by the feature-map kernel).
+template <typename T, int D, int M, int C, bool PHI = true>
 struct Engine {
     using G = Cfg<T, D, M, C>;
     static constexpr int DT = G::DT, MTW = G::MTW, RT = G::RT;
@@ -286,15 +288,15 @@ struct Engine {
     }
 
     __device__ __forceinline__ void store_q(const Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &st, int row0, int N) const {
-        st.template store_natural<true>(sQ, G::LQ, row0, N, tid);
+        st.template store_natural<PHI>(sQ, G::LQ, row0, N, tid);
     }
     __device__ __forceinline__ void store_kv(const Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &stK, const Stage<T, C, M, Cfg<T, D, M, C>::THREADS> &stV, int row0,
                                              int N) const {
         if constexpr (G::F32) {
-            stK.template store_natural<true>(sK, G::LQ, row0, N, tid);
+            stK.template store_natural<PHI>(sK, G::LQ, row0, N, tid);
             stV.template store_natural<false>(sV, G::LV, row0, N, tid);
         } else {
-            stK.template store_transposed<true, true>(sKt, G::LT, sK, G::LQ, row0, N, tid);
+            stK.template store_transposed<PHI, true>(sKt, G::LT, sK, G::LQ, row0, N, tid);
             stV.template store_transposed<false, false>(sV, G::LT, nullptr, 0, row0, N, tid);
         }
     }
@@ -767,8 +769,8 @@ struct KVBuf {
     }
 };
 
-template <typename T, int D, int M, int C>
-__device__ __forceinline__ void phase_a(const Engine<T, D, M, C> &e, const T *__restrict__ Kh,
+template <typename T, int D, int M, int C, bool PHI>
+__device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const T *__restrict__ Kh,
                                         const T *__restrict__ Vh, int N, int c0, int c1,
                                         f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z) {
     // One chunk of loads in flight: chunk c+1 is requested right after chunk c is
@@ -796,8 +798,8 @@ __device__ __forceinline__ void phase_a(const Engine<T, D, M, C> &e, const T *__
 // advance the state over the last chunk (for the final state).  Loads run one
 // chunk ahead.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, bool CAUSAL>
-__device__ __forceinline__ void phase_b(const Engine<T, D, M, C> &e, const T *__restrict__ Qh,
+template <typename T, int D, int M, int C, bool CAUSAL, bool PHI>
+__device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const T *__restrict__ Qh,
                                         const T *__restrict__ Kh, const T *__restrict__ Vh,
                                         float *__restrict__ Oh, int N, int c0, int c1, bool kv_staged,
                                         bool advance_last, Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q0,
@@ -849,8 +851,8 @@ constexpr long kSpinLimit = 1L << 22;
 // ready; the prefix is then incl(j*) + agg(j*+1) + ... + agg(s-1), added into
 // pre / zpre.  Waits are bounded (kSpinLimit polls); on a timeout the error
 // word of the workspace is set and false is returned.
-template <typename T, int D, int M, int C>
-__device__ __forceinline__ bool look_back(const Engine<T, D, M, C> &e, const FusedWs &ws, unsigned *sh_word, int bh,
+template <typename T, int D, int M, int C, bool PHI>
+__device__ __forceinline__ bool look_back(const Engine<T, D, M, C, PHI> &e, const FusedWs &ws, unsigned *sh_word, int bh,
                                           int s, int G_, unsigned ep,
                                           f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &zpre) {
     using Gc = Cfg<T, D, M, C>;
@@ -896,8 +898,8 @@ __device__ __forceinline__ bool look_back(const Engine<T, D, M, C> &e, const Fus
 }
 
 // Publish the inclusive prefix pre + acc of segment `my` (NaN after a failed look-back).
-template <typename T, int D, int M, int C>
-__device__ __forceinline__ void publish_inclusive(const Engine<T, D, M, C> &e, const FusedWs &ws, size_t my,
+template <typename T, int D, int M, int C, bool PHI>
+__device__ __forceinline__ void publish_inclusive(const Engine<T, D, M, C, PHI> &e, const FusedWs &ws, size_t my,
                                                   unsigned ep,
                                                   const f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW],
                                                   float zpre,
@@ -935,14 +937,14 @@ __device__ __forceinline__ void finish_call(const FusedWs &ws, unsigned epoch, u
     }
 }
 
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, bool PHI = true>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                                 const T *__restrict__ V, float *__restrict__ out,
                                                                 void *ws_raw, int BH, int N, int G_, int CPS,
                                                                 float *__restrict__ S_out, float *__restrict__ z_out,
                                                                 const float *S_in, const float *z_in) {
     using Gc = Cfg<T, D, M, C>;
-    using En = Engine<T, D, M, C>;
+    using En = Engine<T, D, M, C, PHI>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
     __shared__ unsigned sh_word[2];
     En e(smem);
@@ -978,7 +980,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const bool last = s == G_ - 1;
     const bool want_final = S_out != nullptr;
     const bool run_a = G_ > 1 && (!last || want_final);
-    if (run_a) phase_a<T, D, M, C>(e, Kh, Vh, N, c0, c1, acc, zacc);
+    if (run_a) phase_a(e, Kh, Vh, N, c0, c1, acc, zacc);
     const size_t my = (size_t)bh * G_ + s;
     // Prefix of the segment: the carried initial state (segment 0, when given),
     // later the look-back's sum of the earlier segments.
@@ -1022,8 +1024,8 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 
     bool failed = false;
     if (G_ > 1 && s > 0) {
-        failed = !look_back<T, D, M, C>(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
-        if (!last) publish_inclusive<T, D, M, C>(e, ws, (size_t)bh * G_ + s, ep, pre, zpre, acc, zacc, failed);
+        failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
+        if (!last) publish_inclusive(e, ws, (size_t)bh * G_ + s, ep, pre, zpre, acc, zacc, failed);
     }
     if (G_ > 1 && last && want_final) {
         f32x4 fin[Gc::DT][Gc::MTW];
@@ -1043,7 +1045,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         const float inv = e.template row_inv<true>();
         e.readout(o, pre, inv, Oh, c0 * C, N, failed);
     } else {
-        phase_b<T, D, M, C, true>(e, Qh, Kh, Vh, Oh, N, c0, c1, false, G_ == 1 && want_final, stQ, pre, zpre,
+        phase_b<T, D, M, C, true, PHI>(e, Qh, Kh, Vh, Oh, N, c0, c1, false, G_ == 1 && want_final, stQ, pre, zpre,
                                   failed);
         if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
     }
@@ -1080,14 +1082,14 @@ struct OnePassLds {
     static constexpr bool fits = (bytes + 64) * Gc::MIN_WG <= kMaxLds;
 };
 
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, bool PHI = true>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void onepass_causal_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, float *__restrict__ out,
     void *ws_raw, int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out,
     const float *S_in, const float *z_in) {
     using Gc = Cfg<T, D, M, C>;
     using L1 = OnePassLds<T, D, M, C>;
-    using En = Engine<T, D, M, C>;
+    using En = Engine<T, D, M, C, PHI>;
     constexpr int NC = kOnePassChunks;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L1::bytes];
     __shared__ unsigned sh_word[2];
@@ -1188,8 +1190,8 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     bool failed = false;
     const bool has_prefix = (G_ > 1 && s > 0) || init;
     if (G_ > 1 && s > 0) {
-        failed = !look_back<T, D, M, C>(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
-        if (!last) publish_inclusive<T, D, M, C>(e, ws, my, ep, pre, zpre, S, z, failed);
+        failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
+        if (!last) publish_inclusive(e, ws, my, ep, pre, zpre, S, z, failed);
     }
     if (last && want_final) {
         f32x4 fin[Gc::DT][Gc::MTW];
@@ -1230,31 +1232,31 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 // Stage workspace: [BH][G + 1][E]; slot s = state of segment s, later its
 // exclusive prefix; slot G = total.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, bool PHI = true>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS)) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
                                                              float *__restrict__ ws, int N, int G_, int CPS,
                                                              int nstates) {
     using Gc = Cfg<T, D, M, C>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
-    Engine<T, D, M, C> e(smem);
+    Engine<T, D, M, C, PHI> e(smem);
     const int bh = blockIdx.x / nstates, s = blockIdx.x % nstates;
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
     f32x4 acc[Gc::DT][Gc::MTW];
     Engine<T, D, M, C>::zero_state(acc);
     float z = 0.0f;
-    phase_a<T, D, M, C>(e, K + (size_t)bh * N * D, V + (size_t)bh * N * M, N, c0, c1, acc, z);
+    phase_a(e, K + (size_t)bh * N * D, V + (size_t)bh * N * M, N, c0, c1, acc, z);
     e.state_store(acc, z, ws + ((size_t)bh * (G_ + 1) + s) * Gc::E);
 }
 
-template <typename T, int D, int M, int C, bool CAUSAL>
+template <typename T, int D, int M, int C, bool CAUSAL, bool PHI = true>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                               const T *__restrict__ V, float *__restrict__ out,
                                                               const float *__restrict__ ws, int N, int G_, int CPS,
                                                               float *__restrict__ S_out, float *__restrict__ z_out) {
     using Gc = Cfg<T, D, M, C>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
-    Engine<T, D, M, C> e(smem);
+    Engine<T, D, M, C, PHI> e(smem);
     const int bh = blockIdx.x / G_, s = blockIdx.x % G_;
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
@@ -1271,7 +1273,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     Stage<T, C, D, Cfg<T, D, M, C>::THREADS> stQ;
     stQ.load(Qh, c0 * C, N, e.tid);
     const bool fin = CAUSAL && S_out != nullptr && s == G_ - 1;
-    phase_b<T, D, M, C, CAUSAL>(e, Qh, K + (size_t)bh * N * D, V + (size_t)bh * N * M, out + (size_t)bh * N * M, N,
+    phase_b<T, D, M, C, CAUSAL, PHI>(e, Qh, K + (size_t)bh * N * D, V + (size_t)bh * N * M, out + (size_t)bh * N * M, N,
                                 c0, c1, false, fin, stQ, S, z, false);
     if (fin) e.state_store(S, z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
 }
@@ -1279,7 +1281,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 // ---------------------------------------------------------------------------
 // Host-side launchers (instantiated per element type in la_prefill_*.hip).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, bool PHI = true>
 hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
                      int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
@@ -1288,13 +1290,13 @@ hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, vo
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
-        hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
+        hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C, PHI>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
                            (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out, S_in, z_in);
         return hipGetLastError();
     }
 }
 
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, bool PHI = true>
 hipError_t run_onepass(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
                        int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
                        hipStream_t stream) {
@@ -1304,14 +1306,14 @@ hipError_t run_onepass(const void *Q, const void *K, const void *V, float *out, 
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((onepass_causal_kernel<T, D, M, C>), dim3((unsigned)(BH * G_)), dim3(Gc::THREADS), 0,
+        hipLaunchKernelGGL((onepass_causal_kernel<T, D, M, C, PHI>), dim3((unsigned)(BH * G_)), dim3(Gc::THREADS), 0,
                            stream, (const T *)Q, (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out,
                            S_in, z_in);
         return hipGetLastError();
     }
 }
 
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, bool PHI = true>
 hipError_t run_states(const void *K, const void *V, float *ws, int BH, int N, int G_, int CPS, int nstates,
                       hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
@@ -1319,13 +1321,13 @@ hipError_t run_states(const void *K, const void *V, float *ws, int BH, int N, in
         return hipErrorInvalidValue;
     } else {
         if (nstates <= 0 || BH <= 0) return hipSuccess;
-        hipLaunchKernelGGL((seg_state_kernel<T, D, M, C>), dim3((unsigned)(BH * nstates)), dim3(Gc::THREADS), 0, stream,
+        hipLaunchKernelGGL((seg_state_kernel<T, D, M, C, PHI>), dim3((unsigned)(BH * nstates)), dim3(Gc::THREADS), 0, stream,
                            (const T *)K, (const T *)V, ws, N, G_, CPS, nstates);
         return hipGetLastError();
     }
 }
 
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, bool PHI = true>
 hipError_t run_outputs(const void *Q, const void *K, const void *V, float *out, const float *ws, int BH, int N,
                        int G_, int CPS, int causal, float *S_out, float *z_out, hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
@@ -1335,10 +1337,10 @@ hipError_t run_outputs(const void *Q, const void *K, const void *V, float *out, 
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const dim3 grid((unsigned)(BH * G_)), block(Gc::THREADS);
         if (causal)
-            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, true>), grid, block, 0, stream, (const T *)Q,
+            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, true, PHI>), grid, block, 0, stream, (const T *)Q,
                                (const T *)K, (const T *)V, out, ws, N, G_, CPS, S_out, z_out);
         else
-            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, false>), grid, block, 0, stream, (const T *)Q,
+            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, false, PHI>), grid, block, 0, stream, (const T *)Q,
                                (const T *)K, (const T *)V, out, ws, N, G_, CPS, S_out, z_out);
         return hipGetLastError();
     }

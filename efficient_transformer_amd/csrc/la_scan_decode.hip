@@ -60,40 +60,50 @@ hipError_t fill_zero(float *p, size_t n, hipStream_t stream) {
 hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
                          void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
                          const float *z_in, hipStream_t stream) {
-    return dtype == 0 ? prefill_fused_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
-                      : prefill_fused_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
+    return dtype == kDtypeF32    ? prefill_fused_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+           : dtype == kDtypeBf16 ? prefill_fused_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+                                 : prefill_fused_feat(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
 }
 
 hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
                            void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
                          const float *z_in, hipStream_t stream) {
-    return dtype == 0 ? prefill_onepass_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
-                      : prefill_onepass_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
+    return dtype == kDtypeF32    ? prefill_onepass_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+           : dtype == kDtypeBf16 ? prefill_onepass_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+                                 : prefill_onepass_feat(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
 }
 
 bool prefill_onepass_supported(int dtype, int D, int M, int C) {
-    return dtype == 0 ? prefill_onepass_supported_f32(D, M, C) : prefill_onepass_supported_bf16(D, M, C);
+    return dtype == kDtypeF32    ? prefill_onepass_supported_f32(D, M, C)
+           : dtype == kDtypeBf16 ? prefill_onepass_supported_bf16(D, M, C)
+                                 : prefill_onepass_supported_feat(D, M, C);
 }
 
 size_t prefill_lds_bytes(int dtype, int D, int M, int C) {
-    return dtype == 0 ? prefill_lds_bytes_f32(D, M, C) : prefill_lds_bytes_bf16(D, M, C);
+    return dtype == kDtypeF32    ? prefill_lds_bytes_f32(D, M, C)
+           : dtype == kDtypeBf16 ? prefill_lds_bytes_bf16(D, M, C)
+                                 : prefill_lds_bytes_feat(D, M, C);
 }
 
 bool prefill_supported(int dtype, int D, int M, int C) {
-    return dtype == 0 ? prefill_supported_f32(D, M, C) : prefill_supported_bf16(D, M, C);
+    return dtype == kDtypeF32    ? prefill_supported_f32(D, M, C)
+           : dtype == kDtypeBf16 ? prefill_supported_bf16(D, M, C)
+                                 : prefill_supported_feat(D, M, C);
 }
 
 hipError_t prefill_states(int dtype, int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N,
                           int G, int CPS, int nstates, hipStream_t stream) {
-    return dtype == 0 ? prefill_states_f32(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream)
-                      : prefill_states_bf16(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream);
+    return dtype == kDtypeF32    ? prefill_states_f32(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream)
+           : dtype == kDtypeBf16 ? prefill_states_bf16(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream)
+                                 : prefill_states_feat(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream);
 }
 
 hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
                            const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out, float *z_out,
                            hipStream_t stream) {
-    return dtype == 0 ? prefill_outputs_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
-                      : prefill_outputs_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream);
+    return dtype == kDtypeF32    ? prefill_outputs_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
+           : dtype == kDtypeBf16 ? prefill_outputs_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
+                                 : prefill_outputs_feat(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -128,7 +138,7 @@ __device__ __forceinline__ f32x4 load4<bf16>(const bf16 *p) {
     return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
 }
 
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *__restrict__ S, float *__restrict__ z,
                                                                       const T *__restrict__ q,
                                                                       const T *__restrict__ k,
@@ -154,8 +164,8 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *
         const int d = tid + i * G::THREADS;
         if (d < D) {
             zz[i] = z[bh * D + d];
-            sq[d] = phi(to_f32(q[bh * D + d]));
-            sk[d] = phi(to_f32(k[bh * D + d]));
+            sq[d] = phi_if<PHI>(to_f32(q[bh * D + d]));
+            sk[d] = phi_if<PHI>(to_f32(k[bh * D + d]));
         }
     }
     __syncthreads();
@@ -219,11 +229,11 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *
     }
 }
 
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 hipError_t run_decode(float *S, float *z, const void *q, const void *k, const void *v, float *out, int BH,
                       hipStream_t stream) {
     if (BH <= 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_kernel<T, D, M>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream, S, z,
+    hipLaunchKernelGGL((decode_kernel<T, D, M, PHI>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream, S, z,
                        (const T *)q, (const T *)k, (const T *)v, out);
     return hipGetLastError();
 }
@@ -240,7 +250,7 @@ hipError_t run_decode(float *S, float *z, const void *q, const void *k, const vo
 // ---------------------------------------------------------------------------
 constexpr int kDecodeTokenBlock = 16;
 
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_steps_kernel(
     float *__restrict__ S, float *__restrict__ z, const T *__restrict__ q, const T *__restrict__ k,
     const T *__restrict__ v, float *__restrict__ out, int Tn) {
@@ -269,8 +279,8 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_steps_kernel(
         __syncthreads();  // the previous block's readers are done
         const T *qb = q + (tok0 + t0) * D, *kb = k + (tok0 + t0) * D;
         for (int e = tid; e < nt * D; e += G::THREADS) {
-            sq[e / D][e % D] = phi(to_f32(qb[e]));
-            sk[e / D][e % D] = phi(to_f32(kb[e]));
+            sq[e / D][e % D] = phi_if<PHI>(to_f32(qb[e]));
+            sk[e / D][e % D] = phi_if<PHI>(to_f32(kb[e]));
         }
         const T *vb = v + (tok0 + t0) * M;
         for (int e = tid; e < nt * G::LPR; e += G::THREADS) sv[e / G::LPR][e % G::LPR] = load4<T>(vb + e * 4);
@@ -331,11 +341,11 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_steps_kernel(
     }
 }
 
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 hipError_t run_decode_steps(float *S, float *z, const void *q, const void *k, const void *v, float *out, int BH,
                             int Tn, hipStream_t stream) {
     if (BH <= 0 || Tn <= 0) return hipSuccess;
-    hipLaunchKernelGGL((decode_steps_kernel<T, D, M>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream,
+    hipLaunchKernelGGL((decode_steps_kernel<T, D, M, PHI>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream,
                        S, z, (const T *)q, (const T *)k, (const T *)v, out, Tn);
     return hipGetLastError();
 }
@@ -344,8 +354,9 @@ hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void 
                         float *out, int BH, int Tn, hipStream_t stream) {
 #define X(D_, M_)                                                                                  \
     if (D == D_ && M == M_)                                                                        \
-        return dtype == 0 ? run_decode_steps<float, D_, M_>(S, z, q, k, v, out, BH, Tn, stream)    \
-                          : run_decode_steps<bf16, D_, M_>(S, z, q, k, v, out, BH, Tn, stream);
+        return dtype == kDtypeF32   ? run_decode_steps<float, D_, M_>(S, z, q, k, v, out, BH, Tn, stream) \
+               : dtype == kDtypeBf16 ? run_decode_steps<bf16, D_, M_>(S, z, q, k, v, out, BH, Tn, stream)  \
+                                     : run_decode_steps<float, D_, M_, false>(S, z, q, k, v, out, BH, Tn, stream);
 #define XM(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
     XM(16) XM(32) XM(64) XM(128)
 #undef XM
@@ -357,8 +368,9 @@ hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *
                        float *out, int BH, hipStream_t stream) {
 #define X(D_, M_)                                                                        \
     if (D == D_ && M == M_)                                                              \
-        return dtype == 0 ? run_decode<float, D_, M_>(S, z, q, k, v, out, BH, stream)    \
-                          : run_decode<bf16, D_, M_>(S, z, q, k, v, out, BH, stream);
+        return dtype == kDtypeF32   ? run_decode<float, D_, M_>(S, z, q, k, v, out, BH, stream) \
+               : dtype == kDtypeBf16 ? run_decode<bf16, D_, M_>(S, z, q, k, v, out, BH, stream)  \
+                                     : run_decode<float, D_, M_, false>(S, z, q, k, v, out, BH, stream);
 #define XM(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
     XM(16) XM(32) XM(64) XM(128)
 #undef XM

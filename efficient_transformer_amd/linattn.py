@@ -13,7 +13,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblinattn.so")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
-LA_F32, LA_BF16 = 0, 1
+LA_F32, LA_BF16, LA_F32_FEATURES = 0, 1, 2
+LA_FEATURE_ELU, LA_FEATURE_PRF, LA_FEATURE_TRF = 0, 1, 2
+LA_FEATURE_NORMALIZE = 1
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -49,6 +51,7 @@ SIGNATURES = {
     "la_softmax_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_decode_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_decode_steps": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
+    "la_feature_map": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp, _i64, _int, _int, _vp]),
 }
 
 
@@ -94,8 +97,13 @@ def _check(status: int, where: str) -> None:
         raise LinAttnError(status, where)
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(t, features: bool = False) -> int:
+    """LA_F32 / LA_BF16 from the tensor; features=True: fp32 rows that already hold phi(q), phi(k)."""
     import torch
+    if features:
+        if t.dtype != torch.float32:
+            raise TypeError("feature inputs must be float32")
+        return LA_F32_FEATURES
     if t.dtype == torch.float32:
         return LA_F32
     if t.dtype == torch.bfloat16:
@@ -164,12 +172,13 @@ def _cached_workspace(nbytes, device, stream, key):
 
 
 def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_out=None, z_out=None,
-                    stream=None):
+                    stream=None, features=False):
     """Parallel-mode attention: Q, K [B,H,N,D], V [B,H,N,M] (float32 or bfloat16) -> out [B,H,N,M] float32.
 
     With S_out [B,H,D,M] and z_out [B,H,D] (float32) the final state is written too.
     A given `workspace` must have been zeroed (workspace_init) for this plan; by
-    default a cached, zeroed one is used.
+    default a cached, zeroed one is used.  features=True: Q and K are float32
+    features (feature_map), no feature map is applied and D is the feature dimension.
     """
     import torch
     if Q.dim() != 4:
@@ -180,7 +189,7 @@ def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_o
     _require(Q, "Q", (B, H, N, D))
     _require(K, "K", (B, H, N, D), Q.dtype, dev)
     _require(V, "V", (B, H, N, M), Q.dtype, dev)
-    dt = _dtype_code(Q)
+    dt = _dtype_code(Q, features)
     if out is None:
         out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
     _require(out, "out", (B, H, N, M), torch.float32, dev)
@@ -208,20 +217,21 @@ def fused_workspace_bytes(B, H, D, M, segments) -> int:
 
 
 def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None,
-                  S_in=None, z_in=None):
+                  S_in=None, z_in=None, features=False):
     """The causal two-phase fused kernel with an explicit plan (chunk, segments)."""
     return _forward_explicit("la_forward_fused", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream,
-                             S_in, z_in)
+                             S_in, z_in, features)
 
 
 def forward_onepass(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None,
-                    S_in=None, z_in=None):
+                    S_in=None, z_in=None, features=False):
     """The causal one-pass kernel with an explicit plan (segments of at most 4 chunks)."""
     return _forward_explicit("la_forward_onepass", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream,
-                             S_in, z_in)
+                             S_in, z_in, features)
 
 
-def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_out=None, z_out=None, stream=None):
+def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_out=None, z_out=None, stream=None,
+                     features=False):
     """Causal attention continuing from the carried state (S_in [B,H,D,M], z_in [B,H,D], fp32)."""
     import torch
     B, H, N, D = Q.shape
@@ -234,7 +244,7 @@ def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_o
         _require(z_in, "z_in", (B, H, D), torch.float32, dev)
     if out is None:
         out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
-    dt = _dtype_code(Q)
+    dt = _dtype_code(Q, features)
     C, G, need = forward_plan(B, H, N, D, M, True, dt, chunk)
     if workspace is None and need > 0:
         workspace = _cached_workspace(need, dev, stream, ("chunked", B * H, N, D, M, True, dt, C, G))
@@ -246,7 +256,7 @@ def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_o
     return out
 
 
-def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream, S_in, z_in):
+def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream, S_in, z_in, features):
     import torch
     B, H, N, D = Q.shape
     M = V.shape[-1]
@@ -257,20 +267,21 @@ def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_o
         out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
     need = fused_workspace_bytes(B, H, D, M, segments)
     if workspace is None and need > 0:
-        workspace = _cached_workspace(need, dev, stream, (name, B * H, N, D, M, _dtype_code(Q), chunk, segments))
+        workspace = _cached_workspace(need, dev, stream, (name, B * H, N, D, M, _dtype_code(Q, features), chunk,
+                                                          segments))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(Q), chunk,
+    st = getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(Q, features), chunk,
                               segments, _ptr(S_in), _ptr(z_in), _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out),
                               _stream(stream, dev))
     _check(st, name)
     return out
 
 
-def segment_states(K, V, ws, chunk, segments, nstates, stream=None):
+def segment_states(K, V, ws, chunk, segments, nstates, stream=None, features=False):
     B, H, N, D = K.shape
     M = V.shape[-1]
     st = lib().la_segment_states(_ptr(K), _ptr(V), _ptr(ws), ws.numel() * ws.element_size(), B, H, N, D, M,
-                                 _dtype_code(K), chunk, segments, nstates, _stream(stream, K.device))
+                                 _dtype_code(K, features), chunk, segments, nstates, _stream(stream, K.device))
     _check(st, "la_segment_states")
 
 
@@ -280,16 +291,17 @@ def segment_scan(ws, B, H, D, M, segments, nstates, S_out=None, z_out=None, stre
     _check(st, "la_segment_scan")
 
 
-def segment_outputs(Q, K, V, out, ws, chunk, segments, causal=True, S_out=None, z_out=None, stream=None):
+def segment_outputs(Q, K, V, out, ws, chunk, segments, causal=True, S_out=None, z_out=None, stream=None,
+                    features=False):
     B, H, N, D = Q.shape
     M = out.shape[-1]
     st = lib().la_segment_outputs(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                                  B, H, N, D, M, int(bool(causal)), _dtype_code(Q), chunk, segments,
+                                  B, H, N, D, M, int(bool(causal)), _dtype_code(Q, features), chunk, segments,
                                   _ptr(S_out), _ptr(z_out), _stream(stream, Q.device))
     _check(st, "la_segment_outputs")
 
 
-def decode_step(S, z, q, k, v, out=None, stream=None):
+def decode_step(S, z, q, k, v, out=None, stream=None, features=False):
     """One recurrent step: S [B,H,D,M], z [B,H,D] (float32, updated in place); q, k [B,H,D]; v [B,H,M]."""
     import torch
     if S.dim() != 4:
@@ -305,12 +317,12 @@ def decode_step(S, z, q, k, v, out=None, stream=None):
         out = torch.empty((B, H, M), dtype=torch.float32, device=dev)
     _require(out, "out", (B, H, M), torch.float32, dev)
     st = lib().la_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, D, M,
-                              _dtype_code(q), _stream(stream, dev))
+                              _dtype_code(q, features), _stream(stream, dev))
     _check(st, "la_decode_step")
     return out
 
 
-def decode_steps(S, z, q, k, v, out=None, stream=None):
+def decode_steps(S, z, q, k, v, out=None, stream=None, features=False):
     """T recurrent steps in one call: S [B,H,D,M], z [B,H,D] (float32, updated in place);
     q, k [B,H,T,D]; v [B,H,T,M]; returns out [B,H,T,M]."""
     import torch
@@ -328,7 +340,7 @@ def decode_steps(S, z, q, k, v, out=None, stream=None):
         out = torch.empty((B, H, T, M), dtype=torch.float32, device=dev)
     _require(out, "out", (B, H, T, M), torch.float32, dev)
     st = lib().la_decode_steps(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, D, M,
-                               _dtype_code(q), _stream(stream, dev))
+                               _dtype_code(q, features), _stream(stream, dev))
     _check(st, "la_decode_steps")
     return out
 
@@ -394,3 +406,37 @@ def softmax_step(m, u, w, q, k, v, out=None, stream=None):
                                _dtype_code(q), _stream(stream, dev))
     _check(st, "la_softmax_step")
     return out
+
+
+FEATURE_KINDS = {"elu": LA_FEATURE_ELU, "prf": LA_FEATURE_PRF, "trf": LA_FEATURE_TRF}
+
+
+def feature_map(X, W, F, kind="prf", normalize=False, out=None, X2=None, out2=None, stream=None):
+    """Random features of every row of X [..., D] (float32 or bfloat16) -> float32 [..., F].
+
+    kind "elu" (F = D, W unused), "prf" (W [F, D] float32) or "trf" (W [F/2, D]);
+    normalize scales every row to unit length first.  X2 (same shape as X) is
+    mapped into out2 in the same launch; returns out, or (out, out2) with X2.
+    """
+    import torch
+    D = X.shape[-1]
+    dev = X.device
+    _require(X, "X", tuple(X.shape), None, dev)
+    k = FEATURE_KINDS[kind]
+    if k != LA_FEATURE_ELU:
+        _require(W, "W", ((F if k == LA_FEATURE_PRF else F // 2), D), torch.float32, dev)
+    shape = (*X.shape[:-1], F)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    _require(out, "out", shape, torch.float32, dev)
+    if X2 is not None:
+        _require(X2, "X2", tuple(X.shape), X.dtype, dev)
+        if out2 is None:
+            out2 = torch.empty(shape, dtype=torch.float32, device=dev)
+        _require(out2, "out2", shape, torch.float32, dev)
+    rows = X.numel() // D if D else 0
+    st = lib().la_feature_map(_ptr(out), _ptr(X), _ptr(out2) if X2 is not None else None, _ptr(X2), rows, D,
+                              _dtype_code(X), _ptr(W) if k != LA_FEATURE_ELU else None, F, k,
+                              LA_FEATURE_NORMALIZE if normalize else 0, _stream(stream, dev))
+    _check(st, "la_feature_map")
+    return out if X2 is None else (out, out2)

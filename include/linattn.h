@@ -53,7 +53,12 @@ enum la_status {
     LA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
 };
 
-enum la_dtype { LA_F32 = 0, LA_BF16 = 1 };
+/* LA_F32_FEATURES: fp32 Q and K rows that already hold the features phi(q),
+ * phi(k) (for example from la_feature_map); the kernels then apply no feature
+ * map, D is the feature dimension, and V is fp32.  Accepted by the forward
+ * entry points, the segment stages and the decode entry points; not by
+ * la_backward_chunked (LA_ERR_UNSUPPORTED) or the softmax scan. */
+enum la_dtype { LA_F32 = 0, LA_BF16 = 1, LA_F32_FEATURES = 2 };
 
 /* Human-readable name of a status code (static string; never NULL). */
 LA_API const char *la_status_str(int status);
@@ -289,6 +294,31 @@ LA_API int la_softmax_scan(const void *q, const void *K, const void *V, float *o
 LA_API int la_softmax_step(float *m, float *u, float *w, const void *q, const void *k,
                            const void *v, float *out, int64_t B, int64_t H, int64_t D,
                            int64_t M, int dtype, void *stream);
+
+/* Random-feature map with feature dimension F (page "Stable, Fast and
+ * Accurate: Kernelized Attention with Relative Positional Encoding", Proposed
+ * method and Main findings: kernelized attention with the feature maps PRF,
+ * TRF, Sphere-PRF and ORF, feature dimension as small as 16, queries and keys
+ * normalised when their norms are large).  Each row x of X is mapped to F
+ * features in out:
+ *   LA_FEATURE_ELU: elu(x) + 1 elementwise (F = D; W unused, may be NULL);
+ *   LA_FEATURE_PRF: exp(w_p . x - |x|^2 / 2) / sqrt(F), p < F, W [F][D] fp32;
+ *   LA_FEATURE_TRF: with P = F / 2 and c = exp(|x|^2 / 2) / sqrt(P):
+ *                   out[p] = c sin(w_p . x), out[P + p] = c cos(w_p . x),
+ *                   W [P][D] fp32.
+ * Over rows w_p ~ N(0, I) the expected phi(q) . phi(k) is exp(q . k) for PRF
+ * and TRF.  ORF (orthogonal rows) and Sphere-PRF (rows on a sphere) are PRF
+ * with the caller's W.  flags: LA_FEATURE_NORMALIZE scales every row to unit
+ * length first (a zero row stays zero).
+ * X [rows][D] (dtype LA_F32 or LA_BF16), out [rows][F] fp32.  X2 / out2: an
+ * optional second tensor of the same shape mapped in the same launch (both NULL
+ * or both set), e.g. Q and K.  D and F must each be 16, 32, 64 or 128.  The
+ * outputs feed the other entry points with dtype LA_F32_FEATURES.
+ */
+enum la_feature_kind { LA_FEATURE_ELU = 0, LA_FEATURE_PRF = 1, LA_FEATURE_TRF = 2 };
+enum { LA_FEATURE_NORMALIZE = 1 };
+LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2, int64_t rows, int64_t D,
+                          int dtype, const float *W, int64_t F, int kind, int flags, void *stream);
 
 #ifdef __cplusplus
 }

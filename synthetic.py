@@ -129,6 +129,9 @@ WORKLOADS = {
     "prefill_bf16_b4h8_n3072_d64": dict(kind="prefill", B=4, H=8, N=3072, D=64, M=64, sigma=0.5, dtype="bf16", chunk=0),
     "prefill_bf16_b1h16_n65536_d128": dict(kind="prefill", B=1, H=16, N=65536, D=128, M=128, sigma=1.0, dtype="bf16", chunk=0),
     "decode_f32_256x8_t4096_d64": dict(kind="decode", B=256, H=8, T=4096, D=64, M=64, sigma=1.0, dtype="f32"),
+    # random features: q, k with sigma = D^(-1/4) (unit-variance q . k), 16 positive random features
+    "prefill_prf16_f32_b8h8_n1024_d64": dict(kind="features", B=8, H=8, N=1024, D=64, M=64, F=16, feature="prf",
+                                             sigma=64 ** -0.25, dtype="f32", chunk=0),
 }
 
 

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     for s in ("la_forward_chunked", "la_decode_step", "la_forward_workspace_bytes", "la_forward_plan",
               "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version",
               "la_forward_fused", "la_forward_onepass", "la_forward_continue", "la_workspace_init",
-              "la_backward_chunked", "la_decode_steps", "la_softmax_scan", "la_softmax_step"):
+              "la_backward_chunked", "la_decode_steps", "la_softmax_scan", "la_softmax_step", "la_feature_map"):
         assert s in syms
 
 
@@ -95,7 +95,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=48), 2), (dict(M=8), 2), (dict(D=256), 2), (dict(dtype=2), 1), (dict(causal=2), 1),
+    (dict(D=48), 2), (dict(M=8), 2), (dict(D=256), 2), (dict(dtype=3), 1), (dict(causal=2), 1),
     (dict(chunk=128), 2), (dict(chunk=8), 2), (dict(N=-1), 1), (dict(B=-1), 1), (dict(H=-3), 1),
     (dict(Q=None), 1), (dict(out=None), 1), (dict(V=FAKE + 4), 1), (dict(S=FAKE), 1),
 ])
@@ -189,7 +189,7 @@ def test_continue_entry_point_checks(L):
              None) == L.LA_ERR_WORKSPACE
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 48, 64, 0, 0, FAKE, FAKE, FAKE, need, None, None,
              None) == L.LA_ERR_UNSUPPORTED
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 2, 0, FAKE, FAKE, FAKE, need, None, None,
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 3, 0, FAKE, FAKE, FAKE, need, None, None,
              None) == L.LA_ERR_INVALID_ARG  # dtype
     assert f(None, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 0, FAKE, FAKE, FAKE, need, None, None,
              None) == L.LA_ERR_INVALID_ARG
@@ -240,3 +240,35 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
             "try:\n    L.version()\nexcept RuntimeError as e:\n    print('raised', 'no fallback' in str(e))\n")
     r = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert "raised True" in r.stdout, r.stdout + r.stderr
+
+
+def test_feature_map_checks(L):
+    f = L.lib().la_feature_map
+    # out, X, out2, X2, rows, D, dtype, W, F, kind, flags, stream
+    assert f(FAKE, FAKE, None, None, 100, 64, 0, FAKE, 16, 3, 0, None) == L.LA_ERR_INVALID_ARG  # kind
+    assert f(FAKE, FAKE, None, None, 100, 64, 0, FAKE, 16, 1, 2, None) == L.LA_ERR_INVALID_ARG  # flag
+    assert f(FAKE, FAKE, None, None, 100, 64, 0, None, 32, 0, 0, None) == L.LA_ERR_INVALID_ARG  # elu: F != D
+    assert f(FAKE, FAKE, None, None, 100, 64, 2, FAKE, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG  # dtype
+    assert f(FAKE, FAKE, None, None, 100, 48, 0, FAKE, 16, 1, 0, None) == L.LA_ERR_UNSUPPORTED  # D
+    assert f(FAKE, FAKE, None, None, 100, 64, 0, FAKE, 24, 1, 0, None) == L.LA_ERR_UNSUPPORTED  # F
+    assert f(FAKE, FAKE, FAKE, None, 100, 64, 0, FAKE, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG  # out2 alone
+    assert f(FAKE, FAKE, None, None, 100, 64, 0, None, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG  # PRF needs W
+    assert f(FAKE, FAKE + 4, None, None, 100, 64, 0, FAKE, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG  # alignment
+    assert f(FAKE, FAKE, None, None, -1, 64, 0, FAKE, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG
+    assert f(None, None, None, None, 0, 64, 0, None, 16, 1, 0, None) == L.LA_OK  # no rows
+
+
+def test_feature_inputs_dtype(L):
+    """LA_F32_FEATURES plans like fp32, is refused by the backward pass and the softmax scan."""
+    for D in (16, 64, 128):
+        for M in (16, 64, 128):
+            assert L.forward_plan(2, 3, 1000, D, M, 1, L.LA_F32_FEATURES, 0) == \
+                L.forward_plan(2, 3, 1000, D, M, 1, L.LA_F32, 0)
+    lib = L.lib()
+    assert lib.la_backward_workspace_bytes(2, 2, 100, 64, 64, L.LA_F32_FEATURES) == 0
+    assert lib.la_backward_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 100, 64, 64,
+                                   L.LA_F32_FEATURES, FAKE, 1 << 30, None) == L.LA_ERR_UNSUPPORTED
+    assert lib.la_softmax_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, L.LA_F32_FEATURES,
+                               None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 48, 64, L.LA_F32_FEATURES,
+                              None) == L.LA_ERR_UNSUPPORTED  # accepted type, unsupported D
