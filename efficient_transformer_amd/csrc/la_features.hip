@@ -10,14 +10,13 @@
 // ORF and Sphere-PRF are PRF with orthogonal rows or rows on a sphere in W.
 // NORM: every row is scaled to unit length first.
 //
-// One workgroup maps 64 rows: the 64 x D tile is staged in LDS with coalesced
-// 16-byte loads, each lane then owns one row, and each of the 4 wavefronts
-// forms a quarter of the projections.  W is read with wave-uniform addresses
-// (scalar loads), so every fma takes its W operand from a scalar register.  The
-// 64 x F results go back through LDS and leave as coalesced 16-byte stores.
-// The projection is a dense contraction, but on gfx950 fp32 matrix and fp32
-// vector throughput are the same (157.3 TFLOP/s), and at F = 16 the kernel is
-// bound by HBM: vector fmas with scalar operands need no operand shuffling.
+// One workgroup maps 64 rows: the 64 x D tile and W are staged in LDS with
+// coalesced 16-byte loads.  The projection x W^T is a dense contraction and runs
+// on fp32 MFMA (16x16x4): each wavefront takes 16 rows, and per 16-deep block
+// one 16-byte LDS read of x and one of each 16-row W tile feed four MFMAs (a
+// lane-per-row vector-fma form needed an LDS read per four fmas and was
+// LDS-bound beyond F = 16).  The 64 x F results go back through LDS and leave
+// as coalesced 16-byte stores.
 #include <math.h>
 
 #include "la_device.hpp"
@@ -31,10 +30,13 @@ constexpr int kFeatThreads = 256;
 template <int D, int F, int KIND>
 struct FeatCfg {
     static constexpr int P = KIND == 2 ? F / 2 : F;  // projections (kind 0: columns)
-    static constexpr int PW = P / 4;                 // per wavefront
+    static constexpr int PW = P / 4;                 // kind 0: columns per wavefront
+    static constexpr int PT = (P + 15) / 16;         // 16-wide projection tiles (W rows past P are zero)
     static constexpr int LX = D + 4;                 // LDS row of the input tile (floats)
+    static constexpr int LW = D + 4;                 // LDS row of W
     static constexpr int LO = F + 4;                 // LDS row of the output tile
     static_assert(PW >= 1 && PW * 4 == P, "projections split over 4 wavefronts");
+    static_assert(D % 16 == 0 && P % 4 == 0, "16-deep contraction blocks, 4-wide result groups");
 };
 
 template <typename T>
@@ -57,6 +59,7 @@ __global__ __launch_bounds__(kFeatThreads) void feature_map_kernel(const T *__re
     using G = FeatCfg<D, F, KIND>;
     __shared__ __attribute__((aligned(16))) float sx[kFeatRows * G::LX];
     __shared__ __attribute__((aligned(16))) float so[kFeatRows * G::LO];
+    __shared__ __attribute__((aligned(16))) float sw[KIND == 0 ? 4 : G::PT * 16 * G::LW];  // W (padded rows)
     const T *Xs = blockIdx.y == 0 ? X : X2;
     float *Os = blockIdx.y == 0 ? out : out2;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -64,63 +67,106 @@ __global__ __launch_bounds__(kFeatThreads) void feature_map_kernel(const T *__re
     const long r0 = (long)blockIdx.x * kFeatRows;
     const int nr = (int)(rows - r0 < kFeatRows ? rows - r0 : kFeatRows);
 
-    // 1. the input tile; rows past the end are zero (their results are not stored)
+    // 1. the input tile and W: every load issued before the first LDS write (rows
+    //    past the end reload the last row; their results are not stored)
     constexpr int V4 = D / 4;
+    constexpr int NL = kFeatRows * V4 / kFeatThreads;
+    constexpr int WL = KIND == 0 ? 0 : (G::PT * 16 * D / 4 + kFeatThreads - 1) / kFeatThreads;
+    static_assert(NL * kFeatThreads == kFeatRows * V4, "whole tile per pass");
+    f32x4 xv[NL], wv[WL > 0 ? WL : 1];
 #pragma unroll
-    for (int e = tid; e < kFeatRows * V4; e += kFeatThreads) {
-        const int r = e / V4, c = (e % V4) * 4;
-        f32x4 v = zero4();
-        if (r < nr) v = feat_load4<T>(Xs + (size_t)(r0 + r) * D + c);
-        *reinterpret_cast<f32x4 *>(sx + r * G::LX + c) = v;
+    for (int i = 0; i < NL; ++i) {
+        const int e = tid + i * kFeatThreads, r = e / V4, c = (e % V4) * 4;
+        xv[i] = feat_load4<T>(Xs + (size_t)(r0 + min(r, nr - 1)) * D + c);
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+        const int e = min(tid + i * kFeatThreads, G::P * D / 4 - 1);  // rows past P: zero below
+        wv[i] = *reinterpret_cast<const f32x4 *>(W + (size_t)e * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int e = tid + i * kFeatThreads, r = e / V4, c = (e % V4) * 4;
+        *reinterpret_cast<f32x4 *>(sx + r * G::LX + c) = xv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < WL; ++i) {
+        const int e = tid + i * kFeatThreads, f = e / (D / 4), c = (e % (D / 4)) * 4;
+        if (f < G::PT * 16) *reinterpret_cast<f32x4 *>(sw + f * G::LW + c) = f < G::P ? wv[i] : zero4();
     }
     __syncthreads();
 
-    // 2. lane = row: |x|^2 (and the normalising scale), then this wavefront's projections
-    const float *xr = sx + lane * G::LX;
-    float sq = 0.0f;
-#pragma unroll
-    for (int c = 0; c < D; c += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
-        sq += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
-    }
-    float scale = 1.0f;
-    if (NORM && sq > 0.0f) {
-        scale = 1.0f / sqrtf(sq);
-        sq = sq * scale * scale;
-    }
-    float *orow = so + lane * G::LO;
     if constexpr (KIND == 0) {
+        // 2. elementwise: lane = row, wavefront w takes a quarter of the columns
+        const float *xr = sx + lane * G::LX;
+        float sq = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D; c += 4) {
+            const f32x4 x4 = *reinterpret_cast<const f32x4 *>(xr + c);
+            sq += x4[0] * x4[0] + x4[1] * x4[1] + x4[2] * x4[2] + x4[3] * x4[3];
+        }
+        const float scale = NORM && sq > 0.0f ? 1.0f / sqrtf(sq) : 1.0f;
 #pragma unroll
         for (int j = 0; j < G::PW; ++j) {
             const int col = w * G::PW + j;
-            orow[col] = phi(xr[col] * scale);
+            so[lane * G::LO + col] = phi(xr[col] * scale);
         }
     } else {
-        float acc[G::PW];
+        // 2. projections on MFMA: wavefront w owns rows 16w .. 16w+15 of the tile.
+        //    C[f][row] = sum_k W[f][k] x[row][k] with W as the A operand (lane: row
+        //    f = l16 of a 16-row W tile) and x as the B operand (lane: row l16 of the
+        //    wavefront's rows); lane (g, l16) ends with projections 4g .. 4g+3 of its
+        //    own row l16.  Within each 16-deep block, lane g contracts over
+        //    k = 16 kb + 4 g + kk for both operands (one 16-byte LDS read each).
+        const int g = lane >> 4, l16 = lane & 15;
+        const float *xr = sx + (16 * w + l16) * G::LX + 4 * g;
+        const float *wr = sw + l16 * G::LW + 4 * g;
+        f32x4 acc[G::PT];
 #pragma unroll
-        for (int j = 0; j < G::PW; ++j) acc[j] = 0.0f;
-        const float *Wb = W + (size_t)(w * G::PW) * D;
+        for (int t = 0; t < G::PT; ++t) acc[t] = zero4();
+        float sq = 0.0f;
 #pragma unroll
-        for (int c = 0; c < D; c += 4) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + c);
+        for (int kb = 0; kb < D / 16; ++kb) {
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(xr + 16 * kb);
+            sq += b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
 #pragma unroll
-            for (int j = 0; j < G::PW; ++j) {
-                const float *wp = Wb + (size_t)j * D + c;
-                acc[j] += v[0] * wp[0] + v[1] * wp[1] + v[2] * wp[2] + v[3] * wp[3];
+            for (int t = 0; t < G::PT; ++t) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(wr + t * 16 * G::LW + 16 * kb);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc[t] = mma_f32(a[kk], b[kk], acc[t]);
             }
         }
-        if constexpr (KIND == 1) {
-            const float inv = 1.0f / sqrtf((float)F);
+        // |x|^2 of row l16: the four lanes g of that row hold a quarter each
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        float scale = 1.0f;
+        if (NORM && sq > 0.0f) {
+            scale = 1.0f / sqrtf(sq);
+            sq = sq * scale * scale;
+        }
+        float *orow = so + (16 * w + l16) * G::LO;
 #pragma unroll
-            for (int j = 0; j < G::PW; ++j) orow[w * G::PW + j] = __expf(acc[j] * scale - 0.5f * sq) * inv;
-        } else {
-            const float c = __expf(0.5f * sq) / sqrtf((float)G::P);
+        for (int t = 0; t < G::PT; ++t) {
+            const int f0 = t * 16 + 4 * g;  // this lane's 4 projections
+            if (f0 >= G::P) continue;
+            f32x4 o;
+            if constexpr (KIND == 1) {
+                const float inv = 1.0f / sqrtf((float)F);
 #pragma unroll
-            for (int j = 0; j < G::PW; ++j) {
-                float s, co;
-                sincosf(acc[j] * scale, &s, &co);
-                orow[w * G::PW + j] = c * s;
-                orow[G::P + w * G::PW + j] = c * co;
+                for (int r = 0; r < 4; ++r) o[r] = __expf(acc[t][r] * scale - 0.5f * sq) * inv;
+                *reinterpret_cast<f32x4 *>(orow + f0) = o;
+            } else {
+                const float c = __expf(0.5f * sq) / sqrtf((float)G::P);
+                f32x4 oc;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float sn, cs;
+                    sincosf(acc[t][r] * scale, &sn, &cs);
+                    o[r] = c * sn;
+                    oc[r] = c * cs;
+                }
+                *reinterpret_cast<f32x4 *>(orow + f0) = o;
+                *reinterpret_cast<f32x4 *>(orow + G::P + f0) = oc;
             }
         }
     }
