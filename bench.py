@@ -67,10 +67,12 @@ def log(*a):
 
 
 def prefill_bytes(cfg) -> int:
-    """Algorithmic bytes of one prefill call: read Q, K, V once, write out (fp32) once."""
+    """Algorithmic bytes of one prefill call: read Q, K, V once, write out once (fp32, or
+    bf16 when cfg["out"] == "bf16")."""
     s = 4 if cfg["dtype"] == "f32" else 2
+    so = 2 if cfg.get("out") == "bf16" else 4
     BH, N, D, M = cfg["B"] * cfg["H"], cfg["N"], cfg["D"], cfg["M"]
-    return BH * N * ((2 * D + M) * s + 4 * M)
+    return BH * N * ((2 * D + M) * s + so * M)
 
 
 def prefill_flops_min(cfg) -> int:
@@ -96,7 +98,8 @@ def make_prefill_sets(cfg, nsets, dev):
                                  cfg["dtype"], dev)
         V = synthetic.draw_torch(r, synthetic.TID_V, (cfg["B"], cfg["H"], cfg["N"], cfg["M"]), cfg["sigma"],
                                  cfg["dtype"], dev)
-        out = torch.empty((cfg["B"], cfg["H"], cfg["N"], cfg["M"]), dtype=torch.float32, device=dev)
+        odt = torch.bfloat16 if cfg.get("out") == "bf16" else torch.float32
+        out = torch.empty((cfg["B"], cfg["H"], cfg["N"], cfg["M"]), dtype=odt, device=dev)
         sets.append((Q, K, V, out))
     torch.cuda.synchronize()
     return sets
@@ -517,13 +520,17 @@ def main():
             "bytes_per_step": dec["bytes_per_step"],
             "note": "the 34 MB state stays resident in the 256 MB last-level cache between steps"}
         others = {}
-        for name in ("prefill_bf16_b4h8_n3072_d64", "prefill_bf16_b1h16_n65536_d128"):
+        for name, outdt in (("prefill_bf16_b4h8_n3072_d64", "fp32"), ("prefill_bf16_b1h16_n65536_d128", "fp32"),
+                            ("prefill_bf16_b4h8_n3072_d64", "bf16"), ("prefill_bf16_b1h16_n65536_d128", "bf16")):
             c = dict(synthetic.WORKLOADS[name])
-            log(f"prefill {name} ...")
+            if outdt == "bf16":
+                c["out"] = "bf16"
+            key = name if outdt == "fp32" else name + "_bf16out"
+            log(f"prefill {key} ...")
             r = bench_prefill(c, max(10, args.steps // 4), 5, dev)
-            log(f"{name}: {r}")
-            others[name] = {
-                "workload": f"causal prefill bf16 in, fp32 out, B={c['B']} H={c['H']} N={c['N']} D=M={c['D']}",
+            log(f"{key}: {r}")
+            others[key] = {
+                "workload": f"causal prefill bf16 in, {outdt} out, B={c['B']} H={c['H']} N={c['N']} D=M={c['D']}",
                 "tokens_per_s": round(r["tokens_per_s"], 1), "ms_per_step": round(r["ms_per_step"], 5),
                 "chunk": r["chunk"], "segments": r["segments"],
                 "kernel_us": round(r["us_kernel"], 2),

@@ -24,7 +24,8 @@ struct Plan {
 // Validate the shape arguments shared by the prefill entry points.
 int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype) {
     if (B < 0 || H < 0 || N < 0 || D <= 0 || M <= 0) return LA_ERR_INVALID_ARG;
-    if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES && dtype != (LA_BF16 | LA_OUT_BF16))
+        return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
     // index arithmetic uses int for counts and size_t for element offsets
     if (N > INT_MAX || B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
@@ -49,7 +50,7 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
     if (chunk_req == 0) {
         // fp32 operands with a small state run 32-position chunks (less masked
         // quadratic work per position on the slower fp32 MFMA); otherwise 64
-        C = (dtype != LA_BF16 && D * M <= 4096) ? 32 : 64;
+        C = ((dtype & ~LA_OUT_BF16) != LA_BF16 && D * M <= 4096) ? 32 : 64;
         if (!la::prefill_supported(dtype, (int)D, (int)M, C)) C = 32;
         if (!la::prefill_supported(dtype, (int)D, (int)M, C)) C = 16;
     } else if (chunk_req == 16 || chunk_req == 32 || chunk_req == 64) {
@@ -133,7 +134,7 @@ LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_
     return make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p) == LA_OK ? p.ws_bytes : 0;
 }
 
-LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, void *out, int64_t B, int64_t H,
                               int64_t N, int64_t D, int64_t M, int causal, int dtype, int chunk_req,
                               void *workspace, size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
     Plan p;
@@ -173,7 +174,7 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
     return hip_status(e);
 }
 
-LA_API int la_forward_continue(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+LA_API int la_forward_continue(const void *Q, const void *K, const void *V, void *out, int64_t B, int64_t H,
                                int64_t N, int64_t D, int64_t M, int dtype, int chunk_req, const float *S_in,
                                const float *z_in, void *workspace, size_t workspace_bytes, float *S_out,
                                float *z_out, void *stream) {
@@ -252,7 +253,7 @@ int cps_of(int64_t N, int chunk, int segments) {
 
 namespace {
 // Shared validation and launch of the two explicit-plan causal entry points.
-int forward_explicit(bool onepass, const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+int forward_explicit(bool onepass, const void *Q, const void *K, const void *V, void *out, int64_t B, int64_t H,
                      int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, const float *S_in,
                      const float *z_in, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
                      void *stream) {
@@ -305,7 +306,7 @@ int forward_explicit(bool onepass, const void *Q, const void *K, const void *V, 
 }
 }  // namespace
 
-LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+LA_API int la_forward_fused(const void *Q, const void *K, const void *V, void *out, int64_t B, int64_t H,
                             int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, const float *S_in,
                             const float *z_in, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
                             void *stream) {
@@ -313,7 +314,7 @@ LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *
                             workspace_bytes, S_out, z_out, stream);
 }
 
-LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, void *out, int64_t B, int64_t H,
                               int64_t N, int64_t D, int64_t M, int dtype, int chunk, int segments, const float *S_in,
                               const float *z_in, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
                               void *stream) {
@@ -352,7 +353,7 @@ LA_API int la_segment_scan(float *ws, size_t ws_bytes, int64_t B, int64_t H, int
                                        as_stream(stream)));
 }
 
-LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, float *out, const float *ws,
+LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, void *out, const float *ws,
                               size_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
                               int dtype, int chunk, int segments, float *S_out, float *z_out, void *stream) {
     int st = check_stage(B, H, N, D, M, dtype, chunk, segments, ws_bytes, ws);
@@ -393,8 +394,9 @@ struct BwdPlan {
     size_t states_bytes = 0, den_bytes = 0, ws_bytes = 0;
 };
 int bwd_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype, BwdPlan *p) {
-    // the gradient is taken through phi = elu + 1; features computed elsewhere are not covered
-    if (dtype == LA_F32_FEATURES) return LA_ERR_UNSUPPORTED;
+    // the gradient is taken through phi = elu + 1; features computed elsewhere are not
+    // covered, and gradients are fp32
+    if (dtype == LA_F32_FEATURES || (dtype & LA_OUT_BF16)) return LA_ERR_UNSUPPORTED;
     int st = check_shape(B, H, N, D, M, dtype);
     if (st != LA_OK) return st;
     const int64_t BH = B * H;

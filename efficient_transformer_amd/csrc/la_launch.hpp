@@ -10,6 +10,8 @@ namespace la {
 // Element types of the inputs: fp32, bf16, or fp32 rows that already hold the
 // features phi(q), phi(k) (the kernels then apply no feature map).
 constexpr int kDtypeF32 = 0, kDtypeBf16 = 1, kDtypeF32Features = 2;
+// OR-ed into the element type of bf16 inputs: the prefill outputs are bf16.
+constexpr int kOutBf16 = 16;
 
 // Workspace layout of the fused causal kernel (shared by host sizing and device code):
 // header words, then one flag word per segment (padded to 64 words), then the
@@ -41,15 +43,15 @@ hipError_t softmax_step(int dtype, int D, int M, float *m, float *u, float *w, c
 bool prefill_supported(int dtype, int D, int M, int C);
 hipError_t prefill_states(int dtype, int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N,
                           int G, int CPS, int nstates, hipStream_t stream);
-hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
                            const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out, float *z_out,
                            hipStream_t stream);
-hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
                          void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream);
 // One-pass causal kernel: segments of at most 4 chunks (see la_prefill.hpp).
 constexpr int kOnePassMaxChunks = 4;
 bool prefill_onepass_supported(int dtype, int D, int M, int C);
-hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
                            void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream);
 size_t prefill_lds_bytes(int dtype, int D, int M, int C);
 hipError_t prefill_scan(float *ws, int BH, int D, int M, int G, int nstates, float *S_out, float *z_out,
@@ -75,6 +77,17 @@ hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void 
 // trigonometric; X2 / out2 optional (a second tensor in the same launch).
 hipError_t feature_map(int dtype, int D, int F, int kind, const void *X, float *out, const void *X2, float *out2,
                        const float *W, long rows, bool norm, hipStream_t stream);
+
+// bf16 inputs, bf16 outputs (la_bf16out.hip)
+hipError_t prefill_fused_bf16o(int D, int M, int C, const void *Q, const void *K, const void *V, void *out, void *ws,
+                               int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
+                               const float *z_in, hipStream_t stream);
+hipError_t prefill_onepass_bf16o(int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
+                                 void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out,
+                                 const float *S_in, const float *z_in, hipStream_t stream);
+hipError_t prefill_outputs_bf16o(int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
+                                 const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out,
+                                 float *z_out, hipStream_t stream);
 
 // feature inputs (la_feat_prefill.hip, la_feat_onepass.hip)
 bool prefill_supported_feat(int D, int M, int C);

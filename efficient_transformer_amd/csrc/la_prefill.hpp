@@ -613,8 +613,10 @@ struct Engine {
         }
     }
 
-    // out[row0 + rows] = o * (1 / den) of the row (inv: lane r holds row r's factor)
-    __device__ __forceinline__ void store_rows(const f32x4 (&o)[RT][MTW], float inv, float *__restrict__ Oh, int row0,
+    // out[row0 + rows] = o * (1 / den) of the row (inv: lane r holds row r's factor).
+    // OT = float: 16-byte stores; OT = bf16: rounded to nearest even, 8-byte stores.
+    template <typename OT>
+    __device__ __forceinline__ void store_rows(const f32x4 (&o)[RT][MTW], float inv, OT *__restrict__ Oh, int row0,
                                                int N, bool poison) const {
         const bool full = row0 + C <= N;  // uniform: no per-row bounds checks needed
 #pragma unroll
@@ -629,14 +631,20 @@ struct Engine {
                     f32x4 v;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) v[r] = poison ? __builtin_nanf("") : o[rt][i][r] * inv_q;
-                    *reinterpret_cast<f32x4 *>(Oh + (size_t)grow * M + mtile(i) * 16 + 4 * g) = v;
+                    OT *dst = Oh + (size_t)grow * M + mtile(i) * 16 + 4 * g;
+                    if constexpr (std::is_same<OT, float>::value) {
+                        *reinterpret_cast<f32x4 *>(dst) = v;
+                    } else {
+                        *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                    }
                 }
             }
         }
     }
 
+    template <typename OT>
     __device__ __forceinline__ void readout(f32x4 (&o)[RT][MTW], const f32x4 (&S)[DT][MTW], float inv,
-                                            float *__restrict__ Oh, int row0, int N, bool poison) const {
+                                            OT *__restrict__ Oh, int row0, int N, bool poison) const {
         readout_mma(o, S);
         store_rows(o, inv, Oh, row0, N, poison);
     }
@@ -798,10 +806,10 @@ __device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const 
 // advance the state over the last chunk (for the final state).  Loads run one
 // chunk ahead.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, bool CAUSAL, bool PHI>
+template <typename T, int D, int M, int C, bool CAUSAL, bool PHI, typename OT>
 __device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const T *__restrict__ Qh,
                                         const T *__restrict__ Kh, const T *__restrict__ Vh,
-                                        float *__restrict__ Oh, int N, int c0, int c1, bool kv_staged,
+                                        OT *__restrict__ Oh, int N, int c0, int c1, bool kv_staged,
                                         bool advance_last, Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q0,
                                         f32x4 (&S)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z,
                                         bool poison) {
@@ -937,9 +945,9 @@ __device__ __forceinline__ void finish_call(const FusedWs &ws, unsigned epoch, u
     }
 }
 
-template <typename T, int D, int M, int C, bool PHI = true>
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                                const T *__restrict__ V, float *__restrict__ out,
+                                                                const T *__restrict__ V, OT *__restrict__ out,
                                                                 void *ws_raw, int BH, int N, int G_, int CPS,
                                                                 float *__restrict__ S_out, float *__restrict__ z_out,
                                                                 const float *S_in, const float *z_in) {
@@ -970,7 +978,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const T *Qh = Q + (size_t)bh * N * D;
     const T *Kh = K + (size_t)bh * N * D;
     const T *Vh = V + (size_t)bh * N * M;
-    float *Oh = out + (size_t)bh * N * M;
+    OT *Oh = out + (size_t)bh * N * M;
 
     e.clear_a();
 
@@ -1045,7 +1053,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         const float inv = e.template row_inv<true>();
         e.readout(o, pre, inv, Oh, c0 * C, N, failed);
     } else {
-        phase_b<T, D, M, C, true, PHI>(e, Qh, Kh, Vh, Oh, N, c0, c1, false, G_ == 1 && want_final, stQ, pre, zpre,
+        phase_b<T, D, M, C, true, PHI, OT>(e, Qh, Kh, Vh, Oh, N, c0, c1, false, G_ == 1 && want_final, stQ, pre, zpre,
                                   failed);
         if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
     }
@@ -1082,9 +1090,9 @@ struct OnePassLds {
     static constexpr bool fits = (bytes + 64) * Gc::MIN_WG <= kMaxLds;
 };
 
-template <typename T, int D, int M, int C, bool PHI = true>
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void onepass_causal_kernel(
-    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, float *__restrict__ out,
+    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, OT *__restrict__ out,
     void *ws_raw, int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out,
     const float *S_in, const float *z_in) {
     using Gc = Cfg<T, D, M, C>;
@@ -1117,7 +1125,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const T *Qh = Q + (size_t)bh * N * D;
     const T *Kh = K + (size_t)bh * N * D;
     const T *Vh = V + (size_t)bh * N * M;
-    float *Oh = out + (size_t)bh * N * M;
+    OT *Oh = out + (size_t)bh * N * M;
     const bool last = s == G_ - 1;
     const bool want_final = S_out != nullptr;
 
@@ -1249,9 +1257,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS)) void seg_state_kernel(c
     e.state_store(acc, z, ws + ((size_t)bh * (G_ + 1) + s) * Gc::E);
 }
 
-template <typename T, int D, int M, int C, bool CAUSAL, bool PHI = true>
+template <typename T, int D, int M, int C, bool CAUSAL, bool PHI = true, typename OT = float>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                              const T *__restrict__ V, float *__restrict__ out,
+                                                              const T *__restrict__ V, OT *__restrict__ out,
                                                               const float *__restrict__ ws, int N, int G_, int CPS,
                                                               float *__restrict__ S_out, float *__restrict__ z_out) {
     using Gc = Cfg<T, D, M, C>;
@@ -1273,7 +1281,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     Stage<T, C, D, Cfg<T, D, M, C>::THREADS> stQ;
     stQ.load(Qh, c0 * C, N, e.tid);
     const bool fin = CAUSAL && S_out != nullptr && s == G_ - 1;
-    phase_b<T, D, M, C, CAUSAL, PHI>(e, Qh, K + (size_t)bh * N * D, V + (size_t)bh * N * M, out + (size_t)bh * N * M, N,
+    phase_b<T, D, M, C, CAUSAL, PHI, OT>(e, Qh, K + (size_t)bh * N * D, V + (size_t)bh * N * M, out + (size_t)bh * N * M, N,
                                 c0, c1, false, fin, stQ, S, z, false);
     if (fin) e.state_store(S, z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
 }
@@ -1281,8 +1289,8 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 // ---------------------------------------------------------------------------
 // Host-side launchers (instantiated per element type in la_prefill_*.hip).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, bool PHI = true>
-hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float>
+hipError_t run_fused(const void *Q, const void *K, const void *V, void *out, void *ws, int BH, int N, int G_,
                      int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in, hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
     if constexpr (!Gc::fits) {
@@ -1290,14 +1298,14 @@ hipError_t run_fused(const void *Q, const void *K, const void *V, float *out, vo
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
-        hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C, PHI>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
-                           (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out, S_in, z_in);
+        hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C, PHI, OT>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
+                           (const T *)K, (const T *)V, (OT *)out, ws, BH, N, G_, CPS, S_out, z_out, S_in, z_in);
         return hipGetLastError();
     }
 }
 
-template <typename T, int D, int M, int C, bool PHI = true>
-hipError_t run_onepass(const void *Q, const void *K, const void *V, float *out, void *ws, int BH, int N, int G_,
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float>
+hipError_t run_onepass(const void *Q, const void *K, const void *V, void *out, void *ws, int BH, int N, int G_,
                        int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
                        hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
@@ -1306,8 +1314,8 @@ hipError_t run_onepass(const void *Q, const void *K, const void *V, float *out, 
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((onepass_causal_kernel<T, D, M, C, PHI>), dim3((unsigned)(BH * G_)), dim3(Gc::THREADS), 0,
-                           stream, (const T *)Q, (const T *)K, (const T *)V, out, ws, BH, N, G_, CPS, S_out, z_out,
+        hipLaunchKernelGGL((onepass_causal_kernel<T, D, M, C, PHI, OT>), dim3((unsigned)(BH * G_)), dim3(Gc::THREADS), 0,
+                           stream, (const T *)Q, (const T *)K, (const T *)V, (OT *)out, ws, BH, N, G_, CPS, S_out, z_out,
                            S_in, z_in);
         return hipGetLastError();
     }
@@ -1327,8 +1335,8 @@ hipError_t run_states(const void *K, const void *V, float *ws, int BH, int N, in
     }
 }
 
-template <typename T, int D, int M, int C, bool PHI = true>
-hipError_t run_outputs(const void *Q, const void *K, const void *V, float *out, const float *ws, int BH, int N,
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float>
+hipError_t run_outputs(const void *Q, const void *K, const void *V, void *out, const float *ws, int BH, int N,
                        int G_, int CPS, int causal, float *S_out, float *z_out, hipStream_t stream) {
     using Gc = Cfg<T, D, M, C>;
     if constexpr (!Gc::fits) {
@@ -1337,11 +1345,11 @@ hipError_t run_outputs(const void *Q, const void *K, const void *V, float *out, 
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const dim3 grid((unsigned)(BH * G_)), block(Gc::THREADS);
         if (causal)
-            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, true, PHI>), grid, block, 0, stream, (const T *)Q,
-                               (const T *)K, (const T *)V, out, ws, N, G_, CPS, S_out, z_out);
+            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, true, PHI, OT>), grid, block, 0, stream, (const T *)Q,
+                               (const T *)K, (const T *)V, (OT *)out, ws, N, G_, CPS, S_out, z_out);
         else
-            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, false, PHI>), grid, block, 0, stream, (const T *)Q,
-                               (const T *)K, (const T *)V, out, ws, N, G_, CPS, S_out, z_out);
+            hipLaunchKernelGGL((seg_output_kernel<T, D, M, C, false, PHI, OT>), grid, block, 0, stream, (const T *)Q,
+                               (const T *)K, (const T *)V, (OT *)out, ws, N, G_, CPS, S_out, z_out);
         return hipGetLastError();
     }
 }

@@ -57,35 +57,44 @@ hipError_t fill_zero(float *p, size_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+hipError_t prefill_fused(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
                          void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
                          const float *z_in, hipStream_t stream) {
-    return dtype == kDtypeF32    ? prefill_fused_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
-           : dtype == kDtypeBf16 ? prefill_fused_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
-                                 : prefill_fused_feat(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
+    if (dtype == (kDtypeBf16 | kOutBf16))
+        return prefill_fused_bf16o(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
+    float *o32 = static_cast<float *>(out);
+    return dtype == kDtypeF32    ? prefill_fused_f32(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+           : dtype == kDtypeBf16 ? prefill_fused_bf16(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+                                 : prefill_fused_feat(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
 }
 
-hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+hipError_t prefill_onepass(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
                            void *ws, int BH, int N, int G, int CPS, float *S_out, float *z_out, const float *S_in,
                          const float *z_in, hipStream_t stream) {
-    return dtype == kDtypeF32    ? prefill_onepass_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
-           : dtype == kDtypeBf16 ? prefill_onepass_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
-                                 : prefill_onepass_feat(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
+    if (dtype == (kDtypeBf16 | kOutBf16))
+        return prefill_onepass_bf16o(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
+    float *o32 = static_cast<float *>(out);
+    return dtype == kDtypeF32    ? prefill_onepass_f32(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+           : dtype == kDtypeBf16 ? prefill_onepass_bf16(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream)
+                                 : prefill_onepass_feat(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, S_out, z_out, S_in, z_in, stream);
 }
 
 bool prefill_onepass_supported(int dtype, int D, int M, int C) {
+    dtype &= ~kOutBf16;  // the output type does not change the kernel's shape limits
     return dtype == kDtypeF32    ? prefill_onepass_supported_f32(D, M, C)
            : dtype == kDtypeBf16 ? prefill_onepass_supported_bf16(D, M, C)
                                  : prefill_onepass_supported_feat(D, M, C);
 }
 
 size_t prefill_lds_bytes(int dtype, int D, int M, int C) {
+    dtype &= ~kOutBf16;  // the output type does not change the kernel's shape limits
     return dtype == kDtypeF32    ? prefill_lds_bytes_f32(D, M, C)
            : dtype == kDtypeBf16 ? prefill_lds_bytes_bf16(D, M, C)
                                  : prefill_lds_bytes_feat(D, M, C);
 }
 
 bool prefill_supported(int dtype, int D, int M, int C) {
+    dtype &= ~kOutBf16;  // the output type does not change the kernel's shape limits
     return dtype == kDtypeF32    ? prefill_supported_f32(D, M, C)
            : dtype == kDtypeBf16 ? prefill_supported_bf16(D, M, C)
                                  : prefill_supported_feat(D, M, C);
@@ -93,17 +102,21 @@ bool prefill_supported(int dtype, int D, int M, int C) {
 
 hipError_t prefill_states(int dtype, int D, int M, int C, const void *K, const void *V, float *ws, int BH, int N,
                           int G, int CPS, int nstates, hipStream_t stream) {
+    dtype &= ~kOutBf16;  // the states do not depend on the output type
     return dtype == kDtypeF32    ? prefill_states_f32(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream)
            : dtype == kDtypeBf16 ? prefill_states_bf16(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream)
                                  : prefill_states_feat(D, M, C, K, V, ws, BH, N, G, CPS, nstates, stream);
 }
 
-hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, float *out,
+hipError_t prefill_outputs(int dtype, int D, int M, int C, const void *Q, const void *K, const void *V, void *out,
                            const float *ws, int BH, int N, int G, int CPS, int causal, float *S_out, float *z_out,
                            hipStream_t stream) {
-    return dtype == kDtypeF32    ? prefill_outputs_f32(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
-           : dtype == kDtypeBf16 ? prefill_outputs_bf16(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
-                                 : prefill_outputs_feat(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream);
+    if (dtype == (kDtypeBf16 | kOutBf16))
+        return prefill_outputs_bf16o(D, M, C, Q, K, V, out, ws, BH, N, G, CPS, causal, S_out, z_out, stream);
+    float *o32 = static_cast<float *>(out);
+    return dtype == kDtypeF32    ? prefill_outputs_f32(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
+           : dtype == kDtypeBf16 ? prefill_outputs_bf16(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, causal, S_out, z_out, stream)
+                                 : prefill_outputs_feat(D, M, C, Q, K, V, o32, ws, BH, N, G, CPS, causal, S_out, z_out, stream);
 }
 
 // ---------------------------------------------------------------------------

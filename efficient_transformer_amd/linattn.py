@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(PKG, "liblinattn.so")
 
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
 LA_F32, LA_BF16, LA_F32_FEATURES = 0, 1, 2
+LA_OUT_BF16 = 16
 LA_FEATURE_ELU, LA_FEATURE_PRF, LA_FEATURE_TRF = 0, 1, 2
 LA_FEATURE_NORMALIZE = 1
 
@@ -111,6 +112,28 @@ def _dtype_code(t, features: bool = False) -> int:
     raise TypeError(f"unsupported input dtype {t.dtype} (float32 or bfloat16)")
 
 
+def _out_code(dt, out, out_dtype, shape, dev):
+    """The output tensor (allocated when None) and the element-type code with the
+    bf16-output flag when out is bfloat16 (bf16 inputs only)."""
+    import torch
+    want = out.dtype if out is not None else (out_dtype or torch.float32)
+    if want not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be float32 or bfloat16")
+    if want == torch.bfloat16:
+        if dt != LA_BF16:
+            raise TypeError("a bfloat16 output needs bfloat16 inputs")
+        dt |= LA_OUT_BF16
+    if out is None:
+        out = torch.empty(shape, dtype=want, device=dev)
+    _require(out, "out", shape, want, dev)
+    return out, dt
+
+
+def _torch_float32():
+    import torch
+    return torch.float32
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -172,13 +195,14 @@ def _cached_workspace(nbytes, device, stream, key):
 
 
 def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_out=None, z_out=None,
-                    stream=None, features=False):
+                    stream=None, features=False, out_dtype=None):
     """Parallel-mode attention: Q, K [B,H,N,D], V [B,H,N,M] (float32 or bfloat16) -> out [B,H,N,M] float32.
 
     With S_out [B,H,D,M] and z_out [B,H,D] (float32) the final state is written too.
     A given `workspace` must have been zeroed (workspace_init) for this plan; by
     default a cached, zeroed one is used.  features=True: Q and K are float32
     features (feature_map), no feature map is applied and D is the feature dimension.
+    A bfloat16 `out` (or out_dtype=torch.bfloat16) with bfloat16 inputs writes bf16 outputs.
     """
     import torch
     if Q.dim() != 4:
@@ -190,9 +214,7 @@ def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_o
     _require(K, "K", (B, H, N, D), Q.dtype, dev)
     _require(V, "V", (B, H, N, M), Q.dtype, dev)
     dt = _dtype_code(Q, features)
-    if out is None:
-        out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
-    _require(out, "out", (B, H, N, M), torch.float32, dev)
+    out, dt = _out_code(dt, out, out_dtype, (B, H, N, M), dev)
     if (S_out is None) != (z_out is None):
         raise ValueError("give both S_out and z_out, or neither")
     if S_out is not None:
@@ -217,21 +239,21 @@ def fused_workspace_bytes(B, H, D, M, segments) -> int:
 
 
 def forward_fused(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None,
-                  S_in=None, z_in=None, features=False):
+                  S_in=None, z_in=None, features=False, out_dtype=None):
     """The causal two-phase fused kernel with an explicit plan (chunk, segments)."""
     return _forward_explicit("la_forward_fused", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream,
-                             S_in, z_in, features)
+                             S_in, z_in, features, out_dtype)
 
 
 def forward_onepass(Q, K, V, chunk, segments, out=None, workspace=None, S_out=None, z_out=None, stream=None,
-                    S_in=None, z_in=None, features=False):
+                    S_in=None, z_in=None, features=False, out_dtype=None):
     """The causal one-pass kernel with an explicit plan (segments of at most 4 chunks)."""
     return _forward_explicit("la_forward_onepass", Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream,
-                             S_in, z_in, features)
+                             S_in, z_in, features, out_dtype)
 
 
 def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_out=None, z_out=None, stream=None,
-                     features=False):
+                     features=False, out_dtype=None):
     """Causal attention continuing from the carried state (S_in [B,H,D,M], z_in [B,H,D], fp32)."""
     import torch
     B, H, N, D = Q.shape
@@ -242,10 +264,9 @@ def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_o
     if S_in is not None:
         _require(S_in, "S_in", (B, H, D, M), torch.float32, dev)
         _require(z_in, "z_in", (B, H, D), torch.float32, dev)
-    if out is None:
-        out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
     dt = _dtype_code(Q, features)
-    C, G, need = forward_plan(B, H, N, D, M, True, dt, chunk)
+    out, dt = _out_code(dt, out, out_dtype, (B, H, N, M), dev)
+    C, G, need = forward_plan(B, H, N, D, M, True, dt & ~LA_OUT_BF16, chunk)
     if workspace is None and need > 0:
         workspace = _cached_workspace(need, dev, stream, ("chunked", B * H, N, D, M, True, dt, C, G))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -256,21 +277,21 @@ def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_o
     return out
 
 
-def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream, S_in, z_in, features):
-    import torch
+def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_out, stream, S_in, z_in, features,
+                      out_dtype=None):
     B, H, N, D = Q.shape
     M = V.shape[-1]
     dev = Q.device
     _require(K, "K", (B, H, N, D), Q.dtype, dev)
     _require(V, "V", (B, H, N, M), Q.dtype, dev)
-    if out is None:
-        out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
+    dt = _dtype_code(Q, features)
+    out, dt = _out_code(dt, out, out_dtype, (B, H, N, M), dev)
     need = fused_workspace_bytes(B, H, D, M, segments)
     if workspace is None and need > 0:
-        workspace = _cached_workspace(need, dev, stream, (name, B * H, N, D, M, _dtype_code(Q, features), chunk,
+        workspace = _cached_workspace(need, dev, stream, (name, B * H, N, D, M, dt & ~LA_OUT_BF16, chunk,
                                                           segments))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(Q, features), chunk,
+    st = getattr(lib(), name)(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, dt, chunk,
                               segments, _ptr(S_in), _ptr(z_in), _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out),
                               _stream(stream, dev))
     _check(st, name)
@@ -295,8 +316,13 @@ def segment_outputs(Q, K, V, out, ws, chunk, segments, causal=True, S_out=None, 
                     features=False):
     B, H, N, D = Q.shape
     M = out.shape[-1]
+    dt = _dtype_code(Q, features)
+    if out.dtype != _torch_float32():
+        if dt != LA_BF16:
+            raise TypeError("a bfloat16 output needs bfloat16 inputs")
+        dt |= LA_OUT_BF16
     st = lib().la_segment_outputs(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
-                                  B, H, N, D, M, int(bool(causal)), _dtype_code(Q, features), chunk, segments,
+                                  B, H, N, D, M, int(bool(causal)), dt, chunk, segments,
                                   _ptr(S_out), _ptr(z_out), _stream(stream, Q.device))
     _check(st, "la_segment_outputs")
 

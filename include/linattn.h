@@ -19,7 +19,8 @@
  *     caller; the library never allocates, frees or keeps a pointer.
  *     Q, K: [B][H][N][D]; V, out: [B][H][N][M]; S: [B][H][D][M]; z: [B][H][D].
  *   - Input element type: LA_F32 (float) or LA_BF16 (bfloat16 bit patterns,
- *     uint16).  Arithmetic and accumulation are fp32; out, S and z are fp32.
+ *     uint16).  Arithmetic and accumulation are fp32; out, S and z are fp32
+ *     (out bf16 with LA_BF16 | LA_OUT_BF16, see la_dtype).
  *   - D and M must each be 16, 32, 64 or 128.  All device pointers must be
  *     16-byte aligned.  Outputs must not alias inputs.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
@@ -58,7 +59,12 @@ enum la_status {
  * map, D is the feature dimension, and V is fp32.  Accepted by the forward
  * entry points, the segment stages and the decode entry points; not by
  * la_backward_chunked (LA_ERR_UNSUPPORTED) or the softmax scan. */
-enum la_dtype { LA_F32 = 0, LA_BF16 = 1, LA_F32_FEATURES = 2 };
+/* LA_BF16 | LA_OUT_BF16: bf16 inputs and bf16 outputs.  The forward entry
+ * points (la_forward_chunked, la_forward_continue, la_forward_fused,
+ * la_forward_onepass, la_segment_outputs; la_segment_states ignores the flag)
+ * then write out as bf16 bit patterns, each the fp32 result rounded to nearest
+ * even; arithmetic, S and z stay fp32.  Other entry points reject it. */
+enum la_dtype { LA_F32 = 0, LA_BF16 = 1, LA_F32_FEATURES = 2, LA_OUT_BF16 = 16 };
 
 /* Human-readable name of a status code (static string; never NULL). */
 LA_API const char *la_status_str(int status);
@@ -111,7 +117,7 @@ LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_
  * N = 0 or B*H = 0 is a valid empty call (with N = 0 and S_out given, the state
  * is written as zeros).
  */
-LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float *out,
+LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, void *out,
                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                               int causal, int dtype, int chunk_req,
                               void *workspace, size_t workspace_bytes,
@@ -131,7 +137,7 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, float
  * la_forward_chunked with causal = 1 (la_forward_workspace_bytes(..., 1, ...)).
  * With N = 0, S_out / z_out receive a copy of S_in / z_in (zeros without them).
  */
-LA_API int la_forward_continue(const void *Q, const void *K, const void *V, float *out,
+LA_API int la_forward_continue(const void *Q, const void *K, const void *V, void *out,
                                int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                                int dtype, int chunk_req,
                                const float *S_in, const float *z_in,
@@ -150,7 +156,7 @@ LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stre
  * initialised as for la_forward_chunked.  S_in / z_in as for la_forward_continue
  * (NULL: start from zero); S_out / z_out as for la_forward_chunked.
  */
-LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *out,
+LA_API int la_forward_fused(const void *Q, const void *K, const void *V, void *out,
                             int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                             int dtype, int chunk, int segments,
                             const float *S_in, const float *z_in,
@@ -170,7 +176,7 @@ LA_API int la_forward_fused(const void *Q, const void *K, const void *V, float *
  * la_forward_fused (the two kernels share the format, not a live workspace).
  * S_in / z_in as for la_forward_continue (NULL: start from zero).
  */
-LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, float *out,
+LA_API int la_forward_onepass(const void *Q, const void *K, const void *V, void *out,
                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                               int dtype, int chunk, int segments,
                               const float *S_in, const float *z_in,
@@ -203,7 +209,7 @@ LA_API int la_segment_states(const void *K, const void *V, float *ws, size_t ws_
                              int dtype, int chunk, int segments, int nstates, void *stream);
 LA_API int la_segment_scan(float *ws, size_t ws_bytes, int64_t B, int64_t H, int64_t D, int64_t M,
                            int segments, int nstates, float *S_out, float *z_out, void *stream);
-LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, float *out,
+LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, void *out,
                               const float *ws, size_t ws_bytes,
                               int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                               int causal, int dtype, int chunk, int segments,

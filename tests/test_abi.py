@@ -272,3 +272,19 @@ def test_feature_inputs_dtype(L):
                                None) == L.LA_ERR_INVALID_ARG
     assert lib.la_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 48, 64, L.LA_F32_FEATURES,
                               None) == L.LA_ERR_UNSUPPORTED  # accepted type, unsupported D
+
+
+def test_bf16_output_flag(L):
+    """LA_BF16 | LA_OUT_BF16 plans like LA_BF16; the flag is refused on other input types and by
+    the entry points that do not write prefill outputs."""
+    lib = L.lib()
+    for D in (16, 64, 128):
+        for M in (16, 64, 128):
+            assert L.forward_plan(2, 3, 5000, D, M, 1, L.LA_BF16 | L.LA_OUT_BF16, 0) == \
+                L.forward_plan(2, 3, 5000, D, M, 1, L.LA_BF16, 0)
+    for bad in (L.LA_F32 | L.LA_OUT_BF16, L.LA_F32_FEATURES | L.LA_OUT_BF16):
+        assert _fwd(L, Q=FAKE, K=FAKE, V=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30, dtype=bad) == L.LA_ERR_INVALID_ARG
+    assert lib.la_backward_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 100, 64, 64,
+                                   L.LA_BF16 | L.LA_OUT_BF16, FAKE, 1 << 30, None) == L.LA_ERR_UNSUPPORTED
+    assert lib.la_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, L.LA_BF16 | L.LA_OUT_BF16,
+                              None) == L.LA_ERR_INVALID_ARG
