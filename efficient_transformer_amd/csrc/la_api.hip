@@ -9,6 +9,13 @@ namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
 
+// la_decode_steps: the chunked kernels beat the register recurrence from about
+// 12 tokens per head for states of 4096+ values, 16 tokens for 2048+, 32 for any
+// (crossovers measured on MI355X with 2048 heads).
+bool decode_steps_chunked(int64_t T, int64_t D, int64_t M) {
+    return (T >= 12 && D * M >= 4096) || (T >= 16 && D * M >= 2048) || T >= 32;
+}
+
 bool dim_ok(int64_t x) { return x == 16 || x == 32 || x == 64 || x == 128; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -526,8 +533,24 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
     if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    return hip_status(la::decode_steps(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), (int)T,
-                                       as_stream(stream)));
+    hipStream_t s = as_stream(stream);
+    // From about a dozen tokens on, the chunked causal kernels (MFMA tiles, the state
+    // carried in and out in place) beat the register recurrence.  They are used when
+    // every head is one segment, i.e. when no workspace is needed.
+    // (fp32 inputs only: with bf16 inputs the chunked kernels round MFMA operands to
+    // bf16, while this entry point keeps fp32 arithmetic for both input types)
+    if (dtype != LA_BF16 && decode_steps_chunked(T, D, M)) {
+        Plan p;
+        if (make_plan(B, H, T, D, M, 1, dtype, 16, &p) == LA_OK && p.ws_bytes == 0 && p.segments == 1) {
+            const int BH = (int)(B * H), Di = (int)D, Mi = (int)M;
+            hipError_t e = p.onepass ? la::prefill_onepass(dtype, Di, Mi, 16, q, k, v, out, nullptr, BH, (int)T, 1,
+                                                           p.chunks_per_segment, S, z, S, z, s)
+                                     : la::prefill_fused(dtype, Di, Mi, 16, q, k, v, out, nullptr, BH, (int)T, 1,
+                                                         p.chunks_per_segment, S, z, S, z, s);
+            return hip_status(e);
+        }
+    }
+    return hip_status(la::decode_steps(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), (int)T, s));
 }
 
 // ---- feature maps ----------------------------------------------------------

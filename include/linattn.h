@@ -262,7 +262,12 @@ LA_API int la_backward_chunked(const void *Q, const void *K, const void *V, cons
  * la_decode_step with q, k, v, out of token t, up to rounding.
  * q, k: [B][H][T][D]; v, out: [B][H][T][M]; S, z updated in place.
  * T = 0 is a valid empty call.  Same element types, alignment and status
- * codes as la_decode_step.
+ * codes as la_decode_step.  Short calls run the recurrence with the state in
+ * registers; longer ones with fp32 inputs (12+ tokens for states of 4096+
+ * values, 16+ for 2048+, 32+ for any, when every head is one segment of the
+ * forward planner) run the chunked causal kernel continuing from S, z in place
+ * (la_forward_continue's fp32 arithmetic on MFMA tiles), which is faster there.
+ * Arithmetic is fp32 for both input types.
  */
 LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, const void *v,
                            float *out, int64_t B, int64_t H, int64_t T, int64_t D, int64_t M,

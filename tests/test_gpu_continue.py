@@ -153,6 +153,27 @@ def test_decode_steps_parity(ea, dtype, D, M, T):
     assert whole_rel(z.cpu().numpy(), z_ref) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype,D,M,T", [("f32", 64, 64, 12), ("f32", 64, 64, 33), ("f32", 128, 128, 12),
+                                         ("f32", 16, 128, 16), ("f32", 32, 32, 16), ("f32", 16, 16, 32),
+                                         ("f32", 128, 64, 40), ("bf16", 64, 64, 16)])
+def test_decode_steps_chunked_path(ea, dtype, D, M, T):
+    """512 heads: one segment per head, so fp32 calls of 12+ tokens run the chunked
+    kernel with the state carried in and out in place (bf16 inputs stay on the fp32
+    register recurrence)."""
+    B, H = 64, 8
+    S0, z0 = carried_state(B, H, D, M, 20, 32)
+    q, k, v = synthetic.prefill_inputs(pcfg(dtype, B, H, T, D, M), 33)
+    S = torch.from_numpy(S0).to(DEV)
+    z = torch.from_numpy(z0).to(DEV)
+    out = ea.decode_steps(S, z, to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype))
+    torch.cuda.synchronize()
+    ref, S_ref, z_ref = oracle.causal_from(synthetic.as_f64(q, dtype), synthetic.as_f64(k, dtype),
+                                           synthetic.as_f64(v, dtype), S0.astype(np.float64), z0.astype(np.float64))
+    assert rowwise_rel(out.cpu().numpy(), ref) <= 1e-4
+    assert whole_rel(S.cpu().numpy(), S_ref) <= 1e-5
+    assert whole_rel(z.cpu().numpy(), z_ref) <= 1e-5
+
+
 def test_decode_steps_equals_single_steps(ea):
     """T steps in one call and T calls of la_decode_step agree to rounding."""
     B, H, D, M, T = 4, 2, 64, 64, 33
