@@ -27,7 +27,7 @@ __host__ __device__ inline size_t fused_ws_bytes(long BH, int G, int E) {
 
 // Softmax scan (la_softmax_scan.hip): one state = M value sums + max + sum,
 // padded to whole 256-byte blocks; workspace = header + flags + 2 states per
-// segment of softmax_scan_rows(M) rows.
+// group of softmax_scan_rows(M) rows.
 __host__ __device__ constexpr int scan_slot_floats(int M) { return (M + 2 + 63) / 64 * 64; }
 __host__ __device__ inline size_t scan_ws_bytes(long items, int M) {
     return (kWsHeaderWords + fused_flag_words(items)) * 4 + 2 * (size_t)items * (size_t)scan_slot_floats(M) * 4;

@@ -11,18 +11,27 @@
 //   m = max(m1, m2).
 //
 // Scan kernel: one wavefront per segment of R = 32 rows of one head (lanes are
-// value columns).  The wavefront
-//   1. stages its K tile in LDS (coalesced) and forms s_i, one row per lane;
-//   2. runs the recurrence over its rows, keeping every row's local state
-//      (w_i in the register that held v_i; m_i, u_i in lane i);
-//   3. publishes its segment state, looks back over the earlier segments of the
-//      head (decoupled look-back, the same flag / epoch protocol as the prefill
-//      kernels; a state is only M + 2 floats) and publishes its inclusive state;
+// value columns), four consecutive segments per workgroup (a group).  The
+// wavefront
+//   1. issues the loads of its K tile and V rows together, stages K in LDS and
+//      forms s_i, one row per lane;
+//   2. forms the running max, the scale factors and u_i for all rows at once
+//      (shuffle scans over lanes = rows), then w_i row after row with one fma
+//      per row and column, keeping every row's local state (w_i in the
+//      register that held v_i; m_i, u_i in lane i);
+//   3. writes its segment state to LDS; wavefront 0 combines the group's four
+//      states, publishes the group state, looks back over the earlier groups of
+//      the head (decoupled look-back, the same flag / epoch protocol as the
+//      prefill kernels; a state is only M + 2 floats), publishes the group's
+//      inclusive state and passes the prefix back through LDS; each wavefront
+//      adds the states of the group's earlier segments;
 //   4. writes out_i = prefix + local state of row i, normalised.
-// The last segment of every head counts itself done after its look-back; the
-// last head to count advances the epoch (as in the prefill kernels).
-// Workspace: 64 header words, one flag word per segment (padded to 64 words),
-// then the aggregate and the inclusive state of every segment (SP floats each).
+// One look-back per group of 128 rows instead of per segment: a quarter of the
+// chain length and of the published states.  The last group of every head
+// counts itself done after its look-back; the last head to count advances the
+// epoch (as in the prefill kernels).
+// Workspace: 64 header words, one flag word per group (padded to 64 words),
+// then the aggregate and the inclusive state of every group (SP floats each).
 #include <math.h>
 
 #include "la_device.hpp"
@@ -47,238 +56,335 @@ template <typename T>
 __device__ __forceinline__ float ld1(const T *p) {
     return to_f32(*p);
 }
+template <typename T>
+__device__ __forceinline__ f32x4 ld4(const T *p);
+template <>
+__device__ __forceinline__ f32x4 ld4<float>(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+template <>
+__device__ __forceinline__ f32x4 ld4<bf16>(const bf16 *p) {
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
 
 template <typename T, int D, int M>
 __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
     const T *__restrict__ q, const T *__restrict__ K, const T *__restrict__ V, float *__restrict__ out,
-    void *ws_raw, int BH, int N, int NS, float *__restrict__ m_out, float *__restrict__ u_out,
+    void *ws_raw, int BH, int N, int NS, int NG, float *__restrict__ m_out, float *__restrict__ u_out,
     float *__restrict__ w_out) {
     using G = ScanCfg<D, M>;
     constexpr int R = G::R, CPL = G::CPL;
     __shared__ __attribute__((aligned(16))) float sk[kScanWaves][R * G::LK];
     __shared__ float sq[kScanWaves][D];
+    __shared__ float sst[kScanWaves][M + 2];  // each segment's local state (w, m, u)
+    __shared__ float spre[M + 3];             // the group's prefix (w, m, u) and a failure flag
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const long items = (long)BH * NS;
-    const long gi = (long)blockIdx.x * kScanWaves + w;
-    if (gi >= items) return;  // whole wavefronts only; no workgroup barrier below
-    const int bh = (int)(gi % BH), seg = (int)(gi / BH);
+    const int bh = (int)(blockIdx.x % (unsigned)BH), grp = (int)(blockIdx.x / (unsigned)BH);
+    const int seg = grp * kScanWaves + w;
     const int row0 = seg * R;
-    const int nrows = min(R, N - row0);
+    const int nrows = max(0, min(R, N - row0));  // 0: a segment past the end (identity state)
     const bool last = seg == NS - 1;
+    const bool last_grp = grp == NG - 1;
 
     unsigned *hdr = static_cast<unsigned *>(ws_raw);
+    const long items = (long)BH * NG;
     unsigned *flags = hdr + kWsHeaderWords;
     float *agg = reinterpret_cast<float *>(flags + fused_flag_words(items));
     float *incl = agg + (size_t)items * G::SP;
     unsigned epoch = 0;
-    if (NS > 1) epoch = __hip_atomic_load(&hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (NG > 1 && w == 0) epoch = __hip_atomic_load(&hdr[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned ep = (epoch & 0x3fffffffu) << 2;
 
-    // 1. scores: K tile through LDS (rows past N are zero), q in LDS
-    float *tile = sk[w];
-    const T *Kh = K + ((size_t)bh * N + row0) * D;
-    for (int x = lane; x < R * D; x += 64) {
-        const int r = x / D, d = x % D;
-        tile[r * G::LK + d] = r < nrows ? ld1(Kh + (size_t)r * D + d) : 0.0f;
-    }
-    for (int d = lane; d < D; d += 64) sq[w][d] = ld1(q + (size_t)bh * D + d);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_wave_barrier();
-    float s = -INFINITY;  // s of row `lane`
-    if (lane < nrows) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int d4 = 0; d4 < D / 4; ++d4) {
-            const f32x4 kv = *reinterpret_cast<const f32x4 *>(tile + lane * G::LK + 4 * d4);
-            const f32x4 qv = *reinterpret_cast<const f32x4 *>(sq[w] + 4 * d4);
-            acc += kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
-        }
-        s = acc;
-    }
-
-    // 2. local recurrence over the segment's rows; lanes = value columns
-    const T *Vh = V + ((size_t)bh * N + row0) * M;
     float wv[R][CPL];  // v_i on load, then the local w_i
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int col = lane + 64 * c;
-            wv[i][c] = (col < M && i < nrows) ? ld1(Vh + (size_t)i * M + col) : 0.0f;
-        }
-    float m = -INFINITY, u = 0.0f;
-    float wl[CPL];
+    float m = -INFINITY, u = 0.0f, wl[CPL];
+    float my_m = -INFINITY, my_u = 0.0f;  // lane i: the local state (m_i, u_i) of row i
 #pragma unroll
     for (int c = 0; c < CPL; ++c) wl[c] = 0.0f;
-    float my_m = -INFINITY, my_u = 0.0f;  // lane i: the local state of row i
+    if (nrows > 0) {
+        // 1. loads: the K tile (16-byte loads, staged in LDS) and the V rows (lane =
+        //    column) are all issued before any of them is used; rows past N reload
+        //    row nrows - 1 and are masked below.
+        float *tile = sk[w];
+        const T *Kh = K + ((size_t)bh * N + row0) * D;
+        const T *Vh = V + ((size_t)bh * N + row0) * M;
+        constexpr int KL = R * D / 4 / 64;  // 4-element K loads per lane
+        f32x4 kreg[KL];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        const float si = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), i));
-        if (si != -INFINITY) {  // uniform: rows past N leave the state as it is
-            const float mn = fmaxf(m, si);
-            const float a = __expf(m - mn), b = __expf(si - mn);
-            u = u * a + b;
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) wl[c] = wl[c] * a + b * wv[i][c];
-            m = mn;
+        for (int x = 0; x < KL; ++x) {
+            const int e = lane + 64 * x, r = e / (D / 4), d = (e % (D / 4)) * 4;
+            kreg[x] = ld4(Kh + (size_t)min(r, nrows - 1) * D + d);
         }
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) wv[i][c] = wl[c];
-        if (lane == i) {
-            my_m = m;
-            my_u = u;
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int col = min(lane + 64 * c, M - 1);
+                wv[i][c] = ld1(Vh + (size_t)min(i, nrows - 1) * M + col);
+            }
+        for (int d = lane; d < D; d += 64) sq[w][d] = ld1(q + (size_t)bh * D + d);
+#pragma unroll
+        for (int x = 0; x < KL; ++x) {
+            const int e = lane + 64 * x, r = e / (D / 4), d = (e % (D / 4)) * 4;
+            *reinterpret_cast<f32x4 *>(tile + r * G::LK + d) = kreg[x];
         }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // LDS writes done (vmcnt left alone: V may be in flight)
+        __builtin_amdgcn_wave_barrier();
+        float s = -INFINITY;  // s of row `lane`
+        if (lane < nrows) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int d4 = 0; d4 < D / 4; ++d4) {
+                const f32x4 kv = *reinterpret_cast<const f32x4 *>(tile + lane * G::LK + 4 * d4);
+                const f32x4 qv = *reinterpret_cast<const f32x4 *>(sq[w] + 4 * d4);
+                acc += kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
+            }
+            s = acc;
+        }
+
+        // 2. the segment's recurrence, with everything that does not depend on v
+        //    done in parallel over rows (lane i = row i): the running max m_i (prefix
+        //    max), the factors a_i = e^(m_{i-1} - m_i) and b_i = e^(s_i - m_i) of
+        //    u_i = a_i u_{i-1} + b_i, and u_i itself (a scan of that affine map).
+        //    Only w_i = a_i w_{i-1} + b_i v_i runs row after row, one fma per row
+        //    and column.  Rows past N have s = -inf: a = 1, b = 0 keep the state.
+        float mx = s;
+#pragma unroll
+        for (int o = 1; o < R; o <<= 1) {
+            const float t = __shfl_up(mx, o, 64);
+            if (lane >= o) mx = fmaxf(mx, t);
+        }
+        const float up = __shfl_up(mx, 1, 64);  // every lane takes part in the shuffle
+        const float mprev = lane == 0 ? -INFINITY : up;
+        const float fa = mx == -INFINITY ? 1.0f : __expf(mprev - mx);
+        const float fb = mx == -INFINITY ? 0.0f : __expf(s - mx);
+        float sa = fa, su = fb;  // composition of the maps of rows <= lane: u -> sa u + su
+#pragma unroll
+        for (int o = 1; o < R; o <<= 1) {
+            const float pa = __shfl_up(sa, o, 64), pb = __shfl_up(su, o, 64);
+            if (lane >= o) {
+                su = sa * pb + su;
+                sa = sa * pa;
+            }
+        }
+        my_m = mx;
+        my_u = su;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float ai = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fa), i));
+            const float bi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fb), i));
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                wl[c] = __builtin_fmaf(wl[c], ai, bi * wv[i][c]);
+                wv[i][c] = wl[c];
+            }
+        }
+        m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), R - 1));
+        u = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, su), R - 1));
     }
 
-    // 3. publish the segment state; look back for the prefix
-    const size_t my = (size_t)gi;
+    // (pm, pu, pw) = (pm, pu, pw) + (sm, su, sw): the state comes after the prefix
     float pm = -INFINITY, pu = 0.0f, pw[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) pw[c] = 0.0f;
-    bool failed = false;
-    auto store_state = [&](float *slot, float sm, float su, const float *sw) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int col = lane + 64 * c;
-            if (col < M) __hip_atomic_store(slot + col, sw[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (lane == 0) {
-            __hip_atomic_store(slot + M, sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(slot + M + 1, su, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    };
-    auto publish = [&](unsigned value) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0) __hip_atomic_store(&flags[my], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    // prefix (pm, pu, pw) = prefix + state (sm, su, sw): the state comes after the prefix
-    auto add_back = [&](float sm, float su, const float *sw) {
+    auto add_back = [&](float sm, float sus, const float *sw) {
         const float mn = fmaxf(sm, pm);
         if (mn != -INFINITY) {
             const float a = __expf(pm - mn), b = __expf(sm - mn);
-            pu = pu * a + su * b;
+            pu = pu * a + sus * b;
 #pragma unroll
             for (int c = 0; c < CPL; ++c) pw[c] = pw[c] * a + sw[c] * b;
             pm = mn;
         }
     };
-    // load up to LB states at once (their latencies overlap), then combine in order
-    constexpr int LB = 16;
-    auto add_slots = [&](const float *first, int j0, int j1) {  // first, then agg of segments j0 .. j1-1
-        {
-            float sw[CPL];
+
+    // 3. the segments of the group exchange their states through LDS; one
+    //    wavefront publishes the group's state and looks back over the earlier
+    //    groups of the head (decoupled look-back); the prefix comes back through LDS.
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) sw[c] = lane + 64 * c < M ? first[lane + 64 * c] : 0.0f;
-            add_back(first[M], first[M + 1], sw);
-        }
-        for (int jb = j0; jb < j1; jb += LB) {
-            float tm[LB], tu[LB], tw[LB][CPL];
-#pragma unroll
-            for (int k = 0; k < LB; ++k) {
-                const int j = jb + k < j1 ? jb + k : jb;
-                const float *slot = agg + ((size_t)j * BH + bh) * G::SP;
-                tm[k] = slot[M];
-                tu[k] = slot[M + 1];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) tw[k][c] = lane + 64 * c < M ? slot[lane + 64 * c] : 0.0f;
-            }
-#pragma unroll
-            for (int k = 0; k < LB; ++k)
-                if (jb + k < j1) add_back(tm[k], tu[k], tw[k]);
-        }
-    };
-    if (NS > 1 && !last) {
-        store_state(agg + my * G::SP, m, u, wl);
-        publish(ep | 1u);
+    for (int c = 0; c < CPL; ++c)
+        if (lane + 64 * c < M) sst[w][lane + 64 * c] = wl[c];
+    if (lane == 0) {
+        sst[w][M] = m;
+        sst[w][M + 1] = u;
     }
-    if (NS > 1 && seg > 0) {
-        const unsigned *fl = flags;  // flag of segment j of this head: item j * BH + bh
-        int base = seg - 1;
-        int jstar = -1;
-        long spins = 0;
-        while (true) {
-            const int j = base - lane;
-            unsigned f = 0u;
-            if (j >= 0) f = __hip_atomic_load(fl + (size_t)j * BH + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool ok = j >= 0 && (f & ~3u) == ep && (f & 3u) != 0u;
-            const bool inc = ok && ((f & 3u) == 2u || j == 0);
-            const unsigned long long okm = __ballot(ok), incm = __ballot(inc);
-            if (incm != 0ull) {
-                const int first = __builtin_ctzll(incm);
-                const unsigned long long need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
-                if ((okm & need) == need) {
-                    jstar = base - first;
+    __syncthreads();
+    auto add_lds = [&](const float *st) {
+        float sw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) sw[c] = lane + 64 * c < M ? st[lane + 64 * c] : 0.0f;
+        add_back(st[M], st[M + 1], sw);
+    };
+    bool failed = false;
+    if (NG > 1 && w == 0) {
+        // the group's aggregate: its segments in order
+        for (int k = 0; k < kScanWaves; ++k) add_lds(sst[k]);
+        const float gm = pm, gu = pu;
+        float gw[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) gw[c] = pw[c];
+        const size_t my = (size_t)grp * BH + bh;  // item of this group
+        auto store_state = [&](float *slot, float sm, float sus, const float *sw) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int col = lane + 64 * c;
+                if (col < M) __hip_atomic_store(slot + col, sw[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (lane == 0) {
+                __hip_atomic_store(slot + M, sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(slot + M + 1, sus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        auto publish = [&](unsigned value) {
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            if (lane == 0) __hip_atomic_store(&flags[my], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        if (!last_grp) {
+            store_state(agg + my * G::SP, gm, gu, gw);
+            publish(ep | 1u);
+        }
+        pm = -INFINITY;
+        pu = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) pw[c] = 0.0f;
+        if (grp > 0) {
+            // load up to LB states at once (their latencies overlap), then combine in order
+            constexpr int LB = 16;
+            auto add_slots = [&](const float *first, int j0, int j1) {  // first, then agg of groups j0 .. j1-1
+                {
+                    float sw[CPL];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) sw[c] = lane + 64 * c < M ? first[lane + 64 * c] : 0.0f;
+                    add_back(first[M], first[M + 1], sw);
+                }
+                for (int jb = j0; jb < j1; jb += LB) {
+                    float tm[LB], tu[LB], tw[LB][CPL];
+#pragma unroll
+                    for (int k = 0; k < LB; ++k) {
+                        const int j = jb + k < j1 ? jb + k : jb;
+                        const float *slot = agg + ((size_t)j * BH + bh) * G::SP;
+                        tm[k] = slot[M];
+                        tu[k] = slot[M + 1];
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) tw[k][c] = lane + 64 * c < M ? slot[lane + 64 * c] : 0.0f;
+                    }
+#pragma unroll
+                    for (int k = 0; k < LB; ++k)
+                        if (jb + k < j1) add_back(tm[k], tu[k], tw[k]);
+                }
+            };
+            int base = grp - 1;
+            int jstar = -1;
+            long spins = 0;
+            while (true) {
+                const int j = base - lane;
+                unsigned f = 0u;
+                if (j >= 0)
+                    f = __hip_atomic_load(flags + (size_t)j * BH + bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool ok = j >= 0 && (f & ~3u) == ep && (f & 3u) != 0u;
+                const bool inc = ok && ((f & 3u) == 2u || j == 0);
+                const unsigned long long okm = __ballot(ok), incm = __ballot(inc);
+                if (incm != 0ull) {
+                    const int first = __builtin_ctzll(incm);
+                    const unsigned long long need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
+                    if ((okm & need) == need) {
+                        jstar = base - first;
+                        break;
+                    }
+                } else if (okm == ~0ull) {
+                    base -= 64;
+                    continue;
+                }
+                if (++spins > kScanSpinLimit) {
+                    if (lane == 0) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
-            } else if (okm == ~0ull) {
-                base -= 64;
-                continue;
+                __builtin_amdgcn_s_sleep(1);
             }
-            if (++spins > kScanSpinLimit) {
-                if (lane == 0) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                break;
+            if (jstar < 0) {
+                failed = true;
+            } else {
+                add_slots((jstar == 0 ? agg : incl) + ((size_t)jstar * BH + bh) * G::SP, jstar + 1, grp);
             }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        if (jstar < 0) {
-            failed = true;
-        } else {
-            add_slots((jstar == 0 ? agg : incl) + ((size_t)jstar * BH + bh) * G::SP, jstar + 1, seg);
-        }
-        if (!last) {
-            // inclusive = prefix + local
-            const float mn = fmaxf(pm, m);
-            const float a = __expf(pm - mn), b = __expf(m - mn);
-            float iw[CPL];
+            if (!last_grp) {
+                // inclusive = prefix + the group's aggregate
+                const float mn = fmaxf(pm, gm);
+                const float a = mn == -INFINITY ? 0.0f : __expf(pm - mn), b = mn == -INFINITY ? 0.0f : __expf(gm - mn);
+                float iw[CPL];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) iw[c] = failed ? __builtin_nanf("") : pw[c] * a + wl[c] * b;
-            store_state(incl + my * G::SP, failed ? __builtin_nanf("") : mn, pu * a + u * b, iw);
-            publish(ep | 2u);
+                for (int c = 0; c < CPL; ++c) iw[c] = failed ? __builtin_nanf("") : pw[c] * a + gw[c] * b;
+                store_state(incl + my * G::SP, failed ? __builtin_nanf("") : mn, pu * a + gu * b, iw);
+                publish(ep | 2u);
+            }
+        }
+        if (last_grp && lane == 0) {
+            // every group of this head has read the epoch (see the prefill kernels'
+            // finish_call): count the head, and the last head advances the epoch
+            const unsigned done = atomicAdd(&hdr[1], 1u);
+            if (done == (unsigned)BH - 1u) {
+                __hip_atomic_store(&hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            if (lane + 64 * c < M) spre[lane + 64 * c] = pw[c];
+        if (lane == 0) {
+            spre[M] = pm;
+            spre[M + 1] = pu;
+            spre[M + 2] = failed ? 1.0f : 0.0f;
         }
     }
-    if (NS > 1 && last && lane == 0) {
-        // every segment of this head has read the epoch (see the prefill kernels'
-        // finish_call): count the head, and the last head advances the epoch
-        const unsigned done = atomicAdd(&hdr[1], 1u);
-        if (done == (unsigned)BH - 1u) {
-            __hip_atomic_store(&hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr[2], epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
+    if (NG > 1) {
+        __syncthreads();
+        pm = -INFINITY;
+        pu = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) pw[c] = 0.0f;
+        add_lds(spre);
+        failed = spre[M + 2] != 0.0f;
     }
+    // the earlier segments of this group follow the group's prefix
+    for (int k = 0; k < w; ++k) add_lds(sst[k]);
+
     if (last && m_out != nullptr) {
         const float mn = fmaxf(pm, m);
         const float a = mn == -INFINITY ? 0.0f : __expf(pm - mn), b = mn == -INFINITY ? 0.0f : __expf(m - mn);
 #pragma unroll
         for (int c = 0; c < CPL; ++c) {
             const int col = lane + 64 * c;
-            if (col < M) w_out[(size_t)bh * M + col] = pw[c] * a + wl[c] * b;
+            if (col < M) w_out[(size_t)bh * M + col] = failed ? __builtin_nanf("") : pw[c] * a + wl[c] * b;
         }
         if (lane == 0) {
-            m_out[bh] = mn;
+            m_out[bh] = failed ? __builtin_nanf("") : mn;
             u_out[bh] = pu * a + u * b;
         }
     }
 
-    // 4. outputs: row i = prefix + local state of row i, normalised
-    float *Oh = out + ((size_t)bh * N + row0) * M;
+    // 4. outputs: row i = prefix + local state of row i, normalised; the factors of
+    //    row i are formed in lane i, then each row is one fma per column
+    if (nrows > 0) {
+        float *Oh = out + ((size_t)bh * N + row0) * M;
+        const float mxp = fmaxf(pm, my_m);
+        const float al = mxp == -INFINITY ? 0.0f : __expf(pm - mxp);  // pm = -inf: 0
+        const float be = mxp == -INFINITY ? 0.0f : __expf(my_m - mxp);
+        const float inv = 1.0f / (pu * al + my_u * be);
+        const float oa = failed ? __builtin_nanf("") : al * inv, ob = be * inv;
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        if (i >= nrows) break;
-        const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_m), i));
-        const float ui = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_u), i));
-        const float mn = fmaxf(pm, mi);
-        const float a = __expf(pm - mn), b = __expf(mi - mn);  // pm = -inf: a = 0
-        const float inv = 1.0f / (pu * a + ui * b);
+        for (int i = 0; i < R; ++i) {
+            if (i >= nrows) break;
+            const float ai = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, oa), i));
+            const float bi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ob), i));
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int col = lane + 64 * c;
-            if (col < M) Oh[(size_t)i * M + col] = failed ? __builtin_nanf("") : (pw[c] * a + wv[i][c] * b) * inv;
+            for (int c = 0; c < CPL; ++c) {
+                const int col = lane + 64 * c;
+                if (col < M) Oh[(size_t)i * M + col] = __builtin_fmaf(pw[c], ai, wv[i][c] * bi);
+            }
         }
     }
-
 }
 
 // One token of the RNN for every head: one wavefront per head, lanes = value
@@ -319,11 +425,11 @@ template <typename T, int D, int M>
 hipError_t run_scan(const void *q, const void *K, const void *V, float *out, void *ws, int BH, int N, float *m_out,
                     float *u_out, float *w_out, hipStream_t stream) {
     const int NS = (N + ScanCfg<D, M>::R - 1) / ScanCfg<D, M>::R;
-    const long items = (long)BH * NS;
-    if (items <= 0) return hipSuccess;
-    const unsigned blocks = (unsigned)((items + kScanWaves - 1) / kScanWaves);
-    hipLaunchKernelGGL((softmax_scan_kernel<T, D, M>), dim3(blocks), dim3(64 * kScanWaves), 0, stream, (const T *)q,
-                       (const T *)K, (const T *)V, out, ws, BH, N, NS, m_out, u_out, w_out);
+    const int NG = (NS + kScanWaves - 1) / kScanWaves;
+    const long groups = (long)BH * NG;
+    if (groups <= 0) return hipSuccess;
+    hipLaunchKernelGGL((softmax_scan_kernel<T, D, M>), dim3((unsigned)groups), dim3(64 * kScanWaves), 0, stream,
+                       (const T *)q, (const T *)K, (const T *)V, out, ws, BH, N, NS, NG, m_out, u_out, w_out);
     return hipGetLastError();
 }
 
@@ -338,7 +444,7 @@ hipError_t run_step(float *m, float *u, float *w, const void *q, const void *k, 
 
 }  // namespace
 
-int softmax_scan_rows(int) { return 32; }
+int softmax_scan_rows(int) { return 32 * kScanWaves; }  // rows per group (one look-back each)
 
 hipError_t softmax_scan(int dtype, int D, int M, const void *q, const void *K, const void *V, float *out, void *ws,
                         int BH, int N, float *m_out, float *u_out, float *w_out, hipStream_t stream) {

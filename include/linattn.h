@@ -286,7 +286,7 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
  * [B][H][N][M] fp32.  m_out, u_out [B][H] and w_out [B][H][M] fp32: optional
  * (all or none), the state after the last position, for la_softmax_step.
  * workspace: la_softmax_scan_workspace_bytes(...) bytes (0 when every head fits
- * one segment of 32 positions), zeroed (la_workspace_init)
+ * one group of 128 positions), zeroed (la_workspace_init)
  * before its first use, then reusable by later calls with the same shape;
  * calls sharing a workspace must not overlap.
  */

@@ -209,9 +209,9 @@ def test_decode_steps_checks(L):
 def test_softmax_scan_checks(L):
     f = L.lib().la_softmax_scan
     need = L.lib().la_softmax_scan_workspace_bytes(2, 2, 1000, 64, 64)
-    items = 2 * 2 * 32  # segments of 32 positions
+    items = 2 * 2 * 8  # groups of 128 positions
     assert need == (64 + 64 * ((items + 63) // 64)) * 4 + 2 * items * 128 * 4
-    assert L.lib().la_softmax_scan_workspace_bytes(2, 2, 32, 64, 64) == 0  # one segment per head
+    assert L.lib().la_softmax_scan_workspace_bytes(2, 2, 128, 64, 64) == 0  # one group per head
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 48, 64, 0, FAKE, need, None, None, None, None) == L.LA_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 2, FAKE, need, None, None, None, None) == L.LA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, FAKE, need - 4, None, None, None,
