@@ -362,7 +362,8 @@ def causal_kernel_name(cfg, chunk, segments) -> str:
     cps = -(-n_chunks // segments)
     kind = "onepass_causal_kernel" if cps <= 4 else "fused_causal_kernel"
     t = "float" if cfg["dtype"] == "f32" else "bf16"
-    return f"{kind}<{t},{cfg['D']},{cfg['M']},{chunk}>"
+    ot = "bf16" if cfg.get("out") == "bf16" else "float"
+    return f"{kind}<{t}, {cfg['D']}, {cfg['M']}, {chunk}, true, {ot}>"
 
 
 def cpu_baseline(cfg, target_s=12.0):

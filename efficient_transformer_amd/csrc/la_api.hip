@@ -77,12 +77,14 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
     }
     const int64_t n_chunks = (N + C - 1) / C;
     // One workgroup per segment; all workgroups of a call resident at once: 256
-    // compute units times the workgroups that fit on one (two when the state is
-    // at most 64 x 64, one otherwise).  Segments are whole chunks; every segment
-    // carries (D*M + D) floats of published state, so fewer, longer segments.
+    // compute units times the workgroups that fit on one (four when the state is
+    // at most 1024 values, two up to 64 x 64, one otherwise).  Segments are whole
+    // chunks; every segment carries (D*M + D) floats of published state, so
+    // fewer, longer segments.  (16 features x 64 values, headline shape: 512
+    // workgroups 22.4 us, 1024 workgroups 19.8 us.)
     // Causal: the fused kernel (look-back across segments).
     // Non-causal: the three stage kernels, with segments sized the same way.
-    const int64_t target_wg = (D * M <= 4096) ? 512 : 256;
+    const int64_t target_wg = (D * M <= 1024) ? 1024 : (D * M <= 4096) ? 512 : 256;
     int64_t cps = (n_chunks * BH + target_wg - 1) / target_wg;
     if (cps < 1) cps = 1;
     int64_t G = (n_chunks + cps - 1) / cps;

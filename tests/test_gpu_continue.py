@@ -85,7 +85,7 @@ def test_explicit_plans_with_initial_state(ea, dtype, kernel, chunk, segments):
 def test_continue_long_two_phase_in_place(ea):
     """Enough positions that the planner takes the two-phase kernel (segments of more
     than four chunks); the state is updated in place (S_out is S_in)."""
-    B, H, N, D, M = 2, 8, 8192, 32, 32
+    B, H, N, D, M = 2, 8, 8192, 64, 32
     S0, z0 = carried_state(B, H, D, M, 500, 25)
     Q, K, V = synthetic.prefill_inputs(pcfg("f32", B, H, N, D, M), 26)
     Qd, Kd, Vd = to_dev(Q, "f32"), to_dev(K, "f32"), to_dev(V, "f32")
