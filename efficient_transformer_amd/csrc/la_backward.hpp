@@ -62,31 +62,67 @@ struct BwdCfg {
     static_assert(C % NCS == 0, "column-sum split");
 };
 
-// Stage a C x W tile of a [N][W] head matrix (element type T) as fp32 into
-// LDS rows of length ld, optionally through phi; rows at or beyond N are zero.
-template <typename T, int C, int W, bool PHI>
-__device__ __forceinline__ void bwd_stage(float *dst, int ld, const T *__restrict__ src, int row0, int N, int tid) {
-    constexpr int NV = W / 4;
-    for (int e = tid; e < C * NV; e += kBwdThreads) {
-        const int row = e / NV, cv = e % NV;
-        const int grow = row0 + row;
-        f32x4 x = zero4();
-        if (grow < N) {
-            const T *p = src + (size_t)grow * W + cv * 4;
-            if constexpr (std::is_same<T, float>::value) {
-                x = *reinterpret_cast<const f32x4 *>(p);
-            } else {
-                const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
-                x = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
-            }
-            if (PHI) {
+// A C x W tile of a [N][W] head matrix (element type T), staged as fp32 into LDS
+// rows of length ld in two steps: load() issues every global load of the tile
+// into registers (rows at or beyond N reload row N - 1), store() writes it to
+// LDS (through phi when asked; rows at or beyond N as zeros).  Loading the next
+// chunk's tiles before the current chunk's arithmetic keeps the loads in flight
+// meanwhile; a load-then-store loop per element instead waits for each load.
+template <typename T, int C, int W>
+struct BwdTile {
+    static constexpr int NV = W / 4;
+    static constexpr int PER = (C * NV + kBwdThreads - 1) / kBwdThreads;
+    f32x4 x[PER];
+    __device__ __forceinline__ void load(const T *__restrict__ src, int row0, int N, int tid) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = phi(x[j]);
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + i * kBwdThreads;
+            if (PER * kBwdThreads == C * NV || e < C * NV) {
+                const int row = e / NV, cv = e % NV;
+                const T *p = src + (size_t)min(row0 + row, N - 1) * W + cv * 4;
+                if constexpr (std::is_same<T, float>::value) {
+                    x[i] = *reinterpret_cast<const f32x4 *>(p);
+                } else {
+                    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p);
+                    x[i] = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+                }
             }
         }
-        *reinterpret_cast<f32x4 *>(dst + row * ld + cv * 4) = x;
     }
-}
+    template <bool PHI>
+    __device__ __forceinline__ void store(float *dst, int ld, int row0, int N, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + i * kBwdThreads;
+            if (PER * kBwdThreads == C * NV || e < C * NV) {
+                const int row = e / NV, cv = e % NV;
+                f32x4 v = x[i];
+                if (PHI) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = phi(v[j]);
+                }
+                if (row0 + row >= N) v = zero4();
+                *reinterpret_cast<f32x4 *>(dst + row * ld + cv * 4) = v;
+            }
+        }
+    }
+};
+
+// The five tiles of a chunk (q, k, v, out, dout).
+template <typename T, int C, int D, int M>
+struct BwdChunk {
+    BwdTile<T, C, D> q, k;
+    BwdTile<T, C, M> v;
+    BwdTile<float, C, M> o, dout;
+    __device__ __forceinline__ void load(const T *Qh, const T *Kh, const T *Vh, const float *Oh, const float *dOh,
+                                         int row0, int N, int tid) {
+        q.load(Qh, row0, N, tid);
+        k.load(Kh, row0, N, tid);
+        v.load(Vh, row0, N, tid);
+        o.load(Oh, row0, N, tid);
+        dout.load(dOh, row0, N, tid);
+    }
+};
 
 template <int D, int M>
 struct BwdEngine {
@@ -260,16 +296,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const T *__restrict
     }
     e.clear_tiles();
 
+    // loads one chunk ahead, unconditional (the index clamped to the last chunk) so
+    // that the compiler's wait counts stay exact
+    BwdChunk<T, C, D, M> ld;
+    ld.load(Q + hq, K + hq, V + hv, O + hv, dO + hv, c0 * C, N, tid);
     for (int c = c0; c < c1; ++c) {
         const int row0 = c * C;
         __syncthreads();
-        bwd_stage<T, C, D, true>(e.sG, Gc::LD, Q + hq, row0, N, tid);
-        bwd_stage<T, C, D, true>(e.sF, Gc::LD, K + hq, row0, N, tid);
-        bwd_stage<T, C, M, false>(e.sV, Gc::LM, V + hv, row0, N, tid);
-        bwd_stage<float, C, M, false>(e.sO, Gc::LM, O + hv, row0, N, tid);
-        bwd_stage<float, C, M, false>(e.sR, Gc::LM, dO + hv, row0, N, tid);
+        ld.q.template store<true>(e.sG, Gc::LD, row0, N, tid);
+        ld.k.template store<true>(e.sF, Gc::LD, row0, N, tid);
+        ld.v.template store<false>(e.sV, Gc::LM, row0, N, tid);
+        ld.o.template store<false>(e.sO, Gc::LM, row0, N, tid);
+        ld.dout.template store<false>(e.sR, Gc::LM, row0, N, tid);
         if (tid < D) e.sZ[tid] = zprev;
         __syncthreads();
+        ld.load(Q + hq, K + hq, V + hv, O + hv, dO + hv, min(c + 1, c1 - 1) * C, N, tid);
         // den_i = rowsum(tril(G F^T)) + g_i . z_prev ; (dout . out)_i
         e.template tri_tiles<D, false>(e.sG, Gc::LD, e.sF, Gc::LD, nullptr, e.sP);
         e.template row_dots<D>(e.sG, Gc::LD, e.sZ, 0, e.sQz);
@@ -438,17 +479,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(const T *__restric
     }
     e.clear_tiles();
 
+    // loads one chunk ahead (walking backward), unconditional (clamped to the first chunk)
+    BwdChunk<T, C, D, M> ld;
+    ld.load(Q + hq, K + hq, V + hv, O + hv, dO + hv, (c1 - 1) * C, N, tid);
     for (int c = c1 - 1; c >= c0; --c) {
         const int row0 = c * C;
         __syncthreads();
-        bwd_stage<T, C, D, true>(e.sG, Gc::LD, Q + hq, row0, N, tid);
-        bwd_stage<T, C, D, true>(e.sF, Gc::LD, K + hq, row0, N, tid);
-        bwd_stage<T, C, M, false>(e.sV, Gc::LM, V + hv, row0, N, tid);
-        bwd_stage<float, C, M, false>(e.sO, Gc::LM, O + hv, row0, N, tid);
-        bwd_stage<float, C, M, false>(e.sR, Gc::LM, dO + hv, row0, N, tid);
+        ld.q.template store<true>(e.sG, Gc::LD, row0, N, tid);
+        ld.k.template store<true>(e.sF, Gc::LD, row0, N, tid);
+        ld.v.template store<false>(e.sV, Gc::LM, row0, N, tid);
+        ld.o.template store<false>(e.sO, Gc::LM, row0, N, tid);
+        ld.dout.template store<false>(e.sR, Gc::LM, row0, N, tid);
         if (tid < D) e.sZ[tid] = wnext;
         if (tid < C) e.sDen[tid] = row0 + tid < N ? den_in[(size_t)bh * N + row0 + tid] : 1.0f;
         __syncthreads();
+        ld.load(Q + hq, K + hq, V + hv, O + hv, dO + hv, max(c - 1, c0) * C, N, tid);
         e.template row_dots<M>(e.sR, Gc::LM, e.sO, Gc::LM, e.sCc);
         __syncthreads();
         if (tid < C) e.sCc[tid] = -e.sCc[tid] / e.sDen[tid];
