@@ -765,7 +765,7 @@ struct Engine {
 
 // ---------------------------------------------------------------------------
 // Phase A: sum the state over chunks [c0, c1) into acc / z (thread tid < D owns z[tid]).
-// Leaves the last chunk's phi(K), V in LDS.  Global loads run one chunk ahead.
+// Leaves the last chunk's phi(K), V in LDS.  Global loads run two chunks ahead.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C>
 struct KVBuf {
@@ -781,21 +781,28 @@ template <typename T, int D, int M, int C, bool PHI>
 __device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const T *__restrict__ Kh,
                                         const T *__restrict__ Vh, int N, int c0, int c1,
                                         f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z) {
-    // One chunk of loads in flight: chunk c+1 is requested right after chunk c is
-    // staged, so a whole chunk of work covers its latency.  The load is issued
-    // unconditionally (index clamped to the last chunk; a clamped reload is an L2
-    // hit) so that the compiler's wait counts stay exact.
-    KVBuf<T, D, M, C> b;
-    b.load(Kh, Vh, c0, N, e.tid);
-    for (int c = c0; c < c1; ++c) {
+    // Two chunks of loads in flight (two register buffers, the loop unrolled by
+    // two): a phase-A chunk has little arithmetic, so one chunk of work does not
+    // cover a load's latency.  Every load is issued unconditionally (index clamped
+    // to the last chunk; a clamped reload is an L2 hit) so that the compiler's
+    // wait counts stay exact; only the arithmetic of the odd last chunk is skipped.
+    KVBuf<T, D, M, C> b0, b1;
+    b0.load(Kh, Vh, c0, N, e.tid);
+    b1.load(Kh, Vh, min(c0 + 1, c1 - 1), N, e.tid);
+    auto body = [&](const KVBuf<T, D, M, C> &b, int c) {
         __syncthreads();  // LDS free (previous chunk's readers are done)
         e.store_kv(b.k, b.v, c * C, N);
         __syncthreads();
-        b.load(Kh, Vh, min(c + 1, c1 - 1), N, e.tid);
         e.z_partials();
         e.state_update(acc);
         __syncthreads();
         if (e.tid < D) z += e.z_delta();
+    };
+    for (int c = c0; c < c1; c += 2) {
+        body(b0, c);
+        b0.load(Kh, Vh, min(c + 2, c1 - 1), N, e.tid);
+        if (c + 1 < c1) body(b1, c + 1);
+        b1.load(Kh, Vh, min(c + 3, c1 - 1), N, e.tid);
     }
 }
 
