@@ -253,7 +253,7 @@ struct BwdEngine {
 // dQ: walk the segment's chunks forward from (S_prev, z_prev).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                              const T *__restrict__ V, const float *__restrict__ O,
                                                              const float *__restrict__ dO,
                                                              const float *__restrict__ fwd_ws, float *rev_ws,
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(const T *__restrict
 // dK, dV: walk the segment's chunks backward from (R_next, w_next).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M>
-__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_kernel(const T *__restrict__ Q, const T *__restrict__ K,
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                               const T *__restrict__ V, const float *__restrict__ O,
                                                               const float *__restrict__ dO,
                                                               const float *__restrict__ rev_ws,
