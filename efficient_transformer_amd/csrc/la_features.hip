@@ -53,7 +53,7 @@ __device__ __forceinline__ f32x4 feat_load4<bf16>(const bf16 *p) {
 
 // blockIdx.y selects the tensor: 0 -> (X, out), 1 -> (X2, out2).
 template <typename T, int D, int F, int KIND, bool NORM>
-__global__ __launch_bounds__(kFeatThreads) void feature_map_kernel(const T *__restrict__ X, float *__restrict__ out,
+__global__ __launch_bounds__(kFeatThreads, 2) void feature_map_kernel(const T *__restrict__ X, float *__restrict__ out,
                                                                    const T *__restrict__ X2, float *__restrict__ out2,
                                                                    const float *__restrict__ W, long rows) {
     using G = FeatCfg<D, F, KIND>;

@@ -1248,7 +1248,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 // exclusive prefix; slot G = total.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int M, int C, bool PHI = true>
-__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS)) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
                                                              float *__restrict__ ws, int N, int G_, int CPS,
                                                              int nstates) {
     using Gc = Cfg<T, D, M, C>;
