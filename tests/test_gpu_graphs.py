@@ -1,0 +1,132 @@
+"""The entry points under HIP graph capture: a captured call replayed several times,
+with eager work (new inputs written by torch) and synchronisations between the
+replays, must give every time what the same eager call gives.  The causal kernels
+keep an epoch in their workspace (advanced by the kernels themselves), so a
+replayed look-back never reads flags of an earlier replay; workspaces are zeroed
+with a fill kernel, never a memset node."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_helpers import TOL, rowwise_rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import efficient_transformer_amd as ea
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return ea
+
+
+def inputs(B, H, N, D, M, seed, dtype="f32"):
+    cfg = dict(kind="prefill", B=B, H=H, N=N, D=D, M=M, sigma=1.0, dtype=dtype, chunk=0)
+    return synthetic.prefill_inputs(cfg, seed)
+
+
+@pytest.mark.parametrize("shape", [(8, 8, 1024, 64, 64), (1, 4, 8192, 64, 64), (2, 2, 300, 32, 128)])
+def test_forward_replays(ea, shape):
+    """One captured la_forward_chunked call (one-pass or two-phase kernel, several
+    segments per head: look-back and epoch), replayed with new inputs each time."""
+    B, H, N, D, M = shape
+    Qd = torch.empty((B, H, N, D), device=DEV)
+    Kd = torch.empty((B, H, N, D), device=DEV)
+    Vd = torch.empty((B, H, N, M), device=DEV)
+    out = torch.empty((B, H, N, M), device=DEV)
+    C, G, need = ea.forward_plan(B, H, N, D, M, True, 0, 0)
+    assert G > 1
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    Qd.copy_(to_dev(inputs(B, H, N, D, M, 80)[0], "f32"))
+    Kd.copy_(Qd)
+    Vd.normal_()
+    ea.forward_chunked(Qd, Kd, Vd, out=out, workspace=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ea.forward_chunked(Qd, Kd, Vd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        Q, K, V = inputs(B, H, N, D, M, 81 + rep)
+        Qd.copy_(to_dev(Q, "f32"))
+        Kd.copy_(to_dev(K, "f32"))
+        Vd.copy_(to_dev(V, "f32"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = ea.forward_chunked(Qd, Kd, Vd)
+        torch.cuda.synchronize()
+        assert rowwise_rel(got.cpu().numpy(), eager.cpu().numpy()) <= 1e-5, rep
+        if rep == 0 and B * H <= 4:
+            assert rowwise_rel(got.cpu().numpy(), oracle.causal(Q, K, V)[0]) <= TOL["f32"]
+
+
+def test_decode_replays(ea):
+    """A captured la_decode_step (state updated in place) replayed T times equals T
+    eager steps; the inputs change between replays."""
+    B, H, D, M, T = 16, 4, 64, 64, 12
+    cfg = dict(kind="decode", B=B, H=H, D=D, M=M, sigma=1.0, dtype="f32")
+    q, k, v = synthetic.decode_inputs(cfg, 3, 0, T)
+    S1 = torch.zeros((B, H, D, M), device=DEV)
+    z1 = torch.zeros((B, H, D), device=DEV)
+    qd = torch.empty((B, H, D), device=DEV)
+    kd = torch.empty((B, H, D), device=DEV)
+    vd = torch.empty((B, H, M), device=DEV)
+    out = torch.empty((B, H, M), device=DEV)
+    graph = torch.cuda.CUDAGraph()
+    Sw, zw = S1.clone(), z1.clone()
+    ea.decode_step(Sw, zw, qd.zero_(), kd.zero_(), vd.zero_(), out=out)  # warm-up on scratch state
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        ea.decode_step(S1, z1, qd, kd, vd, out=out)
+    S2, z2 = torch.zeros_like(S1), torch.zeros_like(z1)
+    for t in range(T):
+        qd.copy_(to_dev(q[t], "f32"))
+        kd.copy_(to_dev(k[t], "f32"))
+        vd.copy_(to_dev(v[t], "f32"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        want = ea.decode_step(S2, z2, qd, kd, vd)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), t  # the same kernel on the same state: bit for bit
+    assert torch.equal(S1, S2) and torch.equal(z1, z2)
+
+
+def test_softmax_scan_replays(ea):
+    """The softmax scan keeps its epoch in the workspace as well."""
+    B, H, N, D, M = 2, 4, 2000, 64, 64
+    rng = np.random.default_rng(5)
+    qd = torch.empty((B, H, D), device=DEV)
+    Kd = torch.empty((B, H, N, D), device=DEV)
+    Vd = torch.empty((B, H, N, M), device=DEV)
+    out = torch.empty((B, H, N, M), device=DEV)
+    wsb = int(ea.linattn.lib().la_softmax_scan_workspace_bytes(B, H, N, D, M))
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    qd.zero_()
+    Kd.zero_()
+    Vd.zero_()
+    ea.softmax_scan(qd, Kd, Vd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ea.softmax_scan(qd, Kd, Vd, out=out, workspace=ws)
+    for rep in range(3):
+        q = (rng.normal(size=(B, H, D)) * 0.125).astype(np.float32)
+        K = rng.normal(size=(B, H, N, D)).astype(np.float32)
+        V = rng.normal(size=(B, H, N, M)).astype(np.float32)
+        qd.copy_(torch.from_numpy(q))
+        Kd.copy_(torch.from_numpy(K))
+        Vd.copy_(torch.from_numpy(V))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        want = oracle.softmax_scan(q, K, V)[0]
+        assert rowwise_rel(got, want) <= TOL["f32"], rep
