@@ -217,31 +217,34 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         add_back(st[M], st[M + 1], sw);
     };
     bool failed = false;
+    const size_t my = (size_t)grp * BH + bh;  // item of this group
+    auto store_state = [&](float *slot, float sm, float sus, const float *sw) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int col = lane + 64 * c;
+            if (col < M) __hip_atomic_store(slot + col, sw[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (lane == 0) {
+            __hip_atomic_store(slot + M, sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(slot + M + 1, sus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    auto publish = [&](unsigned value) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(&flags[my], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    float gm = -INFINITY, gu = 0.0f, gw[CPL];  // wavefront 0: the group's aggregate
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) gw[c] = 0.0f;
     if (NG > 1 && w == 0) {
         // the group's aggregate: its segments in order
         for (int k = 0; k < kScanWaves; ++k) add_lds(sst[k]);
-        const float gm = pm, gu = pu;
-        float gw[CPL];
+        gm = pm;
+        gu = pu;
 #pragma unroll
         for (int c = 0; c < CPL; ++c) gw[c] = pw[c];
-        const size_t my = (size_t)grp * BH + bh;  // item of this group
-        auto store_state = [&](float *slot, float sm, float sus, const float *sw) {
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const int col = lane + 64 * c;
-                if (col < M) __hip_atomic_store(slot + col, sw[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            if (lane == 0) {
-                __hip_atomic_store(slot + M, sm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(slot + M + 1, sus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        };
-        auto publish = [&](unsigned value) {
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __builtin_amdgcn_s_waitcnt(0);
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (lane == 0) __hip_atomic_store(&flags[my], value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        };
         if (!last_grp) {
             store_state(agg + my * G::SP, gm, gu, gw);
             publish(ep | 1u);
@@ -309,16 +312,6 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
             } else {
                 add_slots((jstar == 0 ? agg : incl) + ((size_t)jstar * BH + bh) * G::SP, jstar + 1, grp);
             }
-            if (!last_grp) {
-                // inclusive = prefix + the group's aggregate
-                const float mn = fmaxf(pm, gm);
-                const float a = mn == -INFINITY ? 0.0f : __expf(pm - mn), b = mn == -INFINITY ? 0.0f : __expf(gm - mn);
-                float iw[CPL];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) iw[c] = failed ? __builtin_nanf("") : pw[c] * a + gw[c] * b;
-                store_state(incl + my * G::SP, failed ? __builtin_nanf("") : mn, pu * a + gu * b, iw);
-                publish(ep | 2u);
-            }
         }
         if (last_grp && lane == 0) {
             // every group of this head has read the epoch (see the prefill kernels'
@@ -346,6 +339,17 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         for (int c = 0; c < CPL; ++c) pw[c] = 0.0f;
         add_lds(spre);
         failed = spre[M + 2] != 0.0f;
+        if (w == 0 && grp > 0 && !last_grp) {
+            // the group's inclusive state = prefix + aggregate, published once the
+            // other wavefronts have their prefix (later groups can use aggregates)
+            const float mn = fmaxf(pm, gm);
+            const float a = mn == -INFINITY ? 0.0f : __expf(pm - mn), b = mn == -INFINITY ? 0.0f : __expf(gm - mn);
+            float iw[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) iw[c] = failed ? __builtin_nanf("") : pw[c] * a + gw[c] * b;
+            store_state(incl + my * G::SP, failed ? __builtin_nanf("") : mn, pu * a + gu * b, iw);
+            publish(ep | 2u);
+        }
     }
     // the earlier segments of this group follow the group's prefix
     for (int k = 0; k < w; ++k) add_lds(sst[k]);
