@@ -111,6 +111,12 @@ LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_
  *   again before it is used with a different plan (B*H, N, D, M, dtype or
  *   chunk); every completed call leaves it ready for the next call with the
  *   same plan.  Calls that run concurrently must not share a workspace.
+ *   A segment waits for earlier segments of its head with a bounded wait (about
+ *   4 million polls).  Workgroups are dispatched in segment order, so the wait
+ *   ends unless the GPU is shared so heavily that earlier segments cannot run;
+ *   if it gives up, the affected outputs (and S_out, z_out) are NaN, a nonzero
+ *   error word is left in the workspace, and the workspace must be zeroed again
+ *   before its next use.
  * S_out [B][H][D][M], z_out [B][H][D]: optional (NULL to skip; both or neither);
  *   receive the final state S_{N-1}, z_{N-1}, so that la_decode_step can
  *   continue the sequence.
