@@ -1047,8 +1047,12 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 #pragma unroll
         for (int dt = 0; dt < Gc::DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < Gc::MTW; ++i) fin[dt][i] = pre[dt][i] + acc[dt][i];
-        e.state_store(fin, zpre + zacc, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+            for (int i = 0; i < Gc::MTW; ++i) {
+                fin[dt][i] = pre[dt][i] + acc[dt][i];
+                if (failed) fin[dt][i] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            }
+        e.state_store(fin, failed ? __builtin_nanf("") : zpre + zacc, S_out + (size_t)bh * D * M,
+                      z_out + (size_t)bh * D);
     }
 
     if (single) {
@@ -1213,8 +1217,12 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 #pragma unroll
         for (int dt = 0; dt < Gc::DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < Gc::MTW; ++i) fin[dt][i] = pre[dt][i] + S[dt][i];
-        e.state_store(fin, zpre + z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
+            for (int i = 0; i < Gc::MTW; ++i) {
+                fin[dt][i] = pre[dt][i] + S[dt][i];
+                if (failed) fin[dt][i] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+            }
+        e.state_store(fin, failed ? __builtin_nanf("") : zpre + z, S_out + (size_t)bh * D * M,
+                      z_out + (size_t)bh * D);
     }
 
     // finish the rows with the prefix

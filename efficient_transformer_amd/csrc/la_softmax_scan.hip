@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         }
         if (lane == 0) {
             m_out[bh] = failed ? __builtin_nanf("") : mn;
-            u_out[bh] = pu * a + u * b;
+            u_out[bh] = failed ? __builtin_nanf("") : pu * a + u * b;
         }
     }
 
