@@ -308,9 +308,10 @@ def bench_softmax_scan(cfg, steps, dev):
 
 def bench_features(cfg, steps, dev):
     """Random features (16 positive random features, orthogonal projection) then causal
-    linear attention on them, on the headline shape: one la_feature_map launch (Q and K)
-    and one prefill launch per step, inputs rotated past the last-level cache.  Each
-    launch is bracketed by its own events."""
+    linear attention on them, on the headline shape: one la_forward_features launch per
+    step (the features formed inside the attention kernel), and for comparison the two
+    launches la_feature_map (Q and K) + la_forward_chunked on the features.  Inputs
+    rotate past the last-level cache; each launch is bracketed by its own events."""
     import torch
     import efficient_transformer_amd as ea
     import synthetic
@@ -318,6 +319,7 @@ def bench_features(cfg, steps, dev):
     B, H, N, D, M, F = (cfg[k] for k in ("B", "H", "N", "D", "M", "F"))
     map_bytes = B * H * N * (2 * D * 4 + 2 * F * 4)
     attn_bytes = B * H * N * ((2 * F + M) * 4 + 4 * M)
+    fused_bytes = B * H * N * (2 * D + 2 * M) * 4  # raw q, k, v read, out written
     nsets = max(1, math.ceil(1.25 * LLC_BYTES / (map_bytes + attn_bytes)))
     W = torch.from_numpy(ea.draw_projection(F, D, "orthogonal", 0)).to(dev)
     sets = []
@@ -350,11 +352,29 @@ def bench_features(cfg, steps, dev):
     torch.cuda.synchronize()
     us_map = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e3
     us_attn = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e3
-    us_step = sum(e[0].elapsed_time(e[2]) for e in evs) / steps * 1e3
+    us_two = sum(e[0].elapsed_time(e[2]) for e in evs) / steps * 1e3
+
+    def fused(i, ev=None):
+        Xq, Xk, V, _, _, o = sets[i % nsets]
+        if ev:
+            ev[0].record(stream)
+        ea.forward_features(Xq, Xk, V, W, F, cfg["feature"], out=o, stream=stream)
+        if ev:
+            ev[1].record(stream)
+
+    for i in range(5):
+        fused(i)
+    torch.cuda.synchronize()
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        fused(i, evf[i])
+    torch.cuda.synchronize()
+    us_fused = sum(e[0].elapsed_time(e[1]) for e in evf) / steps * 1e3
     del sets
     torch.cuda.empty_cache()
-    return dict(us_step=us_step, us_map=us_map, us_attn=us_attn, map_bytes=map_bytes, attn_bytes=attn_bytes,
-                tokens_per_s=B * N / (us_step * 1e-6), nsets=nsets)
+    return dict(us_fused=us_fused, us_two=us_two, us_map=us_map, us_attn=us_attn, map_bytes=map_bytes,
+                attn_bytes=attn_bytes, fused_bytes=fused_bytes, tokens_per_s=B * N / (us_fused * 1e-6),
+                two_launch_tokens_per_s=B * N / (us_two * 1e-6), nsets=nsets)
 
 
 def causal_kernel_name(cfg, chunk, segments) -> str:
@@ -429,6 +449,7 @@ def profile_run(dev):
     for _ in range(2):
         fq, fk = ea.feature_map(Q, Wf, fc["F"], "prf", X2=K)
         ea.forward_chunked(fq, fk, V, causal=True, features=True)
+        ea.forward_features(Q, K, V, Wf, fc["F"], "prf")
     for name in ("prefill_bf16_b4h8_n3072_d64", "prefill_bf16_b1h16_n65536_d128"):
         c = dict(synthetic.WORKLOADS[name])
         Qb, Kb, Vb, ob = make_prefill_sets(c, 1, dev)[0]
@@ -573,7 +594,12 @@ def main():
         line["features"] = {
             "workload": "16 positive random features (orthogonal projection) of q, k, then causal linear "
                         "attention on them, fp32, B=8 H=8 N=1024 D=M=64",
-            "tokens_per_s": round(fe["tokens_per_s"], 1), "us_per_step": round(fe["us_step"], 2),
+            "tokens_per_s": round(fe["tokens_per_s"], 1), "us_per_step": round(fe["us_fused"], 2),
+            "fused_kernel_us": round(fe["us_fused"], 2), "fused_bytes": fe["fused_bytes"],
+            "fused_GBs": round(fe["fused_bytes"] / (fe["us_fused"] * 1e-6) / 1e9, 1),
+            "fused_frac_hbm_peak": round(fe["fused_bytes"] / (fe["us_fused"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "two_launch_us_per_step": round(fe["us_two"], 2),
+            "two_launch_tokens_per_s": round(fe["two_launch_tokens_per_s"], 1),
             "feature_map_us": round(fe["us_map"], 2), "attention_us": round(fe["us_attn"], 2),
             "feature_map_GBs": round(fe["map_bytes"] / (fe["us_map"] * 1e-6) / 1e9, 1),
             "attention_GBs": round(fe["attn_bytes"] / (fe["us_attn"] * 1e-6) / 1e9, 1),

@@ -13,6 +13,7 @@ from .linattn import (  # noqa: F401
     feature_map,
     forward_chunked,
     forward_continue,
+    forward_features,
     forward_fused,
     forward_onepass,
     forward_plan,

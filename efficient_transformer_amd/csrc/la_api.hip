@@ -2,6 +2,8 @@
 // Declarations and the contract of every entry point are in include/linattn.h.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "la_launch.hpp"
 #include "linattn.h"
 
@@ -49,7 +51,7 @@ size_t state_ws_bytes(int64_t BH, int64_t D, int64_t M, int G) {
 
 // The planner: chunk length, number of segments and workspace.
 int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype, int chunk_req,
-              Plan *plan) {
+              Plan *plan, int64_t target_wg_override = 0) {
     int st = check_shape(B, H, N, D, M, dtype);
     if (st != LA_OK) return st;
     if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
@@ -84,7 +86,8 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
     // workgroups 22.4 us, 1024 workgroups 19.8 us.)
     // Causal: the fused kernel (look-back across segments).
     // Non-causal: the three stage kernels, with segments sized the same way.
-    const int64_t target_wg = (D * M <= 1024) ? 1024 : (D * M <= 4096) ? 512 : 256;
+    const int64_t target_wg = target_wg_override > 0 ? target_wg_override
+                              : (D * M <= 1024) ? 1024 : (D * M <= 4096) ? 512 : 256;
     int64_t cps = (n_chunks * BH + target_wg - 1) / target_wg;
     if (cps < 1) cps = 1;
     int64_t G = (n_chunks + cps - 1) / cps;
@@ -553,6 +556,58 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
         }
     }
     return hip_status(la::decode_steps(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), (int)T, s));
+}
+
+// ---- causal attention with the random-feature map fused ----------------------
+
+namespace {
+// The plan of la_forward_features (LA_OK only when the fused kernel runs it).
+int features_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F, Plan *p) {
+    if (!dim_ok(D) || !dim_ok(F)) return LA_ERR_UNSUPPORTED;
+    // the fused kernel's LDS (raw rows and W besides the attention tiles) admits
+    // two workgroups per CU: plan 512 resident workgroups
+    int st = make_plan(B, H, N, F, M, 1, LA_F32_FEATURES, la::kFusedFeatureChunk, p, 512);
+    if (st != LA_OK) return st;
+    if (B * H > 0 && N > 0 && (!p->onepass || !la::prefill_features_supported((int)D, (int)F, (int)M)))
+        return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+}  // namespace
+
+LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F) {
+    Plan p;
+    // a supported shape asks for at least 256 bytes, so 0 always means "refused"
+    return features_plan(B, H, N, D, M, F, &p) == LA_OK ? std::max<size_t>(p.ws_bytes, 256) : 0;
+}
+
+LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
+                               int64_t N, int64_t D, int64_t M, const float *W, int64_t F, int kind, int flags,
+                               void *workspace, size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+    if (kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
+    if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
+    Plan p;
+    int st = features_plan(B, H, N, D, M, F, &p);
+    if (st != LA_OK) return st;
+    if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+    const int64_t BH = B * H;
+    if (BH == 0) return LA_OK;
+    hipStream_t s = as_stream(stream);
+    if (N == 0) {
+        if (S_out == nullptr) return LA_OK;
+        (void)hipGetLastError();
+        hipError_t e = la::fill_zero(S_out, (size_t)(BH * F * M), s);
+        if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * F), s);
+        return hip_status(e);
+    }
+    if (!Q || !K || !V || !out || !W) return LA_ERR_INVALID_ARG;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(W)) return LA_ERR_INVALID_ARG;
+    if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) return LA_ERR_WORKSPACE;
+    if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::prefill_features((int)D, (int)F, (int)M, Q, K, V, W, kind,
+                                           (flags & LA_FEATURE_NORMALIZE) != 0, out, workspace, (int)BH, (int)N,
+                                           p.segments, p.chunks_per_segment, S_out, z_out, s));
 }
 
 // ---- feature maps ----------------------------------------------------------

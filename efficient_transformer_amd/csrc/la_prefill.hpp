@@ -767,9 +767,9 @@ struct Engine {
 // Phase A: sum the state over chunks [c0, c1) into acc / z (thread tid < D owns z[tid]).
 // Leaves the last chunk's phi(K), V in LDS.  Global loads run two chunks ahead.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C>
+template <typename T, int D, int M, int C, int DK = D>  // DK: width of the K rows in memory
 struct KVBuf {
-    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> k;
+    Stage<T, C, DK, Cfg<T, D, M, C>::THREADS> k;
     Stage<T, C, M, Cfg<T, D, M, C>::THREADS> v;
     __device__ __forceinline__ void load(const T *Kh, const T *Vh, int c, int N, int tid) {
         k.load(Kh, c * C, N, tid);
@@ -1088,6 +1088,80 @@ constexpr int kOnePassChunks = 4;
 // LDS: phi(Q) of the whole segment [ROWS][LQ] at the start, its last chunk
 // doubling as the engine's phi(Q) tile (the engine's layout starts at
 // `shift`), then the partial denominators and phi(q).z_prefix of every row.
+// ---------------------------------------------------------------------------
+// Random features fused into the staging of Q and K (page "Stable, Fast and
+// Accurate: Kernelized Attention with Relative Positional Encoding", Proposed
+// method and Main findings: PRF and TRF feature maps, feature dimension F).  The
+// raw q and k rows of a chunk (DI wide, fp32) are staged in LDS; the projections
+// x W^T run on MFMA with W staged in LDS once per workgroup (rows past the number
+// of projections zero); then kind 1 (PRF): exp(w . x - |x|^2 / 2) / sqrt(F),
+// kind 2 (TRF, P = F / 2 projections): exp(|x|^2 / 2) / sqrt(P) times sin (column
+// p) and cos (column P + p); norm: rows scaled to unit length first.  Rows at or
+// beyond N get zero features (they must add nothing to the sums).
+// ---------------------------------------------------------------------------
+template <int DI, int F, int C>
+struct FeatLds {
+    static constexpr int LX = DI + 4;           // LDS row of a raw tile
+    static constexpr int WROWS = (F + 15) / 16 * 16;
+    static constexpr int nRaw = 2 * C * LX;     // raw q, raw k
+    static constexpr int nW = WROWS * LX;
+    static constexpr size_t bytes = (size_t)(nRaw + nW) * 4;
+    static_assert(DI % 16 == 0, "16-deep contraction blocks");
+};
+
+// One (tensor, 16-row tile, 16-projection tile) job of the projection: lane
+// (g, l16) ends with projections 4g .. 4g+3 of row l16 (W rows as the MFMA A
+// operand, x rows as B; within each 16-deep block lane g contracts over
+// k = 16 kb + 4 g + kk for both).
+template <int DI, int F, int C>
+__device__ __forceinline__ void feature_job(const float *raw, const float *sw, float *dst, int ld, int rt, int pt,
+                                            int P, int kind, bool norm, int row0, int N, int lane) {
+    using FL = FeatLds<DI, F, C>;
+    const int g = lane >> 4, l16 = lane & 15;
+    const float *xr = raw + (rt * 16 + l16) * FL::LX + 4 * g;
+    const float *wr = sw + (pt * 16 + l16) * FL::LX + 4 * g;
+    f32x4 acc = zero4();
+    float sq = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < DI / 16; ++kb) {
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(xr + 16 * kb);
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(wr + 16 * kb);
+        sq += b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mma_f32(a[kk], b[kk], acc);
+    }
+    sq += __shfl_xor(sq, 16, 64);  // the four lanes g of row l16 hold a quarter each
+    sq += __shfl_xor(sq, 32, 64);
+    float scale = 1.0f;
+    if (norm && sq > 0.0f) {
+        scale = 1.0f / sqrtf(sq);
+        sq = sq * scale * scale;
+    }
+    const int row = rt * 16 + l16, f0 = pt * 16 + 4 * g;
+    if (f0 >= P) return;
+    const bool pad = row0 + row >= N;
+    float *o = dst + row * ld;
+    if (kind == 1) {
+        const float inv = 1.0f / sqrtf((float)F);
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = pad ? 0.0f : __expf(acc[r] * scale - 0.5f * sq) * inv;
+        *reinterpret_cast<f32x4 *>(o + f0) = v;
+    } else {
+        const float c = __expf(0.5f * sq) / sqrtf((float)P);
+        f32x4 vs, vc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float sn, cs;
+            sincosf(acc[r] * scale, &sn, &cs);
+            vs[r] = pad ? 0.0f : c * sn;
+            vc[r] = pad ? 0.0f : c * cs;
+        }
+        *reinterpret_cast<f32x4 *>(o + f0) = vs;
+        *reinterpret_cast<f32x4 *>(o + P + f0) = vc;
+    }
+}
+
 template <typename T, int D, int M, int C>
 struct OnePassLds {
     using Gc = Cfg<T, D, M, C>;
@@ -1101,16 +1175,23 @@ struct OnePassLds {
     static constexpr bool fits = (bytes + 64) * Gc::MIN_WG <= kMaxLds;
 };
 
-template <typename T, int D, int M, int C, bool PHI = true, typename OT = float>
+// DI > 0: Q and K hold raw fp32 rows DI wide and the random-feature map (W, fkind,
+// fnorm) is applied while staging them (D is then the feature dimension F).
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float, int DI = 0>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void onepass_causal_kernel(
     const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, OT *__restrict__ out,
     void *ws_raw, int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out,
-    const float *S_in, const float *z_in) {
+    const float *S_in, const float *z_in, const float *__restrict__ W, int fkind, int fnorm) {
     using Gc = Cfg<T, D, M, C>;
     using L1 = OnePassLds<T, D, M, C>;
     using En = Engine<T, D, M, C, PHI>;
     constexpr int NC = kOnePassChunks;
+    constexpr bool FEAT = DI > 0;
+    constexpr int DQ = FEAT ? DI : D;  // width of the Q, K rows in memory
+    using FL = FeatLds<FEAT ? DI : 16, D, C>;
+    static_assert(!FEAT || (std::is_same<T, float>::value && !PHI), "fused features: fp32 rows, no elu map");
     __shared__ __attribute__((aligned(16))) unsigned char smem[L1::bytes];
+    __shared__ __attribute__((aligned(16))) float sfeat[FEAT ? FL::nRaw + FL::nW : 4];
     __shared__ unsigned sh_word[2];
     En e(smem + L1::shift);
     T *const sQs = reinterpret_cast<T *>(smem);
@@ -1133,12 +1214,23 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS;
     const int nc = min(CPS, n_chunks - c0);  // 1 .. NC (the planner guarantees it)
-    const T *Qh = Q + (size_t)bh * N * D;
-    const T *Kh = K + (size_t)bh * N * D;
+    const T *Qh = Q + (size_t)bh * N * DQ;
+    const T *Kh = K + (size_t)bh * N * DQ;
     const T *Vh = V + (size_t)bh * N * M;
     OT *Oh = out + (size_t)bh * N * M;
     const bool last = s == G_ - 1;
     const bool want_final = S_out != nullptr;
+    float *const sRawQ = sfeat, *const sRawK = sfeat + C * FL::LX, *const sW = sfeat + FL::nRaw;
+    const int P = fkind == 2 ? D / 2 : D;  // projections (fused features)
+    if constexpr (FEAT) {
+        // W once per workgroup, rows past P zero
+        for (int x = tid; x < FL::WROWS * (DI / 4); x += Gc::THREADS) {
+            const int f = x / (DI / 4), c4 = (x % (DI / 4)) * 4;
+            f32x4 v = zero4();
+            if (f < P) v = *reinterpret_cast<const f32x4 *>(W + (size_t)f * DI + c4);
+            *reinterpret_cast<f32x4 *>(sW + f * FL::LX + c4) = v;
+        }
+    }
 
     e.clear_a();
     f32x4 S[Gc::DT][Gc::MTW];
@@ -1151,17 +1243,32 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     // loads one chunk ahead, unconditional (clamped to the segment's last chunk)
     // so the compiler's wait counts stay exact (see phase_a)
     const int clast = c0 + nc - 1;
-    Stage<T, C, D, Gc::THREADS> q;
-    KVBuf<T, D, M, C> b;
+    Stage<T, C, DQ, Gc::THREADS> q;
+    KVBuf<T, D, M, C, DQ> b;
     q.load(Qh, c0 * C, N, tid);
     b.load(Kh, Vh, c0, N, tid);
     auto step = [&](int j, f32x4 (&oj)[Gc::RT][Gc::MTW]) {
         const int c = c0 + j, row0 = c * C;
         __syncthreads();  // sK, sV, sA, side arrays free
         e.sQ = sQs + j * C * Gc::LQ;
-        e.store_q(q, row0, N);
-        e.store_kv(b.k, b.v, row0, N);
-        if (tid < D) e.sz[tid] = round_as<T>(z);
+        if constexpr (FEAT) {
+            // raw rows to LDS, then the features of q and k into the engine's tiles
+            q.template store_natural<false>(sRawQ, FL::LX, row0, N, tid);
+            b.k.template store_natural<false>(sRawK, FL::LX, row0, N, tid);
+            b.v.template store_natural<false>(e.sV, Gc::LV, row0, N, tid);
+            if (tid < D) e.sz[tid] = z;
+            __syncthreads();
+            const int PT = (P + 15) / 16, jobs = 2 * Gc::RT * PT;
+            for (int jb = e.w; jb < jobs; jb += Gc::NW) {
+                const int t = jb / (Gc::RT * PT), rt = (jb % (Gc::RT * PT)) / PT, pt = jb % PT;
+                feature_job<DI, D, C>(t == 0 ? sRawQ : sRawK, sW, t == 0 ? e.sQ : e.sK, Gc::LQ, rt, pt, P, fkind,
+                                      fnorm != 0, row0, N, e.lane);
+            }
+        } else {
+            e.store_q(q, row0, N);
+            e.store_kv(b.k, b.v, row0, N);
+            if (tid < D) e.sz[tid] = round_as<T>(z);
+        }
         __syncthreads();
         if (j + 1 < NC) {  // compile-time: no load past the last possible step
             q.load(Qh, min(c + 1, clast) * C, N, tid);
@@ -1331,7 +1438,33 @@ hipError_t run_onepass(const void *Q, const void *K, const void *V, void *out, v
         if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
         hipLaunchKernelGGL((onepass_causal_kernel<T, D, M, C, PHI, OT>), dim3((unsigned)(BH * G_)), dim3(Gc::THREADS), 0,
                            stream, (const T *)Q, (const T *)K, (const T *)V, (OT *)out, ws, BH, N, G_, CPS, S_out, z_out,
-                           S_in, z_in);
+                           S_in, z_in, nullptr, 0, 0);
+        return hipGetLastError();
+    }
+}
+
+// The one-pass kernel with the random-feature map fused (fp32 q, k rows DI wide,
+// F features, W [P][DI]); see onepass_causal_kernel.
+template <int DI, int F, int M, int C>
+constexpr bool onepass_features_fit() {
+    using Gc = Cfg<float, F, M, C>;
+    return Gc::fits && OnePassLds<float, F, M, C>::fits &&
+           (OnePassLds<float, F, M, C>::bytes + FeatLds<DI, F, C>::bytes + 64) * Gc::MIN_WG <= kMaxLds;
+}
+
+template <int DI, int F, int M, int C>
+hipError_t run_onepass_features(const void *Q, const void *K, const void *V, const float *W, int fkind, int fnorm,
+                                float *out, void *ws, int BH, int N, int G_, int CPS, float *S_out, float *z_out,
+                                hipStream_t stream) {
+    using Gc = Cfg<float, F, M, C>;
+    if constexpr (!onepass_features_fit<DI, F, M, C>()) {
+        return hipErrorInvalidValue;
+    } else {
+        if (BH <= 0 || G_ <= 0) return hipSuccess;
+        if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((onepass_causal_kernel<float, F, M, C, false, float, DI>), dim3((unsigned)(BH * G_)),
+                           dim3(Gc::THREADS), 0, stream, (const float *)Q, (const float *)K, (const float *)V, out, ws,
+                           BH, N, G_, CPS, S_out, z_out, nullptr, nullptr, W, fkind, fnorm);
         return hipGetLastError();
     }
 }

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for s in ("la_forward_chunked", "la_decode_step", "la_forward_workspace_bytes", "la_forward_plan",
               "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version",
               "la_forward_fused", "la_forward_onepass", "la_forward_continue", "la_workspace_init",
-              "la_backward_chunked", "la_decode_steps", "la_softmax_scan", "la_softmax_step", "la_feature_map"):
+              "la_backward_chunked", "la_decode_steps", "la_softmax_scan", "la_softmax_step", "la_feature_map",
+              "la_forward_features", "la_forward_features_workspace_bytes"):
         assert s in syms
 
 
@@ -288,3 +289,36 @@ def test_bf16_output_flag(L):
                                    L.LA_BF16 | L.LA_OUT_BF16, FAKE, 1 << 30, None) == L.LA_ERR_UNSUPPORTED
     assert lib.la_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, L.LA_BF16 | L.LA_OUT_BF16,
                               None) == L.LA_ERR_INVALID_ARG
+
+
+def test_forward_features_checks(L):
+    lib = L.lib()
+    wsb = lib.la_forward_features_workspace_bytes
+    f = lib.la_forward_features
+    # Q, K, V, out, B, H, N, D, M, W, F, kind, flags, ws, ws_bytes, S_out, z_out, stream
+    need = wsb(8, 8, 1024, 64, 64, 16)
+    assert need > 0
+    assert wsb(8, 8, 1024, 48, 64, 16) == 0 and wsb(8, 8, 1024, 64, 64, 24) == 0  # D, F
+    assert wsb(1, 1, 1 << 20, 64, 64, 16) == 0  # segments longer than four chunks
+    assert wsb(-1, 8, 1024, 64, 64, 16) == 0
+
+    def call(**kw):
+        a = dict(Q=FAKE, K=FAKE, V=FAKE, out=FAKE, B=8, H=8, N=1024, D=64, M=64, W=FAKE, F=16, kind=1, flags=0,
+                 ws=FAKE, ws_bytes=need, S=None, z=None)
+        a.update(kw)
+        return f(a["Q"], a["K"], a["V"], a["out"], a["B"], a["H"], a["N"], a["D"], a["M"], a["W"], a["F"],
+                 a["kind"], a["flags"], a["ws"], a["ws_bytes"], a["S"], a["z"], None)
+
+    assert call(kind=0) == L.LA_ERR_INVALID_ARG  # elu+1 is la_forward_chunked
+    assert call(kind=3) == L.LA_ERR_INVALID_ARG
+    assert call(flags=2) == L.LA_ERR_INVALID_ARG
+    assert call(D=48) == L.LA_ERR_UNSUPPORTED
+    assert call(F=64) == L.LA_ERR_UNSUPPORTED  # LDS of D = M = 64 with F = 64 exceeds two workgroups per CU
+    assert call(B=1, H=1, N=1 << 20) == L.LA_ERR_UNSUPPORTED
+    assert call(N=-1) == L.LA_ERR_INVALID_ARG
+    assert call(S=FAKE) == L.LA_ERR_INVALID_ARG  # S_out without z_out
+    assert call(W=None) == L.LA_ERR_INVALID_ARG
+    assert call(V=FAKE + 4) == L.LA_ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == L.LA_ERR_WORKSPACE
+    assert call(ws=None) == L.LA_ERR_WORKSPACE
+    assert call(B=0) == L.LA_OK  # no heads: nothing to do

@@ -1,0 +1,196 @@
+"""Causal attention with the random-feature map inside the attention kernel
+(la_forward_features) against the fp64 oracle: oracle.feature_map forms the
+features of the same raw rows with the same projection W, oracle.attention_mapped
+the running sums over them (page "Stable, Fast and Accurate: Kernelized Attention
+with Relative Positional Encoding": PRF and TRF features, Sphere-PRF and ORF
+draws, normalised rows; page "Transformers are RNNs": the causal running sums).
+
+Outputs are held to the fp32 tolerance 1e-4 row-wise, the final state S, z to
+1e-5 over the whole tensor; against the two-launch path (la_feature_map then
+la_forward_chunked on the features, the same fp32 arithmetic in another order)
+to 1e-5 row-wise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from gpu_helpers import TOL, rowwise_rel, to_dev, whole_rel
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+W_ROWS = {"prf": lambda F: F, "trf": lambda F: F // 2}
+# TRF features can be negative; inputs at a fifth of the unit scale keep every
+# denominator away from zero (cosines dominate), as the estimator needs.
+KIND_SCALE = {"prf": 1.0, "trf": 0.2}
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import efficient_transformer_amd as ea
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return ea
+
+
+def supported(ea, B, H, N, D, M, F):
+    return int(ea.linattn.lib().la_forward_features_workspace_bytes(B, H, N, D, M, F)) > 0
+
+
+def case(ea, B, H, N, D, M, F, kind, seed, normalize=False, draw="gaussian", scale=None):
+    """Seeded raw X_q, X_k, V and W -> device tensors and the fp64 oracle's
+    (out, S, z) over the oracle's own features."""
+    s = (KIND_SCALE[kind] if scale is None else scale) * D ** -0.25
+    Xq = synthetic.draw(seed, synthetic.TID_Q, (B, H, N, D), s, "f32")
+    Xk = synthetic.draw(seed, synthetic.TID_K, (B, H, N, D), s, "f32")
+    V = synthetic.draw(seed, synthetic.TID_V, (B, H, N, M), 1.0, "f32")
+    W = ea.draw_projection(W_ROWS[kind](F), D, draw, seed + 1)
+    dev = tuple(to_dev(x, "f32") for x in (Xq, Xk, V)) + (torch.from_numpy(W).to(DEV),)
+    return dev, (Xq, Xk, V, W)
+
+
+def oracle_out(host, F, kind, normalize, causal=True):
+    Xq, Xk, V, W = host
+    W64 = W.astype(np.float64)
+    Fq = oracle.feature_map(Xq.astype(np.float64), W64, F, kind, normalize)
+    Fk = oracle.feature_map(Xk.astype(np.float64), W64, F, kind, normalize)
+    return oracle.attention_mapped(Fq, Fk, V.astype(np.float64), causal)
+
+
+def run(ea, dev, F, kind, normalize, with_state=True):
+    Qd, Kd, Vd, Wd = dev
+    B, H, N, D = Qd.shape
+    M = Vd.shape[-1]
+    S = torch.full((B, H, F, M), float("nan"), device=DEV) if with_state else None
+    z = torch.full((B, H, F), float("nan"), device=DEV) if with_state else None
+    out = ea.forward_features(Qd, Kd, Vd, Wd, F, kind, normalize, S_out=S, z_out=z)
+    return out, S, z
+
+
+def check(out, S, z, ref):
+    torch.cuda.synchronize()
+    ref_out, S_ref, z_ref = ref
+    err = rowwise_rel(out.cpu().numpy(), ref_out)
+    assert err <= TOL["f32"], f"out {err:.3e}"
+    if S is not None:
+        assert whole_rel(S.cpu().numpy(), S_ref) <= 1e-5
+        assert whole_rel(z.cpu().numpy(), z_ref) <= 1e-5
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+@pytest.mark.parametrize("kind", ["prf", "trf"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("F,M", [(16, 64), (32, 32), (16, 128), (32, 16), (64, 16)])
+def test_fused_features_parity(ea, normalize, kind, D, F, M):
+    """N = 300: nine full chunks of 32 and a ragged one, several segments per head."""
+    B, H, N = 1, 3, 300
+    if not supported(ea, B, H, N, D, M, F):
+        pytest.skip(f"D={D} F={F} M={M}: the kernel's LDS does not fit two workgroups per CU")
+    dev, host = case(ea, B, H, N, D, M, F, kind, 50 + D + F, normalize)
+    out, S, z = run(ea, dev, F, kind, normalize)
+    check(out, S, z, oracle_out(host, F, kind, normalize))
+
+
+def test_supported_shapes(ea):
+    """The shapes the fused kernel takes (the others fall to the two-launch path)."""
+    for D in (16, 32, 64, 128):
+        for F, M in ((16, 16), (16, 64), (16, 128), (32, 128), (64, 128)):
+            assert supported(ea, 8, 8, 1024, D, M, F), (D, F, M)
+    for D in (16, 32, 64):
+        for F, M in ((32, 32), (32, 64)):
+            assert supported(ea, 8, 8, 1024, D, M, F), (D, F, M)
+
+
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 127, 128, 129])
+def test_fused_features_short_and_ragged(ea, N):
+    B, H, D, M, F = 2, 2, 64, 64, 16
+    dev, host = case(ea, B, H, N, D, M, F, "prf", 60)
+    out, S, z = run(ea, dev, F, "prf", False)
+    check(out, S, z, oracle_out(host, F, "prf", False))
+
+
+@pytest.mark.parametrize("draw", ["gaussian", "orthogonal", "sphere"])
+def test_fused_features_draws(ea, draw):
+    B, H, N, D, M, F = 2, 2, 500, 64, 32, 32
+    dev, host = case(ea, B, H, N, D, M, F, "prf", 61, draw=draw)
+    out, S, z = run(ea, dev, F, "prf", False)
+    check(out, S, z, oracle_out(host, F, "prf", False))
+
+
+@pytest.mark.parametrize("kind", ["prf", "trf"])
+@pytest.mark.parametrize("normalize", [False, True])
+def test_fused_matches_two_launches(ea, kind, normalize):
+    """Against la_feature_map + la_forward_chunked(LA_F32_FEATURES) on the same rows."""
+    B, H, N, D, M, F = 4, 4, 1000, 64, 64, 16
+    dev, _ = case(ea, B, H, N, D, M, F, kind, 62, normalize)
+    Qd, Kd, Vd, Wd = dev
+    out, S, z = run(ea, dev, F, kind, normalize)
+    fq, fk = ea.feature_map(Qd, Wd, F, kind, normalize, X2=Kd)
+    S2 = torch.empty_like(S)
+    z2 = torch.empty_like(z)
+    two = ea.forward_chunked(fq, fk, Vd, causal=True, S_out=S2, z_out=z2, features=True)
+    torch.cuda.synchronize()
+    assert rowwise_rel(out.cpu().numpy(), two.cpu().numpy()) <= 1e-5
+    assert whole_rel(S.cpu().numpy(), S2.cpu().numpy()) <= 1e-6
+    assert whole_rel(z.cpu().numpy(), z2.cpu().numpy()) <= 1e-6
+
+
+def test_fused_features_zero_rows_and_empty(ea):
+    """A zero row under normalisation stays finite; N = 0 writes a zero state."""
+    B, H, N, D, M, F = 1, 2, 200, 32, 32, 16
+    dev, host = case(ea, B, H, N, D, M, F, "prf", 63, True)
+    dev[0][0, 1, 17] = 0.0
+    dev[1][0, 0, 5] = 0.0
+    host[0][0, 1, 17] = 0.0
+    host[1][0, 0, 5] = 0.0
+    out, S, z = run(ea, dev, F, "prf", True)
+    check(out, S, z, oracle_out(host, F, "prf", True))
+    assert torch.isfinite(out).all()
+    e = torch.empty((B, H, 0, D), device=DEV)
+    S0 = torch.full((B, H, F, M), float("nan"), device=DEV)
+    z0 = torch.full((B, H, F), float("nan"), device=DEV)
+    ea.forward_features(e, e, torch.empty((B, H, 0, M), device=DEV), dev[3], F, "prf", S_out=S0, z_out=z0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(S0).item() == 0 and torch.count_nonzero(z0).item() == 0
+
+
+def test_fused_features_continue_with_decode(ea):
+    """The fused prefill's state continued by decode steps on the two-launch features:
+    every row equals the running sums over the whole sequence."""
+    B, H, D, M, F = 2, 3, 64, 64, 16
+    n0, n1 = 300, 20
+    dev, host = case(ea, B, H, n0 + n1, D, M, F, "prf", 64)
+    Qd, Kd, Vd, Wd = dev
+    ref = oracle_out(host, F, "prf", False)[0]
+    S = torch.empty((B, H, F, M), device=DEV)
+    z = torch.empty((B, H, F), device=DEV)
+    head = ea.forward_features(Qd[:, :, :n0].contiguous(), Kd[:, :, :n0].contiguous(), Vd[:, :, :n0].contiguous(),
+                               Wd, F, "prf", S_out=S, z_out=z)
+    fq, fk = ea.feature_map(Qd[:, :, n0:].contiguous(), Wd, F, "prf", X2=Kd[:, :, n0:].contiguous())
+    tail = ea.decode_steps(S, z, fq, fk, Vd[:, :, n0:].contiguous(), features=True)
+    torch.cuda.synchronize()
+    assert rowwise_rel(head.cpu().numpy(), ref[:, :, :n0]) <= TOL["f32"]
+    assert rowwise_rel(tail.cpu().numpy(), ref[:, :, n0:]) <= TOL["f32"]
+
+
+def test_fused_features_workload(ea):
+    """The random-feature workload (B=8, H=8, N=1024, D=M=64, 16 PRF features,
+    orthogonal projection) in the launch configuration the benchmark times: two
+    heads against the oracle, every head against the two-launch path."""
+    cfg = synthetic.WORKLOADS["prefill_prf16_f32_b8h8_n1024_d64"]
+    B, H, N, D, M, F = (cfg[k] for k in ("B", "H", "N", "D", "M", "F"))
+    Xq = synthetic.draw(30, synthetic.TID_Q, (B, H, N, D), cfg["sigma"], "f32")
+    Xk = synthetic.draw(30, synthetic.TID_K, (B, H, N, D), cfg["sigma"], "f32")
+    V = synthetic.draw(30, synthetic.TID_V, (B, H, N, M), 1.0, "f32")
+    W = ea.draw_projection(F, D, "orthogonal", 0)
+    Qd, Kd, Vd = (to_dev(x, "f32") for x in (Xq, Xk, V))
+    Wd = torch.from_numpy(W).to(DEV)
+    out = ea.forward_features(Qd, Kd, Vd, Wd, F, "prf")
+    fq, fk = ea.feature_map(Qd, Wd, F, "prf", X2=Kd)
+    two = ea.forward_chunked(fq, fk, Vd, causal=True, features=True)
+    torch.cuda.synchronize()
+    assert rowwise_rel(out.cpu().numpy(), two.cpu().numpy()) <= 1e-5
+    sel = (slice(3, 4), slice(5, 7))
+    ref = oracle_out((Xq[sel], Xk[sel], V[sel], W), F, "prf", False)[0]
+    assert rowwise_rel(out[sel].cpu().numpy(), ref) <= TOL["f32"]
