@@ -1239,6 +1239,13 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     f32x4 o[NC][Gc::RT][Gc::MTW];
 #pragma unroll
     for (int j = 0; j < NC; ++j) En::zero_out(o[j]);
+    // SNAP: the local state after each chunk is kept in registers and every
+    // chunk's read-out phi(Q_c) (prefix + local state) runs once, after the
+    // look-back, instead of a local read-out in the chunk loop plus a prefix
+    // correction afterwards (one state product per chunk fewer, off the chunk
+    // loop).  Used where the copies fit the register budget.
+    constexpr bool SNAP = Gc::DT * Gc::MTW * (NC - 1) <= 12;
+    f32x4 snap[SNAP ? NC - 1 : 1][Gc::DT][Gc::MTW];
 
     // loads one chunk ahead, unconditional (clamped to the segment's last chunk)
     // so the compiler's wait counts stay exact (see phase_a)
@@ -1282,10 +1289,18 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         __syncthreads();
         if (e.w == 0 && e.lane < C) sden[j * C + e.lane] = e.template row_den<true>();
         e.intra(oj);
-        if (j > 0) e.readout_mma(oj, S);
+        if (!SNAP && j > 0) e.readout_mma(oj, S);
         if (adv) {
             e.state_update(S);
             if (tid < D) z += e.z_delta();
+        }
+        if constexpr (SNAP) {
+            if (j + 1 < NC) {
+#pragma unroll
+                for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < Gc::MTW; ++i) snap[j][dt][i] = S[dt][i];
+            }
         }
     };
 #pragma unroll
@@ -1347,7 +1362,17 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         if (j < nc) {
             float inv = 0.0f;
             if (e.lane < C) inv = 1.0f / (sden[j * C + e.lane] + (has_prefix ? sqzs[j * C + e.lane] : 0.0f));
-            if (has_prefix) {
+            if constexpr (SNAP) {
+                if (has_prefix || j > 0) {
+                    f32x4 Sj[Gc::DT][Gc::MTW];
+#pragma unroll
+                    for (int dt = 0; dt < Gc::DT; ++dt)
+#pragma unroll
+                        for (int i = 0; i < Gc::MTW; ++i) Sj[dt][i] = j > 0 ? pre[dt][i] + snap[j - 1][dt][i] : pre[dt][i];
+                    e.sQ = sQs + j * C * Gc::LQ;
+                    e.readout_mma(o[j], Sj);
+                }
+            } else if (has_prefix) {
                 e.sQ = sQs + j * C * Gc::LQ;
                 e.readout_mma(o[j], pre);
             }
