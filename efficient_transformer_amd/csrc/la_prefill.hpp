@@ -857,6 +857,11 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const 
 // With G == 1 there is no look-back and no workspace.
 // ---------------------------------------------------------------------------
 constexpr long kSpinLimit = 1L << 22;
+// One-pass kernel: with at most this many segments per head no inclusive
+// prefix is published; a look-back then sums every earlier aggregate (at most
+// 15 slots, read from the device-wide cache), which costs less than the extra
+// store and flag on every workgroup's path to its outputs.
+constexpr int kOnePassInclusiveMinSegments = 16;
 
 // Decoupled look-back of segment s > 0 of head bh (every thread of the
 // workgroup calls it).  Wavefront 0 polls the flags of segments s-1, s-2, ...
@@ -935,9 +940,10 @@ __device__ __forceinline__ void publish_inclusive(const Engine<T, D, M, C, PHI> 
 }
 
 // Called by the last segment of every head once its look-back is done.  Every
-// segment of that head has then read the epoch (each published a flag tagged
-// with it, and a segment only publishes its inclusive state after its own
-// look-back), so when the last of the n_heads heads has counted, no workgroup of
+// segment of that head has then read the epoch: the look-back saw a flag tagged
+// with it from each earlier segment, directly or through an inclusive state
+// (published only after that segment's own look-back saw the flags before it).
+// So when the last of the n_heads heads has counted, no workgroup of
 // the call will read the epoch again: that one resets the counter and advances
 // the epoch (every flag of the call becomes stale).  One atomic per head instead
 // of one per workgroup.
@@ -1332,7 +1338,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const bool has_prefix = (G_ > 1 && s > 0) || init;
     if (G_ > 1 && s > 0) {
         failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
-        if (!last) publish_inclusive(e, ws, my, ep, pre, zpre, S, z, failed);
+        if (!last && G_ > kOnePassInclusiveMinSegments) publish_inclusive(e, ws, my, ep, pre, zpre, S, z, failed);
     }
     if (last && want_final) {
         f32x4 fin[Gc::DT][Gc::MTW];
