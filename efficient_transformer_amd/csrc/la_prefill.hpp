@@ -917,6 +917,55 @@ __device__ __forceinline__ bool look_back(const Engine<T, D, M, C, PHI> &e, cons
     return true;
 }
 
+// Look-back without inclusive states (one-pass kernel, at most
+// kOnePassInclusiveMinSegments segments per head): the aggregates of segments
+// 0 .. s-1 are summed in segment order, each run of consecutive ready ones as
+// soon as wavefront 0 sees its flags, so the slots that are ready early are
+// read while the later ones are still being computed.  Bounded waits as in
+// look_back; sh_word[0] and [1] alternate between rounds (wavefront 0 writes a
+// word again only after every wavefront has passed the barrier of the round
+// in between).
+template <typename T, int D, int M, int C, bool PHI>
+__device__ __forceinline__ bool look_back_in_order(const Engine<T, D, M, C, PHI> &e, const FusedWs &ws,
+                                                   unsigned *sh_word, int bh, int s, int G_, unsigned ep,
+                                                   f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW],
+                                                   float &zpre) {
+    using Gc = Cfg<T, D, M, C>;
+    const size_t h0 = (size_t)bh * G_;
+    const unsigned *fl = ws.flags + h0;
+    int next = 0;  // segments [0, next) summed
+    for (int round = 0; next < s; ++round) {
+        unsigned *word = sh_word + (round & 1);
+        if (e.w == 0) {
+            int ready = -1;
+            long spins = 0;
+            while (true) {
+                const int j = next + e.lane;
+                unsigned f = 0u;
+                if (j < s) f = __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool ok = j < s && (f & ~3u) == ep && (f & 3u) != 0u;
+                const unsigned long long okm = __ballot(ok);
+                if (okm & 1ull) {  // lanes 0 .. r-1 ready
+                    ready = okm == ~0ull ? 64 : __builtin_ctzll(~okm);
+                    break;
+                }
+                if (++spins > kSpinLimit) {
+                    if (e.lane == 0) __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (e.lane == 0) *word = (unsigned)(ready + 1);
+        }
+        __syncthreads();
+        const int r = (int)*word - 1;
+        if (r < 0) return false;
+        e.state_add_slots(pre, zpre, ws.agg + (h0 + next) * Gc::EP, ws.agg + h0 * Gc::EP, next + 1, next + r);
+        next += r;
+    }
+    return true;
+}
+
 // Publish the inclusive prefix pre + acc of segment `my` (NaN after a failed look-back).
 template <typename T, int D, int M, int C, bool PHI>
 __device__ __forceinline__ void publish_inclusive(const Engine<T, D, M, C, PHI> &e, const FusedWs &ws, size_t my,
@@ -1337,8 +1386,12 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     bool failed = false;
     const bool has_prefix = (G_ > 1 && s > 0) || init;
     if (G_ > 1 && s > 0) {
-        failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
-        if (!last && G_ > kOnePassInclusiveMinSegments) publish_inclusive(e, ws, my, ep, pre, zpre, S, z, failed);
+        if (G_ > kOnePassInclusiveMinSegments) {
+            failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
+            if (!last) publish_inclusive(e, ws, my, ep, pre, zpre, S, z, failed);
+        } else {
+            failed = !look_back_in_order(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
+        }
     }
     if (last && want_final) {
         f32x4 fin[Gc::DT][Gc::MTW];
