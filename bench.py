@@ -142,11 +142,24 @@ def bench_prefill(cfg, steps, warmup, dev):
         step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    us_kernel = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    us_kernel = sum(per) / steps
+    # the same launches on one buffer set (inputs warm in the last-level cache)
+    for i in range(5):
+        step(0)
+    torch.cuda.synchronize()
+    evw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evw[i][0].record(stream)
+        step(0)
+        evw[i][1].record(stream)
+    torch.cuda.synchronize()
+    warm = sorted(a.elapsed_time(b) * 1e3 for a, b in evw)
     del sets
     torch.cuda.empty_cache()
     return dict(chunk=C, segments=G, nsets=nsets, ms_per_step=ms, tokens_per_s=B * N / (ms * 1e-3),
-                bytes=nbytes, flops_min=prefill_flops_min(cfg), us_kernel=us_kernel)
+                bytes=nbytes, flops_min=prefill_flops_min(cfg), us_kernel=us_kernel,
+                us_kernel_median=per[steps // 2], us_kernel_min=per[0], us_warm_median=warm[steps // 2])
 
 
 def bench_decode(cfg, reps, dev, warm_steps=64):
@@ -194,6 +207,43 @@ def bench_decode(cfg, reps, dev, warm_steps=64):
                 bytes_per_step=per_step_bytes,
                 effective_GBs=per_step_bytes * T / (best * 1e-3) / 1e9,
                 kernel_GBs=per_step_bytes / (us_kernel * 1e-6) / 1e9)
+
+
+def bench_decode_hbm(dev, B=4096, H=8, D=64, M=64, T=32, reps=3):
+    """Decode steps with a state larger than the last-level cache (4096 streams x H=8: 545 MB),
+    so every step reads and writes the state in HBM."""
+    import torch
+    import efficient_transformer_amd as ea
+    import synthetic
+
+    cfg = dict(B=B, H=H, D=D, M=M, T=T, dtype="f32")
+    q = synthetic.draw_torch(5, synthetic.TID_DQ, (T, B, H, D), 1.0, "f32", dev)
+    k = synthetic.draw_torch(5, synthetic.TID_DK, (T, B, H, D), 1.0, "f32", dev)
+    v = synthetic.draw_torch(5, synthetic.TID_DV, (T, B, H, M), 1.0, "f32", dev)
+    S = torch.zeros((B, H, D, M), device=dev)
+    z = torch.zeros((B, H, D), device=dev)
+    out = torch.empty((B, H, M), device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for t in range(4):
+        ea.decode_step(S, z, q[t], k[t], v[t], out=out, stream=stream)
+    best = None
+    for _ in range(reps):
+        S.zero_()
+        z.zero_()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(T):
+            ea.decode_step(S, z, q[t], k[t], v[t], out=out, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    nb = decode_bytes_per_step(cfg)
+    del q, k, v, S, z
+    torch.cuda.empty_cache()
+    us = best * 1e3 / T
+    return dict(us_per_step=us, bytes_per_step=nb, GBs=nb / (us * 1e-6) / 1e9, tokens_per_s=B / (us * 1e-6))
 
 
 def backward_bytes(cfg) -> int:
@@ -526,6 +576,9 @@ def main():
                    "B": cfg["B"], "H": cfg["H"], "N": cfg["N"], "D": cfg["D"], "M": cfg["M"],
                    "chunk": pre["chunk"], "segments": pre["segments"], "buffer_sets": pre["nsets"],
                    "parallelism": "single GPU"},
+        "prefill_kernel_us": {"mean": round(pre["us_kernel"], 2), "median": round(pre["us_kernel_median"], 2),
+                              "min": round(pre["us_kernel_min"], 2),
+                              "warm_same_buffers_median": round(pre["us_warm_median"], 2)},
         "roofline": roofline,
     }
 
@@ -542,6 +595,14 @@ def main():
             "kernel_us_event": round(dec["us_kernel_event"], 3),
             "bytes_per_step": dec["bytes_per_step"],
             "note": "the 34 MB state stays resident in the 256 MB last-level cache between steps"}
+        log("decode, state beyond the last-level cache ...")
+        dh = bench_decode_hbm(dev)
+        log(f"decode (HBM): {dh}")
+        line["decode_hbm"] = {
+            "workload": "recurrent decode, fp32, 4096 streams x H=8, D=M=64 (545 MB state), 32 steps",
+            "tokens_per_s": round(dh["tokens_per_s"], 1), "us_per_step": round(dh["us_per_step"], 2),
+            "bytes_per_step": dh["bytes_per_step"], "GBs": round(dh["GBs"], 1),
+            "frac_hbm_peak": round(dh["GBs"] / HBM_PEAK_GBS, 4)}
         others = {}
         for name, outdt in (("prefill_bf16_b4h8_n3072_d64", "fp32"), ("prefill_bf16_b1h16_n65536_d128", "fp32"),
                             ("prefill_bf16_b4h8_n3072_d64", "bf16"), ("prefill_bf16_b1h16_n65536_d128", "bf16")):
