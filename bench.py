@@ -456,9 +456,30 @@ def cpu_baseline(cfg, target_s=12.0):
         el = time.perf_counter() - t0
         if el >= target_s or reps >= 1000:
             break
+    # one thread on two of the 64 heads; tokens/s scaled to all H heads of a token
+    Q1, K1, V1 = (x[:1, :2] for x in (Qf, Kf, Vf))
+    t1 = time.perf_counter()
+    reps1 = 0
+    while True:
+        oracle.causal(Q1, K1, V1, threads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= target_s / 4 or reps1 >= 1000:
+            break
+    one = N * reps1 * 2 / cfg["H"] / el1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return dict(value=B * N * reps / el, unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"{reps} full causal passes over the B={B} H={cfg['H']} N={N} D=M={cfg['D']} "
-                       f"fp32 workload ({el:.1f} s wall, fp64, {threads} threads)")
+                       f"fp32 workload ({el:.1f} s wall, fp64, {threads} threads)",
+                one_thread_value=round(one, 1),
+                one_thread_sample=f"{reps1} passes over 2 heads (B=1, N={N}) on one thread, {el1:.1f} s; "
+                                  f"tokens/s counts a token as all {cfg['H']} heads",
+                cpu_model=model)
 
 
 def profile_run(dev):
