@@ -43,6 +43,10 @@ namespace {
 
 constexpr long kScanSpinLimit = 1L << 22;
 constexpr int kScanWaves = 4;
+// With at most this many groups per head no inclusive state is published: the
+// look-back reads every earlier aggregate (M + 2 floats each) in one batch,
+// and wavefront 0 no longer waits for a store before writing its rows.
+constexpr int kScanInclusiveMinGroups = 16;
 
 template <int D, int M>
 struct ScanCfg {
@@ -339,7 +343,7 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         for (int c = 0; c < CPL; ++c) pw[c] = 0.0f;
         add_lds(spre);
         failed = spre[M + 2] != 0.0f;
-        if (w == 0 && grp > 0 && !last_grp) {
+        if (w == 0 && grp > 0 && !last_grp && NG > kScanInclusiveMinGroups) {
             // the group's inclusive state = prefix + aggregate, published once the
             // other wavefronts have their prefix (later groups can use aggregates)
             const float mn = fmaxf(pm, gm);
