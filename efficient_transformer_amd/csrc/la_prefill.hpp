@@ -864,104 +864,89 @@ constexpr long kSpinLimit = 1L << 22;
 constexpr int kOnePassInclusiveMinSegments = 16;
 
 // Decoupled look-back of segment s > 0 of head bh (every thread of the
-// workgroup calls it).  Wavefront 0 polls the flags of segments s-1, s-2, ...
-// (one lane per segment, 64 at a time, relaxed loads) until it finds the
-// nearest segment j* whose inclusive prefix is published (segment 0's
-// aggregate is its inclusive prefix) with every aggregate between j* and s
-// ready; the prefix is then incl(j*) + agg(j*+1) + ... + agg(s-1), added into
-// pre / zpre.  Waits are bounded (kSpinLimit polls); on a timeout the error
-// word of the workspace is set and false is returned.
+// workgroup calls it); the prefix of the earlier segments is added into pre /
+// zpre.  Wavefront 0 polls the flags (one lane per segment, 64 at a time,
+// relaxed loads) and the workgroup then sums the slots it names, in rounds:
+//   in_order = false: one round, once it finds the nearest segment j* whose
+//     inclusive prefix is published (segment 0's aggregate is its inclusive
+//     prefix) with every aggregate between j* and s ready: incl(j*) +
+//     agg(j*+1) + ... + agg(s-1);
+//   in_order = true (no inclusive states are published): the aggregates of
+//     segments 0 .. s-1 in segment order, each run of consecutive ready ones
+//     as soon as its flags are seen, so the slots of segments that finished
+//     early are read while later ones still compute.
+// Each round passes (first segment + 1, count | inclusive bit) through two LDS
+// words; rounds alternate between sh_word[0..1] and [2..3] (wavefront 0 writes
+// a pair again only after every wavefront has passed the barrier of the round
+// in between).  One code path for both modes keeps one copy of the slot sums
+// (and its registers) in the kernel.  Waits are bounded (kSpinLimit polls); on
+// a timeout the error word of the workspace is set and false is returned.
 template <typename T, int D, int M, int C, bool PHI>
 __device__ __forceinline__ bool look_back(const Engine<T, D, M, C, PHI> &e, const FusedWs &ws, unsigned *sh_word, int bh,
                                           int s, int G_, unsigned ep,
-                                          f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &zpre) {
-    using Gc = Cfg<T, D, M, C>;
-    if (e.w == 0) {
-        const unsigned *fl = ws.flags + (size_t)bh * G_;
-        int base = s - 1;
-        int jstar = -1;
-        long spins = 0;
-        while (true) {
-            const int j = base - e.lane;
-            unsigned f = 0u;
-            if (j >= 0) f = __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const bool ok = j >= 0 && (f & ~3u) == ep && (f & 3u) != 0u;
-            const bool inc = ok && ((f & 3u) == 2u || j == 0);
-            const unsigned long long okm = __ballot(ok), incm = __ballot(inc);
-            if (incm != 0ull) {
-                const int first = __builtin_ctzll(incm);
-                const unsigned long long need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
-                if ((okm & need) == need) {
-                    jstar = base - first;
-                    break;
-                }
-            } else if (okm == ~0ull) {
-                base -= 64;  // 64 aggregates ready, none inclusive: look further back
-                continue;
-            }
-            if (++spins > kSpinLimit) {
-                if (e.lane == 0) __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                jstar = -1;
-                break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        if (e.lane == 0) sh_word[0] = (unsigned)(jstar + 1);
-    }
-    __syncthreads();
-    const int jstar = (int)sh_word[0] - 1;
-    if (jstar < 0) return false;
-    const size_t h0 = (size_t)bh * G_;
-    e.state_add_slots(pre, zpre, (jstar == 0 ? ws.agg : ws.incl) + (h0 + jstar) * Gc::EP, ws.agg + h0 * Gc::EP,
-                      jstar + 1, s);
-    return true;
-}
-
-// Look-back without inclusive states (one-pass kernel, at most
-// kOnePassInclusiveMinSegments segments per head): the aggregates of segments
-// 0 .. s-1 are summed in segment order, each run of consecutive ready ones as
-// soon as wavefront 0 sees its flags, so the slots that are ready early are
-// read while the later ones are still being computed.  Bounded waits as in
-// look_back; sh_word[0] and [1] alternate between rounds (wavefront 0 writes a
-// word again only after every wavefront has passed the barrier of the round
-// in between).
-template <typename T, int D, int M, int C, bool PHI>
-__device__ __forceinline__ bool look_back_in_order(const Engine<T, D, M, C, PHI> &e, const FusedWs &ws,
-                                                   unsigned *sh_word, int bh, int s, int G_, unsigned ep,
-                                                   f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW],
-                                                   float &zpre) {
+                                          f32x4 (&pre)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &zpre,
+                                          bool in_order) {
     using Gc = Cfg<T, D, M, C>;
     const size_t h0 = (size_t)bh * G_;
     const unsigned *fl = ws.flags + h0;
-    int next = 0;  // segments [0, next) summed
+    int next = 0;  // in order: segments [0, next) summed
     for (int round = 0; next < s; ++round) {
-        unsigned *word = sh_word + (round & 1);
+        unsigned *word = sh_word + 2 * (round & 1);
         if (e.w == 0) {
-            int ready = -1;
+            int from = -1, count = 0;
+            bool incl_first = false;
+            int base = s - 1;  // inclusive mode: the newest segment of the polled window
             long spins = 0;
             while (true) {
-                const int j = next + e.lane;
+                const int j = in_order ? next + e.lane : base - e.lane;
+                const bool valid = in_order ? j < s : j >= 0;
                 unsigned f = 0u;
-                if (j < s) f = __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const bool ok = j < s && (f & ~3u) == ep && (f & 3u) != 0u;
+                if (valid) f = __hip_atomic_load(fl + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const bool ok = valid && (f & ~3u) == ep && (f & 3u) != 0u;
                 const unsigned long long okm = __ballot(ok);
-                if (okm & 1ull) {  // lanes 0 .. r-1 ready
-                    ready = okm == ~0ull ? 64 : __builtin_ctzll(~okm);
-                    break;
+                if (in_order) {
+                    if (okm & 1ull) {  // lanes 0 .. count-1 ready
+                        from = next;
+                        count = okm == ~0ull ? 64 : __builtin_ctzll(~okm);
+                        break;
+                    }
+                } else {
+                    const bool inc = ok && ((f & 3u) == 2u || j == 0);
+                    const unsigned long long incm = __ballot(inc);
+                    if (incm != 0ull) {
+                        const int first = __builtin_ctzll(incm);
+                        const unsigned long long need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
+                        if ((okm & need) == need) {
+                            from = base - first;
+                            count = s - from;
+                            incl_first = from != 0;
+                            break;
+                        }
+                    } else if (okm == ~0ull) {
+                        base -= 64;  // 64 aggregates ready, none inclusive: look further back
+                        continue;
+                    }
                 }
                 if (++spins > kSpinLimit) {
                     if (e.lane == 0) __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    from = -1;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
-            if (e.lane == 0) *word = (unsigned)(ready + 1);
+            if (e.lane == 0) {
+                word[0] = (unsigned)(from + 1);
+                word[1] = (unsigned)count | (incl_first ? 0x80000000u : 0u);
+            }
         }
         __syncthreads();
-        const int r = (int)*word - 1;
-        if (r < 0) return false;
-        e.state_add_slots(pre, zpre, ws.agg + (h0 + next) * Gc::EP, ws.agg + h0 * Gc::EP, next + 1, next + r);
-        next += r;
+        const int from = (int)word[0] - 1;
+        if (from < 0) return false;
+        const int count = (int)(word[1] & 0x7fffffffu);
+        const bool incl_first = (word[1] >> 31) != 0u;
+        e.state_add_slots(pre, zpre, (incl_first ? ws.incl : ws.agg) + (h0 + from) * Gc::EP, ws.agg + h0 * Gc::EP,
+                          from + 1, from + count);
+        next = from + count;
     }
     return true;
 }
@@ -1016,7 +1001,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     using Gc = Cfg<T, D, M, C>;
     using En = Engine<T, D, M, C, PHI>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
-    __shared__ unsigned sh_word[2];
+    __shared__ unsigned sh_word[4];
     En e(smem);
     const int tid = e.tid;
 
@@ -1094,7 +1079,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 
     bool failed = false;
     if (G_ > 1 && s > 0) {
-        failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
+        failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre, false);
         if (!last) publish_inclusive(e, ws, (size_t)bh * G_ + s, ep, pre, zpre, acc, zacc, failed);
     }
     if (G_ > 1 && last && want_final) {
@@ -1247,7 +1232,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     static_assert(!FEAT || (std::is_same<T, float>::value && !PHI), "fused features: fp32 rows, no elu map");
     __shared__ __attribute__((aligned(16))) unsigned char smem[L1::bytes];
     __shared__ __attribute__((aligned(16))) float sfeat[FEAT ? FL::nRaw + FL::nW : 4];
-    __shared__ unsigned sh_word[2];
+    __shared__ unsigned sh_word[4];
     En e(smem + L1::shift);
     T *const sQs = reinterpret_cast<T *>(smem);
     float *const sden = reinterpret_cast<float *>(smem + L1::oDen);
@@ -1299,7 +1284,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     // look-back, instead of a local read-out in the chunk loop plus a prefix
     // correction afterwards (one state product per chunk fewer, off the chunk
     // loop).  Used where the copies fit the register budget.
-    constexpr bool SNAP = Gc::DT * Gc::MTW * (NC - 1) <= 12;
+    constexpr bool SNAP = C >= 32 && Gc::DT * Gc::MTW * (NC - 1) <= 12;
     f32x4 snap[SNAP ? NC - 1 : 1][Gc::DT][Gc::MTW];
 
     // loads one chunk ahead, unconditional (clamped to the segment's last chunk)
@@ -1386,12 +1371,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     bool failed = false;
     const bool has_prefix = (G_ > 1 && s > 0) || init;
     if (G_ > 1 && s > 0) {
-        if (G_ > kOnePassInclusiveMinSegments) {
-            failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
-            if (!last) publish_inclusive(e, ws, my, ep, pre, zpre, S, z, failed);
-        } else {
-            failed = !look_back_in_order(e, ws, sh_word, bh, s, G_, ep, pre, zpre);
-        }
+        const bool in_order = G_ <= kOnePassInclusiveMinSegments;
+        failed = !look_back(e, ws, sh_word, bh, s, G_, ep, pre, zpre, in_order);
+        if (!in_order && !last) publish_inclusive(e, ws, my, ep, pre, zpre, S, z, failed);
     }
     if (last && want_final) {
         f32x4 fin[Gc::DT][Gc::MTW];
