@@ -433,7 +433,8 @@ def causal_kernel_name(cfg, chunk, segments) -> str:
     kind = "onepass_causal_kernel" if cps <= 4 else "fused_causal_kernel"
     t = "float" if cfg["dtype"] == "f32" else "bf16"
     ot = "bf16" if cfg.get("out") == "bf16" else "float"
-    extra = ", 0" if kind == "onepass_causal_kernel" else ""  # the one-pass kernel's raw-row width (0: no map)
+    # the one-pass kernel's raw-row width (0: no feature map) and raw-row type
+    extra = f", 0, {t}" if kind == "onepass_causal_kernel" else ""
     return f"{kind}<{t}, {cfg['D']}, {cfg['M']}, {chunk}, true, {ot}{extra}>"
 
 

@@ -581,8 +581,10 @@ LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t 
 }
 
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                               int64_t N, int64_t D, int64_t M, const float *W, int64_t F, int kind, int flags,
-                               void *workspace, size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
+                               int64_t N, int64_t D, int64_t M, int dtype, const float *W, int64_t F, int kind,
+                               int flags, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
+                               void *stream) {
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
     if (kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
     if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
     Plan p;
@@ -605,9 +607,13 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
     if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) return LA_ERR_WORKSPACE;
     if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
-    return hip_status(la::prefill_features((int)D, (int)F, (int)M, Q, K, V, W, kind,
-                                           (flags & LA_FEATURE_NORMALIZE) != 0, out, workspace, (int)BH, (int)N,
-                                           p.segments, p.chunks_per_segment, S_out, z_out, s));
+    const int norm = (flags & LA_FEATURE_NORMALIZE) != 0;
+    return hip_status(dtype == LA_F32
+                          ? la::prefill_features_f32((int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out, workspace,
+                                                     (int)BH, (int)N, p.segments, p.chunks_per_segment, S_out, z_out, s)
+                          : la::prefill_features_bf16((int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out, workspace,
+                                                      (int)BH, (int)N, p.segments, p.chunks_per_segment, S_out, z_out,
+                                                      s));
 }
 
 // ---- feature maps ----------------------------------------------------------

@@ -1,8 +1,5 @@
-// The one-pass causal kernel with the random-feature map fused into the staging
-// of Q and K: fp32 rows DI wide (16, 32, 64, 128), F features (16, 32, 64),
-// M in {16, 32, 64, 128}, chunk 32.
-#include "la_launch.hpp"
-#include "la_prefill.hpp"
+// Fused random features, fp32 raw rows (and the shape check shared by both types).
+#include "la_feat_fused.hpp"
 
 namespace la {
 
@@ -18,20 +15,11 @@ bool prefill_features_supported(int DI, int F, int M) {
     return false;
 }
 
-hipError_t prefill_features(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
-                            int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS, float *S_out,
-                            float *z_out, hipStream_t stream) {
-#define X(DI_, F_, M_)                                                                                   \
-    if (DI == DI_ && F == F_ && M == M_)                                                                 \
-        return run_onepass_features<DI_, F_, M_, kFusedFeatureChunk>(Q, K, V, W, kind, norm, out, ws, BH, N, G, \
-                                                                     CPS, S_out, z_out, stream);
-#define XM(DI_, F_) X(DI_, F_, 16) X(DI_, F_, 32) X(DI_, F_, 64) X(DI_, F_, 128)
-#define XF(DI_) XM(DI_, 16) XM(DI_, 32) XM(DI_, 64)
-    XF(16) XF(32) XF(64) XF(128)
-#undef XF
-#undef XM
-#undef X
-    return hipErrorInvalidValue;
+hipError_t prefill_features_f32(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
+                                int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
+                                float *S_out, float *z_out, hipStream_t stream) {
+    return prefill_features_typed<float>(DI, F, M, Q, K, V, W, kind, norm, out, ws, BH, N, G, CPS, S_out, z_out,
+                                         stream);
 }
 
 }  // namespace la

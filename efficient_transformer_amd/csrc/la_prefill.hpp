@@ -141,6 +141,35 @@ struct Stage {
         else
             store_natural_impl<PHI, true>(dst, ld, row0, N, tid);
     }
+    // fp32 copy dst[row][col] of the tile (natural layout, no phi); rows at or
+    // past N are zeroed.  For fp32 tiles this is store_natural<false>.
+    __device__ __forceinline__ void store_natural_f32(float *dst, int ld, int row0, int N, int tid) const {
+        if constexpr (F32) {
+            store_natural<false>(dst, ld, row0, N, tid);
+        } else {
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+                const int item = tid + p * NT;
+                if (ITEMS % NT == 0 || item < ITEMS) {
+                    const int rq = item / NV, cv = item % NV;
+#pragma unroll
+                    for (int i = 0; i < RPI; ++i) {
+                        const int row = rq * RPI + i;
+                        const float keep = row0 + row < N ? 1.0f : 0.0f;
+                        const bf16x8 x = __builtin_bit_cast(bf16x8, r[p][i]);
+                        f32x4 lo, hi;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            lo[j] = (float)x[j] * keep;
+                            hi[j] = (float)x[4 + j] * keep;
+                        }
+                        *reinterpret_cast<f32x4 *>(dst + row * ld + cv * 8) = lo;
+                        *reinterpret_cast<f32x4 *>(dst + row * ld + cv * 8 + 4) = hi;
+                    }
+                }
+            }
+        }
+    }
     template <bool PHI, bool TAIL>
     __device__ __forceinline__ void store_natural_impl(T *dst, int ld, int row0, int N, int tid) const {
 #pragma unroll
@@ -767,11 +796,13 @@ struct Engine {
 // Phase A: sum the state over chunks [c0, c1) into acc / z (thread tid < D owns z[tid]).
 // Leaves the last chunk's phi(K), V in LDS.  Global loads run two chunks ahead.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, int DK = D>  // DK: width of the K rows in memory
+// DK: width of the K rows in memory; TI: their element type (the engine's T
+// unless raw rows are mapped to fp32 features while staged)
+template <typename T, int D, int M, int C, int DK = D, typename TI = T>
 struct KVBuf {
-    Stage<T, C, DK, Cfg<T, D, M, C>::THREADS> k;
-    Stage<T, C, M, Cfg<T, D, M, C>::THREADS> v;
-    __device__ __forceinline__ void load(const T *Kh, const T *Vh, int c, int N, int tid) {
+    Stage<TI, C, DK, Cfg<T, D, M, C>::THREADS> k;
+    Stage<TI, C, M, Cfg<T, D, M, C>::THREADS> v;
+    __device__ __forceinline__ void load(const TI *Kh, const TI *Vh, int c, int N, int tid) {
         k.load(Kh, c * C, N, tid);
         v.load(Vh, c * C, N, tid);
     }
@@ -1215,11 +1246,12 @@ struct OnePassLds {
     static constexpr bool fits = (bytes + 64) * Gc::MIN_WG <= kMaxLds;
 };
 
-// DI > 0: Q and K hold raw fp32 rows DI wide and the random-feature map (W, fkind,
-// fnorm) is applied while staging them (D is then the feature dimension F).
-template <typename T, int D, int M, int C, bool PHI = true, typename OT = float, int DI = 0>
+// DI > 0: Q and K hold raw rows DI wide (element type TI: fp32 or bf16, V too)
+// and the random-feature map (W, fkind, fnorm) is applied in fp32 while staging
+// them (D is then the feature dimension F, the engine fp32).
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float, int DI = 0, typename TI = T>
 __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void onepass_causal_kernel(
-    const T *__restrict__ Q, const T *__restrict__ K, const T *__restrict__ V, OT *__restrict__ out,
+    const TI *__restrict__ Q, const TI *__restrict__ K, const TI *__restrict__ V, OT *__restrict__ out,
     void *ws_raw, int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out,
     const float *S_in, const float *z_in, const float *__restrict__ W, int fkind, int fnorm) {
     using Gc = Cfg<T, D, M, C>;
@@ -1229,7 +1261,8 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     constexpr bool FEAT = DI > 0;
     constexpr int DQ = FEAT ? DI : D;  // width of the Q, K rows in memory
     using FL = FeatLds<FEAT ? DI : 16, D, C>;
-    static_assert(!FEAT || (std::is_same<T, float>::value && !PHI), "fused features: fp32 rows, no elu map");
+    static_assert(!FEAT || (std::is_same<T, float>::value && !PHI), "fused features: fp32 engine, no elu map");
+    static_assert(FEAT || std::is_same<TI, T>::value, "raw rows of another type only with fused features");
     __shared__ __attribute__((aligned(16))) unsigned char smem[L1::bytes];
     __shared__ __attribute__((aligned(16))) float sfeat[FEAT ? FL::nRaw + FL::nW : 4];
     __shared__ unsigned sh_word[4];
@@ -1254,9 +1287,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS;
     const int nc = min(CPS, n_chunks - c0);  // 1 .. NC (the planner guarantees it)
-    const T *Qh = Q + (size_t)bh * N * DQ;
-    const T *Kh = K + (size_t)bh * N * DQ;
-    const T *Vh = V + (size_t)bh * N * M;
+    const TI *Qh = Q + (size_t)bh * N * DQ;
+    const TI *Kh = K + (size_t)bh * N * DQ;
+    const TI *Vh = V + (size_t)bh * N * M;
     OT *Oh = out + (size_t)bh * N * M;
     const bool last = s == G_ - 1;
     const bool want_final = S_out != nullptr;
@@ -1290,8 +1323,8 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     // loads one chunk ahead, unconditional (clamped to the segment's last chunk)
     // so the compiler's wait counts stay exact (see phase_a)
     const int clast = c0 + nc - 1;
-    Stage<T, C, DQ, Gc::THREADS> q;
-    KVBuf<T, D, M, C, DQ> b;
+    Stage<TI, C, DQ, Gc::THREADS> q;
+    KVBuf<T, D, M, C, DQ, TI> b;
     q.load(Qh, c0 * C, N, tid);
     b.load(Kh, Vh, c0, N, tid);
     auto step = [&](int j, f32x4 (&oj)[Gc::RT][Gc::MTW]) {
@@ -1300,9 +1333,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         e.sQ = sQs + j * C * Gc::LQ;
         if constexpr (FEAT) {
             // raw rows to LDS, then the features of q and k into the engine's tiles
-            q.template store_natural<false>(sRawQ, FL::LX, row0, N, tid);
-            b.k.template store_natural<false>(sRawK, FL::LX, row0, N, tid);
-            b.v.template store_natural<false>(e.sV, Gc::LV, row0, N, tid);
+            q.store_natural_f32(sRawQ, FL::LX, row0, N, tid);
+            b.k.store_natural_f32(sRawK, FL::LX, row0, N, tid);
+            b.v.store_natural_f32(e.sV, Gc::LV, row0, N, tid);
             if (tid < D) e.sz[tid] = z;
             __syncthreads();
             const int PT = (P + 15) / 16, jobs = 2 * Gc::RT * PT;
@@ -1518,7 +1551,7 @@ constexpr bool onepass_features_fit() {
            (OnePassLds<float, F, M, C>::bytes + FeatLds<DI, F, C>::bytes + 64) * Gc::MIN_WG <= kMaxLds;
 }
 
-template <int DI, int F, int M, int C>
+template <int DI, int F, int M, int C, typename TI = float>
 hipError_t run_onepass_features(const void *Q, const void *K, const void *V, const float *W, int fkind, int fnorm,
                                 float *out, void *ws, int BH, int N, int G_, int CPS, float *S_out, float *z_out,
                                 hipStream_t stream) {
@@ -1528,8 +1561,8 @@ hipError_t run_onepass_features(const void *Q, const void *K, const void *V, con
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((onepass_causal_kernel<float, F, M, C, false, float, DI>), dim3((unsigned)(BH * G_)),
-                           dim3(Gc::THREADS), 0, stream, (const float *)Q, (const float *)K, (const float *)V, out, ws,
+        hipLaunchKernelGGL((onepass_causal_kernel<float, F, M, C, false, float, DI, TI>), dim3((unsigned)(BH * G_)),
+                           dim3(Gc::THREADS), 0, stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws,
                            BH, N, G_, CPS, S_out, z_out, nullptr, nullptr, W, fkind, fnorm);
         return hipGetLastError();
     }

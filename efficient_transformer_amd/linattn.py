@@ -54,8 +54,8 @@ SIGNATURES = {
     "la_decode_steps": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_feature_map": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp, _i64, _int, _int, _vp]),
     "la_forward_features_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
-    "la_forward_features": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp, _i64, _int, _int,
-                                   _vp, _sz, _vp, _vp, _vp]),
+    "la_forward_features": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _int,
+                                   _int, _vp, _sz, _vp, _vp, _vp]),
 }
 
 
@@ -474,7 +474,8 @@ def feature_map(X, W, F, kind="prf", normalize=False, out=None, X2=None, out2=No
 def forward_features(Q, K, V, W, F, kind="prf", normalize=False, out=None, workspace=None, S_out=None,
                      z_out=None, stream=None):
     """Causal attention over random features computed inside the attention kernel:
-    Q, K [B,H,N,D], V [B,H,N,M] float32 (raw rows), W as for feature_map ("prf":
+    Q, K [B,H,N,D], V [B,H,N,M] float32 or bfloat16 (raw rows; the map and the
+    attention run in fp32 either way), W as for feature_map ("prf":
     [F, D], "trf": [F/2, D]) -> out [B,H,N,M] float32.  S_out [B,H,F,M] / z_out
     [B,H,F] receive the final state over the features.  Raises LinAttnError
     (LA_ERR_UNSUPPORTED) where the fused kernel does not run the shape; feature_map
@@ -489,9 +490,10 @@ def forward_features(Q, K, V, W, F, kind="prf", normalize=False, out=None, works
     k = FEATURE_KINDS[kind]
     if k == LA_FEATURE_ELU:
         raise ValueError("forward_features takes 'prf' or 'trf' (elu+1 is forward_chunked itself)")
-    _require(Q, "Q", (B, H, N, D), torch.float32, dev)
-    _require(K, "K", (B, H, N, D), torch.float32, dev)
-    _require(V, "V", (B, H, N, M), torch.float32, dev)
+    _require(Q, "Q", (B, H, N, D))
+    _require(K, "K", (B, H, N, D), Q.dtype, dev)
+    _require(V, "V", (B, H, N, M), Q.dtype, dev)
+    dt = _dtype_code(Q)
     _require(W, "W", ((F if k == LA_FEATURE_PRF else F // 2), D), torch.float32, dev)
     if out is None:
         out = torch.empty((B, H, N, M), dtype=torch.float32, device=dev)
@@ -505,7 +507,7 @@ def forward_features(Q, K, V, W, F, kind="prf", normalize=False, out=None, works
     if workspace is None and need > 0:
         workspace = _cached_workspace(need, dev, stream, ("features", B * H, N, D, M, F))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().la_forward_features(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _ptr(W), F, k,
+    st = lib().la_forward_features(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, dt, _ptr(W), F, k,
                                    LA_FEATURE_NORMALIZE if normalize else 0, _ptr(workspace), wbytes,
                                    _ptr(S_out), _ptr(z_out), _stream(stream, dev))
     _check(st, "la_forward_features")

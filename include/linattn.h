@@ -342,9 +342,11 @@ LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2
  * LA_FEATURE_PRF and LA_FEATURE_TRF, flag LA_FEATURE_NORMALIZE) while they are
  * staged, then attended to as with la_forward_chunked on LA_F32_FEATURES
  * inputs; the features never reach memory.
- * Q, K [B][H][N][D] fp32 (raw rows), V [B][H][N][M] fp32, W as for
- * la_feature_map, out [B][H][N][M] fp32; S_out [B][H][F][M], z_out [B][H][F]
- * optional (both or neither): the final state over the features.
+ * Q, K [B][H][N][D] (raw rows) and V [B][H][N][M], all of element type dtype
+ * (LA_F32 or LA_BF16; bf16 values are widened exactly, the map and the
+ * attention run in fp32 as for fp32 rows), W as for la_feature_map, out
+ * [B][H][N][M] fp32; S_out [B][H][F][M], z_out [B][H][F] optional (both or
+ * neither): the final state over the features.
  * workspace: la_forward_features_workspace_bytes(...) bytes (at least 256 for
  * a supported shape, 0 for a refused one), initialised and reused as for
  * la_forward_chunked.
@@ -357,8 +359,9 @@ LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2
  */
 LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F);
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                               int64_t N, int64_t D, int64_t M, const float *W, int64_t F, int kind, int flags,
-                               void *workspace, size_t workspace_bytes, float *S_out, float *z_out, void *stream);
+                               int64_t N, int64_t D, int64_t M, int dtype, const float *W, int64_t F, int kind,
+                               int flags, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
+                               void *stream);
 
 #ifdef __cplusplus
 }

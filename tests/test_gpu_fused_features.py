@@ -194,3 +194,43 @@ def test_fused_features_workload(ea):
     sel = (slice(3, 4), slice(5, 7))
     ref = oracle_out((Xq[sel], Xk[sel], V[sel], W), F, "prf", False)[0]
     assert rowwise_rel(out[sel].cpu().numpy(), ref) <= TOL["f32"]
+
+
+def bf16_case(ea, B, H, N, D, M, F, kind, seed, normalize=False):
+    """bf16 raw rows and V; the oracle gets their exact fp64 images."""
+    s = KIND_SCALE[kind] * D ** -0.25
+    Xq = synthetic.draw(seed, synthetic.TID_Q, (B, H, N, D), s, "bf16")
+    Xk = synthetic.draw(seed, synthetic.TID_K, (B, H, N, D), s, "bf16")
+    V = synthetic.draw(seed, synthetic.TID_V, (B, H, N, M), 1.0, "bf16")
+    W = ea.draw_projection(W_ROWS[kind](F), D, "gaussian", seed + 1)
+    dev = tuple(to_dev(x, "bf16") for x in (Xq, Xk, V)) + (torch.from_numpy(W).to(DEV),)
+    host = tuple(synthetic.as_f64(x, "bf16") for x in (Xq, Xk, V)) + (W,)
+    return dev, host
+
+
+@pytest.mark.parametrize("normalize", [False, True])
+@pytest.mark.parametrize("kind", ["prf", "trf"])
+@pytest.mark.parametrize("D,F,M", [(64, 16, 64), (32, 32, 32), (128, 16, 128), (16, 64, 16)])
+def test_fused_features_bf16_rows(ea, normalize, kind, D, F, M):
+    """bf16 raw rows: widened exactly, then the same fp32 map and attention (fp32
+    tolerance against the oracle on the same bf16 values)."""
+    B, H, N = 2, 2, 300
+    if not supported(ea, B, H, N, D, M, F):
+        pytest.skip(f"D={D} F={F} M={M}: the kernel's LDS does not fit two workgroups per CU")
+    dev, host = bf16_case(ea, B, H, N, D, M, F, kind, 70 + D, normalize)
+    out, S, z = run(ea, dev, F, kind, normalize)
+    check(out, S, z, oracle_out(host, F, kind, normalize))
+
+
+@pytest.mark.parametrize("kind", ["prf", "trf"])
+def test_fused_features_bf16_equals_widened_f32(ea, kind):
+    """The bf16 kernel on bf16 rows and the fp32 kernel on the same values widened
+    to fp32 run identical arithmetic: bit-identical outputs and states."""
+    B, H, N, D, M, F = 4, 4, 1000, 64, 64, 16
+    dev, _ = bf16_case(ea, B, H, N, D, M, F, kind, 71)
+    out16, S16, z16 = run(ea, dev, F, kind, False)
+    wide = tuple(x.float().contiguous() for x in dev[:3]) + (dev[3],)
+    out32, S32, z32 = run(ea, wide, F, kind, False)
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out32)
+    assert torch.equal(S16, S32) and torch.equal(z16, z32)
