@@ -17,6 +17,10 @@ constexpr int kOutBf16 = 16;
 // header words, then one flag word per segment (padded to 64 words), then the
 // aggregate and the inclusive state of every segment (E floats each).
 constexpr int kWsHeaderWords = 64;
+// header words of a look-back workspace: 1 heads counted, 2 epoch, 3 error
+// (a wait gave up), 4 poll cap (0: the built-in bound; set by tests only)
+constexpr int kWsErrorWord = 3;
+constexpr int kWsPollCapWord = 4;
 __host__ __device__ inline size_t fused_flag_words(long BHG) { return ((size_t)BHG + 63) / 64 * 64; }
 // floats of one exchanged state slot: E = D*M + D padded to whole 256-byte blocks
 __host__ __device__ inline int fused_slot_floats(int E) { return (E + 63) / 64 * 64; }

@@ -928,6 +928,9 @@ __device__ __forceinline__ bool look_back(const Engine<T, D, M, C, PHI> &e, cons
             bool incl_first = false;
             int base = s - 1;  // inclusive mode: the newest segment of the polled window
             long spins = 0;
+            // header word 4, when the host has set it, caps the polls (tests of the give-up path)
+            const unsigned cap = __hip_atomic_load(&ws.hdr[kWsPollCapWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const long limit = cap != 0u ? (long)cap : kSpinLimit;
             while (true) {
                 const int j = in_order ? next + e.lane : base - e.lane;
                 const bool valid = in_order ? j < s : j >= 0;
@@ -958,8 +961,9 @@ __device__ __forceinline__ bool look_back(const Engine<T, D, M, C, PHI> &e, cons
                         continue;
                     }
                 }
-                if (++spins > kSpinLimit) {
-                    if (e.lane == 0) __hip_atomic_store(&ws.hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (++spins > limit) {
+                    if (e.lane == 0)
+                        __hip_atomic_store(&ws.hdr[kWsErrorWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     from = -1;
                     break;
                 }

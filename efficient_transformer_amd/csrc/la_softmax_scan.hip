@@ -193,6 +193,17 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
 #pragma unroll
     for (int c = 0; c < CPL; ++c) pw[c] = 0.0f;
     auto add_back = [&](float sm, float sus, const float *sw) {
+        if (sm != sm) {
+            // a state published by a group whose wait gave up (its max is NaN):
+            // the prefix is lost.  fmaxf would drop the NaN (and an empty prefix
+            // would then skip the state), so the loss is made explicit here; the
+            // NaN sums stay NaN through every later combination.
+            pm = __builtin_nanf("");
+            pu = __builtin_nanf("");
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) pw[c] = __builtin_nanf("");
+            return;
+        }
         const float mn = fmaxf(sm, pm);
         if (mn != -INFINITY) {
             const float a = __expf(pm - mn), b = __expf(sm - mn);
@@ -286,6 +297,9 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
             int base = grp - 1;
             int jstar = -1;
             long spins = 0;
+            // header word 4, when the host has set it, caps the polls (tests of the give-up path)
+            const unsigned cap = __hip_atomic_load(&hdr[kWsPollCapWord], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const long limit = cap != 0u ? (long)cap : kScanSpinLimit;
             while (true) {
                 const int j = base - lane;
                 unsigned f = 0u;
@@ -305,8 +319,8 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
                     base -= 64;
                     continue;
                 }
-                if (++spins > kScanSpinLimit) {
-                    if (lane == 0) __hip_atomic_store(&hdr[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (++spins > limit) {
+                    if (lane == 0) __hip_atomic_store(&hdr[kWsErrorWord], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);

@@ -115,8 +115,10 @@ LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_
  *   4 million polls).  Workgroups are dispatched in segment order, so the wait
  *   ends unless the GPU is shared so heavily that earlier segments cannot run;
  *   if it gives up, the affected outputs (and S_out, z_out) are NaN, a nonzero
- *   error word is left in the workspace, and the workspace must be zeroed again
- *   before its next use.
+ *   error word is left in the workspace (32-bit word 3, byte offset 12), and
+ *   the workspace must be zeroed again before its next use.  Word 4 (byte
+ *   offset 16), when nonzero, caps each wait at that many polls; it exists so
+ *   that tests can force the give-up path, and la_workspace_init clears it.
  * S_out [B][H][D][M], z_out [B][H][D]: optional (NULL to skip; both or neither);
  *   receive the final state S_{N-1}, z_{N-1}, so that la_decode_step can
  *   continue the sequence.
@@ -294,7 +296,9 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
  * workspace: la_softmax_scan_workspace_bytes(...) bytes (0 when every head fits
  * one group of 128 positions), zeroed (la_workspace_init)
  * before its first use, then reusable by later calls with the same shape;
- * calls sharing a workspace must not overlap.
+ * calls sharing a workspace must not overlap.  Waits for earlier groups are
+ * bounded as for la_forward_chunked (same error word and poll-cap word); a
+ * wait that gives up leaves NaN in the affected outputs and final state.
  */
 LA_API size_t la_softmax_scan_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M);
 LA_API int la_softmax_scan(const void *q, const void *K, const void *V, float *out,
