@@ -564,12 +564,15 @@ namespace {
 // The plan of la_forward_features (LA_OK only when the fused kernel runs it).
 int features_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F, Plan *p) {
     if (!dim_ok(D) || !dim_ok(F)) return LA_ERR_UNSUPPORTED;
-    // the fused kernel's LDS (raw rows and W besides the attention tiles) admits
+    // the fused kernels' LDS (raw rows and W besides the attention tiles) admits
     // two workgroups per CU: plan 512 resident workgroups
     int st = make_plan(B, H, N, F, M, 1, LA_F32_FEATURES, la::kFusedFeatureChunk, p, 512);
     if (st != LA_OK) return st;
-    if (B * H > 0 && N > 0 && (!p->onepass || !la::prefill_features_supported((int)D, (int)F, (int)M)))
-        return LA_ERR_UNSUPPORTED;
+    if (B * H == 0 || N == 0) return LA_OK;
+    // the one-pass kernel where its segments fit (at most four chunks) and its LDS
+    // does, else the two-phase kernel (any segment length, less LDS)
+    if (p->onepass && !la::prefill_features_supported(true, (int)D, (int)F, (int)M)) p->onepass = false;
+    if (!p->onepass && !la::prefill_features_supported(false, (int)D, (int)F, (int)M)) return LA_ERR_UNSUPPORTED;
     return LA_OK;
 }
 }  // namespace
@@ -609,11 +612,12 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
     (void)hipGetLastError();
     const int norm = (flags & LA_FEATURE_NORMALIZE) != 0;
     return hip_status(dtype == LA_F32
-                          ? la::prefill_features_f32((int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out, workspace,
-                                                     (int)BH, (int)N, p.segments, p.chunks_per_segment, S_out, z_out, s)
-                          : la::prefill_features_bf16((int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out, workspace,
-                                                      (int)BH, (int)N, p.segments, p.chunks_per_segment, S_out, z_out,
-                                                      s));
+                          ? la::prefill_features_f32(p.onepass, (int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
+                                                     workspace, (int)BH, (int)N, p.segments, p.chunks_per_segment,
+                                                     S_out, z_out, s)
+                          : la::prefill_features_bf16(p.onepass, (int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
+                                                      workspace, (int)BH, (int)N, p.segments, p.chunks_per_segment,
+                                                      S_out, z_out, s));
 }
 
 // ---- feature maps ----------------------------------------------------------

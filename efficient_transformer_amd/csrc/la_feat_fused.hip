@@ -3,9 +3,11 @@
 
 namespace la {
 
-bool prefill_features_supported(int DI, int F, int M) {
-#define X(DI_, F_, M_) \
-    if (DI == DI_ && F == F_ && M == M_) return onepass_features_fit<DI_, F_, M_, kFusedFeatureChunk>();
+bool prefill_features_supported(bool onepass, int DI, int F, int M) {
+#define X(DI_, F_, M_)                                                                          \
+    if (DI == DI_ && F == F_ && M == M_)                                                        \
+        return onepass ? onepass_features_fit<DI_, F_, M_, kFusedFeatureChunk>()                \
+                       : fused_features_fit<DI_, F_, M_, kFusedFeatureChunk>();
 #define XM(DI_, F_) X(DI_, F_, 16) X(DI_, F_, 32) X(DI_, F_, 64) X(DI_, F_, 128)
 #define XF(DI_) XM(DI_, 16) XM(DI_, 32) XM(DI_, 64)
     XF(16) XF(32) XF(64) XF(128)
@@ -15,11 +17,11 @@ bool prefill_features_supported(int DI, int F, int M) {
     return false;
 }
 
-hipError_t prefill_features_f32(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
-                                int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
-                                float *S_out, float *z_out, hipStream_t stream) {
-    return prefill_features_typed<float>(DI, F, M, Q, K, V, W, kind, norm, out, ws, BH, N, G, CPS, S_out, z_out,
-                                         stream);
+hipError_t prefill_features_f32(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
+                                const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
+                                int CPS, float *S_out, float *z_out, hipStream_t stream) {
+    return prefill_features_typed<float>(onepass, DI, F, M, Q, K, V, W, kind, norm, out, ws, BH, N, G, CPS, S_out,
+                                         z_out, stream);
 }
 
 }  // namespace la

@@ -3,11 +3,11 @@
 
 namespace la {
 
-hipError_t prefill_features_bf16(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
-                                 int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
-                                 float *S_out, float *z_out, hipStream_t stream) {
-    return prefill_features_typed<bf16>(DI, F, M, Q, K, V, W, kind, norm, out, ws, BH, N, G, CPS, S_out, z_out,
-                                        stream);
+hipError_t prefill_features_bf16(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
+                                 const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
+                                 int CPS, float *S_out, float *z_out, hipStream_t stream) {
+    return prefill_features_typed<bf16>(onepass, DI, F, M, Q, K, V, W, kind, norm, out, ws, BH, N, G, CPS, S_out,
+                                        z_out, stream);
 }
 
 }  // namespace la

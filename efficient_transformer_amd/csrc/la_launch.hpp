@@ -96,13 +96,14 @@ hipError_t prefill_outputs_bf16o(int D, int M, int C, const void *Q, const void 
 // random features fused into the one-pass causal kernel (la_feat_fused*.hip):
 // raw rows (and V) fp32 or bf16, features and attention fp32
 constexpr int kFusedFeatureChunk = 32;
-bool prefill_features_supported(int DI, int F, int M);
-hipError_t prefill_features_f32(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
-                                int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
-                                float *S_out, float *z_out, hipStream_t stream);
-hipError_t prefill_features_bf16(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
-                                 int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
-                                 float *S_out, float *z_out, hipStream_t stream);
+// onepass: the one-pass kernel (segments of at most four chunks), else the two-phase one
+bool prefill_features_supported(bool onepass, int DI, int F, int M);
+hipError_t prefill_features_f32(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
+                                const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
+                                int CPS, float *S_out, float *z_out, hipStream_t stream);
+hipError_t prefill_features_bf16(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
+                                 const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
+                                 int CPS, float *S_out, float *z_out, hipStream_t stream);
 
 // feature inputs (la_feat_prefill.hip, la_feat_onepass.hip)
 bool prefill_supported_feat(int D, int M, int C);

@@ -796,6 +796,70 @@ struct Engine {
 // Phase A: sum the state over chunks [c0, c1) into acc / z (thread tid < D owns z[tid]).
 // Leaves the last chunk's phi(K), V in LDS.  Global loads run two chunks ahead.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+template <int DI, int F, int C>
+struct FeatLds {
+    static constexpr int LX = DI + 4;           // LDS row of a raw tile
+    static constexpr int WROWS = (F + 15) / 16 * 16;
+    static constexpr int nRaw = 2 * C * LX;     // raw q, raw k
+    static constexpr int nW = WROWS * LX;
+    static constexpr size_t bytes = (size_t)(nRaw + nW) * 4;
+    static_assert(DI % 16 == 0, "16-deep contraction blocks");
+};
+
+// One (tensor, 16-row tile, 16-projection tile) job of the projection: lane
+// (g, l16) ends with projections 4g .. 4g+3 of row l16 (W rows as the MFMA A
+// operand, x rows as B; within each 16-deep block lane g contracts over
+// k = 16 kb + 4 g + kk for both).
+template <int DI, int F, int C>
+__device__ __forceinline__ void feature_job(const float *raw, const float *sw, float *dst, int ld, int rt, int pt,
+                                            int P, int kind, bool norm, int row0, int N, int lane) {
+    using FL = FeatLds<DI, F, C>;
+    const int g = lane >> 4, l16 = lane & 15;
+    const float *xr = raw + (rt * 16 + l16) * FL::LX + 4 * g;
+    const float *wr = sw + (pt * 16 + l16) * FL::LX + 4 * g;
+    f32x4 acc = zero4();
+    float sq = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < DI / 16; ++kb) {
+        const f32x4 b = *reinterpret_cast<const f32x4 *>(xr + 16 * kb);
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(wr + 16 * kb);
+        sq += b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mma_f32(a[kk], b[kk], acc);
+    }
+    sq += __shfl_xor(sq, 16, 64);  // the four lanes g of row l16 hold a quarter each
+    sq += __shfl_xor(sq, 32, 64);
+    float scale = 1.0f;
+    if (norm && sq > 0.0f) {
+        scale = 1.0f / sqrtf(sq);
+        sq = sq * scale * scale;
+    }
+    const int row = rt * 16 + l16, f0 = pt * 16 + 4 * g;
+    if (f0 >= P) return;
+    const bool pad = row0 + row >= N;
+    float *o = dst + row * ld;
+    if (kind == 1) {
+        const float inv = 1.0f / sqrtf((float)F);
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = pad ? 0.0f : __expf(acc[r] * scale - 0.5f * sq) * inv;
+        *reinterpret_cast<f32x4 *>(o + f0) = v;
+    } else {
+        const float c = __expf(0.5f * sq) / sqrtf((float)P);
+        f32x4 vs, vc;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float sn, cs;
+            sincosf(acc[r] * scale, &sn, &cs);
+            vs[r] = pad ? 0.0f : c * sn;
+            vc[r] = pad ? 0.0f : c * cs;
+        }
+        *reinterpret_cast<f32x4 *>(o + f0) = vs;
+        *reinterpret_cast<f32x4 *>(o + P + f0) = vc;
+    }
+}
+
 // DK: width of the K rows in memory; TI: their element type (the engine's T
 // unless raw rows are mapped to fp32 features while staged)
 template <typename T, int D, int M, int C, int DK = D, typename TI = T>
@@ -808,22 +872,92 @@ struct KVBuf {
     }
 };
 
-template <typename T, int D, int M, int C, bool PHI>
-__device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const T *__restrict__ Kh,
-                                        const T *__restrict__ Vh, int N, int c0, int c1,
-                                        f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z) {
+// How a chunk's rows reach the engine's tiles: through phi (the elu map), or,
+// with DI > 0, as raw rows DI wide (element type TI) that are mapped in fp32 to
+// the random features of W (fkind, fnorm) once they are in LDS; the engine then
+// works on D = F features.  Raw rows go to their own LDS tiles (store_*), and
+// map() forms the features after the barrier that follows those stores.
+template <typename T, int D, int M, int C, bool PHI, int DI = 0, typename TI = T>
+struct ChunkStager {
+    static constexpr bool FEAT = DI > 0;
+    static constexpr int DQ = FEAT ? DI : D;  // width of the Q, K rows in memory
+    using Gc = Cfg<T, D, M, C>;
+    using En = Engine<T, D, M, C, PHI>;
+    using FL = FeatLds<FEAT ? DI : 16, D, C>;
+    using QStage = Stage<TI, C, DQ, Gc::THREADS>;
+    static_assert(!FEAT || (std::is_same<T, float>::value && !PHI), "random features: fp32 engine, no elu map");
+    static_assert(FEAT || std::is_same<TI, T>::value, "raw rows of another type only with random features");
+    float *sRawQ = nullptr, *sRawK = nullptr, *sW = nullptr;
+    int P = D, fkind = 0;
+    bool fnorm = false;
+
+    // FEAT: W ([P][DI], P = F or F/2) into LDS once per workgroup, rows past P zero
+    __device__ __forceinline__ void init(float *sfeat, const float *__restrict__ W, int kind, int norm, int tid) {
+        if constexpr (FEAT) {
+            sRawQ = sfeat;
+            sRawK = sfeat + C * FL::LX;
+            sW = sfeat + FL::nRaw;
+            fkind = kind;
+            fnorm = norm != 0;
+            P = kind == 2 ? D / 2 : D;
+            for (int x = tid; x < FL::WROWS * (DI / 4); x += Gc::THREADS) {
+                const int f = x / (DI / 4), c4 = (x % (DI / 4)) * 4;
+                f32x4 v = zero4();
+                if (f < P) v = *reinterpret_cast<const f32x4 *>(W + (size_t)f * DI + c4);
+                *reinterpret_cast<f32x4 *>(sW + f * FL::LX + c4) = v;
+            }
+        }
+    }
+    __device__ __forceinline__ void store_q(const En &e, const QStage &q, int row0, int N) const {
+        if constexpr (FEAT)
+            q.store_natural_f32(sRawQ, FL::LX, row0, N, e.tid);
+        else
+            e.store_q(q, row0, N);
+    }
+    __device__ __forceinline__ void store_kv(const En &e, const KVBuf<T, D, M, C, DQ, TI> &b, int row0, int N) const {
+        if constexpr (FEAT) {
+            b.k.store_natural_f32(sRawK, FL::LX, row0, N, e.tid);
+            b.v.store_natural_f32(e.sV, Gc::LV, row0, N, e.tid);
+        } else {
+            e.store_kv(b.k, b.v, row0, N);
+        }
+    }
+    // FEAT: the features of the staged q and/or k rows into e.sQ / e.sK (rows at
+    // or past N zero), then a barrier; nothing otherwise
+    __device__ __forceinline__ void map(const En &e, bool q, bool k, int row0, int N) const {
+        if constexpr (FEAT) {
+            const int PT = (P + 15) / 16, per = Gc::RT * PT;
+            const int j1 = (k ? 2 : 1) * per;
+            for (int jb = e.w + (q ? 0 : per); jb < j1; jb += Gc::NW) {
+                const int t = jb / per, rt = (jb % per) / PT, pt = jb % PT;
+                feature_job<DI, D, C>(t == 0 ? sRawQ : sRawK, sW, t == 0 ? e.sQ : e.sK, Gc::LQ, rt, pt, P, fkind,
+                                      fnorm, row0, N, e.lane);
+            }
+            __syncthreads();
+        }
+    }
+};
+
+
+template <typename T, int D, int M, int C, bool PHI, int DI = 0, typename TI = T>
+__device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const TI *__restrict__ Kh,
+                                        const TI *__restrict__ Vh, int N, int c0, int c1,
+                                        f32x4 (&acc)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z,
+                                        const ChunkStager<T, D, M, C, PHI, DI, TI> &st = {}) {
     // Two chunks of loads in flight (two register buffers, the loop unrolled by
     // two): a phase-A chunk has little arithmetic, so one chunk of work does not
     // cover a load's latency.  Every load is issued unconditionally (index clamped
     // to the last chunk; a clamped reload is an L2 hit) so that the compiler's
     // wait counts stay exact; only the arithmetic of the odd last chunk is skipped.
-    KVBuf<T, D, M, C> b0, b1;
+    using KV = KVBuf<T, D, M, C, ChunkStager<T, D, M, C, PHI, DI, TI>::DQ, TI>;
+    KV b0, b1;
     b0.load(Kh, Vh, c0, N, e.tid);
     b1.load(Kh, Vh, min(c0 + 1, c1 - 1), N, e.tid);
-    auto body = [&](const KVBuf<T, D, M, C> &b, int c) {
+    auto body = [&](const KV &b, int c) {
         __syncthreads();  // LDS free (previous chunk's readers are done)
-        e.store_kv(b.k, b.v, c * C, N);
+        st.store_kv(e, b, c * C, N);
         __syncthreads();
+        st.map(e, false, true, c * C, N);
         e.z_partials();
         e.state_update(acc);
         __syncthreads();
@@ -844,28 +978,30 @@ __device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const 
 // advance the state over the last chunk (for the final state).  Loads run one
 // chunk ahead.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, bool CAUSAL, bool PHI, typename OT>
-__device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const T *__restrict__ Qh,
-                                        const T *__restrict__ Kh, const T *__restrict__ Vh,
+template <typename T, int D, int M, int C, bool CAUSAL, bool PHI, typename OT, int DI = 0, typename TI = T>
+__device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const TI *__restrict__ Qh,
+                                        const TI *__restrict__ Kh, const TI *__restrict__ Vh,
                                         OT *__restrict__ Oh, int N, int c0, int c1, bool kv_staged,
-                                        bool advance_last, Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q0,
+                                        bool advance_last,
+                                        typename ChunkStager<T, D, M, C, PHI, DI, TI>::QStage &q0,
                                         f32x4 (&S)[Cfg<T, D, M, C>::DT][Cfg<T, D, M, C>::MTW], float &z,
-                                        bool poison) {
+                                        bool poison, const ChunkStager<T, D, M, C, PHI, DI, TI> &st = {}) {
     // loads as in phase_a: one chunk ahead, unconditional (clamped)
-    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &q = q0;
-    KVBuf<T, D, M, C> b;
+    auto &q = q0;
+    KVBuf<T, D, M, C, ChunkStager<T, D, M, C, PHI, DI, TI>::DQ, TI> b;
     if (CAUSAL && !kv_staged) b.load(Kh, Vh, c0, N, e.tid);
     for (int c = c0; c < c1; ++c) {
         const int row0 = c * C;
         const bool stage_kv = CAUSAL && !(kv_staged && c == c0);
         __syncthreads();  // LDS free
-        e.store_q(q, row0, N);
-        if (stage_kv) e.store_kv(b.k, b.v, row0, N);
+        st.store_q(e, q, row0, N);
+        if (stage_kv) st.store_kv(e, b, row0, N);
         if (e.tid < D) e.sz[e.tid] = round_as<T>(z);
         __syncthreads();
         const int cn = min(c + 1, c1 - 1);
         q.load(Qh, cn * C, N, e.tid);
         if (CAUSAL) b.load(Kh, Vh, cn, N, e.tid);
+        st.map(e, true, stage_kv, row0, N);
         if (CAUSAL) e.a_tiles();
         e.qz_rows();
         const bool adv = CAUSAL && (c + 1 < c1 || advance_last);
@@ -1027,18 +1163,24 @@ __device__ __forceinline__ void finish_call(const FusedWs &ws, unsigned epoch, u
     }
 }
 
-template <typename T, int D, int M, int C, bool PHI = true, typename OT = float>
-__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void fused_causal_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                                const T *__restrict__ V, OT *__restrict__ out,
-                                                                void *ws_raw, int BH, int N, int G_, int CPS,
-                                                                float *__restrict__ S_out, float *__restrict__ z_out,
-                                                                const float *S_in, const float *z_in) {
+// DI > 0: raw rows DI wide (type TI) mapped to random features while staged,
+// as in the one-pass kernel.
+template <typename T, int D, int M, int C, bool PHI = true, typename OT = float, int DI = 0, typename TI = T>
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void fused_causal_kernel(
+    const TI *__restrict__ Q, const TI *__restrict__ K, const TI *__restrict__ V, OT *__restrict__ out, void *ws_raw,
+    int BH, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out, const float *S_in,
+    const float *z_in, const float *__restrict__ W, int fkind, int fnorm) {
     using Gc = Cfg<T, D, M, C>;
     using En = Engine<T, D, M, C, PHI>;
+    using St = ChunkStager<T, D, M, C, PHI, DI, TI>;
+    constexpr int DQ = St::DQ;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
+    __shared__ __attribute__((aligned(16))) float sfeat[St::FEAT ? St::FL::nRaw + St::FL::nW : 4];
     __shared__ unsigned sh_word[4];
     En e(smem);
     const int tid = e.tid;
+    St st;
+    st.init(sfeat, W, fkind, fnorm, tid);
 
     // Work item: block b -> segment b / BH of head b % BH.  Workgroups are
     // dispatched in block order, so a workgroup only ever waits on segments of
@@ -1057,9 +1199,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
-    const T *Qh = Q + (size_t)bh * N * D;
-    const T *Kh = K + (size_t)bh * N * D;
-    const T *Vh = V + (size_t)bh * N * M;
+    const TI *Qh = Q + (size_t)bh * N * DQ;
+    const TI *Kh = K + (size_t)bh * N * DQ;
+    const TI *Vh = V + (size_t)bh * N * M;
     OT *Oh = out + (size_t)bh * N * M;
 
     e.clear_a();
@@ -1070,7 +1212,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     const bool last = s == G_ - 1;
     const bool want_final = S_out != nullptr;
     const bool run_a = G_ > 1 && (!last || want_final);
-    if (run_a) phase_a(e, Kh, Vh, N, c0, c1, acc, zacc);
+    if (run_a) phase_a(e, Kh, Vh, N, c0, c1, acc, zacc, st);
     const size_t my = (size_t)bh * G_ + s;
     // Prefix of the segment: the carried initial state (segment 0, when given),
     // later the look-back's sum of the earlier segments.
@@ -1096,7 +1238,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         e.publish_flag(&ws.flags[my], ep | 1u);
     }
 
-    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> stQ;
+    typename St::QStage stQ;
     stQ.load(Qh, c0 * C, N, tid);
 
     // A one-chunk segment still holds its phi(K), V in LDS: form A and the
@@ -1105,8 +1247,9 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     En::zero_out(o);
     const bool single = run_a && (c1 - c0 == 1);
     if (single) {
-        e.store_q(stQ, c0 * C, N);
+        st.store_q(e, stQ, c0 * C, N);
         __syncthreads();
+        st.map(e, true, false, c0 * C, N);
         e.a_tiles();
         __syncthreads();
         e.intra(o);
@@ -1139,8 +1282,8 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         const float inv = e.template row_inv<true>();
         e.readout(o, pre, inv, Oh, c0 * C, N, failed);
     } else {
-        phase_b<T, D, M, C, true, PHI, OT>(e, Qh, Kh, Vh, Oh, N, c0, c1, false, G_ == 1 && want_final, stQ, pre, zpre,
-                                  failed);
+        phase_b<T, D, M, C, true, PHI, OT, DI, TI>(e, Qh, Kh, Vh, Oh, N, c0, c1, false, G_ == 1 && want_final, stQ,
+                                                   pre, zpre, failed, st);
         if (G_ == 1 && want_final) e.state_store(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
     }
 
@@ -1173,70 +1316,6 @@ constexpr int kOnePassChunks = 4;
 // kind 2 (TRF, P = F / 2 projections): exp(|x|^2 / 2) / sqrt(P) times sin (column
 // p) and cos (column P + p); norm: rows scaled to unit length first.  Rows at or
 // beyond N get zero features (they must add nothing to the sums).
-// ---------------------------------------------------------------------------
-template <int DI, int F, int C>
-struct FeatLds {
-    static constexpr int LX = DI + 4;           // LDS row of a raw tile
-    static constexpr int WROWS = (F + 15) / 16 * 16;
-    static constexpr int nRaw = 2 * C * LX;     // raw q, raw k
-    static constexpr int nW = WROWS * LX;
-    static constexpr size_t bytes = (size_t)(nRaw + nW) * 4;
-    static_assert(DI % 16 == 0, "16-deep contraction blocks");
-};
-
-// One (tensor, 16-row tile, 16-projection tile) job of the projection: lane
-// (g, l16) ends with projections 4g .. 4g+3 of row l16 (W rows as the MFMA A
-// operand, x rows as B; within each 16-deep block lane g contracts over
-// k = 16 kb + 4 g + kk for both).
-template <int DI, int F, int C>
-__device__ __forceinline__ void feature_job(const float *raw, const float *sw, float *dst, int ld, int rt, int pt,
-                                            int P, int kind, bool norm, int row0, int N, int lane) {
-    using FL = FeatLds<DI, F, C>;
-    const int g = lane >> 4, l16 = lane & 15;
-    const float *xr = raw + (rt * 16 + l16) * FL::LX + 4 * g;
-    const float *wr = sw + (pt * 16 + l16) * FL::LX + 4 * g;
-    f32x4 acc = zero4();
-    float sq = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < DI / 16; ++kb) {
-        const f32x4 b = *reinterpret_cast<const f32x4 *>(xr + 16 * kb);
-        const f32x4 a = *reinterpret_cast<const f32x4 *>(wr + 16 * kb);
-        sq += b[0] * b[0] + b[1] * b[1] + b[2] * b[2] + b[3] * b[3];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mma_f32(a[kk], b[kk], acc);
-    }
-    sq += __shfl_xor(sq, 16, 64);  // the four lanes g of row l16 hold a quarter each
-    sq += __shfl_xor(sq, 32, 64);
-    float scale = 1.0f;
-    if (norm && sq > 0.0f) {
-        scale = 1.0f / sqrtf(sq);
-        sq = sq * scale * scale;
-    }
-    const int row = rt * 16 + l16, f0 = pt * 16 + 4 * g;
-    if (f0 >= P) return;
-    const bool pad = row0 + row >= N;
-    float *o = dst + row * ld;
-    if (kind == 1) {
-        const float inv = 1.0f / sqrtf((float)F);
-        f32x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = pad ? 0.0f : __expf(acc[r] * scale - 0.5f * sq) * inv;
-        *reinterpret_cast<f32x4 *>(o + f0) = v;
-    } else {
-        const float c = __expf(0.5f * sq) / sqrtf((float)P);
-        f32x4 vs, vc;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float sn, cs;
-            sincosf(acc[r] * scale, &sn, &cs);
-            vs[r] = pad ? 0.0f : c * sn;
-            vc[r] = pad ? 0.0f : c * cs;
-        }
-        *reinterpret_cast<f32x4 *>(o + f0) = vs;
-        *reinterpret_cast<f32x4 *>(o + P + f0) = vc;
-    }
-}
-
 template <typename T, int D, int M, int C>
 struct OnePassLds {
     using Gc = Cfg<T, D, M, C>;
@@ -1524,7 +1603,8 @@ hipError_t run_fused(const void *Q, const void *K, const void *V, void *out, voi
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
         hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C, PHI, OT>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
-                           (const T *)K, (const T *)V, (OT *)out, ws, BH, N, G_, CPS, S_out, z_out, S_in, z_in);
+                           (const T *)K, (const T *)V, (OT *)out, ws, BH, N, G_, CPS, S_out, z_out, S_in, z_in, nullptr,
+                           0, 0);
         return hipGetLastError();
     }
 }
@@ -1568,6 +1648,34 @@ hipError_t run_onepass_features(const void *Q, const void *K, const void *V, con
         hipLaunchKernelGGL((onepass_causal_kernel<float, F, M, C, false, float, DI, TI>), dim3((unsigned)(BH * G_)),
                            dim3(Gc::THREADS), 0, stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws,
                            BH, N, G_, CPS, S_out, z_out, nullptr, nullptr, W, fkind, fnorm);
+        return hipGetLastError();
+    }
+}
+
+// The two-phase kernel takes any shape whose LDS fits one workgroup per CU
+// (fewer resident workgroups than planned only cost speed: waits only go to
+// segments dispatched earlier).
+template <int DI, int F, int M, int C>
+constexpr bool fused_features_fit() {
+    using Gc = Cfg<float, F, M, C>;
+    return Gc::fits && Gc::bytes + FeatLds<DI, F, C>::bytes + 64 <= kMaxLds;
+}
+
+// The two-phase kernel with the random-feature map fused (segments longer than
+// the one-pass kernel takes).
+template <int DI, int F, int M, int C, typename TI = float>
+hipError_t run_fused_features(const void *Q, const void *K, const void *V, const float *W, int fkind, int fnorm,
+                              float *out, void *ws, int BH, int N, int G_, int CPS, float *S_out, float *z_out,
+                              hipStream_t stream) {
+    using Gc = Cfg<float, F, M, C>;
+    if constexpr (!fused_features_fit<DI, F, M, C>()) {
+        return hipErrorInvalidValue;
+    } else {
+        if (BH <= 0 || G_ <= 0) return hipSuccess;
+        const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
+        hipLaunchKernelGGL((fused_causal_kernel<float, F, M, C, false, float, DI, TI>), dim3(grid), dim3(Gc::THREADS), 0,
+                           stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws, BH, N, G_, CPS, S_out, z_out,
+                           nullptr, nullptr, W, fkind, fnorm);
         return hipGetLastError();
     }
 }

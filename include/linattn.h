@@ -354,12 +354,13 @@ LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2
  * workspace: la_forward_features_workspace_bytes(...) bytes (at least 256 for
  * a supported shape, 0 for a refused one), initialised and reused as for
  * la_forward_chunked.
- * Supported when the plan (chunks of 32, segments sized for 512 resident
- * workgroups) has segments of at most four chunks and the kernel's LDS fits
- * (la_forward_features_workspace_bytes returns 0 and this call returns
- * LA_ERR_UNSUPPORTED otherwise, as for invalid arguments), and
+ * Plan: chunks of 32, segments sized for 512 resident workgroups; the one-pass
+ * kernel runs segments of at most four chunks where its LDS fits, the
+ * two-phase kernel (the map applied in both phases) everything else.  D and F
+ * outside the instantiated set (D in {16, 32, 64, 128}, F in {16, 32, 64}, M in
+ * {16, 32, 64, 128}) give LA_ERR_UNSUPPORTED (and a workspace size of 0);
  * la_feature_map followed by la_forward_chunked (LA_F32_FEATURES) computes the
- * same result in two launches.
+ * same result in two launches for any supported feature dimension.
  */
 LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F);
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,

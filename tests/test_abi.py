@@ -299,7 +299,9 @@ def test_forward_features_checks(L):
     need = wsb(8, 8, 1024, 64, 64, 16)
     assert need > 0
     assert wsb(8, 8, 1024, 48, 64, 16) == 0 and wsb(8, 8, 1024, 64, 64, 24) == 0  # D, F
-    assert wsb(1, 1, 1 << 20, 64, 64, 16) == 0  # segments longer than four chunks
+    assert wsb(8, 8, 1024, 64, 64, 128) == 0  # F = 128: no fused instantiation
+    assert wsb(1, 1, 1 << 20, 64, 64, 16) > 0  # long segments: the two-phase kernel
+    assert wsb(8, 8, 1024, 64, 64, 64) > 0  # one-pass LDS too small: the two-phase kernel
     assert wsb(-1, 8, 1024, 64, 64, 16) == 0
 
     def call(**kw):
@@ -315,8 +317,7 @@ def test_forward_features_checks(L):
     assert call(kind=3) == L.LA_ERR_INVALID_ARG
     assert call(flags=2) == L.LA_ERR_INVALID_ARG
     assert call(D=48) == L.LA_ERR_UNSUPPORTED
-    assert call(F=64) == L.LA_ERR_UNSUPPORTED  # LDS of D = M = 64 with F = 64 exceeds two workgroups per CU
-    assert call(B=1, H=1, N=1 << 20) == L.LA_ERR_UNSUPPORTED
+    assert call(F=128) == L.LA_ERR_UNSUPPORTED
     assert call(N=-1) == L.LA_ERR_INVALID_ARG
     assert call(S=FAKE) == L.LA_ERR_INVALID_ARG  # S_out without z_out
     assert call(W=None) == L.LA_ERR_INVALID_ARG

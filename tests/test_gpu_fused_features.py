@@ -85,21 +85,20 @@ def check(out, S, z, ref):
 def test_fused_features_parity(ea, normalize, kind, D, F, M):
     """N = 300: nine full chunks of 32 and a ragged one, several segments per head."""
     B, H, N = 1, 3, 300
-    if not supported(ea, B, H, N, D, M, F):
-        pytest.skip(f"D={D} F={F} M={M}: the kernel's LDS does not fit two workgroups per CU")
+    assert supported(ea, B, H, N, D, M, F)
     dev, host = case(ea, B, H, N, D, M, F, kind, 50 + D + F, normalize)
     out, S, z = run(ea, dev, F, kind, normalize)
     check(out, S, z, oracle_out(host, F, kind, normalize))
 
 
 def test_supported_shapes(ea):
-    """The shapes the fused kernel takes (the others fall to the two-launch path)."""
+    """Every instantiated (D, F, M) runs fused: the one-pass kernel where its LDS
+    fits, else the two-phase kernel."""
     for D in (16, 32, 64, 128):
-        for F, M in ((16, 16), (16, 64), (16, 128), (32, 128), (64, 128)):
-            assert supported(ea, 8, 8, 1024, D, M, F), (D, F, M)
-    for D in (16, 32, 64):
-        for F, M in ((32, 32), (32, 64)):
-            assert supported(ea, 8, 8, 1024, D, M, F), (D, F, M)
+        for F in (16, 32, 64):
+            for M in (16, 32, 64, 128):
+                assert supported(ea, 8, 8, 1024, D, M, F), (D, F, M)
+    assert not supported(ea, 8, 8, 1024, 64, 64, 128)  # F = 128: two launches
 
 
 @pytest.mark.parametrize("N", [1, 31, 32, 33, 127, 128, 129])
@@ -231,6 +230,92 @@ def test_fused_features_bf16_equals_widened_f32(ea, kind):
     out16, S16, z16 = run(ea, dev, F, kind, False)
     wide = tuple(x.float().contiguous() for x in dev[:3]) + (dev[3],)
     out32, S32, z32 = run(ea, wide, F, kind, False)
+    torch.cuda.synchronize()
+    assert torch.equal(out16, out32)
+    assert torch.equal(S16, S32) and torch.equal(z16, z32)
+
+
+def plan_is_onepass(B, H, N):
+    """Whether la_forward_features' plan (chunks of 32, segments sized for 512
+    workgroups) has segments of at most four chunks."""
+    n = -(-N // 32)
+    cps = max(1, -(-(n * B * H) // 512))
+    G = -(-n // cps)
+    return -(-n // G) <= 4
+
+
+LONG = [(1, 2, 65536, 64, 16, 64), (2, 1, 40000, 32, 32, 32), (1, 1, 80000, 128, 16, 128)]
+
+
+def two_phase_case(ea, kind, normalize, B, H, N, D, F, M, rows=None):
+    """Runs the fused kernel; checks it against the two-launch path (on the rows
+    selected by `rows`, a function of the oracle inputs, if given)."""
+    if not supported(ea, B, H, N, D, M, F):
+        pytest.skip(f"D={D} F={F} M={M}: the kernel's LDS does not fit")
+    assert not plan_is_onepass(B, H, N)
+    dev, host = case(ea, B, H, N, D, M, F, kind, 80 + D, normalize)
+    out, S, z = run(ea, dev, F, kind, normalize)
+    Qd, Kd, Vd, Wd = dev
+    fq, fk = ea.feature_map(Qd, Wd, F, kind, normalize, X2=Kd)
+    two = ea.forward_chunked(fq, fk, Vd, causal=True, features=True)
+    torch.cuda.synchronize()
+    a, b = out.cpu().numpy(), two.cpu().numpy()
+    mask = rows(host) if rows is not None else np.ones(a.shape[:-1], dtype=bool)
+    assert rowwise_rel(a[mask], b[mask]) <= 1e-5
+    return out, S, z, host, mask
+
+
+@pytest.mark.parametrize("kind,normalize", [("prf", False), ("prf", True), ("trf", False)])
+@pytest.mark.parametrize("B,H,N,D,F,M", LONG)
+def test_fused_features_two_phase(ea, kind, normalize, B, H, N, D, F, M):
+    """Long heads: segments of more than four chunks run the two-phase kernel with
+    the map fused into both phases (ragged last chunk in the second shape):
+    against the oracle and against the two-launch path."""
+    out, S, z, host, _ = two_phase_case(ea, kind, normalize, B, H, N, D, F, M)
+    check(out, S, z, oracle_out(host, F, kind, normalize))
+
+
+KAPPA_MAX = 30.0
+
+
+def well_conditioned(F, kind, normalize):
+    """Rows whose denominator sum cancels little: kappa_i = (|phi(q_i)| . sum_{j<=i}
+    |phi(k_j)|) / |phi(q_i) . sum_{j<=i} phi(k_j)| (an upper bound on the sum of
+    absolute terms over the absolute sum) at most KAPPA_MAX."""
+    def rows(host):
+        Xq, Xk, _, W = host
+        W64 = W.astype(np.float64)
+        Fq = oracle.feature_map(Xq.astype(np.float64), W64, F, kind, normalize)
+        Fk = oracle.feature_map(Xk.astype(np.float64), W64, F, kind, normalize)
+        den = np.abs(np.einsum("...f,...f->...", Fq, np.cumsum(Fk, axis=-2)))
+        bound = np.einsum("...f,...f->...", np.abs(Fq), np.cumsum(np.abs(Fk), axis=-2))
+        return bound <= KAPPA_MAX * den
+    return rows
+
+
+@pytest.mark.parametrize("B,H,N,D,F,M", LONG)
+def test_fused_features_two_phase_trf_normalized(ea, B, H, N, D, F, M):
+    """TRF on unit-length rows: the normalisation undoes the input scale that keeps
+    TRF denominators away from zero, so some rows are ill-conditioned (their
+    denominator sums cancel) and any two fp32 summation orders differ there
+    beyond 1e-4.  The well-conditioned rows (cancellation factor at most 30) are
+    held to the oracle and to the two-launch path; at least nine rows in ten of
+    every head must qualify."""
+    rows = well_conditioned(F, "trf", True)
+    out, S, z, host, mask = two_phase_case(ea, "trf", True, B, H, N, D, F, M, rows)
+    assert mask.mean(axis=-1).min() >= 0.9
+    want = oracle_out(host, F, "trf", True)[0]
+    err = rowwise_rel(out.cpu().numpy()[mask], want[mask])
+    assert err <= TOL["f32"], f"{err:.3e}"
+
+
+def test_fused_features_two_phase_bf16_equals_widened_f32(ea):
+    B, H, N, D, M, F = 1, 2, 65536, 64, 64, 16
+    assert not plan_is_onepass(B, H, N)
+    dev, _ = bf16_case(ea, B, H, N, D, M, F, "prf", 81)
+    out16, S16, z16 = run(ea, dev, F, "prf", False)
+    wide = tuple(x.float().contiguous() for x in dev[:3]) + (dev[3],)
+    out32, S32, z32 = run(ea, wide, F, "prf", False)
     torch.cuda.synchronize()
     assert torch.equal(out16, out32)
     assert torch.equal(S16, S32) and torch.equal(z16, z32)
