@@ -9,6 +9,7 @@ from .linattn import (  # noqa: F401
     LinAttnError,
     backward,
     decode_step,
+    decode_step_features,
     decode_steps,
     feature_map,
     forward_chunked,

@@ -398,6 +398,26 @@ LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, cons
     return hip_status(la::decode_step(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), as_stream(stream)));
 }
 
+LA_API int la_decode_step_features(float *S, float *z, const void *q, const void *k, const void *v, float *out,
+                                   int64_t B, int64_t H, int64_t D, int64_t M, int dtype, const float *W, int64_t F,
+                                   int kind, int flags, void *stream) {
+    if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
+    if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(M) || !(F == 16 || F == 32 || F == 64)) return LA_ERR_UNSUPPORTED;
+    if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (B * H == 0) return LA_OK;
+    if (!S || !z || !q || !k || !v || !out || !W) return LA_ERR_INVALID_ARG;
+    if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        !aligned16(W))
+        return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::decode_step_features(dtype, (int)D, (int)F, (int)M, S, z, q, k, v, out, W, kind,
+                                               (flags & LA_FEATURE_NORMALIZE) != 0, (int)(B * H),
+                                               as_stream(stream)));
+}
+
 namespace {
 // Backward plan: chunks of kBackwardChunk positions, segments sized like the
 // forward planner's (about 512 workgroups, or 256 for states above 64 x 64).

@@ -72,6 +72,10 @@ hipError_t backward_dkv(int dtype, int D, int M, const void *Q, const void *K, c
                         int G, int CPS, hipStream_t stream);
 hipError_t backward_rev_scan(float *ws, int BH, int E, int G, hipStream_t stream);
 
+// one recurrent step on raw q, k rows (DI wide, fp32 or bf16) mapped to F random features in the kernel
+hipError_t decode_step_features(int dtype, int DI, int F, int M, float *S, float *z, const void *q, const void *k,
+                                const void *v, float *out, const float *W, int kind, int norm, int BH,
+                                hipStream_t stream);
 hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
                        float *out, int BH, hipStream_t stream);
 hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,

@@ -151,14 +151,21 @@ __device__ __forceinline__ f32x4 load4<bf16>(const bf16 *p) {
     return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
 }
 
-template <typename T, int D, int M, bool PHI = true>
+// DI > 0: q and k are raw rows DI wide and the random-feature map (W [P][DI],
+// fkind, fnorm; as in the prefill kernels) forms their D = F features here.
+template <typename T, int D, int M, bool PHI = true, int DI = 0>
 __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *__restrict__ S, float *__restrict__ z,
                                                                       const T *__restrict__ q,
                                                                       const T *__restrict__ k,
                                                                       const T *__restrict__ v,
-                                                                      float *__restrict__ out) {
+                                                                      float *__restrict__ out,
+                                                                      const float *__restrict__ W = nullptr,
+                                                                      int fkind = 0, int fnorm = 0) {
     using G = DecCfg<D, M>;
+    constexpr bool FEAT = DI > 0;
+    constexpr int DQ = FEAT ? DI : D;  // width of the q, k rows in memory
     __shared__ float sq[D], sk[D];
+    __shared__ float sx[FEAT ? 2 * DI : 1];  // raw q, k rows
     __shared__ f32x4 sred[G::NW][G::LPR];
     __shared__ float sden[G::NW];
 
@@ -177,8 +184,46 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *
         const int d = tid + i * G::THREADS;
         if (d < D) {
             zz[i] = z[bh * D + d];
-            sq[d] = phi_if<PHI>(to_f32(q[bh * D + d]));
-            sk[d] = phi_if<PHI>(to_f32(k[bh * D + d]));
+            if constexpr (!FEAT) {
+                sq[d] = phi_if<PHI>(to_f32(q[bh * D + d]));
+                sk[d] = phi_if<PHI>(to_f32(k[bh * D + d]));
+            }
+        }
+    }
+    if constexpr (FEAT) {
+        for (int d = tid; d < DI; d += G::THREADS) {
+            sx[d] = to_f32(q[bh * DQ + d]);
+            sx[DI + d] = to_f32(k[bh * DQ + d]);
+        }
+        __syncthreads();
+        // thread f < P: projection f of q; P <= f < 2P: of k.  Each thread also
+        // sums |x|^2 of its row (LDS broadcast reads).
+        const int P = fkind == 2 ? D / 2 : D;
+        for (int f = tid; f < 2 * P; f += G::THREADS) {
+            const int t = f / P, pf = f - t * P;
+            const float *x = sx + t * DI;
+            const float *wr = W + (size_t)pf * DI;
+            float acc = 0.0f, ss = 0.0f;
+#pragma unroll 8
+            for (int d = 0; d < DI; ++d) {
+                acc += wr[d] * x[d];
+                ss += x[d] * x[d];
+            }
+            float scale = 1.0f;
+            if (fnorm && ss > 0.0f) {
+                scale = 1.0f / sqrtf(ss);
+                ss = ss * scale * scale;
+            }
+            float *dst = t == 0 ? sq : sk;
+            if (fkind == 1) {
+                dst[pf] = __expf(acc * scale - 0.5f * ss) * (1.0f / sqrtf((float)D));
+            } else {
+                const float c = __expf(0.5f * ss) / sqrtf((float)P);
+                float sn, cs;
+                sincosf(acc * scale, &sn, &cs);
+                dst[pf] = c * sn;
+                dst[P + pf] = c * cs;
+            }
         }
     }
     __syncthreads();
@@ -247,7 +292,16 @@ hipError_t run_decode(float *S, float *z, const void *q, const void *k, const vo
                       hipStream_t stream) {
     if (BH <= 0) return hipSuccess;
     hipLaunchKernelGGL((decode_kernel<T, D, M, PHI>), dim3((unsigned)BH), dim3(DecCfg<D, M>::THREADS), 0, stream, S, z,
-                       (const T *)q, (const T *)k, (const T *)v, out);
+                       (const T *)q, (const T *)k, (const T *)v, out, nullptr, 0, 0);
+    return hipGetLastError();
+}
+
+template <typename T, int DI, int F, int M>
+hipError_t run_decode_features(float *S, float *z, const void *q, const void *k, const void *v, float *out,
+                               const float *W, int kind, int norm, int BH, hipStream_t stream) {
+    if (BH <= 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_kernel<T, F, M, false, DI>), dim3((unsigned)BH), dim3(DecCfg<F, M>::THREADS), 0, stream,
+                       S, z, (const T *)q, (const T *)k, (const T *)v, out, W, kind, norm);
     return hipGetLastError();
 }
 
@@ -386,6 +440,23 @@ hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *
                                      : run_decode<float, D_, M_, false>(S, z, q, k, v, out, BH, stream);
 #define XM(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
     XM(16) XM(32) XM(64) XM(128)
+#undef XM
+#undef X
+    return hipErrorInvalidValue;
+}
+
+hipError_t decode_step_features(int dtype, int DI, int F, int M, float *S, float *z, const void *q, const void *k,
+                                const void *v, float *out, const float *W, int kind, int norm, int BH,
+                                hipStream_t stream) {
+#define X(DI_, F_, M_)                                                                                        \
+    if (DI == DI_ && F == F_ && M == M_)                                                                      \
+        return dtype == kDtypeF32                                                                             \
+                   ? run_decode_features<float, DI_, F_, M_>(S, z, q, k, v, out, W, kind, norm, BH, stream)  \
+                   : run_decode_features<bf16, DI_, F_, M_>(S, z, q, k, v, out, W, kind, norm, BH, stream);
+#define XM(DI_, F_) X(DI_, F_, 16) X(DI_, F_, 32) X(DI_, F_, 64) X(DI_, F_, 128)
+#define XF(DI_) XM(DI_, 16) XM(DI_, 32) XM(DI_, 64)
+    XF(16) XF(32) XF(64) XF(128)
+#undef XF
 #undef XM
 #undef X
     return hipErrorInvalidValue;

@@ -53,6 +53,8 @@ SIGNATURES = {
     "la_decode_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_decode_steps": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_feature_map": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp, _i64, _int, _int, _vp]),
+    "la_decode_step_features": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _i64, _int,
+                                       _int, _vp]),
     "la_forward_features_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "la_forward_features": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _int,
                                    _int, _vp, _sz, _vp, _vp, _vp]),
@@ -511,4 +513,35 @@ def forward_features(Q, K, V, W, F, kind="prf", normalize=False, out=None, works
                                    LA_FEATURE_NORMALIZE if normalize else 0, _ptr(workspace), wbytes,
                                    _ptr(S_out), _ptr(z_out), _stream(stream, dev))
     _check(st, "la_forward_features")
+    return out
+
+
+def decode_step_features(S, z, q, k, v, W, F, kind="prf", normalize=False, out=None, stream=None):
+    """One recurrent step on raw rows with the random-feature map formed in the kernel:
+    S [B,H,F,M], z [B,H,F] (float32, updated in place); q, k [B,H,D] and v [B,H,M]
+    (float32 or bfloat16); W as for feature_map.  Returns out [B,H,M] float32."""
+    import torch
+    if S.dim() != 4:
+        raise ValueError("S must be [B, H, F, M]")
+    B, H, Fs, M = S.shape
+    if Fs != F:
+        raise ValueError("S must hold F features per head")
+    D = q.shape[-1]
+    dev = S.device
+    k_ = FEATURE_KINDS[kind]
+    if k_ == LA_FEATURE_ELU:
+        raise ValueError("decode_step_features takes 'prf' or 'trf' (elu+1 is decode_step itself)")
+    _require(S, "S", (B, H, F, M), torch.float32, dev)
+    _require(z, "z", (B, H, F), torch.float32, dev)
+    _require(q, "q", (B, H, D), None, dev)
+    _require(k, "k", (B, H, D), q.dtype, dev)
+    _require(v, "v", (B, H, M), q.dtype, dev)
+    _require(W, "W", ((F if k_ == LA_FEATURE_PRF else F // 2), D), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, H, M), dtype=torch.float32, device=dev)
+    _require(out, "out", (B, H, M), torch.float32, dev)
+    st = lib().la_decode_step_features(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, D, M,
+                                       _dtype_code(q), _ptr(W), F, k_, LA_FEATURE_NORMALIZE if normalize else 0,
+                                       _stream(stream, dev))
+    _check(st, "la_decode_step_features")
     return out

@@ -362,6 +362,18 @@ LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2
  * la_feature_map followed by la_forward_chunked (LA_F32_FEATURES) computes the
  * same result in two launches for any supported feature dimension.
  */
+/* One recurrent step (as la_decode_step) on raw rows with the random-feature
+ * map formed inside the kernel: q, k [B][H][D] raw rows and v [B][H][M], all of
+ * element type dtype (LA_F32 or LA_BF16, widened exactly); W, F, kind (PRF or
+ * TRF) and flags (LA_FEATURE_NORMALIZE) as for la_feature_map; S [B][H][F][M]
+ * and z [B][H][F] fp32, updated in place (the state la_forward_features leaves
+ * in S_out, z_out); out [B][H][M] fp32.  F must be 16, 32 or 64.  Equals
+ * la_feature_map followed by la_decode_step with LA_F32_FEATURES.
+ */
+LA_API int la_decode_step_features(float *S, float *z, const void *q, const void *k, const void *v, float *out,
+                                   int64_t B, int64_t H, int64_t D, int64_t M, int dtype, const float *W, int64_t F,
+                                   int kind, int flags, void *stream);
+
 LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F);
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
                                int64_t N, int64_t D, int64_t M, int dtype, const float *W, int64_t F, int kind,

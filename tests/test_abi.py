@@ -325,3 +325,23 @@ def test_forward_features_checks(L):
     assert call(ws_bytes=need - 1) == L.LA_ERR_WORKSPACE
     assert call(ws=None) == L.LA_ERR_WORKSPACE
     assert call(B=0) == L.LA_OK  # no heads: nothing to do
+
+
+def test_decode_step_features_checks(L):
+    f = L.lib().la_decode_step_features
+    # S, z, q, k, v, out, B, H, D, M, dtype, W, F, kind, flags, stream
+    a = [FAKE] * 6 + [2, 2, 64, 64, 0, FAKE, 16, 1, 0, None]
+
+    def call(i, val):
+        b = list(a)
+        b[i] = val
+        return f(*b)
+
+    assert call(10, 2) == L.LA_ERR_INVALID_ARG  # dtype: raw rows only
+    assert call(13, 0) == L.LA_ERR_INVALID_ARG  # elu+1 is la_decode_step
+    assert call(14, 2) == L.LA_ERR_INVALID_ARG  # flag
+    assert call(12, 128) == L.LA_ERR_UNSUPPORTED  # F
+    assert call(8, 48) == L.LA_ERR_UNSUPPORTED  # D
+    assert call(11, None) == L.LA_ERR_INVALID_ARG  # W
+    assert call(4, FAKE + 4) == L.LA_ERR_INVALID_ARG  # alignment
+    assert call(6, 0) == L.LA_OK  # no heads

@@ -319,3 +319,39 @@ def test_fused_features_two_phase_bf16_equals_widened_f32(ea):
     torch.cuda.synchronize()
     assert torch.equal(out16, out32)
     assert torch.equal(S16, S32) and torch.equal(z16, z32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,normalize", [("prf", False), ("prf", True), ("trf", False)])
+@pytest.mark.parametrize("D,F,M", [(64, 16, 64), (32, 32, 128), (128, 64, 16)])
+def test_decode_step_features(ea, dtype, kind, normalize, D, F, M):
+    """Prefill with the map fused (la_forward_features, final state out), then
+    decode steps on raw rows with the map formed in the decode kernel
+    (la_decode_step_features): every decoded row equals the running sums of the
+    whole sequence (oracle), and each step equals la_feature_map +
+    la_decode_step on features."""
+    B, H, n0, T = 2, 3, 200, 12
+    N = n0 + T
+    if dtype == "f32":
+        dev, host = case(ea, B, H, N, D, M, F, kind, 90 + D, normalize)
+    else:
+        dev, host = bf16_case(ea, B, H, N, D, M, F, kind, 90 + D, normalize)
+    Qd, Kd, Vd, Wd = dev
+    ref = oracle_out(host, F, kind, normalize)[0]
+    S = torch.empty((B, H, F, M), device=DEV)
+    z = torch.empty((B, H, F), device=DEV)
+    ea.forward_features(Qd[:, :, :n0].contiguous(), Kd[:, :, :n0].contiguous(), Vd[:, :, :n0].contiguous(), Wd, F,
+                        kind, normalize, S_out=S, z_out=z)
+    S2, z2 = S.clone(), z.clone()
+    steps, steps2 = [], []
+    for t in range(n0, N):
+        q, k, v = (x[:, :, t].contiguous() for x in (Qd, Kd, Vd))
+        steps.append(ea.decode_step_features(S, z, q, k, v, Wd, F, kind, normalize))
+        fq, fk = ea.feature_map(q, Wd, F, kind, normalize, X2=k)
+        steps2.append(ea.decode_step(S2, z2, fq, fk, v.float().contiguous(), features=True))
+    torch.cuda.synchronize()
+    got = torch.stack(steps, dim=2).cpu().numpy()
+    two = torch.stack(steps2, dim=2).cpu().numpy()
+    assert rowwise_rel(got, ref[:, :, n0:]) <= TOL["f32"]
+    assert rowwise_rel(got, two) <= 1e-5
+    assert whole_rel(S.cpu().numpy(), S2.cpu().numpy()) <= 1e-6
