@@ -605,8 +605,8 @@ LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t 
 
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
                                int64_t N, int64_t D, int64_t M, int dtype, const float *W, int64_t F, int kind,
-                               int flags, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
-                               void *stream) {
+                               int flags, void *workspace, size_t workspace_bytes, const float *S_in,
+                               const float *z_in, float *S_out, float *z_out, void *stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
     if (kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
     if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
@@ -614,15 +614,25 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
     int st = features_plan(B, H, N, D, M, F, &p);
     if (st != LA_OK) return st;
     if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+    if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID_ARG;
     if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+    if (S_in && (!aligned16(S_in) || !aligned16(z_in))) return LA_ERR_INVALID_ARG;
     const int64_t BH = B * H;
     if (BH == 0) return LA_OK;
     hipStream_t s = as_stream(stream);
     if (N == 0) {
         if (S_out == nullptr) return LA_OK;
         (void)hipGetLastError();
-        hipError_t e = la::fill_zero(S_out, (size_t)(BH * F * M), s);
-        if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * F), s);
+        hipError_t e = hipSuccess;
+        if (S_in) {  // the state passes through unchanged
+            if (S_out != S_in)
+                e = hipMemcpyAsync(S_out, S_in, (size_t)(BH * F * M) * sizeof(float), hipMemcpyDeviceToDevice, s);
+            if (e == hipSuccess && z_out != z_in)
+                e = hipMemcpyAsync(z_out, z_in, (size_t)(BH * F) * sizeof(float), hipMemcpyDeviceToDevice, s);
+        } else {
+            e = la::fill_zero(S_out, (size_t)(BH * F * M), s);
+            if (e == hipSuccess) e = la::fill_zero(z_out, (size_t)(BH * F), s);
+        }
         return hip_status(e);
     }
     if (!Q || !K || !V || !out || !W) return LA_ERR_INVALID_ARG;
@@ -634,10 +644,10 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
     return hip_status(dtype == LA_F32
                           ? la::prefill_features_f32(p.onepass, (int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
                                                      workspace, (int)BH, (int)N, p.segments, p.chunks_per_segment,
-                                                     S_out, z_out, s)
+                                                     S_out, z_out, S_in, z_in, s)
                           : la::prefill_features_bf16(p.onepass, (int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
                                                       workspace, (int)BH, (int)N, p.segments, p.chunks_per_segment,
-                                                      S_out, z_out, s));
+                                                      S_out, z_out, S_in, z_in, s));
 }
 
 // ---- feature maps ----------------------------------------------------------

@@ -19,9 +19,10 @@ bool prefill_features_supported(bool onepass, int DI, int F, int M) {
 
 hipError_t prefill_features_f32(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
                                 const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                int CPS, float *S_out, float *z_out, hipStream_t stream) {
+                                int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+                                hipStream_t stream) {
     return prefill_features_typed<float>(onepass, DI, F, M, Q, K, V, W, kind, norm, out, ws, BH, N, G, CPS, S_out,
-                                         z_out, stream);
+                                         z_out, S_in, z_in, stream);
 }
 
 }  // namespace la

@@ -14,15 +14,16 @@ namespace la {
 template <typename TI>
 hipError_t prefill_features_typed(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
                                   const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                  int CPS, float *S_out, float *z_out, hipStream_t stream) {
+                                  int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+                                  hipStream_t stream) {
 #define X(DI_, F_, M_)                                                                                        \
     if (DI == DI_ && F == F_ && M == M_)                                                                      \
         return onepass ? run_onepass_features<DI_, F_, M_, kFusedFeatureChunk, TI>(Q, K, V, W, kind, norm, out, ws, \
                                                                                    BH, N, G, CPS, S_out, z_out,    \
-                                                                                   stream)                         \
+                                                                                   S_in, z_in, stream)             \
                        : run_fused_features<DI_, F_, M_, kFusedFeatureChunk, TI>(Q, K, V, W, kind, norm, out, ws,   \
                                                                                  BH, N, G, CPS, S_out, z_out,      \
-                                                                                 stream);
+                                                                                 S_in, z_in, stream);
 #define XM(DI_, F_) X(DI_, F_, 16) X(DI_, F_, 32) X(DI_, F_, 64) X(DI_, F_, 128)
 #define XF(DI_) XM(DI_, 16) XM(DI_, 32) XM(DI_, 64)
     XF(16) XF(32) XF(64) XF(128)

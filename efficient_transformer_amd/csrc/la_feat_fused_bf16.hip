@@ -5,9 +5,10 @@ namespace la {
 
 hipError_t prefill_features_bf16(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
                                  const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                 int CPS, float *S_out, float *z_out, hipStream_t stream) {
+                                 int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+                                hipStream_t stream) {
     return prefill_features_typed<bf16>(onepass, DI, F, M, Q, K, V, W, kind, norm, out, ws, BH, N, G, CPS, S_out,
-                                        z_out, stream);
+                                        z_out, S_in, z_in, stream);
 }
 
 }  // namespace la

@@ -104,10 +104,12 @@ constexpr int kFusedFeatureChunk = 32;
 bool prefill_features_supported(bool onepass, int DI, int F, int M);
 hipError_t prefill_features_f32(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
                                 const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                int CPS, float *S_out, float *z_out, hipStream_t stream);
+                                int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+                                hipStream_t stream);
 hipError_t prefill_features_bf16(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
                                  const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                 int CPS, float *S_out, float *z_out, hipStream_t stream);
+                                 int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+                                 hipStream_t stream);
 
 // feature inputs (la_feat_prefill.hip, la_feat_onepass.hip)
 bool prefill_supported_feat(int D, int M, int C);

@@ -1638,7 +1638,7 @@ constexpr bool onepass_features_fit() {
 template <int DI, int F, int M, int C, typename TI = float>
 hipError_t run_onepass_features(const void *Q, const void *K, const void *V, const float *W, int fkind, int fnorm,
                                 float *out, void *ws, int BH, int N, int G_, int CPS, float *S_out, float *z_out,
-                                hipStream_t stream) {
+                                const float *S_in, const float *z_in, hipStream_t stream) {
     using Gc = Cfg<float, F, M, C>;
     if constexpr (!onepass_features_fit<DI, F, M, C>()) {
         return hipErrorInvalidValue;
@@ -1647,7 +1647,7 @@ hipError_t run_onepass_features(const void *Q, const void *K, const void *V, con
         if (CPS < 1 || CPS > kOnePassChunks) return hipErrorInvalidValue;
         hipLaunchKernelGGL((onepass_causal_kernel<float, F, M, C, false, float, DI, TI>), dim3((unsigned)(BH * G_)),
                            dim3(Gc::THREADS), 0, stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws,
-                           BH, N, G_, CPS, S_out, z_out, nullptr, nullptr, W, fkind, fnorm);
+                           BH, N, G_, CPS, S_out, z_out, S_in, z_in, W, fkind, fnorm);
         return hipGetLastError();
     }
 }
@@ -1666,7 +1666,7 @@ constexpr bool fused_features_fit() {
 template <int DI, int F, int M, int C, typename TI = float>
 hipError_t run_fused_features(const void *Q, const void *K, const void *V, const float *W, int fkind, int fnorm,
                               float *out, void *ws, int BH, int N, int G_, int CPS, float *S_out, float *z_out,
-                              hipStream_t stream) {
+                              const float *S_in, const float *z_in, hipStream_t stream) {
     using Gc = Cfg<float, F, M, C>;
     if constexpr (!fused_features_fit<DI, F, M, C>()) {
         return hipErrorInvalidValue;
@@ -1675,7 +1675,7 @@ hipError_t run_fused_features(const void *Q, const void *K, const void *V, const
         const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
         hipLaunchKernelGGL((fused_causal_kernel<float, F, M, C, false, float, DI, TI>), dim3(grid), dim3(Gc::THREADS), 0,
                            stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws, BH, N, G_, CPS, S_out, z_out,
-                           nullptr, nullptr, W, fkind, fnorm);
+                           S_in, z_in, W, fkind, fnorm);
         return hipGetLastError();
     }
 }

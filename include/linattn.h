@@ -349,8 +349,11 @@ LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2
  * Q, K [B][H][N][D] (raw rows) and V [B][H][N][M], all of element type dtype
  * (LA_F32 or LA_BF16; bf16 values are widened exactly, the map and the
  * attention run in fp32 as for fp32 rows), W as for la_feature_map, out
- * [B][H][N][M] fp32; S_out [B][H][F][M], z_out [B][H][F] optional (both or
- * neither): the final state over the features.
+ * [B][H][N][M] fp32; S_in [B][H][F][M], z_in [B][H][F] optional (both or
+ * neither): a carried state the sequence continues from (as for
+ * la_forward_continue; S_out may be S_in for an in-place update, so a call on T
+ * new tokens is a T-token decode step); S_out [B][H][F][M], z_out [B][H][F]
+ * optional (both or neither): the final state over the features.
  * workspace: la_forward_features_workspace_bytes(...) bytes (at least 256 for
  * a supported shape, 0 for a refused one), initialised and reused as for
  * la_forward_chunked.
@@ -377,8 +380,8 @@ LA_API int la_decode_step_features(float *S, float *z, const void *q, const void
 LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F);
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
                                int64_t N, int64_t D, int64_t M, int dtype, const float *W, int64_t F, int kind,
-                               int flags, void *workspace, size_t workspace_bytes, float *S_out, float *z_out,
-                               void *stream);
+                               int flags, void *workspace, size_t workspace_bytes, const float *S_in,
+                               const float *z_in, float *S_out, float *z_out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -355,3 +355,54 @@ def test_decode_step_features(ea, dtype, kind, normalize, D, F, M):
     assert rowwise_rel(got, ref[:, :, n0:]) <= TOL["f32"]
     assert rowwise_rel(got, two) <= 1e-5
     assert whole_rel(S.cpu().numpy(), S2.cpu().numpy()) <= 1e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,H,n0,n1,D,F,M", [(2, 3, 300, 200, 64, 16, 64), (1, 2, 40000, 30000, 32, 32, 32)])
+def test_fused_features_continue(ea, dtype, B, H, n0, n1, D, F, M):
+    """Continuation from a carried state: the second call's rows (one-pass or
+    two-phase plan) equal the oracle's running sums over the whole sequence, and
+    its final state equals one call over everything; then the same continuation
+    in place (S_out = S_in)."""
+    N = n0 + n1
+    if dtype == "f32":
+        dev, host = case(ea, B, H, N, D, M, F, "prf", 95 + D)
+    else:
+        dev, host = bf16_case(ea, B, H, N, D, M, F, "prf", 95 + D)
+    Qd, Kd, Vd, Wd = dev
+    ref, S_ref, z_ref = oracle_out(host, F, "prf", False)
+    head = [x[:, :, :n0].contiguous() for x in (Qd, Kd, Vd)]
+    tail = [x[:, :, n0:].contiguous() for x in (Qd, Kd, Vd)]
+    S0 = torch.empty((B, H, F, M), device=DEV)
+    z0 = torch.empty((B, H, F), device=DEV)
+    ea.forward_features(*head, Wd, F, "prf", S_out=S0, z_out=z0)
+    S1, z1 = torch.empty_like(S0), torch.empty_like(z0)
+    rest = ea.forward_features(*tail, Wd, F, "prf", S_in=S0, z_in=z0, S_out=S1, z_out=z1)
+    S2, z2 = S0.clone(), z0.clone()
+    rest2 = ea.forward_features(*tail, Wd, F, "prf", S_in=S2, z_in=z2, S_out=S2, z_out=z2)
+    torch.cuda.synchronize()
+    assert rowwise_rel(rest.cpu().numpy(), ref[:, :, n0:]) <= TOL["f32"]
+    assert whole_rel(S1.cpu().numpy(), S_ref) <= 1e-5 and whole_rel(z1.cpu().numpy(), z_ref) <= 1e-5
+    assert rowwise_rel(rest2.cpu().numpy(), rest.cpu().numpy()) <= 1e-6
+    assert whole_rel(S2.cpu().numpy(), S1.cpu().numpy()) <= 1e-6
+
+
+def test_fused_features_multi_token_decode(ea):
+    """T tokens per call with the map fused (a continuation on 16 new rows, state
+    updated in place) equals T single fused decode steps."""
+    B, H, D, M, F, n0, T = 4, 8, 64, 64, 16, 256, 16
+    dev, host = case(ea, B, H, n0 + T, D, M, F, "trf", 97)
+    Qd, Kd, Vd, Wd = dev
+    S = torch.empty((B, H, F, M), device=DEV)
+    z = torch.empty((B, H, F), device=DEV)
+    ea.forward_features(*(x[:, :, :n0].contiguous() for x in (Qd, Kd, Vd)), Wd, F, "trf", S_out=S, z_out=z)
+    S1, z1 = S.clone(), z.clone()
+    multi = ea.forward_features(*(x[:, :, n0:].contiguous() for x in (Qd, Kd, Vd)), Wd, F, "trf", S_in=S, z_in=z,
+                                S_out=S, z_out=z)
+    single = [ea.decode_step_features(S1, z1, *(x[:, :, t].contiguous() for x in (Qd, Kd, Vd)), Wd, F, "trf")
+              for t in range(n0, n0 + T)]
+    torch.cuda.synchronize()
+    ref = oracle_out(host, F, "trf", False)[0][:, :, n0:]
+    assert rowwise_rel(multi.cpu().numpy(), ref) <= TOL["f32"]
+    assert rowwise_rel(torch.stack(single, dim=2).cpu().numpy(), multi.cpu().numpy()) <= 1e-5
+    assert whole_rel(S.cpu().numpy(), S1.cpu().numpy()) <= 1e-5
