@@ -582,13 +582,15 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
 
 namespace {
 // The plan of la_forward_features (LA_OK only when the fused kernel runs it).
-int features_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F, Plan *p) {
+int features_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F, int causal, Plan *p) {
+    if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(F)) return LA_ERR_UNSUPPORTED;
     // the fused kernels' LDS (raw rows and W besides the attention tiles) admits
     // two workgroups per CU: plan 512 resident workgroups
-    int st = make_plan(B, H, N, F, M, 1, LA_F32_FEATURES, la::kFusedFeatureChunk, p, 512);
+    int st = make_plan(B, H, N, F, M, causal, LA_F32_FEATURES, la::kFusedFeatureChunk, p, 512);
     if (st != LA_OK) return st;
     if (B * H == 0 || N == 0) return LA_OK;
+    if (!causal) return la::prefill_features_noncausal_supported((int)D, (int)F, (int)M) ? LA_OK : LA_ERR_UNSUPPORTED;
     // the one-pass kernel where its segments fit (at most four chunks) and its LDS
     // does, else the two-phase kernel (any segment length, less LDS)
     if (p->onepass && !la::prefill_features_supported(true, (int)D, (int)F, (int)M)) p->onepass = false;
@@ -597,21 +599,23 @@ int features_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t
 }
 }  // namespace
 
-LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F) {
+LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F,
+                                                  int causal) {
     Plan p;
     // a supported shape asks for at least 256 bytes, so 0 always means "refused"
-    return features_plan(B, H, N, D, M, F, &p) == LA_OK ? std::max<size_t>(p.ws_bytes, 256) : 0;
+    return features_plan(B, H, N, D, M, F, causal, &p) == LA_OK ? std::max<size_t>(p.ws_bytes, 256) : 0;
 }
 
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                               int64_t N, int64_t D, int64_t M, int dtype, const float *W, int64_t F, int kind,
-                               int flags, void *workspace, size_t workspace_bytes, const float *S_in,
+                               int64_t N, int64_t D, int64_t M, int causal, int dtype, const float *W, int64_t F,
+                               int kind, int flags, void *workspace, size_t workspace_bytes, const float *S_in,
                                const float *z_in, float *S_out, float *z_out, void *stream) {
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
     if (kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
     if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
+    if (causal == 0 && (S_in || z_in || S_out || z_out)) return LA_ERR_INVALID_ARG;  // states: causal only
     Plan p;
-    int st = features_plan(B, H, N, D, M, F, &p);
+    int st = features_plan(B, H, N, D, M, F, causal, &p);
     if (st != LA_OK) return st;
     if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
     if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID_ARG;
@@ -641,6 +645,11 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
     if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
     const int norm = (flags & LA_FEATURE_NORMALIZE) != 0;
+    if (!causal)
+        return hip_status(la::prefill_features_noncausal(dtype == LA_F32 ? la::kDtypeF32 : la::kDtypeBf16, (int)D,
+                                                         (int)F, (int)M, Q, K, V, W, kind, norm, out,
+                                                         static_cast<float *>(workspace), (int)BH, (int)N, p.segments,
+                                                         p.chunks_per_segment, s));
     return hip_status(dtype == LA_F32
                           ? la::prefill_features_f32(p.onepass, (int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
                                                      workspace, (int)BH, (int)N, p.segments, p.chunks_per_segment,

@@ -33,4 +33,22 @@ hipError_t prefill_features_typed(bool onepass, int DI, int F, int M, const void
     return hipErrorInvalidValue;
 }
 
+// Non-causal: the stage path with the map in both stage kernels.
+template <typename TI>
+hipError_t prefill_features_noncausal_typed(int DI, int F, int M, const void *Q, const void *K, const void *V,
+                                            const float *W, int kind, int norm, float *out, float *ws, int BH, int N,
+                                            int G, int CPS, hipStream_t stream) {
+#define X(DI_, F_, M_)                                                                                           \
+    if (DI == DI_ && F == F_ && M == M_)                                                                         \
+        return run_noncausal_features<DI_, F_, M_, kFusedFeatureChunk, TI>(Q, K, V, W, kind, norm, out, ws, BH, N, \
+                                                                           G, CPS, stream);
+#define XM(DI_, F_) X(DI_, F_, 16) X(DI_, F_, 32) X(DI_, F_, 64) X(DI_, F_, 128)
+#define XF(DI_) XM(DI_, 16) XM(DI_, 32) XM(DI_, 64)
+    XF(16) XF(32) XF(64) XF(128)
+#undef XF
+#undef XM
+#undef X
+    return hipErrorInvalidValue;
+}
+
 }  // namespace la

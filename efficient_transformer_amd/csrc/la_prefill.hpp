@@ -1544,35 +1544,47 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 // Stage workspace: [BH][G + 1][E]; slot s = state of segment s, later its
 // exclusive prefix; slot G = total.
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M, int C, bool PHI = true>
-__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_state_kernel(const T *__restrict__ K, const T *__restrict__ V,
-                                                             float *__restrict__ ws, int N, int G_, int CPS,
-                                                             int nstates) {
+// DI > 0 (both stage kernels): raw rows DI wide (type TI) mapped to random
+// features while staged, as in the causal kernels.
+template <typename T, int D, int M, int C, bool PHI = true, int DI = 0, typename TI = T>
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_state_kernel(
+    const TI *__restrict__ K, const TI *__restrict__ V, float *__restrict__ ws, int N, int G_, int CPS, int nstates,
+    const float *__restrict__ W = nullptr, int fkind = 0, int fnorm = 0) {
     using Gc = Cfg<T, D, M, C>;
+    using St = ChunkStager<T, D, M, C, PHI, DI, TI>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
+    __shared__ __attribute__((aligned(16))) float sfeat[St::FEAT ? St::FL::nRaw + St::FL::nW : 4];
     Engine<T, D, M, C, PHI> e(smem);
+    St st;
+    st.init(sfeat, W, fkind, fnorm, e.tid);
     const int bh = blockIdx.x / nstates, s = blockIdx.x % nstates;
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
     f32x4 acc[Gc::DT][Gc::MTW];
     Engine<T, D, M, C>::zero_state(acc);
     float z = 0.0f;
-    phase_a(e, K + (size_t)bh * N * D, V + (size_t)bh * N * M, N, c0, c1, acc, z);
+    phase_a(e, K + (size_t)bh * N * St::DQ, V + (size_t)bh * N * M, N, c0, c1, acc, z, st);
     e.state_store(acc, z, ws + ((size_t)bh * (G_ + 1) + s) * Gc::E);
 }
 
-template <typename T, int D, int M, int C, bool CAUSAL, bool PHI = true, typename OT = float>
-__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_output_kernel(const T *__restrict__ Q, const T *__restrict__ K,
-                                                              const T *__restrict__ V, OT *__restrict__ out,
-                                                              const float *__restrict__ ws, int N, int G_, int CPS,
-                                                              float *__restrict__ S_out, float *__restrict__ z_out) {
+template <typename T, int D, int M, int C, bool CAUSAL, bool PHI = true, typename OT = float, int DI = 0,
+          typename TI = T>
+__global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_WG)) void seg_output_kernel(
+    const TI *__restrict__ Q, const TI *__restrict__ K, const TI *__restrict__ V, OT *__restrict__ out,
+    const float *__restrict__ ws, int N, int G_, int CPS, float *__restrict__ S_out, float *__restrict__ z_out,
+    const float *__restrict__ W = nullptr, int fkind = 0, int fnorm = 0) {
     using Gc = Cfg<T, D, M, C>;
+    using St = ChunkStager<T, D, M, C, PHI, DI, TI>;
+    constexpr int DQ = St::DQ;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
+    __shared__ __attribute__((aligned(16))) float sfeat[St::FEAT ? St::FL::nRaw + St::FL::nW : 4];
     Engine<T, D, M, C, PHI> e(smem);
+    St st;
+    st.init(sfeat, W, fkind, fnorm, e.tid);
     const int bh = blockIdx.x / G_, s = blockIdx.x % G_;
     const int n_chunks = (N + C - 1) / C;
     const int c0 = s * CPS, c1 = min(c0 + CPS, n_chunks);
-    const T *Qh = Q + (size_t)bh * N * D;
+    const TI *Qh = Q + (size_t)bh * N * DQ;
     f32x4 S[Gc::DT][Gc::MTW];
     Engine<T, D, M, C>::zero_state(S);
     float z = 0.0f;
@@ -1582,11 +1594,11 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         e.state_add(S, z, ws + ((size_t)bh * (G_ + 1) + G_) * Gc::E);
     }
     if (CAUSAL) e.clear_a();
-    Stage<T, C, D, Cfg<T, D, M, C>::THREADS> stQ;
+    typename St::QStage stQ;
     stQ.load(Qh, c0 * C, N, e.tid);
     const bool fin = CAUSAL && S_out != nullptr && s == G_ - 1;
-    phase_b<T, D, M, C, CAUSAL, PHI, OT>(e, Qh, K + (size_t)bh * N * D, V + (size_t)bh * N * M, out + (size_t)bh * N * M, N,
-                                c0, c1, false, fin, stQ, S, z, false);
+    phase_b<T, D, M, C, CAUSAL, PHI, OT, DI, TI>(e, Qh, K + (size_t)bh * N * DQ, V + (size_t)bh * N * M,
+                                                 out + (size_t)bh * N * M, N, c0, c1, false, fin, stQ, S, z, false, st);
     if (fin) e.state_store(S, z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
 }
 
@@ -1676,6 +1688,35 @@ hipError_t run_fused_features(const void *Q, const void *K, const void *V, const
         hipLaunchKernelGGL((fused_causal_kernel<float, F, M, C, false, float, DI, TI>), dim3(grid), dim3(Gc::THREADS), 0,
                            stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws, BH, N, G_, CPS, S_out, z_out,
                            S_in, z_in, W, fkind, fnorm);
+        return hipGetLastError();
+    }
+}
+
+// Non-causal attention over random features (the stage path: segment states,
+// their scan, outputs), raw rows of type TI mapped in both stage kernels.
+template <int DI, int F, int M, int C>
+constexpr bool stage_features_fit() {
+    using Gc = Cfg<float, F, M, C>;
+    return Gc::fits && Gc::bytes + FeatLds<DI, F, C>::bytes + 64 <= kMaxLds;
+}
+
+template <int DI, int F, int M, int C, typename TI = float>
+hipError_t run_noncausal_features(const void *Q, const void *K, const void *V, const float *W, int fkind, int fnorm,
+                                  float *out, float *ws, int BH, int N, int G_, int CPS, hipStream_t stream) {
+    using Gc = Cfg<float, F, M, C>;
+    if constexpr (!stage_features_fit<DI, F, M, C>()) {
+        return hipErrorInvalidValue;
+    } else {
+        if (BH <= 0 || G_ <= 0) return hipSuccess;
+        hipLaunchKernelGGL((seg_state_kernel<float, F, M, C, false, DI, TI>), dim3((unsigned)(BH * G_)),
+                           dim3(Gc::THREADS), 0, stream, (const TI *)K, (const TI *)V, ws, N, G_, CPS, G_, W, fkind,
+                           fnorm);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess) e = prefill_scan(ws, BH, F, M, G_, G_, nullptr, nullptr, stream);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((seg_output_kernel<float, F, M, C, false, false, float, DI, TI>), dim3((unsigned)(BH * G_)),
+                           dim3(Gc::THREADS), 0, stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws, N, G_,
+                           CPS, nullptr, nullptr, W, fkind, fnorm);
         return hipGetLastError();
     }
 }

@@ -55,8 +55,8 @@ SIGNATURES = {
     "la_feature_map": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp, _i64, _int, _int, _vp]),
     "la_decode_step_features": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _i64, _int,
                                        _int, _vp]),
-    "la_forward_features_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
-    "la_forward_features": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _int,
+    "la_forward_features_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64, _int]),
+    "la_forward_features": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _i64, _int,
                                    _int, _vp, _sz, _vp, _vp, _vp, _vp, _vp]),
 }
 
@@ -474,13 +474,14 @@ def feature_map(X, W, F, kind="prf", normalize=False, out=None, X2=None, out2=No
 
 
 def forward_features(Q, K, V, W, F, kind="prf", normalize=False, out=None, workspace=None, S_out=None,
-                     z_out=None, stream=None, S_in=None, z_in=None):
+                     z_out=None, stream=None, S_in=None, z_in=None, causal=True):
     """Causal attention over random features computed inside the attention kernel:
     Q, K [B,H,N,D], V [B,H,N,M] float32 or bfloat16 (raw rows; the map and the
     attention run in fp32 either way), W as for feature_map ("prf":
     [F, D], "trf": [F/2, D]) -> out [B,H,N,M] float32.  S_out [B,H,F,M] / z_out
     [B,H,F] receive the final state over the features; S_in / z_in (same shapes)
-    continue from a carried state (S_out may be S_in).  Raises LinAttnError
+    continue from a carried state (S_out may be S_in); causal=False: every row
+    attends to all N positions (no states).  Raises LinAttnError
     (LA_ERR_UNSUPPORTED) where the fused kernel does not run the shape; feature_map
     followed by forward_chunked(features=True) computes the same there.
     """
@@ -511,11 +512,12 @@ def forward_features(Q, K, V, W, F, kind="prf", normalize=False, out=None, works
     if S_in is not None:
         _require(S_in, "S_in", (B, H, F, M), torch.float32, dev)
         _require(z_in, "z_in", (B, H, F), torch.float32, dev)
-    need = int(lib().la_forward_features_workspace_bytes(B, H, N, D, M, F))  # 0: the call refuses the shape
+    c = int(bool(causal))
+    need = int(lib().la_forward_features_workspace_bytes(B, H, N, D, M, F, c))  # 0: the call refuses the shape
     if workspace is None and need > 0:
-        workspace = _cached_workspace(need, dev, stream, ("features", B * H, N, D, M, F))
+        workspace = _cached_workspace(need, dev, stream, ("features", B * H, N, D, M, F, c))
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().la_forward_features(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, dt, _ptr(W), F, k,
+    st = lib().la_forward_features(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, c, dt, _ptr(W), F, k,
                                    LA_FEATURE_NORMALIZE if normalize else 0, _ptr(workspace), wbytes,
                                    _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out), _stream(stream, dev))
     _check(st, "la_forward_features")

@@ -341,30 +341,6 @@ enum { LA_FEATURE_NORMALIZE = 1 };
 LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2, int64_t rows, int64_t D,
                           int dtype, const float *W, int64_t F, int kind, int flags, void *stream);
 
-/* Causal attention with the random-feature map fused into one kernel: each
- * chunk's raw q, k rows are mapped to F features (as la_feature_map, kinds
- * LA_FEATURE_PRF and LA_FEATURE_TRF, flag LA_FEATURE_NORMALIZE) while they are
- * staged, then attended to as with la_forward_chunked on LA_F32_FEATURES
- * inputs; the features never reach memory.
- * Q, K [B][H][N][D] (raw rows) and V [B][H][N][M], all of element type dtype
- * (LA_F32 or LA_BF16; bf16 values are widened exactly, the map and the
- * attention run in fp32 as for fp32 rows), W as for la_feature_map, out
- * [B][H][N][M] fp32; S_in [B][H][F][M], z_in [B][H][F] optional (both or
- * neither): a carried state the sequence continues from (as for
- * la_forward_continue; S_out may be S_in for an in-place update, so a call on T
- * new tokens is a T-token decode step); S_out [B][H][F][M], z_out [B][H][F]
- * optional (both or neither): the final state over the features.
- * workspace: la_forward_features_workspace_bytes(...) bytes (at least 256 for
- * a supported shape, 0 for a refused one), initialised and reused as for
- * la_forward_chunked.
- * Plan: chunks of 32, segments sized for 512 resident workgroups; the one-pass
- * kernel runs segments of at most four chunks where its LDS fits, the
- * two-phase kernel (the map applied in both phases) everything else.  D and F
- * outside the instantiated set (D in {16, 32, 64, 128}, F in {16, 32, 64}, M in
- * {16, 32, 64, 128}) give LA_ERR_UNSUPPORTED (and a workspace size of 0);
- * la_feature_map followed by la_forward_chunked (LA_F32_FEATURES) computes the
- * same result in two launches for any supported feature dimension.
- */
 /* One recurrent step (as la_decode_step) on raw rows with the random-feature
  * map formed inside the kernel: q, k [B][H][D] raw rows and v [B][H][M], all of
  * element type dtype (LA_F32 or LA_BF16, widened exactly); W, F, kind (PRF or
@@ -377,10 +353,37 @@ LA_API int la_decode_step_features(float *S, float *z, const void *q, const void
                                    int64_t B, int64_t H, int64_t D, int64_t M, int dtype, const float *W, int64_t F,
                                    int kind, int flags, void *stream);
 
-LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F);
+/* Attention with the random-feature map fused into the attention kernels: each
+ * chunk's raw q, k rows are mapped to F features (as la_feature_map, kinds
+ * LA_FEATURE_PRF and LA_FEATURE_TRF, flag LA_FEATURE_NORMALIZE) while they are
+ * staged, then attended to as with la_forward_chunked on LA_F32_FEATURES
+ * inputs; the features never reach memory.  causal = 1 or 0 as for
+ * la_forward_chunked (0: the stage kernels, the map in both; no states).
+ * Q, K [B][H][N][D] (raw rows) and V [B][H][N][M], all of element type dtype
+ * (LA_F32 or LA_BF16; bf16 values are widened exactly, the map and the
+ * attention run in fp32 as for fp32 rows), W as for la_feature_map, out
+ * [B][H][N][M] fp32; S_in [B][H][F][M], z_in [B][H][F] optional (both or
+ * neither): a carried state the sequence continues from (as for
+ * la_forward_continue; S_out may be S_in for an in-place update, so a call on T
+ * new tokens is a T-token decode step); S_out [B][H][F][M], z_out [B][H][F]
+ * optional (both or neither): the final state over the features (causal = 1
+ * only; with causal = 0 all four must be NULL).
+ * workspace: la_forward_features_workspace_bytes(...) bytes (at least 256 for
+ * a supported shape, 0 for a refused one), initialised and reused as for
+ * la_forward_chunked.
+ * Plan: chunks of 32, segments sized for 512 resident workgroups; causal: the
+ * one-pass kernel runs segments of at most four chunks where its LDS fits, the
+ * two-phase kernel (the map applied in both phases) everything else.  D and F
+ * outside the instantiated set (D in {16, 32, 64, 128}, F in {16, 32, 64}, M in
+ * {16, 32, 64, 128}) give LA_ERR_UNSUPPORTED (and a workspace size of 0);
+ * la_feature_map followed by la_forward_chunked (LA_F32_FEATURES) computes the
+ * same result in two launches for any supported feature dimension.
+ */
+LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F,
+                                                  int causal);
 LA_API int la_forward_features(const void *Q, const void *K, const void *V, float *out, int64_t B, int64_t H,
-                               int64_t N, int64_t D, int64_t M, int dtype, const float *W, int64_t F, int kind,
-                               int flags, void *workspace, size_t workspace_bytes, const float *S_in,
+                               int64_t N, int64_t D, int64_t M, int causal, int dtype, const float *W, int64_t F,
+                               int kind, int flags, void *workspace, size_t workspace_bytes, const float *S_in,
                                const float *z_in, float *S_out, float *z_out, void *stream);
 
 #ifdef __cplusplus

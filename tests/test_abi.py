@@ -295,21 +295,22 @@ def test_forward_features_checks(L):
     lib = L.lib()
     wsb = lib.la_forward_features_workspace_bytes
     f = lib.la_forward_features
-    # Q, K, V, out, B, H, N, D, M, dtype, W, F, kind, flags, ws, ws_bytes, S_in, z_in, S_out, z_out, stream
-    need = wsb(8, 8, 1024, 64, 64, 16)
+    # Q, K, V, out, B, H, N, D, M, causal, dtype, W, F, kind, flags, ws, ws_bytes, S_in, z_in, S_out, z_out, stream
+    need = wsb(8, 8, 1024, 64, 64, 16, 1)
     assert need > 0
-    assert wsb(8, 8, 1024, 48, 64, 16) == 0 and wsb(8, 8, 1024, 64, 64, 24) == 0  # D, F
-    assert wsb(8, 8, 1024, 64, 64, 128) == 0  # F = 128: no fused instantiation
-    assert wsb(1, 1, 1 << 20, 64, 64, 16) > 0  # long segments: the two-phase kernel
-    assert wsb(8, 8, 1024, 64, 64, 64) > 0  # one-pass LDS too small: the two-phase kernel
-    assert wsb(-1, 8, 1024, 64, 64, 16) == 0
+    assert wsb(8, 8, 1024, 48, 64, 16, 1) == 0 and wsb(8, 8, 1024, 64, 64, 24, 1) == 0  # D, F
+    assert wsb(8, 8, 1024, 64, 64, 128, 1) == 0  # F = 128: no fused instantiation
+    assert wsb(1, 1, 1 << 20, 64, 64, 16, 1) > 0  # long segments: the two-phase kernel
+    assert wsb(8, 8, 1024, 64, 64, 64, 1) > 0  # one-pass LDS too small: the two-phase kernel
+    assert wsb(-1, 8, 1024, 64, 64, 16, 1) == 0 and wsb(8, 8, 1024, 64, 64, 16, 2) == 0
+    assert wsb(8, 8, 1024, 64, 64, 16, 0) > 0  # non-causal: the stage path
 
     def call(**kw):
-        a = dict(Q=FAKE, K=FAKE, V=FAKE, out=FAKE, B=8, H=8, N=1024, D=64, M=64, dtype=0, W=FAKE, F=16, kind=1,
-                 flags=0, ws=FAKE, ws_bytes=need, Si=None, zi=None, S=None, z=None)
+        a = dict(Q=FAKE, K=FAKE, V=FAKE, out=FAKE, B=8, H=8, N=1024, D=64, M=64, causal=1, dtype=0, W=FAKE, F=16,
+                 kind=1, flags=0, ws=FAKE, ws_bytes=need, Si=None, zi=None, S=None, z=None)
         a.update(kw)
-        return f(a["Q"], a["K"], a["V"], a["out"], a["B"], a["H"], a["N"], a["D"], a["M"], a["dtype"], a["W"],
-                 a["F"], a["kind"], a["flags"], a["ws"], a["ws_bytes"], a["Si"], a["zi"], a["S"], a["z"], None)
+        return f(a["Q"], a["K"], a["V"], a["out"], a["B"], a["H"], a["N"], a["D"], a["M"], a["causal"], a["dtype"],
+                 a["W"], a["F"], a["kind"], a["flags"], a["ws"], a["ws_bytes"], a["Si"], a["zi"], a["S"], a["z"], None)
 
     assert call(dtype=2) == L.LA_ERR_INVALID_ARG  # raw rows: LA_F32 or LA_BF16 only
     assert call(dtype=1, ws_bytes=need - 1) == L.LA_ERR_WORKSPACE  # bf16 rows: the same plan
@@ -320,6 +321,9 @@ def test_forward_features_checks(L):
     assert call(F=128) == L.LA_ERR_UNSUPPORTED
     assert call(N=-1) == L.LA_ERR_INVALID_ARG
     assert call(S=FAKE) == L.LA_ERR_INVALID_ARG  # S_out without z_out
+    assert call(causal=2) == L.LA_ERR_INVALID_ARG
+    assert call(causal=0, S=FAKE, z=FAKE) == L.LA_ERR_INVALID_ARG  # states only with causal = 1
+    assert call(causal=0, ws_bytes=0) == L.LA_ERR_WORKSPACE
     assert call(Si=FAKE) == L.LA_ERR_INVALID_ARG  # S_in without z_in
     assert call(Si=FAKE + 4, zi=FAKE) == L.LA_ERR_INVALID_ARG  # alignment
     assert call(W=None) == L.LA_ERR_INVALID_ARG

@@ -34,8 +34,8 @@ def ea():
     return ea
 
 
-def supported(ea, B, H, N, D, M, F):
-    return int(ea.linattn.lib().la_forward_features_workspace_bytes(B, H, N, D, M, F)) > 0
+def supported(ea, B, H, N, D, M, F, causal=True):
+    return int(ea.linattn.lib().la_forward_features_workspace_bytes(B, H, N, D, M, F, int(causal))) > 0
 
 
 def case(ea, B, H, N, D, M, F, kind, seed, normalize=False, draw="gaussian", scale=None):
@@ -406,3 +406,26 @@ def test_fused_features_multi_token_decode(ea):
     assert rowwise_rel(multi.cpu().numpy(), ref) <= TOL["f32"]
     assert rowwise_rel(torch.stack(single, dim=2).cpu().numpy(), multi.cpu().numpy()) <= 1e-5
     assert whole_rel(S.cpu().numpy(), S1.cpu().numpy()) <= 1e-5
+
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,normalize", [("prf", False), ("prf", True), ("trf", False)])
+@pytest.mark.parametrize("B,H,N,D,F,M", [(2, 3, 300, 64, 16, 64), (1, 2, 5000, 32, 32, 128), (2, 2, 33, 128, 64, 16)])
+def test_fused_features_noncausal(ea, dtype, kind, normalize, B, H, N, D, F, M):
+    """Non-causal attention with the map fused into both stage kernels: against
+    the oracle (every row attends to all N positions) and the two-launch path."""
+    assert supported(ea, B, H, N, D, M, F, causal=False)
+    if dtype == "f32":
+        dev, host = case(ea, B, H, N, D, M, F, kind, 110 + D, normalize)
+    else:
+        dev, host = bf16_case(ea, B, H, N, D, M, F, kind, 110 + D, normalize)
+    Qd, Kd, Vd, Wd = dev
+    out = ea.forward_features(Qd, Kd, Vd, Wd, F, kind, normalize, causal=False)
+    fq, fk = ea.feature_map(Qd, Wd, F, kind, normalize, X2=Kd)
+    two = ea.forward_chunked(fq, fk, Vd.float().contiguous(), causal=False, features=True)
+    torch.cuda.synchronize()
+    ref = oracle_out(host, F, kind, normalize, causal=False)
+    ref = ref[0] if isinstance(ref, tuple) else ref
+    assert rowwise_rel(out.cpu().numpy(), ref) <= TOL["f32"]
+    assert rowwise_rel(out.cpu().numpy(), two.cpu().numpy()) <= 1e-5
