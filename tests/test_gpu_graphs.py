@@ -130,3 +130,51 @@ def test_softmax_scan_replays(ea):
         got = out.cpu().numpy()
         want = oracle.softmax_scan(q, K, V)[0]
         assert rowwise_rel(got, want) <= TOL["f32"], rep
+
+
+@pytest.mark.parametrize("N", [1024, 65536])
+def test_forward_features_replays(ea, N):
+    """A captured la_forward_features call (one-pass plan at N = 1024, two-phase at
+    N = 65536; look-back and epoch in both) and a captured la_decode_step_features
+    step, replayed with new raw rows written eagerly between the replays."""
+    B, H, D, M, F = (8, 8, 64, 64, 16) if N == 1024 else (1, 2, 64, 64, 16)
+    W = torch.from_numpy(ea.draw_projection(F, D, "orthogonal", 4)).to(DEV)
+    Qd = torch.zeros((B, H, N, D), device=DEV)
+    Kd = torch.zeros((B, H, N, D), device=DEV)
+    Vd = torch.zeros((B, H, N, M), device=DEV)
+    out = torch.empty((B, H, N, M), device=DEV)
+    need = int(ea.linattn.lib().la_forward_features_workspace_bytes(B, H, N, D, M, F, 1))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    S = torch.empty((B, H, F, M), device=DEV)
+    z = torch.empty((B, H, F), device=DEV)
+    ea.forward_features(Qd, Kd, Vd, W, F, "prf", out=out, workspace=ws, S_out=S, z_out=z)  # warm-up
+    qd = torch.zeros((B, H, D), device=DEV)
+    kd = torch.zeros((B, H, D), device=DEV)
+    vd = torch.zeros((B, H, M), device=DEV)
+    y = torch.empty((B, H, M), device=DEV)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ea.forward_features(Qd, Kd, Vd, W, F, "prf", out=out, workspace=ws, S_out=S, z_out=z)
+        ea.decode_step_features(S, z, qd, kd, vd, W, F, "prf", out=y)
+    torch.cuda.synchronize()
+    s = 64 ** -0.25
+    for rep in range(3):
+        Qd.copy_(synthetic.draw_torch(120 + rep, synthetic.TID_Q, (B, H, N, D), s, "f32", DEV))
+        Kd.copy_(synthetic.draw_torch(120 + rep, synthetic.TID_K, (B, H, N, D), s, "f32", DEV))
+        Vd.copy_(synthetic.draw_torch(120 + rep, synthetic.TID_V, (B, H, N, M), 1.0, "f32", DEV))
+        qd.copy_(synthetic.draw_torch(130 + rep, synthetic.TID_DQ, (B, H, D), s, "f32", DEV))
+        kd.copy_(synthetic.draw_torch(130 + rep, synthetic.TID_DK, (B, H, D), s, "f32", DEV))
+        vd.copy_(synthetic.draw_torch(130 + rep, synthetic.TID_DV, (B, H, M), 1.0, "f32", DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got, got_y, got_S = out.clone(), y.clone(), S.clone()
+        S2 = torch.empty_like(S)
+        z2 = torch.empty_like(z)
+        want = ea.forward_features(Qd, Kd, Vd, W, F, "prf", S_out=S2, z_out=z2)
+        want_y = ea.decode_step_features(S2, z2, qd, kd, vd, W, F, "prf")
+        torch.cuda.synchronize()
+        assert rowwise_rel(got.cpu().numpy(), want.cpu().numpy()) <= 1e-5, rep
+        assert rowwise_rel(got_y.cpu().numpy(), want_y.cpu().numpy()) <= 1e-5, rep
+        assert torch.allclose(got_S, S2, rtol=1e-5, atol=1e-6), rep
