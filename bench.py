@@ -246,6 +246,31 @@ def bench_decode_hbm(dev, B=4096, H=8, D=64, M=64, T=32, reps=3):
     return dict(us_per_step=us, bytes_per_step=nb, GBs=nb / (us * 1e-6) / 1e9, tokens_per_s=B / (us * 1e-6))
 
 
+def bench_hbm_copy(dev, nbytes=1 << 30, reps=5):
+    """Attainable HBM rate of a plain device-to-device copy (torch's copy kernel) of a buffer four
+    times the last-level cache: read plus written bytes per second, best of several copies."""
+    import torch
+
+    n = nbytes // 4
+    a = torch.ones(n, device=dev)
+    b = torch.empty(n, device=dev)
+    b.copy_(a)
+    best = None
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del a, b
+    torch.cuda.empty_cache()
+    moved = 2 * n * 4
+    return dict(bytes=moved, us=best * 1e3, GBs=moved / (best * 1e-3) / 1e9)
+
+
 def backward_bytes(cfg) -> int:
     """Algorithmic bytes of one backward call: read q, k, v, out, dout; write dq, dk, dv."""
     s_in = 4 if cfg["dtype"] == "f32" else 2
@@ -625,6 +650,14 @@ def main():
             "tokens_per_s": round(dh["tokens_per_s"], 1), "us_per_step": round(dh["us_per_step"], 2),
             "bytes_per_step": dh["bytes_per_step"], "GBs": round(dh["GBs"], 1),
             "frac_hbm_peak": round(dh["GBs"] / HBM_PEAK_GBS, 4)}
+        log("plain device copy ...")
+        cp = bench_hbm_copy(dev)
+        log(f"copy: {cp}")
+        line["hbm_copy"] = {
+            "workload": "plain device-to-device copy of 1 GiB (torch copy kernel): attainable HBM rate",
+            "bytes_moved": cp["bytes"], "us": round(cp["us"], 1), "GBs": round(cp["GBs"], 1),
+            "frac_hbm_peak": round(cp["GBs"] / HBM_PEAK_GBS, 4)}
+        line["decode_hbm"]["frac_of_copy_rate"] = round(dh["GBs"] / cp["GBs"], 4)
         others = {}
         for name, outdt in (("prefill_bf16_b4h8_n3072_d64", "fp32"), ("prefill_bf16_b1h16_n65536_d128", "fp32"),
                             ("prefill_bf16_b4h8_n3072_d64", "bf16"), ("prefill_bf16_b1h16_n65536_d128", "bf16")):
