@@ -246,29 +246,44 @@ def bench_decode_hbm(dev, B=4096, H=8, D=64, M=64, T=32, reps=3):
     return dict(us_per_step=us, bytes_per_step=nb, GBs=nb / (us * 1e-6) / 1e9, tokens_per_s=B / (us * 1e-6))
 
 
-def bench_hbm_copy(dev, nbytes=1 << 30, reps=5):
-    """Attainable HBM rate of a plain device-to-device copy (torch's copy kernel) of a buffer four
-    times the last-level cache: read plus written bytes per second, best of several copies."""
+def bench_probes(dev, nbytes=1 << 30, reps=5):
+    """Attainable peaks: a plain device-to-device copy of a buffer four times the last-level
+    cache (the library's copy probe, and torch's copy kernel beside it; read plus written bytes
+    per second), and the library's fp32 and bf16 MFMA loops (8 independent chains per
+    wavefront, 2 wavefronts per SIMD).  Best of several launches each."""
     import torch
+    import efficient_transformer_amd as ea
+
+    def best_ms(fn):
+        fn()
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
 
     n = nbytes // 4
     a = torch.ones(n, device=dev)
     b = torch.empty(n, device=dev)
-    b.copy_(a)
-    best = None
-    for _ in range(reps):
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
-        best = ms if best is None else min(best, ms)
+    moved = 2 * n * 4
+    ms_probe = best_ms(lambda: ea.probe_copy(b, a))
+    ms_torch = best_ms(lambda: b.copy_(a))
     del a, b
     torch.cuda.empty_cache()
-    moved = 2 * n * 4
-    return dict(bytes=moved, us=best * 1e3, GBs=moved / (best * 1e-3) / 1e9)
+    blocks = 256 * 2  # two 4-wavefront workgroups per CU: 2 wavefronts per SIMD
+    out = torch.empty(blocks * 256, device=dev)
+    mfma = {}
+    for kind, iters in (("f32", 4096), ("bf16", 4096)):
+        flops = ea.probe_mfma(kind, blocks, iters, out=out)[1]
+        mfma[kind] = flops / (best_ms(lambda: ea.probe_mfma(kind, blocks, iters, out=out)) * 1e-3) / 1e12
+    return dict(bytes=moved, us=ms_probe * 1e3, GBs=moved / (ms_probe * 1e-3) / 1e9,
+                torch_GBs=moved / (ms_torch * 1e-3) / 1e9, mfma_f32_TFs=mfma["f32"], mfma_bf16_TFs=mfma["bf16"])
 
 
 def backward_bytes(cfg) -> int:
@@ -650,13 +665,18 @@ def main():
             "tokens_per_s": round(dh["tokens_per_s"], 1), "us_per_step": round(dh["us_per_step"], 2),
             "bytes_per_step": dh["bytes_per_step"], "GBs": round(dh["GBs"], 1),
             "frac_hbm_peak": round(dh["GBs"] / HBM_PEAK_GBS, 4)}
-        log("plain device copy ...")
-        cp = bench_hbm_copy(dev)
-        log(f"copy: {cp}")
+        log("peak probes ...")
+        cp = bench_probes(dev)
+        log(f"probes: {cp}")
         line["hbm_copy"] = {
-            "workload": "plain device-to-device copy of 1 GiB (torch copy kernel): attainable HBM rate",
+            "workload": "plain device-to-device copy of 1 GiB (the library's copy probe): attainable HBM rate",
             "bytes_moved": cp["bytes"], "us": round(cp["us"], 1), "GBs": round(cp["GBs"], 1),
-            "frac_hbm_peak": round(cp["GBs"] / HBM_PEAK_GBS, 4)}
+            "frac_hbm_peak": round(cp["GBs"] / HBM_PEAK_GBS, 4), "torch_copy_GBs": round(cp["torch_GBs"], 1)}
+        line["mfma_probe"] = {
+            "workload": "dense MFMA loops, 8 independent chains per wavefront, 512 workgroups of 4 wavefronts",
+            "f32_TFs": round(cp["mfma_f32_TFs"], 1), "f32_frac_peak": round(cp["mfma_f32_TFs"] / FP32_MFMA_PEAK_TFS, 4),
+            "bf16_TFs": round(cp["mfma_bf16_TFs"], 1),
+            "bf16_frac_peak": round(cp["mfma_bf16_TFs"] / BF16_MFMA_PEAK_TFS, 4)}
         line["decode_hbm"]["frac_of_copy_rate"] = round(dh["GBs"] / cp["GBs"], 4)
         others = {}
         for name, outdt in (("prefill_bf16_b4h8_n3072_d64", "fp32"), ("prefill_bf16_b1h16_n65536_d128", "fp32"),

@@ -18,6 +18,8 @@ from .linattn import (  # noqa: F401
     forward_fused,
     forward_onepass,
     forward_plan,
+    probe_copy,
+    probe_mfma,
     fused_workspace_bytes,
     lib_path,
     segment_outputs,

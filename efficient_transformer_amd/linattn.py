@@ -58,6 +58,8 @@ SIGNATURES = {
     "la_forward_features_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64, _int]),
     "la_forward_features": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _i64, _int,
                                    _int, _vp, _sz, _vp, _vp, _vp, _vp, _vp]),
+    "la_probe_copy": (_int, [_vp, _vp, _sz, _vp]),
+    "la_probe_mfma": (_int, [_vp, _int, _i64, _int, ctypes.c_float, _vp]),
 }
 
 
@@ -553,3 +555,26 @@ def decode_step_features(S, z, q, k, v, W, F, kind="prf", normalize=False, out=N
                                        _stream(stream, dev))
     _check(st, "la_decode_step_features")
     return out
+
+
+def probe_copy(dst, src, stream=None):
+    """Plain device copy src -> dst (same byte size) by the library's copy probe."""
+    if dst.numel() * dst.element_size() != src.numel() * src.element_size():
+        raise ValueError("probe_copy: dst and src differ in size")
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("probe_copy: tensors must be contiguous")
+    _check(lib().la_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(stream, src.device)),
+           "la_probe_copy")
+    return dst
+
+
+def probe_mfma(kind: str, blocks: int, iters: int, x: float = 0.5, out=None, stream=None, device=None):
+    """MFMA throughput probe ("f32" or "bf16"); returns (out, flops of the launch)."""
+    import torch
+    dt = {"f32": LA_F32, "bf16": LA_BF16}[kind]
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=device or "cuda")
+    if out.dtype != torch.float32 or out.numel() < blocks * 256 or not out.is_contiguous():
+        raise ValueError("probe_mfma: out must be contiguous float32 with blocks * 256 elements")
+    _check(lib().la_probe_mfma(_ptr(out), dt, blocks, iters, x, _stream(stream, out.device)), "la_probe_mfma")
+    return out, blocks * 4 * iters * 8 * (2048 if kind == "f32" else 16384)

@@ -386,6 +386,28 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
                                int kind, int flags, void *workspace, size_t workspace_bytes, const float *S_in,
                                const float *z_in, float *S_out, float *z_out, void *stream);
 
+/*
+ * Peak probes (measurement support, not a step of the method): the attainable
+ * rates that the kernels' rooflines are set against, beside the nominal peaks.
+ *
+ * la_probe_copy: copies `bytes` bytes from src to dst (device memory, both
+ * 16-byte aligned, not overlapping; bytes a multiple of 16, else
+ * LA_ERR_INVALID_ARG; 0 is a no-op).  Result bit-exact.  Read + written bytes
+ * over the launch's time give the attainable HBM rate.
+ *
+ * la_probe_mfma: `blocks` workgroups of 256 threads (4 wavefronts); every
+ * wavefront runs `iters` rounds of 8 independent MFMA chains: fp32 16x16x4
+ * (dtype LA_F32, 2048 flops each) or bf16 16x16x32 (LA_BF16, 16384 flops each),
+ * every operand element x (rounded to bf16 for LA_BF16).  Flops per launch:
+ * blocks * 4 * iters * 8 * (2048 or 16384).  out [blocks * 256] fp32 (device):
+ * lane i writes the sum of its 32 accumulator values, 32 * iters * K * x^2 with
+ * K = 4 (fp32) or 32 (bf16), exact while that and iters * K * x^2 are integers
+ * below 2^24.  blocks in [0, 2^20] and iters >= 0, else LA_ERR_INVALID_ARG;
+ * blocks = 0 is a no-op.
+ */
+LA_API int la_probe_copy(void *dst, const void *src, size_t bytes, void *stream);
+LA_API int la_probe_mfma(float *out, int dtype, int64_t blocks, int iters, float x, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -351,3 +351,18 @@ def test_decode_step_features_checks(L):
     assert call(11, None) == L.LA_ERR_INVALID_ARG  # W
     assert call(4, FAKE + 4) == L.LA_ERR_INVALID_ARG  # alignment
     assert call(6, 0) == L.LA_OK  # no heads
+
+
+def test_probe_checks(L):
+    lib = L.lib()
+    assert lib.la_probe_copy(None, None, 0, None) == L.LA_OK
+    assert lib.la_probe_copy(None, None, 20, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_copy(None, None, 32, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_copy(16, 17, 32, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_mfma(None, L.LA_F32, 0, 10, 0.5, None) == L.LA_OK
+    assert lib.la_probe_mfma(None, L.LA_F32, 4, 10, 0.5, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_mfma(None, 7, 4, 10, 0.5, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_mfma(None, L.LA_BF16, -1, 10, 0.5, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_mfma(None, L.LA_BF16, 1 << 21, 10, 0.5, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_mfma(None, L.LA_BF16, 4, -1, 0.5, None) == L.LA_ERR_INVALID_ARG
+

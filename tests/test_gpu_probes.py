@@ -1,0 +1,44 @@
+"""The peak probes through the C ABI: the copy is bit-exact and every MFMA chain
+reaches the value its closed form gives (sum of 32 accumulator values per lane,
+each iters * K * x^2, with K = 4 for fp32 16x16x4 and 32 for bf16 16x16x32)."""
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ea():
+    import efficient_transformer_amd as ea
+    return ea
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1000003, 1 << 26])
+def test_copy_is_exact(ea, nbytes):
+    print(f"probe_copy {nbytes}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(nbytes % 9973)
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g).cuda()
+    dst = torch.full_like(src, 7)
+    ea.probe_copy(dst, src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+
+
+def test_copy_leaves_the_rest(ea):
+    src = torch.arange(64, dtype=torch.int32, device="cuda")
+    dst = torch.full((80,), -1, dtype=torch.int32, device="cuda")
+    ea.probe_copy(dst[:64], src)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:64], src) and bool((dst[64:] == -1).all())
+
+
+@pytest.mark.parametrize("kind,K", [("f32", 4), ("bf16", 32)])
+@pytest.mark.parametrize("blocks,iters,x", [(1, 1, 0.5), (3, 17, 0.5), (512, 64, 0.25), (7, 0, 0.5)])
+def test_mfma_closed_form(ea, kind, K, blocks, iters, x):
+    print(f"probe_mfma {kind} blocks={blocks} iters={iters} x={x}", flush=True)
+    out, flops = ea.probe_mfma(kind, blocks, iters, x)
+    torch.cuda.synchronize()
+    want = 32.0 * iters * K * x * x
+    assert flops == blocks * 4 * iters * 8 * (2048 if kind == "f32" else 16384)
+    assert out.shape == (blocks * 256,)
+    assert bool((out == want).all()), (out.min().item(), out.max().item(), want)
