@@ -250,7 +250,7 @@ def bench_probes(dev, nbytes=1 << 30, reps=5):
     """Attainable peaks: a plain device-to-device copy of a buffer four times the last-level
     cache (the library's copy probe, and torch's copy kernel beside it; read plus written bytes
     per second), and the library's fp32 and bf16 MFMA loops (8 independent chains per
-    wavefront, 2 wavefronts per SIMD).  Best of several launches each."""
+    wavefront, 8 wavefronts per SIMD).  Best of several launches each."""
     import torch
     import efficient_transformer_amd as ea
 
@@ -276,10 +276,10 @@ def bench_probes(dev, nbytes=1 << 30, reps=5):
     ms_torch = best_ms(lambda: b.copy_(a))
     del a, b
     torch.cuda.empty_cache()
-    blocks = 256 * 2  # two 4-wavefront workgroups per CU: 2 wavefronts per SIMD
+    blocks = 256 * 8  # eight 4-wavefront workgroups per CU: 8 wavefronts per SIMD
     out = torch.empty(blocks * 256, device=dev)
     mfma = {}
-    for kind, iters in (("f32", 4096), ("bf16", 4096)):
+    for kind, iters in (("f32", 2048), ("bf16", 2048)):
         flops = ea.probe_mfma(kind, blocks, iters, out=out)[1]
         mfma[kind] = flops / (best_ms(lambda: ea.probe_mfma(kind, blocks, iters, out=out)) * 1e-3) / 1e12
     return dict(bytes=moved, us=ms_probe * 1e3, GBs=moved / (ms_probe * 1e-3) / 1e9,
@@ -673,7 +673,7 @@ def main():
             "bytes_moved": cp["bytes"], "us": round(cp["us"], 1), "GBs": round(cp["GBs"], 1),
             "frac_hbm_peak": round(cp["GBs"] / HBM_PEAK_GBS, 4), "torch_copy_GBs": round(cp["torch_GBs"], 1)}
         line["mfma_probe"] = {
-            "workload": "dense MFMA loops, 8 independent chains per wavefront, 512 workgroups of 4 wavefronts",
+            "workload": "dense MFMA loops, 8 independent chains per wavefront, 2048 workgroups of 4 wavefronts",
             "f32_TFs": round(cp["mfma_f32_TFs"], 1), "f32_frac_peak": round(cp["mfma_f32_TFs"] / FP32_MFMA_PEAK_TFS, 4),
             "bf16_TFs": round(cp["mfma_bf16_TFs"], 1),
             "bf16_frac_peak": round(cp["mfma_bf16_TFs"] / BF16_MFMA_PEAK_TFS, 4)}
