@@ -30,4 +30,5 @@ from .linattn import (  # noqa: F401
     version,
     workspace_bytes,
     workspace_init,
+    workspace_status,
 )

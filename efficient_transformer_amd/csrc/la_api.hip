@@ -18,7 +18,13 @@ bool decode_steps_chunked(int64_t T, int64_t D, int64_t M) {
     return (T >= 12 && D * M >= 4096) || (T >= 16 && D * M >= 2048) || T >= 32;
 }
 
+// widths with specialised kernels
 bool dim_ok(int64_t x) { return x == 16 || x == 32 || x == 64 || x == 128; }
+// widths the prefill and decode entry points also take: multiples of 16 up to
+// 128; those without a kernel of their own run on tiles of the next width up
+bool dim_padded_ok(int64_t x) { return x >= 16 && x <= 128 && x % 16 == 0; }
+int64_t dim_up(int64_t x) { return x <= 16 ? 16 : x <= 32 ? 32 : x <= 64 ? 64 : 128; }
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Plan {
@@ -28,14 +34,21 @@ struct Plan {
     int nstates = 0;  // segment states the causal/non-causal path computes
     bool onepass = false;  // causal: one-pass kernel (segments of at most 4 chunks)
     size_t ws_bytes = 0;
+    // D or M without a kernel of its own: the kernels run at widths Dk, Mk on
+    // padded copies held in the workspace after the kernels' own inner_ws bytes
+    bool padded = false;
+    int64_t Dk = 0, Mk = 0;
+    size_t inner_ws = 0, oQ = 0, oK = 0, oV = 0, oO = 0, oS = 0, oZ = 0;
 };
 
 // Validate the shape arguments shared by the prefill entry points.
-int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype) {
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype, bool allow_pad = false) {
     if (B < 0 || H < 0 || N < 0 || D <= 0 || M <= 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES && dtype != (LA_BF16 | LA_OUT_BF16))
         return LA_ERR_INVALID_ARG;
-    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (!dim_ok(D) || !dim_ok(M)) {
+        if (!allow_pad || !dim_padded_ok(D) || !dim_padded_ok(M)) return LA_ERR_UNSUPPORTED;
+    }
     // index arithmetic uses int for counts and size_t for element offsets
     if (N > INT_MAX || B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
     if (B > 0 && H > 0 && N > 0) {
@@ -51,9 +64,41 @@ size_t state_ws_bytes(int64_t BH, int64_t D, int64_t M, int G) {
 
 // The planner: chunk length, number of segments and workspace.
 int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype, int chunk_req,
-              Plan *plan, int64_t target_wg_override = 0) {
-    int st = check_shape(B, H, N, D, M, dtype);
+              Plan *plan, int64_t target_wg_override = 0, bool allow_pad = false) {
+    int st = check_shape(B, H, N, D, M, dtype, allow_pad);
     if (st != LA_OK) return st;
+    if (!dim_ok(D) || !dim_ok(M)) {
+        // the kernels' plan at the padded widths, then room for the padded copies
+        const int64_t Dk = dim_up(D), Mk = dim_up(M);
+        st = make_plan(B, H, N, Dk, Mk, causal, dtype, chunk_req, plan, target_wg_override, false);
+        if (st != LA_OK) return st;
+        plan->padded = true;
+        plan->Dk = Dk;
+        plan->Mk = Mk;
+        const int64_t BH = B * H;
+        if (BH == 0 || N == 0) return LA_OK;
+        if (BH * N > INT64_MAX / 1024) return LA_ERR_UNSUPPORTED;
+        const size_t s_in = (dtype & ~LA_OUT_BF16) == LA_BF16 ? 2 : 4, s_out = (dtype & LA_OUT_BF16) ? 2 : 4;
+        const size_t rows = (size_t)BH * (size_t)N;
+        plan->inner_ws = plan->ws_bytes;
+        // at least one 256-byte block in front: its header words stay zero when the
+        // kernels need no workspace, so la_workspace_status reads a clean error word
+        size_t off = round256(plan->ws_bytes > 256 ? plan->ws_bytes : 256);
+        plan->oQ = off;
+        off += round256(rows * Dk * s_in);
+        plan->oK = off;
+        off += round256(rows * Dk * s_in);
+        plan->oV = off;
+        off += round256(rows * Mk * s_in);
+        plan->oO = off;
+        off += round256(rows * Mk * s_out);
+        plan->oS = off;
+        off += round256((size_t)BH * Dk * Mk * 4);
+        plan->oZ = off;
+        off += round256((size_t)BH * Dk * 4);
+        plan->ws_bytes = off;
+        return LA_OK;
+    }
     if (causal != 0 && causal != 1) return LA_ERR_INVALID_ARG;
     int C = 0;
     if (chunk_req == 0) {
@@ -112,6 +157,54 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
 
+// A padded plan (Plan::padded): copy Q and K into rows Dk wide (extra columns
+// -inf, which phi maps to exactly 0; 0 for inputs that already hold features),
+// V into rows Mk wide (extra columns 0) and a carried state into [Dk][Mk] (zeros
+// outside), run the kernels of the plan on those, then copy the first M columns
+// of every output row and the [D][M] corner of the final state back.
+hipError_t run_padded(const Plan &p, const void *Q, const void *K, const void *V, void *out, int64_t BH, int64_t N,
+                      int64_t D, int64_t M, int causal, int dtype, void *workspace, const float *S_in,
+                      const float *z_in, float *S_out, float *z_out, hipStream_t s) {
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    const long Dk = (long)p.Dk, Mk = (long)p.Mk;
+    const int base = dtype & ~LA_OUT_BF16;
+    const long s_in = base == LA_BF16 ? 2 : 4, s_out = (dtype & LA_OUT_BF16) ? 2 : 4;
+    const unsigned fill = base == LA_F32_FEATURES ? 0u : base == LA_BF16 ? 0xFF80FF80u : 0xFF800000u;
+    void *Qp = ws + p.oQ, *Kp = ws + p.oK, *Vp = ws + p.oV, *Op = ws + p.oO;
+    float *Sp = reinterpret_cast<float *>(ws + p.oS), *zp = reinterpret_cast<float *>(ws + p.oZ);
+    hipError_t e = la::pad_copy(Q, Qp, BH, N, D * s_in, N, Dk * s_in, fill, s);
+    if (e == hipSuccess) e = la::pad_copy(K, Kp, BH, N, D * s_in, N, Dk * s_in, fill, s);
+    if (e == hipSuccess) e = la::pad_copy(V, Vp, BH, N, M * s_in, N, Mk * s_in, 0u, s);
+    if (e == hipSuccess && S_in) {
+        e = la::pad_copy(S_in, Sp, BH, D, M * 4, Dk, Mk * 4, 0u, s);
+        if (e == hipSuccess) e = la::pad_copy(z_in, zp, BH, 1, D * 4, 1, Dk * 4, 0u, s);
+    }
+    float *So = S_out ? Sp : nullptr, *zo = S_out ? zp : nullptr;
+    const float *Si = S_in ? Sp : nullptr, *zi = S_in ? zp : nullptr;
+    void *iw = p.inner_ws > 0 ? workspace : nullptr;
+    const int Di = (int)Dk, Mi = (int)Mk, C = p.chunk, G = p.segments, cps = p.chunks_per_segment;
+    const int bh = (int)BH, n = (int)N;
+    if (e == hipSuccess) {
+        if (causal && p.onepass) {
+            e = la::prefill_onepass(dtype, Di, Mi, C, Qp, Kp, Vp, Op, iw, bh, n, G, cps, So, zo, Si, zi, s);
+        } else if (causal) {
+            e = la::prefill_fused(dtype, Di, Mi, C, Qp, Kp, Vp, Op, iw, bh, n, G, cps, So, zo, Si, zi, s);
+        } else {
+            float *sw = static_cast<float *>(iw);
+            e = la::prefill_states(dtype, Di, Mi, C, Kp, Vp, sw, bh, n, G, cps, G, s);
+            if (e == hipSuccess) e = la::prefill_scan(sw, bh, Di, Mi, G, G, So, zo, s);
+            if (e == hipSuccess)
+                e = la::prefill_outputs(dtype, Di, Mi, C, Qp, Kp, Vp, Op, sw, bh, n, G, cps, 0, nullptr, nullptr, s);
+        }
+    }
+    if (e == hipSuccess) e = la::unpad_copy(Op, out, BH, N, M * s_out, N, Mk * s_out, s);
+    if (e == hipSuccess && S_out) {
+        e = la::unpad_copy(Sp, S_out, BH, D, M * 4, Dk, Mk * 4, s);
+        if (e == hipSuccess) e = la::unpad_copy(zp, z_out, BH, 1, D * 4, 1, Dk * 4, s);
+    }
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,6 +216,8 @@ LA_API const char *la_status_str(int status) {
         case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: unsupported shape, chunk or plan";
         case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
         case LA_ERR_HIP: return "LA_ERR_HIP: HIP runtime error at launch";
+        case LA_ERR_GAVE_UP:
+            return "LA_ERR_GAVE_UP: a wait for earlier segments gave up; the calls' outputs hold NaN rows";
         default: return "unknown status";
     }
 }
@@ -132,7 +227,7 @@ LA_API int la_version(void) { return kVersion; }
 LA_API int la_forward_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
                            int chunk_req, int *chunk_out, int *segments_out, size_t *workspace_bytes_out) {
     Plan p;
-    const int st = make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p);
+    const int st = make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p, 0, true);
     if (st != LA_OK) return st;
     if (chunk_out) *chunk_out = p.chunk;
     if (segments_out) *segments_out = p.segments;
@@ -143,14 +238,14 @@ LA_API int la_forward_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M
 LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
                                          int dtype, int chunk_req) {
     Plan p;
-    return make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p) == LA_OK ? p.ws_bytes : 0;
+    return make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p, 0, true) == LA_OK ? p.ws_bytes : 0;
 }
 
 LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, void *out, int64_t B, int64_t H,
                               int64_t N, int64_t D, int64_t M, int causal, int dtype, int chunk_req,
                               void *workspace, size_t workspace_bytes, float *S_out, float *z_out, void *stream) {
     Plan p;
-    int st = make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p);
+    int st = make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p, 0, true);
     if (st != LA_OK) return st;
     if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
     if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
@@ -169,6 +264,9 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, void 
     if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
     const int dt = dtype, Di = (int)D, Mi = (int)M, C = p.chunk, G = p.segments, cps = p.chunks_per_segment;
     (void)hipGetLastError();  // clear a stale error so that the checks below report this call's launches
+    if (p.padded)
+        return hip_status(run_padded(p, Q, K, V, out, BH, N, D, M, causal, dtype, workspace, nullptr, nullptr, S_out,
+                                     z_out, s));
     hipError_t e = hipSuccess;
     if (causal && p.onepass) {
         e = la::prefill_onepass(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps, S_out, z_out,
@@ -191,7 +289,7 @@ LA_API int la_forward_continue(const void *Q, const void *K, const void *V, void
                                const float *z_in, void *workspace, size_t workspace_bytes, float *S_out,
                                float *z_out, void *stream) {
     Plan p;
-    int st = make_plan(B, H, N, D, M, 1, dtype, chunk_req, &p);
+    int st = make_plan(B, H, N, D, M, 1, dtype, chunk_req, &p, 0, true);
     if (st != LA_OK) return st;
     if ((S_in == nullptr) != (z_in == nullptr)) return LA_ERR_INVALID_ARG;
     if (S_in && (!aligned16(S_in) || !aligned16(z_in))) return LA_ERR_INVALID_ARG;
@@ -220,12 +318,26 @@ LA_API int la_forward_continue(const void *Q, const void *K, const void *V, void
     if (p.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < p.ws_bytes)) return LA_ERR_WORKSPACE;
     if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
+    if (p.padded)
+        return hip_status(run_padded(p, Q, K, V, out, BH, N, D, M, 1, dtype, workspace, S_in, z_in, S_out, z_out, s));
     const int dt = dtype, Di = (int)D, Mi = (int)M, C = p.chunk, G = p.segments, cps = p.chunks_per_segment;
     hipError_t e = p.onepass ? la::prefill_onepass(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps,
                                                    S_out, z_out, S_in, z_in, s)
                              : la::prefill_fused(dt, Di, Mi, C, Q, K, V, out, workspace, (int)BH, (int)N, G, cps,
                                                  S_out, z_out, S_in, z_in, s);
     return hip_status(e);
+}
+
+LA_API int la_workspace_status(const void *workspace, size_t workspace_bytes, void *stream) {
+    if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < 16) return LA_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    (void)hipGetLastError();
+    unsigned word = 0;
+    hipError_t e = hipMemcpyAsync(&word, static_cast<const unsigned *>(workspace) + la::kWsErrorWord, sizeof(word),
+                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return LA_ERR_HIP;
+    return word == 0u ? LA_OK : LA_ERR_GAVE_UP;
 }
 
 LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
@@ -388,13 +500,16 @@ LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, cons
                           int64_t H, int64_t D, int64_t M, int dtype, void *stream) {
     if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
-    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (!dim_padded_ok(D) || !dim_padded_ok(M)) return LA_ERR_UNSUPPORTED;
     if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
     if (B * H == 0) return LA_OK;
     if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
     if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
+    if (!dim_ok(D) || !dim_ok(M))
+        return hip_status(la::decode_any(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), 1,
+                                         as_stream(stream)));
     return hip_status(la::decode_step(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), as_stream(stream)));
 }
 
@@ -550,7 +665,7 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
                            int64_t H, int64_t T, int64_t D, int64_t M, int dtype, void *stream) {
     if (B < 0 || H < 0 || T < 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
-    if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
+    if (!dim_padded_ok(D) || !dim_padded_ok(M)) return LA_ERR_UNSUPPORTED;
     if (B * H > INT_MAX || T > INT_MAX) return LA_ERR_UNSUPPORTED;
     if (B * H > 0 && T > INT64_MAX / (B * H * (D > M ? D : M))) return LA_ERR_UNSUPPORTED;
     if (B * H == 0 || T == 0) return LA_OK;
@@ -559,6 +674,8 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
         return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
     hipStream_t s = as_stream(stream);
+    if (!dim_ok(D) || !dim_ok(M))
+        return hip_status(la::decode_any(dtype, (int)D, (int)M, S, z, q, k, v, out, (int)(B * H), (int)T, s));
     // From about a dozen tokens on, the chunked causal kernels (MFMA tiles, the state
     // carried in and out in place) beat the register recurrence.  They are used when
     // every head is one segment, i.e. when no workspace is needed.

@@ -81,6 +81,18 @@ hipError_t decode_step(int dtype, int D, int M, float *S, float *z, const void *
 hipError_t decode_steps(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
                         float *out, int BH, int Tn, hipStream_t stream);
 
+// Widths that are multiples of 16 up to 128 without a specialised kernel (la_pad.hip).
+// pad_copy: dst[h][r][c] = src[h][r][c] for r < Rs and byte column c < Cs_bytes, else
+// `fill` in every 32-bit word (rows of Cd_bytes, Rd rows per h); unpad_copy: the
+// inverse selection.  Column widths are whole 16-byte units.
+hipError_t pad_copy(const void *src, void *dst, long BH, long Rs, long Cs_bytes, long Rd, long Cd_bytes,
+                    unsigned fill, hipStream_t stream);
+hipError_t unpad_copy(const void *src, void *dst, long BH, long Rs, long Cs_bytes, long Rd, long Cd_bytes,
+                      hipStream_t stream);
+// Tn recurrent steps of every head for D, M given at run time (multiples of 16 up to 128).
+hipError_t decode_any(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
+                      float *out, int BH, int Tn, hipStream_t stream);
+
 // Random-feature map (la_features.hip): kind 0 elu (F = D), 1 positive, 2
 // trigonometric; X2 / out2 optional (a second tensor in the same launch).
 hipError_t feature_map(int dtype, int D, int F, int kind, const void *X, float *out, const void *X2, float *out2,

@@ -176,7 +176,7 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *
     f32x4 *Sh = reinterpret_cast<f32x4 *>(S + bh * D * M);
     f32x4 Sv[G::PASSES];
 #pragma unroll
-    for (int p = 0; p < G::PASSES; ++p) Sv[p] = Sh[(roff + p * G::RP) * G::LPR + col4];
+    for (int p = 0; p < G::PASSES; ++p) Sv[p] = __builtin_nontemporal_load(Sh + (roff + p * G::RP) * G::LPR + col4);
     const f32x4 vv = load4<T>(v + bh * M + col4 * 4);
     float zz[(D + G::THREADS - 1) / G::THREADS];
 #pragma unroll
@@ -252,7 +252,7 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *
             s[j] += fk * vv[j];
             num[j] += fq * s[j];
         }
-        Sh[d * G::LPR + col4] = s;
+        __builtin_nontemporal_store(s, Sh + d * G::LPR + col4);
     }
 
     // reduce num over the lanes of a wavefront that share col4, then over wavefronts
@@ -337,7 +337,7 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_steps_kernel(
     float zl[G::PASSES];
 #pragma unroll
     for (int p = 0; p < G::PASSES; ++p) {
-        Sv[p] = Sh[(roff + p * G::RP) * G::LPR + col4];
+        Sv[p] = __builtin_nontemporal_load(Sh + (roff + p * G::RP) * G::LPR + col4);
         zl[p] = z[bh * D + roff + p * G::RP];
     }
     const size_t tok0 = bh * (size_t)Tn;
@@ -403,7 +403,7 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_steps_kernel(
     }
 #pragma unroll
     for (int p = 0; p < G::PASSES; ++p) {
-        Sh[(roff + p * G::RP) * G::LPR + col4] = Sv[p];
+        __builtin_nontemporal_store(Sv[p], Sh + (roff + p * G::RP) * G::LPR + col4);
         if (col4 == 0) z[bh * D + roff + p * G::RP] = zl[p];
     }
 }

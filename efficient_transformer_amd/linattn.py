@@ -6,13 +6,14 @@ built, every call raises -- there is no fallback implementation.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblinattn.so")
 
-LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP, LA_ERR_GAVE_UP = range(6)
 LA_F32, LA_BF16, LA_F32_FEATURES = 0, 1, 2
 LA_OUT_BF16 = 16
 LA_FEATURE_ELU, LA_FEATURE_PRF, LA_FEATURE_TRF = 0, 1, 2
@@ -33,6 +34,7 @@ SIGNATURES = {
     "la_forward_chunked": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _vp, _sz, _vp, _vp, _vp]),
     "la_workspace_init": (_int, [_vp, _sz, _vp]),
+    "la_workspace_status": (_int, [_vp, _sz, _vp]),
     "la_forward_continue": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp,
                                    _vp, _sz, _vp, _vp, _vp]),
     "la_forward_fused": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _vp,
@@ -179,7 +181,19 @@ def workspace_bytes(B, H, N, D, M, causal=True, dtype=LA_F32, chunk=0) -> int:
     return forward_plan(B, H, N, D, M, causal, dtype, chunk)[2]
 
 
-_ws_cache = {}
+# Workspaces made by the binding when the caller passes none: one per (device,
+# stream, plan), at most WS_CACHE_PER_STREAM per (device, stream), the least
+# recently used dropped first.  A cached buffer serves only the plan it was
+# zeroed for, so the "zero before first use with a plan" rule of the look-back
+# workspaces holds without re-zeroing.
+WS_CACHE_PER_STREAM = 8
+_ws_cache = collections.OrderedDict()
+
+# When true (environment LA_CHECK_WAITS=1), every call that used a look-back
+# workspace waits for its stream and raises LinAttnError(LA_ERR_GAVE_UP) if a
+# wait for earlier segments gave up (see workspace_status).  Off by default: the
+# check synchronises.
+CHECK_WAITS = os.environ.get("LA_CHECK_WAITS", "0") == "1"
 
 
 def workspace_init(ws, stream=None):
@@ -188,21 +202,41 @@ def workspace_init(ws, stream=None):
            "la_workspace_init")
 
 
+def workspace_status(ws, stream=None) -> None:
+    """Wait for `stream`, then raise LinAttnError (status LA_ERR_GAVE_UP) if a look-back wait
+    gave up in a call that used `ws` since it was last zeroed; the outputs of such a call hold
+    NaN rows and the workspace must be zeroed (workspace_init) before it is used again."""
+    _check(lib().la_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream, ws.device)),
+           "la_workspace_status")
+
+
+def _after_call(ws, stream, check):
+    if ws is not None and (CHECK_WAITS if check is None else check):
+        workspace_status(ws, stream)
+
+
 def _cached_workspace(nbytes, device, stream, key):
-    """A zero-initialised workspace kept per (device, stream, plan); calls with one plan on one
-    stream run in order, so they may share it."""
+    """A zero-initialised workspace for one plan on one (device, stream); calls with one plan
+    on one stream run in order, so they may share it."""
     import torch
-    sid = (stream if stream is not None else torch.cuda.current_stream(device)).cuda_stream
-    k = (str(device), sid, key)
+    st = stream if stream is not None else torch.cuda.current_stream(device)
+    dk = (str(device), st.cuda_stream)
+    k = dk + (key,)
     ws = _ws_cache.get(k)
-    if ws is None:
+    if ws is not None and ws.numel() >= nbytes:
+        _ws_cache.move_to_end(k)
+        return ws
+    with torch.cuda.stream(st):
         ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
-        _ws_cache[k] = ws
+    _ws_cache[k] = ws
+    same = [kk for kk in _ws_cache if kk[:2] == dk]
+    for old in same[:max(0, len(same) - WS_CACHE_PER_STREAM)]:
+        del _ws_cache[old]
     return ws
 
 
 def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_out=None, z_out=None,
-                    stream=None, features=False, out_dtype=None):
+                    stream=None, features=False, out_dtype=None, check=None):
     """Parallel-mode attention: Q, K [B,H,N,D], V [B,H,N,M] (float32 or bfloat16) -> out [B,H,N,M] float32.
 
     With S_out [B,H,D,M] and z_out [B,H,D] (float32) the final state is written too.
@@ -210,6 +244,9 @@ def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_o
     default a cached, zeroed one is used.  features=True: Q and K are float32
     features (feature_map), no feature map is applied and D is the feature dimension.
     A bfloat16 `out` (or out_dtype=torch.bfloat16) with bfloat16 inputs writes bf16 outputs.
+    D and M may be any multiple of 16 up to 128 (widths other than 16, 32, 64, 128 run on padded
+    copies in the workspace).  check=True (default: CHECK_WAITS) synchronises and raises if a
+    look-back wait gave up.
     """
     import torch
     if Q.dim() != 4:
@@ -234,6 +271,8 @@ def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_o
     st = lib().la_forward_chunked(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, int(bool(causal)), dt,
                                   chunk, _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
     _check(st, "la_forward_chunked")
+    if causal:
+        _after_call(workspace, stream, check)
     return out
 
 
@@ -260,7 +299,7 @@ def forward_onepass(Q, K, V, chunk, segments, out=None, workspace=None, S_out=No
 
 
 def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_out=None, z_out=None, stream=None,
-                     features=False, out_dtype=None):
+                     features=False, out_dtype=None, check=None):
     """Causal attention continuing from the carried state (S_in [B,H,D,M], z_in [B,H,D], fp32)."""
     import torch
     B, H, N, D = Q.shape
@@ -281,6 +320,7 @@ def forward_continue(Q, K, V, S_in, z_in, out=None, chunk=0, workspace=None, S_o
                                    _ptr(z_in), _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out),
                                    _stream(stream, dev))
     _check(st, "la_forward_continue")
+    _after_call(workspace, stream, check)
     return out
 
 
@@ -302,6 +342,7 @@ def _forward_explicit(name, Q, K, V, chunk, segments, out, workspace, S_out, z_o
                               segments, _ptr(S_in), _ptr(z_in), _ptr(workspace), wbytes, _ptr(S_out), _ptr(z_out),
                               _stream(stream, dev))
     _check(st, name)
+    _after_call(workspace, stream, None)
     return out
 
 
@@ -419,6 +460,7 @@ def softmax_scan(q, K, V, out=None, workspace=None, m_out=None, u_out=None, w_ou
     st = lib().la_softmax_scan(_ptr(q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, _dtype_code(K), _ptr(workspace),
                                wbytes, _ptr(m_out), _ptr(u_out), _ptr(w_out), _stream(stream, dev))
     _check(st, "la_softmax_scan")
+    _after_call(workspace, stream, None)
     return out
 
 
@@ -523,6 +565,8 @@ def forward_features(Q, K, V, W, F, kind="prf", normalize=False, out=None, works
                                    LA_FEATURE_NORMALIZE if normalize else 0, _ptr(workspace), wbytes,
                                    _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out), _stream(stream, dev))
     _check(st, "la_forward_features")
+    if causal:
+        _after_call(workspace, stream, None)
     return out
 
 

@@ -21,8 +21,12 @@
  *   - Input element type: LA_F32 (float) or LA_BF16 (bfloat16 bit patterns,
  *     uint16).  Arithmetic and accumulation are fp32; out, S and z are fp32
  *     (out bf16 with LA_BF16 | LA_OUT_BF16, see la_dtype).
- *   - D and M must each be 16, 32, 64 or 128.  All device pointers must be
- *     16-byte aligned.  Outputs must not alias inputs.
+ *   - D and M must each be 16, 32, 64 or 128, except where an entry point
+ *     says otherwise: la_forward_plan, la_forward_workspace_bytes,
+ *     la_forward_chunked, la_forward_continue, la_decode_step and
+ *     la_decode_steps take any multiple of 16 up to 128 (see "Widths without a
+ *     kernel of their own" below).  All device pointers must be 16-byte
+ *     aligned.  Outputs must not alias inputs.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns without waiting.  Concurrent calls that share a
  *     workspace race; calls with separate workspaces are thread safe.
@@ -51,7 +55,8 @@ enum la_status {
     LA_ERR_INVALID_ARG = 1, /* null pointer, negative size, misalignment, bad flag */
     LA_ERR_UNSUPPORTED = 2, /* D, M, chunk or segment count outside the supported set */
     LA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-    LA_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+    LA_ERR_HIP = 4,         /* the HIP runtime reported an error at launch */
+    LA_ERR_GAVE_UP = 5      /* la_workspace_status: a look-back wait gave up (NaN rows written) */
 };
 
 /* LA_F32_FEATURES: fp32 Q and K rows that already hold the features phi(q),
@@ -65,6 +70,23 @@ enum la_status {
  * then write out as bf16 bit patterns, each the fp32 result rounded to nearest
  * even; arithmetic, S and z stay fp32.  Other entry points reject it. */
 enum la_dtype { LA_F32 = 0, LA_BF16 = 1, LA_F32_FEATURES = 2, LA_OUT_BF16 = 16 };
+
+/*
+ * Widths without a kernel of their own (D or M of 48, 80, 96 or 112).  The
+ * page's statement (page "Transformers are RNNs", Proposed method: the
+ * similarity is the dot product phi(q)^T phi(k) of feature vectors of any
+ * length) holds for every width; the kernels are built for 16, 32, 64 and 128.
+ * la_forward_chunked and la_forward_continue run other multiples of 16 on
+ * copies padded to the next of those widths, held in the workspace: Q and K
+ * columns beyond D are -inf, which phi maps to exactly 0 (0 for
+ * LA_F32_FEATURES inputs), V columns beyond M are 0, and only the first M
+ * output columns and the [D][M] corner of the state are copied back.  The
+ * workspace (la_forward_workspace_bytes) then also holds those copies, and such
+ * calls move about twice the bytes of a call at a kernel width.  la_decode_step
+ * and la_decode_steps run them on one generic kernel with the widths as
+ * arguments (no workspace).  Results are those of the same problem at any
+ * width: the extra features and values add exact zeros.
+ */
 
 /* Human-readable name of a status code (static string; never NULL). */
 LA_API const char *la_status_str(int status);
@@ -91,7 +113,10 @@ LA_API int la_forward_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M
                            int causal, int dtype, int chunk_req,
                            int *chunk_out, int *segments_out, size_t *workspace_bytes_out);
 
-/* Workspace bytes la_forward_chunked needs for these arguments (0 on invalid arguments). */
+/* Workspace bytes la_forward_chunked needs for these arguments (0 on invalid
+ * arguments).  `causal` is an argument because the two modes keep different
+ * workspaces: causal calls keep look-back flags and two states per segment,
+ * non-causal calls one state per segment plus the total. */
 LA_API size_t la_forward_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
                                          int causal, int dtype, int chunk_req);
 
@@ -154,6 +179,19 @@ LA_API int la_forward_continue(const void *Q, const void *K, const void *V, void
 
 /* Zero a workspace (an enqueued fill kernel; graph-capture safe). bytes % 4 == 0. */
 LA_API int la_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Whether a look-back wait gave up in the calls that used this workspace since
+ * it was last zeroed (causal la_forward_chunked, la_forward_continue,
+ * la_forward_fused, la_forward_onepass, la_softmax_scan): waits for `stream`
+ * (every call enqueued on it so far completes), then reads the error word
+ * (32-bit word 3).  Returns LA_OK when no wait gave up, LA_ERR_GAVE_UP when one
+ * did (the affected outputs and final states are NaN; zero the workspace with
+ * la_workspace_init before its next use), LA_ERR_INVALID_ARG for a NULL or
+ * misaligned workspace or fewer than 16 bytes, LA_ERR_HIP if the copy or the
+ * wait fails.  Blocks the calling thread; not for use under graph capture.
+ */
+LA_API int la_workspace_status(const void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The causal fused kernel of la_forward_chunked with an explicit plan: chunk
@@ -232,7 +270,7 @@ LA_API int la_segment_outputs(const void *Q, const void *K, const void *V, void 
  * j <= i.  S [B][H][D][M] and z [B][H][D] (fp32) are read and rewritten in place
  * (start from zeros for an empty history).  q, k: [B][H][D]; v: [B][H][M];
  * out: [B][H][M] fp32.  The state is the whole history: copying S and z out and
- * back resumes a sequence exactly.
+ * back resumes a sequence exactly.  D and M: any multiple of 16 up to 128.
  */
 LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, const void *v,
                           float *out, int64_t B, int64_t H, int64_t D, int64_t M,

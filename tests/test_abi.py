@@ -34,7 +34,7 @@ def test_header_declares_the_entry_points():
               "la_status_str", "la_segment_states", "la_segment_scan", "la_segment_outputs", "la_version",
               "la_forward_fused", "la_forward_onepass", "la_forward_continue", "la_workspace_init",
               "la_backward_chunked", "la_decode_steps", "la_softmax_scan", "la_softmax_step", "la_feature_map",
-              "la_forward_features", "la_forward_features_workspace_bytes"):
+              "la_forward_features", "la_forward_features_workspace_bytes", "la_workspace_status"):
         assert s in syms
 
 
@@ -49,9 +49,9 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(5):
+    for code in range(6):
         assert L.status_str(code).startswith(["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED",
-                                              "LA_ERR_WORKSPACE", "LA_ERR_HIP"][code])
+                                              "LA_ERR_WORKSPACE", "LA_ERR_HIP", "LA_ERR_GAVE_UP"][code])
     assert L.status_str(99) == "unknown status"
     assert L.version() >= 100
 
@@ -96,7 +96,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails its checks
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(D=48), 2), (dict(M=8), 2), (dict(D=256), 2), (dict(dtype=3), 1), (dict(causal=2), 1),
+    (dict(D=40), 2), (dict(M=8), 2), (dict(D=256), 2), (dict(D=144), 2), (dict(M=120), 2), (dict(dtype=3), 1), (dict(causal=2), 1),
     (dict(chunk=128), 2), (dict(chunk=8), 2), (dict(N=-1), 1), (dict(B=-1), 1), (dict(H=-3), 1),
     (dict(Q=None), 1), (dict(out=None), 1), (dict(V=FAKE + 4), 1), (dict(S=FAKE), 1),
 ])
@@ -104,6 +104,52 @@ def test_forward_rejects_bad_arguments(L, kw, status):
     args = dict(Q=FAKE, K=FAKE, V=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
     args.update(kw)
     assert _fwd(L, **args) == status
+
+
+def _round256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("D,M", [(48, 64), (64, 48), (112, 112), (80, 96), (48, 16), (96, 128), (16, 112)])
+@pytest.mark.parametrize("causal,dtype", [(1, 0), (1, 1), (0, 0), (1, 17), (1, 2)])
+def test_padded_widths_plan(L, D, M, causal, dtype):
+    """Widths without a kernel of their own plan like the next kernel width up, with the
+    padded copies of Q, K, V, out and the state after the kernels' own workspace."""
+    B, H, N = 2, 3, 1000
+    up = lambda x: 16 if x <= 16 else 32 if x <= 32 else 64 if x <= 64 else 128
+    Dk, Mk = up(D), up(M)
+    C, G, ws = L.forward_plan(B, H, N, D, M, causal, dtype, 0)
+    Ck, Gk, wsk = L.forward_plan(B, H, N, Dk, Mk, causal, dtype, 0)
+    assert (C, G) == (Ck, Gk)
+    s_in = 2 if dtype & ~16 == 1 else 4
+    s_out = 2 if dtype & 16 else 4
+    rows = B * H * N
+    want = (_round256(max(wsk, 256)) + 2 * _round256(rows * Dk * s_in) + _round256(rows * Mk * s_in)
+            + _round256(rows * Mk * s_out) + _round256(B * H * Dk * Mk * 4) + _round256(B * H * Dk * 4))
+    assert ws == want
+    assert L.workspace_bytes(B, H, N, D, M, causal, dtype, 0) == ws
+    # empty problems need no workspace
+    assert L.forward_plan(B, H, 0, D, M, causal, dtype, 0)[2] == 0
+    assert L.forward_plan(0, H, N, D, M, causal, dtype, 0)[2] == 0
+
+
+def test_padded_widths_need_their_workspace(L):
+    need = L.workspace_bytes(1, 1, 64, 48, 48, 1, 0, 0)
+    assert need > 0
+    assert _fwd(L, Q=FAKE, K=FAKE, V=FAKE, out=FAKE, N=64, D=48, M=48, ws=None, ws_bytes=0) == L.LA_ERR_WORKSPACE
+    assert _fwd(L, Q=FAKE, K=FAKE, V=FAKE, out=FAKE, N=64, D=48, M=48, ws=FAKE,
+                ws_bytes=need - 1) == L.LA_ERR_WORKSPACE
+    # the explicit-plan and stage entry points keep the kernel widths
+    f = L.lib().la_forward_fused
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 48, 48, 0, 16, 1, None, None, None, 0, None, None,
+             None) == L.LA_ERR_UNSUPPORTED
+
+
+def test_workspace_status_checks(L):
+    f = L.lib().la_workspace_status
+    assert f(None, 1024, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE + 4, 1024, None) == L.LA_ERR_INVALID_ARG
+    assert f(FAKE, 8, None) == L.LA_ERR_INVALID_ARG
 
 
 def test_forward_workspace_checks(L):
@@ -124,7 +170,8 @@ def test_empty_batch_is_a_no_op(L):
 
 def test_decode_rejects_bad_arguments(L):
     f = L.lib().la_decode_step
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 48, 64, 0, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 40, 64, 0, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 144, 0, None) == L.LA_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 3, None) == L.LA_ERR_INVALID_ARG
     assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
     assert f(FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
@@ -188,7 +235,7 @@ def test_continue_entry_point_checks(L):
              None) == L.LA_ERR_INVALID_ARG  # misaligned S_in
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 0, 0, FAKE, FAKE, FAKE, need - 4, None, None,
              None) == L.LA_ERR_WORKSPACE
-    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 48, 64, 0, 0, FAKE, FAKE, FAKE, need, None, None,
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 40, 64, 0, 0, FAKE, FAKE, FAKE, need, None, None,
              None) == L.LA_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 2, 1000, 64, 64, 3, 0, FAKE, FAKE, FAKE, need, None, None,
              None) == L.LA_ERR_INVALID_ARG  # dtype
@@ -200,7 +247,7 @@ def test_continue_entry_point_checks(L):
 def test_decode_steps_checks(L):
     f = L.lib().la_decode_steps
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, -1, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 48, 64, 0, None) == L.LA_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 40, 64, 0, None) == L.LA_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 3, None) == L.LA_ERR_INVALID_ARG
     assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
     assert f(FAKE, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 2, 2, 8, 64, 64, 0, None) == L.LA_ERR_INVALID_ARG
@@ -271,7 +318,7 @@ def test_feature_inputs_dtype(L):
                                    L.LA_F32_FEATURES, FAKE, 1 << 30, None) == L.LA_ERR_UNSUPPORTED
     assert lib.la_softmax_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, L.LA_F32_FEATURES,
                                None) == L.LA_ERR_INVALID_ARG
-    assert lib.la_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 48, 64, L.LA_F32_FEATURES,
+    assert lib.la_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 40, 64, L.LA_F32_FEATURES,
                               None) == L.LA_ERR_UNSUPPORTED  # accepted type, unsupported D
 
 

@@ -41,12 +41,25 @@ def run(ea, dtype, B, H, N, D, M, seed):
 
 
 def check(got, ref, tol):
-    """max |x - y| over the tensor relative to max |y| (floored at 1e-2: with one
-    position the exact query and key gradients are zero)."""
+    """The row-wise metric on every (b, h, i) row of dQ, dK and dV: max over rows of
+    max_m |x - y| / max_m |y|.  Rows whose exact value is zero are held absolutely
+    against the tensor's scale instead (max |x| <= tol * max |y|): dq at position 0
+    (out_0 = v_0 whatever q_0 is) and, for a one-position sequence, dk at position 0."""
+    N = got[0].shape[2]
     for name, x, y in zip(("dQ", "dK", "dV"), got, ref):
         assert np.all(np.isfinite(x)), name
-        err = float(np.abs(x - y).max() / max(np.abs(y).max(), 1e-2))
-        assert err <= tol, f"{name} whole-tensor relative error {err:.3e} > {tol}"
+        zero = np.zeros(N, dtype=bool)
+        if name == "dQ" or (name == "dK" and N == 1):
+            zero[0] = True
+        if (~zero).any():
+            num = np.abs(x - y)[:, :, ~zero].max(axis=-1)
+            den = np.abs(y)[:, :, ~zero].max(axis=-1)
+            err = float((num / den).max())
+            assert err <= tol, f"{name} row-wise relative error {err:.3e} > {tol}"
+        if zero.any():
+            scale = max(float(np.abs(y).max()), 1e-30) if (~zero).any() else 1.0
+            err0 = float(np.abs(x[:, :, zero]).max() / scale)
+            assert err0 <= tol, f"{name} exact-zero rows: {err0:.3e} > {tol}"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

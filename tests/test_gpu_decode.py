@@ -117,37 +117,33 @@ def test_decode_resume_is_bitwise(ea):
     assert torch.equal(S, S3) and torch.equal(z, z3)
 
 
-def test_decode_256x8_t4096_sampled(ea):
-    """Full decode workload (256 streams x 8 heads, 4096 steps); 16 sampled heads against the oracle."""
+def test_decode_256x8_t4096_full(ea):
+    """Full decode workload (256 streams x 8 heads, D=M=64, 4096 steps from a zero state):
+    every head's output at every step, and every head's final state, against the oracle's
+    recurrence (fp64), in blocks of 256 steps."""
     cfg = synthetic.WORKLOADS["decode_f32_256x8_t4096_d64"]
     B, H, D, M, T = cfg["B"], cfg["H"], cfg["D"], cfg["M"], cfg["T"]
     BH = B * H
-    rng = np.random.default_rng(0)
-    heads = np.unique(np.concatenate([[0, BH - 1], rng.integers(0, BH, 14)]))
-    hidx = torch.from_numpy(heads).to(DEV)
     S = torch.zeros((B, H, D, M), device=DEV)
     z = torch.zeros((B, H, D), device=DEV)
-    hist = torch.empty((T, len(heads), M), device=DEV)
-    out = torch.empty((B, H, M), device=DEV)
     block = 256
-    sq, sk, sv = [], [], []
+    hist = torch.empty((block, B, H, M), device=DEV)
+    So = np.zeros((BH, D, M))
+    zo = np.zeros((BH, D))
+    worst = 0.0
     for t0 in range(0, T, block):
         q, k, v = synthetic.decode_inputs(cfg, 0, t0, t0 + block)
-        sq.append(q.reshape(block, BH, D)[:, heads])
-        sk.append(k.reshape(block, BH, D)[:, heads])
-        sv.append(v.reshape(block, BH, M)[:, heads])
         qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
         for i in range(block):
-            ea.decode_step(S, z, qd[i], kd[i], vd[i], out=out)
-            hist[t0 + i] = out.view(BH, M).index_select(0, hidx)
-    torch.cuda.synchronize()
-    got = hist.cpu().numpy()
-    q, k, v = np.concatenate(sq), np.concatenate(sk), np.concatenate(sv)
-    So = np.zeros((len(heads), D, M))
-    zo = np.zeros((len(heads), D))
-    ref = np.stack([oracle.decode_step(So, zo, q[t], k[t], v[t]) for t in range(T)])
-    err = rowwise_rel(got, ref)
-    print(f"256x8 t4096 sampled row-wise rel err {err:.3e}")
-    assert err <= TOL["f32"], f"{err:.3e}"
-    err = whole_rel(S.view(BH, D, M)[hidx].cpu().numpy(), So)
-    assert err <= 1e-5, f"whole_rel {err:.3e} > {1e-5}"
+            ea.decode_step(S, z, qd[i], kd[i], vd[i], out=hist[i])
+        torch.cuda.synchronize()
+        got = hist.view(block, BH, M).cpu().numpy()
+        q, k, v = (x.reshape(block, BH, -1).astype(np.float64) for x in (q, k, v))
+        for i in range(block):
+            ref = oracle.decode_step(So, zo, q[i], k[i], v[i])
+            err = rowwise_rel(got[i], ref)
+            worst = max(worst, err)
+            assert err <= TOL["f32"], f"step {t0 + i}: {err:.3e}"
+    print(f"256x8 t4096 all heads, every step: row-wise rel err {worst:.3e}")
+    assert whole_rel(S.view(BH, D, M).cpu().numpy(), So) <= 1e-5
+    assert whole_rel(z.view(BH, D).cpu().numpy(), zo) <= 1e-5

@@ -3,7 +3,8 @@ of the workspace header caps every wait at one poll, so workgroups whose
 predecessors have not published yet give up.  Every kernel still ends; the
 rows (and final states) that lost their prefix are NaN, the error word (word 3)
 is set, every row that is not NaN equals the normal call's, and after the
-workspace is zeroed again the next call is whole."""
+workspace is zeroed again the next call is whole.  la_workspace_status (and the
+binding's check after a call) reports the give-up exactly when the word is set."""
 import pytest
 import torch
 
@@ -60,11 +61,18 @@ def test_forward_gives_up_cleanly(ea, shape):
     # a head whose rows lost their prefix near the end also has a NaN final state
     last_nan = nan_rows[:, :, -1]
     assert torch.isnan(S).any(dim=(-1, -2)).eq(last_nan).all()
+    # the C ABI reports it, and so does the binding's check after a call
+    with pytest.raises(ea.LinAttnError) as info:
+        ea.workspace_status(ws)
+    assert info.value.status == ea.linattn.LA_ERR_GAVE_UP
+    with pytest.raises(ea.LinAttnError):
+        ea.forward_chunked(Q, K, V, workspace=ws, check=True)
     # zeroed again, the workspace serves a whole call
     ws.zero_()
-    again = ea.forward_chunked(Q, K, V, workspace=ws)
+    again = ea.forward_chunked(Q, K, V, workspace=ws, check=True)
     torch.cuda.synchronize()
     assert int(words[ERROR_WORD].item()) == 0
+    ea.workspace_status(ws)
     assert torch.allclose(again, want, rtol=1e-5, atol=1e-6)
 
 
@@ -87,7 +95,24 @@ def test_softmax_scan_gives_up_cleanly(ea):
     assert failed == bool(nan_rows.any())
     if not failed:
         pytest.skip("every earlier group had published at the first poll")
+    with pytest.raises(ea.LinAttnError) as info:
+        ea.workspace_status(ws)
+    assert info.value.status == ea.linattn.LA_ERR_GAVE_UP
     ws.zero_()
     again = ea.softmax_scan(q, K, V, workspace=ws)
     torch.cuda.synchronize()
+    ea.workspace_status(ws)
     assert torch.allclose(again, want, rtol=1e-5, atol=1e-6)
+
+
+def test_status_of_a_clean_workspace(ea):
+    """Normal calls leave the error word clear; the binding's check passes."""
+    B, H, N, D, M = 2, 4, 8192, 64, 64
+    cfg = dict(kind="prefill", B=B, H=H, N=N, D=D, M=M, sigma=1.0, dtype="f32", chunk=0)
+    Q, K, V = (to_dev(x, "f32") for x in synthetic.prefill_inputs(cfg, 91))
+    _, G, need = ea.forward_plan(B, H, N, D, M, True, 0, 0)
+    assert G > 1
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for _ in range(3):
+        ea.forward_chunked(Q, K, V, workspace=ws, check=True)
+    ea.workspace_status(ws)
