@@ -13,6 +13,7 @@ from .linattn import (  # noqa: F401
     decode_steps,
     feature_map,
     forward_chunked,
+    forward_chunked_noalloc,
     forward_continue,
     forward_features,
     forward_fused,
@@ -22,6 +23,7 @@ from .linattn import (  # noqa: F401
     probe_mfma,
     fused_workspace_bytes,
     lib_path,
+    noalloc_scratch_bytes,
     segment_outputs,
     segment_scan,
     segment_states,

@@ -3,6 +3,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "la_launch.hpp"
 #include "linattn.h"
@@ -205,6 +206,31 @@ hipError_t run_padded(const Plan &p, const void *Q, const void *K, const void *V
     return e;
 }
 
+// ---- scratch of la_forward_chunked_noalloc ----------------------------------
+// A file-scope device array (each device that loads the library holds its own
+// copy until the process ends).  Host code never passes `scratch` itself to a
+// kernel: its name on the host is a stand-in, not a device address.  The
+// address on each device comes from hipGetSymbolAddress, taken once per device
+// with that device current, and is kept in scratch_ptr.
+constexpr size_t kScratchBytes = LA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device, or nullptr when it cannot be had.
+void *device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        scratch_ptr[dev] = ptr;
+    }
+    return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +308,37 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, void 
             e = la::prefill_outputs(dt, Di, Mi, C, Q, K, V, out, ws, (int)BH, (int)N, G, cps, 0, nullptr, nullptr, s);
     }
     return hip_status(e);
+}
+
+LA_API size_t la_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+LA_API int la_forward_chunked_noalloc(const void *Q, const void *K, const void *V, void *out, int64_t B,
+                                      int64_t H, int64_t N, int64_t D, int64_t M, int causal, int dtype,
+                                      int chunk_req, float *S_out, float *z_out, void *stream) {
+    Plan p;
+    int st = make_plan(B, H, N, D, M, causal, dtype, chunk_req, &p, 0, true);
+    if (st != LA_OK) return st;
+    if (p.ws_bytes > kScratchBytes) return LA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (p.ws_bytes > 0 && B * H > 0 && N > 0) {
+        // the same argument checks as la_forward_chunked, before the scratch is touched
+        if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
+        if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
+        if (!Q || !K || !V || !out) return LA_ERR_INVALID_ARG;
+        if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(out)) return LA_ERR_INVALID_ARG;
+        ws = device_scratch();
+        if (ws == nullptr) return LA_ERR_HIP;
+        if (causal) {
+            // the look-back header and flags start at zero on every call (the kernels'
+            // own workspace is at the front of the scratch for padded plans too); the
+            // state slots are written before they are read
+            const size_t words = la::kWsHeaderWords + la::fused_flag_words((long)(B * H) * p.segments);
+            (void)hipGetLastError();
+            if (la::fill_zero(static_cast<float *>(ws), words, as_stream(stream)) != hipSuccess) return LA_ERR_HIP;
+        }
+    }
+    return la_forward_chunked(Q, K, V, out, B, H, N, D, M, causal, dtype, chunk_req, ws, ws ? kScratchBytes : 0,
+                              S_out, z_out, stream);
 }
 
 LA_API int la_forward_continue(const void *Q, const void *K, const void *V, void *out, int64_t B, int64_t H,

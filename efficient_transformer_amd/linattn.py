@@ -34,6 +34,9 @@ SIGNATURES = {
     "la_forward_chunked": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
                                   _vp, _sz, _vp, _vp, _vp]),
     "la_workspace_init": (_int, [_vp, _sz, _vp]),
+    "la_noalloc_scratch_bytes": (_sz, []),
+    "la_forward_chunked_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _int,
+                                          _vp, _vp, _vp]),
     "la_workspace_status": (_int, [_vp, _sz, _vp]),
     "la_forward_continue": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp,
                                    _vp, _sz, _vp, _vp, _vp]),
@@ -274,6 +277,27 @@ def forward_chunked(Q, K, V, causal=True, chunk=0, out=None, workspace=None, S_o
     if causal:
         _after_call(workspace, stream, check)
     return out
+
+
+def forward_chunked_noalloc(Q, K, V, out, causal=True, chunk=0, S_out=None, z_out=None, stream=None):
+    """la_forward_chunked_noalloc: the same attention as forward_chunked with the library's
+    static device scratch as workspace; the caller supplies `out` (and S_out, z_out), so
+    nothing is allocated.  Calls that overlap in time on one device race on the scratch."""
+    B, H, N, D = Q.shape
+    M = V.shape[-1]
+    dev = Q.device
+    _require(K, "K", (B, H, N, D), Q.dtype, dev)
+    _require(V, "V", (B, H, N, M), Q.dtype, dev)
+    dt = _dtype_code(Q)
+    out, dt = _out_code(dt, out, None, (B, H, N, M), dev)
+    st = lib().la_forward_chunked_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(out), B, H, N, D, M, int(bool(causal)),
+                                          dt, chunk, _ptr(S_out), _ptr(z_out), _stream(stream, dev))
+    _check(st, "la_forward_chunked_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().la_noalloc_scratch_bytes())
 
 
 def fused_workspace_bytes(B, H, D, M, segments) -> int:

@@ -157,6 +157,29 @@ LA_API int la_forward_chunked(const void *Q, const void *K, const void *V, void 
                               float *S_out, float *z_out, void *stream);
 
 /*
+ * la_forward_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The call allocates nothing: the
+ * workspace is a file-scope device array of la_noalloc_scratch_bytes() bytes
+ * (LA_NOALLOC_SCRATCH_BYTES, 64 MiB) that every device using the library holds
+ * until the process ends.  Arguments, results and errors as for
+ * la_forward_chunked, plus LA_ERR_WORKSPACE when the plan needs more workspace
+ * than the scratch holds (for example B*H = 16, N = 65536, D = M = 128 bf16
+ * needs about 34 MB; a width padded to a kernel width also needs room for the
+ * padded copies).  A causal call first clears the look-back header and flags
+ * of the scratch with a fill kernel on `stream`, then runs la_forward_chunked's
+ * kernels on it.  All calls on one device share that device's scratch: calls
+ * that overlap in time on one device (another stream, another thread) race
+ * and must be serialised by the caller.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+LA_API size_t la_noalloc_scratch_bytes(void);
+LA_API int la_forward_chunked_noalloc(const void *Q, const void *K, const void *V, void *out,
+                                      int64_t B, int64_t H, int64_t N, int64_t D, int64_t M,
+                                      int causal, int dtype, int chunk_req,
+                                      float *S_out, float *z_out, void *stream);
+
+/*
  * Causal attention continuing a sequence from a carried state: the positions
  * of this call come after earlier ones whose state is (S_in, z_in), so
  *   out_i = phi(q_i)^T (S_in + S_i) / phi(q_i)^T (z_in + z_i)
