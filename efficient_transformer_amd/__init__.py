@@ -21,6 +21,7 @@ from .linattn import (  # noqa: F401
     forward_plan,
     probe_copy,
     probe_mfma,
+    probe_read,
     fused_workspace_bytes,
     lib_path,
     noalloc_scratch_bytes,

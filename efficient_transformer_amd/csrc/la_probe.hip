@@ -1,6 +1,9 @@
 // Peak probes: the attainable rates that the kernels' rooflines are set against.
-//   la_probe_copy: a plain device-to-device copy (16-byte words, four in flight
-//                  per thread) -> attainable HBM read + write rate;
+//   la_probe_copy: a plain device-to-device copy (16-byte nontemporal loads and
+//                  stores, four in flight per thread) -> attainable HBM read +
+//                  write rate;
+//   la_probe_read: a read-only stream (16-byte nontemporal loads summed per
+//                  thread) -> attainable HBM read rate;
 //   la_probe_mfma: chains of fp32 16x16x4 or bf16 16x16x32 MFMAs on eight
 //                  independent accumulators per wavefront -> attainable matrix rate.
 // Both are checkable: the copy is bit-exact and every MFMA chain reaches a value
@@ -16,6 +19,8 @@ namespace {
 
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;
+constexpr int kCopyBlocks = 256 * 32;    // grid of the copy (measured best of 4096..8192 per 1 GiB)
+constexpr int kReadBlocks = 1024;        // grid of the read stream (measured best of 1024..8192)
 constexpr int kMfmaThreads = 256;
 constexpr int kMfmaChains = 8;
 
@@ -27,14 +32,33 @@ __global__ __launch_bounds__(kCopyThreads) void probe_copy_kernel(const la::f32x
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
             const size_t j = i + (size_t)u * kCopyThreads;
-            if (j < n4) v[u] = src[j];
+            if (j < n4) v[u] = __builtin_nontemporal_load(src + j);
         }
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
             const size_t j = i + (size_t)u * kCopyThreads;
-            if (j < n4) dst[j] = v[u];
+            if (j < n4) __builtin_nontemporal_store(v[u], dst + j);
         }
     }
+}
+
+// Each thread sums the floats of its 16-byte words (grid-stride, four loads in
+// flight) and writes one partial sum.
+__global__ __launch_bounds__(kCopyThreads) void probe_read_kernel(const la::f32x4 *__restrict__ src,
+                                                                  float *__restrict__ out, size_t n4) {
+    const size_t step = (size_t)gridDim.x * kCopyThreads * kCopyUnroll;
+    la::f32x4 acc = la::zero4();
+    for (size_t i = (size_t)blockIdx.x * kCopyThreads * kCopyUnroll + threadIdx.x; i < n4; i += step) {
+        la::f32x4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const size_t j = i + (size_t)u * kCopyThreads;
+            v[u] = j < n4 ? __builtin_nontemporal_load(src + j) : la::zero4();
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) acc += v[u];
+    }
+    out[(size_t)blockIdx.x * kCopyThreads + threadIdx.x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // Every operand element is x (rounded to the operand type); each MFMA adds K x^2
@@ -77,11 +101,23 @@ LA_API int la_probe_copy(void *dst, const void *src, size_t bytes, void *stream)
     const size_t n4 = bytes / 16;
     const size_t per_block = (size_t)kCopyThreads * kCopyUnroll;
     // enough workgroups to fill every CU many times over; the loop strides over the rest
-    const size_t blocks = std::min<size_t>((n4 + per_block - 1) / per_block, 256 * 16);
+    const size_t blocks = std::min<size_t>((n4 + per_block - 1) / per_block, kCopyBlocks);
     (void)hipGetLastError();
     hipLaunchKernelGGL(probe_copy_kernel, dim3((unsigned)blocks), dim3(kCopyThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const la::f32x4 *>(src),
                        static_cast<la::f32x4 *>(dst), n4);
+    return status_of(hipGetLastError());
+}
+
+LA_API size_t la_probe_read_partials(void) { return (size_t)kReadBlocks * kCopyThreads; }
+
+LA_API int la_probe_read(float *out, const void *src, size_t bytes, void *stream) {
+    if (bytes % 16 != 0) return LA_ERR_INVALID_ARG;
+    if (!out || ((uintptr_t)out & 3u)) return LA_ERR_INVALID_ARG;
+    if (bytes > 0 && (!src || ((uintptr_t)src & 15u))) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(probe_read_kernel, dim3(kReadBlocks), dim3(kCopyThreads), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const la::f32x4 *>(src), out, bytes / 16);
     return status_of(hipGetLastError());
 }
 

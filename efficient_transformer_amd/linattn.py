@@ -64,6 +64,8 @@ SIGNATURES = {
     "la_forward_features": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _i64, _int,
                                    _int, _vp, _sz, _vp, _vp, _vp, _vp, _vp]),
     "la_probe_copy": (_int, [_vp, _vp, _sz, _vp]),
+    "la_probe_read_partials": (_sz, []),
+    "la_probe_read": (_int, [_vp, _vp, _sz, _vp]),
     "la_probe_mfma": (_int, [_vp, _int, _i64, _int, ctypes.c_float, _vp]),
 }
 
@@ -634,6 +636,21 @@ def probe_copy(dst, src, stream=None):
     _check(lib().la_probe_copy(_ptr(dst), _ptr(src), src.numel() * src.element_size(), _stream(stream, src.device)),
            "la_probe_copy")
     return dst
+
+
+def probe_read(src, out=None, stream=None):
+    """Read-only stream probe: per-thread partial sums of src's fp32 words (returns them)."""
+    import torch
+    n = int(lib().la_probe_read_partials())
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=src.device)
+    if out.numel() != n or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"probe_read: out must be contiguous float32 with {n} elements")
+    if not src.is_contiguous():
+        raise ValueError("probe_read: src must be contiguous")
+    _check(lib().la_probe_read(_ptr(out), _ptr(src), src.numel() * src.element_size(), _stream(stream, src.device)),
+           "la_probe_read")
+    return out
 
 
 def probe_mfma(kind: str, blocks: int, iters: int, x: float = 0.5, out=None, stream=None, device=None):

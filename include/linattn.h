@@ -467,6 +467,13 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
  * blocks = 0 is a no-op.
  */
 LA_API int la_probe_copy(void *dst, const void *src, size_t bytes, void *stream);
+/* la_probe_read: sums the fp32 words of src (bytes % 16 == 0; 16-byte aligned)
+ * with nontemporal 16-byte loads over a fixed grid; out receives one partial
+ * sum per thread, la_probe_read_partials() floats in all (every one written,
+ * also for bytes == 0).  Their sum is the sum of src up to rounding order (exact
+ * for small integer values).  Measures the attainable read-only HBM rate. */
+LA_API size_t la_probe_read_partials(void);
+LA_API int la_probe_read(float *out, const void *src, size_t bytes, void *stream);
 LA_API int la_probe_mfma(float *out, int dtype, int64_t blocks, int iters, float x, void *stream);
 
 #ifdef __cplusplus

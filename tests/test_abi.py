@@ -406,6 +406,12 @@ def test_probe_checks(L):
     assert lib.la_probe_copy(None, None, 20, None) == L.LA_ERR_INVALID_ARG
     assert lib.la_probe_copy(None, None, 32, None) == L.LA_ERR_INVALID_ARG
     assert lib.la_probe_copy(16, 17, 32, None) == L.LA_ERR_INVALID_ARG
+    assert lib.la_probe_read_partials() == 1024 * 256
+    assert lib.la_probe_read(None, None, 0, None) == L.LA_ERR_INVALID_ARG  # no out
+    assert lib.la_probe_read(FAKE, None, 16, None) == L.LA_ERR_INVALID_ARG  # no src
+    assert lib.la_probe_read(FAKE, FAKE, 20, None) == L.LA_ERR_INVALID_ARG  # not whole 16-byte words
+    assert lib.la_probe_read(FAKE + 2, FAKE, 32, None) == L.LA_ERR_INVALID_ARG  # misaligned out
+    assert lib.la_probe_read(FAKE, FAKE + 8, 32, None) == L.LA_ERR_INVALID_ARG  # misaligned src
     assert lib.la_probe_mfma(None, L.LA_F32, 0, 10, 0.5, None) == L.LA_OK
     assert lib.la_probe_mfma(None, L.LA_F32, 4, 10, 0.5, None) == L.LA_ERR_INVALID_ARG
     assert lib.la_probe_mfma(None, 7, 4, 10, 0.5, None) == L.LA_ERR_INVALID_ARG

@@ -32,6 +32,17 @@ def test_copy_leaves_the_rest(ea):
     assert torch.equal(dst[:64], src) and bool((dst[64:] == -1).all())
 
 
+@pytest.mark.parametrize("nbytes", [0, 16, 4096, 16 * 1000003, 1 << 28])
+def test_read_sums_exactly(ea, nbytes):
+    print(f"probe_read {nbytes}", flush=True)
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    part = ea.probe_read(src)
+    torch.cuda.synchronize()
+    # every partial is a count of ones below 2^24: exact
+    assert part.numel() == ea.linattn.lib().la_probe_read_partials()
+    assert float(part.double().sum().item()) == nbytes // 4
+
+
 @pytest.mark.parametrize("kind,K", [("f32", 4), ("bf16", 32)])
 @pytest.mark.parametrize("blocks,iters,x", [(1, 1, 0.5), (3, 17, 0.5), (512, 64, 0.25), (7, 0, 0.5)])
 def test_mfma_closed_form(ea, kind, K, blocks, iters, x):
