@@ -26,6 +26,8 @@ bool dim_ok(int64_t x) { return x == 16 || x == 32 || x == 64 || x == 128; }
 bool dim_padded_ok(int64_t x) { return x >= 16 && x <= 128 && x % 16 == 0; }
 int64_t dim_up(int64_t x) { return x <= 16 ? 16 : x <= 32 ? 32 : x <= 64 ? 64 : 128; }
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+// B * H > lim, for B, H >= 0, without forming a product that can overflow
+bool bh_over(int64_t B, int64_t H, int64_t lim) { return B > lim || H > lim || (B > 0 && H > lim / B); }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Plan {
@@ -51,7 +53,7 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype
         if (!allow_pad || !dim_padded_ok(D) || !dim_padded_ok(M)) return LA_ERR_UNSUPPORTED;
     }
     // index arithmetic uses int for counts and size_t for element offsets
-    if (N > INT_MAX || B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
+    if (N > INT_MAX || bh_over(B, H, INT_MAX / 8)) return LA_ERR_UNSUPPORTED;
     if (B > 0 && H > 0 && N > 0) {
         const int64_t per_head = N * (D > M ? D : M);
         if (per_head > INT64_MAX / (B * H)) return LA_ERR_UNSUPPORTED;
@@ -524,7 +526,7 @@ LA_API int la_segment_scan(float *ws, size_t ws_bytes, int64_t B, int64_t H, int
     if (nstates != segments && nstates != segments - 1) return LA_ERR_INVALID_ARG;
     if ((S_out == nullptr) != (z_out == nullptr)) return LA_ERR_INVALID_ARG;
     if (S_out && (!aligned16(S_out) || !aligned16(z_out))) return LA_ERR_INVALID_ARG;
-    if (B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
+    if (bh_over(B, H, INT_MAX / 8)) return LA_ERR_UNSUPPORTED;
     const size_t need = state_ws_bytes(B * H, D, M, segments);
     if (ws == nullptr || ws_bytes < need) return LA_ERR_WORKSPACE;
     if (!aligned16(ws)) return LA_ERR_INVALID_ARG;
@@ -558,7 +560,7 @@ LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, cons
     if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
     if (!dim_padded_ok(D) || !dim_padded_ok(M)) return LA_ERR_UNSUPPORTED;
-    if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (bh_over(B, H, INT_MAX)) return LA_ERR_UNSUPPORTED;
     if (B * H == 0) return LA_OK;
     if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
     if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -578,7 +580,7 @@ LA_API int la_decode_step_features(float *S, float *z, const void *q, const void
     if (kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
     if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(M) || !(F == 16 || F == 32 || F == 64)) return LA_ERR_UNSUPPORTED;
-    if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (bh_over(B, H, INT_MAX)) return LA_ERR_UNSUPPORTED;
     if (B * H == 0) return LA_OK;
     if (!S || !z || !q || !k || !v || !out || !W) return LA_ERR_INVALID_ARG;
     if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
@@ -668,7 +670,7 @@ int scan_check(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype,
     if (B < 0 || H < 0 || N < 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
-    if (N > INT_MAX || B * H > INT_MAX / 8) return LA_ERR_UNSUPPORTED;
+    if (N > INT_MAX || bh_over(B, H, INT_MAX / 8)) return LA_ERR_UNSUPPORTED;
     const int64_t R = la::softmax_scan_rows((int)M);
     const int64_t NS = (N + R - 1) / R;
     if (B * H * NS > INT_MAX / 64) return LA_ERR_UNSUPPORTED;
@@ -708,7 +710,7 @@ LA_API int la_softmax_step(float *m, float *u, float *w, const void *q, const vo
     if (B < 0 || H < 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
     if (!dim_ok(D) || !dim_ok(M)) return LA_ERR_UNSUPPORTED;
-    if (B * H > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (bh_over(B, H, INT_MAX)) return LA_ERR_UNSUPPORTED;
     if (B * H == 0) return LA_OK;
     if (!m || !u || !w || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -723,7 +725,7 @@ LA_API int la_decode_steps(float *S, float *z, const void *q, const void *k, con
     if (B < 0 || H < 0 || T < 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_F32 && dtype != LA_BF16 && dtype != LA_F32_FEATURES) return LA_ERR_INVALID_ARG;
     if (!dim_padded_ok(D) || !dim_padded_ok(M)) return LA_ERR_UNSUPPORTED;
-    if (B * H > INT_MAX || T > INT_MAX) return LA_ERR_UNSUPPORTED;
+    if (bh_over(B, H, INT_MAX) || T > INT_MAX) return LA_ERR_UNSUPPORTED;
     if (B * H > 0 && T > INT64_MAX / (B * H * (D > M ? D : M))) return LA_ERR_UNSUPPORTED;
     if (B * H == 0 || T == 0) return LA_OK;
     if (!S || !z || !q || !k || !v || !out) return LA_ERR_INVALID_ARG;
