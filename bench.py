@@ -186,9 +186,12 @@ def make_prefill_sets(cfg, nsets, dev, seed0=0):
     return sets
 
 
-def prefill_runner(cfg, dev, min_bytes=None):
+MAX_SETS = 64  # a launch-bound workload gains nothing from more rotation
+
+
+def prefill_runner(cfg, dev, nsets=None):
     """(step function, plan) of a causal prefill workload; inputs rotate over enough buffer
-    sets that the last-level cache cannot hold them."""
+    sets that the last-level cache cannot hold them (at most MAX_SETS), or over `nsets`."""
     import torch
     import efficient_transformer_amd as ea
     from efficient_transformer_amd import linattn as L
@@ -196,7 +199,8 @@ def prefill_runner(cfg, dev, min_bytes=None):
     B, H, N, D, M = cfg["B"], cfg["H"], cfg["N"], cfg["D"], cfg["M"]
     C, G, wsb = ea.forward_plan(B, H, N, D, M, True, code, cfg.get("chunk", 0))
     nbytes = prefill_bytes(cfg)
-    nsets = max(1, math.ceil(1.25 * LLC_BYTES / max(nbytes, min_bytes or 1)))
+    if nsets is None:
+        nsets = min(MAX_SETS, max(1, math.ceil(1.25 * LLC_BYTES / nbytes)))
     sets = make_prefill_sets(cfg, nsets, dev)
     ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)  # zeroed once; each call leaves it ready
     stream = torch.cuda.current_stream(dev)
@@ -573,7 +577,7 @@ def profile_run(workload, dev, launches=8):
     import efficient_transformer_amd as ea
     import synthetic
     if workload in synthetic.WORKLOADS and synthetic.WORKLOADS[workload]["kind"] == "prefill":
-        step, plan = prefill_runner(dict(synthetic.WORKLOADS[workload]), dev)
+        step, plan = prefill_runner(dict(synthetic.WORKLOADS[workload]), dev, nsets=1)
         for i in range(launches):
             step(i)
     elif workload == DECODE:
