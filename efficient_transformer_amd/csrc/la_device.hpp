@@ -68,30 +68,6 @@ __device__ __forceinline__ f32x4 mma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.0f, 0.0f, 0.0f, 0.0f}; }
 
-// acc += A (16 x K) * B (K x 16) where, for lane (g, l16), row l16 of A starts at
-// `a` and column l16 of B starts at `b`; the K elements of each are contiguous.
-// 32-deep MFMA steps (K == 16 runs as one zero-padded step).
-template <int K>
-__device__ __forceinline__ f32x4 tile_dot_bf16(const bf16 *a, const bf16 *b, int g, f32x4 acc) {
-    static_assert(K % 16 == 0, "K must be a multiple of 16");
-    if constexpr (K % 32 == 0) {
-#pragma unroll
-        for (int ks = 0; ks < K / 32; ++ks) {
-            bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + ks * 32 + 8 * g);
-            bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + ks * 32 + 8 * g);
-            acc = mma_bf16_k32(av, bv, acc);
-        }
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < K / 16; ++ks) {
-            bf16x4 av = *reinterpret_cast<const bf16x4 *>(a + ks * 16 + 4 * g);
-            bf16x4 bv = *reinterpret_cast<const bf16x4 *>(b + ks * 16 + 4 * g);
-            acc = mma_bf16_k16(av, bv, acc);
-        }
-    }
-    return acc;
-}
-
 // fp32 variant with strided operands: for contraction index k = 4*ks + g the lane
 // reads A at a[k * a_ks] (a points at row l16 of A) and B at b[k * b_ks] (b points
 // at column l16 of B).

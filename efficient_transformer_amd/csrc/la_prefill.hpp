@@ -26,11 +26,17 @@
 // shared out over the wavefronts) and passed through LDS.
 //
 // LDS (element type T = float or bf16):
-//   phi(Q) [C][D+p]   phi(K) [C][D+p]   A [C][C+p]
-//   fp32: V [C][M+p]             bf16: V^T [M][C+p], phi(K)^T [D][C+p]
+//   fp32: phi(Q) [C][D+p]   phi(K) [C][D+p]   V [C][M+p]   A [C][C+p]
+//   bf16: phi(Q) [C][D]     phi(K) [C][D]     V [C][M]     A [C][C+p]
 //   fp32 side arrays: z [D], column-sum partials, row-sum partials, phi(q).z
-// bf16 MFMA operands need the contraction index contiguous per lane, hence the
-// transposed copies; fp32 MFMA takes one element per lane.
+// bf16 tiles are unpadded with their 16-byte blocks XOR-swizzled per row (bswz),
+// so that both row reads (sixteen rows, one block each) and the transposed reads
+// of gfx950 (ds_read_b64_tr_b16: four rows, two blocks each, handed out column
+// by column) spread over the LDS banks.  The bf16 MFMA operands that need the
+// key index contiguous per lane (phi(K)^T and V^T in the state update, V^T in
+// the intra-chunk term, the key sums of phi(K)) come from those transposed reads
+// of the natural tiles, so no transposed copy is stored; fp32 MFMA takes one
+// element per lane from any layout.
 #pragma once
 
 #include <type_traits>
@@ -55,10 +61,9 @@ struct Cfg {
     static constexpr int MTW = (MT + NW - 1) / NW;  // m-tiles per wavefront
     static constexpr int NA = RT * (RT + 1) / 2;            // lower-triangle tiles of A
     static constexpr int PAD = F32 ? 12 : 8;
-    static constexpr int LQ = D + PAD;  // rows of phi(Q), phi(K)
-    static constexpr int LA = C + PAD;  // rows of A
-    static constexpr int LV = M + PAD;  // fp32: rows of V
-    static constexpr int LT = C;        // bf16: rows of V^T and phi(K)^T (swizzled, see tsw)
+    static constexpr int LQ = F32 ? D + PAD : D;  // rows of phi(Q), phi(K) (bf16: swizzled, unpadded)
+    static constexpr int LA = C + PAD;            // rows of A
+    static constexpr int LV = F32 ? M + PAD : M;  // rows of V (bf16: swizzled, unpadded)
     static constexpr int E = D * M + D; // floats of one state (S then z)
     static constexpr int EP = (E + 63) / 64 * 64;  // exchanged-state slot: whole 256-byte blocks
     static constexpr int NZP = THREADS / D < C ? THREADS / D : C;  // column-sum partial groups
@@ -71,10 +76,8 @@ struct Cfg {
     static constexpr int oQ = 0;
     static constexpr int oK = oQ + C * LQ;
     static constexpr int oV = oK + C * LQ;
-    static constexpr int nV = F32 ? C * LV : M * LT;
-    static constexpr int oKt = oV + nV;
-    static constexpr int nKt = F32 ? 0 : D * LT;
-    static constexpr int oA = oKt + nKt;
+    static constexpr int nV = C * LV;
+    static constexpr int oA = oV + nV;
     static constexpr int nT = oA + C * LA;
     static constexpr size_t fbase = ((nT * sizeof(T) + 15) / 16) * 16;
     // float offsets (from fbase)
@@ -89,20 +92,60 @@ struct Cfg {
 
 // ---------------------------------------------------------------------------
 // Staging of a C x W tile of a [N][W] head matrix: global -> registers -> LDS.
-// fp32: an item is one 16-byte vector of one row (rows of W/4 items).
-// bf16: an item is one 16-byte column block of RPI (4 or 2) consecutive rows, so that
-//       the transposed store can write RPI keys of one column at once.
+// An item is one 16-byte vector of one row (rows of W/VEC items).
 // Rows at or beyond N are stored as zeros (after phi, so they add nothing).
 // ---------------------------------------------------------------------------
-// Element offset of `key` within a row of a transposed bf16 tile (unpadded rows of
-// C keys).  Keys are grouped in octets (16 bytes); octet o of row r is stored at
-// position o ^ ((r / 8) ^ r) mod (C / 8).  The staging writes (one column j of
-// sixteen row blocks: rows 8*cv + j) and the MFMA operand reads (sixteen
-// consecutive rows, one octet each) then spread over the LDS banks.
-template <int C>
-__device__ __forceinline__ int tsw(int row, int key) {
-    constexpr int mask = C / 8 - 1;
-    return ((((key >> 3) ^ (row >> 3) ^ row) & mask) << 3) | (key & 7);
+// Swizzle of the bf16 tiles: a row of NB 16-byte blocks (NB = W / 8 <= 16) keeps
+// its logical block b at position b ^ bswz<NB>(row).  With R = 16 / NB rows in
+// one 256-byte window of the LDS banks and a = row / R, bswz = (2a + a / (NB/2))
+// mod NB: sixteen consecutive rows put one logical block in sixteen different
+// bank groups (row reads of MFMA operands), and four consecutive rows put a pair
+// of blocks (2j, 2j+1) in eight different bank groups (transposed reads).
+template <int NB>
+__device__ __forceinline__ int bswz(int row) {
+    static_assert(NB >= 2 && NB <= 16 && (NB & (NB - 1)) == 0, "blocks per row");
+    constexpr int R = 16 / NB;
+    constexpr int SH = NB == 16 ? 3 : NB == 8 ? 2 : NB == 4 ? 1 : 0;
+    const int a = row / R;
+    return (2 * a + (a >> SH)) & (NB - 1);
+}
+// element offset of logical block b (8 elements) of row r in a swizzled tile W wide
+template <int W>
+__device__ __forceinline__ int boff(int r, int b) {
+    return r * W + ((b ^ bswz<W / 8>(r)) << 3);
+}
+// 8 elements (logical block b) / 4 elements from column c (c % 4 == 0) of row r
+template <int W>
+__device__ __forceinline__ bf16x8 rd8(const bf16 *tile, int r, int b) {
+    return *reinterpret_cast<const bf16x8 *>(tile + boff<W>(r, b));
+}
+template <int W>
+__device__ __forceinline__ bf16x4 rd4(const bf16 *tile, int r, int c) {
+    return *reinterpret_cast<const bf16x4 *>(tile + boff<W>(r, c >> 3) + (c & 7));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Transposed read (ds_read_b64_tr_b16) of a swizzled bf16 tile [keys][W]: within
+// each group of 16 lanes, lane j names 4 consecutive elements (row key_j, columns
+// col0 + 4 (j % 4) ..), and lane i receives column i % 4 of the rows named by
+// lanes i / 4 + 4k, k = 0..3.  With key_j = kb + j / 4 lane l16 receives
+// tile[kb .. kb + 3][col0 + l16]: four keys of one column, the layout of a
+// 4-deep slice of an MFMA operand whose contraction index is the key.
+template <int W>
+__device__ __forceinline__ bf16x4 tr4(const bf16 *tile, int kb, int col0, int l16) {
+    const int key = kb + (l16 >> 2);
+    const int b = (col0 >> 3) + ((l16 & 3) >> 1);
+    const bf16 *p = tile + key * W + ((b ^ bswz<W / 8>(key)) << 3) + 4 * (l16 & 1);
+    const s16x4 v =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(const_cast<bf16 *>(p)));
+    return __builtin_bit_cast(bf16x4, v);
+}
+// the 32-deep operand slice of lane (g, l16): keys kb + 8g .. kb + 8g + 7 of column col0 + l16
+template <int W>
+__device__ __forceinline__ bf16x8 tr8(const bf16 *tile, int kb, int col0, int g, int l16) {
+    const bf16x4 lo = tr4<W>(tile, kb + 8 * g, col0, l16);
+    const bf16x4 hi = tr4<W>(tile, kb + 8 * g + 4, col0, l16);
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 template <typename T, int C, int W, int NT>
@@ -110,8 +153,7 @@ struct Stage {
     static constexpr bool F32 = std::is_same<T, float>::value;
     static constexpr int VEC = 16 / (int)sizeof(T);
     static constexpr int NV = W / VEC;
-    // bf16 rows per item: four, or two where four would leave threads without an item
-    static constexpr int RPI = F32 ? 1 : ((C / 4) * (W / 8) >= NT ? 4 : 2);
+    static constexpr int RPI = 1;  // rows per item
     static constexpr int ITEMS = (C / RPI) * NV;
     static constexpr int PER = (ITEMS + NT - 1) / NT;
     uint4 r[PER][RPI];
@@ -132,14 +174,15 @@ struct Stage {
         }
     }
 
-    // natural layout dst[row][col], optionally through phi.  Rows at or past N
-    // (only in the last chunk) are zeroed; full chunks take a branch-free path.
-    template <bool PHI>
+    // natural layout dst[row][col], optionally through phi; SWZ (bf16 tiles W wide):
+    // blocks swizzled per row (bswz).  Rows at or past N (only in the last chunk)
+    // are zeroed; full chunks take a branch-free path.
+    template <bool PHI, bool SWZ = false>
     __device__ __forceinline__ void store_natural(T *dst, int ld, int row0, int N, int tid) const {
         if (row0 + C <= N)
-            store_natural_impl<PHI, false>(dst, ld, row0, N, tid);
+            store_natural_impl<PHI, false, SWZ>(dst, ld, row0, N, tid);
         else
-            store_natural_impl<PHI, true>(dst, ld, row0, N, tid);
+            store_natural_impl<PHI, true, SWZ>(dst, ld, row0, N, tid);
     }
     // fp32 copy dst[row][col] of the tile (natural layout, no phi); rows at or
     // past N are zeroed.  For fp32 tiles this is store_natural<false>.
@@ -170,8 +213,9 @@ struct Stage {
             }
         }
     }
-    template <bool PHI, bool TAIL>
+    template <bool PHI, bool TAIL, bool SWZ = false>
     __device__ __forceinline__ void store_natural_impl(T *dst, int ld, int row0, int N, int tid) const {
+        static_assert(!SWZ || !F32, "swizzled tiles are bf16");
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
             const int item = tid + p * NT;
@@ -190,63 +234,23 @@ struct Stage {
                     } else {
                         bf16x8 x = __builtin_bit_cast(bf16x8, r[p][i]);
                         bf16x8 y;
+                        if constexpr (!PHI && !TAIL) {
+                            y = x;  // a plain copy
+                        } else {
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const float f = (float)x[j];
-                            y[j] = (bf16)((PHI ? phi(f) : f) * keep);
+                            for (int j = 0; j < 8; ++j) {
+                                const float f = (float)x[j];
+                                y[j] = (bf16)((PHI ? phi(f) : f) * keep);
+                            }
                         }
-                        *reinterpret_cast<bf16x8 *>(dst + row * ld + cv * 8) = y;
+                        const int blk = SWZ ? (cv ^ bswz<NV>(row)) : cv;
+                        *reinterpret_cast<bf16x8 *>(dst + row * ld + blk * 8) = y;
                     }
                 }
             }
         }
     }
 
-    // bf16 only: transposed layout dst[col][row] (and optionally the natural one too)
-    template <bool PHI, bool ALSO_NATURAL>
-    __device__ __forceinline__ void store_transposed(T *dst_t, int ldt, T *dst_n, int ldn, int row0, int N,
-                                                     int tid) const {
-        if (row0 + C <= N)
-            store_transposed_impl<PHI, ALSO_NATURAL, false>(dst_t, ldt, dst_n, ldn, row0, N, tid);
-        else
-            store_transposed_impl<PHI, ALSO_NATURAL, true>(dst_t, ldt, dst_n, ldn, row0, N, tid);
-    }
-    template <bool PHI, bool ALSO_NATURAL, bool TAIL>
-    __device__ __forceinline__ void store_transposed_impl(T *dst_t, int ldt, T *dst_n, int ldn, int row0, int N,
-                                                          int tid) const {
-        static_assert(!F32, "transposed staging is for bf16 operands");
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int item = tid + p * NT;
-            if (ITEMS % NT == 0 || item < ITEMS) {
-                const int rq = item / NV, cv = item % NV;
-                bf16x8 y[RPI];
-#pragma unroll
-                for (int i = 0; i < RPI; ++i) {
-                    const float keep = (!TAIL || row0 + rq * RPI + i < N) ? 1.0f : 0.0f;
-                    bf16x8 x = __builtin_bit_cast(bf16x8, r[p][i]);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const float f = (float)x[j];
-                        y[i][j] = (bf16)((PHI ? phi(f) : f) * keep);
-                    }
-                    if constexpr (ALSO_NATURAL)
-                        *reinterpret_cast<bf16x8 *>(dst_n + (rq * RPI + i) * ldn + cv * 8) = y[i];
-                }
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int row = cv * 8 + j;
-                    if constexpr (RPI == 4) {
-                        bf16x4 t = {y[0][j], y[1][j], y[2][j], y[3][j]};
-                        *reinterpret_cast<bf16x4 *>(dst_t + row * ldt + tsw<C>(row, rq * 4)) = t;
-                    } else {
-                        bf16x2 t = {y[0][j], y[1][j]};
-                        *reinterpret_cast<bf16x2 *>(dst_t + row * ldt + tsw<C>(row, rq * 2)) = t;
-                    }
-                }
-            }
-        }
-    }
 };
 
 
@@ -285,7 +289,7 @@ template <typename T, int D, int M, int C, bool PHI = true>
 struct Engine {
     using G = Cfg<T, D, M, C>;
     static constexpr int DT = G::DT, MTW = G::MTW, RT = G::RT;
-    T *sQ, *sK, *sV, *sKt, *sA;
+    T *sQ, *sK, *sV, *sA;
     float *sz, *szp, *sdenp, *sqz;
     int tid, lane, w, g, l16;
 
@@ -294,7 +298,6 @@ struct Engine {
         sQ = t + G::oQ;
         sK = t + G::oK;
         sV = t + G::oV;
-        sKt = t + G::oKt;
         sA = t + G::oA;
         float *f = reinterpret_cast<float *>(smem + G::fbase);
         sz = f + G::fz;
@@ -317,7 +320,7 @@ struct Engine {
     }
 
     __device__ __forceinline__ void store_q(const Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &st, int row0, int N) const {
-        st.template store_natural<PHI>(sQ, G::LQ, row0, N, tid);
+        st.template store_natural<PHI, !G::F32>(sQ, G::LQ, row0, N, tid);
     }
     __device__ __forceinline__ void store_kv(const Stage<T, C, D, Cfg<T, D, M, C>::THREADS> &stK, const Stage<T, C, M, Cfg<T, D, M, C>::THREADS> &stV, int row0,
                                              int N) const {
@@ -325,14 +328,15 @@ struct Engine {
             stK.template store_natural<PHI>(sK, G::LQ, row0, N, tid);
             stV.template store_natural<false>(sV, G::LV, row0, N, tid);
         } else {
-            stK.template store_transposed<PHI, true>(sKt, G::LT, sK, G::LQ, row0, N, tid);
-            stV.template store_transposed<false, false>(sV, G::LT, nullptr, 0, row0, N, tid);
+            stK.template store_natural<PHI, true>(sK, G::LQ, row0, N, tid);
+            stV.template store_natural<false, true>(sV, G::LV, row0, N, tid);
         }
     }
 
     // Column sums of phi(K_c).  fp32: partial sums over ZROWS rows into szp[q][d].
-    // bf16: row sums of the transposed tile phi(K)^T (a row holds all C keys of one
-    // column d, in permuted octets), 16-byte reads, into szp[d].
+    // bf16: phi(K_c)^T 1 on MFMA (the key-contiguous operand from transposed reads,
+    // a B operand of ones), wavefront w summing the d-tiles w, w + NW, ...; the
+    // result row d of the tile lands in szp[d].
     static constexpr int ZP = G::F32 ? G::NZP : 1;  // partials per column
     __device__ __forceinline__ void z_partials() const {
         if constexpr (G::F32) {
@@ -344,21 +348,18 @@ struct Engine {
                 szp[q * D + d] = s;
             }
         } else {
-            constexpr int TPD = G::THREADS / D < C / 8 ? G::THREADS / D : C / 8;  // threads per column
-            constexpr int OCT = C / 8 / TPD;                                       // octets per thread
-            const int d = tid / TPD, p = tid % TPD;
-            if (TPD * D == G::THREADS || d < D) {
-                const T *row = sKt + d * G::LT + p * OCT * 8;
-                float s = 0.0f;
+            const bf16 one = (bf16)1.0f;
+            for (int dt = w; dt < DT; dt += G::NW) {
+                f32x4 acc = zero4();
+                if constexpr (C % 32 == 0) {
+                    const bf16x8 ones = {one, one, one, one, one, one, one, one};
 #pragma unroll
-                for (int o = 0; o < OCT; ++o) {
-                    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(row + 8 * o);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) s += (float)v[j];
+                    for (int ks = 0; ks < C / 32; ++ks) acc = mma_bf16_k32(tr8<D>(sK, ks * 32, dt * 16, g, l16), ones, acc);
+                } else {
+                    const bf16x4 ones = {one, one, one, one};
+                    acc = mma_bf16_k16(tr4<D>(sK, 4 * g, dt * 16, l16), ones, acc);
                 }
-#pragma unroll
-                for (int sh = TPD / 2; sh > 0; sh >>= 1) s += __shfl_xor(s, sh, 64);
-                if (p == 0) szp[d] = s;
+                if (l16 == 0) *reinterpret_cast<f32x4 *>(szp + dt * 16 + 4 * g) = acc;
             }
         }
     }
@@ -387,36 +388,28 @@ struct Engine {
                 }
             }
         } else {
+            // A = phi(K)^T (rows d, keys), B = V (keys, columns m): both from transposed reads
 #pragma unroll
             for (int i = 0; i < MTW; ++i) {
                 if (!owns(i)) continue;
-                const int vr = mtile(i) * 16 + l16;
+                const int mc = mtile(i) * 16;
+                if constexpr (C % 32 == 0) {
+                    bf16x8 bv[C / 32];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int kr = dt * 16 + l16;
-                    acc[dt][i] = dot_t(sKt + kr * G::LT, kr, sV + vr * G::LT, vr, acc[dt][i]);
+                    for (int ks = 0; ks < C / 32; ++ks) bv[ks] = tr8<M>(sV, ks * 32, mc, g, l16);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                        for (int ks = 0; ks < C / 32; ++ks)
+                            acc[dt][i] = mma_bf16_k32(tr8<D>(sK, ks * 32, dt * 16, g, l16), bv[ks], acc[dt][i]);
+                } else {
+                    const bf16x4 bv = tr4<M>(sV, 4 * g, mc, l16);
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+                        acc[dt][i] = mma_bf16_k16(tr4<D>(sK, 4 * g, dt * 16, l16), bv, acc[dt][i]);
                 }
             }
         }
-    }
-
-    // bf16: acc += A B over the C keys of two transposed (swizzled) rows: lane reads
-    // row `ra` of A and row `rb` of B, contraction slots = keys.
-    __device__ __forceinline__ f32x4 dot_t(const T *a, int ra, const T *b, int rb, f32x4 acc) const {
-        if constexpr (C % 32 == 0) {
-#pragma unroll
-            for (int ks = 0; ks < C / 32; ++ks) {
-                const int key = ks * 32 + 8 * g;
-                const bf16x8 av = *reinterpret_cast<const bf16x8 *>(a + tsw<C>(ra, key));
-                const bf16x8 bv = *reinterpret_cast<const bf16x8 *>(b + tsw<C>(rb, key));
-                acc = mma_bf16_k32(av, bv, acc);
-            }
-        } else {
-            const bf16x4 av = *reinterpret_cast<const bf16x4 *>(a + tsw<C>(ra, 4 * g));
-            const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(b + tsw<C>(rb, 4 * g));
-            acc = mma_bf16_k16(av, bv, acc);
-        }
-        return acc;
     }
 
     // Lower-triangle tiles of A (tile t = w, w+NW, ... in row-major order of (rt, kt<=rt)),
@@ -437,9 +430,9 @@ struct Engine {
             acc[k] = zero4();
             if (G::NA % G::NW == 0 || t < G::NA) {
                 const int rt = tile_row(t), kt = t - rt * (rt + 1) / 2;
-                const T *krow = sK + (kt * 16 + l16) * G::LQ;
-                const T *qrow = sQ + (rt * 16 + l16) * G::LQ;
                 if constexpr (G::F32) {
+                    const T *krow = sK + (kt * 16 + l16) * G::LQ;
+                    const T *qrow = sQ + (rt * 16 + l16) * G::LQ;
                     // contraction index d = g*(D/4) + j: each lane reads a contiguous quarter of the row
 #pragma unroll
                     for (int j4 = 0; j4 < D / 16; ++j4) {
@@ -449,7 +442,16 @@ struct Engine {
                         for (int j = 0; j < 4; ++j) acc[k] = mma_f32(av[j], bv[j], acc[k]);
                     }
                 } else {
-                    acc[k] = tile_dot_bf16<D>(krow, qrow, g, acc[k]);
+                    // contraction slots of lane (g, l16): logical block 4 ks + g of the rows
+                    const int kr = kt * 16 + l16, qr = rt * 16 + l16;
+                    if constexpr (D % 32 == 0) {
+#pragma unroll
+                        for (int ks = 0; ks < D / 32; ++ks)
+                            acc[k] = mma_bf16_k32(rd8<D>(sK, kr, 4 * ks + g), rd8<D>(sQ, qr, 4 * ks + g), acc[k]);
+                    } else {
+                        static_assert(D == 16, "bf16 widths are 16, 32, 64 or 128");
+                        acc[k] = mma_bf16_k16(rd4<D>(sK, kr, 4 * g), rd4<D>(sQ, qr, 4 * g), acc[k]);
+                    }
                 }
             }
         }
@@ -488,7 +490,7 @@ struct Engine {
         constexpr int VW = 16 / (int)sizeof(T);
         const int i = tid / TPR, p = tid % TPR;
         if (G::TPR * C < G::THREADS && i >= C) return;  // whole wavefronts beyond the rows
-        const T *qr = sQ + i * G::LQ + p * EPT;
+        const T *qr = sQ + i * G::LQ + p * EPT;  // fp32 rows are plain
         const float *zr = sz + p * EPT;
         float s = 0.0f;
         if constexpr (EPT % VW == 0) {
@@ -501,16 +503,22 @@ struct Engine {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) s += a[j] * b[j];
                 } else {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(qr + 8 * v);
+                    const bf16x8 a = rd8<D>(sQ, i, (p * EPT) / 8 + v);
                     const f32x4 b0 = *reinterpret_cast<const f32x4 *>(zr + 8 * v);
                     const f32x4 b1 = *reinterpret_cast<const f32x4 *>(zr + 8 * v + 4);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) s += (float)a[j] * b0[j] + (float)a[4 + j] * b1[j];
                 }
             }
+        } else if constexpr (G::F32) {
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) s += qr[j] * zr[j];
         } else {
 #pragma unroll
-            for (int j = 0; j < EPT; ++j) s += to_f32(qr[j]) * zr[j];
+            for (int j = 0; j < EPT; ++j) {
+                const int col = p * EPT + j;
+                s += to_f32(sQ[boff<D>(i, col >> 3) + (col & 7)]) * zr[j];
+            }
         }
 #pragma unroll
         for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
@@ -564,9 +572,7 @@ struct Engine {
 #pragma unroll
                 for (int i = 0; i < MTW; ++i) {
                     if (!owns(i)) continue;
-                    const int vr = mtile(i) * 16 + l16;
-                    const bf16x4 av = *reinterpret_cast<const bf16x4 *>(sV + vr * G::LT + tsw<C>(vr, 4 * g));
-                    o[rt][i] = mma_bf16_k16(av, bv, o[rt][i]);
+                    o[rt][i] = mma_bf16_k16(tr4<M>(sV, 4 * g, mtile(i) * 16, l16), bv, o[rt][i]);
                 }
             } else {
 #pragma unroll
@@ -575,10 +581,7 @@ struct Engine {
 #pragma unroll
                     for (int i = 0; i < MTW; ++i) {
                         if (!owns(i)) continue;
-                        const int vr = mtile(i) * 16 + l16;
-                        const bf16x8 av =
-                            *reinterpret_cast<const bf16x8 *>(sV + vr * G::LT + tsw<C>(vr, kk * 32 + 8 * g));
-                        o[rt][i] = mma_bf16_k32(av, bv, o[rt][i]);
+                        o[rt][i] = mma_bf16_k32(tr8<M>(sV, kk * 32, mtile(i) * 16, g, l16), bv, o[rt][i]);
                     }
                 }
             }
@@ -610,7 +613,7 @@ struct Engine {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
                 const int qrow = rt * 16 + l16;
-                const bf16x4 qv = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + 4 * g);
+                const bf16x4 qv = rd4<D>(sQ, qrow, 4 * g);
 #pragma unroll
                 for (int i = 0; i < MTW; ++i)
                     if (owns(i)) o[rt][i] = mma_bf16_k16(sb[i], qv, o[rt][i]);
@@ -631,8 +634,8 @@ struct Engine {
                 const int qrow = rt * 16 + l16;
 #pragma unroll
                 for (int p = 0; p < DT / 2; ++p) {
-                    const bf16x4 q0 = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + (2 * p) * 16 + 4 * g);
-                    const bf16x4 q1 = *reinterpret_cast<const bf16x4 *>(sQ + qrow * G::LQ + (2 * p + 1) * 16 + 4 * g);
+                    const bf16x4 q0 = rd4<D>(sQ, qrow, (2 * p) * 16 + 4 * g);
+                    const bf16x4 q1 = rd4<D>(sQ, qrow, (2 * p + 1) * 16 + 4 * g);
                     const bf16x8 qv = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
 #pragma unroll
                     for (int i = 0; i < MTW; ++i)
