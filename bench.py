@@ -59,6 +59,10 @@ PROFILE_FILES = {
     HEADLINE: "prefill_bf16_B1H16N65536_D128M128.md",
     DECODE: "decode_f32_256x8_D64M64.md",
     "decode_hbm": "decode_f32_4096x8_D64M64.md",
+    "backward": "backward_f32_B8H8N1024_D64M64.md",
+    "decode_steps": "decode_steps_f32_256x8_T16_D64M64.md",
+    "softmax_scan": "softmax_scan_f32_B8H8N1024_D64M64.md",
+    "features": "features_prf16_f32_B8H8N1024_D64M64.md",
 }
 
 
@@ -222,9 +226,18 @@ def causal_kernel_name(cfg, chunk, segments) -> str:
     return f"{kind}<{t}, {cfg['D']}, {cfg['M']}, {chunk}, true, {ot}{extra}>"
 
 
-def bench_prefill(name, cfg, steps, warmup, dev):
+def bench_prefill(name, cfg, steps, warmup, dev, warm_s=0.0):
     import torch
     step, plan = prefill_runner(cfg, dev)
+    if warm_s > 0:  # untimed launches until the clocks have settled (at least warm_s seconds)
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < warm_s:
+            step(i)
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
     ms = timed(step, steps, warmup, plan["stream"])
     lat = None
     if cfg["N"] * cfg["B"] * cfg["H"] <= 4096:
@@ -584,6 +597,21 @@ def profile_run(workload, dev, launches=8):
         bench_decode_loop(dict(synthetic.WORKLOADS[DECODE], T=256), dev, reps=1)
     elif workload == "decode_hbm":
         bench_decode_loop(dict(DECODE_HBM, T=16), dev, reps=1)
+    elif workload == "backward":
+        bench_backward(dict(synthetic.WORKLOADS["prefill_f32_b8h8_n1024_d64"]), 4, dev)
+    elif workload == "decode_steps":
+        bench_decode_steps(dict(synthetic.WORKLOADS[DECODE]), 16, 4, dev)
+    elif workload == "softmax_scan":
+        bench_softmax_scan(dict(synthetic.WORKLOADS["prefill_f32_b8h8_n1024_d64"]), 4, dev)
+    elif workload == "features":  # the fused launch only
+        c = dict(synthetic.WORKLOADS["prefill_prf16_f32_b8h8_n1024_d64"])
+        B, H, N, D, M, F = (c[k] for k in ("B", "H", "N", "D", "M", "F"))
+        W = torch.from_numpy(ea.draw_projection(F, D, "orthogonal", 0)).to(dev)
+        X = [synthetic.draw_torch(30, t, (B, H, N, D if t < 2 else M), c["sigma"] if t < 2 else 1.0, "f32", dev)
+             for t in range(3)]
+        o = torch.empty((B, H, N, M), device=dev)
+        for _ in range(8):
+            ea.forward_features(X[0], X[1], X[2], W, F, c["feature"], out=o)
     elif workload == "copy512":
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -626,7 +654,7 @@ def main():
 
     cfg = dict(synthetic.WORKLOADS[HEADLINE])
     log(f"headline prefill {cfg}")
-    head = bench_prefill(HEADLINE, cfg, args.steps, args.warmup, dev)
+    head = bench_prefill(HEADLINE, cfg, args.steps, args.warmup, dev, warm_s=0.3)
     log(f"headline: {head}")
     line = {
         "metric": METRIC,
