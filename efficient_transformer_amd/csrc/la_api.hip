@@ -138,6 +138,10 @@ int make_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int causal,
                               : (D * M <= 1024) ? 1024 : (D * M <= 4096) ? 512 : 256;
     int64_t cps = (n_chunks * BH + target_wg - 1) / target_wg;
     if (cps < 1) cps = 1;
+    // a causal head of at most kOnePassMaxChunks chunks stays one segment: splitting
+    // it only adds a look-back chain to a launch-bound call (64 positions at chunk
+    // 16: 12.4 -> 9.5 us per call with one segment instead of four)
+    if (causal && n_chunks <= la::kOnePassMaxChunks) cps = n_chunks;
     int64_t G = (n_chunks + cps - 1) / cps;
     cps = (n_chunks + G - 1) / G;
     G = (n_chunks + cps - 1) / cps;
