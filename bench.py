@@ -585,15 +585,41 @@ def bench_probes(dev, nbytes=1 << 30, reps=5):
 # profile mode: untimed launches of one workload, for rocprofv3
 # ---------------------------------------------------------------------------
 
-def profile_run(workload, dev, launches=8):
+def warm_clocks(dev, seconds=0.3):
+    """Untimed device work (torch's own elementwise kernels, not the library's) until the clocks have
+    settled, so that a profiler's kernel averages see the same clocks as the timed bench."""
+    import torch
+    x = torch.ones(1 << 26, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            x.mul_(1.0)
+        torch.cuda.synchronize()
+    del x
+
+
+def profile_run(workload, dev, launches=16):
     import torch
     import efficient_transformer_amd as ea
     import synthetic
     if workload in synthetic.WORKLOADS and synthetic.WORKLOADS[workload]["kind"] == "prefill":
+        # as the timed bench: the kernel itself for 0.3 s (at most 2048 launches) first; after an idle
+        # spell the long-head kernel runs up to 30 % slow for its first few dozen launches
         step, plan = prefill_runner(dict(synthetic.WORKLOADS[workload]), dev, nsets=1)
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < 0.3 and i < 2048:
+            step(i)
+            i += 1
+            if i % 16 == 0:
+                torch.cuda.synchronize()
         for i in range(launches):
             step(i)
-    elif workload == DECODE:
+        torch.cuda.synchronize()
+        log(f"profile run of {workload} done")
+        return
+    warm_clocks(dev)
+    if workload == DECODE:
         bench_decode_loop(dict(synthetic.WORKLOADS[DECODE], T=256), dev, reps=1)
     elif workload == "decode_hbm":
         bench_decode_loop(dict(DECODE_HBM, T=16), dev, reps=1)
