@@ -31,8 +31,12 @@ constexpr int kCachePolicyAgent = 16;
 using bf16 = __bf16;
 
 // phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (page "Transformers are
-// RNNs", Main findings: elu-based feature map).  Branch free (a select).
-__device__ __forceinline__ float phi(float x) { return x > 0.0f ? x + 1.0f : __expf(x); }
+// RNNs", Main findings: elu-based feature map).  Written as max(x + 1, exp(-|x|)):
+// for x > 0, exp(-x) < 1 < x + 1; for x <= 0, exp(x) >= 1 + x, and -|x| = x.  Four
+// VALU operations (the negated absolute value is a source modifier of the scaling
+// multiply) instead of a compare and a select on top of the same three; -inf
+// maps to exactly 0.
+__device__ __forceinline__ float phi(float x) { return fmaxf(x + 1.0f, __expf(-fabsf(x))); }
 // phi when P, else the identity (the input already holds features).
 template <bool P>
 __device__ __forceinline__ float phi_if(float x) {

@@ -166,9 +166,12 @@ struct Stage {
                 const int rq = item / NV, cv = item % NV;
 #pragma unroll
                 for (int i = 0; i < RPI; ++i) {
-                    // rows past the end re-read the last row (no branch); the stores zero them
+                    // rows past the end re-read the last row (no branch); the stores zero them.
+                    // Nontemporal: each row is streamed through once per pass (the two-phase
+                    // kernel's second pass starts long after the first has left the caches).
                     const int grow = min(row0 + rq * RPI + i, N - 1);
-                    r[p][i] = *reinterpret_cast<const uint4 *>(head + (size_t)grow * W + cv * VEC);
+                    r[p][i] = __builtin_bit_cast(
+                        uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(head + (size_t)grow * W + cv * VEC)));
                 }
             }
         }
