@@ -315,6 +315,15 @@ struct Engine {
     }
 
     __device__ __forceinline__ bool owns(int i) const { return G::MT % G::NW == 0 || w + G::NW * i < G::MT; }
+
+    // z[tid] of the running sums for the phi(q) . z products (thread tid < D): fp32,
+    // or rounded to bf16 (stored packed in the first half of sz) for the bf16 engine
+    __device__ __forceinline__ void set_z(float z) const {
+        if constexpr (G::F32)
+            sz[tid] = z;
+        else
+            reinterpret_cast<bf16 *>(sz)[tid] = (bf16)z;
+    }
     __device__ __forceinline__ int mtile(int i) const { return w + G::NW * i; }
 
     // The upper triangle of A is never written by a_tiles; zero it (all of A) once.
@@ -465,18 +474,24 @@ struct Engine {
                 const int rt = tile_row(t), kt = t - rt * (rt + 1) / 2;
                 f32x4 a = acc[k];
                 // a[r] = A[query = rt*16 + l16][key = kt*16 + 4g + r]
-                float rs = 0.0f;
+                if (kt == rt) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (kt == rt && 4 * g + r > l16) a[r] = 0.0f;
-                    a[r] = round_as<T>(a[r]);
-                    rs += a[r];
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * g + r > l16) a[r] = 0.0f;
                 }
+                float rs = 0.0f;
                 T *arow = sA + (rt * 16 + l16) * G::LA + kt * 16 + 4 * g;
                 if constexpr (G::F32) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) rs += a[r];
                     *reinterpret_cast<f32x4 *>(arow) = a;
                 } else {
-                    bf16x4 v = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+                    // the row sum of the rounded values (those the intra-chunk product uses),
+                    // by two dot2 instructions against ones
+                    const bf16x4 v = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+                    const bf16x2 one2 = {(bf16)1.0f, (bf16)1.0f};
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[0], v[1]}, one2, 0.0f, false);
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, one2, rs, false);
                     *reinterpret_cast<bf16x4 *>(arow) = v;
                 }
                 rs = sum_over_groups(rs);
@@ -506,11 +521,13 @@ struct Engine {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) s += a[j] * b[j];
                 } else {
+                    // packed bf16 pairs of phi(q) and z: two products per dot2 instruction
                     const bf16x8 a = rd8<D>(sQ, i, (p * EPT) / 8 + v);
-                    const f32x4 b0 = *reinterpret_cast<const f32x4 *>(zr + 8 * v);
-                    const f32x4 b1 = *reinterpret_cast<const f32x4 *>(zr + 8 * v + 4);
+                    const bf16x8 b = *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const bf16 *>(sz) + p * EPT + 8 * v);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) s += (float)a[j] * b0[j] + (float)a[4 + j] * b1[j];
+                    for (int j = 0; j < 4; ++j)
+                        s = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a[2 * j], a[2 * j + 1]}, bf16x2{b[2 * j], b[2 * j + 1]}, s,
+                                                            false);
                 }
             }
         } else if constexpr (G::F32) {
@@ -520,7 +537,7 @@ struct Engine {
 #pragma unroll
             for (int j = 0; j < EPT; ++j) {
                 const int col = p * EPT + j;
-                s += to_f32(sQ[boff<D>(i, col >> 3) + (col & 7)]) * zr[j];
+                s += to_f32(sQ[boff<D>(i, col >> 3) + (col & 7)]) * (float)reinterpret_cast<const bf16 *>(sz)[col];
             }
         }
 #pragma unroll
@@ -1002,7 +1019,7 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const 
         __syncthreads();  // LDS free
         st.store_q(e, q, row0, N);
         if (stage_kv) st.store_kv(e, b, row0, N);
-        if (e.tid < D) e.sz[e.tid] = round_as<T>(z);
+        if (e.tid < D) e.set_z(z);
         __syncthreads();
         const int cn = min(c + 1, c1 - 1);
         q.load(Qh, cn * C, N, e.tid);
@@ -1281,7 +1298,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 
     if (single) {
         // the rest of the one-chunk segment: normaliser and the inter-chunk term
-        if (tid < D) e.sz[tid] = round_as<T>(zpre);
+        if (tid < D) e.set_z(zpre);
         __syncthreads();
         e.qz_rows();
         __syncthreads();
@@ -1425,7 +1442,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
             q.store_natural_f32(sRawQ, FL::LX, row0, N, tid);
             b.k.store_natural_f32(sRawK, FL::LX, row0, N, tid);
             b.v.store_natural_f32(e.sV, Gc::LV, row0, N, tid);
-            if (tid < D) e.sz[tid] = z;
+            if (tid < D) e.set_z(z);
             __syncthreads();
             const int PT = (P + 15) / 16, jobs = 2 * Gc::RT * PT;
             for (int jb = e.w; jb < jobs; jb += Gc::NW) {
@@ -1436,7 +1453,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
         } else {
             e.store_q(q, row0, N);
             e.store_kv(b.k, b.v, row0, N);
-            if (tid < D) e.sz[tid] = round_as<T>(z);
+            if (tid < D) e.set_z(z);
         }
         __syncthreads();
         if (j + 1 < NC) {  // compile-time: no load past the last possible step
@@ -1512,7 +1529,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
 
     // finish the rows with the prefix
     if (has_prefix) {
-        if (tid < D) e.sz[tid] = round_as<T>(zpre);
+        if (tid < D) e.set_z(zpre);
         __syncthreads();
         for (int j = 0; j < nc; ++j) {
             e.sQ = sQs + j * C * Gc::LQ;
