@@ -66,6 +66,10 @@ class Oracle:
         L.oracle_feature_map.argtypes = [_dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.oracle_attention_mapped.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64, ctypes.c_int,
                                               ctypes.c_int]
+        L.oracle_backward_mapped.argtypes = [_dp, _dp, _dp, _dp, _dp, _dp, _dp, _i64, _i64, _i64, _i64,
+                                             ctypes.c_int]
+        L.oracle_feature_map_backward.argtypes = [_dp, _dp, _dp, _dp, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int]
         self.L = L
         self.path = path
 
@@ -227,6 +231,38 @@ class Oracle:
         return out, S, z
 
 
+    def backward_mapped(self, Fq, Fk, V, dO, threads: int = 0):
+        """Gradients (dFq, dFk, dV) of causal linear attention on mapped features Fq, Fk [..., N, F]
+        (no feature map applied) for the output gradient dO [..., N, M]."""
+        Fq, Fk, V, dO = _f64(Fq), _f64(Fk), _f64(V), _f64(dO)
+        *lead, N, F = Fq.shape
+        M = V.shape[-1]
+        assert Fk.shape == Fq.shape and V.shape == dO.shape and tuple(V.shape[:-1]) == tuple(Fq.shape[:-1])
+        BH = int(np.prod(lead)) if lead else 1
+        dFq, dFk, dV = np.empty(Fq.shape), np.empty(Fk.shape), np.empty(V.shape)
+        self.L.oracle_backward_mapped(_p(Fq), _p(Fk), _p(V), _p(dO), _p(dFq), _p(dFk), _p(dV), BH, N, F, M, threads)
+        return dFq, dFk, dV
+
+    def feature_map_backward(self, X, W, dOut, F: int, kind: str, normalize: bool = False,
+                             threads: int = 0) -> np.ndarray:
+        """Gradient with respect to X [..., D] of sum(dOut * feature_map(X, W, F, kind, normalize))."""
+        X, dOut = _f64(X), _f64(dOut)
+        D = X.shape[-1]
+        rows = X.size // D if D else 0
+        k = self.FEATURE_KINDS[kind]
+        if k == 0:
+            assert F == D
+            W = np.zeros(1)
+        else:
+            W = _f64(W)
+            assert W.shape == ((F if k == 1 else F // 2), D)
+        assert dOut.shape == (*X.shape[:-1], F)
+        dX = np.empty(X.shape)
+        self.L.oracle_feature_map_backward(_p(X), _p(W), _p(dOut), _p(dX), rows, D, F, k, int(bool(normalize)),
+                                           threads)
+        return dX
+
+
 def _f64(a) -> np.ndarray:
     return np.ascontiguousarray(a, dtype=np.float64)
 
@@ -293,3 +329,11 @@ def feature_map(X, W, F: int, kind: str, normalize: bool = False, threads: int =
 
 def attention_mapped(Fq, Fk, V, causal: bool = True, threads: int = 0):
     return default().attention_mapped(Fq, Fk, V, causal, threads)
+
+
+def backward_mapped(Fq, Fk, V, dO, threads: int = 0):
+    return default().backward_mapped(Fq, Fk, V, dO, threads)
+
+
+def feature_map_backward(X, W, dOut, F: int, kind: str, normalize: bool = False, threads: int = 0):
+    return default().feature_map_backward(X, W, dOut, F, kind, normalize, threads)

@@ -487,3 +487,145 @@ void oracle_attention_mapped(const double *Fq, const double *Fk, const double *V
         free(S); free(z);
     }
 }
+
+/* Gradients of causal linear attention on mapped features (Fq = phi(Q), Fk = phi(K)
+ * already formed, [BH][N][F]; no feature map inside): the running-sum gradients of
+ * oracle_causal_backward with phi the identity, so phi' = 1 and the results are the
+ * gradients with respect to the features themselves (page "Transformers are RNNs",
+ * Proposed method: gradients by running sums in linear time).  dFq, dFk [BH][N][F],
+ * dV [BH][N][M]. */
+void oracle_backward_mapped(const double *Fq, const double *Fk, const double *V, const double *dO,
+                            double *dFq, double *dFk, double *dV,
+                            int64_t BH, int64_t N, int64_t F, int64_t M, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
+    for (int64_t h = 0; h < BH; ++h) {
+        const double *Gh = Fq + h * N * F, *Fh = Fk + h * N * F, *Vh = V + h * N * M, *dOh = dO + h * N * M;
+        double *dGh = dFq + h * N * F, *dFh = dFk + h * N * F, *dVh = dV + h * N * M;
+        double *S = (double *)calloc((size_t)(F * M), sizeof(double));
+        double *z = (double *)calloc((size_t)F, sizeof(double));
+        double *r = (double *)malloc((size_t)(N * M) * sizeof(double));
+        double *c = (double *)malloc((size_t)N * sizeof(double));
+        /* forward running sums: r_i = dout_i / den_i, c_i = -(dout_i . out_i) / den_i,
+         * and dL/dg_i = S_i r_i + c_i z_i */
+        for (int64_t i = 0; i < N; ++i) {
+            const double *g = Gh + i * F, *f = Fh + i * F, *v = Vh + i * M, *dout = dOh + i * M;
+            for (int64_t d = 0; d < F; ++d) {
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += f[d] * v[m];
+                z[d] += f[d];
+            }
+            double den = 0.0;
+            for (int64_t d = 0; d < F; ++d) den += g[d] * z[d];
+            double dot = 0.0;
+            for (int64_t m = 0; m < M; ++m) {
+                double num = 0.0;
+                for (int64_t d = 0; d < F; ++d) num += g[d] * S[d * M + m];
+                dot += dout[m] * (num / den);
+            }
+            for (int64_t m = 0; m < M; ++m) r[i * M + m] = dout[m] / den;
+            c[i] = -dot / den;
+            for (int64_t d = 0; d < F; ++d) {
+                double dg = c[i] * z[d];
+                for (int64_t m = 0; m < M; ++m) dg += S[d * M + m] * r[i * M + m];
+                dGh[i * F + d] = dg;
+            }
+        }
+        /* reverse running sums R_j = sum_{i>=j} g_i r_i^T, w_j = sum_{i>=j} c_i g_i:
+         * dL/df_j = R_j v_j + w_j, dL/dv_j = R_j^T f_j */
+        memset(S, 0, (size_t)(F * M) * sizeof(double));
+        memset(z, 0, (size_t)F * sizeof(double));
+        for (int64_t j = N - 1; j >= 0; --j) {
+            const double *g = Gh + j * F, *f = Fh + j * F, *v = Vh + j * M;
+            for (int64_t d = 0; d < F; ++d) {
+                for (int64_t m = 0; m < M; ++m) S[d * M + m] += g[d] * r[j * M + m];
+                z[d] += c[j] * g[d];
+            }
+            for (int64_t d = 0; d < F; ++d) {
+                double df = z[d];
+                for (int64_t m = 0; m < M; ++m) df += S[d * M + m] * v[m];
+                dFh[j * F + d] = df;
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                double dv = 0.0;
+                for (int64_t d = 0; d < F; ++d) dv += S[d * M + m] * f[d];
+                dVh[j * M + m] = dv;
+            }
+        }
+        free(S); free(z); free(r); free(c);
+    }
+}
+
+/* Gradient of the feature map of oracle_feature_map with respect to its input rows:
+ * dX = J(x)^T dOut row by row, by the chain rule through the definitions there
+ * (page "Stable, Fast and Accurate: Kernelized Attention with Relative Positional
+ * Encoding", Proposed method: the PRF and TRF maps).  With y the (normalised) row:
+ *   elu:  d out_d / d y_d = 1 for y_d > 0, exp(y_d) otherwise;
+ *   PRF:  out_f = exp(w_f . y - |y|^2 / 2) / sqrt(F), so
+ *         d out_f / d y = out_f (w_f - y);
+ *   TRF:  out_p = c sin(a_p), out_{P+p} = c cos(a_p), a_p = w_p . y,
+ *         c = exp(|y|^2 / 2) / sqrt(P), d c / d y = c y, so
+ *         d out_p / d y = y out_p + c cos(a_p) w_p,
+ *         d out_{P+p} / d y = y out_{P+p} - c sin(a_p) w_p.
+ * normalize != 0: y = x / |x|, and d y / d x = (I - y y^T) / |x|; a zero row
+ * (where the normalisation is not differentiable) gets a zero gradient.
+ * X [rows][D]; dOut [rows][F]; dX [rows][D]. */
+void oracle_feature_map_backward(const double *X, const double *W, const double *dOut, double *dX, int64_t rows,
+                                 int64_t D, int64_t F, int kind, int normalize, int threads) {
+    int nt = pick_threads(threads);
+#pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t r = 0; r < rows; ++r) {
+        double *y = (double *)malloc((size_t)D * sizeof(double));
+        double *dy = (double *)calloc((size_t)D, sizeof(double));
+        double sq = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            y[d] = X[r * D + d];
+            sq += y[d] * y[d];
+        }
+        const double len = sqrt(sq);
+        const int scaled = normalize && sq > 0.0;
+        if (scaled) {
+            sq = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                y[d] /= len;
+                sq += y[d] * y[d];
+            }
+        }
+        const double *g = dOut + r * F;
+        if (kind == 0) {
+            for (int64_t d = 0; d < D; ++d) dy[d] = g[d] * (y[d] > 0.0 ? 1.0 : exp(y[d]));
+        } else if (kind == 1) {
+            for (int64_t f = 0; f < F; ++f) {
+                double a = 0.0;
+                for (int64_t d = 0; d < D; ++d) a += W[f * D + d] * y[d];
+                const double out_f = exp(a - 0.5 * sq) / sqrt((double)F);
+                for (int64_t d = 0; d < D; ++d) dy[d] += g[f] * out_f * (W[f * D + d] - y[d]);
+            }
+        } else {
+            const int64_t P = F / 2;
+            const double c = exp(0.5 * sq) / sqrt((double)P);
+            for (int64_t p = 0; p < P; ++p) {
+                double a = 0.0;
+                for (int64_t d = 0; d < D; ++d) a += W[p * D + d] * y[d];
+                const double s = sin(a), co = cos(a);
+                for (int64_t d = 0; d < D; ++d) {
+                    dy[d] += g[p] * (y[d] * c * s + c * co * W[p * D + d]);
+                    dy[d] += g[P + p] * (y[d] * c * co - c * s * W[p * D + d]);
+                }
+            }
+        }
+        double *dx = dX + r * D;
+        if (normalize) {
+            if (scaled) {
+                double ydy = 0.0;
+                for (int64_t d = 0; d < D; ++d) ydy += y[d] * dy[d];
+                for (int64_t d = 0; d < D; ++d) dx[d] = (dy[d] - y[d] * ydy) / len;
+            } else {
+                for (int64_t d = 0; d < D; ++d) dx[d] = 0.0;
+            }
+        } else {
+            for (int64_t d = 0; d < D; ++d) dx[d] = dy[d];
+        }
+        free(y);
+        free(dy);
+    }
+}

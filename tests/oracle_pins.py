@@ -482,8 +482,90 @@ def pin_features(o, fails):
         fails.append(f"prf attention vs softmax: {np.max(np.abs(got - soft)):.3e}")
 
 
+def _central_diff(loss, X, h):
+    """Central differences of a scalar function of the array X, element by element."""
+    g = np.zeros_like(X)
+    for idx in np.ndindex(X.shape):
+        Xp, Xm = X.copy(), X.copy()
+        Xp[idx] += h
+        Xm[idx] -= h
+        g[idx] = (loss(Xp) - loss(Xm)) / (2 * h)
+    return g
+
+
+def pin_feature_gradients(o, fails):
+    """Gradients through random-feature maps:
+
+    * attention on mapped features: fp64 autograd through the quadratic masked form on the
+      features (torch CPU), central differences of the (pinned) mapped forward, and the chain
+      rule back to the elu path: with features phi(Q), phi(K) the gradients times phi' are the
+      causal backward's (pinned above);
+    * the feature maps: central differences of the (pinned) forward map for elu, PRF and TRF,
+      with and without row normalisation, and a zero row under normalisation gets zero."""
+    import torch
+    rng = np.random.default_rng(83)
+
+    def quad(Gt, Ft, Vt):
+        A = torch.tril(Gt @ Ft.T)
+        return (A @ Vt) / A.sum(dim=1, keepdim=True)
+
+    for (N, F, M) in [(1, 3, 2), (7, 5, 3), (20, 16, 6)]:
+        Fq = np.abs(rng.normal(size=(N, F))) + 0.1
+        Fk = np.abs(rng.normal(size=(N, F))) + 0.1
+        V = rng.normal(size=(N, M))
+        dO = rng.normal(size=(N, M))
+        dFq, dFk, dV = o.backward_mapped(Fq[None], Fk[None], V[None], dO[None])
+        Gt, Ft, Vt = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Fq, Fk, V)]
+        (quad(Gt, Ft, Vt) * torch.tensor(dO)).sum().backward()
+        for nm, got, want in (("dFq", dFq[0], Gt.grad.numpy()), ("dFk", dFk[0], Ft.grad.numpy()),
+                              ("dV", dV[0], Vt.grad.numpy())):
+            err = np.max(np.abs(got - want)) / max(np.max(np.abs(want)), 1e-3)
+            if not err <= 1e-11:
+                fails.append(f"mapped backward autograd {nm} N{N} F{F} M{M}: {err:.3e}")
+    N, F, M = 5, 3, 2
+    Fq, Fk = np.abs(rng.normal(size=(N, F))) + 0.2, np.abs(rng.normal(size=(N, F))) + 0.2
+    V, dO = rng.normal(size=(N, M)), rng.normal(size=(N, M))
+    dFq, dFk, dV = o.backward_mapped(Fq[None], Fk[None], V[None], dO[None])
+    args = [Fq, Fk, V]
+    for pos, (nm, G) in enumerate((("Fq", dFq[0]), ("Fk", dFk[0]), ("V", dV[0]))):
+        def loss(X, pos=pos):
+            a = list(args)
+            a[pos] = X
+            return float(np.sum(o.attention_mapped(a[0][None], a[1][None], a[2][None])[0][0] * dO))
+        num = _central_diff(loss, args[pos], 1e-6)
+        err = np.max(np.abs(num - G)) / max(np.max(np.abs(G)), 1e-300)
+        if not err <= 1e-6:
+            fails.append(f"mapped backward finite differences d{nm}: {err:.3e}")
+    Q, K, V = rng.normal(size=(2, 12, 4)), rng.normal(size=(2, 12, 4)), rng.normal(size=(2, 12, 3))
+    dO = rng.normal(size=(2, 12, 3))
+    dFq, dFk, dVm = o.backward_mapped(o.phi(Q), o.phi(K), V, dO)
+    dQ, dK, dV = o.causal_backward(Q, K, V, dO)
+    dphi = lambda x: np.where(x > 0, 1.0, np.exp(x))
+    _close("mapped backward chain dQ", dFq * dphi(Q), dQ, 1e-12, fails)
+    _close("mapped backward chain dK", dFk * dphi(K), dK, 1e-12, fails)
+    _close("mapped backward chain dV", dVm, dV, 1e-12, fails)
+    # the feature maps
+    for (D, F) in [(3, 4), (5, 8)]:
+        X = rng.normal(size=(3, D)) * 0.6
+        W = rng.normal(size=(F, D))
+        for kind, Wk, Fk_ in (("elu", None, D), ("prf", W, F), ("trf", W[:F // 2], F)):
+            for normalize in (False, True):
+                dOut = rng.normal(size=(3, Fk_))
+                got = o.feature_map_backward(X, Wk, dOut, Fk_, kind, normalize)
+                loss = lambda Xv: float(np.sum(o.feature_map(Xv, Wk, Fk_, kind, normalize) * dOut))
+                num = _central_diff(loss, X, 1e-6)
+                err = np.max(np.abs(num - got)) / max(np.max(np.abs(got)), 1e-300)
+                if not err <= 1e-6:
+                    fails.append(f"feature map backward {kind} norm={normalize} D{D} F{Fk_}: {err:.3e}")
+        Z = np.zeros((2, D))
+        for kind, Wk, Fk_ in (("prf", W, F), ("trf", W[:F // 2], F)):
+            g = o.feature_map_backward(Z, Wk, rng.normal(size=(2, Fk_)), Fk_, kind, True)
+            if not np.all(g == 0.0):
+                fails.append(f"feature map backward {kind}: zero row not zero under normalisation")
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_mpmath, pin_invariants, pin_rnn, pin_chunked, pin_continue,
-            pin_backward, pin_softmax_scan, pin_features]
+            pin_backward, pin_softmax_scan, pin_features, pin_feature_gradients]
 
 
 def run_all(o, pins=ALL_PINS):

@@ -66,6 +66,21 @@ MUTANTS = {
                           "for (int64_t d = 0; d < F; ++d) den += f[d] * z[d];"),
     "mapped_noncausal_sums_q": ("const double *f = Kh + j * F, *v = Vh + j * M;",
                                 "const double *f = Qh + j * F, *v = Vh + j * M;"),
+    "mapped_backward_c_sign": ("c[i] = -dot / den;\n            for (int64_t d = 0; d < F; ++d) {",
+                               "c[i] = dot / den;\n            for (int64_t d = 0; d < F; ++d) {"),
+    "mapped_backward_dq_missing_z": ("double dg = c[i] * z[d];\n                for (int64_t m = 0; m < M; ++m) dg += S[d * M + m] * r[i * M + m];\n                dGh",
+                                     "double dg = 0.0;\n                for (int64_t m = 0; m < M; ++m) dg += S[d * M + m] * r[i * M + m];\n                dGh"),
+    "mapped_backward_missing_w": ("double df = z[d];", "double df = 0.0;"),
+    "mapped_backward_dv_uses_g": ("dv += S[d * M + m] * f[d];", "dv += S[d * M + m] * g[d];"),
+    "fmb_prf_drops_minus_y": ("dy[d] += g[f] * out_f * (W[f * D + d] - y[d]);", "dy[d] += g[f] * out_f * W[f * D + d];"),
+    "fmb_prf_scale": ("const double out_f = exp(a - 0.5 * sq) / sqrt((double)F);", "const double out_f = exp(a - 0.5 * sq);"),
+    "fmb_trf_cos_sign": ("dy[d] += g[P + p] * (y[d] * c * co - c * s * W[p * D + d]);",
+                         "dy[d] += g[P + p] * (y[d] * c * co + c * s * W[p * D + d]);"),
+    "fmb_trf_no_magnitude_term": ("dy[d] += g[p] * (y[d] * c * s + c * co * W[p * D + d]);",
+                                  "dy[d] += g[p] * (c * co * W[p * D + d]);"),
+    "fmb_elu_derivative": ("dy[d] = g[d] * (y[d] > 0.0 ? 1.0 : exp(y[d]));", "dy[d] = g[d] * (y[d] > 0.0 ? y[d] + 1.0 : exp(y[d]));"),
+    "fmb_norm_no_projection": ("dx[d] = (dy[d] - y[d] * ydy) / len;", "dx[d] = dy[d] / len;"),
+    "fmb_norm_no_length": ("dx[d] = (dy[d] - y[d] * ydy) / len;", "dx[d] = dy[d] - y[d] * ydy;"),
     "decode_den_uses_k": ("den += oracle_phi1(qh[d]) * zh[d];", "den += oracle_phi1(kh[d]) * zh[d];"),
     "decode_reads_before_update": (
         "        for (int64_t d = 0; d < D; ++d) {\n            double f = oracle_phi1(kh[d]);\n            for (int64_t m = 0; m < M; ++m) Sh[d * M + m] += f * vh[m];\n            zh[d] += f;\n        }\n        double den = 0.0;\n        for (int64_t d = 0; d < D; ++d) den += oracle_phi1(qh[d]) * zh[d];\n        for (int64_t m = 0; m < M; ++m) {\n            double num = 0.0;\n            for (int64_t d = 0; d < D; ++d) num += oracle_phi1(qh[d]) * Sh[d * M + m];\n            oh[m] = num / den;\n        }\n",
