@@ -12,6 +12,7 @@ from .linattn import (  # noqa: F401
     decode_step_features,
     decode_steps,
     feature_map,
+    feature_map_backward,
     forward_chunked,
     forward_chunked_noalloc,
     forward_continue,

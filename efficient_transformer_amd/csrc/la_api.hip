@@ -604,9 +604,9 @@ struct BwdPlan {
     size_t states_bytes = 0, den_bytes = 0, ws_bytes = 0;
 };
 int bwd_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int dtype, BwdPlan *p) {
-    // the gradient is taken through phi = elu + 1; features computed elsewhere are not
-    // covered, and gradients are fp32
-    if (dtype == LA_F32_FEATURES || (dtype & LA_OUT_BF16)) return LA_ERR_UNSUPPORTED;
+    // the gradient is taken through phi = elu + 1, or (LA_F32_FEATURES) with respect
+    // to the features themselves; gradients are fp32
+    if (dtype & LA_OUT_BF16) return LA_ERR_UNSUPPORTED;
     int st = check_shape(B, H, N, D, M, dtype);
     if (st != LA_OK) return st;
     const int64_t BH = B * H;
@@ -840,6 +840,22 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
 }
 
 // ---- feature maps ----------------------------------------------------------
+
+LA_API int la_feature_map_backward(float *dX, const void *X, const float *dOut, int64_t rows, int64_t D, int dtype,
+                                   const float *W, int64_t F, int kind, int flags, void *stream) {
+    if (rows < 0 || D <= 0 || F <= 0) return LA_ERR_INVALID_ARG;
+    if (dtype != LA_F32 && dtype != LA_BF16) return LA_ERR_INVALID_ARG;
+    if (kind != LA_FEATURE_ELU && kind != LA_FEATURE_PRF && kind != LA_FEATURE_TRF) return LA_ERR_INVALID_ARG;
+    if ((flags & ~LA_FEATURE_NORMALIZE) != 0) return LA_ERR_INVALID_ARG;
+    if (kind == LA_FEATURE_ELU && F != D) return LA_ERR_INVALID_ARG;
+    if (!dim_ok(D) || !dim_ok(F)) return LA_ERR_UNSUPPORTED;
+    if (rows > INT64_MAX / 256) return LA_ERR_UNSUPPORTED;
+    if (rows == 0) return LA_OK;
+    if (!dX || !X || !dOut || (kind != LA_FEATURE_ELU && !W)) return LA_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hip_status(la::feature_map_backward(dtype, (int)D, (int)F, kind, X, dOut, W, dX, (long)rows,
+                                               (flags & LA_FEATURE_NORMALIZE) != 0, as_stream(stream)));
+}
 
 LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2, int64_t rows, int64_t D,
                           int dtype, const float *W, int64_t F, int kind, int flags, void *stream) {

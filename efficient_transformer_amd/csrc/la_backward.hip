@@ -1,4 +1,5 @@
-// Backward kernels instantiated for D, M in {16, 32, 64, 128}, fp32 and bf16 inputs.
+// Backward kernels instantiated for D, M in {16, 32, 64, 128}: fp32 and bf16 inputs
+// through phi = elu + 1 (dtype 0, 1), fp32 inputs that already hold features (dtype 2).
 #include "la_backward.hpp"
 #include "la_launch.hpp"
 
@@ -9,9 +10,10 @@ hipError_t backward_dq(int dtype, int D, int M, const void *Q, const void *K, co
                        int G, int CPS, hipStream_t stream) {
 #define X(D_, M_)                                                                                             \
     if (D == D_ && M == M_)                                                                                   \
-        return dtype == 0                                                                                     \
-                   ? run_bwd_dq<float, D_, M_>(Q, K, V, O, dO, fwd_ws, rev_ws, den, dQ, BH, N, G, CPS, stream) \
-                   : run_bwd_dq<bf16, D_, M_>(Q, K, V, O, dO, fwd_ws, rev_ws, den, dQ, BH, N, G, CPS, stream);
+        return dtype == 0   ? run_bwd_dq<float, D_, M_>(Q, K, V, O, dO, fwd_ws, rev_ws, den, dQ, BH, N, G, CPS, stream) \
+               : dtype == 2 ? run_bwd_dq<float, D_, M_, false>(Q, K, V, O, dO, fwd_ws, rev_ws, den, dQ, BH, N, G, CPS,  \
+                                                              stream)                                                  \
+                            : run_bwd_dq<bf16, D_, M_>(Q, K, V, O, dO, fwd_ws, rev_ws, den, dQ, BH, N, G, CPS, stream);
 #define XM(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
     XM(16) XM(32) XM(64) XM(128)
 #undef XM
@@ -24,9 +26,10 @@ hipError_t backward_dkv(int dtype, int D, int M, const void *Q, const void *K, c
                         int G, int CPS, hipStream_t stream) {
 #define X(D_, M_)                                                                                            \
     if (D == D_ && M == M_)                                                                                  \
-        return dtype == 0                                                                                    \
-                   ? run_bwd_dkv<float, D_, M_>(Q, K, V, O, dO, rev_ws, den, dK, dV, BH, N, G, CPS, stream) \
-                   : run_bwd_dkv<bf16, D_, M_>(Q, K, V, O, dO, rev_ws, den, dK, dV, BH, N, G, CPS, stream);
+        return dtype == 0   ? run_bwd_dkv<float, D_, M_>(Q, K, V, O, dO, rev_ws, den, dK, dV, BH, N, G, CPS, stream) \
+               : dtype == 2 ? run_bwd_dkv<float, D_, M_, false>(Q, K, V, O, dO, rev_ws, den, dK, dV, BH, N, G, CPS,  \
+                                                               stream)                                              \
+                            : run_bwd_dkv<bf16, D_, M_>(Q, K, V, O, dO, rev_ws, den, dK, dV, BH, N, G, CPS, stream);
 #define XM(D_) X(D_, 16) X(D_, 32) X(D_, 64) X(D_, 128)
     XM(16) XM(32) XM(64) XM(128)
 #undef XM

@@ -11,6 +11,9 @@
 //   df_j = R_j v_j + w_j,   dv_j = R_j^T f_j          (reverse sums, i >= j)
 // with R_j = sum_{i>=j} g_i r_i^T and w_j = sum_{i>=j} c_i g_i;
 // dq = dg * phi'(q), dk = df * phi'(k), and phi'(x) = min(phi(x), 1).
+// Inputs that already hold features (PHI = false, for example random features
+// formed by the feature-map kernel) get dg and df themselves: the gradients with
+// respect to the features, which the feature map's own backward carries on.
 //
 // Chunked form, chunk c of C rows, masks keep i >= j:
 //   dG_c = tril(R_c V_c^T + c 1^T) F_c + R_c S_prev^T + c z_prev^T
@@ -252,7 +255,7 @@ struct BwdEngine {
 // ---------------------------------------------------------------------------
 // dQ: walk the segment's chunks forward from (S_prev, z_prev).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                              const T *__restrict__ V, const float *__restrict__ O,
                                                              const float *__restrict__ dO,
@@ -303,8 +306,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const T *__restr
     for (int c = c0; c < c1; ++c) {
         const int row0 = c * C;
         __syncthreads();
-        ld.q.template store<true>(e.sG, Gc::LD, row0, N, tid);
-        ld.k.template store<true>(e.sF, Gc::LD, row0, N, tid);
+        ld.q.template store<PHI>(e.sG, Gc::LD, row0, N, tid);
+        ld.k.template store<PHI>(e.sF, Gc::LD, row0, N, tid);
         ld.v.template store<false>(e.sV, Gc::LM, row0, N, tid);
         ld.o.template store<false>(e.sO, Gc::LM, row0, N, tid);
         ld.dout.template store<false>(e.sR, Gc::LM, row0, N, tid);
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const T *__restr
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float dg = acc[r] + ci * e.sZ[dt * 16 + 4 * e.g + r];
-                    outv[r] = dg * fminf(gq[r], 1.0f);
+                    outv[r] = PHI ? dg * fminf(gq[r], 1.0f) : dg;
                 }
                 if (grow < N) *reinterpret_cast<f32x4 *>(dQ + hq + (size_t)grow * D + dt * 16 + 4 * e.g) = outv;
             }
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_kernel(const T *__restr
 // ---------------------------------------------------------------------------
 // dK, dV: walk the segment's chunks backward from (R_next, w_next).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(const T *__restrict__ Q, const T *__restrict__ K,
                                                               const T *__restrict__ V, const float *__restrict__ O,
                                                               const float *__restrict__ dO,
@@ -485,8 +488,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(const T *__rest
     for (int c = c1 - 1; c >= c0; --c) {
         const int row0 = c * C;
         __syncthreads();
-        ld.q.template store<true>(e.sG, Gc::LD, row0, N, tid);
-        ld.k.template store<true>(e.sF, Gc::LD, row0, N, tid);
+        ld.q.template store<PHI>(e.sG, Gc::LD, row0, N, tid);
+        ld.k.template store<PHI>(e.sF, Gc::LD, row0, N, tid);
         ld.v.template store<false>(e.sV, Gc::LM, row0, N, tid);
         ld.o.template store<false>(e.sO, Gc::LM, row0, N, tid);
         ld.dout.template store<false>(e.sR, Gc::LM, row0, N, tid);
@@ -537,7 +540,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dkv_kernel(const T *__rest
                 const f32x4 fk = *reinterpret_cast<const f32x4 *>(e.sF + jrow * Gc::LD + dt * 16 + 4 * e.g);
                 f32x4 outv;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) outv[r] = (acc[r] + e.sZ[dt * 16 + 4 * e.g + r]) * fminf(fk[r], 1.0f);
+                for (int r = 0; r < 4; ++r)
+                    outv[r] = (acc[r] + e.sZ[dt * 16 + 4 * e.g + r]) * (PHI ? fminf(fk[r], 1.0f) : 1.0f);
                 if (grow < N) *reinterpret_cast<f32x4 *>(dK + hq + (size_t)grow * D + dt * 16 + 4 * e.g) = outv;
             }
         }
@@ -612,20 +616,20 @@ __global__ __launch_bounds__(256) void bwd_rev_scan_kernel(float *ws, int E, int
     h[(size_t)G_ * E + x] = acc;  // total
 }
 
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 hipError_t run_bwd_dq(const void *Q, const void *K, const void *V, const float *O, const float *dO,
                       const float *fwd_ws, float *rev_ws, float *den, float *dQ, int BH, int N, int G_, int CPS,
                       hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, M>), dim3((unsigned)(BH * G_)), dim3(kBwdThreads), 0, stream,
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, M, PHI>), dim3((unsigned)(BH * G_)), dim3(kBwdThreads), 0, stream,
                        (const T *)Q, (const T *)K, (const T *)V, O, dO, fwd_ws, rev_ws, den, dQ, N, G_, CPS);
     return hipGetLastError();
 }
 
-template <typename T, int D, int M>
+template <typename T, int D, int M, bool PHI = true>
 hipError_t run_bwd_dkv(const void *Q, const void *K, const void *V, const float *O, const float *dO,
                        const float *rev_ws, const float *den, float *dK, float *dV, int BH, int N, int G_, int CPS,
                        hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, M>), dim3((unsigned)(BH * G_)), dim3(kBwdThreads), 0, stream,
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, M, PHI>), dim3((unsigned)(BH * G_)), dim3(kBwdThreads), 0, stream,
                        (const T *)Q, (const T *)K, (const T *)V, O, dO, rev_ws, den, dK, dV, N, G_, CPS);
     return hipGetLastError();
 }

@@ -223,4 +223,174 @@ hipError_t feature_map(int dtype, int D, int F, int kind, const void *X, float *
                                : feature_map_t<float>(D, F, kind, X, out, X2, out2, W, rows, norm, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Gradient of the map with respect to its input rows, dX = J(x)^T dOut row by row
+// (the chain rule through the definitions above).  With y the (normalised) row:
+//   elu: dy_d = dout_d * (1 for y_d > 0, exp(y_d) otherwise);
+//   PRF: d out_p / dy = out_p (w_p - y), so dy = W^T a - y sum_p a_p, a_p = dout_p out_p;
+//   TRF: with out_p = c sin(u_p), out_{P+p} = c cos(u_p), u_p = w_p . y, dc/dy = c y:
+//        dy = W^T b + y sum_p (dout_p out_p + dout_{P+p} out_{P+p}),
+//        b_p = dout_p out_{P+p} - dout_{P+p} out_p;
+//   NORM: y = x / |x|, dx = (dy - y (y . dy)) / |x|; a zero row gets zero.
+// One wavefront per row (lanes over the projections for u = W y, then over the
+// input columns for W^T b); W is staged in LDS once per workgroup with rows of
+// D + 1 floats, so that lanes reading one column of W (one row each) and lanes
+// reading one row of W hit distinct banks.  Not a contraction that pays on MFMA
+// at one row per wavefront; the attention backward dominates the training step.
+// ---------------------------------------------------------------------------
+constexpr int kFmbThreads = 256;
+constexpr int kFmbWaves = kFmbThreads / 64;
+
+__device__ __forceinline__ float fmb_wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+template <typename T, int D, int F, int KIND, bool NORM>
+__global__ __launch_bounds__(kFmbThreads) void feature_map_backward_kernel(const T *__restrict__ X,
+                                                                         const float *__restrict__ dOut,
+                                                                         const float *__restrict__ W,
+                                                                         float *__restrict__ dX, long rows) {
+    constexpr int P = KIND == 2 ? F / 2 : F;  // projections (elu: unused)
+    constexpr int LW = D + 1;
+    constexpr int DL = (D + 63) / 64;  // input columns per lane
+    constexpr int PL = (P + 63) / 64;  // projections per lane
+    __shared__ float sW[KIND == 0 ? 1 : P * LW];
+    __shared__ float sy[kFmbWaves][D];
+    __shared__ float sb[kFmbWaves][KIND == 0 ? 1 : P];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if constexpr (KIND != 0) {
+        for (int e = tid; e < P * D; e += kFmbThreads) sW[(e / D) * LW + e % D] = W[e];
+        __syncthreads();
+    }
+    for (long row = (long)blockIdx.x * kFmbWaves + w; row < rows; row += (long)gridDim.x * kFmbWaves) {
+        float y[DL];
+        float sq = 0.0f;
+#pragma unroll
+        for (int j = 0; j < DL; ++j) {
+            const int d = lane + 64 * j;
+            y[j] = d < D ? to_f32<T>(X[row * D + d]) : 0.0f;
+            sq += y[j] * y[j];
+        }
+        sq = fmb_wave_sum(sq);
+        const float len = sqrtf(sq);
+        const bool scaled = NORM && sq > 0.0f;
+        if (scaled) {
+            sq = 0.0f;
+#pragma unroll
+            for (int j = 0; j < DL; ++j) {
+                y[j] /= len;
+                sq += y[j] * y[j];
+            }
+            sq = fmb_wave_sum(sq);
+        }
+        const float *g = dOut + row * F;
+        float dy[DL];
+        if constexpr (KIND == 0) {
+#pragma unroll
+            for (int j = 0; j < DL; ++j) {
+                const int d = lane + 64 * j;
+                dy[j] = d < D ? g[d] * (y[j] > 0.0f ? 1.0f : __expf(y[j])) : 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < DL; ++j)
+                if (lane + 64 * j < D) sy[w][lane + 64 * j] = y[j];
+            __builtin_amdgcn_wave_barrier();
+            // projections u_p = w_p . y (lanes over p), then the coefficients
+            float ys = 0.0f;  // sum over the own projections of the coefficient of y
+#pragma unroll
+            for (int j = 0; j < PL; ++j) {
+                const int pp = lane + 64 * j;
+                if (pp < P) {
+                    float u = 0.0f;
+#pragma unroll 8
+                    for (int d = 0; d < D; ++d) u += sW[pp * LW + d] * sy[w][d];
+                    if constexpr (KIND == 1) {
+                        const float o = __expf(u - 0.5f * sq) * (1.0f / sqrtf((float)F));
+                        const float a = g[pp] * o;
+                        sb[w][pp] = a;
+                        ys -= a;
+                    } else {
+                        const float c = __expf(0.5f * sq) * (1.0f / sqrtf((float)P));
+                        const float os = c * sinf(u), oc = c * cosf(u);
+                        const float gs = g[pp], gc = g[P + pp];
+                        sb[w][pp] = gs * oc - gc * os;
+                        ys += gs * os + gc * oc;
+                    }
+                }
+            }
+            ys = fmb_wave_sum(ys);
+            __builtin_amdgcn_wave_barrier();
+            // dy = W^T b + y * ys (lanes over d)
+#pragma unroll
+            for (int j = 0; j < DL; ++j) {
+                const int d = lane + 64 * j;
+                float acc = 0.0f;
+                if (d < D) {
+#pragma unroll 8
+                    for (int pp = 0; pp < P; ++pp) acc += sb[w][pp] * sW[pp * LW + d];
+                }
+                dy[j] = d < D ? acc + y[j] * ys : 0.0f;
+            }
+            __builtin_amdgcn_wave_barrier();  // sy, sb reused by this wavefront's next row
+        }
+        if constexpr (NORM) {
+            float ydy = 0.0f;
+#pragma unroll
+            for (int j = 0; j < DL; ++j) ydy += y[j] * dy[j];
+            ydy = fmb_wave_sum(ydy);
+#pragma unroll
+            for (int j = 0; j < DL; ++j) dy[j] = scaled ? (dy[j] - y[j] * ydy) / len : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < DL; ++j) {
+            const int d = lane + 64 * j;
+            if (d < D) dX[row * D + d] = dy[j];
+        }
+    }
+}
+
+template <typename T, int D, int F, int KIND>
+hipError_t run_feature_map_backward(const void *X, const float *dOut, const float *W, float *dX, long rows, bool norm,
+                                    hipStream_t stream) {
+    if constexpr (KIND == 0 && D != F) {
+        return hipErrorInvalidValue;
+    } else {
+        if (rows <= 0) return hipSuccess;
+        const long want = (rows + kFmbWaves - 1) / kFmbWaves;
+        const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+        if (norm)
+            hipLaunchKernelGGL((feature_map_backward_kernel<T, D, F, KIND, true>), dim3(grid), dim3(kFmbThreads), 0,
+                               stream, (const T *)X, dOut, W, dX, rows);
+        else
+            hipLaunchKernelGGL((feature_map_backward_kernel<T, D, F, KIND, false>), dim3(grid), dim3(kFmbThreads), 0,
+                               stream, (const T *)X, dOut, W, dX, rows);
+        return hipGetLastError();
+    }
+}
+
+template <typename T>
+hipError_t feature_map_backward_t(int D, int F, int kind, const void *X, const float *dOut, const float *W, float *dX,
+                                  long rows, bool norm, hipStream_t stream) {
+#define X_(D_, F_)                                                                                              \
+    if (D == D_ && F == F_) {                                                                                   \
+        if (kind == 1) return run_feature_map_backward<T, D_, F_, 1>(X, dOut, W, dX, rows, norm, stream);        \
+        if (kind == 2) return run_feature_map_backward<T, D_, F_, 2>(X, dOut, W, dX, rows, norm, stream);        \
+        if (kind == 0) return run_feature_map_backward<T, D_, F_, 0>(X, dOut, W, dX, rows, norm, stream);        \
+    }
+#define XF_(D_) X_(D_, 16) X_(D_, 32) X_(D_, 64) X_(D_, 128)
+    XF_(16) XF_(32) XF_(64) XF_(128)
+#undef XF_
+#undef X_
+    return hipErrorInvalidValue;
+}
+
+hipError_t feature_map_backward(int dtype, int D, int F, int kind, const void *X, const float *dOut, const float *W,
+                                float *dX, long rows, bool norm, hipStream_t stream) {
+    return dtype == kDtypeBf16 ? feature_map_backward_t<bf16>(D, F, kind, X, dOut, W, dX, rows, norm, stream)
+                               : feature_map_backward_t<float>(D, F, kind, X, dOut, W, dX, rows, norm, stream);
+}
+
 }  // namespace la

@@ -97,6 +97,9 @@ hipError_t decode_any(int dtype, int D, int M, float *S, float *z, const void *q
 // trigonometric; X2 / out2 optional (a second tensor in the same launch).
 hipError_t feature_map(int dtype, int D, int F, int kind, const void *X, float *out, const void *X2, float *out2,
                        const float *W, long rows, bool norm, hipStream_t stream);
+// Its gradient with respect to the rows of X: dX [rows][D] fp32 from dOut [rows][F].
+hipError_t feature_map_backward(int dtype, int D, int F, int kind, const void *X, const float *dOut, const float *W,
+                                float *dX, long rows, bool norm, hipStream_t stream);
 
 // bf16 inputs, bf16 outputs (la_bf16out.hip)
 hipError_t prefill_fused_bf16o(int D, int M, int C, const void *Q, const void *K, const void *V, void *out, void *ws,

@@ -58,6 +58,7 @@ SIGNATURES = {
     "la_decode_step": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_decode_steps": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "la_feature_map": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp, _i64, _int, _int, _vp]),
+    "la_feature_map_backward": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _vp, _i64, _int, _int, _vp]),
     "la_decode_step_features": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp, _i64, _int,
                                        _int, _vp]),
     "la_forward_features_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64, _int]),
@@ -445,8 +446,10 @@ def decode_steps(S, z, q, k, v, out=None, stream=None, features=False):
     return out
 
 
-def backward(Q, K, V, out, dout, workspace=None, stream=None):
-    """Gradients (dQ, dK, dV) of causal attention; out is the forward's output."""
+def backward(Q, K, V, out, dout, workspace=None, stream=None, features=False):
+    """Gradients (dQ, dK, dV) of causal attention; out is the forward's output.
+    features=True: Q, K (float32) hold features, and dQ, dK are the gradients with respect
+    to them (feature_map_backward carries them on to the raw rows)."""
     import torch
     B, H, N, D = Q.shape
     M = V.shape[-1]
@@ -455,7 +458,7 @@ def backward(Q, K, V, out, dout, workspace=None, stream=None):
     _require(V, "V", (B, H, N, M), Q.dtype, dev)
     _require(out, "out", (B, H, N, M), torch.float32, dev)
     _require(dout, "dout", (B, H, N, M), torch.float32, dev)
-    dt = _dtype_code(Q)
+    dt = _dtype_code(Q, features)
     need = int(lib().la_backward_workspace_bytes(B, H, N, D, M, dt))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -510,6 +513,28 @@ def softmax_step(m, u, w, q, k, v, out=None, stream=None):
 
 
 FEATURE_KINDS = {"elu": LA_FEATURE_ELU, "prf": LA_FEATURE_PRF, "trf": LA_FEATURE_TRF}
+
+
+def feature_map_backward(X, dout, W, F, kind="prf", normalize=False, dX=None, stream=None):
+    """Gradient with respect to X [..., D] (float32 or bfloat16) of sum(dout * feature_map(X, W, F, kind,
+    normalize)), dout [..., F] float32 -> float32 [..., D]."""
+    import torch
+    D = X.shape[-1]
+    dev = X.device
+    _require(X, "X", tuple(X.shape), None, dev)
+    k = FEATURE_KINDS[kind]
+    if k != LA_FEATURE_ELU:
+        _require(W, "W", ((F if k == LA_FEATURE_PRF else F // 2), D), torch.float32, dev)
+    _require(dout, "dout", (*X.shape[:-1], F), torch.float32, dev)
+    if dX is None:
+        dX = torch.empty(tuple(X.shape), dtype=torch.float32, device=dev)
+    _require(dX, "dX", tuple(X.shape), torch.float32, dev)
+    rows = X.numel() // D if D else 0
+    st = lib().la_feature_map_backward(_ptr(dX), _ptr(X), _ptr(dout), rows, D, _dtype_code(X),
+                                       _ptr(W) if k != LA_FEATURE_ELU else None, F, k,
+                                       LA_FEATURE_NORMALIZE if normalize else 0, _stream(stream, dev))
+    _check(st, "la_feature_map_backward")
+    return dX
 
 
 def feature_map(X, W, F, kind="prf", normalize=False, out=None, X2=None, out2=None, stream=None):

@@ -62,8 +62,9 @@ enum la_status {
 /* LA_F32_FEATURES: fp32 Q and K rows that already hold the features phi(q),
  * phi(k) (for example from la_feature_map); the kernels then apply no feature
  * map, D is the feature dimension, and V is fp32.  Accepted by the forward
- * entry points, the segment stages and the decode entry points; not by
- * la_backward_chunked (LA_ERR_UNSUPPORTED) or the softmax scan. */
+ * entry points, the segment stages, the decode entry points and
+ * la_backward_chunked (which then returns the gradients with respect to the
+ * features); not by the softmax scan. */
 /* LA_BF16 | LA_OUT_BF16: bf16 inputs and bf16 outputs.  The forward entry
  * points (la_forward_chunked, la_forward_continue, la_forward_fused,
  * la_forward_onepass, la_segment_outputs; la_segment_states ignores the flag)
@@ -312,6 +313,10 @@ LA_API int la_decode_step(float *S, float *z, const void *q, const void *k, cons
  * out: the forward's output [B][H][N][M] fp32 (from la_forward_chunked, causal);
  * dout [B][H][N][M] fp32; dQ, dK [B][H][N][D] and dV [B][H][N][M] fp32, fully
  * written.  Q, K, V as for the forward (fp32 or bf16); all arithmetic fp32.
+ * dtype LA_F32_FEATURES: Q and K hold features phi(q), phi(k) (fp32, V fp32,
+ * D the feature dimension); phi' is then 1, so dQ and dK are the gradients with
+ * respect to those features (la_feature_map_backward carries them on to the
+ * raw rows).  LA_OUT_BF16 is refused.
  * workspace: at least la_backward_workspace_bytes(...) bytes, no
  * initialisation needed (every byte the call reads it writes first).
  * Five kernels on `stream`: segment states, their scan, dQ (with the reverse
@@ -401,6 +406,23 @@ enum la_feature_kind { LA_FEATURE_ELU = 0, LA_FEATURE_PRF = 1, LA_FEATURE_TRF = 
 enum { LA_FEATURE_NORMALIZE = 1 };
 LA_API int la_feature_map(float *out, const void *X, float *out2, const void *X2, int64_t rows, int64_t D,
                           int dtype, const float *W, int64_t F, int kind, int flags, void *stream);
+
+/* Gradient of la_feature_map with respect to its input rows: dX = J(x)^T dOut
+ * for every row x of X, where J is the Jacobian of the map (same X, dtype, W, F,
+ * kind and flags as the forward call).  By the chain rule through the
+ * definitions above (page "Stable, Fast and Accurate: Kernelized Attention with
+ * Relative Positional Encoding", Proposed method): for PRF
+ * d phi_p / dx = phi_p (w_p - x); for TRF the magnitude c contributes c x and
+ * the angle c cos / -c sin times w_p; elu: 1 for x > 0, exp(x) otherwise; with
+ * LA_FEATURE_NORMALIZE the unit-length scaling contributes (I - y y^T) / |x|
+ * (y = x / |x|), and a zero row gets a zero gradient.  dOut [rows][F] fp32,
+ * dX [rows][D] fp32 (4-byte alignment suffices).  Together with
+ * la_backward_chunked on LA_F32_FEATURES inputs (the gradients with respect to
+ * the features) this gives the gradients of attention through a random-feature
+ * map.  D and F as for la_feature_map.
+ */
+LA_API int la_feature_map_backward(float *dX, const void *X, const float *dOut, int64_t rows, int64_t D, int dtype,
+                                   const float *W, int64_t F, int kind, int flags, void *stream);
 
 /* One recurrent step (as la_decode_step) on raw rows with the random-feature
  * map formed inside the kernel: q, k [B][H][D] raw rows and v [B][H][M], all of

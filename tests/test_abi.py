@@ -306,15 +306,36 @@ def test_feature_map_checks(L):
     assert f(None, None, None, None, 0, 64, 0, None, 16, 1, 0, None) == L.LA_OK  # no rows
 
 
+def test_feature_map_backward_checks(L):
+    f = L.lib().la_feature_map_backward
+    # dX, X, dOut, rows, D, dtype, W, F, kind, flags, stream
+    assert f(FAKE, FAKE, FAKE, 100, 64, 0, FAKE, 16, 3, 0, None) == L.LA_ERR_INVALID_ARG  # kind
+    assert f(FAKE, FAKE, FAKE, 100, 64, 0, FAKE, 16, 1, 2, None) == L.LA_ERR_INVALID_ARG  # flag
+    assert f(FAKE, FAKE, FAKE, 100, 64, 0, None, 32, 0, 0, None) == L.LA_ERR_INVALID_ARG  # elu: F != D
+    assert f(FAKE, FAKE, FAKE, 100, 64, 2, FAKE, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG  # dtype
+    assert f(FAKE, FAKE, FAKE, 100, 48, 0, FAKE, 16, 1, 0, None) == L.LA_ERR_UNSUPPORTED  # D
+    assert f(FAKE, FAKE, FAKE, 100, 64, 0, FAKE, 24, 1, 0, None) == L.LA_ERR_UNSUPPORTED  # F
+    assert f(FAKE, FAKE, FAKE, 100, 64, 0, None, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG  # PRF needs W
+    assert f(None, FAKE, FAKE, 100, 64, 0, FAKE, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG  # dX
+    assert f(FAKE, FAKE, FAKE, -1, 64, 0, FAKE, 16, 1, 0, None) == L.LA_ERR_INVALID_ARG
+    assert f(None, None, None, 0, 64, 0, None, 16, 1, 0, None) == L.LA_OK  # no rows
+
+
 def test_feature_inputs_dtype(L):
-    """LA_F32_FEATURES plans like fp32, is refused by the backward pass and the softmax scan."""
+    """LA_F32_FEATURES plans like fp32 (forward and backward), is refused by the softmax scan."""
     for D in (16, 64, 128):
         for M in (16, 64, 128):
             assert L.forward_plan(2, 3, 1000, D, M, 1, L.LA_F32_FEATURES, 0) == \
                 L.forward_plan(2, 3, 1000, D, M, 1, L.LA_F32, 0)
     lib = L.lib()
-    assert lib.la_backward_workspace_bytes(2, 2, 100, 64, 64, L.LA_F32_FEATURES) == 0
+    for (N, D, M) in ((100, 64, 64), (5000, 16, 128), (70000, 128, 32)):
+        want = lib.la_backward_workspace_bytes(2, 2, N, D, M, L.LA_F32)
+        assert want > 0 and lib.la_backward_workspace_bytes(2, 2, N, D, M, L.LA_F32_FEATURES) == want
+    # refused before anything runs: a workspace one byte short, and a width without kernels
+    need = lib.la_backward_workspace_bytes(2, 2, 100, 64, 64, L.LA_F32_FEATURES)
     assert lib.la_backward_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 100, 64, 64,
+                                   L.LA_F32_FEATURES, FAKE, need - 1, None) == L.LA_ERR_WORKSPACE
+    assert lib.la_backward_chunked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 100, 48, 64,
                                    L.LA_F32_FEATURES, FAKE, 1 << 30, None) == L.LA_ERR_UNSUPPORTED
     assert lib.la_softmax_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, L.LA_F32_FEATURES,
                                None) == L.LA_ERR_INVALID_ARG
