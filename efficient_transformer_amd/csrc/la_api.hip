@@ -42,6 +42,11 @@ struct Plan {
     bool padded = false;
     int64_t Dk = 0, Mk = 0;
     size_t inner_ws = 0, oQ = 0, oK = 0, oV = 0, oO = 0, oS = 0, oZ = 0;
+    // la_forward_features in two launches (map, then attention on the features held
+    // in the workspace at oQ, oK; bf16 V widened to fp32 at oV): the attention's plan
+    bool split = false;
+    int att_chunk = 0, att_segments = 0, att_cps = 0;
+    bool att_onepass = false;
 };
 
 // Validate the shape arguments shared by the prefill entry points.
@@ -772,9 +777,34 @@ int features_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t
     if (B * H == 0 || N == 0) return LA_OK;
     if (!causal) return la::prefill_features_noncausal_supported((int)D, (int)F, (int)M) ? LA_OK : LA_ERR_UNSUPPORTED;
     // the one-pass kernel where its segments fit (at most four chunks) and its LDS
-    // does, else the two-phase kernel (any segment length, less LDS)
+    // does; otherwise two launches: the map into the workspace, then the attention
+    // kernels on the features.  (The fused two-phase kernel forms the projections of
+    // the k rows in both of its phases, and measured slower than the two launches:
+    // 204 against 193 us at B1 H8 N65536 D64 F16 M64, 56.9 against 51.5 us at
+    // B8 H8 N1024 D64 F64 M64.)
     if (p->onepass && !la::prefill_features_supported(true, (int)D, (int)F, (int)M)) p->onepass = false;
     if (!p->onepass && !la::prefill_features_supported(false, (int)D, (int)F, (int)M)) return LA_ERR_UNSUPPORTED;
+    if (!p->onepass) {
+        Plan a;
+        st = make_plan(B, H, N, F, M, 1, LA_F32_FEATURES, 0, &a);
+        if (st != LA_OK) return st;
+        const size_t rows = (size_t)(B * H) * (size_t)N;
+        p->split = true;
+        p->att_chunk = a.chunk;
+        p->att_segments = a.segments;
+        p->att_cps = a.chunks_per_segment;
+        p->att_onepass = a.onepass;
+        // the attention's look-back header stays at the front of the workspace
+        size_t off = round256(a.ws_bytes > 256 ? a.ws_bytes : 256);
+        p->inner_ws = a.ws_bytes;
+        p->oQ = off;
+        off += round256(rows * (size_t)F * 4);
+        p->oK = off;
+        off += round256(rows * (size_t)F * 4);
+        p->oV = off;  // bf16 V widened (fp32 V is read in place)
+        off += round256(rows * (size_t)M * 4);
+        p->ws_bytes = off;
+    }
     return LA_OK;
 }
 }  // namespace
@@ -825,6 +855,26 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
     if (p.ws_bytes > 0 && !aligned16(workspace)) return LA_ERR_INVALID_ARG;
     (void)hipGetLastError();
     const int norm = (flags & LA_FEATURE_NORMALIZE) != 0;
+    if (p.split) {
+        unsigned char *w = static_cast<unsigned char *>(workspace);
+        float *fq = reinterpret_cast<float *>(w + p.oQ), *fk = reinterpret_cast<float *>(w + p.oK);
+        const int dt = dtype == LA_F32 ? la::kDtypeF32 : la::kDtypeBf16;
+        hipError_t e = la::feature_map(dt, (int)D, (int)F, kind, Q, fq, K, fk, W, (long)(BH * N), norm != 0, s);
+        const void *Vf = V;
+        if (e == hipSuccess && dtype == LA_BF16) {
+            float *vw = reinterpret_cast<float *>(w + p.oV);
+            e = la::widen_bf16(V, vw, (long)(BH * N * M), s);
+            Vf = vw;
+        }
+        void *iw = p.inner_ws > 0 ? workspace : nullptr;
+        const int Fi = (int)F, Mi = (int)M, C = p.att_chunk, G = p.att_segments, cps = p.att_cps;
+        if (e == hipSuccess)
+            e = p.att_onepass ? la::prefill_onepass(LA_F32_FEATURES, Fi, Mi, C, fq, fk, Vf, out, iw, (int)BH, (int)N, G,
+                                                    cps, S_out, z_out, S_in, z_in, s)
+                              : la::prefill_fused(LA_F32_FEATURES, Fi, Mi, C, fq, fk, Vf, out, iw, (int)BH, (int)N, G,
+                                                  cps, S_out, z_out, S_in, z_in, s);
+        return hip_status(e);
+    }
     if (!causal)
         return hip_status(la::prefill_features_noncausal(dtype == LA_F32 ? la::kDtypeF32 : la::kDtypeBf16, (int)D,
                                                          (int)F, (int)M, Q, K, V, W, kind, norm, out,

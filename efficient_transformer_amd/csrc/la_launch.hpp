@@ -89,6 +89,8 @@ hipError_t pad_copy(const void *src, void *dst, long BH, long Rs, long Cs_bytes,
                     unsigned fill, hipStream_t stream);
 hipError_t unpad_copy(const void *src, void *dst, long BH, long Rs, long Cs_bytes, long Rd, long Cd_bytes,
                       hipStream_t stream);
+// n bf16 values (n % 8 == 0, 16-byte aligned) widened exactly to fp32.
+hipError_t widen_bf16(const void *src, float *dst, long n, hipStream_t stream);
 // Tn recurrent steps of every head for D, M given at run time (multiples of 16 up to 128).
 hipError_t decode_any(int dtype, int D, int M, float *S, float *z, const void *q, const void *k, const void *v,
                       float *out, int BH, int Tn, hipStream_t stream);

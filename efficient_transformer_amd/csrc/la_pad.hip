@@ -48,6 +48,25 @@ __global__ __launch_bounds__(kPadThreads) void unpad_kernel(const u32x4 *__restr
     }
 }
 
+// dst[i] = src[i] widened from bf16 to fp32, eight values per item
+__global__ __launch_bounds__(kPadThreads) void widen_kernel(const u32x4 *__restrict__ src, f32x4 *__restrict__ dst,
+                                                            long items) {
+    const long step = (long)gridDim.x * kPadThreads;
+    for (long i = (long)blockIdx.x * kPadThreads + threadIdx.x; i < items; i += step) {
+        const u32x4 v = __builtin_nontemporal_load(src + i);
+        f32x4 lo, hi;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            lo[2 * j] = __builtin_bit_cast(float, v[j] << 16);
+            lo[2 * j + 1] = __builtin_bit_cast(float, v[j] & 0xffff0000u);
+            hi[2 * j] = __builtin_bit_cast(float, v[2 + j] << 16);
+            hi[2 * j + 1] = __builtin_bit_cast(float, v[2 + j] & 0xffff0000u);
+        }
+        __builtin_nontemporal_store(lo, dst + 2 * i);
+        __builtin_nontemporal_store(hi, dst + 2 * i + 1);
+    }
+}
+
 unsigned grid_for(long units) {
     const long b = (units + kPadThreads - 1) / kPadThreads;
     return (unsigned)(b < 256 * 16 ? (b > 0 ? b : 1) : 256 * 16);
@@ -162,6 +181,15 @@ hipError_t unpad_copy(const void *src, void *dst, long BH, long Rs, long Cs_byte
     if (units <= 0) return hipSuccess;
     hipLaunchKernelGGL(unpad_kernel, dim3(grid_for(units)), dim3(kPadThreads), 0, stream,
                        static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), BH, Rs, Cs, Rd, Cd);
+    return hipGetLastError();
+}
+
+hipError_t widen_bf16(const void *src, float *dst, long n, hipStream_t stream) {
+    if (n % 8) return hipErrorInvalidValue;
+    const long items = n / 8;
+    if (items <= 0) return hipSuccess;
+    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(items)), dim3(kPadThreads), 0, stream,
+                       static_cast<const u32x4 *>(src), reinterpret_cast<f32x4 *>(dst), items);
     return hipGetLastError();
 }
 

@@ -455,8 +455,12 @@ LA_API int la_decode_step_features(float *S, float *z, const void *q, const void
  * a supported shape, 0 for a refused one), initialised and reused as for
  * la_forward_chunked.
  * Plan: chunks of 32, segments sized for 512 resident workgroups; causal: the
- * one-pass kernel runs segments of at most four chunks where its LDS fits, the
- * two-phase kernel (the map applied in both phases) everything else.  D and F
+ * one-pass kernel runs segments of at most four chunks where its LDS fits;
+ * everything else runs as two launches, the map into the workspace and then the
+ * attention kernels on those features (bf16 V widened into the workspace), which
+ * measured faster there than a fused two-phase kernel (that forms the k-row
+ * projections in both of its phases).  The features then pass through memory
+ * (rows * F * 8 bytes of workspace, plus rows * M * 4 for V).  D and F
  * outside the instantiated set (D in {16, 32, 64, 128}, F in {16, 32, 64}, M in
  * {16, 32, 64, 128}) give LA_ERR_UNSUPPORTED (and a workspace size of 0);
  * la_feature_map followed by la_forward_chunked (LA_F32_FEATURES) computes the

@@ -92,8 +92,8 @@ def test_fused_features_parity(ea, normalize, kind, D, F, M):
 
 
 def test_supported_shapes(ea):
-    """Every instantiated (D, F, M) runs fused: the one-pass kernel where its LDS
-    fits, else the two-phase kernel."""
+    """Every instantiated (D, F, M) is supported: the fused one-pass kernel where its
+    LDS fits, else the map and the attention kernels as two launches."""
     for D in (16, 32, 64, 128):
         for F in (16, 32, 64):
             for M in (16, 32, 64, 128):
@@ -248,8 +248,9 @@ LONG = [(1, 2, 65536, 64, 16, 64), (2, 1, 40000, 32, 32, 32), (1, 1, 80000, 128,
 
 
 def two_phase_case(ea, kind, normalize, B, H, N, D, F, M, rows=None):
-    """Runs the fused kernel; checks it against the two-launch path (on the rows
-    selected by `rows`, a function of the oracle inputs, if given)."""
+    """Runs la_forward_features on a plan without the one-pass kernel (two launches
+    inside the entry point); checks it against the caller's own two launches (on the
+    rows selected by `rows`, a function of the oracle inputs, if given)."""
     if not supported(ea, B, H, N, D, M, F):
         pytest.skip(f"D={D} F={F} M={M}: the kernel's LDS does not fit")
     assert not plan_is_onepass(B, H, N)
@@ -268,9 +269,9 @@ def two_phase_case(ea, kind, normalize, B, H, N, D, F, M, rows=None):
 @pytest.mark.parametrize("kind,normalize", [("prf", False), ("prf", True), ("trf", False)])
 @pytest.mark.parametrize("B,H,N,D,F,M", LONG)
 def test_fused_features_two_phase(ea, kind, normalize, B, H, N, D, F, M):
-    """Long heads: segments of more than four chunks run the two-phase kernel with
-    the map fused into both phases (ragged last chunk in the second shape):
-    against the oracle and against the two-launch path."""
+    """Long heads: segments of more than four chunks (ragged last chunk in the second
+    shape) run as two launches inside the entry point: against the oracle and against
+    the caller's two-launch path."""
     out, S, z, host, _ = two_phase_case(ea, kind, normalize, B, H, N, D, F, M)
     check(out, S, z, oracle_out(host, F, kind, normalize))
 
