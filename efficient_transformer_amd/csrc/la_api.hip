@@ -782,8 +782,7 @@ int features_plan(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t
     // the k rows in both of its phases, and measured slower than the two launches:
     // 204 against 193 us at B1 H8 N65536 D64 F16 M64, 56.9 against 51.5 us at
     // B8 H8 N1024 D64 F64 M64.)
-    if (p->onepass && !la::prefill_features_supported(true, (int)D, (int)F, (int)M)) p->onepass = false;
-    if (!p->onepass && !la::prefill_features_supported(false, (int)D, (int)F, (int)M)) return LA_ERR_UNSUPPORTED;
+    if (p->onepass && !la::prefill_features_onepass_supported((int)D, (int)F, (int)M)) p->onepass = false;
     if (!p->onepass) {
         Plan a;
         st = make_plan(B, H, N, F, M, 1, LA_F32_FEATURES, 0, &a);
@@ -881,10 +880,10 @@ LA_API int la_forward_features(const void *Q, const void *K, const void *V, floa
                                                          static_cast<float *>(workspace), (int)BH, (int)N, p.segments,
                                                          p.chunks_per_segment, s));
     return hip_status(dtype == LA_F32
-                          ? la::prefill_features_f32(p.onepass, (int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
+                          ? la::prefill_features_f32((int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
                                                      workspace, (int)BH, (int)N, p.segments, p.chunks_per_segment,
                                                      S_out, z_out, S_in, z_in, s)
-                          : la::prefill_features_bf16(p.onepass, (int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
+                          : la::prefill_features_bf16((int)D, (int)F, (int)M, Q, K, V, W, kind, norm, out,
                                                       workspace, (int)BH, (int)N, p.segments, p.chunks_per_segment,
                                                       S_out, z_out, S_in, z_in, s));
 }

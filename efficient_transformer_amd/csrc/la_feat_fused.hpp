@@ -9,21 +9,17 @@
 
 namespace la {
 
-// onepass: the one-pass kernel (segments of at most four chunks), else the
-// two-phase kernel.
+// The one-pass kernel (segments of at most four chunks); longer segments run the
+// map and the attention as two launches (la_forward_features).
 template <typename TI>
-hipError_t prefill_features_typed(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
-                                  const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                  int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+hipError_t prefill_features_typed(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
+                                  int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
+                                  float *S_out, float *z_out, const float *S_in, const float *z_in,
                                   hipStream_t stream) {
-#define X(DI_, F_, M_)                                                                                        \
-    if (DI == DI_ && F == F_ && M == M_)                                                                      \
-        return onepass ? run_onepass_features<DI_, F_, M_, kFusedFeatureChunk, TI>(Q, K, V, W, kind, norm, out, ws, \
-                                                                                   BH, N, G, CPS, S_out, z_out,    \
-                                                                                   S_in, z_in, stream)             \
-                       : run_fused_features<DI_, F_, M_, kFusedFeatureChunk, TI>(Q, K, V, W, kind, norm, out, ws,   \
-                                                                                 BH, N, G, CPS, S_out, z_out,      \
-                                                                                 S_in, z_in, stream);
+#define X(DI_, F_, M_)                                                                                          \
+    if (DI == DI_ && F == F_ && M == M_)                                                                        \
+        return run_onepass_features<DI_, F_, M_, kFusedFeatureChunk, TI>(Q, K, V, W, kind, norm, out, ws, BH, N, G, \
+                                                                         CPS, S_out, z_out, S_in, z_in, stream);
 #define XM(DI_, F_) X(DI_, F_, 16) X(DI_, F_, 32) X(DI_, F_, 64) X(DI_, F_, 128)
 #define XF(DI_) XM(DI_, 16) XM(DI_, 32) XM(DI_, 64)
     XF(16) XF(32) XF(64) XF(128)

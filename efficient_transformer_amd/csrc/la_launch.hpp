@@ -117,8 +117,8 @@ hipError_t prefill_outputs_bf16o(int D, int M, int C, const void *Q, const void 
 // random features fused into the one-pass causal kernel (la_feat_fused*.hip):
 // raw rows (and V) fp32 or bf16, features and attention fp32
 constexpr int kFusedFeatureChunk = 32;
-// onepass: the one-pass kernel (segments of at most four chunks), else the two-phase one
-bool prefill_features_supported(bool onepass, int DI, int F, int M);
+// whether the one-pass kernel with the map fused fits (LDS) for this shape
+bool prefill_features_onepass_supported(int DI, int F, int M);
 // non-causal attention over random features (stage path; ws as la_segment_states')
 bool prefill_features_noncausal_supported(int DI, int F, int M);
 hipError_t prefill_features_noncausal(int dtype, int DI, int F, int M, const void *Q, const void *K, const void *V,
@@ -127,13 +127,13 @@ hipError_t prefill_features_noncausal(int dtype, int DI, int F, int M, const voi
 hipError_t prefill_features_noncausal_bf16(int DI, int F, int M, const void *Q, const void *K, const void *V,
                                            const float *W, int kind, int norm, float *out, float *ws, int BH, int N,
                                            int G, int CPS, hipStream_t stream);
-hipError_t prefill_features_f32(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
-                                const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+hipError_t prefill_features_f32(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
+                                int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
+                                float *S_out, float *z_out, const float *S_in, const float *z_in,
                                 hipStream_t stream);
-hipError_t prefill_features_bf16(bool onepass, int DI, int F, int M, const void *Q, const void *K, const void *V,
-                                 const float *W, int kind, int norm, float *out, void *ws, int BH, int N, int G,
-                                 int CPS, float *S_out, float *z_out, const float *S_in, const float *z_in,
+hipError_t prefill_features_bf16(int DI, int F, int M, const void *Q, const void *K, const void *V, const float *W,
+                                 int kind, int norm, float *out, void *ws, int BH, int N, int G, int CPS,
+                                 float *S_out, float *z_out, const float *S_in, const float *z_in,
                                  hipStream_t stream);
 
 // feature inputs (la_feat_prefill.hip, la_feat_onepass.hip)

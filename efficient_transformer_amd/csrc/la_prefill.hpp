@@ -1687,34 +1687,6 @@ hipError_t run_onepass_features(const void *Q, const void *K, const void *V, con
     }
 }
 
-// The two-phase kernel takes any shape whose LDS fits one workgroup per CU
-// (fewer resident workgroups than planned only cost speed: waits only go to
-// segments dispatched earlier).
-template <int DI, int F, int M, int C>
-constexpr bool fused_features_fit() {
-    using Gc = Cfg<float, F, M, C>;
-    return Gc::fits && Gc::bytes + FeatLds<DI, F, C>::bytes + 64 <= kMaxLds;
-}
-
-// The two-phase kernel with the random-feature map fused (segments longer than
-// the one-pass kernel takes).
-template <int DI, int F, int M, int C, typename TI = float>
-hipError_t run_fused_features(const void *Q, const void *K, const void *V, const float *W, int fkind, int fnorm,
-                              float *out, void *ws, int BH, int N, int G_, int CPS, float *S_out, float *z_out,
-                              const float *S_in, const float *z_in, hipStream_t stream) {
-    using Gc = Cfg<float, F, M, C>;
-    if constexpr (!fused_features_fit<DI, F, M, C>()) {
-        return hipErrorInvalidValue;
-    } else {
-        if (BH <= 0 || G_ <= 0) return hipSuccess;
-        const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
-        hipLaunchKernelGGL((fused_causal_kernel<float, F, M, C, false, float, DI, TI>), dim3(grid), dim3(Gc::THREADS), 0,
-                           stream, (const TI *)Q, (const TI *)K, (const TI *)V, out, ws, BH, N, G_, CPS, S_out, z_out,
-                           S_in, z_in, W, fkind, fnorm);
-        return hipGetLastError();
-    }
-}
-
 // Non-causal attention over random features (the stage path: segment states,
 // their scan, outputs), raw rows of type TI mapped in both stage kernels.
 template <int DI, int F, int M, int C>

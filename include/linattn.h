@@ -436,11 +436,12 @@ LA_API int la_decode_step_features(float *S, float *z, const void *q, const void
                                    int64_t B, int64_t H, int64_t D, int64_t M, int dtype, const float *W, int64_t F,
                                    int kind, int flags, void *stream);
 
-/* Attention with the random-feature map fused into the attention kernels: each
- * chunk's raw q, k rows are mapped to F features (as la_feature_map, kinds
- * LA_FEATURE_PRF and LA_FEATURE_TRF, flag LA_FEATURE_NORMALIZE) while they are
- * staged, then attended to as with la_forward_chunked on LA_F32_FEATURES
- * inputs; the features never reach memory.  causal = 1 or 0 as for
+/* Attention on random features of raw rows in one call: each chunk's raw q, k
+ * rows are mapped to F features (as la_feature_map, kinds LA_FEATURE_PRF and
+ * LA_FEATURE_TRF, flag LA_FEATURE_NORMALIZE) and attended to as with
+ * la_forward_chunked on LA_F32_FEATURES inputs.  On one-pass plans the map is
+ * fused into the attention kernel's staging and the features never reach
+ * memory (other plans: see Plan below).  causal = 1 or 0 as for
  * la_forward_chunked (0: the stage kernels, the map in both; no states).
  * Q, K [B][H][N][D] (raw rows) and V [B][H][N][M], all of element type dtype
  * (LA_F32 or LA_BF16; bf16 values are widened exactly, the map and the
@@ -461,10 +462,9 @@ LA_API int la_decode_step_features(float *S, float *z, const void *q, const void
  * measured faster there than a fused two-phase kernel (that forms the k-row
  * projections in both of its phases).  The features then pass through memory
  * (rows * F * 8 bytes of workspace, plus rows * M * 4 for V).  D and F
- * outside the instantiated set (D in {16, 32, 64, 128}, F in {16, 32, 64}, M in
- * {16, 32, 64, 128}) give LA_ERR_UNSUPPORTED (and a workspace size of 0);
- * la_feature_map followed by la_forward_chunked (LA_F32_FEATURES) computes the
- * same result in two launches for any supported feature dimension.
+ * outside the supported set (D, F and M in {16, 32, 64, 128}; non-causal F up
+ * to 64) give LA_ERR_UNSUPPORTED (and a workspace size of 0); F = 128 always runs
+ * as two launches.
  */
 LA_API size_t la_forward_features_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t D, int64_t M, int64_t F,
                                                   int causal);

@@ -367,9 +367,14 @@ def test_forward_features_checks(L):
     need = wsb(8, 8, 1024, 64, 64, 16, 1)
     assert need > 0
     assert wsb(8, 8, 1024, 48, 64, 16, 1) == 0 and wsb(8, 8, 1024, 64, 64, 24, 1) == 0  # D, F
-    assert wsb(8, 8, 1024, 64, 64, 128, 1) == 0  # F = 128: no fused instantiation
-    assert wsb(1, 1, 1 << 20, 64, 64, 16, 1) > 0  # long segments: the two-phase kernel
-    assert wsb(8, 8, 1024, 64, 64, 64, 1) > 0  # one-pass LDS too small: the two-phase kernel
+    # no fused one-pass instantiation (F = 128), long segments, one-pass LDS too small: the map
+    # and the attention as two launches, the features in the workspace (rows * F * 8 bytes and
+    # rows * M * 4 for widened values besides the attention's own workspace)
+    rows = 8 * 8 * 1024
+    assert wsb(8, 8, 1024, 64, 64, 128, 1) >= rows * (128 * 8 + 64 * 4)
+    assert wsb(8, 8, 1024, 64, 64, 128, 0) == 0  # non-causal: stage kernels, F up to 64
+    assert wsb(1, 1, 1 << 20, 64, 64, 16, 1) >= (1 << 20) * (16 * 8 + 64 * 4)
+    assert wsb(8, 8, 1024, 64, 64, 64, 1) >= rows * (64 * 8 + 64 * 4)
     assert wsb(-1, 8, 1024, 64, 64, 16, 1) == 0 and wsb(8, 8, 1024, 64, 64, 16, 2) == 0
     assert wsb(8, 8, 1024, 64, 64, 16, 0) > 0  # non-causal: the stage path
 
@@ -386,7 +391,8 @@ def test_forward_features_checks(L):
     assert call(kind=3) == L.LA_ERR_INVALID_ARG
     assert call(flags=2) == L.LA_ERR_INVALID_ARG
     assert call(D=48) == L.LA_ERR_UNSUPPORTED
-    assert call(F=128) == L.LA_ERR_UNSUPPORTED
+    assert call(F=128, causal=0) == L.LA_ERR_UNSUPPORTED
+    assert call(F=128) == L.LA_ERR_WORKSPACE  # supported (two launches), with a larger workspace
     assert call(N=-1) == L.LA_ERR_INVALID_ARG
     assert call(S=FAKE) == L.LA_ERR_INVALID_ARG  # S_out without z_out
     assert call(causal=2) == L.LA_ERR_INVALID_ARG

@@ -81,7 +81,7 @@ def check(out, S, z, ref):
 @pytest.mark.parametrize("normalize", [False, True])
 @pytest.mark.parametrize("kind", ["prf", "trf"])
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
-@pytest.mark.parametrize("F,M", [(16, 64), (32, 32), (16, 128), (32, 16), (64, 16)])
+@pytest.mark.parametrize("F,M", [(16, 64), (32, 32), (16, 128), (32, 16), (64, 16), (128, 64)])
 def test_fused_features_parity(ea, normalize, kind, D, F, M):
     """N = 300: nine full chunks of 32 and a ragged one, several segments per head."""
     B, H, N = 1, 3, 300
@@ -92,13 +92,14 @@ def test_fused_features_parity(ea, normalize, kind, D, F, M):
 
 
 def test_supported_shapes(ea):
-    """Every instantiated (D, F, M) is supported: the fused one-pass kernel where its
-    LDS fits, else the map and the attention kernels as two launches."""
+    """Every (D, F, M) of widths 16 .. 128 is supported causally: the fused one-pass kernel
+    where it is instantiated (F up to 64) and its LDS fits, else the map and the attention
+    kernels as two launches; non-causal attention has F up to 64."""
     for D in (16, 32, 64, 128):
-        for F in (16, 32, 64):
+        for F in (16, 32, 64, 128):
             for M in (16, 32, 64, 128):
                 assert supported(ea, 8, 8, 1024, D, M, F), (D, F, M)
-    assert not supported(ea, 8, 8, 1024, 64, 64, 128)  # F = 128: two launches
+                assert supported(ea, 8, 8, 1024, D, M, F, causal=False) == (F <= 64), (D, F, M)
 
 
 @pytest.mark.parametrize("N", [1, 31, 32, 33, 127, 128, 129])
