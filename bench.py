@@ -603,12 +603,16 @@ def profile_run(workload, dev, launches=16):
     import efficient_transformer_amd as ea
     import synthetic
     if workload in synthetic.WORKLOADS and synthetic.WORKLOADS[workload]["kind"] == "prefill":
-        # as the timed bench: the kernel itself for 0.3 s (at most 2048 launches) first; after an idle
+        # as the timed bench: the kernel itself for 0.3 s (at most 256 launches) first; after an idle
         # spell the long-head kernel runs up to 30 % slow for its first few dozen launches
-        step, plan = prefill_runner(dict(synthetic.WORKLOADS[workload]), dev, nsets=1)
+        # the bench's input rotation (at most 8 sets: under a counter profiler every dispatch,
+        # the input generator's included, is collected one at a time)
+        cfg = dict(synthetic.WORKLOADS[workload])
+        nsets = min(8, max(1, math.ceil(1.25 * LLC_BYTES / prefill_bytes(cfg))))
+        step, plan = prefill_runner(cfg, dev, nsets=nsets)
         t0 = time.perf_counter()
         i = 0
-        while time.perf_counter() - t0 < 0.3 and i < 2048:
+        while time.perf_counter() - t0 < 0.3 and i < 256:
             step(i)
             i += 1
             if i % 16 == 0:

@@ -158,6 +158,7 @@ struct Stage {
     static constexpr int PER = (ITEMS + NT - 1) / NT;
     uint4 r[PER][RPI];
 
+    template <bool NTL = false>
     __device__ __forceinline__ void load(const T *__restrict__ head, int row0, int N, int tid) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
@@ -167,11 +168,16 @@ struct Stage {
 #pragma unroll
                 for (int i = 0; i < RPI; ++i) {
                     // rows past the end re-read the last row (no branch); the stores zero them.
-                    // Nontemporal: each row is streamed through once per pass (the two-phase
-                    // kernel's second pass starts long after the first has left the caches).
+                    // NTL (the two-phase kernel's passes): nontemporal, each row streams through
+                    // once per pass and the second pass starts long after the first has left the
+                    // caches (417 -> 400 us on a 16 x 65536-row bf16 head set); the one-pass
+                    // kernel keeps cached loads (nontemporal ones cost its 16-token decode 10 %).
                     const int grow = min(row0 + rq * RPI + i, N - 1);
-                    r[p][i] = __builtin_bit_cast(
-                        uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(head + (size_t)grow * W + cv * VEC)));
+                    if constexpr (NTL)
+                        r[p][i] = __builtin_bit_cast(
+                            uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(head + (size_t)grow * W + cv * VEC)));
+                    else
+                        r[p][i] = *reinterpret_cast<const uint4 *>(head + (size_t)grow * W + cv * VEC);
                 }
             }
         }
@@ -889,9 +895,10 @@ template <typename T, int D, int M, int C, int DK = D, typename TI = T>
 struct KVBuf {
     Stage<TI, C, DK, Cfg<T, D, M, C>::THREADS> k;
     Stage<TI, C, M, Cfg<T, D, M, C>::THREADS> v;
+    template <bool NTL = false>
     __device__ __forceinline__ void load(const TI *Kh, const TI *Vh, int c, int N, int tid) {
-        k.load(Kh, c * C, N, tid);
-        v.load(Vh, c * C, N, tid);
+        k.template load<NTL>(Kh, c * C, N, tid);
+        v.template load<NTL>(Vh, c * C, N, tid);
     }
 };
 
@@ -974,8 +981,8 @@ __device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const 
     // wait counts stay exact; only the arithmetic of the odd last chunk is skipped.
     using KV = KVBuf<T, D, M, C, ChunkStager<T, D, M, C, PHI, DI, TI>::DQ, TI>;
     KV b0, b1;
-    b0.load(Kh, Vh, c0, N, e.tid);
-    b1.load(Kh, Vh, min(c0 + 1, c1 - 1), N, e.tid);
+    b0.template load<true>(Kh, Vh, c0, N, e.tid);
+    b1.template load<true>(Kh, Vh, min(c0 + 1, c1 - 1), N, e.tid);
     auto body = [&](const KV &b, int c) {
         __syncthreads();  // LDS free (previous chunk's readers are done)
         st.store_kv(e, b, c * C, N);
@@ -988,9 +995,9 @@ __device__ __forceinline__ void phase_a(const Engine<T, D, M, C, PHI> &e, const 
     };
     for (int c = c0; c < c1; c += 2) {
         body(b0, c);
-        b0.load(Kh, Vh, min(c + 2, c1 - 1), N, e.tid);
+        b0.template load<true>(Kh, Vh, min(c + 2, c1 - 1), N, e.tid);
         if (c + 1 < c1) body(b1, c + 1);
-        b1.load(Kh, Vh, min(c + 3, c1 - 1), N, e.tid);
+        b1.template load<true>(Kh, Vh, min(c + 3, c1 - 1), N, e.tid);
     }
 }
 
@@ -1012,7 +1019,7 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const 
     // loads as in phase_a: one chunk ahead, unconditional (clamped)
     auto &q = q0;
     KVBuf<T, D, M, C, ChunkStager<T, D, M, C, PHI, DI, TI>::DQ, TI> b;
-    if (CAUSAL && !kv_staged) b.load(Kh, Vh, c0, N, e.tid);
+    if (CAUSAL && !kv_staged) b.template load<true>(Kh, Vh, c0, N, e.tid);
     for (int c = c0; c < c1; ++c) {
         const int row0 = c * C;
         const bool stage_kv = CAUSAL && !(kv_staged && c == c0);
@@ -1022,8 +1029,8 @@ __device__ __forceinline__ void phase_b(const Engine<T, D, M, C, PHI> &e, const 
         if (e.tid < D) e.set_z(z);
         __syncthreads();
         const int cn = min(c + 1, c1 - 1);
-        q.load(Qh, cn * C, N, e.tid);
-        if (CAUSAL) b.load(Kh, Vh, cn, N, e.tid);
+        q.template load<true>(Qh, cn * C, N, e.tid);
+        if (CAUSAL) b.template load<true>(Kh, Vh, cn, N, e.tid);
         st.map(e, true, stage_kv, row0, N);
         if (CAUSAL) e.a_tiles();
         e.qz_rows();
@@ -1262,7 +1269,7 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     }
 
     typename St::QStage stQ;
-    stQ.load(Qh, c0 * C, N, tid);
+    stQ.template load<true>(Qh, c0 * C, N, tid);
 
     // A one-chunk segment still holds its phi(K), V in LDS: form A and the
     // intra-chunk term now, while earlier segments may still be publishing.

@@ -72,7 +72,15 @@ int main(void) {
     EXPECT(la_decode_step(F, F, F, F, F, F, 2, 2, 64, 64, 7, NULL) == LA_ERR_INVALID_ARG, "decode dtype");
     EXPECT(la_decode_steps(F, F, F, F, F, F, 2, 2, -1, 64, 64, LA_F32, NULL) == LA_ERR_INVALID_ARG, "negative T");
     EXPECT(la_decode_steps(F, F, F, F, F, F, 2, 2, 0, 48, 48, LA_F32, NULL) == LA_OK, "T = 0");
-    EXPECT(la_backward_workspace_bytes(2, 2, 100, 64, 64, LA_F32_FEATURES) == 0, "backward refuses features");
+    EXPECT(la_backward_workspace_bytes(2, 2, 100, 64, 64, LA_F32_FEATURES) ==
+               la_backward_workspace_bytes(2, 2, 100, 64, 64, LA_F32), "backward plans features like fp32");
+    EXPECT(la_backward_workspace_bytes(2, 2, 100, 64, 64, LA_F32 | LA_OUT_BF16) == 0, "backward refuses bf16 outputs");
+    EXPECT(la_feature_map_backward(F, F, F, 100, 64, LA_F32, F, 16, 3, 0, NULL) == LA_ERR_INVALID_ARG,
+           "feature map backward kind");
+    EXPECT(la_feature_map_backward(F, F, F, 100, 48, LA_F32, F, 16, 1, 0, NULL) == LA_ERR_UNSUPPORTED,
+           "feature map backward width");
+    EXPECT(la_feature_map_backward(NULL, NULL, NULL, 0, 64, LA_F32, NULL, 16, 1, 0, NULL) == LA_OK,
+           "feature map backward no rows");
     EXPECT(la_backward_chunked(F, F, F, F, F, F, F, F, 2, 2, 100, 64, 64, LA_F32, NULL, 0, NULL) == LA_ERR_WORKSPACE,
            "backward workspace");
     EXPECT(la_softmax_scan_workspace_bytes(2, 2, 128, 64, 64) == 0, "one softmax group");
