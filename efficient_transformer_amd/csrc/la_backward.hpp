@@ -608,10 +608,18 @@ __global__ __launch_bounds__(256) void bwd_rev_scan_kernel(float *ws, int E, int
     if (x >= E) return;
     float *h = ws + (size_t)blockIdx.y * (G_ + 1) * E;
     float acc = 0.0f;
-    for (int s = G_ - 1; s >= 0; --s) {
-        const float v = h[(size_t)s * E + x];
-        h[(size_t)s * E + x] = acc;
-        acc += v;
+    // kScanBatch slots loaded before any is overwritten (one round trip per batch)
+    for (int s1 = G_ - 1; s1 >= 0; s1 -= kScanBatch) {
+        float v[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) v[j] = s1 - j >= 0 ? h[(size_t)(s1 - j) * E + x] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+            if (s1 - j >= 0) {
+                h[(size_t)(s1 - j) * E + x] = acc;
+                acc += v[j];
+            }
+        }
     }
     h[(size_t)G_ * E + x] = acc;  // total
 }

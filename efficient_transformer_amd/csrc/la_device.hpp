@@ -28,6 +28,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // Cache-policy bits of buffer stores: sc1 = agent scope (write-through past the
 // per-XCD L2, so another XCD reads the stored value from memory).
 constexpr int kCachePolicyAgent = 16;
+// Segment states read per memory round trip by the element-wise state scans.
+constexpr int kScanBatch = 8;
 using bf16 = __bf16;
 
 // phi(x) = elu(x) + 1: x + 1 for x > 0, exp(x) otherwise (page "Transformers are

@@ -18,10 +18,19 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(float *__restrict__ ws, i
     if (e >= E) return;
     float *base = ws + (size_t)bh * (G + 1) * E + e;
     float run = 0.0f;
-    for (int s = 0; s < nstates; ++s) {
-        const float x = base[(size_t)s * E];
-        base[(size_t)s * E] = run;
-        run += x;
+    // the loads of kScanBatch slots are issued before any of them is overwritten:
+    // one memory round trip per batch instead of one per segment (same sum order)
+    for (int s0 = 0; s0 < nstates; s0 += kScanBatch) {
+        float x[kScanBatch];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) x[j] = s0 + j < nstates ? base[(size_t)(s0 + j) * E] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+            if (s0 + j < nstates) {
+                base[(size_t)(s0 + j) * E] = run;
+                run += x[j];
+            }
+        }
     }
     for (int s = nstates; s < G; ++s) base[(size_t)s * E] = run;
     base[(size_t)G * E] = run;
