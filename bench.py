@@ -160,9 +160,23 @@ def roofline(workload, nbytes, us, flops=None, mfma_peak=None, mfma_dtype=None, 
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def timed(step, steps, warmup, stream):
-    """Average ms of one step over `steps` back-to-back steps between events on `stream`."""
+# Upper bound on the untimed warm-up calls of `timed`; profile mode lowers it (a counter
+# profiler serialises every dispatch, so 0.3 s of calls would take minutes there).
+WARM_CALLS_MAX = 1 << 30
+
+
+def timed(step, steps, warmup, stream, warm_s=0.3):
+    """Average ms of one step over `steps` back-to-back steps between events on `stream`, after
+    untimed steps for at least `warm_s` seconds (the clocks settle on the workload's own kernels:
+    a few warm-up calls left the backward 4 % slow) and then `warmup` more."""
     import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < warm_s and i < WARM_CALLS_MAX:
+        step(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -226,18 +240,9 @@ def causal_kernel_name(cfg, chunk, segments) -> str:
     return f"{kind}<{t}, {cfg['D']}, {cfg['M']}, {chunk}, true, {ot}{extra}>"
 
 
-def bench_prefill(name, cfg, steps, warmup, dev, warm_s=0.0):
+def bench_prefill(name, cfg, steps, warmup, dev):
     import torch
     step, plan = prefill_runner(cfg, dev)
-    if warm_s > 0:  # untimed launches until the clocks have settled (at least warm_s seconds)
-        t0 = time.perf_counter()
-        i = 0
-        while time.perf_counter() - t0 < warm_s:
-            step(i)
-            i += 1
-            if i % 16 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
     ms = timed(step, steps, warmup, plan["stream"])
     lat = None
     if cfg["N"] * cfg["B"] * cfg["H"] <= 4096:
@@ -622,6 +627,8 @@ def profile_run(workload, dev, launches=16):
         torch.cuda.synchronize()
         log(f"profile run of {workload} done")
         return
+    global WARM_CALLS_MAX
+    WARM_CALLS_MAX = 256  # the timed functions below warm up on their own calls, as in the bench
     warm_clocks(dev)
     if workload == DECODE:
         bench_decode_loop(dict(synthetic.WORKLOADS[DECODE], T=256), dev, reps=1)
@@ -640,8 +647,8 @@ def profile_run(workload, dev, launches=16):
         X = [synthetic.draw_torch(30, t, (B, H, N, D if t < 2 else M), c["sigma"] if t < 2 else 1.0, "f32", dev)
              for t in range(3)]
         o = torch.empty((B, H, N, M), device=dev)
-        for _ in range(8):
-            ea.forward_features(X[0], X[1], X[2], W, F, c["feature"], out=o)
+        timed(lambda i: ea.forward_features(X[0], X[1], X[2], W, F, c["feature"], out=o), 8, 0,
+              torch.cuda.current_stream(dev))
     elif workload == "copy512":
         src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -684,7 +691,7 @@ def main():
 
     cfg = dict(synthetic.WORKLOADS[HEADLINE])
     log(f"headline prefill {cfg}")
-    head = bench_prefill(HEADLINE, cfg, args.steps, args.warmup, dev, warm_s=0.3)
+    head = bench_prefill(HEADLINE, cfg, args.steps, args.warmup, dev)
     log(f"headline: {head}")
     line = {
         "metric": METRIC,
