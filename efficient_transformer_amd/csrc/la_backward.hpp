@@ -243,8 +243,8 @@ struct BwdEngine {
 #pragma unroll
             for (int k = 0; k < EPT; ++k) s += x[k] * y[k];
         }
-#pragma unroll
-        for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        static_assert(TPR <= 16, "threads of a row within one 16-lane row");
+        s = row_group_sum<TPR>(s);
         if (p == 0) out[i] = s;
     }
 };

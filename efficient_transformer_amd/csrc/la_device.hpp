@@ -89,6 +89,45 @@ __device__ __forceinline__ f32x4 tile_dot_f32(const float *a, int a_ks, const fl
     return acc;
 }
 
+// x of another lane of the same 16-lane row, by a DPP move (a VALU operation; no LDS
+// traffic): CTRL 0xB1 / 0x4E swap lanes i and i^1 / i^2 within each quad, 0x141 mirrors
+// each half-row (lane i of 8 reads lane 7 - i), 0x140 mirrors the row (i reads 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// sum of x over each aligned group of N consecutive lanes (N = 1, 2, 4, 8 or 16), in
+// every lane of the group: the quad sums by two swaps, then the half-row mirror adds
+// the other quad's sum and the row mirror the other half-row's
+template <int N>
+__device__ __forceinline__ float row_group_sum(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1, 2, 4, 8 or 16 lanes");
+    if constexpr (N >= 2) x += dpp_move<0xB1>(x);
+    if constexpr (N >= 4) x += dpp_move<0x4E>(x);
+    if constexpr (N >= 8) x += dpp_move<0x141>(x);
+    if constexpr (N >= 16) x += dpp_move<0x140>(x);
+    return x;
+}
+
+// Shifts for scans over lanes, by DPP moves; lanes without a source lane get `fill`:
+// row_shr (0x110 + O): lane i reads lane i - O of its own 16-lane row;
+// row_bcast:15 (0x142, written in rows 1 and 3 only): every lane of a row reads lane
+// 15 of the row before; wave_shr:1 (0x138): lane i reads lane i - 1 of the wavefront.
+template <int O>
+__device__ __forceinline__ float dpp_row_shr(float x, float fill) {
+    static_assert(O >= 1 && O <= 15, "shift within a row");
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, x),
+                                                                 0x110 + O, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_row_bcast15(float x, float fill) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, x),
+                                                                 0x142, 0xA, 0xF, false));
+}
+__device__ __forceinline__ float dpp_wave_shr1(float x, float fill) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill), __builtin_bit_cast(int, x),
+                                                                 0x138, 0xF, 0xF, false));
+}
+
 // sum of x over the four lanes {l16, l16+16, l16+32, l16+48}
 __device__ __forceinline__ float sum_over_groups(float x) {
     x += __shfl_xor(x, 16, 64);

@@ -84,7 +84,7 @@ struct Cfg {
     static constexpr int fz = 0;
     static constexpr int fzp = fz + D;
     static constexpr int fdenp = fzp + (NZP > 0 ? NZP : 1) * D;
-    static constexpr int fqz = fdenp + RT * C;
+    static constexpr int fqz = fdenp + 4 * RT * C;  // sdenp: [kt][lane group][query]
     static constexpr int nF = fqz + C;
     static constexpr size_t bytes = fbase + nF * sizeof(float);
     static constexpr bool fits = bytes + 64 <= kMaxLds;
@@ -431,7 +431,9 @@ struct Engine {
     }
 
     // Lower-triangle tiles of A (tile t = w, w+NW, ... in row-major order of (rt, kt<=rt)),
-    // rounded to T, into sA[query][key]; their row sums into sdenp[kt][query].  All of
+    // rounded to T, into sA[query][key]; each lane group's share of their row sums
+    // into sdenp[kt][g][query] (summed by row_den after the next barrier, instead of
+    // two cross-lane exchanges here on the chunk's critical path).  All of
     // a wavefront's tile products are issued before any epilogue, so their latencies
     // overlap.
     static __device__ __forceinline__ int tile_row(int t) {
@@ -500,8 +502,7 @@ struct Engine {
                     rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, one2, rs, false);
                     *reinterpret_cast<bf16x4 *>(arow) = v;
                 }
-                rs = sum_over_groups(rs);
-                if (g == 0) sdenp[kt * C + rt * 16 + l16] = rs;
+                sdenp[(kt * 4 + g) * C + rt * 16 + l16] = rs;
             }
         }
     }
@@ -546,8 +547,9 @@ struct Engine {
                 s += to_f32(sQ[boff<D>(i, col >> 3) + (col & 7)]) * (float)reinterpret_cast<const bf16 *>(sz)[col];
             }
         }
-#pragma unroll
-        for (int o = TPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        s = row_group_sum<(TPR < 16 ? TPR : 16)>(s);
+        if constexpr (TPR >= 32) s += __shfl_xor(s, 16, 64);
+        if constexpr (TPR >= 64) s += __shfl_xor(s, 32, 64);
         if (p == 0) dst[i] = s;
     }
 
@@ -560,7 +562,10 @@ struct Engine {
         if constexpr (CAUSAL) {
 #pragma unroll
             for (int kt = 0; kt < RT; ++kt)
-                if (kt <= rt) den += sdenp[kt * C + lane];
+                if (kt <= rt) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) den += sdenp[(kt * 4 + q) * C + lane];
+                }
         }
         return den;
     }

@@ -270,8 +270,9 @@ __global__ __launch_bounds__((DecCfg<D, M>::THREADS)) void decode_kernel(float *
 #pragma unroll
         for (int j = 0; j < 4; ++j) num[j] += __shfl_xor(num[j], sh, 64);
     }
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) den += __shfl_xor(den, sh, 64);
+    den = row_group_sum<16>(den);  // within 16-lane rows on DPP moves, then across rows
+    den += __shfl_xor(den, 16, 64);
+    den += __shfl_xor(den, 32, 64);
     if (G::NW > 1) {
         if (lane < G::LPR) sred[w][lane] = num;
         if (lane == 0) sden[w] = den;

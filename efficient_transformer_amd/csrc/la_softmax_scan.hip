@@ -153,25 +153,32 @@ __global__ __launch_bounds__(64 * kScanWaves) void softmax_scan_kernel(
         //    u_i = a_i u_{i-1} + b_i, and u_i itself (a scan of that affine map).
         //    Only w_i = a_i w_{i-1} + b_i v_i runs row after row, one fma per row
         //    and column.  Rows past N have s = -inf: a = 1, b = 0 keep the state.
+        //    The scans over the 32 rows (lanes 0 .. 31) run on DPP moves: within each
+        //    16-lane row by shifts of 1, 2, 4 and 8 lanes, then the second row takes
+        //    the first row's total from its lane 15; lanes without a source lane
+        //    combine with the identity.
+        static_assert(R == 32, "rows are lanes 0 .. 31: two 16-lane rows");
         float mx = s;
-#pragma unroll
-        for (int o = 1; o < R; o <<= 1) {
-            const float t = __shfl_up(mx, o, 64);
-            if (lane >= o) mx = fmaxf(mx, t);
-        }
-        const float up = __shfl_up(mx, 1, 64);  // every lane takes part in the shuffle
-        const float mprev = lane == 0 ? -INFINITY : up;
+        mx = fmaxf(mx, dpp_row_shr<1>(mx, -INFINITY));
+        mx = fmaxf(mx, dpp_row_shr<2>(mx, -INFINITY));
+        mx = fmaxf(mx, dpp_row_shr<4>(mx, -INFINITY));
+        mx = fmaxf(mx, dpp_row_shr<8>(mx, -INFINITY));
+        mx = fmaxf(mx, dpp_row_bcast15(mx, -INFINITY));
+        const float mprev = dpp_wave_shr1(mx, -INFINITY);  // the running max of the rows before
         const float fa = mx == -INFINITY ? 1.0f : __expf(mprev - mx);
         const float fb = mx == -INFINITY ? 0.0f : __expf(s - mx);
         float sa = fa, su = fb;  // composition of the maps of rows <= lane: u -> sa u + su
-#pragma unroll
-        for (int o = 1; o < R; o <<= 1) {
-            const float pa = __shfl_up(sa, o, 64), pb = __shfl_up(su, o, 64);
-            if (lane >= o) {
-                su = sa * pb + su;
-                sa = sa * pa;
-            }
-        }
+        // after the maps of the earlier rows (pa, pb): u -> sa (pa u + pb) + su; the
+        // identity (1, 0) leaves (sa, su) unchanged
+        auto after = [&](float pa, float pb) {
+            su = sa * pb + su;
+            sa = sa * pa;
+        };
+        after(dpp_row_shr<1>(sa, 1.0f), dpp_row_shr<1>(su, 0.0f));
+        after(dpp_row_shr<2>(sa, 1.0f), dpp_row_shr<2>(su, 0.0f));
+        after(dpp_row_shr<4>(sa, 1.0f), dpp_row_shr<4>(su, 0.0f));
+        after(dpp_row_shr<8>(sa, 1.0f), dpp_row_shr<8>(su, 0.0f));
+        after(dpp_row_bcast15(sa, 1.0f), dpp_row_bcast15(su, 0.0f));
         my_m = mx;
         my_u = su;
 #pragma unroll
@@ -421,8 +428,9 @@ __global__ __launch_bounds__(64) void softmax_step_kernel(float *__restrict__ m,
     const size_t h = blockIdx.x;
     float s = 0.0f;
     for (int d = lane; d < D; d += 64) s += ld1(q + h * D + d) * ld1(k + h * D + d);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    s = row_group_sum<16>(s);
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
     const float m0 = m[h], u0 = u[h];
     const float mn = fmaxf(m0, s);
     const float a = __expf(m0 - mn), b = __expf(s - mn);
