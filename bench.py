@@ -534,8 +534,9 @@ def bench_features(cfg, steps, dev):
 
 def bench_probes(dev, nbytes=1 << 30, reps=5):
     """Attainable peaks: the library's copy probe (read + written bytes per second), its
-    read-only stream probe, torch's copy kernel, and the fp32 / bf16 MFMA loops (8
-    independent chains per wavefront, 8 wavefronts per SIMD).  Best of several launches."""
+    read-only and write-only stream probes, torch's copy kernel, and the fp32 / bf16 MFMA
+    loops (8 independent chains per wavefront, 4 for the bf16 32x32x16 shape; 8 wavefronts
+    per SIMD).  Best of several launches."""
     import torch
     import efficient_transformer_amd as ea
 
@@ -559,17 +560,19 @@ def bench_probes(dev, nbytes=1 << 30, reps=5):
     part = torch.empty(int(ea.linattn.lib().la_probe_read_partials()), device=dev)
     ms_copy = best_ms(lambda: ea.probe_copy(b, a))
     ms_read = best_ms(lambda: ea.probe_read(a, out=part))
+    ms_write = best_ms(lambda: ea.probe_write(b, 1.0))
     ms_torch = best_ms(lambda: b.copy_(a))
     del a, b
     torch.cuda.empty_cache()
     blocks = 256 * 8
     out = torch.empty(blocks * 256, device=dev)
     mfma = {}
-    for kind in ("f32", "bf16"):
+    for kind in ("f32", "bf16", "bf16_32x32"):
         flops = ea.probe_mfma(kind, blocks, 2048, out=out)[1]
         mfma[kind] = flops / (best_ms(lambda: ea.probe_mfma(kind, blocks, 2048, out=out)) * 1e-3) / 1e12
     copy_gbs = 2 * nbytes / (ms_copy * 1e-3) / 1e9
     read_gbs = nbytes / (ms_read * 1e-3) / 1e9
+    write_gbs = nbytes / (ms_write * 1e-3) / 1e9
     return dict(
         hbm_copy=dict(workload="device-to-device copy of 1 GiB (nontemporal 16-byte loads and stores): "
                                "attainable read + write rate",
@@ -579,8 +582,13 @@ def bench_probes(dev, nbytes=1 << 30, reps=5):
         hbm_read=dict(workload="read-only stream over 1 GiB (nontemporal 16-byte loads): attainable read rate",
                       bytes_read=nbytes, us=round(ms_read * 1e3, 1), GBs=round(read_gbs, 1),
                       frac_hbm_peak=round(read_gbs / HBM_PEAK_GBS, 4)),
-        mfma_probe=dict(workload="dense MFMA loops, 8 independent chains per wavefront, 2048 workgroups of 4 "
-                                 "wavefronts",
+        hbm_write=dict(workload="write-only stream over 1 GiB (nontemporal 16-byte stores): attainable write rate",
+                       bytes_written=nbytes, us=round(ms_write * 1e3, 1), GBs=round(write_gbs, 1),
+                       frac_hbm_peak=round(write_gbs / HBM_PEAK_GBS, 4)),
+        mfma_probe=dict(workload="dense MFMA loops, 8 independent chains per wavefront (4 for the bf16 32x32x16 "
+                                 "shape), 2048 workgroups of 4 wavefronts",
+                        bf16_32x32_TFs=round(mfma["bf16_32x32"], 1),
+                        bf16_32x32_frac_peak=round(mfma["bf16_32x32"] / BF16_MFMA_PEAK_TFS, 4),
                         f32_TFs=round(mfma["f32"], 1), f32_frac_peak=round(mfma["f32"] / FP32_MFMA_PEAK_TFS, 4),
                         bf16_TFs=round(mfma["bf16"], 1),
                         bf16_frac_peak=round(mfma["bf16"] / BF16_MFMA_PEAK_TFS, 4)))

@@ -23,6 +23,7 @@ from .linattn import (  # noqa: F401
     probe_copy,
     probe_mfma,
     probe_read,
+    probe_write,
     fused_workspace_bytes,
     lib_path,
     noalloc_scratch_bytes,

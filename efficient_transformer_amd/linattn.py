@@ -68,6 +68,8 @@ SIGNATURES = {
     "la_probe_read_partials": (_sz, []),
     "la_probe_read": (_int, [_vp, _vp, _sz, _vp]),
     "la_probe_mfma": (_int, [_vp, _int, _i64, _int, ctypes.c_float, _vp]),
+    "la_probe_write": (_int, [_vp, _sz, ctypes.c_float, _vp]),
+    "la_probe_mfma32": (_int, [_vp, _i64, _int, ctypes.c_float, _vp]),
 }
 
 
@@ -678,13 +680,28 @@ def probe_read(src, out=None, stream=None):
     return out
 
 
+def probe_write(dst, value: float = 0.0, stream=None):
+    """Write-only stream probe: fills dst (contiguous) with the fp32 value by nontemporal stores."""
+    if not dst.is_contiguous():
+        raise ValueError("probe_write: dst must be contiguous")
+    _check(lib().la_probe_write(_ptr(dst), dst.numel() * dst.element_size(), value, _stream(stream, dst.device)),
+           "la_probe_write")
+    return dst
+
+
 def probe_mfma(kind: str, blocks: int, iters: int, x: float = 0.5, out=None, stream=None, device=None):
-    """MFMA throughput probe ("f32" or "bf16"); returns (out, flops of the launch)."""
+    """MFMA throughput probe ("f32": 16x16x4, "bf16": 16x16x32, "bf16_32x32": 32x32x16); returns
+    (out, flops of the launch)."""
     import torch
-    dt = {"f32": LA_F32, "bf16": LA_BF16}[kind]
+    if kind not in ("f32", "bf16", "bf16_32x32"):
+        raise ValueError(f"probe_mfma: unknown kind {kind!r}")
     if out is None:
         out = torch.empty(blocks * 256, dtype=torch.float32, device=device or "cuda")
     if out.dtype != torch.float32 or out.numel() < blocks * 256 or not out.is_contiguous():
         raise ValueError("probe_mfma: out must be contiguous float32 with blocks * 256 elements")
+    if kind == "bf16_32x32":
+        _check(lib().la_probe_mfma32(_ptr(out), blocks, iters, x, _stream(stream, out.device)), "la_probe_mfma32")
+        return out, blocks * 4 * iters * 4 * 32768
+    dt = {"f32": LA_F32, "bf16": LA_BF16}[kind]
     _check(lib().la_probe_mfma(_ptr(out), dt, blocks, iters, x, _stream(stream, out.device)), "la_probe_mfma")
     return out, blocks * 4 * iters * 8 * (2048 if kind == "f32" else 16384)

@@ -501,6 +501,18 @@ LA_API int la_probe_copy(void *dst, const void *src, size_t bytes, void *stream)
 LA_API size_t la_probe_read_partials(void);
 LA_API int la_probe_read(float *out, const void *src, size_t bytes, void *stream);
 LA_API int la_probe_mfma(float *out, int dtype, int64_t blocks, int iters, float x, void *stream);
+/* la_probe_write: fills `bytes` bytes of dst (device memory, 16-byte aligned;
+ * bytes a multiple of 16, else LA_ERR_INVALID_ARG; 0 is a no-op) with the fp32
+ * value `value` by nontemporal 16-byte stores.  Result bit-exact.  Written bytes
+ * over the launch's time give the attainable write-only HBM rate. */
+LA_API int la_probe_write(void *dst, size_t bytes, float value, void *stream);
+/* la_probe_mfma32: as la_probe_mfma with LA_BF16, on the bf16 32x32x16 shape:
+ * every wavefront runs `iters` rounds of 4 independent chains (32768 flops per
+ * MFMA), so flops per launch = blocks * 4 * iters * 4 * 32768; lane i writes the
+ * sum of its 64 accumulator values, 64 * iters * 16 * x^2 (x rounded to bf16),
+ * exact while that is an integer below 2^24.  blocks in [0, 2^20] and iters >= 0,
+ * else LA_ERR_INVALID_ARG; blocks = 0 is a no-op. */
+LA_API int la_probe_mfma32(float *out, int64_t blocks, int iters, float x, void *stream);
 
 #ifdef __cplusplus
 }

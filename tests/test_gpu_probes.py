@@ -1,6 +1,7 @@
 """The peak probes through the C ABI: the copy is bit-exact and every MFMA chain
 reaches the value its closed form gives (sum of 32 accumulator values per lane,
-each iters * K * x^2, with K = 4 for fp32 16x16x4 and 32 for bf16 16x16x32)."""
+each iters * K * x^2, with K = 4 for fp32 16x16x4 and 32 for bf16 16x16x32; 64 values per lane,
+each iters * 16 * x^2, for bf16 32x32x16); the write-only stream is bit-exact."""
 import pytest
 
 torch = pytest.importorskip("torch")
@@ -51,5 +52,25 @@ def test_mfma_closed_form(ea, kind, K, blocks, iters, x):
     torch.cuda.synchronize()
     want = 32.0 * iters * K * x * x
     assert flops == blocks * 4 * iters * 8 * (2048 if kind == "f32" else 16384)
+    assert out.shape == (blocks * 256,)
+    assert bool((out == want).all()), (out.min().item(), out.max().item(), want)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1000003, 1 << 26])
+def test_write_is_exact(ea, nbytes):
+    print(f"probe_write {nbytes}", flush=True)
+    dst = torch.full((nbytes // 4 + 8,), -1.0, dtype=torch.float32, device="cuda")
+    ea.probe_write(dst[:nbytes // 4], 1.5)
+    torch.cuda.synchronize()
+    assert bool((dst[:nbytes // 4] == 1.5).all()) and bool((dst[nbytes // 4:] == -1.0).all())
+
+
+@pytest.mark.parametrize("blocks,iters,x", [(1, 1, 0.5), (3, 17, 0.5), (512, 64, 0.25), (7, 0, 0.5)])
+def test_mfma32_closed_form(ea, blocks, iters, x):
+    print(f"probe_mfma bf16_32x32 blocks={blocks} iters={iters} x={x}", flush=True)
+    out, flops = ea.probe_mfma("bf16_32x32", blocks, iters, x)
+    torch.cuda.synchronize()
+    want = 64.0 * iters * 16 * x * x
+    assert flops == blocks * 4 * iters * 4 * 32768
     assert out.shape == (blocks * 256,)
     assert bool((out == want).all()), (out.min().item(), out.max().item(), want)
