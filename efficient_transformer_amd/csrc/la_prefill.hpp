@@ -1637,6 +1637,12 @@ __global__ __launch_bounds__((Cfg<T, D, M, C>::THREADS), (Cfg<T, D, M, C>::MIN_W
     if (fin) e.state_store(S, z, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
 }
 
+}  // namespace la
+
+#include "la_engine32.hpp"
+
+namespace la {
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (instantiated per element type in la_prefill_*.hip).
 // ---------------------------------------------------------------------------
@@ -1649,6 +1655,13 @@ hipError_t run_fused(const void *Q, const void *K, const void *V, void *out, voi
     } else {
         if (BH <= 0 || G_ <= 0) return hipSuccess;
         const unsigned grid = (unsigned)(G_ > 1 ? BH * G_ : BH);
+        if constexpr (std::is_same<T, bf16>::value && D == 128 && M == 128 && C == 64 && PHI) {
+            // bf16, D = M = 128, chunk 64: the engine on 32x32x16 tiles
+            hipLaunchKernelGGL((fused_causal32_kernel<OT>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const bf16 *)Q,
+                               (const bf16 *)K, (const bf16 *)V, (OT *)out, ws, BH, N, G_, CPS, S_out, z_out, S_in,
+                               z_in);
+            return hipGetLastError();
+        }
         hipLaunchKernelGGL((fused_causal_kernel<T, D, M, C, PHI, OT>), dim3(grid), dim3(Gc::THREADS), 0, stream, (const T *)Q,
                            (const T *)K, (const T *)V, (OT *)out, ws, BH, N, G_, CPS, S_out, z_out, S_in, z_in, nullptr,
                            0, 0);
