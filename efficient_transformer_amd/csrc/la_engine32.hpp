@@ -142,7 +142,7 @@ struct Engine32 : Engine<bf16, 128, 128, 64, true> {
     // the hand-over tile just read (only this wavefront uses it until the next
     // chunk's hand-over) as rows of 32 floats, 16-byte pieces XOR-swizzled by the
     // row, and is read back a row-piece per lane: every store instruction then
-    // writes 8 rows of 128 contiguous bytes.  LDS operations of one wavefront run
+    // writes 8 rows of 128 contiguous bytes (nontemporal: written once, not read).  LDS operations of one wavefront run
     // in issue order; the fence keeps the compiler from moving the reads first.
     template <typename OT>
     __device__ __forceinline__ void finish(const f32x16 &Pm, float inv_q, OT *__restrict__ Oh, int row0, int N,
@@ -169,9 +169,10 @@ struct Engine32 : Engine<bf16, 128, 128, 64, true> {
             if (grow < N) {
                 OT *dst = Oh + (size_t)grow * M + 32 * mb + 4 * p;
                 if constexpr (std::is_same<OT, float>::value) {
-                    *reinterpret_cast<f32x4 *>(dst) = y;
+                    __builtin_nontemporal_store(y, reinterpret_cast<f32x4 *>(dst));
                 } else {
-                    *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+                    __builtin_nontemporal_store(bf16x4{(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]},
+                                                reinterpret_cast<bf16x4 *>(dst));
                 }
             }
         }
@@ -253,9 +254,11 @@ __device__ __forceinline__ void phase_b32(const Engine32 &e, const bf16 *__restr
     for (int c = c0; c < c1; ++c) {
         const int row0 = c * C;
         __syncthreads();  // LDS free; the previous chunk's hand-overs are written
-        if (c > c0) e.finish(Pm, inv_q, Oh, row0 - C, N, poison);
         e.store_q(q, row0, N);
         e.store_kv(b.k, b.v, row0, N);
+        // the previous chunk's rows after the staging: its stores then do not
+        // delay the waits for this chunk's loads (the wait counter counts both)
+        if (c > c0) e.finish(Pm, inv_q, Oh, row0 - C, N, poison);
         if (e.tid < 128) e.set_z(z);
         __syncthreads();
         const int cn = min(c + 1, c1 - 1);
