@@ -237,6 +237,8 @@ def causal_kernel_name(cfg, chunk, segments) -> str:
     t = "float" if cfg["dtype"] == "f32" else "bf16"
     ot = "bf16" if cfg.get("out") == "bf16" else "float"
     extra = f", 0, {t}" if kind == "onepass_causal_kernel" else ""
+    if kind == "fused_causal_kernel" and t == "bf16" and cfg["D"] == cfg["M"] == 128 and chunk == 64:
+        return f"fused_causal32_kernel<{ot}>"  # the 32x32x16 engine for this shape
     return f"{kind}<{t}, {cfg['D']}, {cfg['M']}, {chunk}, true, {ot}{extra}>"
 
 
