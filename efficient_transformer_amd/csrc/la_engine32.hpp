@@ -239,42 +239,71 @@ __device__ __forceinline__ void phase_a32(const Engine32 &e, const bf16 *__restr
 }
 
 // Phase B on the 32x32 engine: outputs of chunks [c0, c1) from the state S of all
-// earlier positions; loads one chunk ahead; each chunk's rows are stored after
-// the next chunk's first barrier (the last ones after a barrier of their own).
+// earlier positions.  The phi(Q), phi(K), V tiles are double-buffered in LDS
+// (e: buffer 0, e1: buffer 1, fixed per unrolled step so that every tile
+// address stays a constant offset): a step stages chunk c + 1 into the other
+// buffer and issues the loads of chunk c + 2, then forms chunk c's outputs and
+// state update; after one barrier it stores chunk c's rows (the hand-over of
+// the row halves is complete) and forms chunk c + 1's A tiles, phi(q) . z and
+// column sums; a second barrier ends the step.  Two barriers per chunk, and
+// the staging of one chunk sits beside the products of the previous one.
 template <typename OT>
-__device__ __forceinline__ void phase_b32(const Engine32 &e, const bf16 *__restrict__ Qh, const bf16 *__restrict__ Kh,
-                                          const bf16 *__restrict__ Vh, OT *__restrict__ Oh, int N, int c0, int c1,
-                                          bool advance_last, Stage<bf16, 64, 128, 512> &q, f32x16 (&S)[2], float &z,
-                                          bool poison) {
+__device__ __forceinline__ void phase_b32(const Engine32 &e, const Engine32 &e1, const bf16 *__restrict__ Qh,
+                                          const bf16 *__restrict__ Kh, const bf16 *__restrict__ Vh,
+                                          OT *__restrict__ Oh, int N, int c0, int c1, bool advance_last,
+                                          Stage<bf16, 64, 128, 512> &q, f32x16 (&S)[2], float &z, bool poison) {
     constexpr int C = 64;
     KVBuf<bf16, 128, 128, 64> b;
     b.template load<true>(Kh, Vh, c0, N, e.tid);
-    f32x16 Pm = zero16();
-    float inv_q = 0.0f;
-    for (int c = c0; c < c1; ++c) {
-        const int row0 = c * C;
-        __syncthreads();  // LDS free; the previous chunk's hand-overs are written
-        e.store_q(q, row0, N);
-        e.store_kv(b.k, b.v, row0, N);
-        // the previous chunk's rows after the staging: its stores then do not
-        // delay the waits for this chunk's loads (the wait counter counts both)
-        if (c > c0) e.finish(Pm, inv_q, Oh, row0 - C, N, poison);
-        if (e.tid < 128) e.set_z(z);
-        __syncthreads();
-        const int cn = min(c + 1, c1 - 1);
+    // prologue: chunk c0 into buffer 0, its A tiles and sums
+    __syncthreads();  // LDS free (phase A and the look-back are done with it)
+    e.store_q(q, c0 * C, N);
+    e.store_kv(b.k, b.v, c0 * C, N);
+    if (e.tid < 128) e.set_z(z);
+    {
+        const int cn = min(c0 + 1, c1 - 1);
         q.template load<true>(Qh, cn * C, N, e.tid);
         b.template load<true>(Kh, Vh, cn, N, e.tid);
-        e.a_tiles();
-        e.qz_rows();
-        const bool adv = c + 1 < c1 || advance_last;
-        if (adv) e.z_partials();
-        __syncthreads();
-        inv_q = __shfl(e.row_inv<true>(), 32 * e.dh + e.l32, 64);
-        Pm = e.chunk_outputs(S, adv);
-        if (adv && e.tid < 128) z += e.z_delta();
     }
     __syncthreads();
-    e.finish(Pm, inv_q, Oh, (c1 - 1) * C, N, poison);
+    e.a_tiles();
+    e.qz_rows();
+    if (c0 + 1 < c1 || advance_last) e.z_partials();
+    __syncthreads();
+    // step for chunk c (valid: c < c1; uniform) with its tiles in `cur`
+    auto step = [&](const Engine32 &cur, const Engine32 &nxt, int c, bool valid) {
+        const bool has_next = valid && c + 1 < c1;
+        if (has_next) {
+            nxt.store_q(q, (c + 1) * C, N);
+            nxt.store_kv(b.k, b.v, (c + 1) * C, N);
+        }
+        {
+            const int cn = min(c + 2, c1 - 1);
+            q.template load<true>(Qh, cn * C, N, e.tid);
+            b.template load<true>(Kh, Vh, cn, N, e.tid);
+        }
+        f32x16 Pm;
+        float inv_q = 0.0f;
+        if (valid) {
+            const bool adv = c + 1 < c1 || advance_last;
+            inv_q = __shfl(cur.row_inv<true>(), 32 * e.dh + e.l32, 64);
+            Pm = cur.chunk_outputs(S, adv);
+            if (adv && e.tid < 128) z += cur.z_delta();
+            if (e.tid < 128) cur.set_z(z);  // for chunk c + 1
+        }
+        __syncthreads();  // chunk c's reads of A, the sums and its buffer done; hand-overs written
+        if (valid) cur.finish(Pm, inv_q, Oh, c * C, N, poison);
+        if (has_next) {
+            nxt.a_tiles();
+            nxt.qz_rows();
+            if (c + 2 < c1 || advance_last) nxt.z_partials();
+        }
+        __syncthreads();
+    };
+    for (int c = c0; c < c1; c += 2) {
+        step(e, e1, c, true);
+        step(e1, e, c + 1, c + 1 < c1);
+    }
 }
 
 // Phase A, decoupled look-back, phase B (as fused_causal_kernel, without the
@@ -289,8 +318,13 @@ __global__ __launch_bounds__(512, 1) void fused_causal32_kernel(const bf16 *__re
     constexpr int C = 64, D = 128, M = 128;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
     __shared__ __attribute__((aligned(16))) float sx[8 * 4 * 64 * 4];
+    __shared__ __attribute__((aligned(16))) bf16 stiles[3 * 64 * 128];  // phase B's second tile buffer
     __shared__ unsigned sh_word[4];
     Engine32 e(smem, sx);
+    Engine32 e1 = e;
+    e1.sQ = stiles;
+    e1.sK = stiles + 64 * 128;
+    e1.sV = stiles + 2 * 64 * 128;
     const int tid = e.tid;
 
     // block b -> segment b / BH of head b % BH (dispatched in block order; see fused_causal_kernel)
@@ -362,7 +396,7 @@ __global__ __launch_bounds__(512, 1) void fused_causal32_kernel(const bf16 *__re
                         z_out + (size_t)bh * D);
     }
 
-    phase_b32<OT>(e, Qh, Kh, Vh, Oh, N, c0, c1, G_ == 1 && want_final, stQ, pre, zpre, failed);
+    phase_b32<OT>(e, e1, Qh, Kh, Vh, Oh, N, c0, c1, G_ == 1 && want_final, stQ, pre, zpre, failed);
     if (G_ == 1 && want_final) e.state_store32(pre, zpre, S_out + (size_t)bh * D * M, z_out + (size_t)bh * D);
 
     if (G_ > 1 && last) finish_call(ws, epoch, (unsigned)BH);
