@@ -212,29 +212,38 @@ struct Engine32 : Engine<bf16, 128, 128, 64, true> {
     }
 };
 
-// Phase A on the 32x32 engine: the segment's state over chunks [c0, c1); two
-// chunks of loads in flight, as in phase_a.
-__device__ __forceinline__ void phase_a32(const Engine32 &e, const bf16 *__restrict__ Kh, const bf16 *__restrict__ Vh,
-                                          int N, int c0, int c1, f32x16 (&acc)[2], float &z) {
+// Phase A on the 32x32 engine: the segment's state over chunks [c0, c1).  Two
+// register buffers (loads two chunks ahead, reloaded unconditionally with the
+// chunk index clamped) and two LDS tile buffers with their own column-sum
+// partials (e and e1, fixed per unrolled step): a step stages chunk c + 1 into
+// the other buffer, then forms chunk c's column sums and state update; one
+// barrier per chunk, after which chunk c's column sums are added.
+__device__ __forceinline__ void phase_a32(const Engine32 &e, const Engine32 &e1, const bf16 *__restrict__ Kh,
+                                          const bf16 *__restrict__ Vh, int N, int c0, int c1, f32x16 (&acc)[2],
+                                          float &z) {
     using KV = KVBuf<bf16, 128, 128, 64>;
     constexpr int C = 64;
     KV b0, b1;
     b0.template load<true>(Kh, Vh, c0, N, e.tid);
     b1.template load<true>(Kh, Vh, min(c0 + 1, c1 - 1), N, e.tid);
-    auto body = [&](const KV &b, int c) {
-        __syncthreads();  // LDS free
-        e.store_kv(b.k, b.v, c * C, N);
+    __syncthreads();
+    e.store_kv(b0.k, b0.v, c0 * C, N);
+    b0.template load<true>(Kh, Vh, min(c0 + 2, c1 - 1), N, e.tid);
+    __syncthreads();
+    // bn holds chunk c + 1 on entry and is reloaded with chunk c + 3
+    auto step = [&](const Engine32 &cur, const Engine32 &nxt, KV &bn, int c, bool valid) {
+        if (valid && c + 1 < c1) nxt.store_kv(bn.k, bn.v, (c + 1) * C, N);
+        bn.template load<true>(Kh, Vh, min(c + 3, c1 - 1), N, e.tid);
+        if (valid) {
+            cur.z_partials();
+            cur.state_update32(acc);
+        }
         __syncthreads();
-        e.z_partials();
-        e.state_update32(acc);
-        __syncthreads();
-        if (e.tid < 128) z += e.z_delta();
+        if (valid && e.tid < 128) z += cur.z_delta();
     };
     for (int c = c0; c < c1; c += 2) {
-        body(b0, c);
-        b0.template load<true>(Kh, Vh, min(c + 2, c1 - 1), N, e.tid);
-        if (c + 1 < c1) body(b1, c + 1);
-        b1.template load<true>(Kh, Vh, min(c + 3, c1 - 1), N, e.tid);
+        step(e, e1, b1, c, true);
+        step(e1, e, b0, c + 1, c + 1 < c1);
     }
 }
 
@@ -318,13 +327,15 @@ __global__ __launch_bounds__(512, 1) void fused_causal32_kernel(const bf16 *__re
     constexpr int C = 64, D = 128, M = 128;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Gc::bytes];
     __shared__ __attribute__((aligned(16))) float sx[8 * 4 * 64 * 4];
-    __shared__ __attribute__((aligned(16))) bf16 stiles[3 * 64 * 128];  // phase B's second tile buffer
+    __shared__ __attribute__((aligned(16))) bf16 stiles[3 * 64 * 128];  // second tile buffer
+    __shared__ __attribute__((aligned(16))) float szp1[128];            // its column-sum partials (phase A)
     __shared__ unsigned sh_word[4];
     Engine32 e(smem, sx);
     Engine32 e1 = e;
     e1.sQ = stiles;
     e1.sK = stiles + 64 * 128;
     e1.sV = stiles + 2 * 64 * 128;
+    e1.szp = szp1;
     const int tid = e.tid;
 
     // block b -> segment b / BH of head b % BH (dispatched in block order; see fused_causal_kernel)
@@ -353,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void fused_causal32_kernel(const bf16 *__re
     const bool last = s == G_ - 1;
     const bool want_final = S_out != nullptr;
     const bool run_a = G_ > 1 && (!last || want_final);
-    if (run_a) phase_a32(e, Kh, Vh, N, c0, c1, acc, zacc);
+    if (run_a) phase_a32(e, e1, Kh, Vh, N, c0, c1, acc, zacc);
     const size_t my = (size_t)bh * G_ + s;
     f32x16 pre[2] = {zero16(), zero16()};
     float zpre = 0.0f;
