@@ -17,8 +17,10 @@
 // 64 rows of the chunk; the two wavefronts of one column block add their
 // partials through LDS: wavefront (mb, dh) finishes the chunk rows of half dh
 // (adding its partner's partial and the intra-chunk term) and hands over the
-// other half.  The hand-over is read after the next chunk's first barrier, so a
-// chunk still takes three barriers.
+// other half, read after the barrier that follows the products.  The phi(Q),
+// phi(K), V tiles are double-buffered, so a chunk is staged beside the
+// previous chunk's products: phase B takes two barriers per chunk, phase A
+// one.
 //
 // Register layouts (lane l, h = l / 32, l32 = l % 32; value v of a 16-value
 // accumulator): a 32 x 32 result holds row 8 (v / 4) + 4 h + v % 4 and column
@@ -142,8 +144,9 @@ struct Engine32 : Engine<bf16, 128, 128, 64, true> {
     // the hand-over tile just read (only this wavefront uses it until the next
     // chunk's hand-over) as rows of 32 floats, 16-byte pieces XOR-swizzled by the
     // row, and is read back a row-piece per lane: every store instruction then
-    // writes 8 rows of 128 contiguous bytes (nontemporal: written once, not read).  LDS operations of one wavefront run
-    // in issue order; the fence keeps the compiler from moving the reads first.
+    // writes 8 rows of 128 contiguous bytes (nontemporal: written once, not
+    // read).  LDS operations of one wavefront run in issue order; the fence keeps
+    // the compiler from moving the reads first.
     template <typename OT>
     __device__ __forceinline__ void finish(const f32x16 &Pm, float inv_q, OT *__restrict__ Oh, int row0, int N,
                                            bool poison) const {
@@ -179,7 +182,9 @@ struct Engine32 : Engine<bf16, 128, 128, 64, true> {
     }
 
     // state value v of block t <-> (d, m)
-    __device__ __forceinline__ int srow(int t, int v) const { return 32 * (2 * dh + t) + 8 * (v >> 2) + 4 * h + (v & 3); }
+    __device__ __forceinline__ int srow(int t, int v) const {
+        return 32 * (2 * dh + t) + 8 * (v >> 2) + 4 * h + (v & 3);
+    }
     __device__ __forceinline__ int scol() const { return 32 * mb + l32; }
     __device__ __forceinline__ void state_store32(const f32x16 (&S)[2], float z, float *Sd, float *zd) const {
 #pragma unroll
@@ -200,7 +205,8 @@ struct Engine32 : Engine<bf16, 128, 128, 64, true> {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) X[4 * t + j][0] = f32x4{S[t][4 * j], S[t][4 * j + 1], S[t][4 * j + 2], S[t][4 * j + 3]};
+            for (int j = 0; j < 4; ++j)
+                X[4 * t + j][0] = f32x4{S[t][4 * j], S[t][4 * j + 1], S[t][4 * j + 2], S[t][4 * j + 3]};
     }
     static __device__ __forceinline__ void from4(const f32x4 (&X)[8][1], f32x16 (&S)[2]) {
 #pragma unroll
