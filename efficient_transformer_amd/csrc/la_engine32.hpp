@@ -151,12 +151,13 @@ struct Engine32 : Engine<bf16, 128, 128, 64, true> {
     __device__ __forceinline__ void finish(const f32x16 &Pm, float inv_q, OT *__restrict__ Oh, int row0, int N,
                                            bool poison) const {
         f32x4 *tile = reinterpret_cast<f32x4 *>(sx) + ((w ^ 4) * 4) * 64;
+        const float f = poison ? __builtin_nanf("") : inv_q;  // a poisoned call's rows are NaN
         f32x4 v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4 x = tile[j * 64 + lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[j][r] = poison ? __builtin_nanf("") : (Pm[4 * j + r] + x[r]) * inv_q;
+            for (int r = 0; r < 4; ++r) v[j][r] = (Pm[4 * j + r] + x[r]) * f;
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         // row q = l32 of the tile, columns 8 j + 4 h .. + 3: 16-byte piece 2 j + h
