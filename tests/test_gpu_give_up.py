@@ -33,15 +33,21 @@ def check_rows(got, want, rows_ok):
     return nan_rows
 
 
-@pytest.mark.parametrize("shape", [(8, 8, 1024, 64, 64), (1, 4, 8192, 64, 64), (1, 2, 65536, 64, 64)])
-def test_forward_gives_up_cleanly(ea, shape):
+@pytest.mark.parametrize("dtype,shape", [("f32", (8, 8, 1024, 64, 64)), ("f32", (1, 4, 8192, 64, 64)),
+                                         ("f32", (1, 2, 65536, 64, 64)), ("bf16", (1, 2, 65536, 128, 128))])
+def test_forward_gives_up_cleanly(ea, dtype, shape):
     """In-order look-back (8 segments per head), inclusive look-back (one-pass
-    kernel with 128 segments) and the two-phase kernel."""
+    kernel with 128 segments), the two-phase kernel, and the two-phase kernel on
+    32x32x16 tiles (bf16, D = M = 128: 128 segments of 8 chunks per head)."""
     B, H, N, D, M = shape
-    cfg = dict(kind="prefill", B=B, H=H, N=N, D=D, M=M, sigma=1.0, dtype="f32", chunk=0)
-    Q, K, V = (to_dev(x, "f32") for x in synthetic.prefill_inputs(cfg, 90))
-    C, G, need = ea.forward_plan(B, H, N, D, M, True, 0, 0)
+    print(f"give-up {dtype} {shape}", flush=True)
+    cfg = dict(kind="prefill", B=B, H=H, N=N, D=D, M=M, sigma=1.0, dtype=dtype, chunk=0)
+    Q, K, V = (to_dev(x, dtype) for x in synthetic.prefill_inputs(cfg, 90))
+    code = ea.linattn.LA_F32 if dtype == "f32" else ea.linattn.LA_BF16
+    C, G, need = ea.forward_plan(B, H, N, D, M, True, code, 0)
     assert G > 1
+    if dtype == "bf16":
+        assert C == 64 and -(-(-(-N // C)) // G) > 4  # segments of more than 4 chunks: the two-phase kernel
     want = ea.forward_chunked(Q, K, V)
     ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
     words = ws.view(torch.int32)
