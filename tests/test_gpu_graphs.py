@@ -66,6 +66,49 @@ def test_forward_replays(ea, shape):
             assert rowwise_rel(got.cpu().numpy(), oracle.causal(Q, K, V)[0]) <= TOL["f32"]
 
 
+def test_forward_replays_long_head_bf16(ea):
+    """A captured call of the two-phase kernel on 32x32x16 tiles (bf16, D = M = 128:
+    128 segments of 8 chunks per head), replayed with new inputs each time."""
+    B, H, N, D, M = 1, 2, 65536, 128, 128
+    code = ea.linattn.LA_BF16
+    C, G, need = ea.forward_plan(B, H, N, D, M, True, code, 0)
+    assert C == 64 and -(-(-(-N // C)) // G) > 4
+    Qd = torch.empty((B, H, N, D), device=DEV, dtype=torch.bfloat16)
+    Kd = torch.empty_like(Qd)
+    Vd = torch.empty((B, H, N, M), device=DEV, dtype=torch.bfloat16)
+    out = torch.empty((B, H, N, M), device=DEV)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+
+    def load(seed):
+        Q, K, V = inputs(B, H, N, D, M, seed, "bf16")
+        Qd.copy_(to_dev(Q, "bf16"))
+        Kd.copy_(to_dev(K, "bf16"))
+        Vd.copy_(to_dev(V, "bf16"))
+        return Q, K, V
+
+    load(85)
+    ea.forward_chunked(Qd, Kd, Vd, out=out, workspace=ws)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ea.forward_chunked(Qd, Kd, Vd, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        print(f"long-head bf16 replay {rep}", flush=True)
+        Q, K, V = load(86 + rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        eager = ea.forward_chunked(Qd, Kd, Vd)
+        torch.cuda.synchronize()
+        assert rowwise_rel(got.cpu().numpy(), eager.cpu().numpy()) <= 1e-5, rep
+        if rep == 0:  # the first 4096 rows of head 0 depend only on themselves
+            n = 4096
+            ref = oracle.causal(*(synthetic.as_f64(x[:, :1, :n], "bf16") for x in (Q, K, V)))[0]
+            assert rowwise_rel(got[:, :1, :n].cpu().numpy(), ref) <= TOL["bf16"]
+
+
 def test_decode_replays(ea):
     """A captured la_decode_step (state updated in place) replayed T times equals T
     eager steps; the inputs change between replays."""
